@@ -1,0 +1,637 @@
+"""CPU oracle for low-bit KV-cache quantize-on-append and packed-cache decode attention.
+
+TEST INFRASTRUCTURE ONLY. This module is the slow, plain reference the HIP
+path is checked against. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run it; the library
+``bit_kv_cache_quantize_amd`` never does, and this module imports nothing from
+it. It shares no code with the HIP kernels.
+
+Sources (cited by page title and section; the pages are web pages on one
+subject, quoted nowhere here):
+  [KVQ]  "KVQuant reading notes" (KVQuant: Towards 10 Million Context Length LLM
+         Inference with KV Cache Quantization), sections 1.1-1.3, 3.1-3.4, 3.6,
+         3.8 (Algorithm 1), 9.1, 9.3 and the appendix worked example.
+  [KVARN] "KVarN: Variance-Normalized KV-Cache Quantization ..." summary,
+         background (KIVI / RTN representation), core method and method steps.
+  [BLOG] "reproducing TurboQuant" blog post, sections 1.1, 2.1, 4.1, 4.2, 5.2.
+
+Precision: quantization decisions (statistics and codes) are taken in IEEE
+fp32 with a fixed operation order and round-half-even, exactly as the kernels
+take them, because an fp32 result decides an integer code. Dequantization,
+RoPE, the Hadamard rotation, VarN and attention are computed in fp64.
+
+Readings of the pages where they are silent or inconsistent are listed in the
+design notes; the ones that change arithmetic are repeated at the function
+that implements them.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+except VarN's agreement with the KVarN paper's own algorithm, which the
+summary page does not print: VarN is pinned only by invariants (row std = 1
+after the final token step, exact reconstruction, column-scale equivariance,
+shrinking dispersion). That part is "parity unpinned" against the paper.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+T = 128          # tokens per quantization block
+D = 128          # head dimension (channels)
+
+MODE_RTN, MODE_NUQ, MODE_KVARN, MODE_SYM_INT4 = 0, 1, 2, 3
+
+
+# ---------------------------------------------------------------------------
+# Sizes and bit accounting
+# ---------------------------------------------------------------------------
+
+def kv_cache_bytes(n_layers: int, n_heads: int, head_dim: int, bytes_per_elem: float,
+                   batch: int, seq_len: int) -> float:
+    """KV-cache size 2 * n * h * d * e * b * l bytes ([KVQ] 1.1; [BLOG] 1.1 with KV heads)."""
+    return 2.0 * n_layers * n_heads * head_dim * bytes_per_elem * batch * seq_len
+
+
+def dense_sparse_avg_bits(bits: int, outlier_fraction: float, outlier_bits: int = 16) -> float:
+    """Average bits of a dense b-bit part plus a sparse fp16 fraction ([KVQ] 3.4)."""
+    return (1.0 - outlier_fraction) * bits + outlier_fraction * outlier_bits
+
+
+def block_scale_bits(bits: int, block: int, scale_bits: int = 16) -> float:
+    """Bits per element of b-bit codes with one scale per block of elements ([BLOG] 2.1)."""
+    return bits + scale_bits / block
+
+
+# ---------------------------------------------------------------------------
+# fp16 helpers
+# ---------------------------------------------------------------------------
+
+def f16_magnitude(x16: np.ndarray) -> np.ndarray:
+    """|x| of fp16 values as integers: the low 15 bits order finite magnitudes."""
+    return (np.asarray(x16, np.float16).view(np.uint16) & np.uint16(0x7FFF)).astype(np.int32)
+
+
+def n_outliers(fraction: float, vec_len: int = 128) -> int:
+    """Outliers per vector: round-half-even(fraction * length); 1% of 128 -> 1."""
+    return int(np.rint(fraction * vec_len))
+
+
+# ---------------------------------------------------------------------------
+# Outlier selection ([KVQ] 3.4 dense-and-sparse split; per vector, top-k)
+# ---------------------------------------------------------------------------
+
+def outlier_mask(x16: np.ndarray, k: int, axis: int) -> np.ndarray:
+    """Boolean mask of the k largest |x| along ``axis``; ties go to the lower index.
+
+    [KVQ] 3.4 keeps about 1% of each vector in fp16. The notes use an offline
+    per-channel threshold; with no calibration data this build selects, per
+    vector, the k entries of largest magnitude (reading: per-vector top-k).
+    """
+    mask = np.zeros(x16.shape, bool)
+    if k <= 0:
+        return mask
+    mag = f16_magnitude(x16)
+    order = np.argsort(-mag, axis=axis, kind="stable")
+    top = np.take(order, np.arange(k), axis=axis)
+    np.put_along_axis(mask, top, True, axis=axis)
+    return mask
+
+
+# ---------------------------------------------------------------------------
+# Uniform asymmetric RTN ([KVQ] 1.2 and 3.1; [KVARN] background, KIVI form)
+# ---------------------------------------------------------------------------
+
+def rtn_stats(x32: np.ndarray, keep: np.ndarray, bits: int, axis: int):
+    """Scale and zero point of each vector: m = min, s = (max - min) / (2^b - 1).
+
+    Taken over the vector's non-outlier entries ``keep`` ([KVQ] Algorithm 1,
+    step 4 excludes outliers). One fp32 subtraction and one fp32 division.
+    """
+    lo = np.where(keep, x32, np.float32(np.inf)).min(axis=axis)
+    hi = np.where(keep, x32, np.float32(-np.inf)).max(axis=axis)
+    s = (hi - lo).astype(np.float32) / np.float32((1 << bits) - 1)
+    return s.astype(np.float32), lo.astype(np.float32)
+
+
+def rtn_codes(x32: np.ndarray, s: np.ndarray, m: np.ndarray, bits: int) -> np.ndarray:
+    """q = clamp(rint((x - m) / s), 0, 2^b - 1); a zero range gives code 0."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = (x32 - m).astype(np.float32) / s
+    q = np.clip(np.rint(u), 0, (1 << bits) - 1)
+    q = np.where(s == 0, 0, q)
+    return q.astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# Non-uniform quantization ([KVQ] 1.2 NUQ argmin, 3.3, appendix example)
+# ---------------------------------------------------------------------------
+
+def nuq_stats(x32: np.ndarray, keep: np.ndarray, axis: int):
+    """Centre z = (max + min) / 2 and half range h = (max - min) / 2 (fp32).
+
+    Reading: the codebook lives on [-1, 1], so each vector is normalised by its
+    midpoint and half range before the lookup (the appendix example divides by
+    a scale and clips 1.45 to 1.0).
+    """
+    lo = np.where(keep, x32, np.float32(np.inf)).min(axis=axis)
+    hi = np.where(keep, x32, np.float32(-np.inf)).max(axis=axis)
+    z = (hi + lo).astype(np.float32) * np.float32(0.5)
+    h = (hi - lo).astype(np.float32) * np.float32(0.5)
+    return z.astype(np.float32), h.astype(np.float32)
+
+
+def nuq_normalise(x32: np.ndarray, z: np.ndarray, h: np.ndarray) -> np.ndarray:
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = (x32 - z).astype(np.float32) / h
+    u = np.where(h == 0, np.float32(0), u)
+    return np.clip(u, np.float32(-1), np.float32(1)).astype(np.float32)
+
+
+def nuq_codes(x32: np.ndarray, z: np.ndarray, h: np.ndarray, codebook: np.ndarray) -> np.ndarray:
+    """q = argmin_j |u - C_j| in fp32, u the normalised value; ties take the smaller j."""
+    u = nuq_normalise(x32, z, h)
+    C = np.asarray(codebook, np.float32)
+    best = np.full(u.shape, np.inf, np.float32)
+    q = np.zeros(u.shape, np.uint8)
+    for j in range(C.size):                      # scan in index order, strict '<'
+        d = np.abs((u - C[j]).astype(np.float32))
+        better = d < best
+        best = np.where(better, d, best)
+        q = np.where(better, np.uint8(j), q)
+    return q
+
+
+# ---------------------------------------------------------------------------
+# Symmetric block int4 ([BLOG] 2.1 and 4.2)
+# ---------------------------------------------------------------------------
+
+def sym_scale(x32: np.ndarray, keep: np.ndarray, axis: int) -> np.ndarray:
+    """fp16 scale = f16_rne(max|x| / 7) over the vector's non-outlier entries."""
+    a = np.where(keep, np.abs(x32), np.float32(0)).max(axis=axis).astype(np.float32)
+    return (a / np.float32(7.0)).astype(np.float32).astype(np.float16)
+
+
+def sym_codes(x32: np.ndarray, s16: np.ndarray) -> np.ndarray:
+    """u = clamp(rint(x / s), -8, 7) + 8, offset binary in 0..15; s = 0 gives u = 8.
+
+    Reading: the blog's quantizer keeps q & 0xF (two's complement) while its
+    dequantizer subtracts 8; the stored code here is the offset-binary q + 8 so
+    that dequantisation is (u - 8) * s.
+    """
+    s = np.asarray(s16, np.float16).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = x32 / s
+    q = np.clip(np.rint(u), -8, 7)
+    q = np.where(s == 0, 0, q)
+    return (q + 8).astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# Hadamard rotation and VarN ([KVARN] core method and method steps)
+# ---------------------------------------------------------------------------
+
+def sylvester_hadamard(n: int) -> np.ndarray:
+    """H[i][j] = (-1)^popcount(i & j), the Sylvester (natural-order) Hadamard matrix."""
+    i = np.arange(n)
+    bits = np.bitwise_and.outer(i, i)
+    pc = np.zeros_like(bits)
+    while np.any(bits):
+        pc += bits & 1
+        bits >>= 1
+    return np.where(pc % 2 == 0, 1, -1).astype(np.int64)
+
+
+_H128 = sylvester_hadamard(D).astype(np.float64)
+
+
+def hadamard_rotate(x: np.ndarray) -> np.ndarray:
+    """Orthonormal rotation across channels: y = H x / sqrt(128) for every row (fp64).
+
+    H is symmetric and H H^T = 128 I, so the same call also undoes the rotation.
+    """
+    return (np.asarray(x, np.float64) @ _H128) / math.sqrt(D)
+
+
+def varn(y: np.ndarray, iters: int):
+    """Dual-axis variance normalisation in the log-std domain (fp64).
+
+    Per iteration: normalise channels, then tokens. X~ = Y * exp(-r_t - c_ch);
+    c_ch += log(std over tokens of X~[:, ch]); X~ is formed again;
+    r_t += log(std over channels of X~[t, :]). Population std (mean removed).
+    A zero std leaves its log-scale unchanged. Returns (r[T], c[D]).
+    Reading: channel step first, then token step, ``iters`` full iterations.
+    """
+    y = np.asarray(y, np.float64)
+    r = np.zeros(y.shape[0])
+    c = np.zeros(y.shape[1])
+    for _ in range(iters):
+        xt = y * np.exp(-r[:, None] - c[None, :])
+        sc = xt.std(axis=0)
+        c = c + np.where(sc > 0, np.log(np.where(sc > 0, sc, 1.0)), 0.0)
+        xt = y * np.exp(-r[:, None] - c[None, :])
+        st = xt.std(axis=1)
+        r = r + np.where(st > 0, np.log(np.where(st > 0, st, 1.0)), 0.0)
+    return r, c
+
+
+# ---------------------------------------------------------------------------
+# Cache configuration
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Config:
+    n_layers: int
+    batch: int
+    n_kv_heads: int
+    n_q_heads: int
+    max_tokens: int
+    mode: int
+    bits: int
+    outliers_per_vec: int = 0
+    pre_rope: int = 0
+    rope_theta: float = 10000.0
+    varn_iters: int = 8
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+
+# ---------------------------------------------------------------------------
+# Quantizing one 128-token block (the per-block record)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Block:
+    kcodes: np.ndarray          # [T][D] u8, code of key (token t, channel c)
+    vcodes: np.ndarray          # [T][D] u8, code of value (token t, channel c)
+    kstat: tuple                # RTN/KVARN (s[D], m[D]); NUQ (z[D], h[D]); SYM (s16[D],)
+    vstat: tuple                # RTN/KVARN (s[T], m[T]); NUQ (z[T], h[T]); SYM (s16[D],)
+    ks1: np.ndarray | None = None   # KVARN: f32 [T], per token
+    vs1: np.ndarray | None = None   # KVARN: f32 [D], per channel
+    kmask: np.ndarray | None = None  # [T][D] outlier positions of keys
+    vmask: np.ndarray | None = None
+    kout: np.ndarray | None = None   # fp16 key values at the outlier positions ([T][D], else 0)
+    vout: np.ndarray | None = None
+
+
+def quantize_block(k16: np.ndarray, v16: np.ndarray, cfg: Config,
+                   cb_k: np.ndarray | None = None, cb_v: np.ndarray | None = None) -> Block:
+    """Quantize one block of 128 tokens x 128 channels of keys and values.
+
+    Keys: statistics per channel over the block's tokens ([KVQ] 3.1 per-channel
+    keys, with a 128-token window as in [KVARN] and [BLOG]). Values: statistics
+    per token over channels ([KVQ] 3.6), except symmetric int4, whose values are
+    also grouped along the sequence ([BLOG] 2.1: 128-element blocks in the
+    sequence direction).
+    """
+    k16 = np.asarray(k16, np.float16).reshape(T, D)
+    v16 = np.asarray(v16, np.float16).reshape(T, D)
+    b, mode, ko = cfg.bits, cfg.mode, cfg.outliers_per_vec
+    out = {}
+    if mode == MODE_KVARN:
+        yk = hadamard_rotate(k16.astype(np.float64))
+        yv = hadamard_rotate(v16.astype(np.float64))
+        rk, _ = varn(yk, cfg.varn_iters)
+        _, cv = varn(yv, cfg.varn_iters)
+        ks1 = np.exp(rk).astype(np.float32)                      # per token
+        vs1 = np.exp(cv).astype(np.float32)                      # per channel
+        kx = (yk / ks1.astype(np.float64)[:, None]).astype(np.float32)
+        vx = (yv / vs1.astype(np.float64)[None, :]).astype(np.float32)
+        keep = np.ones((T, D), bool)
+        ks, km = rtn_stats(kx, keep, b, axis=0)
+        vs, vm = rtn_stats(vx, keep, b, axis=1)
+        return Block(rtn_codes(kx, ks[None, :], km[None, :], b),
+                     rtn_codes(vx, vs[:, None], vm[:, None], b),
+                     (ks, km), (vs, vm), ks1=ks1, vs1=vs1)
+
+    kx = k16.astype(np.float32)
+    vx = v16.astype(np.float32)
+    kmask = outlier_mask(k16, ko, axis=0)      # per channel, over tokens
+    vmask = outlier_mask(v16, ko, axis=1)      # per token, over channels
+    if mode == MODE_SYM_INT4:
+        vmask = outlier_mask(v16, ko, axis=0)  # values grouped per channel too
+    kkeep, vkeep = ~kmask, ~vmask
+    if mode == MODE_RTN:
+        ks, km = rtn_stats(kx, kkeep, b, axis=0)
+        vs, vm = rtn_stats(vx, vkeep, b, axis=1)
+        kc = rtn_codes(kx, ks[None, :], km[None, :], b)
+        vc = rtn_codes(vx, vs[:, None], vm[:, None], b)
+        kstat, vstat = (ks, km), (vs, vm)
+    elif mode == MODE_NUQ:
+        kz, kh = nuq_stats(kx, kkeep, axis=0)
+        vz, vh = nuq_stats(vx, vkeep, axis=1)
+        kc = nuq_codes(kx, kz[None, :], kh[None, :], cb_k)
+        vc = nuq_codes(vx, vz[:, None], vh[:, None], cb_v)
+        kstat, vstat = (kz, kh), (vz, vh)
+    elif mode == MODE_SYM_INT4:
+        kss = sym_scale(kx, kkeep, axis=0)
+        vss = sym_scale(vx, vkeep, axis=0)
+        kc = sym_codes(kx, kss[None, :])
+        vc = sym_codes(vx, vss[None, :])
+        kstat, vstat = (kss,), (vss,)
+    else:
+        raise ValueError(mode)
+    blk = Block(kc, vc, kstat, vstat)
+    if ko > 0:
+        blk.kmask, blk.vmask = kmask, vmask
+        blk.kout = np.where(kmask, k16, np.float16(0))
+        blk.vout = np.where(vmask, v16, np.float16(0))
+    return blk
+
+
+# ---------------------------------------------------------------------------
+# Dequantization (fp64) ([KVQ] 1.2 and Algorithm 1; [KVARN] method step 5; [BLOG] 4.2)
+# ---------------------------------------------------------------------------
+
+def dequant_block(blk: Block, cfg: Config, cb_k=None, cb_v=None):
+    """(K_hat, V_hat) fp64 [T][D] in the original (un-rotated, pre-RoPE) domain.
+
+    Outlier positions take the stored fp16 value. Reading: the notes zero the
+    dense part and add the sparse value back, which is the same as replacing
+    the dequantized value whenever the dense part decodes to zero; an
+    asymmetric grid cannot represent zero exactly, so replacement is used.
+    """
+    kc = blk.kcodes.astype(np.float64)
+    vc = blk.vcodes.astype(np.float64)
+    mode = cfg.mode
+    if mode in (MODE_RTN, MODE_KVARN):
+        ks, km = (a.astype(np.float64) for a in blk.kstat)
+        vs, vm = (a.astype(np.float64) for a in blk.vstat)
+        kh = kc * ks[None, :] + km[None, :]
+        vh = vc * vs[:, None] + vm[:, None]
+        if mode == MODE_KVARN:
+            kh = kh * blk.ks1.astype(np.float64)[:, None]
+            vh = vh * blk.vs1.astype(np.float64)[None, :]
+            return hadamard_rotate(kh), hadamard_rotate(vh)
+    elif mode == MODE_NUQ:
+        kz, khh = (a.astype(np.float64) for a in blk.kstat)
+        vz, vhh = (a.astype(np.float64) for a in blk.vstat)
+        Ck = np.asarray(cb_k, np.float32).astype(np.float64)
+        Cv = np.asarray(cb_v, np.float32).astype(np.float64)
+        kh = Ck[blk.kcodes] * khh[None, :] + kz[None, :]
+        vh = Cv[blk.vcodes] * vhh[:, None] + vz[:, None]
+    elif mode == MODE_SYM_INT4:
+        ks = blk.kstat[0].astype(np.float64)
+        vs = blk.vstat[0].astype(np.float64)
+        kh = (kc - 8.0) * ks[None, :]
+        vh = (vc - 8.0) * vs[None, :]
+    else:
+        raise ValueError(mode)
+    if blk.kmask is not None:
+        kh = np.where(blk.kmask, blk.kout.astype(np.float64), kh)
+        vh = np.where(blk.vmask, blk.vout.astype(np.float64), vh)
+    return kh, vh
+
+
+# ---------------------------------------------------------------------------
+# Packing and the per-block record layout
+# ---------------------------------------------------------------------------
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack rows of 128 codes into 16*bits bytes each.
+
+    4-bit: byte j holds element 2j in its low nibble and 2j+1 in its high one.
+    2-bit: byte j holds element 4j+i at bits 2i.
+    3-bit: the low two bits of every element packed as 2-bit (32 bytes), then
+    bit 2 of every element, byte j bit i = element 8j+i (16 bytes): 48 bytes
+    per 128 codes ([KVQ] 9.3 counts 384 bits = 48 bytes).
+    """
+    c = np.asarray(codes, np.uint8)
+    rows = c.reshape(-1, 128)
+    if bits == 4:
+        out = rows[:, 0::2] | (rows[:, 1::2] << 4)
+    elif bits == 2:
+        r = rows.reshape(-1, 32, 4)
+        out = r[:, :, 0] | (r[:, :, 1] << 2) | (r[:, :, 2] << 4) | (r[:, :, 3] << 6)
+    elif bits == 3:
+        lo = pack_codes(rows & 3, 2)
+        hb = ((rows >> 2) & 1).reshape(-1, 16, 8)
+        hi = np.zeros((rows.shape[0], 16), np.uint8)
+        for i in range(8):
+            hi |= (hb[:, :, i] << i).astype(np.uint8)
+        out = np.concatenate([lo, hi], axis=1)
+    else:
+        raise ValueError(bits)
+    return out.astype(np.uint8).reshape(c.shape[:-1] + (16 * bits,))
+
+
+def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
+    p = np.asarray(packed, np.uint8)
+    rows = p.reshape(-1, 16 * bits)
+    if bits == 4:
+        out = np.empty((rows.shape[0], 128), np.uint8)
+        out[:, 0::2] = rows & 15
+        out[:, 1::2] = rows >> 4
+    elif bits == 2:
+        out = np.stack([(rows >> (2 * i)) & 3 for i in range(4)], axis=2).reshape(-1, 128)
+    elif bits == 3:
+        lo = unpack_codes(rows[:, :32], 2)
+        hi = np.stack([(rows[:, 32:] >> i) & 1 for i in range(8)], axis=2).reshape(-1, 128)
+        out = lo | (hi << 2)
+    else:
+        raise ValueError(bits)
+    return out.astype(np.uint8).reshape(p.shape[:-1] + (128,))
+
+
+def _align(x: int, a: int) -> int:
+    return (x + a - 1) // a * a
+
+
+def record_layout(mode: int, bits: int, k_out: int) -> tuple[dict, int]:
+    """Byte offsets of the segments of one block record and its padded size.
+
+    Order: key codes (128 token rows), value codes (128 channel rows), key
+    statistics, value statistics, [KVARN: key s1 per token, value s1 per
+    channel], [outliers: key CSR (values fp16, row pointers u16[129], channel
+    u8), value CSC (values fp16, column pointers u16[129], token u8)]. Each
+    segment starts on a 16-byte boundary; the record is padded to 256 bytes.
+    """
+    R = 16 * bits
+    stat = 256 if mode == MODE_SYM_INT4 else 1024
+    segs = [("kc", T * R), ("vc", D * R), ("ks", stat), ("vs", stat)]
+    if mode == MODE_KVARN:
+        segs += [("k1", 4 * T), ("v1", 4 * D)]
+    if k_out > 0:
+        n = 128 * k_out
+        for p in ("ko", "vo"):
+            segs += [(p + "_val", 2 * n), (p + "_ptr", 2 * 129), (p + "_idx", n)]
+    off, pos = {}, 0
+    for name, size in segs:
+        pos = _align(pos, 16)
+        off[name] = (pos, size)
+        pos += size
+    return off, _align(pos, 256)
+
+
+def record_payload_bytes(mode: int, bits: int, k_out: int) -> int:
+    """Bytes of a record that carry data (segment sizes without padding)."""
+    off, _ = record_layout(mode, bits, k_out)
+    return sum(size for _, size in off.values())
+
+
+def serialize_block(blk: Block, cfg: Config) -> np.ndarray:
+    """The block record as bytes, in the layout of ``record_layout``."""
+    off, size = record_layout(cfg.mode, cfg.bits, cfg.outliers_per_vec)
+    buf = np.zeros(size, np.uint8)
+
+    def put(name, arr):
+        o, n = off[name]
+        raw = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
+        assert raw.size == n, (name, raw.size, n)
+        buf[o:o + n] = raw
+
+    put("kc", pack_codes(blk.kcodes, cfg.bits))             # token-major rows
+    put("vc", pack_codes(blk.vcodes.T, cfg.bits))           # channel-major rows
+    if cfg.mode == MODE_SYM_INT4:
+        put("ks", blk.kstat[0].astype(np.float16))
+        put("vs", blk.vstat[0].astype(np.float16))
+    else:
+        put("ks", np.concatenate([a.astype(np.float32) for a in blk.kstat]))
+        put("vs", np.concatenate([a.astype(np.float32) for a in blk.vstat]))
+    if cfg.mode == MODE_KVARN:
+        put("k1", blk.ks1.astype(np.float32))
+        put("v1", blk.vs1.astype(np.float32))
+    if cfg.outliers_per_vec > 0:
+        # keys: CSR by token row, entries sorted by (token, channel) [KVQ] 3.4
+        t_idx, c_idx = np.nonzero(blk.kmask)
+        put("ko_val", blk.kout[t_idx, c_idx].astype(np.float16))
+        put("ko_ptr", np.concatenate([[0], np.cumsum(blk.kmask.sum(axis=1))]).astype(np.uint16))
+        put("ko_idx", c_idx.astype(np.uint8))
+        # values: CSC by channel column, entries sorted by (channel, token) [KVQ] 3.4
+        c2, t2 = np.nonzero(blk.vmask.T)
+        put("vo_val", blk.vout[t2, c2].astype(np.float16))
+        put("vo_ptr", np.concatenate([[0], np.cumsum(blk.vmask.sum(axis=0))]).astype(np.uint16))
+        put("vo_idx", t2.astype(np.uint8))
+    return buf
+
+
+# ---------------------------------------------------------------------------
+# RoPE ([KVQ] 1.3 and 3.2) and attention ([KVQ] Algorithm 1 attention part)
+# ---------------------------------------------------------------------------
+
+def rope_angles(positions: np.ndarray, theta: float = 10000.0) -> np.ndarray:
+    """Angle n * theta_i with theta_i = theta^(-2i/128), i = 0..63 (fp64) -> [n][64]."""
+    i = np.arange(D // 2, dtype=np.float64)
+    th = theta ** (-2.0 * i / D)
+    return np.asarray(positions, np.float64)[:, None] * th[None, :]
+
+
+def rope_rotate(x: np.ndarray, positions: np.ndarray, theta: float = 10000.0) -> np.ndarray:
+    """Rotate channel pairs (2i, 2i+1) of each row by its position's angle (fp64)."""
+    x = np.asarray(x, np.float64)
+    a = rope_angles(positions, theta)
+    c, s = np.cos(a), np.sin(a)
+    out = np.empty_like(x)
+    out[:, 0::2] = x[:, 0::2] * c - x[:, 1::2] * s
+    out[:, 1::2] = x[:, 0::2] * s + x[:, 1::2] * c
+    return out
+
+
+def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(scale * K q) weighted sum of V rows, dense fp64."""
+    s = (np.asarray(k, np.float64) @ np.asarray(q, np.float64)) * scale
+    p = np.exp(s - s.max())
+    return (p @ np.asarray(v, np.float64)) / p.sum()
+
+
+def error_decomposition(k: np.ndarray, kdq: np.ndarray):
+    """||K - K_dq||^2 split into a magnitude part and a direction part ([KVARN] core method).
+
+    E_M = (||K|| - ||K_dq||)^2, E_D = 2 ||K|| ||K_dq|| (1 - cos angle).
+    """
+    k = np.asarray(k, np.float64).ravel()
+    d = np.asarray(kdq, np.float64).ravel()
+    nk, nd = np.linalg.norm(k), np.linalg.norm(d)
+    cos = float(k @ d) / (nk * nd) if nk > 0 and nd > 0 else 1.0
+    return (nk - nd) ** 2, 2.0 * nk * nd * (1.0 - cos)
+
+
+# ---------------------------------------------------------------------------
+# The cache: append with a fp16 tail, decode over everything
+# ---------------------------------------------------------------------------
+
+class OracleCache:
+    """Per layer and (batch row, kv head): a list of quantized blocks plus a fp16 tail.
+
+    Append semantics: tokens fill positions in order; every time 128 tokens of
+    a sequence have accumulated they are quantized as one block; the remaining
+    (< 128) most recent tokens stay in fp16 ([BLOG] 5.2: the last partial block
+    takes a separate fp16 path). Decode attends to every cached token.
+    """
+
+    def __init__(self, cfg: Config):
+        self.cfg = cfg
+        self.len = [0] * cfg.n_layers
+        nb = cfg.batch * cfg.n_kv_heads
+        self.blocks = [[[] for _ in range(nb)] for _ in range(cfg.n_layers)]
+        self.tail_k = [[np.zeros((0, D), np.float16) for _ in range(nb)] for _ in range(cfg.n_layers)]
+        self.tail_v = [[np.zeros((0, D), np.float16) for _ in range(nb)] for _ in range(cfg.n_layers)]
+        self.codebooks = {}
+
+    def load_codebook(self, layer: int, kv_head: int, which: int, cb: np.ndarray):
+        self.codebooks[(layer, kv_head, which)] = np.asarray(cb, np.float32)
+
+    def _unit(self, b: int, h: int) -> int:
+        return b * self.cfg.n_kv_heads + h
+
+    def append(self, layer: int, k16: np.ndarray, v16: np.ndarray):
+        """k16, v16: fp16 [B][Hkv][n_new][128]."""
+        cfg = self.cfg
+        n_new = k16.shape[2]
+        assert self.len[layer] + n_new <= cfg.max_tokens
+        for b in range(cfg.batch):
+            for h in range(cfg.n_kv_heads):
+                u = self._unit(b, h)
+                tk = np.concatenate([self.tail_k[layer][u], k16[b, h]])
+                tv = np.concatenate([self.tail_v[layer][u], v16[b, h]])
+                nfull = tk.shape[0] // T
+                cbk = self.codebooks.get((layer, h, 0))
+                cbv = self.codebooks.get((layer, h, 1))
+                for j in range(nfull):
+                    self.blocks[layer][u].append(
+                        quantize_block(tk[j * T:(j + 1) * T], tv[j * T:(j + 1) * T], cfg, cbk, cbv))
+                self.tail_k[layer][u] = tk[nfull * T:].copy()
+                self.tail_v[layer][u] = tv[nfull * T:].copy()
+        self.len[layer] += n_new
+
+    def dequantized(self, layer: int, b: int, h: int):
+        """(K_hat, V_hat) fp64 [L][128] of one sequence/kv-head, keys pre-RoPE."""
+        u = self._unit(b, h)
+        cbk = self.codebooks.get((layer, h, 0))
+        cbv = self.codebooks.get((layer, h, 1))
+        ks, vs = [], []
+        for blk in self.blocks[layer][u]:
+            kh, vh = dequant_block(blk, self.cfg, cbk, cbv)
+            ks.append(kh)
+            vs.append(vh)
+        ks.append(self.tail_k[layer][u].astype(np.float64))
+        vs.append(self.tail_v[layer][u].astype(np.float64))
+        return np.concatenate(ks), np.concatenate(vs)
+
+    def decode(self, layer: int, q16: np.ndarray, scale: float = 0.0, heads=None) -> np.ndarray:
+        """q16 fp16 [B][Hq][128] (already rotated by its own position). Returns fp64 out.
+
+        Query head h reads kv head h // (Hq / Hkv). Scores are scale * q . RoPE(k_n, n)
+        with n the absolute position; scale = 1/sqrt(128) unless given.
+        """
+        cfg = self.cfg
+        if scale <= 0:
+            scale = 1.0 / math.sqrt(D)
+        out = np.zeros((cfg.batch, cfg.n_q_heads, D))
+        sel = heads if heads is not None else [(b, h) for b in range(cfg.batch) for h in range(cfg.n_q_heads)]
+        cache = {}
+        for b, h in sel:
+            kvh = h // cfg.group
+            if (b, kvh) not in cache:
+                kh, vh = self.dequantized(layer, b, kvh)
+                if cfg.pre_rope:
+                    kh = rope_rotate(kh, np.arange(kh.shape[0]), cfg.rope_theta)
+                cache = {(b, kvh): (kh, vh)}
+            kh, vh = cache[(b, kvh)]
+            out[b, h] = softmax_attention(q16[b, h].astype(np.float64), kh, vh, scale)
+        return out
+
+
+__all__ = [name for name in dir() if not name.startswith("_")]

@@ -1,0 +1,507 @@
+"""Pins of the CPU oracle against what the pages print and what mathematics fixes.
+
+Each test checks the oracle by a route other than its own formula: printed
+values from the pages (tests/golden/*.json, each citing its passage), closed
+forms, invariants, brute force on small inputs, an independent recursive
+Walsh-Hadamard butterfly, torch CPU for the blog's int4 semantics, and
+pure-Python loops for tiny attention problems.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvq_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------- P1
+def test_kv_size_formula_matches_printed_tables():
+    g = golden("kv_size.json")
+    for row in g["kvquant_gib"]:
+        b = O.kv_cache_bytes(row["layers"], row["heads"], row["head_dim"], row["bits"] / 8,
+                             row["batch"], row["seq"])
+        assert b / 2**30 == pytest.approx(row["printed"], rel=row["rel_tol"]), row
+    for row in g["blog_gb"]:
+        b = O.kv_cache_bytes(row["layers"], row["kv_heads"], row["head_dim"], 2, row["batch"], row["seq"])
+        assert round(b / 1e9, 1) == row["printed"], row
+
+
+# --------------------------------------------------------------------------- P11
+def test_bit_and_byte_accounting():
+    g = golden("bit_accounting.json")
+    ds = g["dense_sparse_bits"]
+    assert round(O.dense_sparse_avg_bits(ds["bits"], ds["fraction"]), 2) == ds["printed"]
+    row = O.pack_codes(np.zeros(128, np.uint8), 3)
+    assert row.size == g["row_bytes_3bit"]
+    assert round(256 / row.size, 1) == g["ratio_3bit"]
+    # one fp16 outlier per 128-vector: value (2 B) + channel index (1 B) + share of a
+    # u16 row pointer (2 B) -> 48 + 2 + 1 + 2 = 53 B in this layout; the page's ~52 B
+    # counts 1.28 outliers at 2 B + index overhead. Both give 4.8-4.9x.
+    assert round(256 / g["row_bytes_3bit_with_outliers"], 1) == g["ratio_3bit_with_outliers"]
+    bpe = O.block_scale_bits(4, 128, 16)
+    assert bpe == g["blog_bits_per_element"]
+    assert g["blog_fp16_gb"] * bpe / 16 == pytest.approx(g["blog_4bit_gb_printed"], rel=g["blog_4bit_gb_rel_tol"])
+    # payload of the record layout: C1 (4-bit, no outliers) = 144 B per token.kv-head
+    assert O.record_payload_bytes(O.MODE_RTN, 4, 0) == 144 * 128
+
+
+# --------------------------------------------------------------------------- P2
+def test_per_token_vs_per_channel_scale_example():
+    g = golden("scales_and_rope.json")
+    r = rng(1)
+    K = r.uniform(-1, 1, size=(2048, 128)).astype(np.float32)
+    K[0, :] = np.clip(K[0, :], -1, 1)
+    K[:, 5] = r.uniform(-15, 15, size=2048).astype(np.float32)
+    K[0, 5], K[1, 5] = 15.0, -15.0
+    K[0, 6], K[1, 6] = 1.0, -1.0   # every normal channel spans exactly [-1, 1]
+    K[:, 6] = np.clip(K[:, 6], -1, 1)
+    keep = np.ones_like(K, bool)
+    s_c, m_c = O.rtn_stats(K, keep, 3, axis=0)
+    # the page prints about 4.3 and 0.29: compare at the printed number of digits
+    assert round(float(s_c[5]), 1) == g["per_token_scale_3bit"]
+    assert round(float(s_c[6]), 2) == g["per_channel_scale_3bit"]
+    # per token: a row holding +15 and -15 gets s = 30/7, and every |x| <= 1 entry of that
+    # row lands in one of the two middle bins (the page's "same bin" failure mode)
+    row = np.concatenate([[15.0, -15.0], r.uniform(-1, 1, 126)]).astype(np.float32)[None, :]
+    s_t, m_t = O.rtn_stats(row, np.ones_like(row, bool), 3, axis=1)
+    assert s_t[0] == pytest.approx(30 / 7, rel=1e-6)
+    q = O.rtn_codes(row, s_t[:, None], m_t[:, None], 3)
+    assert set(np.unique(q[0, 2:])) <= {3, 4}
+    # per channel the same small entries spread over all 8 levels
+    qc = O.rtn_codes(K[:, 6:7], s_c[None, 6:7], m_c[None, 6:7], 3)
+    assert len(np.unique(qc)) == 8
+
+
+# --------------------------------------------------------------------------- P3
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("k_out", [0, 1, 2])
+def test_rtn_error_bound_and_endpoints(bits, k_out):
+    r = rng(bits * 10 + k_out)
+    k16 = (r.standard_normal((128, 128)) * r.uniform(0.1, 20, 128)[None, :]).astype(np.float16)
+    v16 = (r.standard_normal((128, 128)) * r.lognormal(0, 0.5, 128)[:, None]).astype(np.float16)
+    cfg = O.Config(1, 1, 1, 1, 128, O.MODE_RTN, bits, outliers_per_vec=k_out)
+    blk = O.quantize_block(k16, v16, cfg)
+    kh, vh = O.dequant_block(blk, cfg)
+    for x16, xh, (s, m), axis, mask in ((k16, kh, blk.kstat, 0, blk.kmask), (v16, vh, blk.vstat, 1, blk.vmask)):
+        x = x16.astype(np.float64)
+        sb = np.expand_dims(s.astype(np.float64), axis)
+        mb = np.expand_dims(m.astype(np.float64), axis)
+        keep = np.ones_like(x, bool) if mask is None else ~mask
+        slack = 4 * np.finfo(np.float32).eps * (np.abs(mb) + sb * (2**bits))
+        err = np.abs(x - xh)
+        assert np.all((err <= sb / 2 + slack)[keep])
+        if mask is not None:
+            assert np.all(xh[mask] == x[mask])            # outliers reproduced exactly
+            assert mask.sum() == 128 * k_out
+        lo = np.where(keep, x, np.inf).min(axis=axis)
+        hi = np.where(keep, x, -np.inf).max(axis=axis)
+        assert np.all(lo == m)
+        codes = blk.kcodes if axis == 0 else blk.vcodes
+        at_min = (x == np.expand_dims(lo, axis)) & keep
+        at_max = (x == np.expand_dims(hi, axis)) & keep & (sb > 0)
+        assert np.all(codes[at_min] == 0)
+        assert np.all(codes[at_max] == 2**bits - 1)
+
+
+def test_rtn_degenerate_vector_gives_code_zero():
+    x = np.full((128, 1), 0.75, np.float32)
+    s, m = O.rtn_stats(x, np.ones_like(x, bool), 4, axis=0)
+    assert s[0] == 0 and m[0] == np.float32(0.75)
+    assert np.all(O.rtn_codes(x, s[None], m[None], 4) == 0)
+
+
+# --------------------------------------------------------------------------- P4
+def test_nuq_worked_example_from_the_notes():
+    g = golden("nuq_worked_example.json")
+    C = np.array(g["codebook"], np.float32)
+    for case in g["cases"]:
+        x = np.array([case["x"]], np.float32)
+        z = np.array([case["z"]], np.float32)
+        h = np.array([case["h"]], np.float32)
+        u = O.nuq_normalise(x, z, h)
+        assert u[0] == pytest.approx(case["u"], abs=1e-3)
+        assert O.nuq_codes(x, z, h, C)[0] == case["code"]
+    # the notes' outlier (9.3 above its threshold) is the largest |x| of its vector,
+    # so a top-1 per-vector split selects it
+    vec = np.array([0.45, -0.03, 9.3] + [0.2] * 125, np.float16)[None, :]
+    mask = O.outlier_mask(vec, 1, axis=1)
+    assert mask[0, 2] and mask.sum() == 1
+    assert g["outlier"]["x"] > g["outlier"]["tau"]
+
+
+# --------------------------------------------------------------------------- P5
+def _all_finite_f16():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x = bits.view(np.float16)
+    return x[np.isfinite(x)].astype(np.float32)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_nuq_argmin_against_midpoint_search(bits):
+    """Brute force over every finite fp16 input: the argmin equals the index found by
+    searching the codebook's fp64 midpoints, except within 1e-6 of a midpoint."""
+    r = rng(100 + bits)
+    C = np.sort(r.uniform(-1, 1, 1 << bits)).astype(np.float32)
+    C[0], C[-1] = -1, 1
+    x = _all_finite_f16()
+    z = np.float32(0.3)
+    h = np.float32(2.75)
+    q = O.nuq_codes(x, z, h, C)
+    u = O.nuq_normalise(x, z, h).astype(np.float64)
+    mids = (C[:-1].astype(np.float64) + C[1:].astype(np.float64)) / 2
+    ref = np.searchsorted(mids, u, side="left")
+    near = np.min(np.abs(u[:, None] - mids[None, :]), axis=1) < 1e-6
+    assert np.all(q[~near] == ref[~near])
+    assert near.mean() < 0.01
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_nuq_with_uniform_codebook_reduces_to_rtn(bits):
+    r = rng(7 + bits)
+    n = 1 << bits
+    C = (-1 + 2 * np.arange(n) / (n - 1)).astype(np.float32)
+    x = (r.standard_normal((128, 64)) * 3).astype(np.float16).astype(np.float32)
+    keep = np.ones_like(x, bool)
+    z, h = O.nuq_stats(x, keep, axis=0)
+    s, m = O.rtn_stats(x, keep, bits, axis=0)
+    qn = O.nuq_codes(x, z[None], h[None], C)
+    qr = O.rtn_codes(x, s[None], m[None], bits)
+    pos = (x.astype(np.float64) - m[None]) / s[None]
+    near_tie = np.abs(pos - np.floor(pos) - 0.5) < 1e-4
+    assert np.all(qn[~near_tie] == qr[~near_tie])
+
+
+# --------------------------------------------------------------------------- P6
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_outlier_selection_against_full_sort(k):
+    r = rng(40 + k)
+    x = r.standard_normal((128, 128)).astype(np.float16)
+    x[3, 9] = x[77, 9] = np.float16(-9.0)          # a tie in magnitude within a channel
+    x[12, 9] = np.float16(9.0)
+    for axis in (0, 1):
+        mask = O.outlier_mask(x, k, axis)
+        assert mask.sum() == 128 * k
+        for j in range(128):
+            vec = x[:, j] if axis == 0 else x[j, :]
+            order = sorted(range(128), key=lambda i: (-abs(float(vec[i])), i))
+            expect = set(order[:k])
+            got = set(np.nonzero(mask[:, j] if axis == 0 else mask[j, :])[0])
+            assert got == expect
+
+
+# --------------------------------------------------------------------------- P7
+def test_rope_properties_and_variance_example():
+    r = rng(5)
+    k = r.standard_normal((6, 128))
+    q = r.standard_normal(128)
+    pos = np.array([0, 1, 7, 128, 4097, 1 << 20])
+    kr = O.rope_rotate(k, pos)
+    assert np.allclose(np.linalg.norm(kr, axis=1), np.linalg.norm(k, axis=1), rtol=1e-12)
+    assert np.allclose(kr[0], k[0], atol=0)                         # R_0 = I
+    for m, n in ((3, 10), (100, 5000), (1 << 19, (1 << 20) - 1)):
+        lhs = O.rope_rotate(q[None], [m])[0] @ O.rope_rotate(k[:1], [n])[0]
+        rhs = q @ O.rope_rotate(k[:1], [n - m])[0]
+        assert lhs == pytest.approx(rhs, rel=1e-9, abs=1e-9)
+    # pair (2i, 2i+1) rotated by n*theta_i, theta_i = 10000^(-2i/128): check one pair by hand
+    n, i = 5, 3
+    a = n * 10000 ** (-2 * i / 128)
+    e = np.zeros((1, 128)); e[0, 2 * i] = 1.0
+    got = O.rope_rotate(e, [n])[0]
+    assert got[2 * i] == pytest.approx(math.cos(a)) and got[2 * i + 1] == pytest.approx(math.sin(a))
+    g = golden("scales_and_rope.json")["rope_variance"]
+    x = np.zeros((200000, 128)); x[:, 0] = g["k0"]; x[:, 1] = g["k1"]
+    ch0 = O.rope_rotate(x, np.arange(x.shape[0]))[:, 0]
+    assert np.mean(ch0 ** 2) == pytest.approx(g["variance"], rel=2e-3)
+    assert math.sqrt(np.mean(ch0 ** 2)) == pytest.approx(g["std"], abs=g["std_abs_tol"])
+
+
+# --------------------------------------------------------------------------- P8
+def _fwht_recursive(x):
+    """Unnormalised Walsh-Hadamard transform by the recursive butterfly (natural order)."""
+    x = list(x)
+    n = len(x)
+    if n == 1:
+        return x
+    a = _fwht_recursive(x[: n // 2])
+    b = _fwht_recursive(x[n // 2:])
+    return [p + q for p, q in zip(a, b)] + [p - q for p, q in zip(a, b)]
+
+
+def test_hadamard_closed_forms():
+    H = O.sylvester_hadamard(128)
+    assert np.array_equal(H @ H.T, 128 * np.eye(128, dtype=np.int64))
+    assert np.array_equal(H, H.T)
+    r = rng(9)
+    x = r.standard_normal((3, 128))
+    y = O.hadamard_rotate(x)
+    for i in range(3):
+        assert np.allclose(y[i], np.array(_fwht_recursive(x[i])) / math.sqrt(128), atol=1e-12)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
+    assert np.allclose(O.hadamard_rotate(y), x, atol=1e-12)
+
+
+def test_varn_invariants():
+    r = rng(11)
+    y = r.standard_normal((128, 128)) * r.lognormal(0, 1, 128)[None, :] * r.lognormal(0, 1, 128)[:, None]
+    rr, cc = O.varn(y, 8)
+    xt = y * np.exp(-rr[:, None] - cc[None, :])
+    assert np.allclose(xt.std(axis=1), 1.0, atol=1e-12)                     # last step: rows
+    assert np.allclose(np.exp(rr)[:, None] * xt * np.exp(cc)[None, :], y, rtol=1e-12)
+    col_disp = [np.std(np.log((y * np.exp(-O.varn(y, it)[0][:, None] - O.varn(y, it)[1][None, :])).std(axis=0)))
+                for it in (1, 2, 8)]
+    assert col_disp[0] >= col_disp[1] >= col_disp[2]
+    assert col_disp[2] < 0.05 * np.std(np.log(y.std(axis=0)))
+    gamma = r.lognormal(0, 1, 128)
+    rr2, cc2 = O.varn(y * gamma[None, :], 8)
+    assert np.allclose(rr2, rr, atol=1e-9)
+    assert np.allclose(cc2 - cc, np.log(gamma), atol=1e-9)
+
+
+def test_varn_zero_std_leaves_scale_unchanged():
+    y = np.ones((128, 128))
+    rr, cc = O.varn(y, 8)
+    assert np.all(rr == 0) and np.all(cc == 0)
+
+
+# --------------------------------------------------------------------------- P9
+def test_kvarn_dequant_identity_and_bound():
+    r = rng(12)
+    k16 = (r.standard_normal((128, 128)) + np.where(np.arange(128) % 37 == 0, 12.0, 0.0)[None, :]).astype(np.float16)
+    v16 = (r.standard_normal((128, 128)) * r.lognormal(0, 0.5, 128)[:, None]).astype(np.float16)
+    cfg = O.Config(1, 1, 1, 1, 128, O.MODE_KVARN, 2, varn_iters=8)
+    blk = O.quantize_block(k16, v16, cfg)
+    s, m = (a.astype(np.float64) for a in blk.kstat)
+    s1 = blk.ks1.astype(np.float64)
+    q = blk.kcodes.astype(np.float64)
+    z = m / s
+    a = (q + z[None, :]) * s[None, :] * s1[:, None]
+    b = (q * s[None, :] + m[None, :]) * s1[:, None]
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+    # the rotated domain error is at most half a level: |y - y_hat| <= s_RTN * s1 / 2
+    y = O.hadamard_rotate(k16.astype(np.float64))
+    bound = s[None, :] * s1[:, None] / 2 * (1 + 1e-5) + 1e-6
+    assert np.all(np.abs(y - b) <= bound)
+    kh, vh = O.dequant_block(blk, cfg)
+    assert np.allclose(O.hadamard_rotate(kh), b, atol=1e-9)       # original domain = H * rotated / sqrt(128)
+    # V: s1 per channel, s_RTN per token
+    vs, vm = (a.astype(np.float64) for a in blk.vstat)
+    yv = O.hadamard_rotate(v16.astype(np.float64))
+    bv = (blk.vcodes * vs[:, None] + vm[:, None]) * blk.vs1.astype(np.float64)[None, :]
+    assert np.all(np.abs(yv - bv) <= vs[:, None] * blk.vs1[None, :] / 2 * (1 + 1e-5) + 1e-6)
+
+
+# --------------------------------------------------------------------------- P10
+def test_error_decomposition_is_law_of_cosines():
+    r = rng(13)
+    k = r.standard_normal((128, 128))
+    kdq = k + 0.1 * r.standard_normal((128, 128))
+    em, ed = O.error_decomposition(k, kdq)
+    assert em + ed == pytest.approx(float(np.sum((k - kdq) ** 2)), rel=1e-10)
+    em2, ed2 = O.error_decomposition(k, 1.5 * k)
+    assert ed2 == pytest.approx(0.0, abs=1e-9) and em2 == pytest.approx(0.25 * np.sum(k ** 2), rel=1e-12)
+
+
+# --------------------------------------------------------------------------- P12
+def test_symmetric_int4_matches_blog_semantics_in_torch():
+    """The blog's block quantizer (absmax / 7, clamp to [-8, 7], round) written with torch
+    CPU ops on a 128-element sequence block, given the same fp16 scale."""
+    r = rng(14)
+    x16 = (r.standard_normal((128, 128)) * np.array([1.0, 13.0] * 64)[None, :]).astype(np.float16)
+    x = x16.astype(np.float32)
+    keep = np.ones_like(x, bool)
+    s16 = O.sym_scale(x, keep, axis=0)
+    u = O.sym_codes(x, s16[None, :])
+    xt = torch.from_numpy(x)
+    scale_t = (xt.abs().max(dim=0, keepdim=True).values / 7.0).to(torch.float16)
+    assert np.array_equal(scale_t.numpy()[0], s16)
+    qt = (xt / scale_t.float()).clamp(-8, 7).round()
+    assert np.array_equal((qt + 8).to(torch.uint8).numpy(), u)
+    deq = (u.astype(np.float64) - 8) * s16.astype(np.float64)[None, :]
+    assert np.all(np.abs(deq - x) <= s16.astype(np.float64)[None, :] / 2 * (1 + 1e-3) + 1e-7)
+    assert set(np.unique(u[np.abs(x) == np.abs(x).max(axis=0)[None, :]])) <= {1, 15}
+    assert np.all(O.sym_codes(np.zeros((4, 1), np.float32), np.zeros((1, 1), np.float16)) == 8)
+
+
+# --------------------------------------------------------------------------- P13
+def test_packing_byte_patterns_and_round_trip():
+    c4 = np.arange(128) % 16
+    p4 = O.pack_codes(c4, 4)
+    assert list(p4[:8]) == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
+    c2 = np.arange(128) % 4
+    assert list(O.pack_codes(c2, 2)[:2]) == [0b11100100, 0b11100100]
+    c3 = np.arange(128) % 8
+    p3 = O.pack_codes(c3, 3)
+    assert p3.size == 48
+    assert p3[0] == 0b11100100          # low bits of codes 0,1,2,3
+    assert p3[32] == 0b11110000         # bit 2 of codes 0..7
+    r = rng(15)
+    for bits in (2, 3, 4):
+        c = r.integers(0, 1 << bits, size=(37, 128)).astype(np.uint8)
+        assert np.array_equal(O.unpack_codes(O.pack_codes(c, bits), bits), c)
+
+
+def test_record_layout_sizes():
+    assert O.record_layout(O.MODE_RTN, 4, 0)[1] == 18432
+    assert O.record_layout(O.MODE_KVARN, 2, 0)[1] == 11264
+    assert O.record_layout(O.MODE_SYM_INT4, 4, 0)[1] == 16896
+    off, size = O.record_layout(O.MODE_NUQ, 3, 1)
+    spans = sorted(off.values())
+    for (a, n), (b, _) in zip(spans, spans[1:]):
+        assert a + n <= b and b % 16 == 0
+    assert size % 256 == 0
+
+
+def test_serialized_record_reads_back():
+    r = rng(16)
+    cfg = O.Config(1, 1, 1, 1, 128, O.MODE_RTN, 3, outliers_per_vec=1)
+    k16 = r.standard_normal((128, 128)).astype(np.float16)
+    v16 = r.standard_normal((128, 128)).astype(np.float16)
+    blk = O.quantize_block(k16, v16, cfg)
+    buf = O.serialize_block(blk, cfg)
+    off, _ = O.record_layout(cfg.mode, 3, 1)
+    o, n = off["kc"]
+    kc = O.unpack_codes(buf[o:o + n].reshape(128, 48), 3)
+    assert np.array_equal(kc, blk.kcodes)
+    o, n = off["vc"]
+    vc = O.unpack_codes(buf[o:o + n].reshape(128, 48), 3)
+    assert np.array_equal(vc.T, blk.vcodes)
+    o, n = off["ko_ptr"]
+    ptr = buf[o:o + n].view(np.uint16)
+    o, n = off["ko_idx"]
+    col = buf[o:o + n]
+    o, n = off["ko_val"]
+    val = buf[o:o + n].view(np.float16)
+    for t in range(128):
+        for e in range(ptr[t], ptr[t + 1]):
+            assert blk.kmask[t, col[e]] and val[e] == k16[t, col[e]]
+    assert ptr[128] == 128
+
+
+# --------------------------------------------------------------------------- P14
+def _attention_loops(q, K, V, scale):
+    s = [scale * sum(qi * ki for qi, ki in zip(q, k)) for k in K]
+    m = max(s)
+    p = [math.exp(x - m) for x in s]
+    z = sum(p)
+    return [sum(p[t] * V[t][c] for t in range(len(K))) / z for c in range(len(q))]
+
+
+def test_attention_small_cases():
+    r = rng(17)
+    for L in (1, 2, 5, 8):
+        q = r.standard_normal(8)
+        K = r.standard_normal((L, 8))
+        V = r.standard_normal((L, 8))
+        got = O.softmax_attention(q, K, V, 0.3)
+        ref = _attention_loops(q.tolist(), K.tolist(), V.tolist(), 0.3)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    V = r.standard_normal((6, 128))
+    assert np.array_equal(O.softmax_attention(r.standard_normal(128), V[:1] * 0 + 1, V[:1], 0.1), V[0])
+    K = np.tile(r.standard_normal((1, 128)), (6, 1))
+    assert np.allclose(O.softmax_attention(r.standard_normal(128), K, V, 0.1), V.mean(axis=0), atol=1e-12)
+    assert np.allclose(O.softmax_attention(np.zeros(128), r.standard_normal((6, 128)), V, 0.1), V.mean(axis=0))
+
+
+def test_split_merge_equals_single_pass():
+    r = rng(18)
+    q = r.standard_normal(128)
+    K = r.standard_normal((300, 128)) * 3
+    V = r.standard_normal((300, 128))
+    full = O.softmax_attention(q, K, V, 1 / math.sqrt(128))
+    parts = []
+    for lo, hi in ((0, 97), (97, 256), (256, 300)):
+        s = K[lo:hi] @ q / math.sqrt(128)
+        m = s.max()
+        p = np.exp(s - m)
+        parts.append((m, p.sum(), p @ V[lo:hi]))
+    M = max(p[0] for p in parts)
+    num = sum(np.exp(m - M) * o for m, _, o in parts)
+    den = sum(np.exp(m - M) * l for m, l, _ in parts)
+    assert np.allclose(num / den, full, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- cache semantics
+@pytest.mark.parametrize("mode,bits,k_out,pre_rope", [
+    (O.MODE_RTN, 4, 0, 0), (O.MODE_NUQ, 3, 1, 1), (O.MODE_SYM_INT4, 4, 0, 0), (O.MODE_KVARN, 2, 0, 0)])
+def test_append_in_chunks_equals_append_at_once(mode, bits, k_out, pre_rope):
+    r = rng(19)
+    cfg = O.Config(1, 2, 2, 4, 512, mode, bits, outliers_per_vec=k_out, pre_rope=pre_rope, varn_iters=3)
+    L = 300
+    k = r.standard_normal((2, 2, L, 128)).astype(np.float16)
+    v = r.standard_normal((2, 2, L, 128)).astype(np.float16)
+    caches = []
+    for chunks in ([L], [1, 127, 128, 44], [129, 171]):
+        c = O.OracleCache(cfg)
+        for h in range(2):
+            for w in (0, 1):
+                c.load_codebook(0, h, w, np.linspace(-1, 1, 1 << bits).astype(np.float32))
+        pos = 0
+        for n in chunks:
+            c.append(0, k[:, :, pos:pos + n], v[:, :, pos:pos + n])
+            pos += n
+        caches.append(c)
+    q = r.standard_normal((2, 4, 128)).astype(np.float16)
+    outs = [c.decode(0, q) for c in caches]
+    for c in caches[1:]:
+        assert c.len[0] == L
+        for u in range(4):
+            assert len(c.blocks[0][u]) == 2
+            for b0, b1 in zip(caches[0].blocks[0][u], c.blocks[0][u]):
+                assert np.array_equal(O.serialize_block(b0, cfg), O.serialize_block(b1, cfg))
+            assert np.array_equal(c.tail_k[0][u], caches[0].tail_k[0][u])
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_decode_single_token_returns_its_value():
+    cfg = O.Config(1, 1, 1, 2, 256, O.MODE_RTN, 4, pre_rope=1)
+    r = rng(20)
+    c = O.OracleCache(cfg)
+    k = r.standard_normal((1, 1, 1, 128)).astype(np.float16)
+    v = r.standard_normal((1, 1, 1, 128)).astype(np.float16)
+    c.append(0, k, v)
+    out = c.decode(0, r.standard_normal((1, 2, 128)).astype(np.float16))
+    assert np.array_equal(out[0, 0], v[0, 0, 0].astype(np.float64))
+    assert np.array_equal(out[0, 1], v[0, 0, 0].astype(np.float64))
+
+
+def test_quantized_attention_close_to_fp16_attention():
+    """End to end sanity: 4-bit per-channel keys / per-token values keep the attention
+    output close to unquantized attention on the C1-like generator structure."""
+    r = rng(21)
+    cfg = O.Config(1, 1, 1, 1, 2048, O.MODE_RTN, 4)
+    k = r.standard_normal((1, 1, 2048, 128))
+    k[..., 7] += 12
+    k = k.astype(np.float16)
+    v = r.standard_normal((1, 1, 2048, 128)).astype(np.float16)
+    c = O.OracleCache(cfg)
+    c.append(0, k, v)
+    q = r.standard_normal((1, 1, 128)).astype(np.float16)
+    out = c.decode(0, q)[0, 0]
+    ref = O.softmax_attention(q[0, 0].astype(np.float64), k[0, 0].astype(np.float64),
+                              v[0, 0].astype(np.float64), 1 / math.sqrt(128))
+    assert np.max(np.abs(out - ref)) < 0.05 * np.max(np.abs(ref)) + 0.02
+
+
+def test_nuq_exact_tie_takes_the_smaller_index():
+    """u exactly halfway between two entries (reading: ties go to the smaller index)."""
+    C = np.array([-1.0, -0.5, 0.5, 1.0], np.float32)
+    x = np.array([0.25, 0.25 + 0.5 * 2.0, 0.25 - 0.75 * 2.0], np.float32)  # u = 0, 0.5 -> 0.5 exact, -0.75
+    q = O.nuq_codes(x, np.float32(0.25), np.float32(2.0), C)
+    assert q[0] == 1            # |0 - (-0.5)| == |0 - 0.5|
+    assert q[1] == 2            # exactly on an entry
+    assert q[2] == 0            # |-0.75 - (-1)| == |-0.75 - (-0.5)|
