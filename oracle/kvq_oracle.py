@@ -390,49 +390,60 @@ def dequant_block(blk: Block, cfg: Config, cb_k=None, cb_v=None):
 # ---------------------------------------------------------------------------
 
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
-    """Pack rows of 128 codes into 16*bits bytes each.
+    """Pack rows of n codes (n a multiple of 8, the last axis) into n*bits/8 bytes each.
 
     4-bit: byte j holds element 2j in its low nibble and 2j+1 in its high one.
     2-bit: byte j holds element 4j+i at bits 2i.
-    3-bit: the low two bits of every element packed as 2-bit (32 bytes), then
-    bit 2 of every element, byte j bit i = element 8j+i (16 bytes): 48 bytes
-    per 128 codes ([KVQ] 9.3 counts 384 bits = 48 bytes).
+    3-bit: the low two bits of every element packed as 2-bit (n/4 bytes), then
+    bit 2 of every element, byte j bit i = element 8j+i (n/8 bytes); 128 codes
+    take 48 bytes ([KVQ] 9.3 counts 384 bits = 48 bytes).
     """
     c = np.asarray(codes, np.uint8)
-    rows = c.reshape(-1, 128)
+    n = c.shape[-1]
+    assert n % 8 == 0
+    rows = c.reshape(-1, n)
     if bits == 4:
         out = rows[:, 0::2] | (rows[:, 1::2] << 4)
     elif bits == 2:
-        r = rows.reshape(-1, 32, 4)
+        r = rows.reshape(-1, n // 4, 4)
         out = r[:, :, 0] | (r[:, :, 1] << 2) | (r[:, :, 2] << 4) | (r[:, :, 3] << 6)
     elif bits == 3:
         lo = pack_codes(rows & 3, 2)
-        hb = ((rows >> 2) & 1).reshape(-1, 16, 8)
-        hi = np.zeros((rows.shape[0], 16), np.uint8)
+        hb = ((rows >> 2) & 1).reshape(-1, n // 8, 8)
+        hi = np.zeros((rows.shape[0], n // 8), np.uint8)
         for i in range(8):
             hi |= (hb[:, :, i] << i).astype(np.uint8)
         out = np.concatenate([lo, hi], axis=1)
     else:
         raise ValueError(bits)
-    return out.astype(np.uint8).reshape(c.shape[:-1] + (16 * bits,))
+    return out.astype(np.uint8).reshape(c.shape[:-1] + (n * bits // 8,))
 
 
 def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of pack_codes over the last axis."""
     p = np.asarray(packed, np.uint8)
-    rows = p.reshape(-1, 16 * bits)
+    nb = p.shape[-1]
+    n = nb * 8 // bits
+    rows = p.reshape(-1, nb)
     if bits == 4:
-        out = np.empty((rows.shape[0], 128), np.uint8)
+        out = np.empty((rows.shape[0], n), np.uint8)
         out[:, 0::2] = rows & 15
         out[:, 1::2] = rows >> 4
     elif bits == 2:
-        out = np.stack([(rows >> (2 * i)) & 3 for i in range(4)], axis=2).reshape(-1, 128)
+        out = np.stack([(rows >> (2 * i)) & 3 for i in range(4)], axis=2).reshape(-1, n)
     elif bits == 3:
-        lo = unpack_codes(rows[:, :32], 2)
-        hi = np.stack([(rows[:, 32:] >> i) & 1 for i in range(8)], axis=2).reshape(-1, 128)
+        lo = unpack_codes(rows[:, :n // 4], 2)
+        hi = np.stack([(rows[:, n // 4:] >> i) & 1 for i in range(8)], axis=2).reshape(-1, n)
         out = lo | (hi << 2)
     else:
         raise ValueError(bits)
-    return out.astype(np.uint8).reshape(p.shape[:-1] + (128,))
+    return out.astype(np.uint8).reshape(p.shape[:-1] + (n,))
+
+
+def value_code_planes(vcodes: np.ndarray) -> np.ndarray:
+    """[T][D] value codes -> [2][D][64]: two token halves, channel-major within each."""
+    v = np.asarray(vcodes).reshape(T, D)
+    return np.stack([v[:64].T, v[64:].T])
 
 
 def _align(x: int, a: int) -> int:
@@ -442,7 +453,8 @@ def _align(x: int, a: int) -> int:
 def record_layout(mode: int, bits: int, k_out: int) -> tuple[dict, int]:
     """Byte offsets of the segments of one block record and its padded size.
 
-    Order: key codes (128 token rows), value codes (128 channel rows), key
+    Order: key codes (128 token rows), value codes (two token halves, each
+    128 channel rows of 64 codes), key
     statistics, value statistics, [KVARN: key s1 per token, value s1 per
     channel], [outliers: key CSR (values fp16, row pointers u16[129], channel
     u8), value CSC (values fp16, column pointers u16[129], token u8)]. Each
@@ -483,7 +495,7 @@ def serialize_block(blk: Block, cfg: Config) -> np.ndarray:
         buf[o:o + n] = raw
 
     put("kc", pack_codes(blk.kcodes, cfg.bits))             # token-major rows
-    put("vc", pack_codes(blk.vcodes.T, cfg.bits))           # channel-major rows
+    put("vc", pack_codes(value_code_planes(blk.vcodes), cfg.bits))   # [half][channel] rows
     if cfg.mode == MODE_SYM_INT4:
         put("ks", blk.kstat[0].astype(np.float16))
         put("vs", blk.vstat[0].astype(np.float16))

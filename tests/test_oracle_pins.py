@@ -350,8 +350,12 @@ def test_packing_byte_patterns_and_round_trip():
     assert p3[32] == 0b11110000         # bit 2 of codes 0..7
     r = rng(15)
     for bits in (2, 3, 4):
-        c = r.integers(0, 1 << bits, size=(37, 128)).astype(np.uint8)
-        assert np.array_equal(O.unpack_codes(O.pack_codes(c, bits), bits), c)
+        for n in (128, 64):
+            c = r.integers(0, 1 << bits, size=(37, n)).astype(np.uint8)
+            assert np.array_equal(O.unpack_codes(O.pack_codes(c, bits), bits), c)
+    c3h = np.arange(64) % 8
+    p3h = O.pack_codes(c3h, 3)
+    assert p3h.size == 24 and p3h[16] == 0b11110000
 
 
 def test_record_layout_sizes():
@@ -377,8 +381,8 @@ def test_serialized_record_reads_back():
     kc = O.unpack_codes(buf[o:o + n].reshape(128, 48), 3)
     assert np.array_equal(kc, blk.kcodes)
     o, n = off["vc"]
-    vc = O.unpack_codes(buf[o:o + n].reshape(128, 48), 3)
-    assert np.array_equal(vc.T, blk.vcodes)
+    vc = O.unpack_codes(buf[o:o + n].reshape(2, 128, 24), 3)      # [half][channel][64 tokens]
+    assert np.array_equal(np.concatenate([vc[0].T, vc[1].T]), blk.vcodes)
     o, n = off["ko_ptr"]
     ptr = buf[o:o + n].view(np.uint16)
     o, n = off["ko_idx"]
