@@ -1,0 +1,220 @@
+"""Python binding of libkvq (include/kvq.h): argument marshalling only.
+
+Every step of quantize-on-append and decode attention runs in the HIP kernels
+of libkvq.so. PyTorch is used for device memory and streams. Importing this
+package raises if libkvq.so has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvq.so")
+
+KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_SIZE, KVQ_ERR_CAPACITY, KVQ_ERR_STATE, KVQ_ERR_HIP = 0, -1, -2, -3, -4, -5
+KVQ_MODE_RTN, KVQ_MODE_NUQ, KVQ_MODE_KVARN, KVQ_MODE_SYM_INT4 = 0, 1, 2, 3
+KVQ_HEAD_DIM = 128
+KVQ_BLOCK_TOKENS = 128
+KVQ_MAX_SPLITS = 64
+
+
+class kvq_config(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32), ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+        ("mode", ctypes.c_int32), ("bits", ctypes.c_int32), ("outliers_per_vec", ctypes.c_int32),
+        ("pre_rope", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("varn_iters", ctypes.c_int32),
+    ]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        super().__init__(f"{func}: {msg} (status {status})")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (no fallback exists)")
+
+lib = ctypes.CDLL(LIB_PATH)
+_vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_sig = {
+    "kvq_cache_bytes": [ctypes.POINTER(kvq_config), ctypes.POINTER(_sz)],
+    "kvq_cache_init": [ctypes.POINTER(kvq_config), _vp, _sz, _vp, ctypes.POINTER(_vp)],
+    "kvq_codebook_load": [_vp, _i, _i, _i, ctypes.POINTER(ctypes.c_float), _i, _vp],
+    "kvq_quantize_append": [_vp, _i, _vp, _vp, _i, _vp],
+    "kvq_decode_attn": [_vp, _i, _vp, _vp, ctypes.c_float, _vp],
+    "kvq_cache_length": [_vp, _i, ctypes.POINTER(ctypes.c_int32)],
+    "kvq_cache_reset": [_vp, _i],
+    "kvq_set_decode_splits": [_vp, _i],
+    "kvq_block_span": [_vp, _i, _i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)],
+    "kvq_tail_span": [_vp, _i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)],
+    "kvq_decode_bytes": [_vp, _i, ctypes.POINTER(_sz)],
+}
+for _name, _args in _sig.items():
+    getattr(lib, _name).argtypes = _args
+    getattr(lib, _name).restype = ctypes.c_int
+lib.kvq_cache_destroy.argtypes = [_vp]
+lib.kvq_cache_destroy.restype = None
+lib.kvq_strerror.argtypes = [_i]
+lib.kvq_strerror.restype = ctypes.c_char_p
+lib.kvq_last_error.argtypes = []
+lib.kvq_last_error.restype = ctypes.c_char_p
+
+EXPORTED = list(_sig) + ["kvq_cache_destroy", "kvq_strerror", "kvq_last_error"]
+
+
+def _check(status: int, func: str):
+    if status != KVQ_OK:
+        raise KvqError(status, func, lib.kvq_last_error().decode() or lib.kvq_strerror(status).decode())
+
+
+def _ptr(x):
+    """Device or host address of a tensor / int / None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_config(n_layers, batch, n_kv_heads, n_q_heads, max_tokens, mode, bits, outliers_per_vec=0,
+                pre_rope=0, rope_theta=10000.0, varn_iters=8, head_dim=KVQ_HEAD_DIM) -> kvq_config:
+    return kvq_config(n_layers, batch, n_kv_heads, n_q_heads, head_dim, max_tokens, mode, bits,
+                      outliers_per_vec, pre_rope, rope_theta, varn_iters)
+
+
+def kvq_cache_bytes(cfg: kvq_config) -> int:
+    n = _sz(0)
+    _check(lib.kvq_cache_bytes(ctypes.byref(cfg), ctypes.byref(n)), "kvq_cache_bytes")
+    return n.value
+
+
+def kvq_cache_init(cfg: kvq_config, dev_buf, nbytes: int, stream=None) -> int:
+    h = _vp(0)
+    _check(lib.kvq_cache_init(ctypes.byref(cfg), _ptr(dev_buf), nbytes, _stream(stream), ctypes.byref(h)),
+           "kvq_cache_init")
+    return h.value
+
+
+def kvq_cache_destroy(handle: int):
+    lib.kvq_cache_destroy(handle)
+
+
+def kvq_codebook_load(handle: int, layer: int, kv_head: int, which: int, codebook, stream=None):
+    import numpy as np
+    cb = np.ascontiguousarray(codebook, dtype=np.float32)
+    arr = (ctypes.c_float * cb.size)(*cb.tolist())
+    _check(lib.kvq_codebook_load(handle, layer, kv_head, which, arr, cb.size, _stream(stream)), "kvq_codebook_load")
+
+
+def kvq_quantize_append(handle: int, layer: int, k, v, n_new: int, stream=None):
+    _check(lib.kvq_quantize_append(handle, layer, _ptr(k), _ptr(v), n_new, _stream(stream)), "kvq_quantize_append")
+
+
+def kvq_decode_attn(handle: int, layer: int, q, out, softmax_scale: float = 0.0, stream=None):
+    _check(lib.kvq_decode_attn(handle, layer, _ptr(q), _ptr(out), softmax_scale, _stream(stream)), "kvq_decode_attn")
+
+
+def kvq_cache_length(handle: int, layer: int) -> int:
+    n = ctypes.c_int32(0)
+    _check(lib.kvq_cache_length(handle, layer, ctypes.byref(n)), "kvq_cache_length")
+    return n.value
+
+
+def kvq_cache_reset(handle: int, layer: int):
+    _check(lib.kvq_cache_reset(handle, layer), "kvq_cache_reset")
+
+
+def kvq_set_decode_splits(handle: int, splits: int):
+    _check(lib.kvq_set_decode_splits(handle, splits), "kvq_set_decode_splits")
+
+
+def kvq_block_span(handle: int, layer: int, b: int, kv_head: int, block: int):
+    off, n = _sz(0), _sz(0)
+    _check(lib.kvq_block_span(handle, layer, b, kv_head, block, ctypes.byref(off), ctypes.byref(n)), "kvq_block_span")
+    return off.value, n.value
+
+
+def kvq_tail_span(handle: int, layer: int, b: int, kv_head: int):
+    off, n = _sz(0), _sz(0)
+    _check(lib.kvq_tail_span(handle, layer, b, kv_head, ctypes.byref(off), ctypes.byref(n)), "kvq_tail_span")
+    return off.value, n.value
+
+
+def kvq_decode_bytes(handle: int, layer: int) -> int:
+    n = _sz(0)
+    _check(lib.kvq_decode_bytes(handle, layer, ctypes.byref(n)), "kvq_decode_bytes")
+    return n.value
+
+
+def kvq_strerror(status: int) -> str:
+    return lib.kvq_strerror(status).decode()
+
+
+def kvq_last_error() -> str:
+    return lib.kvq_last_error().decode()
+
+
+class KVCache:
+    """A cache handle over a torch-allocated device buffer (the buffer lives as long as this object)."""
+
+    def __init__(self, cfg: kvq_config, device="cuda", stream=None):
+        import torch
+        self.cfg = cfg
+        self.nbytes = kvq_cache_bytes(cfg)
+        raw = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device)
+        pad = (-raw.data_ptr()) % 256
+        self.buf = raw[pad:pad + self.nbytes]
+        self._raw = raw
+        self.handle = kvq_cache_init(cfg, self.buf, self.nbytes, stream)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            kvq_cache_destroy(h)
+            self.handle = None
+
+    def codebook_load(self, layer, kv_head, which, codebook, stream=None):
+        kvq_codebook_load(self.handle, layer, kv_head, which, codebook, stream)
+
+    def append(self, layer, k, v, stream=None):
+        assert k.dtype == v.dtype and k.is_contiguous() and v.is_contiguous()
+        assert k.shape == v.shape and k.shape[0] == self.cfg.batch and k.shape[1] == self.cfg.n_kv_heads
+        assert k.shape[3] == KVQ_HEAD_DIM
+        kvq_quantize_append(self.handle, layer, k, v, k.shape[2], stream)
+
+    def decode(self, layer, q, out, softmax_scale=0.0, stream=None):
+        assert q.is_contiguous() and out.is_contiguous()
+        assert tuple(q.shape) == (self.cfg.batch, self.cfg.n_q_heads, KVQ_HEAD_DIM)
+        assert tuple(out.shape) == tuple(q.shape)
+        kvq_decode_attn(self.handle, layer, q, out, softmax_scale, stream)
+
+    def length(self, layer):
+        return kvq_cache_length(self.handle, layer)
+
+    def reset(self, layer):
+        kvq_cache_reset(self.handle, layer)
+
+    def set_splits(self, splits):
+        kvq_set_decode_splits(self.handle, splits)
+
+    def block_bytes(self, layer, b, kv_head, block):
+        off, n = kvq_block_span(self.handle, layer, b, kv_head, block)
+        return self.buf[off:off + n]
+
+    def tail_bytes(self, layer, b, kv_head):
+        off, n = kvq_tail_span(self.handle, layer, b, kv_head)
+        return self.buf[off:off + n]
+
+    def decode_bytes(self, layer):
+        return kvq_decode_bytes(self.handle, layer)

@@ -1,0 +1,455 @@
+// Host side of the C ABI declared in include/kvq.h: validation, the device
+// buffer layout, RoPE tables, split planning and kernel launches on the
+// caller's stream. No device memory is allocated here.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+kvq_status ok() { return KVQ_OK; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+namespace kvq {
+
+RecordLayout make_layout(int mode, int bits, int k_out) {
+  RecordLayout L{};
+  uint32_t pos = 0, payload = 0;
+  auto seg = [&](uint32_t size) {
+    pos = (uint32_t)align_up(pos, 16);
+    const uint32_t at = pos;
+    pos += size;
+    payload += size;
+    return at;
+  };
+  const uint32_t R = 16u * (uint32_t)bits;
+  const uint32_t stat = mode == SYM ? 256u : 1024u;
+  L.kc = seg(kT * R);
+  L.vc = seg(kD * R);
+  L.ks = seg(stat);
+  L.vs = seg(stat);
+  if (mode == KVARN) {
+    L.k1 = seg(4 * kT);
+    L.v1 = seg(4 * kD);
+  }
+  if (k_out > 0) {
+    const uint32_t n = 128u * (uint32_t)k_out;
+    L.ko_val = seg(2 * n);
+    L.ko_ptr = seg(2 * 129);
+    L.ko_idx = seg(n);
+    L.vo_val = seg(2 * n);
+    L.vo_ptr = seg(2 * 129);
+    L.vo_idx = seg(n);
+  }
+  L.rec_bytes = (uint32_t)align_up(pos, 256);
+  L.payload = payload;
+  return L;
+}
+
+}  // namespace kvq
+
+struct kvq_cache_s {
+  kvq_config cfg;
+  kvq::RecordLayout lay;
+  uint8_t* base = nullptr;
+  size_t bytes = 0;
+  int max_blocks = 0;
+  size_t off_rec = 0, layer_rec_bytes = 0;
+  size_t off_tail = 0, layer_tail_bytes = 0;
+  size_t off_cb = 0, off_rope_base = 0, off_rope_off = 0, off_work = 0;
+  std::vector<int32_t> len;
+  std::vector<uint8_t> cb_loaded;   // [layer][kv_head][2]
+  std::vector<float> cb_host;       // [layer][kv_head][2][16]
+  std::vector<float> rope_host;     // base table then offset table
+  int splits_override = 0;
+};
+
+namespace {
+
+struct Regions {
+  int max_blocks;
+  size_t layer_rec, rec, layer_tail, tail, cb, rope_base, rope_off, work, total;
+  size_t off_rec, off_tail, off_cb, off_rope_base, off_rope_off, off_work;
+};
+
+kvq_status validate_config(const kvq_config* c) {
+  if (!c) return fail(KVQ_ERR_ARG, "config is NULL");
+  if (c->n_layers < 1 || c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1)
+    return fail(KVQ_ERR_ARG, "n_layers, batch, n_kv_heads and n_q_heads must be >= 1");
+  if (c->head_dim != KVQ_HEAD_DIM) return fail(KVQ_ERR_ARG, "head_dim must be 128 (got %d)", c->head_dim);
+  if (c->n_q_heads % c->n_kv_heads != 0)
+    return fail(KVQ_ERR_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_q_heads, c->n_kv_heads);
+  const int g = c->n_q_heads / c->n_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return fail(KVQ_ERR_ARG, "query group %d not in {1,2,4,8}", g);
+  if (c->max_tokens < KVQ_BLOCK_TOKENS || c->max_tokens % KVQ_BLOCK_TOKENS != 0)
+    return fail(KVQ_ERR_ARG, "max_tokens must be a positive multiple of 128 (got %d)", c->max_tokens);
+  if (c->mode < KVQ_MODE_RTN || c->mode > KVQ_MODE_SYM_INT4) return fail(KVQ_ERR_ARG, "unknown mode %d", c->mode);
+  if (c->bits < 2 || c->bits > 4) return fail(KVQ_ERR_ARG, "bits must be 2, 3 or 4 (got %d)", c->bits);
+  if (c->mode == KVQ_MODE_SYM_INT4 && c->bits != 4) return fail(KVQ_ERR_ARG, "symmetric int4 requires bits = 4");
+  if (c->outliers_per_vec < 0 || c->outliers_per_vec > KVQ_MAX_OUTLIERS)
+    return fail(KVQ_ERR_ARG, "outliers_per_vec must be in 0..8 (got %d)", c->outliers_per_vec);
+  if (c->pre_rope != 0 && c->pre_rope != 1) return fail(KVQ_ERR_ARG, "pre_rope must be 0 or 1");
+  if (c->pre_rope && !(c->rope_theta > 0.f && std::isfinite(c->rope_theta)))
+    return fail(KVQ_ERR_ARG, "rope_theta must be finite and > 0");
+  if (c->mode == KVQ_MODE_KVARN) {
+    if (c->outliers_per_vec != 0 || c->pre_rope != 0)
+      return fail(KVQ_ERR_ARG, "KVARN mode supports neither outliers nor pre-RoPE keys");
+    if (c->varn_iters < 0 || c->varn_iters > 64) return fail(KVQ_ERR_ARG, "varn_iters must be in 0..64");
+  }
+  const double rec = kvq::make_layout(c->mode, c->bits, c->outliers_per_vec).rec_bytes;
+  const double total = rec * c->n_layers * c->batch * c->n_kv_heads * (c->max_tokens / 128.0);
+  if (total > 4.0e12) return fail(KVQ_ERR_ARG, "cache larger than 4 TB requested");
+  return KVQ_OK;
+}
+
+Regions regions(const kvq_config* c) {
+  Regions r{};
+  const kvq::RecordLayout L = kvq::make_layout(c->mode, c->bits, c->outliers_per_vec);
+  r.max_blocks = c->max_tokens / KVQ_BLOCK_TOKENS;
+  const size_t units = (size_t)c->batch * c->n_kv_heads;
+  r.layer_rec = units * r.max_blocks * L.rec_bytes;
+  r.rec = r.layer_rec * c->n_layers;
+  r.layer_tail = units * 2 * kvq::kT * kvq::kD * sizeof(__half);
+  r.tail = r.layer_tail * c->n_layers;
+  r.cb = c->mode == KVQ_MODE_NUQ ? (size_t)c->n_layers * c->n_kv_heads * 2 * 16 * sizeof(float) : 0;
+  r.rope_base = c->pre_rope ? (size_t)(r.max_blocks + 1) * 64 * 2 * sizeof(float) : 0;
+  r.rope_off = c->pre_rope ? (size_t)128 * 64 * 2 * sizeof(float) : 0;
+  r.work = (size_t)c->batch * c->n_q_heads * KVQ_MAX_SPLITS * kvq::kPartStride * sizeof(float);
+  size_t pos = 0;
+  auto place = [&](size_t size) { pos = align_up(pos, 256); const size_t at = pos; pos += size; return at; };
+  r.off_rec = place(r.rec);
+  r.off_tail = place(r.tail);
+  r.off_cb = place(r.cb);
+  r.off_rope_base = place(r.rope_base);
+  r.off_rope_off = place(r.rope_off);
+  r.off_work = place(r.work);
+  r.total = align_up(pos, 256);
+  return r;
+}
+
+kvq_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+kvq_status check_layer(kvq_cache c, int layer) {
+  if (!c) return fail(KVQ_ERR_ARG, "cache handle is NULL");
+  if (layer < 0 || layer >= c->cfg.n_layers)
+    return fail(KVQ_ERR_ARG, "layer %d out of range [0, %d)", layer, c->cfg.n_layers);
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(KVQ_ERR_ARG, "bytes is NULL");
+  const kvq_status st = validate_config(cfg);
+  if (st != KVQ_OK) return st;
+  *bytes = regions(cfg).total;
+  return ok();
+}
+
+kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_buf, size_t bytes, void* stream,
+                          kvq_cache* out) {
+  if (!out) return fail(KVQ_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  kvq_status st = validate_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!dev_buf) return fail(KVQ_ERR_ARG, "dev_buf is NULL");
+  if (reinterpret_cast<uintptr_t>(dev_buf) % 256 != 0) return fail(KVQ_ERR_ARG, "dev_buf must be 256-byte aligned");
+  const Regions r = regions(cfg);
+  if (bytes < r.total) return fail(KVQ_ERR_SIZE, "dev_buf holds %zu bytes, %zu needed", bytes, r.total);
+
+  auto* c = new kvq_cache_s();
+  c->cfg = *cfg;
+  c->lay = kvq::make_layout(cfg->mode, cfg->bits, cfg->outliers_per_vec);
+  c->base = static_cast<uint8_t*>(dev_buf);
+  c->bytes = bytes;
+  c->max_blocks = r.max_blocks;
+  c->off_rec = r.off_rec;
+  c->layer_rec_bytes = r.layer_rec;
+  c->off_tail = r.off_tail;
+  c->layer_tail_bytes = r.layer_tail;
+  c->off_cb = r.off_cb;
+  c->off_rope_base = r.off_rope_base;
+  c->off_rope_off = r.off_rope_off;
+  c->off_work = r.off_work;
+  c->len.assign(cfg->n_layers, 0);
+  c->cb_loaded.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2, 0);
+  c->cb_host.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2 * 16, 0.f);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cfg->pre_rope) {
+    // RoPE angles n * theta_i, theta_i = theta^(-2i/128), evaluated in double precision:
+    // base rows for n = 128 * block and offset rows for n = 0..127 (KVQuant notes 1.3)
+    const int nb = r.max_blocks + 1;
+    c->rope_host.resize((size_t)nb * 128 + 128 * 128);
+    for (int i = 0; i < 64; ++i) {
+      const double th = std::pow((double)cfg->rope_theta, -2.0 * i / 128.0);
+      for (int blk = 0; blk < nb; ++blk) {
+        const double ang = (double)blk * 128.0 * th;
+        c->rope_host[((size_t)blk * 64 + i) * 2] = (float)std::cos(ang);
+        c->rope_host[((size_t)blk * 64 + i) * 2 + 1] = (float)std::sin(ang);
+      }
+      for (int jj = 0; jj < 128; ++jj) {
+        const double ang = (double)jj * th;
+        c->rope_host[(size_t)nb * 128 + ((size_t)jj * 64 + i) * 2] = (float)std::cos(ang);
+        c->rope_host[(size_t)nb * 128 + ((size_t)jj * 64 + i) * 2 + 1] = (float)std::sin(ang);
+      }
+    }
+    st = hip_check(hipMemcpyAsync(c->base + c->off_rope_base, c->rope_host.data(), (size_t)nb * 128 * sizeof(float),
+                                  hipMemcpyHostToDevice, s), "upload RoPE base table");
+    if (st == KVQ_OK)
+      st = hip_check(hipMemcpyAsync(c->base + c->off_rope_off, c->rope_host.data() + (size_t)nb * 128,
+                                    128 * 128 * sizeof(float), hipMemcpyHostToDevice, s), "upload RoPE offset table");
+    if (st == KVQ_OK) st = hip_check(hipStreamSynchronize(s), "synchronize after init");
+    if (st != KVQ_OK) {
+      delete c;
+      return st;
+    }
+  }
+  *out = c;
+  return ok();
+}
+
+void kvq_cache_destroy(kvq_cache cache) { delete cache; }
+
+kvq_status kvq_codebook_load(kvq_cache c, int layer, int kv_head, int which, const float* host_codebook,
+                             int n_entries, void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (c->cfg.mode != KVQ_MODE_NUQ) return fail(KVQ_ERR_STATE, "codebooks are only used in NUQ mode");
+  if (kv_head < 0 || kv_head >= c->cfg.n_kv_heads) return fail(KVQ_ERR_ARG, "kv_head %d out of range", kv_head);
+  if (which != 0 && which != 1) return fail(KVQ_ERR_ARG, "which must be 0 (keys) or 1 (values)");
+  if (!host_codebook) return fail(KVQ_ERR_ARG, "codebook is NULL");
+  if (n_entries != (1 << c->cfg.bits))
+    return fail(KVQ_ERR_ARG, "codebook needs %d entries (got %d)", 1 << c->cfg.bits, n_entries);
+  for (int i = 0; i < n_entries; ++i) {
+    const float v = host_codebook[i];
+    if (!std::isfinite(v) || v < -1.f || v > 1.f) return fail(KVQ_ERR_ARG, "codebook entry %d not in [-1, 1]", i);
+    if (i > 0 && !(v > host_codebook[i - 1])) return fail(KVQ_ERR_ARG, "codebook not strictly ascending at %d", i);
+  }
+  const size_t slot = ((size_t)layer * c->cfg.n_kv_heads + kv_head) * 2 + which;
+  float* dst = c->cb_host.data() + slot * 16;
+  for (int i = 0; i < 16; ++i) dst[i] = i < n_entries ? host_codebook[i] : 0.f;
+  st = hip_check(hipMemcpyAsync(c->base + c->off_cb + slot * 16 * sizeof(float), dst, 16 * sizeof(float),
+                                hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)), "upload codebook");
+  if (st != KVQ_OK) return st;
+  c->cb_loaded[slot] = 1;
+  return ok();
+}
+
+kvq_status kvq_quantize_append(kvq_cache c, int layer, const void* k_f16, const void* v_f16, int n_new,
+                               void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (n_new < 0) return fail(KVQ_ERR_ARG, "n_new must be >= 0");
+  if (n_new == 0) return ok();
+  if (!k_f16 || !v_f16) return fail(KVQ_ERR_ARG, "k or v is NULL");
+  if (reinterpret_cast<uintptr_t>(k_f16) % 16 || reinterpret_cast<uintptr_t>(v_f16) % 16)
+    return fail(KVQ_ERR_ARG, "k and v must be 16-byte aligned");
+  const kvq_config& cfg = c->cfg;
+  const int len = c->len[layer];
+  if ((int64_t)len + n_new > cfg.max_tokens)
+    return fail(KVQ_ERR_CAPACITY, "layer %d holds %d tokens; %d more exceed max_tokens %d", layer, len, n_new,
+                cfg.max_tokens);
+  if (cfg.mode == KVQ_MODE_NUQ) {
+    for (int h = 0; h < cfg.n_kv_heads; ++h)
+      for (int w = 0; w < 2; ++w)
+        if (!c->cb_loaded[((size_t)layer * cfg.n_kv_heads + h) * 2 + w])
+          return fail(KVQ_ERR_STATE, "NUQ codebook of layer %d kv head %d (%s) not loaded", layer, h, w ? "V" : "K");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int t0 = len % KVQ_BLOCK_TOKENS;
+  const int nb = (t0 + n_new) / KVQ_BLOCK_TOKENS;
+  const int rem = (t0 + n_new) % KVQ_BLOCK_TOKENS;
+  __half* tail = reinterpret_cast<__half*>(c->base + c->off_tail + (size_t)layer * c->layer_tail_bytes);
+  if (nb > 0) {
+    kvq::QuantArgs a{};
+    a.lay = c->lay;
+    a.k_out = cfg.outliers_per_vec;
+    a.varn_iters = cfg.varn_iters;
+    a.k_in = static_cast<const __half*>(k_f16);
+    a.v_in = static_cast<const __half*>(v_f16);
+    a.n_new = n_new;
+    a.t0 = t0;
+    a.blk0 = len / KVQ_BLOCK_TOKENS;
+    a.Hkv = cfg.n_kv_heads;
+    a.max_blocks = c->max_blocks;
+    a.rec = c->base + c->off_rec + (size_t)layer * c->layer_rec_bytes;
+    a.tail = tail;
+    a.cb = reinterpret_cast<const float*>(c->base + c->off_cb) + (size_t)layer * cfg.n_kv_heads * 2 * 16;
+    st = hip_check(kvq::launch_quantize(cfg.mode, cfg.bits, a, nb, cfg.batch, s), "launch quantize");
+    if (st != KVQ_OK) return st;
+  }
+  kvq::TailArgs ta{};
+  ta.k_in = static_cast<const __half*>(k_f16);
+  ta.v_in = static_cast<const __half*>(v_f16);
+  ta.n_new = n_new;
+  ta.Hkv = cfg.n_kv_heads;
+  ta.tail = tail;
+  if (nb == 0) { ta.src0 = 0; ta.dst0 = t0; ta.count = n_new; }
+  else { ta.src0 = n_new - rem; ta.dst0 = 0; ta.count = rem; }
+  if (ta.count > 0) {
+    st = hip_check(kvq::launch_tail(ta, cfg.batch, s), "launch tail copy");
+    if (st != KVQ_OK) return st;
+  }
+  c->len[layer] = len + n_new;
+  return ok();
+}
+
+kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out, float softmax_scale,
+                           void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (!q_f16 || !out) return fail(KVQ_ERR_ARG, "q or out is NULL");
+  if (reinterpret_cast<uintptr_t>(q_f16) % 4 || reinterpret_cast<uintptr_t>(out) % 4)
+    return fail(KVQ_ERR_ARG, "q and out must be 4-byte aligned");
+  if (!(softmax_scale <= 0.f || std::isfinite(softmax_scale))) return fail(KVQ_ERR_ARG, "softmax_scale not finite");
+  const kvq_config& cfg = c->cfg;
+  const int L = c->len[layer];
+  if (L == 0) return fail(KVQ_ERR_STATE, "layer %d holds no tokens", layer);
+  const int nblk = L / KVQ_BLOCK_TOKENS, tail_n = L % KVQ_BLOCK_TOKENS;
+  const int units = cfg.batch * cfg.n_kv_heads;
+  int splits = 1, bps = 0;
+  if (nblk > 0) {
+    if (c->splits_override > 0) {
+      splits = std::min(c->splits_override, nblk);
+    } else {
+      const int target_wgs = 2048;                 // 8 workgroups per CU on 256 CUs
+      splits = (target_wgs + units - 1) / units;
+      splits = std::min(splits, (nblk + 1) / 2);   // at least two blocks (four halves) per split
+      splits = std::max(1, std::min(splits, KVQ_MAX_SPLITS));
+    }
+    bps = (nblk + splits - 1) / splits;
+    splits = (nblk + bps - 1) / bps;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  kvq::DecodeArgs a{};
+  a.lay = c->lay;
+  a.k_out = cfg.outliers_per_vec;
+  a.rec = c->base + c->off_rec + (size_t)layer * c->layer_rec_bytes;
+  a.tail = reinterpret_cast<const __half*>(c->base + c->off_tail + (size_t)layer * c->layer_tail_bytes);
+  a.cb = reinterpret_cast<const float*>(c->base + c->off_cb) + (size_t)layer * cfg.n_kv_heads * 2 * 16;
+  a.rope_base = reinterpret_cast<const float*>(c->base + c->off_rope_base);
+  a.rope_off = reinterpret_cast<const float*>(c->base + c->off_rope_off);
+  a.q = static_cast<const __half*>(q_f16);
+  a.part = reinterpret_cast<float*>(c->base + c->off_work);
+  a.Hkv = cfg.n_kv_heads;
+  a.Hq = cfg.n_q_heads;
+  a.max_blocks = c->max_blocks;
+  a.nblk = nblk;
+  a.tail_n = tail_n;
+  a.splits = splits;
+  a.blocks_per_split = bps;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  st = hip_check(kvq::launch_decode(cfg.mode, cfg.bits, cfg.n_q_heads / cfg.n_kv_heads, cfg.pre_rope, a, cfg.batch, s),
+                 "launch decode");
+  if (st != KVQ_OK) return st;
+  kvq::CombineArgs ca{a.part, out, cfg.n_q_heads, splits};
+  st = hip_check(kvq::launch_combine(ca, cfg.batch, s), "launch split combine");
+  if (st != KVQ_OK) return st;
+  return ok();
+}
+
+kvq_status kvq_cache_length(kvq_cache c, int layer, int32_t* n_tokens) {
+  const kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (!n_tokens) return fail(KVQ_ERR_ARG, "n_tokens is NULL");
+  *n_tokens = c->len[layer];
+  return ok();
+}
+
+kvq_status kvq_cache_reset(kvq_cache c, int layer) {
+  const kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  c->len[layer] = 0;
+  return ok();
+}
+
+kvq_status kvq_set_decode_splits(kvq_cache c, int splits) {
+  if (!c) return fail(KVQ_ERR_ARG, "cache handle is NULL");
+  if (splits < 0 || splits > KVQ_MAX_SPLITS) return fail(KVQ_ERR_ARG, "splits must be in 0..%d", KVQ_MAX_SPLITS);
+  c->splits_override = splits;
+  return ok();
+}
+
+kvq_status kvq_block_span(kvq_cache c, int layer, int b, int kv_head, int block, size_t* offset, size_t* bytes) {
+  const kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (b < 0 || b >= c->cfg.batch || kv_head < 0 || kv_head >= c->cfg.n_kv_heads || block < 0 ||
+      block >= c->max_blocks)
+    return fail(KVQ_ERR_ARG, "block coordinates out of range");
+  if (!offset || !bytes) return fail(KVQ_ERR_ARG, "offset or bytes is NULL");
+  const size_t unit = (size_t)b * c->cfg.n_kv_heads + kv_head;
+  *offset = c->off_rec + (size_t)layer * c->layer_rec_bytes + (unit * c->max_blocks + block) * c->lay.rec_bytes;
+  *bytes = c->lay.rec_bytes;
+  return ok();
+}
+
+kvq_status kvq_tail_span(kvq_cache c, int layer, int b, int kv_head, size_t* offset, size_t* bytes) {
+  const kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (b < 0 || b >= c->cfg.batch || kv_head < 0 || kv_head >= c->cfg.n_kv_heads)
+    return fail(KVQ_ERR_ARG, "tail coordinates out of range");
+  if (!offset || !bytes) return fail(KVQ_ERR_ARG, "offset or bytes is NULL");
+  const size_t unit = (size_t)b * c->cfg.n_kv_heads + kv_head;
+  *offset = c->off_tail + (size_t)layer * c->layer_tail_bytes + unit * 2 * kvq::kT * kvq::kD * sizeof(__half);
+  *bytes = 2 * kvq::kT * kvq::kD * sizeof(__half);
+  return ok();
+}
+
+kvq_status kvq_decode_bytes(kvq_cache c, int layer, size_t* bytes) {
+  const kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (!bytes) return fail(KVQ_ERR_ARG, "bytes is NULL");
+  const kvq_config& cfg = c->cfg;
+  const size_t units = (size_t)cfg.batch * cfg.n_kv_heads;
+  const int L = c->len[layer];
+  const size_t nblk = L / KVQ_BLOCK_TOKENS, tail_n = L % KVQ_BLOCK_TOKENS;
+  size_t n = units * (nblk * c->lay.payload + tail_n * 2 * KVQ_HEAD_DIM * sizeof(__half));
+  n += (size_t)cfg.batch * cfg.n_q_heads * KVQ_HEAD_DIM * (sizeof(__half) + sizeof(float));
+  if (cfg.mode == KVQ_MODE_NUQ) n += (size_t)cfg.n_kv_heads * 2 * (1u << cfg.bits) * sizeof(float);
+  if (cfg.pre_rope) n += (nblk + (tail_n ? 1 : 0)) * 64 * 2 * sizeof(float) + 128 * 64 * 2 * sizeof(float);
+  *bytes = n;
+  return ok();
+}
+
+const char* kvq_strerror(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_ARG: return "invalid argument";
+    case KVQ_ERR_SIZE: return "buffer too small";
+    case KVQ_ERR_CAPACITY: return "capacity exceeded";
+    case KVQ_ERR_STATE: return "invalid state";
+    case KVQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* kvq_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal declarations shared by the host API and the HIP kernels of libkvq.
+// Layout of a block record and the argument blocks the launches take.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kT = 128;          // tokens per quantization block
+constexpr int kD = 128;          // head dimension
+constexpr int kMaxOut = 8;       // outliers per vector
+constexpr int kPartStride = 2 + kD;  // one split partial: m, l, o[128]
+
+enum Mode { RTN = 0, NUQ = 1, KVARN = 2, SYM = 3 };
+
+// Byte offsets of the segments of one block record (all 16-byte aligned).
+struct RecordLayout {
+  uint32_t kc, vc, ks, vs, k1, v1;
+  uint32_t ko_val, ko_ptr, ko_idx, vo_val, vo_ptr, vo_idx;
+  uint32_t rec_bytes;   // padded to 256
+  uint32_t payload;     // sum of segment sizes
+};
+
+RecordLayout make_layout(int mode, int bits, int k_out);
+
+struct QuantArgs {
+  RecordLayout lay;
+  int k_out, varn_iters;
+  const __half* k_in;    // [B][Hkv][n_new][128]
+  const __half* v_in;
+  int n_new, t0, blk0;   // t0: tokens already in the tail; blk0: index of the block being completed
+  int Hkv, max_blocks;
+  uint8_t* rec;          // records of the layer, [B][Hkv][max_blocks]
+  const __half* tail;    // tails of the layer, [B][Hkv][2][128][128]
+  const float* cb;       // codebooks of the layer, [Hkv][2][16]
+};
+
+struct TailArgs {
+  const __half* k_in;
+  const __half* v_in;
+  int n_new, src0, dst0, count, Hkv;
+  __half* tail;
+};
+
+struct DecodeArgs {
+  RecordLayout lay;
+  int k_out;
+  const uint8_t* rec;
+  const __half* tail;
+  const float* cb;
+  const float* rope_base;   // [max_blocks + 1][64][2]: cos, sin of (128 * block) * theta_i
+  const float* rope_off;    // [128][64][2]: cos, sin of j * theta_i
+  const __half* q;          // [B][Hq][128]
+  float* part;              // [B][Hq][splits][2 + 128]
+  int Hkv, Hq, max_blocks;
+  int nblk, tail_n, splits, blocks_per_split;
+  float scale_log2;         // softmax scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* part;
+  float* out;               // [B][Hq][128]
+  int Hq, splits;
+};
+
+hipError_t launch_quantize(int mode, int bits, const QuantArgs& a, int n_blocks, int batch,
+                           hipStream_t s);
+hipError_t launch_tail(const TailArgs& a, int batch, hipStream_t s);
+hipError_t launch_decode(int mode, int bits, int group, int rope, const DecodeArgs& a, int batch,
+                         hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int batch, hipStream_t s);
+
+}  // namespace kvq

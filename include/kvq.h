@@ -1,0 +1,196 @@
+/*
+ * kvq.h - low-bit KV-cache quantize-on-append and packed-cache decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources cited by page and section):
+ *   - "KVQuant reading notes": keys quantized per channel and before RoPE, values
+ *     per token (sections 3.1, 3.2, 3.6); non-uniform codebooks looked up by
+ *     argmin (sections 1.2, 3.3); about 1% of each vector kept exactly in fp16 as
+ *     sparse outliers, CSR for keys and CSC for values (section 3.4); the
+ *     attention kernel dequantizes, merges outliers and applies RoPE on the fly
+ *     (section 3.7, Algorithm 1).
+ *   - "KVarN" summary: a 128-point Hadamard rotation across channels and 8
+ *     Sinkhorn-style variance-normalisation iterations per 128-token block before
+ *     RTN, with a second stored scale s1 (core method, method steps).
+ *   - "reproducing TurboQuant" blog: symmetric int4 over 128-element
+ *     sequence-direction blocks with fp16 scales, dequantized inside attention
+ *     (sections 2.1, 4.1, 4.2, 5.2).
+ *
+ * Conventions for every function:
+ *   - Host-callable, never throws, returns kvq_status (KVQ_OK = 0).
+ *   - "dev" pointers are device pointers (hipMalloc / torch CUDA tensors); "host"
+ *     pointers are host memory. The caller owns every buffer it passes and keeps
+ *     it alive until the stream has passed the call.
+ *   - stream is a hipStream_t (NULL = the default stream). Work is enqueued on it
+ *     and the call returns without synchronizing, except kvq_cache_init, which
+ *     synchronizes its stream once after uploading its tables.
+ *   - Arguments, shapes and state are validated on the host before anything is
+ *     launched; a failed check launches nothing and changes no state.
+ *     kvq_last_error() describes the last failure of the calling thread.
+ *   - Device faults surface at the caller's next synchronization.
+ *   - One handle is used from one stream at a time; calls on one handle that
+ *     overlap on different streams race (they share the decode workspace).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = -1,       /* invalid argument or configuration */
+  KVQ_ERR_SIZE = -2,      /* a buffer is too small */
+  KVQ_ERR_CAPACITY = -3,  /* append would exceed max_tokens */
+  KVQ_ERR_STATE = -4,     /* operation not valid in the current state */
+  KVQ_ERR_HIP = -5        /* a HIP runtime call failed */
+} kvq_status;
+
+typedef enum {
+  KVQ_MODE_RTN = 0,       /* asymmetric uniform RTN, min/range (KVQuant notes 1.2, 3.1) */
+  KVQ_MODE_NUQ = 1,       /* codebook argmin on [-1, 1] (KVQuant notes 1.2, 3.3) */
+  KVQ_MODE_KVARN = 2,     /* Hadamard + VarN + RTN with s1 (KVarN core method) */
+  KVQ_MODE_SYM_INT4 = 3   /* symmetric int4, fp16 scales (TurboQuant blog 4.2) */
+} kvq_mode;
+
+#define KVQ_HEAD_DIM 128
+#define KVQ_BLOCK_TOKENS 128
+#define KVQ_MAX_OUTLIERS 8
+#define KVQ_MAX_GROUP 8
+#define KVQ_MAX_SPLITS 64
+
+typedef struct {
+  int32_t n_layers;         /* >= 1 */
+  int32_t batch;            /* >= 1; every sequence holds the same number of tokens */
+  int32_t n_kv_heads;       /* >= 1 */
+  int32_t n_q_heads;        /* multiple of n_kv_heads, group n_q_heads/n_kv_heads in {1,2,4,8} */
+  int32_t head_dim;         /* must be 128 */
+  int32_t max_tokens;       /* capacity per sequence and layer, multiple of 128, >= 128 */
+  int32_t mode;             /* kvq_mode */
+  int32_t bits;             /* 2, 3 or 4; KVQ_MODE_SYM_INT4 requires 4 */
+  int32_t outliers_per_vec; /* 0..8 fp16 outliers per quantization vector; 0 with KVARN */
+  int32_t pre_rope;         /* 1: keys are stored before RoPE and rotated at decode; 0 with KVARN */
+  float rope_theta;         /* RoPE base (10000 in the pages), > 0 when pre_rope */
+  int32_t varn_iters;       /* KVARN: 0..64 Sinkhorn iterations (8 in the pages) */
+} kvq_config;
+
+typedef struct kvq_cache_s* kvq_cache;   /* opaque host handle; owns no device memory */
+
+/* Bytes of device memory a cache with this configuration needs (pure host). */
+kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes);
+
+/*
+ * Create a handle over a caller-owned device buffer dev_buf of at least
+ * kvq_cache_bytes(cfg) bytes, 256-byte aligned. Uploads the RoPE tables (when
+ * pre_rope), sets every layer's length to 0 and synchronizes stream once.
+ * The buffer holds, per layer and (sequence, kv head): 128-token block records
+ * (layout below), a fp16 tail of up to 127 tokens, the codebooks, the RoPE
+ * tables and a workspace for decode split partials.
+ */
+kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_buf, size_t bytes, void* stream,
+                          kvq_cache* out);
+
+/* Free the host handle (not dev_buf). NULL is ignored. */
+void kvq_cache_destroy(kvq_cache cache);
+
+/*
+ * Load the NUQ codebook of one (layer, kv head) for keys (which = 0) or values
+ * (which = 1). host_codebook: n_entries = 2^bits fp32 values, finite, strictly
+ * ascending, within [-1, 1] (KVQuant notes 3.3: one datatype per layer and head;
+ * this build keeps one per (layer, kv head, K/V)). The handle keeps a host copy,
+ * so host_codebook may be freed on return. Only valid in KVQ_MODE_NUQ.
+ */
+kvq_status kvq_codebook_load(kvq_cache cache, int layer, int kv_head, int which,
+                             const float* host_codebook, int n_entries, void* stream);
+
+/*
+ * Append n_new tokens to every sequence of one layer.
+ * k_f16, v_f16: dev, fp16 [batch][n_kv_heads][n_new][128], contiguous; keys
+ * before RoPE when pre_rope. Tokens take the next absolute positions.
+ * Every time a sequence has 128 new tokens they are quantized as one block
+ * (KVQuant notes Algorithm 1; KVarN method steps; blog 4.2); the rest stay in
+ * the fp16 tail (blog 5.2). n_new = 0 is a no-op.
+ * Errors: KVQ_ERR_CAPACITY if length + n_new > max_tokens; KVQ_ERR_STATE in
+ * NUQ mode unless both codebooks of every kv head of the layer are loaded.
+ */
+kvq_status kvq_quantize_append(kvq_cache cache, int layer, const void* k_f16, const void* v_f16,
+                               int n_new, void* stream);
+
+/*
+ * Decode attention for one layer over every cached token (quantized blocks and
+ * the fp16 tail), reading the packed cache directly.
+ * q_f16: dev, fp16 [batch][n_q_heads][128], already rotated for its own position.
+ * out:   dev, fp32 [batch][n_q_heads][128].
+ * Query head h reads kv head h / (n_q_heads / n_kv_heads). Scores are
+ * softmax_scale * q . RoPE(k_n, n) (RoPE only when pre_rope; n is the 0-based
+ * absolute position); softmax_scale <= 0 selects 1/sqrt(128)
+ * (KVQuant notes Algorithm 1, attention part).
+ * Errors: KVQ_ERR_STATE if the layer holds no tokens.
+ */
+kvq_status kvq_decode_attn(kvq_cache cache, int layer, const void* q_f16, float* out,
+                           float softmax_scale, void* stream);
+
+/* Tokens currently held by a layer (host-side counter, no device access). */
+kvq_status kvq_cache_length(kvq_cache cache, int layer, int32_t* n_tokens);
+
+/* Forget the tokens of a layer (length = 0; device memory is not touched). */
+kvq_status kvq_cache_reset(kvq_cache cache, int layer);
+
+/*
+ * Number of decode splits per (sequence, kv head): 0 = automatic (default),
+ * otherwise 1..KVQ_MAX_SPLITS (capped to the number of 64-token half blocks).
+ */
+kvq_status kvq_set_decode_splits(kvq_cache cache, int splits);
+
+/*
+ * Byte range of one block record inside dev_buf. The record of block j of
+ * (layer, sequence b, kv head h) holds, each segment starting on a 16-byte
+ * boundary, the record padded to 256 bytes (T = 128 tokens, D = 128 channels,
+ * R = 16*bits bytes per 128 codes):
+ *   kc  key codes, token-major: 128 rows of R bytes, row t = channels 0..127
+ *   vc  value codes, channel-major in two token halves: [2][128][R/2],
+ *       row (half, c) = tokens 64*half .. 64*half+63 of channel c
+ *   ks  key statistics per channel: RTN/KVARN f32 s[128] then f32 m[128];
+ *       NUQ f32 z[128] then f32 h[128]; SYM_INT4 f16 s[128]
+ *   vs  value statistics: per token (RTN/KVARN s then m, NUQ z then h, f32);
+ *       SYM_INT4 per channel f16 s[128]
+ *   k1  KVARN only: f32 s1[128] per token;  v1: KVARN only: f32 s1[128] per channel
+ *   outliers (outliers_per_vec = k > 0):
+ *       key CSR by token:     f16 val[128k], u16 row_ptr[129], u8 channel[128k]
+ *       value CSC by channel: f16 val[128k], u16 col_ptr[129], u8 token[128k]
+ *       entries sorted by (row, column); val holds the original fp16 bits.
+ * Code packing of n codes: 4-bit byte j = code 2j | code 2j+1 << 4; 2-bit byte j
+ * = codes 4j..4j+3 at bits 2i; 3-bit = the low 2 bits of all n codes packed as
+ * 2-bit (n/4 bytes) then bit 2 of code 8j+i at bit i of byte j (n/8 bytes).
+ * Codes: RTN/KVARN q in 0..2^b-1 with x = q*s + m (KVARN: times s1);
+ * NUQ q indexes the codebook, x = C[q]*h + z; SYM_INT4 u = q + 8, x = (u-8)*s.
+ */
+kvq_status kvq_block_span(kvq_cache cache, int layer, int b, int kv_head, int block,
+                          size_t* offset, size_t* bytes);
+
+/* Byte range of the fp16 tail of (layer, b, kv head): K [128][128] then V [128][128]. */
+kvq_status kvq_tail_span(kvq_cache cache, int layer, int b, int kv_head, size_t* offset,
+                         size_t* bytes);
+
+/*
+ * Algorithmic bytes a decode call on this layer must move now: block records
+ * without padding, the fp16 tail rows, q, out, codebooks and the RoPE base rows
+ * of the blocks it reads.
+ */
+kvq_status kvq_decode_bytes(kvq_cache cache, int layer, size_t* bytes);
+
+/* Static text for a status code. */
+const char* kvq_strerror(kvq_status status);
+
+/* Description of the calling thread's last failure ("" if none). */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,186 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded inputs.
+
+Codes, scales and outlier lists are compared byte for byte (KVarN: the tolerance of
+its fp32 normalisation, see _kvq_helpers.compare_record); attention outputs to
+max |diff| <= 1e-3 * max |out| per (sequence, query head)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import synth
+from oracle import kvq_oracle as O
+from tests import _kvq_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def K():
+    import bit_kv_cache_quantize_amd as K
+    assert torch.cuda.is_available(), "a GPU is required"
+    return K
+
+
+def run_case(K, wl, chunks, splits=0, layer=0, check_records=True):
+    """Append the same inputs on both sides, compare every record and the tail, then decode."""
+    _say(f"case {wl.name} B={wl.batch} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} L={sum(chunks)} chunks={chunks}")
+    L = sum(chunks)
+    max_tokens = H.ceil128(L)
+    cache = K.KVCache(H.lib_cfg(wl, max_tokens))
+    oc = O.OracleCache(H.oracle_cfg(wl, max_tokens))
+    if wl.mode == synth.MODE_NUQ:
+        for (h, w), cb in H.codebooks(wl, layer).items():
+            cache.codebook_load(layer, h, w, cb)
+            oc.load_codebook(layer, h, w, cb)
+    pos = 0
+    for n in chunks:
+        k, v = H.host_kv(wl, layer, pos, n)
+        cache.append(layer, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        oc.append(layer, k, v)
+        pos += n
+    torch.cuda.synchronize()
+    assert cache.length(layer) == L
+    ocfg = oc.cfg
+    stats = H.RecordStats()
+    if check_records:
+        for b in range(wl.batch):
+            for h in range(wl.n_kv_heads):
+                u = b * wl.n_kv_heads + h
+                for j, blk in enumerate(oc.blocks[layer][u]):
+                    got = cache.block_bytes(layer, b, h, j).cpu().numpy()
+                    H.compare_record(got, blk, ocfg, stats, where=f"b{b} h{h} block {j}")
+                nt = L % 128
+                tail = cache.tail_bytes(layer, b, h).cpu().numpy().view(np.float16).reshape(2, 128, 128)
+                assert np.array_equal(tail[0, :nt], oc.tail_k[layer][u])
+                assert np.array_equal(tail[1, :nt], oc.tail_v[layer][u])
+        if wl.mode == synth.MODE_KVARN and stats.codes:
+            assert stats.diff <= 1e-4 * stats.codes, f"{stats.diff} of {stats.codes} codes differ"
+    q = H.host_q(wl, layer)
+    out = torch.empty((wl.batch, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
+    if splits:
+        cache.set_splits(splits)
+    cache.decode(layer, torch.from_numpy(q).cuda(), out)
+    torch.cuda.synchronize()
+    ref = oc.decode(layer, q)
+    worst = H.attention_close(out.cpu().numpy(), ref)
+    _say(f"  ok: worst attention error {worst:.2e} of the bar; KVarN code diffs {stats.diff}/{stats.codes}")
+    return cache, out, ref
+
+
+def small(name, **kw):
+    return synth.WORKLOADS[name].replace(**kw)
+
+
+CASES = {
+    "c1_full": (synth.WORKLOADS["c1_single_head_2k_rtn4"], [2048]),
+    "rtn2_rope_out1_g1": (small("c5_llama7b_1m_rtn2", n_layers=1, batch=2, n_q_heads=2, n_kv_heads=2), [300]),
+    "rtn3_out2_g2": (small("c1_single_head_2k_rtn4", bits=3, outliers_per_vec=2, batch=2, n_q_heads=4,
+                           n_kv_heads=2), [200, 100]),
+    "rtn4_rope_g4": (small("c1_single_head_2k_rtn4", pre_rope=1, batch=1, n_q_heads=8, n_kv_heads=2), [384]),
+    "nuq3_rope_out1_g1": (small("c2_llama7b_layer_32k_nuq3", n_q_heads=2, n_kv_heads=2, batch=2), [1, 299]),
+    "nuq2_out1_g4": (small("c2_llama7b_layer_32k_nuq3", bits=2, pre_rope=0, n_q_heads=8, n_kv_heads=2), [256]),
+    "nuq4_rope_out3_g8": (small("c2_llama7b_layer_32k_nuq3", bits=4, outliers_per_vec=3, n_q_heads=16,
+                                n_kv_heads=2), [129, 130]),
+    "kvarn2_g4": (small("c3_kvarn_gqa_b16_8k", batch=2, n_q_heads=8, n_kv_heads=2), [128, 128, 128, 50]),
+    "kvarn3_g1": (small("c3_kvarn_gqa_b16_8k", bits=3, batch=1, n_q_heads=2, n_kv_heads=2), [300]),
+    "kvarn4_g2_iters3": (small("c3_kvarn_gqa_b16_8k", bits=4, varn_iters=3, batch=1, n_q_heads=4, n_kv_heads=2),
+                         [70, 200]),
+    "sym4_g4": (small("c4_blog_int4_32l_b32_32k", n_layers=1, batch=2, n_q_heads=8, n_kv_heads=2), [512]),
+    "sym4_rope_out1_g1": (small("c4_blog_int4_32l_b32_32k", n_layers=1, batch=1, n_q_heads=2, n_kv_heads=2,
+                                pre_rope=1, outliers_per_vec=1), [257]),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_parity_modes(K, case):
+    wl, chunks = CASES[case]
+    run_case(K, wl, chunks)
+
+
+@pytest.mark.parametrize("L", [1, 2, 64, 65, 127, 128, 129, 255, 256, 257])
+def test_parity_ragged_lengths(K, L):
+    wl = small("c2_llama7b_layer_32k_nuq3", n_q_heads=4, n_kv_heads=2, batch=1)
+    run_case(K, wl, [L])
+
+
+@pytest.mark.parametrize("L", [1, 127, 129])
+def test_parity_ragged_kvarn(K, L):
+    wl = small("c3_kvarn_gqa_b16_8k", batch=1, n_q_heads=8, n_kv_heads=2)
+    run_case(K, wl, [L])
+
+
+def test_single_token_returns_its_value(K):
+    wl = small("c5_llama7b_1m_rtn2", n_layers=1, n_q_heads=2, n_kv_heads=1)
+    _, out, _ = run_case(K, wl, [1])
+    k, v = H.host_kv(wl, 0, 0, 1)
+    assert np.array_equal(out.cpu().numpy()[0, 0], v[0, 0, 0].astype(np.float32))
+
+
+def test_split_count_invariance(K):
+    wl = small("c1_single_head_2k_rtn4", batch=2, n_q_heads=8, n_kv_heads=2)
+    outs = []
+    for s in (1, 2, 3, 5, 0):
+        _, out, ref = run_case(K, wl, [2048 + 77], splits=s, check_records=(s == 1))
+        outs.append(out.cpu().numpy())
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 1e-5 * np.max(np.abs(outs[0]))
+
+
+def test_determinism(K):
+    wl = small("c2_llama7b_layer_32k_nuq3", n_q_heads=4, n_kv_heads=2, batch=2)
+    a, oa, _ = run_case(K, wl, [700])
+    b, ob, _ = run_case(K, wl, [700])
+    for j in range(5):
+        assert torch.equal(a.block_bytes(0, 1, 1, j), b.block_bytes(0, 1, 1, j))
+    assert torch.equal(oa, ob)
+    q = torch.from_numpy(H.host_q(wl, 0)).cuda()
+    o2 = torch.empty_like(oa)
+    a.decode(0, q, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, oa)
+
+
+def test_device_generator_matches_host(K):
+    import synth.device as SD
+    wl = synth.WORKLOADS["c2_llama7b_layer_32k_nuq3"]
+    gen = SD.DeviceGenerator(wl)
+    k = torch.empty((1, 32, 300, 128), dtype=torch.float16, device="cuda")
+    v = torch.empty_like(k)
+    gen.fill_kv(k, v, 0, 1000, 300)
+    q = torch.empty((1, 32, 128), dtype=torch.float16, device="cuda")
+    gen.fill_q(q, 0)
+    torch.cuda.synchronize()
+    for h in (0, 7, 31):
+        assert np.array_equal(k[0, h].cpu().numpy(), synth.gen_k(wl, 0, 0, h, 1000, 300))
+        assert np.array_equal(v[0, h].cpu().numpy(), synth.gen_v(wl, 0, 0, h, 1000, 300))
+        assert np.array_equal(q[0, h].cpu().numpy(), synth.gen_q(wl, 0, 0, h))
+
+
+def test_errors_on_device(K):
+    wl = small("c1_single_head_2k_rtn4")
+    cache = K.KVCache(H.lib_cfg(wl, 256))
+    q = torch.zeros((1, 1, 128), dtype=torch.float16, device="cuda")
+    out = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(K.KvqError) as e:
+        cache.decode(0, q, out)
+    assert e.value.status == K.KVQ_ERR_STATE
+    k = torch.zeros((1, 1, 257, 128), dtype=torch.float16, device="cuda")
+    with pytest.raises(K.KvqError) as e:
+        cache.append(0, k, k)
+    assert e.value.status == K.KVQ_ERR_CAPACITY
+    assert cache.length(0) == 0
+    # degenerate vectors: a constant block quantizes to code 0 and decodes exactly
+    kk = torch.full((1, 1, 128, 128), 0.75, dtype=torch.float16, device="cuda")
+    cache.append(0, kk, kk)
+    cache.decode(0, torch.ones((1, 1, 128), dtype=torch.float16, device="cuda"), out)
+    torch.cuda.synchronize()
+    assert torch.allclose(out, torch.full_like(out, 0.75), rtol=0, atol=1e-6)
