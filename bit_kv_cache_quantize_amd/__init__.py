@@ -9,6 +9,12 @@ from __future__ import annotations
 import ctypes
 import os
 
+# torch brings its own HIP runtime (soname libamdhip64.so.7); loading it before
+# libkvq.so makes the library bind to that same runtime, so device memory and
+# streams from torch are valid for the kernels. Loaded the other way round, the
+# process would hold two HIP runtimes.
+import torch  # noqa: F401
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 

@@ -83,14 +83,16 @@ struct kvq_cache_s {
   std::vector<float> cb_host;       // [layer][kv_head][2][16]
   std::vector<float> rope_host;     // base table then offset table
   int splits_override = 0;
+  size_t off_counters = 0;
+  bool counters_ready = false;      // decode split counters cleared on the device
 };
 
 namespace {
 
 struct Regions {
   int max_blocks;
-  size_t layer_rec, rec, layer_tail, tail, cb, rope_base, rope_off, work, total;
-  size_t off_rec, off_tail, off_cb, off_rope_base, off_rope_off, off_work;
+  size_t layer_rec, rec, layer_tail, tail, cb, rope_base, rope_off, work, counters, total;
+  size_t off_rec, off_tail, off_cb, off_rope_base, off_rope_off, off_work, off_counters;
 };
 
 kvq_status validate_config(const kvq_config* c) {
@@ -136,6 +138,7 @@ Regions regions(const kvq_config* c) {
   r.rope_base = c->pre_rope ? (size_t)(r.max_blocks + 1) * 64 * 2 * sizeof(float) : 0;
   r.rope_off = c->pre_rope ? (size_t)128 * 64 * 2 * sizeof(float) : 0;
   r.work = (size_t)c->batch * c->n_q_heads * KVQ_MAX_SPLITS * kvq::kPartStride * sizeof(float);
+  r.counters = (size_t)c->batch * c->n_kv_heads * sizeof(unsigned);
   size_t pos = 0;
   auto place = [&](size_t size) { pos = align_up(pos, 256); const size_t at = pos; pos += size; return at; };
   r.off_rec = place(r.rec);
@@ -144,6 +147,7 @@ Regions regions(const kvq_config* c) {
   r.off_rope_base = place(r.rope_base);
   r.off_rope_off = place(r.rope_off);
   r.off_work = place(r.work);
+  r.off_counters = place(r.counters);
   r.total = align_up(pos, 256);
   return r;
 }
@@ -197,6 +201,7 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_buf, size_t bytes, vo
   c->off_rope_base = r.off_rope_base;
   c->off_rope_off = r.off_rope_off;
   c->off_work = r.off_work;
+  c->off_counters = r.off_counters;
   c->len.assign(cfg->n_layers, 0);
   c->cb_loaded.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2, 0);
   c->cb_host.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2 * 16, 0.f);
@@ -347,6 +352,13 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
     splits = (nblk + bps - 1) / bps;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned* counters = reinterpret_cast<unsigned*>(c->base + c->off_counters);
+  if (!c->counters_ready) {
+    // the split counters return to zero at the end of every decode; clear them once (a kernel, not a memset)
+    st = hip_check(kvq::launch_zero(counters, (size_t)units, s), "clear decode counters");
+    if (st != KVQ_OK) return st;
+    c->counters_ready = true;
+  }
   kvq::DecodeArgs a{};
   a.lay = c->lay;
   a.k_out = cfg.outliers_per_vec;
@@ -357,6 +369,8 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
   a.rope_off = reinterpret_cast<const float*>(c->base + c->off_rope_off);
   a.q = static_cast<const __half*>(q_f16);
   a.part = reinterpret_cast<float*>(c->base + c->off_work);
+  a.counters = counters;
+  a.out = out;
   a.Hkv = cfg.n_kv_heads;
   a.Hq = cfg.n_q_heads;
   a.max_blocks = c->max_blocks;
@@ -368,9 +382,6 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
   a.scale_log2 = scale * 1.4426950408889634f;
   st = hip_check(kvq::launch_decode(cfg.mode, cfg.bits, cfg.n_q_heads / cfg.n_kv_heads, cfg.pre_rope, a, cfg.batch, s),
                  "launch decode");
-  if (st != KVQ_OK) return st;
-  kvq::CombineArgs ca{a.part, out, cfg.n_q_heads, splits};
-  st = hip_check(kvq::launch_combine(ca, cfg.batch, s), "launch split combine");
   if (st != KVQ_OK) return st;
   return ok();
 }

@@ -20,8 +20,10 @@
 //   * P.V: lane = channel pair, 64 tokens of a channel-major half-row; the
 //     probabilities are broadcast with v_readlane.
 //   * the four wave states are merged in LDS; KVarN returns to the original
-//     domain with one Hadamard rotation of the merged output; a second kernel
-//     merges the splits with the log-sum-exp rule.
+//     domain with one Hadamard rotation of the merged output; the split's
+//     partial (m, l, o) goes to the workspace, and the last split of a
+//     (sequence, kv head) to finish merges all of them (log-sum-exp rule) and
+//     writes the output, so one decode call is one kernel launch.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -523,22 +525,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       part[1] = L;
     }
   }
+
+  // ---- the last split of this (sequence, kv head) to finish merges all splits
+  // (log-sum-exp rule) and writes the output; it then clears the counter.
+  __shared__ int s_last;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  const size_t unit = (size_t)b * a.Hkv + kvh;
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (unsigned)(a.splits - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int i = tid; i < G * 128; i += kThreads) {
+    const int h = i >> 7, c = i & 127;
+    const size_t row = (size_t)b * a.Hq + (size_t)kvh * G + h;
+    const float* part = a.part + row * a.splits * kPartStride;
+    float M = -INFINITY;
+    for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, part[sp * kPartStride]);
+    float L = 0.f, o = 0.f;
+    for (int sp = 0; sp < a.splits; ++sp) {
+      const float m = part[sp * kPartStride];
+      if (m == -INFINITY) continue;
+      const float wgt = exp2f(m - M);
+      L = fmaf(wgt, part[sp * kPartStride + 1], L);
+      o = fmaf(wgt, part[sp * kPartStride + 2 + c], o);
+    }
+    a.out[row * kD + c] = o / L;
+  }
+  if (tid == 0) __hip_atomic_store(a.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
-  const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-  const float* part = a.part + ((size_t)b * a.Hq + hq) * a.splits * kPartStride;
-  float M = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, part[s * kPartStride]);
-  float L = 0.f, o = 0.f;
-  for (int s = 0; s < a.splits; ++s) {
-    const float m = part[s * kPartStride];
-    if (m == -INFINITY) continue;
-    const float wgt = exp2f(m - M);
-    L = fmaf(wgt, part[s * kPartStride + 1], L);
-    o = fmaf(wgt, part[s * kPartStride + 2 + c], o);
-  }
-  a.out[((size_t)b * a.Hq + hq) * kD + c] = o / L;
+__global__ void zero_kernel(unsigned* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 template <int MODE, int BITS, int G, bool ROPE>
@@ -589,8 +611,8 @@ hipError_t launch_decode(int mode, int bits, int group, int rope, const DecodeAr
   }
 }
 
-hipError_t launch_combine(const CombineArgs& a, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.Hq, batch), dim3(128), 0, s, a);
+hipError_t launch_zero(unsigned* p, size_t n, hipStream_t s) {
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 
