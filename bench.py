@@ -92,6 +92,8 @@ class Bench:
                     v = torch.empty_like(k)
                     self.gen.fill_kv(k, v, layer, t0, n)
                     self.inputs[(layer, t0)] = (k, v)
+            for copy in range(self.copies):      # both copies hold the context before the first step
+                self.append_all(copy)
         else:
             self._build_streamed()
         torch.cuda.synchronize()
