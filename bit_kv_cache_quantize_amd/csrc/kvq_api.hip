@@ -83,16 +83,14 @@ struct kvq_cache_s {
   std::vector<float> cb_host;       // [layer][kv_head][2][16]
   std::vector<float> rope_host;     // base table then offset table
   int splits_override = 0;
-  size_t off_counters = 0;
-  bool counters_ready = false;      // decode split counters cleared on the device
 };
 
 namespace {
 
 struct Regions {
   int max_blocks;
-  size_t layer_rec, rec, layer_tail, tail, cb, rope_base, rope_off, work, counters, total;
-  size_t off_rec, off_tail, off_cb, off_rope_base, off_rope_off, off_work, off_counters;
+  size_t layer_rec, rec, layer_tail, tail, cb, rope_base, rope_off, work, total;
+  size_t off_rec, off_tail, off_cb, off_rope_base, off_rope_off, off_work;
 };
 
 kvq_status validate_config(const kvq_config* c) {
@@ -136,9 +134,8 @@ Regions regions(const kvq_config* c) {
   r.tail = r.layer_tail * c->n_layers;
   r.cb = c->mode == KVQ_MODE_NUQ ? (size_t)c->n_layers * c->n_kv_heads * 2 * 16 * sizeof(float) : 0;
   r.rope_base = c->pre_rope ? (size_t)(r.max_blocks + 1) * 64 * 2 * sizeof(float) : 0;
-  r.rope_off = c->pre_rope ? (size_t)128 * 64 * 2 * sizeof(float) : 0;
+  r.rope_off = c->pre_rope ? ((size_t)128 * 64 * 2 + 64) * sizeof(float) : 0;   // offsets, then theta_i
   r.work = (size_t)c->batch * c->n_q_heads * KVQ_MAX_SPLITS * kvq::kPartStride * sizeof(float);
-  r.counters = (size_t)c->batch * c->n_kv_heads * sizeof(unsigned);
   size_t pos = 0;
   auto place = [&](size_t size) { pos = align_up(pos, 256); const size_t at = pos; pos += size; return at; };
   r.off_rec = place(r.rec);
@@ -147,7 +144,6 @@ Regions regions(const kvq_config* c) {
   r.off_rope_base = place(r.rope_base);
   r.off_rope_off = place(r.rope_off);
   r.off_work = place(r.work);
-  r.off_counters = place(r.counters);
   r.total = align_up(pos, 256);
   return r;
 }
@@ -201,7 +197,6 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_buf, size_t bytes, vo
   c->off_rope_base = r.off_rope_base;
   c->off_rope_off = r.off_rope_off;
   c->off_work = r.off_work;
-  c->off_counters = r.off_counters;
   c->len.assign(cfg->n_layers, 0);
   c->cb_loaded.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2, 0);
   c->cb_host.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2 * 16, 0.f);
@@ -210,7 +205,7 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_buf, size_t bytes, vo
     // RoPE angles n * theta_i, theta_i = theta^(-2i/128), evaluated in double precision:
     // base rows for n = 128 * block and offset rows for n = 0..127 (KVQuant notes 1.3)
     const int nb = r.max_blocks + 1;
-    c->rope_host.resize((size_t)nb * 128 + 128 * 128);
+    c->rope_host.resize((size_t)nb * 128 + 128 * 128 + 64);
     for (int i = 0; i < 64; ++i) {
       const double th = std::pow((double)cfg->rope_theta, -2.0 * i / 128.0);
       for (int blk = 0; blk < nb; ++blk) {
@@ -218,17 +213,18 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_buf, size_t bytes, vo
         c->rope_host[((size_t)blk * 64 + i) * 2] = (float)std::cos(ang);
         c->rope_host[((size_t)blk * 64 + i) * 2 + 1] = (float)std::sin(ang);
       }
+      c->rope_host[(size_t)nb * 128 + 128 * 128 + i] = (float)th;
       for (int jj = 0; jj < 128; ++jj) {
         const double ang = (double)jj * th;
-        c->rope_host[(size_t)nb * 128 + ((size_t)jj * 64 + i) * 2] = (float)std::cos(ang);
-        c->rope_host[(size_t)nb * 128 + ((size_t)jj * 64 + i) * 2 + 1] = (float)std::sin(ang);
+        c->rope_host[(size_t)nb * 128 + ((size_t)i * 128 + jj) * 2] = (float)std::cos(ang);
+        c->rope_host[(size_t)nb * 128 + ((size_t)i * 128 + jj) * 2 + 1] = (float)std::sin(ang);
       }
     }
     st = hip_check(hipMemcpyAsync(c->base + c->off_rope_base, c->rope_host.data(), (size_t)nb * 128 * sizeof(float),
                                   hipMemcpyHostToDevice, s), "upload RoPE base table");
     if (st == KVQ_OK)
       st = hip_check(hipMemcpyAsync(c->base + c->off_rope_off, c->rope_host.data() + (size_t)nb * 128,
-                                    128 * 128 * sizeof(float), hipMemcpyHostToDevice, s), "upload RoPE offset table");
+                                    (128 * 128 + 64) * sizeof(float), hipMemcpyHostToDevice, s), "upload RoPE offset table");
     if (st == KVQ_OK) st = hip_check(hipStreamSynchronize(s), "synchronize after init");
     if (st != KVQ_OK) {
       delete c;
@@ -343,22 +339,17 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
     if (c->splits_override > 0) {
       splits = std::min(c->splits_override, nblk);
     } else {
-      const int target_wgs = 2048;                 // 8 workgroups per CU on 256 CUs
+      // about two resident workgroups per CU (512 on 256 CUs), each streaming at least
+      // 8 blocks, so that per-workgroup set-up and the split merge stay small
+      const int target_wgs = 512;
       splits = (target_wgs + units - 1) / units;
-      splits = std::min(splits, (nblk + 1) / 2);   // at least two blocks (four halves) per split
+      splits = std::min(splits, (nblk + 7) / 8);
       splits = std::max(1, std::min(splits, KVQ_MAX_SPLITS));
     }
     bps = (nblk + splits - 1) / splits;
     splits = (nblk + bps - 1) / bps;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  unsigned* counters = reinterpret_cast<unsigned*>(c->base + c->off_counters);
-  if (!c->counters_ready) {
-    // the split counters return to zero at the end of every decode; clear them once (a kernel, not a memset)
-    st = hip_check(kvq::launch_zero(counters, (size_t)units, s), "clear decode counters");
-    if (st != KVQ_OK) return st;
-    c->counters_ready = true;
-  }
   kvq::DecodeArgs a{};
   a.lay = c->lay;
   a.k_out = cfg.outliers_per_vec;
@@ -369,7 +360,6 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
   a.rope_off = reinterpret_cast<const float*>(c->base + c->off_rope_off);
   a.q = static_cast<const __half*>(q_f16);
   a.part = reinterpret_cast<float*>(c->base + c->off_work);
-  a.counters = counters;
   a.out = out;
   a.Hkv = cfg.n_kv_heads;
   a.Hq = cfg.n_q_heads;
@@ -380,9 +370,18 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
   a.blocks_per_split = bps;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
   a.scale_log2 = scale * 1.4426950408889634f;
+  if (cfg.outliers_per_vec > 0) {
+    // per-wave staging for the sparse fix-ups: outlier segments, key S/M, value S/M of a half, RoPE base row
+    const uint32_t blob = c->lay.vo_idx + 128u * cfg.outliers_per_vec - c->lay.ko_val;
+    a.wave_lds = (int)(((blob + 15u) & ~15u) + 1024u + 512u + 512u);
+  }
   st = hip_check(kvq::launch_decode(cfg.mode, cfg.bits, cfg.n_q_heads / cfg.n_kv_heads, cfg.pre_rope, a, cfg.batch, s),
                  "launch decode");
   if (st != KVQ_OK) return st;
+  if (splits > 1) {
+    st = hip_check(kvq::launch_combine(a.part, out, cfg.n_q_heads, splits, cfg.batch, s), "launch split combine");
+    if (st != KVQ_OK) return st;
+  }
   return ok();
 }
 

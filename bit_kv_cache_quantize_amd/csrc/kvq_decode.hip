@@ -21,9 +21,11 @@
 //     probabilities are broadcast with v_readlane.
 //   * the four wave states are merged in LDS; KVarN returns to the original
 //     domain with one Hadamard rotation of the merged output; the split's
-//     partial (m, l, o) goes to the workspace, and the last split of a
-//     (sequence, kv head) to finish merges all of them (log-sum-exp rule) and
-//     writes the output, so one decode call is one kernel launch.
+//     partial (m, l, o) goes to the workspace and a small second kernel merges
+//     the splits (log-sum-exp rule); with a single split the workgroup writes
+//     the output itself. (Merging inside the kernel through a completion
+//     counter needs an agent-scope release per workgroup, i.e. an L2
+//     write-back per workgroup, which costs far more than a second launch.)
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -77,20 +79,6 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t* w, int i) {
   }
 }
 
-// code of element i of a packed row in memory (used for the sparse outlier fix-ups)
-template <int BITS, int N>
-__device__ __forceinline__ uint32_t code_mem(const uint8_t* row, int i) {
-  if constexpr (BITS == 4) {
-    return (row[i >> 1] >> (4 * (i & 1))) & 15u;
-  } else if constexpr (BITS == 2) {
-    return (row[i >> 2] >> (2 * (i & 3))) & 3u;
-  } else {
-    const uint32_t lo = (row[i >> 2] >> (2 * (i & 3))) & 3u;
-    const uint32_t hi = (row[N / 4 + (i >> 3)] >> (i & 7)) & 1u;
-    return lo | (hi << 2);
-  }
-}
-
 template <int NBYTES>
 __device__ __forceinline__ void load_row(uint32_t* w, const uint8_t* p) {
   static_assert(NBYTES % 8 == 0, "row bytes");
@@ -109,23 +97,69 @@ __device__ __forceinline__ void load_row(uint32_t* w, const uint8_t* p) {
   }
 }
 
+// code of element i (runtime) of a packed row held in registers: selects the word
+// without dynamic register indexing (sparse outlier fix-ups only)
+template <int BITS, int N>
+__device__ __forceinline__ uint32_t code_sel(const uint32_t* w, int i) {
+  constexpr int NW = N * BITS / 32;
+  if constexpr (BITS == 3) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < N / 16; ++k) lo = (k == (i >> 4)) ? w[k] : lo;
+#pragma unroll
+    for (int k = 0; k < N / 32; ++k) hi = (k == (i >> 5)) ? w[N / 16 + k] : hi;
+    return ((lo >> (2 * (i & 15))) & 3u) | (((hi >> (i & 31)) & 1u) << 2);
+  } else {
+    constexpr int PER = 32 / BITS;
+    uint32_t x = 0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) x = (k == i / PER) ? w[k] : x;
+    return (x >> (BITS * (i % PER))) & ((1u << BITS) - 1u);
+  }
+}
+
+// Per-wave LDS staging used by the sparse outlier fix-ups of one half block.
+struct OutlierLds {
+  uint8_t* blob;   // the record's outlier segments, from ko_val to the end of vo_idx
+  float* kS;       // [128] key scale (S) per channel
+  float* kM;       // [128] key offset (M) per channel
+  float* vS;       // [64] value scale per token of this half
+  float* vM;       // [64]
+  float2* rb;      // [64] RoPE base (cos, sin) of the block
+};
+
 template <int MODE, int BITS, int G, bool ROPE>
 struct Decoder {
   static constexpr int R = 16 * BITS;      // bytes per 128 codes
   static constexpr int RH = R / 2;         // bytes per 64 codes
+  static constexpr int NOB = 3;            // prefetched 16-byte chunks of the outlier blob per lane
+
+  // Everything one half block needs, loaded one half block ahead.
+  struct Buf {
+    uint32_t kw[R / 4];     // key row of token j
+    uint32_t vw[R / 4];     // value half-rows of channels 2*lane, 2*lane+1
+    float2 ks, km;          // key (S, M) of channels 2*lane, 2*lane+1
+    float2 tst;             // value (S, M) of token j; SYM: value scales of channels 2*lane, 2*lane+1
+    float s1t;              // KVarN s1 of token j
+    float2 s1c;             // KVarN s1 of channels 2*lane, 2*lane+1
+    float2 rb;              // RoPE (cos, sin) of the block base for pair lane
+  };
 
   const DecodeArgs& a;
   const int lane, w, par, j;
   const float* lut;                        // NUQ: [0,16) keys, [16,32) values
   float* pbuf;                             // this wave's probabilities [G][64]
   const float* qs;                         // query, original domain [G][128]
+  const float* theta;                      // RoPE theta_i [64] (LDS)
+  OutlierLds ol;
+  int ob_bytes, ob_chunks;
   float qx[G], qy[G];                      // query pair (2*lane, 2*lane+1), rotated for KVarN
   float m_run[G], l_run[G], pm[G], acc0[G], acc1[G];
 
   __device__ Decoder(const DecodeArgs& args, int lane_, int w_, const float* lut_, float* pbuf_,
-                     const float* qs_)
+                     const float* qs_, const float* theta_, uint8_t* wlds)
       : a(args), lane(lane_), w(w_), par(w_ & 1), j(64 * (w_ & 1) + lane_), lut(lut_), pbuf(pbuf_),
-        qs(qs_) {
+        qs(qs_), theta(theta_) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       qx[h] = qs[h * 128 + 2 * lane];
@@ -133,6 +167,23 @@ struct Decoder {
       if constexpr (MODE == KVARN) fwht_wave(qx[h], qy[h], lane);
       m_run[h] = -INFINITY; l_run[h] = 0.f; pm[h] = 0.f; acc0[h] = 0.f; acc1[h] = 0.f;
     }
+    ob_bytes = 0;
+    ob_chunks = 0;
+    if (a.k_out > 0) {
+      ob_bytes = (int)(a.lay.vo_idx + 128u * a.k_out - a.lay.ko_val);
+      ob_chunks = (ob_bytes + 15) / 16;
+      const int blob = (ob_bytes + 15) & ~15;
+      ol.blob = wlds;
+      ol.kS = reinterpret_cast<float*>(wlds + blob);
+      ol.kM = ol.kS + 128;
+      ol.vS = ol.kM + 128;
+      ol.vM = ol.vS + 64;
+      ol.rb = reinterpret_cast<float2*>(ol.vM + 64);
+    }
+  }
+
+  __device__ __forceinline__ const uint8_t* record(int blk) const {
+    return a.rec + ((size_t)(blockIdx.z * a.Hkv + blockIdx.y) * a.max_blocks + blk) * (size_t)a.lay.rec_bytes;
   }
 
   __device__ __forceinline__ float kval(uint32_t code) const {
@@ -144,18 +195,32 @@ struct Decoder {
     else return (float)code;
   }
 
-  // per-channel key statistics of channel c as (S, M): x = val(code) * S + M
-  __device__ __forceinline__ void kstat(const uint8_t* rec, int c, float& S, float& M) const {
+  // Issue every load of one half block (no use of the results here).
+  __device__ __forceinline__ void fetch(Buf& B, int blk) const {
+    const uint8_t* rec = record(blk);
+    load_row<R>(B.kw, rec + a.lay.kc + (size_t)j * R);
+    load_row<R>(B.vw, rec + a.lay.vc + (size_t)par * (128 * RH) + (size_t)lane * R);   // rows 2*lane, 2*lane+1
     if constexpr (MODE == SYM) {
-      S = __half2float(reinterpret_cast<const __half*>(rec + a.lay.ks)[c]);
-      M = -8.f * S;
+      const __half2 k2 = reinterpret_cast<const __half2*>(rec + a.lay.ks)[lane];
+      B.ks = __half22float2(k2);
+      B.km = make_float2(-8.f * B.ks.x, -8.f * B.ks.y);
+      B.tst = __half22float2(reinterpret_cast<const __half2*>(rec + a.lay.vs)[lane]);
     } else if constexpr (MODE == NUQ) {
-      M = reinterpret_cast<const float*>(rec + a.lay.ks)[c];
-      S = reinterpret_cast<const float*>(rec + a.lay.ks)[128 + c];
+      B.km = reinterpret_cast<const float2*>(rec + a.lay.ks)[lane];          // z
+      B.ks = reinterpret_cast<const float2*>(rec + a.lay.ks + 512)[lane];    // h
+      B.tst.x = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + j];     // h of token j
+      B.tst.y = reinterpret_cast<const float*>(rec + a.lay.vs)[j];           // z of token j
     } else {
-      S = reinterpret_cast<const float*>(rec + a.lay.ks)[c];
-      M = reinterpret_cast<const float*>(rec + a.lay.ks)[128 + c];
+      B.ks = reinterpret_cast<const float2*>(rec + a.lay.ks)[lane];
+      B.km = reinterpret_cast<const float2*>(rec + a.lay.ks + 512)[lane];
+      B.tst.x = reinterpret_cast<const float*>(rec + a.lay.vs)[j];
+      B.tst.y = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + j];
     }
+    if constexpr (MODE == KVARN) {
+      B.s1t = reinterpret_cast<const float*>(rec + a.lay.k1)[j];
+      B.s1c = reinterpret_cast<const float2*>(rec + a.lay.v1)[lane];
+    }
+    if constexpr (ROPE) B.rb = reinterpret_cast<const float2*>(a.rope_base)[(size_t)blk * 64 + lane];
   }
 
   // Online-softmax update with this lane's log2-domain scores sl[h]; returns p[h].
@@ -173,81 +238,131 @@ struct Decoder {
     }
   }
 
-  // One 64-token half (parity par) of block blk.
-  __device__ void half_block(int blk, const float (&rc)[64], const float (&rs)[64]) {
-    const uint8_t* rec = a.rec + ((size_t)(blockIdx.z * a.Hkv + blockIdx.y) * a.max_blocks + blk) *
-                                     (size_t)a.lay.rec_bytes;
+  __device__ __forceinline__ void wave_sync() const {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // Stage the outlier lists and the statistics the fix-ups read into this wave's LDS.
+  // o0..o2: blob chunks lane, lane+64, lane+128 (indices clamped to the blob), loaded
+  // at the start of the half block so that their latency hides behind the q.K loop.
+  __device__ __forceinline__ void stage_outliers(const Buf& B, const uint8_t* rec, const uint4& o0,
+                                                 const uint4& o1, const uint4& o2) {
+    if (ob_chunks <= NOB * 64) {
+      uint4* dst = reinterpret_cast<uint4*>(ol.blob);
+      if (lane < ob_chunks) dst[lane] = o0;
+      if (lane + 64 < ob_chunks) dst[lane + 64] = o1;
+      if (lane + 128 < ob_chunks) dst[lane + 128] = o2;
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(rec + a.lay.ko_val);
+      uint4* dst = reinterpret_cast<uint4*>(ol.blob);
+      for (int k = lane; k < ob_chunks; k += 64) dst[k] = src[k];
+    }
+    ol.kS[2 * lane] = B.ks.x; ol.kS[2 * lane + 1] = B.ks.y;
+    ol.kM[2 * lane] = B.km.x; ol.kM[2 * lane + 1] = B.km.y;
+    if constexpr (MODE != SYM) { ol.vS[lane] = B.tst.x; ol.vM[lane] = B.tst.y; }
+    if constexpr (ROPE) ol.rb[lane] = B.rb;
+    wave_sync();
+  }
+
+  // One 64-token half (parity par) of block blk whose loads are in B.
+  __device__ __forceinline__ void process(const Buf& B, int blk, const float (&rc)[64], const float (&rs)[64]) {
+    const uint8_t* rec = record(blk);
+    const bool outl = MODE != KVARN && a.k_out > 0;
+    uint4 ob0, ob1, ob2;
+    if (outl) {
+      const uint4* src = reinterpret_cast<const uint4*>(rec + a.lay.ko_val);
+      const int last = ob_chunks - 1;
+      ob0 = src[min(lane, last)];
+      ob1 = src[min(lane + 64, last)];
+      ob2 = src[min(lane + 128, last)];
+    }
+
     // ---- q . K for token j
-    uint32_t kw[R / 4];
-    load_row<R>(kw, rec + a.lay.kc + (size_t)j * R);
-    float Sx, Sy, Mx, My;
-    kstat(rec, 2 * lane, Sx, Mx);
-    kstat(rec, 2 * lane + 1, Sy, My);
     float sc[G];
     if constexpr (!ROPE) {
       float QSx[G], QSy[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        QSx[h] = qx[h] * Sx;
-        QSy[h] = qy[h] * Sy;
-        sc[h] = wave_sum(fmaf(qx[h], Mx, qy[h] * My));   // sum_c q_c * M_c
+        QSx[h] = qx[h] * B.ks.x;
+        QSy[h] = qy[h] * B.ks.y;
+        sc[h] = wave_sum(fmaf(qx[h], B.km.x, qy[h] * B.km.y));   // sum_c q_c * M_c
       }
 #pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const float vx = kval(code_at<BITS, 128>(kw, 2 * i));
-        const float vy = kval(code_at<BITS, 128>(kw, 2 * i + 1));
+      for (int i0 = 0; i0 < 64; i0 += 8) {
+        float vx[8], vy[8];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          sc[h] = fmaf(vx, readlane_f(QSx[h], i), sc[h]);
-          sc[h] = fmaf(vy, readlane_f(QSy[h], i), sc[h]);
+        for (int i = 0; i < 8; ++i) {
+          vx[i] = kval(code_at<BITS, 128>(B.kw, 2 * (i0 + i)));
+          vy[i] = kval(code_at<BITS, 128>(B.kw, 2 * (i0 + i) + 1));
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            sc[h] = fmaf(vx[i], readlane_f(QSx[h], i0 + i), sc[h]);
+            sc[h] = fmaf(vy[i], readlane_f(QSy[h], i0 + i), sc[h]);
+          }
       }
     } else {
-      // rotate the query pair back by the block base angle n0*theta_i (angle addition)
-      const float2 cs0 = reinterpret_cast<const float2*>(a.rope_base)[(size_t)blk * 64 + lane];
+      // the query pair rotated back by the block base angle n0*theta_i, folded with the
+      // channel statistics: U = P1 vx + P2 vy + P3, W = P4 vx + P5 vy + P6,
+      // score += cos(j theta_i) U + sin(j theta_i) W
       float P1[G], P2[G], P3[G], P4[G], P5[G], P6[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float al = fmaf(qx[h], cs0.x, qy[h] * cs0.y);
-        const float be = fmaf(qy[h], cs0.x, -qx[h] * cs0.y);
-        P1[h] = al * Sx; P2[h] = be * Sy; P3[h] = fmaf(al, Mx, be * My);
-        P4[h] = be * Sx; P5[h] = -al * Sy; P6[h] = fmaf(be, Mx, -al * My);
+        const float al = fmaf(qx[h], B.rb.x, qy[h] * B.rb.y);
+        const float be = fmaf(qy[h], B.rb.x, -qx[h] * B.rb.y);
+        P1[h] = al * B.ks.x; P2[h] = be * B.ks.y; P3[h] = fmaf(al, B.km.x, be * B.km.y);
+        P4[h] = be * B.ks.x; P5[h] = -al * B.ks.y; P6[h] = fmaf(be, B.km.x, -al * B.km.y);
         sc[h] = 0.f;
       }
 #pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const float vx = kval(code_at<BITS, 128>(kw, 2 * i));
-        const float vy = kval(code_at<BITS, 128>(kw, 2 * i + 1));
+      for (int i0 = 0; i0 < 64; i0 += 8) {
+        float vx[8], vy[8];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float U = fmaf(vx, readlane_f(P1[h], i), fmaf(vy, readlane_f(P2[h], i), readlane_f(P3[h], i)));
-          const float W = fmaf(vx, readlane_f(P4[h], i), fmaf(vy, readlane_f(P5[h], i), readlane_f(P6[h], i)));
-          sc[h] = fmaf(rc[i], U, fmaf(rs[i], W, sc[h]));
+        for (int i = 0; i < 8; ++i) {
+          vx[i] = kval(code_at<BITS, 128>(B.kw, 2 * (i0 + i)));
+          vy[i] = kval(code_at<BITS, 128>(B.kw, 2 * (i0 + i) + 1));
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const int ii = i0 + i;
+            const float U = fmaf(vx[i], readlane_f(P1[h], ii), fmaf(vy[i], readlane_f(P2[h], ii), readlane_f(P3[h], ii)));
+            const float W = fmaf(vx[i], readlane_f(P4[h], ii), fmaf(vy[i], readlane_f(P5[h], ii), readlane_f(P6[h], ii)));
+            sc[h] = fmaf(rc[ii], U, fmaf(rs[ii], W, sc[h]));
+          }
       }
     }
     if constexpr (MODE != KVARN) {
-      if (a.k_out > 0) {
-        // key outliers of row j (CSR): replace the dense value by the fp16 one
-        const uint16_t* ptr = reinterpret_cast<const uint16_t*>(rec + a.lay.ko_ptr);
-        const uint8_t* idx = rec + a.lay.ko_idx;
-        const __half* val = reinterpret_cast<const __half*>(rec + a.lay.ko_val);
+      if (outl) {
+        stage_outliers(B, rec, ob0, ob1, ob2);
+        // key outliers of row j (CSR): the fp16 value replaces the dense one
+        const uint16_t* ptr = reinterpret_cast<const uint16_t*>(ol.blob + (a.lay.ko_ptr - a.lay.ko_val));
+        const uint8_t* idx = ol.blob + (a.lay.ko_idx - a.lay.ko_val);
+        const __half* val = reinterpret_cast<const __half*>(ol.blob);
         const int e1 = ptr[j + 1];
         for (int e = ptr[j]; e < e1; ++e) {
           const int c = idx[e];
-          float S, M;
-          kstat(rec, c, S, M);
-          const float dense = fmaf(kval(code_mem<BITS, 128>(rec + a.lay.kc + (size_t)j * R, c)), S, M);
+          const float dense = fmaf(kval(code_sel<BITS, 128>(B.kw, c)), ol.kS[c], ol.kM[c]);
           const float delta = __half2float(val[e]) - dense;
+          float cp = 1.f, sp = 0.f;
+          if constexpr (ROPE) {
+            const int i = c >> 1;
+            float sj, cj;
+            sincosf((float)j * theta[i], &sj, &cj);
+            const float2 b0 = ol.rb[i];
+            cp = b0.x * cj - b0.y * sj;
+            sp = b0.y * cj + b0.x * sj;
+          }
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             float coef;
             if constexpr (ROPE) {
               const int i = c >> 1;
-              const float2 cs0 = reinterpret_cast<const float2*>(a.rope_base)[(size_t)blk * 64 + i];
-              const float2 csj = reinterpret_cast<const float2*>(a.rope_off)[j * 64 + i];
-              const float cp = cs0.x * csj.x - cs0.y * csj.y;
-              const float sp = cs0.y * csj.x + cs0.x * csj.y;
               const float qa = qs[h * 128 + 2 * i], qb = qs[h * 128 + 2 * i + 1];
               coef = (c & 1) ? qb * cp - qa * sp : qa * cp + qb * sp;
             } else {
@@ -259,8 +374,7 @@ struct Decoder {
       }
     }
     float sl[G], p[G];
-    float s1t = 1.f;
-    if constexpr (MODE == KVARN) s1t = reinterpret_cast<const float*>(rec + a.lay.k1)[j];
+    const float s1t = MODE == KVARN ? B.s1t : 1.f;
 #pragma unroll
     for (int h = 0; h < G; ++h) sl[h] = sc[h] * s1t * a.scale_log2;
     softmax_step(sl, p);
@@ -271,70 +385,60 @@ struct Decoder {
 #pragma unroll
       for (int h = 0; h < G; ++h) { pp[h] = p[h]; pmb[h] = wave_sum(p[h]); }
     } else {
-      float S_t, M_t;
-      if constexpr (MODE == NUQ) {
-        M_t = reinterpret_cast<const float*>(rec + a.lay.vs)[j];
-        S_t = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + j];
-      } else {
-        S_t = reinterpret_cast<const float*>(rec + a.lay.vs)[j];
-        M_t = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + j];
-      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        pp[h] = p[h] * S_t;
-        if constexpr (MODE == KVARN) pmb[h] = wave_sum(p[h] * M_t);
-        else pm[h] = fmaf(p[h], M_t, pm[h]);
+        pp[h] = p[h] * B.tst.x;
+        if constexpr (MODE == KVARN) pmb[h] = wave_sum(p[h] * B.tst.y);
+        else pm[h] = fmaf(p[h], B.tst.y, pm[h]);
       }
     }
-    if (a.k_out > 0) {
+    if (outl) {
 #pragma unroll
       for (int h = 0; h < G; ++h) pbuf[h * 64 + lane] = p[h];
     }
-    uint32_t vw[R / 4];
-    const uint8_t* vbase = rec + a.lay.vc + (size_t)par * (128 * RH);
-    load_row<R>(vw, vbase + (size_t)lane * R);          // rows 2*lane and 2*lane+1
     float o0[G], o1[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) { o0[h] = 0.f; o1[h] = 0.f; }
 #pragma unroll
-    for (int t = 0; t < 64; ++t) {
-      const float v0 = vval(code_at<BITS, 64>(vw, t));
-      const float v1 = vval(code_at<BITS, 64>(vw + R / 8, t));
+    for (int t0 = 0; t0 < 64; t0 += 8) {
+      float v0[8], v1[8];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float pv = readlane_f(pp[h], t);
-        o0[h] = fmaf(pv, v0, o0[h]);
-        o1[h] = fmaf(pv, v1, o1[h]);
+      for (int t = 0; t < 8; ++t) {
+        v0[t] = vval(code_at<BITS, 64>(B.vw, t0 + t));
+        v1[t] = vval(code_at<BITS, 64>(B.vw + R / 8, t0 + t));
       }
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float pv = readlane_f(pp[h], t0 + t);
+          o0[h] = fmaf(pv, v0[t], o0[h]);
+          o1[h] = fmaf(pv, v1[t], o1[h]);
+        }
     }
     if constexpr (MODE == KVARN) {
-      const float2 s1c = reinterpret_cast<const float2*>(rec + a.lay.v1)[lane];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        acc0[h] = fmaf(s1c.x, o0[h] + pmb[h], acc0[h]);
-        acc1[h] = fmaf(s1c.y, o1[h] + pmb[h], acc1[h]);
+        acc0[h] = fmaf(B.s1c.x, o0[h] + pmb[h], acc0[h]);
+        acc1[h] = fmaf(B.s1c.y, o1[h] + pmb[h], acc1[h]);
       }
     } else if constexpr (MODE == SYM) {
-      const __half2 sc2 = reinterpret_cast<const __half2*>(rec + a.lay.vs)[lane];
-      const float s0 = __low2float(sc2), s1 = __high2float(sc2);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        acc0[h] = fmaf(s0, fmaf(-8.f, pmb[h], o0[h]), acc0[h]);
-        acc1[h] = fmaf(s1, fmaf(-8.f, pmb[h], o1[h]), acc1[h]);
+        acc0[h] = fmaf(B.tst.x, fmaf(-8.f, pmb[h], o0[h]), acc0[h]);
+        acc1[h] = fmaf(B.tst.y, fmaf(-8.f, pmb[h], o1[h]), acc1[h]);
       }
     } else {
 #pragma unroll
       for (int h = 0; h < G; ++h) { acc0[h] += o0[h]; acc1[h] += o1[h]; }
     }
     if constexpr (MODE != KVARN) {
-      if (a.k_out > 0) {
+      if (outl) {
         // value outliers of channels 2*lane, 2*lane+1 (CSC) that fall in this half
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const uint16_t* ptr = reinterpret_cast<const uint16_t*>(rec + a.lay.vo_ptr);
-        const uint8_t* idx = rec + a.lay.vo_idx;
-        const __half* val = reinterpret_cast<const __half*>(rec + a.lay.vo_val);
+        wave_sync();
+        const uint16_t* ptr = reinterpret_cast<const uint16_t*>(ol.blob + (a.lay.vo_ptr - a.lay.ko_val));
+        const uint8_t* idx = ol.blob + (a.lay.vo_idx - a.lay.ko_val);
+        const __half* val = reinterpret_cast<const __half*>(ol.blob + (a.lay.vo_val - a.lay.ko_val));
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int c = 2 * lane + k;
@@ -342,20 +446,10 @@ struct Decoder {
           for (int e = ptr[c]; e < e1; ++e) {
             const int t = idx[e] - 64 * par;
             if (t < 0 || t >= 64) continue;
-            const uint32_t code = code_mem<BITS, 64>(vbase + (size_t)c * RH, t);
+            const uint32_t code = code_sel<BITS, 64>(B.vw + k * (R / 8), t);
             float dense;
-            if constexpr (MODE == SYM) {
-              const float S = __half2float(reinterpret_cast<const __half*>(rec + a.lay.vs)[c]);
-              dense = ((float)code - 8.f) * S;
-            } else if constexpr (MODE == NUQ) {
-              const float Z = reinterpret_cast<const float*>(rec + a.lay.vs)[64 * par + t];
-              const float H = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + 64 * par + t];
-              dense = fmaf(vval(code), H, Z);
-            } else {
-              const float S = reinterpret_cast<const float*>(rec + a.lay.vs)[64 * par + t];
-              const float M = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + 64 * par + t];
-              dense = fmaf(vval(code), S, M);
-            }
+            if constexpr (MODE == SYM) dense = ((float)code - 8.f) * (k ? B.tst.y : B.tst.x);
+            else dense = fmaf(vval(code), ol.vS[t], ol.vM[t]);
             const float delta = __half2float(val[e]) - dense;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
@@ -364,13 +458,13 @@ struct Decoder {
             }
           }
         }
-        __builtin_amdgcn_wave_barrier();
+        wave_sync();
       }
     }
   }
 
   // Tokens 64*par .. 64*par+63 of the fp16 tail (n_valid of them), position 128*nblk + j.
-  __device__ void tail_half(const float (&rc)[64], const float (&rs)[64]) {
+  __device__ __forceinline__ void tail_half(const float (&rc)[64], const float (&rs)[64]) {
     const int n_valid = min(64, a.tail_n - 64 * par);
     const __half* tk = a.tail + (size_t)(blockIdx.z * a.Hkv + blockIdx.y) * (2 * kT * kD);
     const __half* tv = tk + kT * kD;
@@ -384,7 +478,7 @@ struct Decoder {
     for (int h = 0; h < G; ++h) { ox[h] = qs[h * 128 + 2 * lane]; oy[h] = qs[h * 128 + 2 * lane + 1]; }
     const __half2* krow = reinterpret_cast<const __half2*>(tk + (size_t)j * kD);
     if constexpr (!ROPE) {
-#pragma unroll 8
+#pragma unroll
       for (int i = 0; i < 64; ++i) {
         const float2 kk = valid ? __half22float2(krow[i]) : make_float2(0.f, 0.f);
 #pragma unroll
@@ -437,12 +531,30 @@ struct Decoder {
       acc1[h] += o1[h];
     }
   }
+
+  // All half blocks of this wave, one half block of loads in flight ahead of the math.
+  __device__ __forceinline__ void run(int blo, int bhi, const float (&rc)[64], const float (&rs)[64]) {
+    Buf A, Bb;
+    int blk = blo + (w >> 1);
+    if (blk < bhi) fetch(A, blk);
+    while (blk < bhi) {
+      if (blk + 2 < bhi) fetch(Bb, blk + 2);
+      process(A, blk, rc, rs);
+      blk += 2;
+      if (blk >= bhi) break;
+      if (blk + 2 < bhi) fetch(A, blk + 2);
+      process(Bb, blk, rc, rs);
+      blk += 2;
+    }
+  }
 };
 
 template <int MODE, int BITS, int G, bool ROPE>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t s_dyn[];
   __shared__ float s_q[G * 128];
   __shared__ float s_lut[32];
+  __shared__ float s_theta[64];
   __shared__ float s_p[4][G * 64];
   __shared__ float s_m[4][G], s_l[4][G];
   __shared__ float s_o[4][G * 128];
@@ -454,19 +566,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   for (int i = tid; i < G * 128; i += kThreads)
     s_q[i] = __half2float(a.q[((size_t)b * a.Hq + (size_t)kvh * G) * 128 + i]);
   if (MODE == NUQ && tid < 32) s_lut[tid] = a.cb[(kvh * 2 + (tid >> 4)) * 16 + (tid & 15)];
+  if (ROPE && tid < 64) s_theta[tid] = a.rope_off[128 * 64 * 2 + tid];
   __syncthreads();
 
-  Decoder<MODE, BITS, G, ROPE> d(a, lane, w, s_lut, s_p[w], s_q);
+  Decoder<MODE, BITS, G, ROPE> d(a, lane, w, s_lut, s_p[w], s_q, s_theta, s_dyn + (size_t)w * a.wave_lds);
   float rc[64], rs[64];
   if constexpr (ROPE) {
-    const float2* off = reinterpret_cast<const float2*>(a.rope_off) + (size_t)d.j * 64;
+    const float2* off = reinterpret_cast<const float2*>(a.rope_off) + d.j;   // pair-major: [i][j]
 #pragma unroll
-    for (int i = 0; i < 64; ++i) { const float2 v = off[i]; rc[i] = v.x; rs[i] = v.y; }
+    for (int i = 0; i < 64; ++i) { const float2 v = off[i * 128]; rc[i] = v.x; rs[i] = v.y; }
   }
 
   const int blo = split * a.blocks_per_split;
   const int bhi = min(a.nblk, blo + a.blocks_per_split);
-  for (int blk = blo + (w >> 1); blk < bhi; blk += 2) d.half_block(blk, rc, rs);
+  d.run(blo, bhi, rc, rs);
   if (split == a.splits - 1 && 64 * d.par < a.tail_n && w < 2) d.tail_half(rc, rs);
 
   // ---- merge the four wave states
@@ -511,62 +624,47 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
   for (int i = tid; i < G * 128; i += kThreads) {
     const int h = i >> 7, c = i & 127;
-    float* part = a.part + (((size_t)b * a.Hq + (size_t)kvh * G + h) * a.splits + split) * kPartStride;
+    const size_t row = (size_t)b * a.Hq + (size_t)kvh * G + h;
     float o = s_o[0][i];
     if constexpr (MODE == KVARN) o *= kInvSqrt128;
-    part[2 + c] = o;
-    if (c == 0) {
-      const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
-      float L = 0.f;
+    const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+    float L = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww)
-        if (s_m[ww][h] != -INFINITY) L = fmaf(exp2f(s_m[ww][h] - M), s_l[ww][h], L);
-      part[0] = M;
-      part[1] = L;
+    for (int ww = 0; ww < 4; ++ww)
+      if (s_m[ww][h] != -INFINITY) L = fmaf(exp2f(s_m[ww][h] - M), s_l[ww][h], L);
+    if (a.splits == 1) {
+      a.out[row * kD + c] = o / L;          // one split: this workgroup saw every token
+    } else {
+      float* part = a.part + (row * a.splits + split) * kPartStride;
+      part[2 + c] = o;
+      if (c == 0) { part[0] = M; part[1] = L; }
     }
   }
-
-  // ---- the last split of this (sequence, kv head) to finish merges all splits
-  // (log-sum-exp rule) and writes the output; it then clears the counter.
-  __shared__ int s_last;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  const size_t unit = (size_t)b * a.Hkv + kvh;
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == (unsigned)(a.splits - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  for (int i = tid; i < G * 128; i += kThreads) {
-    const int h = i >> 7, c = i & 127;
-    const size_t row = (size_t)b * a.Hq + (size_t)kvh * G + h;
-    const float* part = a.part + row * a.splits * kPartStride;
-    float M = -INFINITY;
-    for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, part[sp * kPartStride]);
-    float L = 0.f, o = 0.f;
-    for (int sp = 0; sp < a.splits; ++sp) {
-      const float m = part[sp * kPartStride];
-      if (m == -INFINITY) continue;
-      const float wgt = exp2f(m - M);
-      L = fmaf(wgt, part[sp * kPartStride + 1], L);
-      o = fmaf(wgt, part[sp * kPartStride + 2 + c], o);
-    }
-    a.out[row * kD + c] = o / L;
-  }
-  if (tid == 0) __hip_atomic_store(a.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ void zero_kernel(unsigned* p, size_t n) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+// Merge the split partials of one (sequence, query head) with the log-sum-exp rule.
+__global__ __launch_bounds__(128) void combine_kernel(const float* part_all, float* out, int Hq, int splits) {
+  const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const size_t row = (size_t)b * Hq + hq;
+  const float* part = part_all + row * splits * kPartStride;
+  float M = -INFINITY;
+  for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, part[sp * kPartStride]);
+  float L = 0.f, o = 0.f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const float m = part[sp * kPartStride];
+    if (m == -INFINITY) continue;
+    const float wgt = exp2f(m - M);
+    L = fmaf(wgt, part[sp * kPartStride + 1], L);
+    o = fmaf(wgt, part[sp * kPartStride + 2 + c], o);
+  }
+  out[row * kD + c] = o / L;
 }
+
 
 template <int MODE, int BITS, int G, bool ROPE>
 hipError_t launch_d(const DecodeArgs& a, int batch, hipStream_t s) {
   hipLaunchKernelGGL((decode_kernel<MODE, BITS, G, ROPE>), dim3(a.splits, a.Hkv, batch), dim3(kThreads),
-                     0, s, a);
+                     (size_t)4 * a.wave_lds, s, a);
   return hipGetLastError();
 }
 
@@ -611,8 +709,8 @@ hipError_t launch_decode(int mode, int bits, int group, int rope, const DecodeAr
   }
 }
 
-hipError_t launch_zero(unsigned* p, size_t n, hipStream_t s) {
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+hipError_t launch_combine(const float* part, float* out, int Hq, int splits, int batch, hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel, dim3(Hq, batch), dim3(128), 0, s, part, out, Hq, splits);
   return hipGetLastError();
 }
 

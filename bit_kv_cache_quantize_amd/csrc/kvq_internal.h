@@ -51,14 +51,14 @@ struct DecodeArgs {
   const __half* tail;
   const float* cb;
   const float* rope_base;   // [max_blocks + 1][64][2]: cos, sin of (128 * block) * theta_i
-  const float* rope_off;    // [128][64][2]: cos, sin of j * theta_i
+  const float* rope_off;    // [64][128][2]: cos, sin of j * theta_i (pair-major); then theta_i[64]
   const __half* q;          // [B][Hq][128]
   float* part;              // [B][Hq][splits][2 + 128]
-  unsigned* counters;       // [B][Hkv] finished splits, zero between calls
   float* out;               // [B][Hq][128]
   int Hkv, Hq, max_blocks;
   int nblk, tail_n, splits, blocks_per_split;
   float scale_log2;         // softmax scale * log2(e)
+  int wave_lds;             // dynamic LDS bytes per wave for outlier staging (0 without outliers)
 };
 
 hipError_t launch_quantize(int mode, int bits, const QuantArgs& a, int n_blocks, int batch,
@@ -66,6 +66,6 @@ hipError_t launch_quantize(int mode, int bits, const QuantArgs& a, int n_blocks,
 hipError_t launch_tail(const TailArgs& a, int batch, hipStream_t s);
 hipError_t launch_decode(int mode, int bits, int group, int rope, const DecodeArgs& a, int batch,
                          hipStream_t s);
-hipError_t launch_zero(unsigned* p, size_t n, hipStream_t s);
+hipError_t launch_combine(const float* part, float* out, int Hq, int splits, int batch, hipStream_t s);
 
 }  // namespace kvq

@@ -122,9 +122,8 @@ kvq_status kvq_quantize_append(kvq_cache cache, int layer, const void* k_f16, co
 
 /*
  * Decode attention for one layer over every cached token (quantized blocks and
- * the fp16 tail), reading the packed cache directly, in one kernel launch
- * (the first call on a handle also launches a small kernel that clears the
- * split counters in the workspace).
+ * the fp16 tail), reading the packed cache directly: one split-K kernel and,
+ * when the context is split, a small kernel that merges the split partials.
  * q_f16: dev, fp16 [batch][n_q_heads][128], already rotated for its own position.
  * out:   dev, fp32 [batch][n_q_heads][128].
  * Query head h reads kv head h / (n_q_heads / n_kv_heads). Scores are

@@ -62,9 +62,8 @@ def test_cache_bytes_matches_oracle_record_layout(mode, bits, k_out, pre_rope):
     if mode == K.KVQ_MODE_NUQ:
         total += a(c.n_layers * c.n_kv_heads * 2 * 16 * 4)
     if pre_rope:
-        total += a((nblk + 1) * 512) + a(128 * 512)
+        total += a((nblk + 1) * 512) + a(128 * 512 + 256)
     total += a(c.batch * c.n_q_heads * K.KVQ_MAX_SPLITS * 130 * 4)
-    total += a(c.batch * c.n_kv_heads * 4)
     assert K.kvq_cache_bytes(c) == total
 
 
