@@ -375,8 +375,11 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
     const uint32_t blob = c->lay.vo_idx + 128u * cfg.outliers_per_vec - c->lay.ko_val;
     a.wave_lds = (int)(((blob + 15u) & ~15u) + 1024u + 512u + 512u);
   }
-  st = hip_check(kvq::launch_decode(cfg.mode, cfg.bits, cfg.n_q_heads / cfg.n_kv_heads, cfg.pre_rope, a, cfg.batch, s),
-                 "launch decode");
+  const int group = cfg.n_q_heads / cfg.n_kv_heads;
+  if (kvq::mfma_supported(cfg.mode, cfg.bits, cfg.pre_rope, cfg.outliers_per_vec))
+    st = hip_check(kvq::launch_decode_mfma(cfg.mode, cfg.bits, group, a, cfg.batch, s), "launch decode");
+  else
+    st = hip_check(kvq::launch_decode(cfg.mode, cfg.bits, group, cfg.pre_rope, a, cfg.batch, s), "launch decode");
   if (st != KVQ_OK) return st;
   if (splits > 1) {
     st = hip_check(kvq::launch_combine(a.part, out, cfg.n_q_heads, splits, cfg.batch, s), "launch split combine");

@@ -1,0 +1,546 @@
+// Split-K decode attention on the matrix cores (v_mfma_f32_16x16x32_f16), for
+// caches without pre-RoPE keys, without outliers and at 2 or 4 bits (uniform
+// RTN, KVarN and symmetric int4). Other configurations use the VALU kernel.
+//
+// Same computation as the VALU kernel ("KVQuant reading notes" Algorithm 1
+// attention part; "KVarN" method step 5; "reproducing TurboQuant" 4.2): for the
+// query heads of one kv head, softmax(scale * q . k_hat) weighted sum of v_hat
+// over all cached tokens, dequantized from the packed codes on the fly.
+//
+// Per wave and 64-token half block (the same split / wave / prefetch structure
+// as the VALU kernel):
+//   * scores S^T = K_codes (64 tokens x 128 channels) . Q' (128 x 16): the
+//     codes enter the matrix core as exact fp16 integers; Q' = q * s_c per block
+//     (the per-channel key scale) rounded to fp16, heads padded to 16 columns;
+//     the zero point enters as a per-head bias sum_c q_c m_c.
+//   * P.V as O = V_codes^T (128 channels x 64 tokens) . P' (64 x 16): P' is the
+//     probability times the per-token value scale, taken straight from the
+//     score registers (the value half-rows store tokens in the order that makes
+//     this possible); per-channel scales (KVarN s1, int4 scales) multiply the
+//     per-block product before it is accumulated.
+//   * the online softmax runs per head on the 16 scores each lane holds; the
+//     fp16 tail is handled by the VALU half-block decoder.
+#include "kvq_decode_common.h"
+
+namespace kvq {
+namespace {
+
+using namespace dec;
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {   // two fp32 -> fp16 pair, RNE
+  h2 v;
+  v[0] = (_Float16)a;
+  v[1] = (_Float16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ h8 make8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u4v v = {a, b, c, d};
+  return __builtin_bit_cast(h8, v);
+}
+
+// A pair (1024 + c0, 1024 + c1) built with the 0x6400 exponent trick, minus (1024 + OFF):
+// the exact small integers c - OFF as fp16.
+template <int OFF>
+__device__ __forceinline__ uint32_t fix(uint32_t magic_pair) {
+  const h2 d = __builtin_bit_cast(h2, magic_pair) - h2{(_Float16)(1024 + OFF), (_Float16)(1024 + OFF)};
+  return __builtin_bit_cast(uint32_t, d);
+}
+
+// Slot i (0..7) of an MFMA operand built from one packed word of codes: 4-bit words give
+// pairs (e, e+4) of their 8 codes; 2-bit words give pairs (e, e+8) of their 16 codes, the
+// low (h = 0) or high (h = 1) four pairs per operand.
+__host__ __device__ constexpr int slot4(int i) { return (i & 1) ? (i >> 1) + 4 : (i >> 1); }
+__host__ __device__ constexpr int slot2(int h, int i) { return (i & 1) ? (i >> 1) + 4 * h + 8 : (i >> 1) + 4 * h; }
+
+// Eight codes of operand k-step ks, as fp16 integers minus OFF.
+template <int BITS, int OFF>
+__device__ __forceinline__ h8 codes8(const uint32_t* w, int ks) {
+  if constexpr (BITS == 4) {
+    const uint32_t x = w[ks];
+    return make8(fix<OFF>((x & 0x000F000Fu) | 0x64006400u), fix<OFF>(((x >> 4) & 0x000F000Fu) | 0x64006400u),
+                 fix<OFF>(((x >> 8) & 0x000F000Fu) | 0x64006400u), fix<OFF>(((x >> 12) & 0x000F000Fu) | 0x64006400u));
+  } else {
+    const uint32_t x = w[ks >> 1] >> (8 * (ks & 1));
+    return make8(fix<OFF>((x & 0x00030003u) | 0x64006400u), fix<OFF>(((x >> 2) & 0x00030003u) | 0x64006400u),
+                 fix<OFF>(((x >> 4) & 0x00030003u) | 0x64006400u), fix<OFF>(((x >> 6) & 0x00030003u) | 0x64006400u));
+  }
+}
+
+// Channel (0..31, within a lane's 32-channel key chunk) of slot i of score k-step ks.
+template <int BITS>
+__host__ __device__ constexpr int kchan(int ks, int i) {
+  return BITS == 4 ? 8 * ks + slot4(i) : 16 * (ks >> 1) + slot2(ks & 1, i);
+}
+// Position (0..15, within a lane's 16-position value chunk) of slot i of P.V k-step ks.
+template <int BITS>
+__host__ __device__ constexpr int vpos(int ks, int i) {
+  return BITS == 4 ? 8 * ks + slot4(i) : slot2(ks, i);
+}
+
+template <int MODE, int BITS, int G>
+struct MfmaDecoder {
+  static constexpr int R = 16 * BITS;        // bytes per 128 codes
+  static constexpr int RH = R / 2;           // bytes per 64 codes
+  static constexpr int KW = R / 16;          // dwords of a lane's 32-channel key chunk
+  static constexpr int VW = RH / 16;         // dwords of a lane's 16-position value chunk
+  static constexpr int OFFK = MODE == SYM ? 8 : 0;          // key codes enter as c - OFFK
+  static constexpr int OFFV = MODE == SYM ? 8 : (1 << (BITS - 1));   // value codes: c - OFFV (centred)
+  static constexpr int META = MODE == SYM ? 512 : (MODE == KVARN ? 3072 : 2048);   // ks, vs (, k1, v1) bytes
+  static constexpr int NMETA = (META + 1023) / 1024;                              // 16-byte chunks per lane
+
+  struct Buf {
+    uint32_t kw[4][KW];       // key chunks of tokens 16*tt + n, channels 32*q .. 32*q+31
+    uint32_t vw[8][VW];       // value chunks of channels 16*ct + n, positions 16*q .. 16*q+15
+    uint4 meta[NMETA];        // block statistics (staged in LDS)
+  };
+
+  const DecodeArgs& a;
+  const int lane, w, par, n, q;
+  uint8_t* meta;              // this wave's LDS copy of the block statistics
+  float qv[32];               // query of head n (0 for padding heads), channels 32*q .. 32*q+31
+  f4 acc[8];                  // O[16*ct + 4*q + e][head n]
+  float m_run, l_run, pm;     // head n (l_run, pm: this lane's share)
+
+  __device__ MfmaDecoder(const DecodeArgs& args, int lane_, int w_, const float* qs, uint8_t* meta_)
+      : a(args), lane(lane_), w(w_), par(w_ & 1), n(lane_ & 15), q(lane_ >> 4), meta(meta_) {
+    const float* qrow = qs + (n < G ? n : 0) * 128 + 32 * q;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) qv[c] = n < G ? qrow[c] : 0.f;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+    pm = 0.f;
+  }
+
+  __device__ __forceinline__ const uint8_t* record(int blk) const {
+    return a.rec + ((size_t)(blockIdx.z * a.Hkv + blockIdx.y) * a.max_blocks + blk) * (size_t)a.lay.rec_bytes;
+  }
+
+  __device__ __forceinline__ void fetch(Buf& B, int blk) const {
+    const uint8_t* rec = record(blk);
+    const uint8_t* krow = rec + a.lay.kc + (size_t)(64 * par + n) * R + q * (R / 4);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      if constexpr (KW == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(krow + (size_t)16 * tt * R);
+        B.kw[tt][0] = v.x; B.kw[tt][1] = v.y; B.kw[tt][2] = v.z; B.kw[tt][3] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(krow + (size_t)16 * tt * R);
+        B.kw[tt][0] = v.x; B.kw[tt][1] = v.y;
+      }
+    }
+    const uint8_t* vrow = rec + a.lay.vc + (size_t)par * (128 * RH) + (size_t)n * RH + q * (RH / 4);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      if constexpr (VW == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(vrow + (size_t)16 * ct * RH);
+        B.vw[ct][0] = v.x; B.vw[ct][1] = v.y;
+      } else {
+        B.vw[ct][0] = *reinterpret_cast<const uint32_t*>(vrow + (size_t)16 * ct * RH);
+      }
+    }
+    const uint4* src = reinterpret_cast<const uint4*>(rec + a.lay.ks);
+    constexpr int last = META / 16 - 1;
+#pragma unroll
+    for (int k = 0; k < NMETA; ++k) B.meta[k] = src[min(lane + 64 * k, last)];
+  }
+
+  __device__ __forceinline__ void wave_sync() const {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  __device__ __forceinline__ void process(const Buf& B) {
+    // ---- stage the block statistics: [ks | vs | k1 | v1] as in the record
+#pragma unroll
+    for (int k = 0; k < NMETA; ++k)
+      if (lane + 64 * k < META / 16) reinterpret_cast<uint4*>(meta)[lane + 64 * k] = B.meta[k];
+    wave_sync();
+    const float* kS = reinterpret_cast<const float*>(meta);                 // RTN / KVarN
+    const float* kM = kS + 128;
+    const __half* kS16 = reinterpret_cast<const __half*>(meta);             // SYM
+    const uint8_t* vbase = meta + (MODE == SYM ? 256 : 1024);
+    const float* vS = reinterpret_cast<const float*>(vbase);
+    const float* vM = vS + 128;
+    const __half* vS16 = reinterpret_cast<const __half*>(vbase);
+    const float* k1 = reinterpret_cast<const float*>(meta + 2048);
+    const float* v1 = k1 + 128;
+
+    // ---- Q' = q * s_c for head n over this lane's channels, in operand slot order, as an
+    // fp16 pair hi + lo (hi = Q' rounded, lo = the rounding error rounded); bias sum_c q_c m_c
+    uint32_t qh[4][4], ql[4][4];
+    float bias = 0.f;
+    {
+      const int c0 = 32 * q;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int ca = kchan<BITS>(ks, 2 * s), cb = kchan<BITS>(ks, 2 * s + 1);
+          float sa, sb;
+          if constexpr (MODE == SYM) {
+            sa = __half2float(kS16[c0 + ca]);
+            sb = __half2float(kS16[c0 + cb]);
+          } else {
+            sa = kS[c0 + ca];
+            sb = kS[c0 + cb];
+          }
+          const float xa = qv[ca] * sa, xb = qv[cb] * sb;
+          const _Float16 ha = (_Float16)xa, hb = (_Float16)xb;
+          qh[ks][s] = __builtin_bit_cast(uint32_t, h2{ha, hb});
+          ql[ks][s] = pack2(xa - (float)ha, xb - (float)hb);
+          if constexpr (MODE != SYM) bias = fmaf(qv[ca], kM[c0 + ca], fmaf(qv[cb], kM[c0 + cb], bias));
+        }
+      if constexpr (MODE != SYM) {
+        bias += __shfl_xor(bias, 16);
+        bias += __shfl_xor(bias, 32);
+      }
+    }
+
+    // ---- scores for tokens 16*tt + 4*q + e, head n (log2 domain)
+    float sc[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const h8 av = codes8<BITS, OFFK>(B.kw[tt], ks);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, make8(qh[ks][0], qh[ks][1], qh[ks][2], qh[ks][3]), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, make8(ql[ks][0], ql[ks][1], ql[ks][2], ql[ks][3]), d, 0, 0, 0);
+      }
+      float s1[4] = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (MODE == KVARN) {
+        const float4 t = *reinterpret_cast<const float4*>(k1 + 64 * par + 16 * tt + 4 * q);
+        s1[0] = t.x; s1[1] = t.y; s1[2] = t.z; s1[3] = t.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[tt][e] = (d[e] + bias) * s1[e] * a.scale_log2;
+    }
+
+    // ---- online softmax for head n (16 scores per lane, 4 lanes per head)
+    float mx = sc[0][0];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[tt][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - mnew);
+    m_run = mnew;
+    // p' = p * S_t (value scale per token; 1 for int4). The value codes enter centred, so
+    // the part of sum_t p_t v_t that does not depend on the code is sum_t p_t (M_t + OFFV * S_t).
+    float p[4][4], lsum = 0.f, msum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      float S_t[4] = {1.f, 1.f, 1.f, 1.f}, M_t[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (MODE != SYM) {
+        const float4 ts = *reinterpret_cast<const float4*>(vS + 64 * par + 16 * tt + 4 * q);
+        const float4 tm = *reinterpret_cast<const float4*>(vM + 64 * par + 16 * tt + 4 * q);
+        S_t[0] = ts.x; S_t[1] = ts.y; S_t[2] = ts.z; S_t[3] = ts.w;
+        M_t[0] = tm.x; M_t[1] = tm.y; M_t[2] = tm.z; M_t[3] = tm.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pe = exp2f(sc[tt][e] - mnew);
+        lsum += pe;
+        if constexpr (MODE != SYM) msum = fmaf(pe, fmaf((float)OFFV, S_t[e], M_t[e]), msum);
+        p[tt][e] = pe * S_t[e];
+      }
+    }
+    l_run = fmaf(l_run, alpha, lsum);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) acc[ct] *= alpha;
+    float g = 0.f;                     // KVarN: code-independent part, added before the channel s1
+    if constexpr (MODE == RTN) {
+      pm = fmaf(pm, alpha, msum);
+    } else if constexpr (MODE == KVARN) {
+      g = msum;
+      g += __shfl_xor(g, 16);
+      g += __shfl_xor(g, 32);
+    }
+
+    // ---- P' operand (fp16 hi + lo), slots in the order of the value chunks
+    uint32_t ph[2][4], pl[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int pa = vpos<BITS>(ks, 2 * s), pbp = vpos<BITS>(ks, 2 * s + 1);
+        const float xa = p[(pa >> 2) & 3][pa & 3], xb = p[(pbp >> 2) & 3][pbp & 3];
+        const _Float16 ha = (_Float16)xa, hb = (_Float16)xb;
+        ph[ks][s] = __builtin_bit_cast(uint32_t, h2{ha, hb});
+        pl[ks][s] = pack2(xa - (float)ha, xb - (float)hb);
+      }
+    const h8 b0h = make8(ph[0][0], ph[0][1], ph[0][2], ph[0][3]);
+    const h8 b0l = make8(pl[0][0], pl[0][1], pl[0][2], pl[0][3]);
+    const h8 b1h = make8(ph[1][0], ph[1][1], ph[1][2], ph[1][3]);
+    const h8 b1l = make8(pl[1][0], pl[1][1], pl[1][2], pl[1][3]);
+
+    // ---- O += V^T P' per 16-channel tile
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const h8 a0 = codes8<BITS, OFFV>(B.vw[ct], 0);
+      const h8 a1 = codes8<BITS, OFFV>(B.vw[ct], 1);
+      f4 t = MODE == RTN ? acc[ct] : f4{0.f, 0.f, 0.f, 0.f};
+      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0h, t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0l, t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1h, t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1l, t, 0, 0, 0);
+      if constexpr (MODE == RTN) {
+        acc[ct] = t;
+      } else {
+        float f[4];
+        if constexpr (MODE == KVARN) {
+          const float4 v = *reinterpret_cast<const float4*>(v1 + 16 * ct + 4 * q);
+          f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+        } else {
+          const uint2 v = *reinterpret_cast<const uint2*>(vS16 + 16 * ct + 4 * q);
+          const float2 lo = __half22float2(__builtin_bit_cast(__half2, v.x));
+          const float2 hi = __half22float2(__builtin_bit_cast(__half2, v.y));
+          f[0] = lo.x; f[1] = lo.y; f[2] = hi.x; f[3] = hi.y;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[ct][e] = fmaf(f[e], t[e] + g, acc[ct][e]);
+      }
+    }
+    wave_sync();   // the statistics area is rewritten by the next half block
+  }
+
+  __device__ __forceinline__ void run(int blo, int bhi) {
+    Buf A, Bb;
+    int blk = blo + (w >> 1);
+    if (blk < bhi) fetch(A, blk);
+    while (blk < bhi) {
+      if (blk + 2 < bhi) fetch(Bb, blk + 2);
+      process(A);
+      blk += 2;
+      if (blk >= bhi) break;
+      if (blk + 2 < bhi) fetch(A, blk + 2);
+      process(Bb);
+      blk += 2;
+    }
+  }
+};
+
+// Tokens 64*w .. 64*w+63 of the fp16 tail (w = 0, 1) for the G heads: lane = token for the
+// scores, lane = channel pair for P.V; the query and the probabilities are read from LDS
+// as broadcasts. Writes (m, l, o) of this half into m_out[G], l_out[G], o_out[G][128]
+// (KVarN: o in the rotated domain, like the block accumulators).
+template <int MODE, int G>
+__device__ __forceinline__ void tail_half_lds(const DecodeArgs& a, int w, int lane, bool active, const float* qs,
+                                              float* pbuf, float* m_out, float* l_out, float* o_out) {
+  const int n_valid = active ? min(64, a.tail_n - 64 * w) : 0;
+  const __half* tk = a.tail + (size_t)(blockIdx.z * a.Hkv + blockIdx.y) * (2 * kT * kD);
+  const __half* tv = tk + kT * kD;
+  float sc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) sc[h] = 0.f;
+  if (lane < n_valid) {
+    const uint4* krow = reinterpret_cast<const uint4*>(tk + (size_t)(64 * w + lane) * kD);
+#pragma unroll 2
+    for (int c8 = 0; c8 < 16; ++c8) {
+      const uint4 kv = krow[c8];
+      const float2 k0 = __half22float2(__builtin_bit_cast(__half2, kv.x));
+      const float2 k1 = __half22float2(__builtin_bit_cast(__half2, kv.y));
+      const float2 k2 = __half22float2(__builtin_bit_cast(__half2, kv.z));
+      const float2 k3 = __half22float2(__builtin_bit_cast(__half2, kv.w));
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float4 qa = *reinterpret_cast<const float4*>(qs + h * 128 + 8 * c8);
+        const float4 qb = *reinterpret_cast<const float4*>(qs + h * 128 + 8 * c8 + 4);
+        float t = sc[h];
+        t = fmaf(k0.x, qa.x, t); t = fmaf(k0.y, qa.y, t); t = fmaf(k1.x, qa.z, t); t = fmaf(k1.y, qa.w, t);
+        t = fmaf(k2.x, qb.x, t); t = fmaf(k2.y, qb.y, t); t = fmaf(k3.x, qb.z, t); t = fmaf(k3.y, qb.w, t);
+        sc[h] = t;
+      }
+    }
+  }
+  if (n_valid == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (lane == 0) { m_out[h] = -INFINITY; l_out[h] = 0.f; }
+      o_out[h * 128 + 2 * lane] = 0.f;
+      o_out[h * 128 + 2 * lane + 1] = 0.f;
+    }
+    return;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float sl = lane < n_valid ? sc[h] * a.scale_log2 : -INFINITY;
+    const float m = wave_max(sl);
+    const float p = lane < n_valid ? exp2f(sl - m) : 0.f;
+    const float l = wave_sum(p);
+    pbuf[h * 64 + lane] = p;
+    if (lane == 0) { m_out[h] = m; l_out[h] = l; }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float o0[G], o1[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { o0[h] = 0.f; o1[h] = 0.f; }
+  const __half2* vcol = reinterpret_cast<const __half2*>(tv + (size_t)(64 * w) * kD) + lane;
+  for (int t = 0; t < n_valid; ++t) {
+    const float2 vv = __half22float2(vcol[(size_t)t * (kD / 2)]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float pv = pbuf[h * 64 + t];
+      o0[h] = fmaf(pv, vv.x, o0[h]);
+      o1[h] = fmaf(pv, vv.y, o1[h]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if constexpr (MODE == KVARN) fwht_wave(o0[h], o1[h], lane);
+    o_out[h * 128 + 2 * lane] = o0[h];
+    o_out[h * 128 + 2 * lane + 1] = o1[h];
+  }
+}
+
+template <int MODE, int BITS, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
+  __shared__ float s_q[G * 128];                 // query, original domain
+  __shared__ float s_qr[G * 128];                // query for the blocks (KVarN: rotated)
+  __shared__ __align__(16) uint8_t s_meta[4][3072];
+  __shared__ float s_m[6][G], s_l[6][G];
+  __shared__ float s_o[6][G * 128];
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  for (int i = tid; i < G * 128; i += kThreads) {
+    const float v = __half2float(a.q[((size_t)b * a.Hq + (size_t)kvh * G) * 128 + i]);
+    s_q[i] = v;
+    s_qr[i] = v;
+  }
+  __syncthreads();
+  if constexpr (MODE == KVARN) {
+    // rotate each head's query into the Hadamard domain of the keys (one wave per head)
+    for (int h = w; h < G; h += 4) {
+      float x = s_q[h * 128 + 2 * lane], y = s_q[h * 128 + 2 * lane + 1];
+      fwht_wave(x, y, lane);
+      s_qr[h * 128 + 2 * lane] = x;
+      s_qr[h * 128 + 2 * lane + 1] = y;
+    }
+    __syncthreads();
+  }
+
+  MfmaDecoder<MODE, BITS, G> d(a, lane, w, s_qr, s_meta[w]);
+  const int blo = split * a.blocks_per_split;
+  const int bhi = min(a.nblk, blo + a.blocks_per_split);
+  d.run(blo, bhi);
+
+  // ---- this wave's matrix-core state
+  const int n = lane & 15, q = lane >> 4;
+  float l = d.l_run;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  float pmw = d.pm;
+  pmw += __shfl_xor(pmw, 16);
+  pmw += __shfl_xor(pmw, 32);
+  if (n < G) {
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_o[w][n * 128 + 16 * ct + 4 * q + e] = d.acc[ct][e] + pmw;
+    if (q == 0) { s_m[w][n] = d.m_run; s_l[w][n] = l; }
+  }
+  // ---- the fp16 tail (waves 0 and 1; it belongs to the last split)
+  if (w < 2) {
+    const bool active = split == a.splits - 1 && 64 * w < a.tail_n;
+    tail_half_lds<MODE, G>(a, w, lane, active, s_q, reinterpret_cast<float*>(s_meta[w]), s_m[4 + w], s_l[4 + w],
+                           s_o[4 + w]);
+  }
+  __syncthreads();
+  for (int i = tid; i < G * 128; i += kThreads) {
+    const int h = i >> 7;
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 6; ++s) M = fmaxf(M, s_m[s][h]);
+    float o = 0.f;
+#pragma unroll
+    for (int s = 0; s < 6; ++s)
+      if (s_m[s][h] != -INFINITY) o = fmaf(exp2f(s_m[s][h] - M), s_o[s][i], o);
+    s_o[0][i] = o;
+  }
+  __syncthreads();
+  if constexpr (MODE == KVARN) {
+    for (int s = 0; s < 7; ++s) {
+      const int hs = 1 << s;
+      for (int id = tid; id < G * 64; id += kThreads) {
+        const int h = id >> 6, k = id & 63;
+        const int i = h * 128 + (((k >> s) << (s + 1)) | (k & (hs - 1)));
+        const float x = s_o[0][i], y = s_o[0][i + hs];
+        s_o[0][i] = x + y;
+        s_o[0][i + hs] = x - y;
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < G * 128; i += kThreads) {
+    const int h = i >> 7, c = i & 127;
+    const size_t row = (size_t)b * a.Hq + (size_t)kvh * G + h;
+    float o = s_o[0][i];
+    if constexpr (MODE == KVARN) o *= kInvSqrt128;
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 6; ++s) M = fmaxf(M, s_m[s][h]);
+    float L = 0.f;
+#pragma unroll
+    for (int s = 0; s < 6; ++s)
+      if (s_m[s][h] != -INFINITY) L = fmaf(exp2f(s_m[s][h] - M), s_l[s][h], L);
+    if (a.splits == 1) {
+      a.out[row * kD + c] = o / L;
+    } else {
+      float* part = a.part + (row * a.splits + split) * kPartStride;
+      part[2 + c] = o;
+      if (c == 0) { part[0] = M; part[1] = L; }
+    }
+  }
+}
+
+template <int MODE, int BITS, int G>
+hipError_t launch_m(const DecodeArgs& a, int batch, hipStream_t s) {
+  hipLaunchKernelGGL((decode_mfma_kernel<MODE, BITS, G>), dim3(a.splits, a.Hkv, batch), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int MODE, int BITS>
+hipError_t launch_mg(int group, const DecodeArgs& a, int batch, hipStream_t s) {
+  switch (group) {
+    case 1: return launch_m<MODE, BITS, 1>(a, batch, s);
+    case 2: return launch_m<MODE, BITS, 2>(a, batch, s);
+    case 4: return launch_m<MODE, BITS, 4>(a, batch, s);
+    case 8: return launch_m<MODE, BITS, 8>(a, batch, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool mfma_supported(int mode, int bits, int rope, int k_out) {
+  return !rope && k_out == 0 && (bits == 2 || bits == 4) && (mode == RTN || mode == KVARN || mode == SYM);
+}
+
+hipError_t launch_decode_mfma(int mode, int bits, int group, const DecodeArgs& a, int batch, hipStream_t s) {
+  switch (mode * 8 + bits) {
+    case RTN * 8 + 2: return launch_mg<RTN, 2>(group, a, batch, s);
+    case RTN * 8 + 4: return launch_mg<RTN, 4>(group, a, batch, s);
+    case KVARN * 8 + 2: return launch_mg<KVARN, 2>(group, a, batch, s);
+    case KVARN * 8 + 4: return launch_mg<KVARN, 4>(group, a, batch, s);
+    case SYM * 8 + 4: return launch_mg<SYM, 4>(group, a, batch, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq

@@ -12,7 +12,8 @@
 //     RTN (notes 1.2, 3.1), codebook argmin (notes 1.2, 3.3) or symmetric int4
 //     with an fp16 scale ("reproducing TurboQuant" 4.2);
 //   - pack codes (key rows token-major, value rows channel-major in two token
-//     halves), write statistics, s1 and the CSR / CSC outlier lists.
+//     halves, each half-row in a 4x4-group transposed token order), write
+//     statistics, s1 and the CSR / CSC outlier lists.
 // Every quantization decision uses IEEE fp32 operations written out with
 // explicit rounding intrinsics (no contraction), rintf (round half even) and
 // fp16 round-to-nearest-even, so that codes and scales are reproducible.
@@ -283,7 +284,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
       for (int id = tid; id < 2 * kD * DW; id += kThreads) {
         const int row = id / DW, w = id % DW;
         const int half = row >> 7, c = row & 127;
-        dst[id] = pack_dword<BITS>(64, w, [&](int i) { return sm.q[(64 * half + i) * kD + c]; });
+        // position i of a half-row holds token 16*((i>>2)&3) + 4*(i>>4) + (i&3) of the half
+        dst[id] = pack_dword<BITS>(64, w, [&](int i) {
+          return sm.q[(64 * half + 16 * ((i >> 2) & 3) + 4 * (i >> 4) + (i & 3)) * kD + c];
+        });
       }
     }
 

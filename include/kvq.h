@@ -154,7 +154,9 @@ kvq_status kvq_set_decode_splits(kvq_cache cache, int splits);
  * R = 16*bits bytes per 128 codes):
  *   kc  key codes, token-major: 128 rows of R bytes, row t = channels 0..127
  *   vc  value codes, channel-major in two token halves: [2][128][R/2],
- *       row (half, c) = tokens 64*half .. 64*half+63 of channel c
+ *       row (half, c) holds the 64 tokens 64*half + u of channel c with the 4x4
+ *       grid of 4-token groups transposed: position p holds
+ *       u = 16*((p>>2)&3) + 4*(p>>4) + (p&3) (storage order only)
  *   ks  key statistics per channel: RTN/KVARN f32 s[128] then f32 m[128];
  *       NUQ f32 z[128] then f32 h[128]; SYM_INT4 f16 s[128]
  *   vs  value statistics: per token (RTN/KVARN s then m, NUQ z then h, f32);

@@ -440,10 +440,23 @@ def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
     return out.astype(np.uint8).reshape(p.shape[:-1] + (n,))
 
 
+def half_row_token(pos: np.ndarray) -> np.ndarray:
+    """Token (0..63, relative to its half) stored at position pos of a value half-row.
+
+    Position 16a + 4b + c holds token 16b + 4a + c: the 4x4 grid of 4-token groups
+    is transposed, which puts the 16 tokens a matrix-core lane contracts over next
+    to each other (a storage order only; the mapping is its own inverse).
+    """
+    pos = np.asarray(pos)
+    return 16 * ((pos >> 2) & 3) + 4 * (pos >> 4) + (pos & 3)
+
+
 def value_code_planes(vcodes: np.ndarray) -> np.ndarray:
-    """[T][D] value codes -> [2][D][64]: two token halves, channel-major within each."""
+    """[T][D] value codes -> [2][D][64]: two token halves, channel-major within each,
+    tokens within a half-row in the order of half_row_token."""
     v = np.asarray(vcodes).reshape(T, D)
-    return np.stack([v[:64].T, v[64:].T])
+    order = half_row_token(np.arange(64))
+    return np.stack([v[:64][order].T, v[64:][order].T])
 
 
 def _align(x: int, a: int) -> int:
@@ -454,7 +467,7 @@ def record_layout(mode: int, bits: int, k_out: int) -> tuple[dict, int]:
     """Byte offsets of the segments of one block record and its padded size.
 
     Order: key codes (128 token rows), value codes (two token halves, each
-    128 channel rows of 64 codes), key
+    128 channel rows of 64 codes in the order of half_row_token), key
     statistics, value statistics, [KVARN: key s1 per token, value s1 per
     channel], [outliers: key CSR (values fp16, row pointers u16[129], channel
     u8), value CSC (values fp16, column pointers u16[129], token u8)]. Each

@@ -74,7 +74,8 @@ def compare_record(got: np.ndarray, blk, ocfg, stats: RecordStats | None = None,
     kc = O.unpack_codes(got[o:o + n].reshape(128, R), bits).astype(np.int32)
     o, n = off["vc"]
     vp = O.unpack_codes(got[o:o + n].reshape(2, 128, R // 2), bits).astype(np.int32)
-    vc = np.concatenate([vp[0].T, vp[1].T])
+    inv = O.half_row_token(np.arange(64))          # involution: position <-> token
+    vc = np.concatenate([vp[0][:, inv].T, vp[1][:, inv].T])
     for g, r in ((kc, blk.kcodes.astype(np.int32)), (vc, blk.vcodes.astype(np.int32))):
         d = np.abs(g - r)
         assert d.max() <= 1, f"{where}: a code differs by {d.max()}"

@@ -381,8 +381,13 @@ def test_serialized_record_reads_back():
     kc = O.unpack_codes(buf[o:o + n].reshape(128, 48), 3)
     assert np.array_equal(kc, blk.kcodes)
     o, n = off["vc"]
-    vc = O.unpack_codes(buf[o:o + n].reshape(2, 128, 24), 3)      # [half][channel][64 tokens]
-    assert np.array_equal(np.concatenate([vc[0].T, vc[1].T]), blk.vcodes)
+    vc = O.unpack_codes(buf[o:o + n].reshape(2, 128, 24), 3)      # [half][channel][64 positions]
+    for half in (0, 1):
+        for p in range(64):
+            t = 64 * half + 16 * ((p // 4) % 4) + 4 * (p // 16) + p % 4
+            assert np.array_equal(vc[half][:, p], blk.vcodes[t])
+    perm = O.half_row_token(np.arange(64))
+    assert np.array_equal(O.half_row_token(perm), np.arange(64))   # an involution
     o, n = off["ko_ptr"]
     ptr = buf[o:o + n].view(np.uint16)
     o, n = off["ko_idx"]
