@@ -1,8 +1,8 @@
-// Quantize-on-append: one workgroup turns one completed 128-token block of one
-// (sequence, kv head) into its packed record.
+// Quantize-on-append: one workgroup turns one tensor (the keys or the values) of
+// one completed 128-token block of one (sequence, kv head) into its part of the
+// packed record.
 //
-// Steps per tensor (keys, then values), following the pages:
-//   - stage the 128 x 128 fp16 block (fp16 tail rows + new rows) in LDS as fp32;
+// Steps per tensor, following the pages:
 //   - KVarN only: 128-point Hadamard rotation of every token across channels and
 //     Sinkhorn-style variance normalisation in the log-std domain, giving s1
 //     ("KVarN" summary, core method and method steps);
@@ -14,323 +14,623 @@
 //   - pack codes (key rows token-major, value rows channel-major in two token
 //     halves, each half-row in a 4x4-group transposed token order), write
 //     statistics, s1 and the CSR / CSC outlier lists.
-// Every quantization decision uses IEEE fp32 operations written out with
-// explicit rounding intrinsics (no contraction), rintf (round half even) and
-// fp16 round-to-nearest-even, so that codes and scales are reproducible.
+// Every quantization decision uses IEEE fp32 operations (no contraction:
+// the library is built with -ffp-contract=off and correctly rounded division),
+// rintf (round half even) and fp16 round-to-nearest-even, so that codes and
+// scales are reproducible.
+//
+// The 128 x 128 tile stays in registers: wave w holds tokens 32w .. 32w+31 and
+// lane (r = lane >> 4, g = lane & 15) holds tokens t_i = 32w + 4i + r (i = 0..7)
+// at channels 8g .. 8g+7, widened to fp32. Each 16-byte load covers 8 channels of
+// one token, so a wave reads four consecutive 256-byte rows per instruction.
+//   per-channel reductions: the lane's 8 tokens, the four r lanes (xor 16, 32),
+//     then the four waves through LDS (all threads combine the four partials in
+//     the same order, so every holder of a channel gets the same value);
+//   per-token reductions: the lane's 8 channels, then the 16 g lanes (xor 1..8).
+// Key codes are packed straight from registers (a lane holds 8 consecutive
+// channels of a token row); value codes go through an LDS tile for the
+// channel-major layout. Outlier lists are built with a per-row bitmask in LDS:
+// the row pointer is a prefix sum of row popcounts and an entry's slot is the
+// row pointer plus the popcount of the bits below its column.
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
-constexpr int kPitch = 129;          // LDS row pitch of the fp32 tile (bank spread)
 constexpr int kThreads = 256;
+constexpr float kInvSqrt128 = 0.08838834764831845f;
 
-struct QuantSmem {
-  float x[kT * kPitch];              // element (t, c) at x[t * kPitch + c]
-  uint8_t q[kT * kD];                // code of (t, c) at q[t * kD + c]
-  uint8_t olist[kD * kMaxOut];       // outlier element indices per vector
-  float ra[kT], cb[kD];              // VarN: exp(-r_t), exp(-c_ch)
-  float rl[kT], cl[kD];              // VarN: log scales
-  int cnt[kT + 1];
-  float lut[16];
+struct Smem {
+  uint8_t vq[kT * kD];            // value codes, (t, c) at t * 128 + c
+  uint32_t red[2][4][kD];         // per-channel cross-wave partials, two alternating buffers
+  float rlo[4][kD], rhi[4][kD];   // per-channel min / max partials
+  uint32_t omask[kD][4];          // outlier bitmask per storage row
+  uint16_t optr[kD + 1];          // storage row pointers
 };
 
-__device__ __forceinline__ int xidx(int va, int v, int e) {
-  // va == 0: vector = channel v, element = token e; va == 1: vector = token v, element = channel e
-  return va == 0 ? e * kPitch + v : v * kPitch + e;
+// Order of the top-k |x| selection: larger magnitude first, then lower element index.
+// x is a widened fp16, so the fp32 magnitude bits below bit 13 are zero.
+__device__ __forceinline__ uint32_t mag_key(float x, int e) {
+  return (((__float_as_uint(x) & 0x7fffffffu) >> 13) << 7) | (uint32_t)(127 - e);
 }
 
-__device__ __forceinline__ uint64_t mag_key(float x, int e) {
-  // larger key = larger |x|, then smaller element index
-  return ((uint64_t)(__float_as_uint(x) & 0x7fffffffu) << 8) | (uint64_t)(255 - e);
+// The block tile of one lane: 8 tokens x 8 channels. Non-KVarN modes keep the fp16
+// input bits (two channels per register) and widen on use, which halves the live
+// registers; KVarN keeps fp32, since it rotates and rescales the tile.
+template <bool F32> struct Tile;
+template <> struct Tile<true> {
+  float v[8][8];
+  __device__ __forceinline__ float f(int i, int e) const { return v[i][e]; }
+  __device__ __forceinline__ uint32_t key(int i, int e, int idx) const { return mag_key(v[i][e], idx); }
+};
+template <> struct Tile<false> {
+  uint32_t v[8][4];
+  __device__ __forceinline__ uint32_t bits(int i, int e) const { return (e & 1) ? v[i][e >> 1] >> 16 : v[i][e >> 1] & 0xffffu; }
+  __device__ __forceinline__ float f(int i, int e) const { return __half2float(__ushort_as_half((unsigned short)bits(i, e))); }
+  __device__ __forceinline__ uint32_t key(int i, int e, int idx) const { return ((bits(i, e) & 0x7fffu) << 7) | (uint32_t)(127 - idx); }
+};
+
+struct MaxU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
+struct MinF { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
+struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct AddF { __device__ float operator()(float a, float b) const { return __fadd_rn(a, b); } };
+
+template <typename T>
+__device__ __forceinline__ T shfl_x(T v, int m) {
+  if constexpr (sizeof(T) == 4 && !__is_same(T, float)) return (T)__shfl_xor((int)v, m);
+  else return __shfl_xor(v, m);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Pack dword w of a row of n codes, code i given by get(i).
-template <int BITS, typename Get>
-__device__ __forceinline__ uint32_t pack_dword(int n, int w, Get get) {
-  uint32_t r = 0;
-  if constexpr (BITS == 4) {
+// v[e] = this lane's partial for channel 8g + e. Returns the channel totals over
+// all 128 tokens in v (identical in every lane holding the channel).
+template <typename T, typename Op>
+__device__ __forceinline__ void chan_reduce(T (&v)[8], T* buf, int w, int r, int g, Op op) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r |= (uint32_t)get(8 * w + i) << (4 * i);
-  } else if constexpr (BITS == 2) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r |= (uint32_t)get(16 * w + i) << (2 * i);
-  } else {
-    const int ncrumb = n / 16;       // dwords of the 2-bit plane
-    if (w < ncrumb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) r |= (uint32_t)(get(16 * w + i) & 3) << (2 * i);
-    } else {
-      const int wb = w - ncrumb;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) r |= (uint32_t)((get(32 * wb + i) >> 2) & 1) << i;
-    }
+  for (int e = 0; e < 8; ++e) {
+    v[e] = op(v[e], shfl_x(v[e], 16));
+    v[e] = op(v[e], shfl_x(v[e], 32));
   }
-  return r;
-}
-
-// Rotate every token row of the tile by the orthonormal Sylvester Hadamard matrix.
-__device__ void fwht_rows(QuantSmem& sm, int tid) {
-  for (int s = 0; s < 7; ++s) {
-    const int hs = 1 << s;
-    for (int id = tid; id < kT * 64; id += kThreads) {
-      const int t = id >> 6, k = id & 63;
-      const int i = ((k >> s) << (s + 1)) | (k & (hs - 1));
-      float* row = sm.x + t * kPitch;
-      const float a = row[i], b = row[i + hs];
-      row[i] = __fadd_rn(a, b);
-      row[i + hs] = __fsub_rn(a, b);
-    }
-    __syncthreads();
-  }
-  const float inv = 0.08838834764831845f;   // 1 / sqrt(128)
-  for (int id = tid; id < kT * kD; id += kThreads) {
-    float& x = sm.x[(id >> 7) * kPitch + (id & 127)];
-    x = __fmul_rn(x, inv);
+  if (r == 0) {
+    uint4* dst = reinterpret_cast<uint4*>(buf + w * kD + 8 * g);
+    dst[0] = make_uint4(__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
+                        __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3]));
+    dst[1] = make_uint4(__builtin_bit_cast(uint32_t, v[4]), __builtin_bit_cast(uint32_t, v[5]),
+                        __builtin_bit_cast(uint32_t, v[6]), __builtin_bit_cast(uint32_t, v[7]));
   }
   __syncthreads();
+  T p[4][8];
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    const uint4* src = reinterpret_cast<const uint4*>(buf + ww * kD + 8 * g);
+    const uint4 lo = src[0], hi = src[1];
+    p[ww][0] = __builtin_bit_cast(T, lo.x); p[ww][1] = __builtin_bit_cast(T, lo.y);
+    p[ww][2] = __builtin_bit_cast(T, lo.z); p[ww][3] = __builtin_bit_cast(T, lo.w);
+    p[ww][4] = __builtin_bit_cast(T, hi.x); p[ww][5] = __builtin_bit_cast(T, hi.y);
+    p[ww][6] = __builtin_bit_cast(T, hi.z); p[ww][7] = __builtin_bit_cast(T, hi.w);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = op(op(op(p[0][e], p[1][e]), p[2][e]), p[3][e]);
 }
 
-// Population std over 128 elements of the scaled tile, two threads per vector.
-// va == 0: per channel v over tokens; va == 1: per token v over channels.
-__device__ float varn_std(const QuantSmem& sm, int va, int v, int hf) {
-  float sum = 0.f;
-  for (int i = 0; i < 64; ++i) {
-    const int e = hf * 64 + i;
-    const int t = va == 0 ? e : v, c = va == 0 ? v : e;
-    sum = __fadd_rn(sum, __fmul_rn(__fmul_rn(sm.x[t * kPitch + c], sm.ra[t]), sm.cb[c]));
-  }
-  sum = __fadd_rn(sum, __shfl_xor(sum, 1));
-  const float mean = __fdiv_rn(sum, 128.f);
-  float ss = 0.f;
-  for (int i = 0; i < 64; ++i) {
-    const int e = hf * 64 + i;
-    const int t = va == 0 ? e : v, c = va == 0 ? v : e;
-    const float d = __fsub_rn(__fmul_rn(__fmul_rn(sm.x[t * kPitch + c], sm.ra[t]), sm.cb[c]), mean);
-    ss = __fadd_rn(ss, __fmul_rn(d, d));
-  }
-  ss = __fadd_rn(ss, __shfl_xor(ss, 1));
-  return __fsqrt_rn(__fdiv_rn(ss, 128.f));
+// Total over the 16 g lanes of a token (identical in all of them).
+template <typename T, typename Op>
+__device__ __forceinline__ T tok_reduce(T v, Op op) {
+  v = op(v, shfl_x(v, 1));
+  v = op(v, shfl_x(v, 2));
+  v = op(v, shfl_x(v, 4));
+  v = op(v, shfl_x(v, 8));
+  return v;
 }
 
-// Variance normalisation (channel step, then token step, per iteration) in the
-// log-std domain; leaves rl (per token) and cl (per channel) log scales in LDS.
-__device__ void varn(QuantSmem& sm, int tid, int iters) {
-  if (tid < 128) { sm.rl[tid] = 0.f; sm.cl[tid] = 0.f; }
-  __syncthreads();
-  const int v = tid >> 1, hf = tid & 1;
+// Orthonormal Sylvester Hadamard rotation of every token row (8 channels per lane,
+// channel bits 3..6 = g bits 0..3).
+__device__ __forceinline__ void fwht_rows(float (&x)[8][8], int g) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int hs = 1; hs < 8; hs <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!(e & hs)) {
+          const float p = x[i][e], q = x[i][e | hs];
+          x[i][e] = __fadd_rn(p, q);
+          x[i][e | hs] = __fsub_rn(p, q);
+        }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      const bool hi = (g & m) != 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __shfl_xor(x[i][e], m);
+        x[i][e] = hi ? __fsub_rn(p, x[i][e]) : __fadd_rn(x[i][e], p);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[i][e] = __fmul_rn(x[i][e], kInvSqrt128);
+  }
+}
+
+// Makes the tile look modified to the optimiser, so that values derived from it are
+// recomputed where they are used instead of being kept live.
+template <typename T, int N>
+__device__ __forceinline__ void opaque(T (&x)[8][N]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < N; ++e) asm volatile("" : "+v"(x[i][e]));
+}
+
+// Population standard deviation of a vector from its sum and the centred sum of squares.
+__device__ __forceinline__ float pop_std(float ss) { return __fsqrt_rn(__fdiv_rn(ss, 128.f)); }
+
+// Variance normalisation: per iteration a channel step, then a token step, each adding
+// log(std) of the currently scaled tile to its log-scale (a zero std leaves it). Returns
+// the log-scales of this lane's tokens (rl) and channels (cl).
+__device__ __forceinline__ void varn(float (&x)[8][8], float (&rl)[8], float (&cl)[8], int iters, Smem& sm,
+                                     int& ph, int w, int r, int g) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) { rl[k] = 0.f; cl[k] = 0.f; }
   for (int it = 0; it < iters; ++it) {
-    if (tid < 128) { sm.ra[tid] = expf(-sm.rl[tid]); sm.cb[tid] = expf(-sm.cl[tid]); }
+    float er[8], ec[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) { er[k] = expf(-rl[k]); ec[k] = expf(-cl[k]); }
+    // channel step
+    float s[8], ss[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = __fadd_rn(acc, __fmul_rn(__fmul_rn(x[i][e], er[i]), ec[e]));
+      s[e] = acc;
+    }
+    chan_reduce(s, reinterpret_cast<float*>(&sm.red[ph][0][0]), w, r, g, AddF());
+    ph ^= 1;
+    opaque(x);   // recompute the scaled tile rather than keep 64 products live
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float mean = __fdiv_rn(s[e], 128.f);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float d = __fsub_rn(__fmul_rn(__fmul_rn(x[i][e], er[i]), ec[e]), mean);
+        acc = __fadd_rn(acc, __fmul_rn(d, d));
+      }
+      ss[e] = acc;
+    }
+    chan_reduce(ss, reinterpret_cast<float*>(&sm.red[ph][0][0]), w, r, g, AddF());
+    ph ^= 1;
+    opaque(x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sd = pop_std(ss[e]);
+      if (sd > 0.f) cl[e] = __fadd_rn(cl[e], logf(sd));
+      ec[e] = expf(-cl[e]);
+    }
+    // token step
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __fadd_rn(acc, __fmul_rn(__fmul_rn(x[i][e], er[i]), ec[e]));
+      const float mean = __fdiv_rn(tok_reduce(acc, AddF()), 128.f);
+      float sq = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = __fsub_rn(__fmul_rn(__fmul_rn(x[i][e], er[i]), ec[e]), mean);
+        sq = __fadd_rn(sq, __fmul_rn(d, d));
+      }
+      const float sd = pop_std(tok_reduce(sq, AddF()));
+      if (sd > 0.f) rl[i] = __fadd_rn(rl[i], logf(sd));
+    }
+  }
+}
+
+// Code of one element given the vector's statistics (sa, sb): RTN/KVarN (s, m), NUQ (z, h),
+// symmetric int4 (s, -).
+template <int MODE, int BITS>
+__device__ __forceinline__ uint32_t code_of(float x, float sa, float sb, const float* lut) {
+  constexpr int QMAX = (1 << BITS) - 1;
+  if constexpr (MODE == NUQ) {
+    float u = sb == 0.f ? 0.f : __fdiv_rn(__fsub_rn(x, sa), sb);
+    u = fminf(fmaxf(u, -1.f), 1.f);
+    float best = INFINITY;
+    uint32_t code = 0;
+#pragma unroll
+    for (int c = 0; c <= QMAX; ++c) {
+      const float d = fabsf(__fsub_rn(u, lut[c]));
+      if (d < best) { best = d; code = c; }
+    }
+    return code;
+  } else if constexpr (MODE == SYM) {
+    const float q = sa == 0.f ? 0.f : rintf(__fdiv_rn(x, sa));
+    return (uint32_t)((int)fminf(fmaxf(q, -8.f), 7.f) + 8);
+  } else {
+    const float q = sa == 0.f ? 0.f : rintf(__fdiv_rn(__fsub_rn(x, sb), sa));
+    return (uint32_t)fminf(fmaxf(q, 0.f), (float)QMAX);
+  }
+}
+
+// Statistics (sa, sb) of a vector from its min / max / max|x| over the non-outliers.
+template <int MODE, int BITS>
+__device__ __forceinline__ void stats_of(float lo, float hi, float amax, float& sa, float& sb) {
+  if constexpr (MODE == NUQ) {
+    sa = __fmul_rn(__fadd_rn(hi, lo), 0.5f);   // z
+    sb = __fmul_rn(__fsub_rn(hi, lo), 0.5f);   // h
+  } else if constexpr (MODE == SYM) {
+    sa = __half2float(__float2half_rn(__fdiv_rn(amax, 7.0f)));
+    sb = 0.f;
+  } else {
+    sa = __fdiv_rn(__fsub_rn(hi, lo), (float)((1 << BITS) - 1));   // s
+    sb = lo;                                                       // m
+  }
+}
+
+// One tensor (TENSOR 0: keys, 1: values) of block j of (sequence b, kv head h).
+template <int MODE, int BITS, int TENSOR>
+__device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, int j, int h, int b) {
+  constexpr int tensor = TENSOR;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane >> 4, g = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const size_t unit = (size_t)b * a.Hkv + h;
+  uint8_t* rec = a.rec + (unit * a.max_blocks + (size_t)(a.blk0 + j)) * a.lay.rec_bytes;
+  constexpr int R = 16 * BITS;                                  // bytes per 128 codes
+  const int k_out = MODE == KVARN ? 0 : a.k_out;
+  constexpr bool per_chan = TENSOR == 0 || MODE == SYM;         // vector = a channel over the block's tokens
+  int ph = 0;                                                   // alternating cross-wave buffer
+
+  if (k_out > 0)
+    for (int i = tid; i < kD * 4; i += kThreads) (&sm.omask[0][0])[i] = 0u;
+
+  // ---- load the block: rows < t0 of the first block come from the fp16 tail
+  Tile<MODE == KVARN> X;
+  {
+    const __half* in = (tensor ? a.v_in : a.k_in) + unit * (size_t)a.n_new * kD;
+    const __half* tl = a.tail + unit * (2 * kT * kD) + (size_t)tensor * kT * kD;
+    uint4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = 32 * w + 4 * i + r;
+      const __half* src = (j == 0 && t < a.t0) ? tl + (size_t)t * kD : in + ((size_t)j * kT + t - a.t0) * kD;
+      raw[i] = *reinterpret_cast<const uint4*>(src + 8 * g);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t wd[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (MODE == KVARN) {
+          const float2 f = __half22float2(__builtin_bit_cast(__half2, wd[k]));
+          X.v[i][2 * k] = f.x;
+          X.v[i][2 * k + 1] = f.y;
+        } else {
+          X.v[i][k] = wd[k];
+        }
+      }
+    }
+  }
+  float lut[16];
+  if constexpr (MODE == NUQ) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) lut[c] = a.cb[(h * 2 + tensor) * 16 + c];
+  }
+
+  // ---- KVarN: rotate, normalise, divide by s1
+  if constexpr (MODE == KVARN) {
+    float (&x)[8][8] = X.v;
+    fwht_rows(x, g);
+    float rl[8], cl[8];
+    varn(x, rl, cl, a.varn_iters, sm, ph, w, r, g);
+    float* s1dst = reinterpret_cast<float*>(rec + (tensor == 0 ? a.lay.k1 : a.lay.v1));
+    if (tensor == 0) {   // keys: s1 per token
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float s1 = expf(rl[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[i][e] = __fdiv_rn(x[i][e], s1);
+        if (g == 0) s1dst[32 * w + 4 * i + r] = s1;
+      }
+    } else {             // values: s1 per channel
+      float s1[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s1[e] = expf(cl[e]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[i][e] = __fdiv_rn(x[i][e], s1[e]);
+      if (w == 0 && r == 0) {
+        reinterpret_cast<float4*>(s1dst + 8 * g)[0] = make_float4(s1[0], s1[1], s1[2], s1[3]);
+        reinterpret_cast<float4*>(s1dst + 8 * g)[1] = make_float4(s1[4], s1[5], s1[6], s1[7]);
+      }
+    }
+  }
+
+  // ---- outlier thresholds: the k-th largest key of each vector (UINT_MAX: none)
+  // thr[e] for channel 8g+e when per_chan, thr[i] for token t_i otherwise
+  uint32_t thr[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) thr[k] = 0xffffffffu;
+  for (int p = 0; p < k_out; ++p) {
+    opaque(X.v);   // keeps the per-element keys from being hoisted out of the loop (64 more live registers)
+    uint32_t best[8];
+    if constexpr (per_chan) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t key = X.key(i, e, 32 * w + 4 * i + r);
+          m = (key < thr[e] && key > m) ? key : m;
+        }
+        best[e] = m;
+      }
+      chan_reduce(best, &sm.red[ph][0][0], w, r, g, MaxU());
+      ph ^= 1;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t key = X.key(i, e, 8 * g + e);
+          m = (key < thr[i] && key > m) ? key : m;
+        }
+        best[i] = tok_reduce(m, MaxU());
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) thr[k] = best[k];
+  }
+  // this lane's outliers, bit 8i + e
+  uint64_t omask = 0;
+  if (MODE != KVARN && k_out > 0) {
+    opaque(X.v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool o = per_chan ? X.key(i, e, 32 * w + 4 * i + r) >= thr[e] : X.key(i, e, 8 * g + e) >= thr[i];
+        omask |= (uint64_t)o << (8 * i + e);
+      }
+  }
+  auto is_out = [&](int i, int e) -> bool { return (omask >> (8 * i + e)) & 1u; };
+
+  // ---- statistics over the non-outliers
+  if constexpr (MODE != KVARN) opaque(X.v);   // widen again where used (keeps 32, not 64, tile registers)
+  float sa[8], sb[8];
+  if constexpr (per_chan) {
+    float lo[8], hi[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      lo[e] = INFINITY;
+      hi[e] = MODE == SYM ? 0.f : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (!is_out(i, e)) {
+          lo[e] = fminf(lo[e], X.f(i, e));
+          hi[e] = MODE == SYM ? fmaxf(hi[e], fabsf(X.f(i, e))) : fmaxf(hi[e], X.f(i, e));
+        }
+      }
+    }
+    // both reductions share one barrier
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      lo[e] = fminf(lo[e], __shfl_xor(lo[e], 16));
+      lo[e] = fminf(lo[e], __shfl_xor(lo[e], 32));
+      hi[e] = fmaxf(hi[e], __shfl_xor(hi[e], 16));
+      hi[e] = fmaxf(hi[e], __shfl_xor(hi[e], 32));
+    }
+    if (r == 0) {
+      float4* dl = reinterpret_cast<float4*>(&sm.rlo[w][8 * g]);
+      float4* dh = reinterpret_cast<float4*>(&sm.rhi[w][8 * g]);
+      dl[0] = make_float4(lo[0], lo[1], lo[2], lo[3]); dl[1] = make_float4(lo[4], lo[5], lo[6], lo[7]);
+      dh[0] = make_float4(hi[0], hi[1], hi[2], hi[3]); dh[1] = make_float4(hi[4], hi[5], hi[6], hi[7]);
+    }
     __syncthreads();
-    float sd = varn_std(sm, 0, v, hf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = 8 * g + e;
+      const float l = fminf(fminf(fminf(sm.rlo[0][c], sm.rlo[1][c]), sm.rlo[2][c]), sm.rlo[3][c]);
+      const float u = fmaxf(fmaxf(fmaxf(sm.rhi[0][c], sm.rhi[1][c]), sm.rhi[2][c]), sm.rhi[3][c]);
+      stats_of<MODE, BITS>(l, u, u, sa[e], sb[e]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (!is_out(i, e)) { lo = fminf(lo, X.f(i, e)); hi = fmaxf(hi, X.f(i, e)); }
+      }
+      lo = tok_reduce(lo, MinF());
+      hi = tok_reduce(hi, MaxF());
+      stats_of<MODE, BITS>(lo, hi, hi, sa[i], sb[i]);
+    }
+  }
+
+  // ---- statistics out
+  {
+    uint8_t* st = rec + (tensor == 0 ? a.lay.ks : a.lay.vs);
+    if constexpr (per_chan) {
+      if (w == 0 && r == 0) {
+        if constexpr (MODE == SYM) {
+          uint32_t hw[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            hw[k] = __builtin_bit_cast(uint32_t, __halves2half2(__float2half_rn(sa[2 * k]), __float2half_rn(sa[2 * k + 1])));
+          *reinterpret_cast<uint4*>(st + 16 * g) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        } else {
+          float4* ds = reinterpret_cast<float4*>(st) + 2 * g;
+          float4* dm = reinterpret_cast<float4*>(st + 512) + 2 * g;
+          ds[0] = make_float4(sa[0], sa[1], sa[2], sa[3]); ds[1] = make_float4(sa[4], sa[5], sa[6], sa[7]);
+          dm[0] = make_float4(sb[0], sb[1], sb[2], sb[3]); dm[1] = make_float4(sb[4], sb[5], sb[6], sb[7]);
+        }
+      }
+    } else if (g == 0) {
+      float* ds = reinterpret_cast<float*>(st);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = 32 * w + 4 * i + r;
+        ds[t] = sa[i];
+        ds[128 + t] = sb[i];
+      }
+    }
+  }
+
+  // ---- codes
+  if constexpr (MODE != KVARN) opaque(X.v);
+  if constexpr (TENSOR == 0) {
+    // key rows, token-major: this lane's 8 codes of row t_i go straight to memory
+    uint8_t* kc = rec + a.lay.kc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = 32 * w + 4 * i + r;
+      uint32_t c[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c[e] = code_of<MODE, BITS>(X.f(i, e), sa[e], sb[e], lut);
+      uint8_t* row = kc + (size_t)t * R;
+      if constexpr (BITS == 4) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v |= c[e] << (4 * e);
+        *reinterpret_cast<uint32_t*>(row + 4 * g) = v;
+      } else if constexpr (BITS == 2) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v |= c[e] << (2 * e);
+        *reinterpret_cast<uint16_t*>(row + 2 * g) = (uint16_t)v;
+      } else {
+        uint32_t lo2 = 0, hi1 = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          lo2 |= (c[e] & 3u) << (2 * e);
+          hi1 |= ((c[e] >> 2) & 1u) << e;
+        }
+        *reinterpret_cast<uint16_t*>(row + 2 * g) = (uint16_t)lo2;
+        row[32 + g] = (uint8_t)hi1;
+      }
+    }
+  } else {
+    // value codes: LDS tile, then one thread per channel-major half-row
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = 32 * w + 4 * i + r;
+      uint32_t c[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        c[e] = code_of<MODE, BITS>(X.f(i, e), per_chan ? sa[e] : sa[i], per_chan ? sb[e] : sb[i], lut);
+      *reinterpret_cast<uint2*>(&sm.vq[t * kD + 8 * g]) =
+          make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+    }
     __syncthreads();
-    if (hf == 0 && sd > 0.f) sm.cl[v] = __fadd_rn(sm.cl[v], logf(sd));
+    {
+      constexpr int RH = R / 2;
+      const int half = tid >> 7, c = tid & 127;
+      // position p of the half-row holds token 16*((p>>2)&3) + 4*(p>>4) + (p&3) of the half
+      auto code = [&](int p) -> uint32_t {
+        return sm.vq[(64 * half + 16 * ((p >> 2) & 3) + 4 * (p >> 4) + (p & 3)) * kD + c];
+      };
+      uint8_t* dst = rec + a.lay.vc + (size_t)(half * 128 + c) * RH;
+      if constexpr (BITS == 4) {
+        uint32_t wd[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v |= code(8 * k + e) << (4 * e);
+          wd[k] = v;
+        }
+        reinterpret_cast<uint4*>(dst)[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        reinterpret_cast<uint4*>(dst)[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+      } else if constexpr (BITS == 2) {
+        uint32_t wd[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) v |= code(16 * k + e) << (2 * e);
+          wd[k] = v;
+        }
+        *reinterpret_cast<uint4*>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      } else {
+        uint32_t lo2[4], hi1[2] = {0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t cc = code(16 * k + e);
+            v |= (cc & 3u) << (2 * e);
+            hi1[k >> 1] |= ((cc >> 2) & 1u) << (16 * (k & 1) + e);
+          }
+          lo2[k] = v;
+        }
+        *reinterpret_cast<uint4*>(dst) = make_uint4(lo2[0], lo2[1], lo2[2], lo2[3]);
+        *reinterpret_cast<uint2*>(dst + 16) = make_uint2(hi1[0], hi1[1]);
+      }
+    }
+  }
+
+  // ---- outliers: keys CSR by token (row t, column c), values CSC by channel (row c,
+  // column t); entries sorted by (row, column), fp16 value bits kept exactly
+  if (MODE != KVARN && k_out > 0) {
+    opaque(X.v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (is_out(i, e)) {
+          const int t = 32 * w + 4 * i + r, c = 8 * g + e;
+          const int row = tensor == 0 ? t : c, col = tensor == 0 ? c : t;
+          atomicOr(&sm.omask[row][col >> 5], 1u << (col & 31));
+        }
     __syncthreads();
-    if (tid < 128) sm.cb[tid] = expf(-sm.cl[tid]);
+    if (w == 0) {
+      const int n0 = __popc(sm.omask[2 * lane][0]) + __popc(sm.omask[2 * lane][1]) + __popc(sm.omask[2 * lane][2]) +
+                     __popc(sm.omask[2 * lane][3]);
+      const int n1 = __popc(sm.omask[2 * lane + 1][0]) + __popc(sm.omask[2 * lane + 1][1]) +
+                     __popc(sm.omask[2 * lane + 1][2]) + __popc(sm.omask[2 * lane + 1][3]);
+      int incl = n0 + n1;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+      }
+      const int excl = incl - n0 - n1;
+      sm.optr[2 * lane] = (uint16_t)excl;
+      sm.optr[2 * lane + 1] = (uint16_t)(excl + n0);
+      if (lane == 63) sm.optr[128] = (uint16_t)incl;
+    }
     __syncthreads();
-    sd = varn_std(sm, 1, v, hf);
-    __syncthreads();
-    if (hf == 0 && sd > 0.f) sm.rl[v] = __fadd_rn(sm.rl[v], logf(sd));
-    __syncthreads();
+    __half* val = reinterpret_cast<__half*>(rec + (tensor == 0 ? a.lay.ko_val : a.lay.vo_val));
+    uint16_t* ptr = reinterpret_cast<uint16_t*>(rec + (tensor == 0 ? a.lay.ko_ptr : a.lay.vo_ptr));
+    uint8_t* idx = rec + (tensor == 0 ? a.lay.ko_idx : a.lay.vo_idx);
+    if (tid <= 128) ptr[tid] = sm.optr[tid];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (is_out(i, e)) {
+          const int t = 32 * w + 4 * i + r, c = 8 * g + e;
+          const int row = tensor == 0 ? t : c, col = tensor == 0 ? c : t;
+          int pos = sm.optr[row];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t m = sm.omask[row][d];
+            const int lim = col - 32 * d;   // bits of word d below col
+            pos += lim >= 32 ? __popc(m) : (lim > 0 ? __popc(m & ((1u << lim) - 1u)) : 0);
+          }
+          val[pos] = __float2half_rn(X.f(i, e));   // exact: x is a widened fp16
+          idx[pos] = (uint8_t)col;
+        }
   }
 }
 
 template <int MODE, int BITS>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
-  __shared__ QuantSmem sm;
-  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const size_t unit = (size_t)b * a.Hkv + h;
-  uint8_t* rec = a.rec + (unit * a.max_blocks + (size_t)(a.blk0 + j)) * a.lay.rec_bytes;
-  constexpr int R = 16 * BITS;                 // bytes per 128 codes
-  constexpr int QMAX = (1 << BITS) - 1;
-  const int k_out = a.k_out;
-
-  for (int tensor = 0; tensor < 2; ++tensor) {
-    const __half* in = (tensor ? a.v_in : a.k_in) + unit * (size_t)a.n_new * kD;
-    const __half* tl = a.tail + unit * (2 * kT * kD) + (size_t)tensor * kT * kD;
-    // --- stage the block: rows < t0 of block 0 come from the fp16 tail
-    for (int id = tid; id < kT * 16; id += kThreads) {
-      const int row = id >> 4, ch = (id & 15) * 8;
-      const __half* src = (j == 0 && row < a.t0) ? tl + row * kD + ch
-                                                 : in + (size_t)(j * kT + row - a.t0) * kD + ch;
-      const uint4 w = *reinterpret_cast<const uint4*>(src);
-      const __half* hv = reinterpret_cast<const __half*>(&w);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm.x[row * kPitch + ch + e] = __half2float(hv[e]);
-    }
-    if (tid < 16 && MODE == NUQ) sm.lut[tid] = a.cb[(h * 2 + tensor) * 16 + tid];
-    __syncthreads();
-
-    // vector axis: keys per channel; values per token, except symmetric int4
-    const int va = (tensor == 0 || MODE == SYM) ? 0 : 1;
-
-    if constexpr (MODE == KVARN) {
-      fwht_rows(sm, tid);
-      varn(sm, tid, a.varn_iters);
-      // s1: keys per token, values per channel; divide the tile by it
-      if (tid < 128) {
-        const float s1 = expf(tensor == 0 ? sm.rl[tid] : sm.cl[tid]);
-        sm.ra[tid] = s1;
-        float* dst = reinterpret_cast<float*>(rec + (tensor == 0 ? a.lay.k1 : a.lay.v1));
-        dst[tid] = s1;
-      }
-      __syncthreads();
-      for (int id = tid; id < kT * kD; id += kThreads) {
-        const int t = id >> 7, c = id & 127;
-        float& x = sm.x[t * kPitch + c];
-        x = __fdiv_rn(x, sm.ra[tensor == 0 ? t : c]);
-      }
-      __syncthreads();
-    }
-
-    // --- per vector: outliers, statistics, codes (two threads per vector)
-    const int v = tid >> 1, hf = tid & 1;
-    uint64_t thr = ~0ull;
-    if (MODE != KVARN && k_out > 0) {
-      uint64_t prev = ~0ull;
-      for (int p = 0; p < k_out; ++p) {
-        uint64_t best = 0;
-        for (int i = 0; i < 64; ++i) {
-          const int e = hf * 64 + i;
-          const uint64_t key = mag_key(sm.x[xidx(va, v, e)], e);
-          if (key < prev && key > best) best = key;
-        }
-        const uint64_t o = shfl_xor_u64(best, 1);
-        best = o > best ? o : best;
-        if (hf == 0) sm.olist[v * kMaxOut + p] = (uint8_t)(255 - (int)(best & 255));
-        prev = best;
-      }
-      thr = prev;
-    }
-    float lo = INFINITY, hi = -INFINITY, amax = 0.f;
-    for (int i = 0; i < 64; ++i) {
-      const int e = hf * 64 + i;
-      const float x = sm.x[xidx(va, v, e)];
-      const bool outl = (MODE != KVARN && k_out > 0) && mag_key(x, e) >= thr;
-      if (!outl) { lo = fminf(lo, x); hi = fmaxf(hi, x); amax = fmaxf(amax, fabsf(x)); }
-    }
-    lo = fminf(lo, __shfl_xor(lo, 1));
-    hi = fmaxf(hi, __shfl_xor(hi, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-
-    float sa, sb;           // RTN/KVARN: s, m; NUQ: z, h; SYM: s (fp16-rounded), unused
-    if constexpr (MODE == NUQ) {
-      sa = __fmul_rn(__fadd_rn(hi, lo), 0.5f);
-      sb = __fmul_rn(__fsub_rn(hi, lo), 0.5f);
-    } else if constexpr (MODE == SYM) {
-      sa = __half2float(__float2half_rn(__fdiv_rn(amax, 7.0f)));
-      sb = 0.f;
-    } else {
-      sa = __fdiv_rn(__fsub_rn(hi, lo), (float)QMAX);
-      sb = lo;
-    }
-    for (int i = 0; i < 64; ++i) {
-      const int e = hf * 64 + i;
-      const float x = sm.x[xidx(va, v, e)];
-      int code;
-      if constexpr (MODE == NUQ) {
-        float u = sb == 0.f ? 0.f : __fdiv_rn(__fsub_rn(x, sa), sb);
-        u = fminf(fmaxf(u, -1.f), 1.f);
-        float best = INFINITY;
-        code = 0;
-#pragma unroll
-        for (int c = 0; c <= QMAX; ++c) {
-          const float d = fabsf(__fsub_rn(u, sm.lut[c]));
-          if (d < best) { best = d; code = c; }
-        }
-      } else if constexpr (MODE == SYM) {
-        const float r = sa == 0.f ? 0.f : rintf(__fdiv_rn(x, sa));
-        code = (int)fminf(fmaxf(r, -8.f), 7.f) + 8;
-      } else {
-        const float r = sa == 0.f ? 0.f : rintf(__fdiv_rn(__fsub_rn(x, sb), sa));
-        code = (int)fminf(fmaxf(r, 0.f), (float)QMAX);
-      }
-      const int t = va == 0 ? e : v, c = va == 0 ? v : e;
-      sm.q[t * kD + c] = (uint8_t)code;
-    }
-    // statistics of vector v
-    if (hf == 0) {
-      uint8_t* st = rec + (tensor == 0 ? a.lay.ks : a.lay.vs);
-      if constexpr (MODE == SYM) {
-        reinterpret_cast<__half*>(st)[v] = __float2half_rn(sa);
-      } else if constexpr (MODE == NUQ) {
-        reinterpret_cast<float*>(st)[v] = sa;          // z
-        reinterpret_cast<float*>(st)[128 + v] = sb;    // h
-      } else {
-        reinterpret_cast<float*>(st)[v] = sa;          // s
-        reinterpret_cast<float*>(st)[128 + v] = sb;    // m
-      }
-    }
-    __syncthreads();
-
-    // --- pack codes
-    if (tensor == 0) {
-      // key rows, token-major: row t = channels 0..127
-      constexpr int DW = R / 4;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(rec + a.lay.kc);
-      for (int id = tid; id < kT * DW; id += kThreads) {
-        const int t = id / DW, w = id % DW;
-        dst[id] = pack_dword<BITS>(128, w, [&](int i) { return sm.q[t * kD + i]; });
-      }
-    } else {
-      // value rows, channel-major in two token halves: row (half, c) = tokens 64*half + i
-      constexpr int DW = R / 8;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(rec + a.lay.vc);
-      for (int id = tid; id < 2 * kD * DW; id += kThreads) {
-        const int row = id / DW, w = id % DW;
-        const int half = row >> 7, c = row & 127;
-        // position i of a half-row holds token 16*((i>>2)&3) + 4*(i>>4) + (i&3) of the half
-        dst[id] = pack_dword<BITS>(64, w, [&](int i) {
-          return sm.q[(64 * half + 16 * ((i >> 2) & 3) + 4 * (i >> 4) + (i & 3)) * kD + c];
-        });
-      }
-    }
-
-    // --- outliers: keys CSR by token, values CSC by channel, sorted by (row, column)
-    if (MODE != KVARN && k_out > 0) {
-      // storage row r and column u: keys (r = token, u = channel), values (r = channel, u = token)
-      auto member = [&](int r, int u) -> bool {
-        const int t = tensor == 0 ? r : u, c = tensor == 0 ? u : r;
-        const int vv = va == 0 ? c : t, ee = va == 0 ? t : c;
-        for (int p = 0; p < k_out; ++p)
-          if (sm.olist[vv * kMaxOut + p] == ee) return true;
-        return false;
-      };
-      if (tid < 128) {
-        int n = 0;
-        for (int u = 0; u < 128; ++u) n += member(tid, u) ? 1 : 0;
-        sm.cnt[tid + 1] = n;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        sm.cnt[0] = 0;
-        for (int r = 0; r < 128; ++r) sm.cnt[r + 1] += sm.cnt[r];
-      }
-      __syncthreads();
-      uint8_t* base = rec;
-      __half* val = reinterpret_cast<__half*>(base + (tensor == 0 ? a.lay.ko_val : a.lay.vo_val));
-      uint16_t* ptr = reinterpret_cast<uint16_t*>(base + (tensor == 0 ? a.lay.ko_ptr : a.lay.vo_ptr));
-      uint8_t* idx = base + (tensor == 0 ? a.lay.ko_idx : a.lay.vo_idx);
-      if (tid <= 128) ptr[tid] = (uint16_t)sm.cnt[tid];
-      if (tid < 128) {
-        int pos = sm.cnt[tid];
-        for (int u = 0; u < 128; ++u) {
-          if (member(tid, u)) {
-            const int t = tensor == 0 ? tid : u, c = tensor == 0 ? u : tid;
-            val[pos] = __float2half_rn(sm.x[t * kPitch + c]);   // exact: the tile holds widened fp16
-            idx[pos] = (uint8_t)u;
-            ++pos;
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MODE == KVARN ? 2 : 4))) void quantize_kernel(QuantArgs a) {
+  __shared__ Smem sm;
+  const int j = blockIdx.x >> 1, h = blockIdx.y, b = blockIdx.z;
+  if (blockIdx.x & 1) quantize_tensor<MODE, BITS, 1>(a, sm, j, h, b);
+  else quantize_tensor<MODE, BITS, 0>(a, sm, j, h, b);
 }
 
 __global__ __launch_bounds__(kThreads) void tail_kernel(TailArgs a) {
@@ -349,7 +649,8 @@ __global__ __launch_bounds__(kThreads) void tail_kernel(TailArgs a) {
 
 template <int MODE, int BITS>
 hipError_t launch_q(const QuantArgs& a, int n_blocks, int batch, hipStream_t s) {
-  hipLaunchKernelGGL((quantize_kernel<MODE, BITS>), dim3(n_blocks, a.Hkv, batch), dim3(kThreads), 0, s, a);
+  // x: (block, tensor) pairs, tensor = the low bit
+  hipLaunchKernelGGL((quantize_kernel<MODE, BITS>), dim3(2 * n_blocks, a.Hkv, batch), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
