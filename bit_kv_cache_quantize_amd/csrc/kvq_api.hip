@@ -29,6 +29,45 @@ kvq_status ok() { return KVQ_OK; }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+static_assert(KVQ_MAX_SPLITS == kvq::kMaxSplits, "split limit");
+
+// Smallest distance between consecutive NUQ codebook entries: with entries at least this far
+// apart, fp32 rounding of |u - C_j| (u, C_j in [-1, 1]) can never make an entry tie with or beat
+// a nearer one (the spacing of fp32 values up to 2 is at most 2^-22).
+constexpr double kMinCodebookGap = 1.0 / (1 << 21);
+
+// Order-preserving map between fp32 values and integers (for a binary search over floats).
+int32_t f2key(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return (u & 0x80000000u) ? -(int32_t)(u & 0x7fffffffu) : (int32_t)u;
+}
+float key2f(int32_t k) {
+  const uint32_t u = k < 0 ? ((uint32_t)(-k) | 0x80000000u) : (uint32_t)k;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Decision threshold between consecutive NUQ entries lo < hi (KVQuant notes 1.2 and 3.3: the
+// code is the argmin of |u - C_j|, ties to the smaller index). The predicate "hi is strictly
+// closer than lo" in fp32, P(u) = |RN(u - hi)| < |RN(u - lo)|, is false at u = lo, true at
+// u = hi and monotone in u, so it switches at one fp32 value tau. With sorted entries at least
+// kMinCodebookGap apart, the first-index argmin over all entries equals the number of
+// thresholds tau_j <= u, which the quantize kernel evaluates with a short binary search.
+float nuq_threshold(float lo, float hi) {
+  auto closer_hi = [&](float u) {
+    const float dlo = std::fabs(u - lo), dhi = std::fabs(u - hi);
+    return dhi < dlo;
+  };
+  int32_t a = f2key(lo), b = f2key(hi);   // P(key2f(a)) false, P(key2f(b)) true
+  while (b - a > 1) {
+    const int32_t m = a + (b - a) / 2;
+    if (closer_hi(key2f(m))) b = m; else a = m;
+  }
+  return key2f(b);
+}
+
 }  // namespace
 
 namespace kvq {
@@ -132,7 +171,7 @@ Regions regions(const kvq_config* c) {
   r.rec = r.layer_rec * c->n_layers;
   r.layer_tail = units * 2 * kvq::kT * kvq::kD * sizeof(__half);
   r.tail = r.layer_tail * c->n_layers;
-  r.cb = c->mode == KVQ_MODE_NUQ ? (size_t)c->n_layers * c->n_kv_heads * 2 * 16 * sizeof(float) : 0;
+  r.cb = c->mode == KVQ_MODE_NUQ ? (size_t)c->n_layers * c->n_kv_heads * 2 * kvq::kCbStride * sizeof(float) : 0;
   r.rope_base = c->pre_rope ? (size_t)(r.max_blocks + 1) * 64 * 2 * sizeof(float) : 0;
   r.rope_off = c->pre_rope ? ((size_t)128 * 64 * 2 + 64) * sizeof(float) : 0;   // offsets, then theta_i
   r.work = (size_t)c->batch * c->n_q_heads * KVQ_MAX_SPLITS * kvq::kPartStride * sizeof(float);
@@ -199,7 +238,7 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_buf, size_t bytes, vo
   c->off_work = r.off_work;
   c->len.assign(cfg->n_layers, 0);
   c->cb_loaded.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2, 0);
-  c->cb_host.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2 * 16, 0.f);
+  c->cb_host.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2 * kvq::kCbStride, 0.f);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (cfg->pre_rope) {
     // RoPE angles n * theta_i, theta_i = theta^(-2i/128), evaluated in double precision:
@@ -250,13 +289,17 @@ kvq_status kvq_codebook_load(kvq_cache c, int layer, int kv_head, int which, con
   for (int i = 0; i < n_entries; ++i) {
     const float v = host_codebook[i];
     if (!std::isfinite(v) || v < -1.f || v > 1.f) return fail(KVQ_ERR_ARG, "codebook entry %d not in [-1, 1]", i);
-    if (i > 0 && !(v > host_codebook[i - 1])) return fail(KVQ_ERR_ARG, "codebook not strictly ascending at %d", i);
+    if (i > 0 && !((double)v - (double)host_codebook[i - 1] >= kMinCodebookGap))
+      return fail(KVQ_ERR_ARG, "codebook entries %d and %d are not ascending by at least 2^-21", i - 1, i);
   }
   const size_t slot = ((size_t)layer * c->cfg.n_kv_heads + kv_head) * 2 + which;
-  float* dst = c->cb_host.data() + slot * 16;
-  for (int i = 0; i < 16; ++i) dst[i] = i < n_entries ? host_codebook[i] : 0.f;
-  st = hip_check(hipMemcpyAsync(c->base + c->off_cb + slot * 16 * sizeof(float), dst, 16 * sizeof(float),
-                                hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)), "upload codebook");
+  float* dst = c->cb_host.data() + slot * kvq::kCbStride;
+  for (int i = 0; i < kvq::kCbStride; ++i) dst[i] = 0.f;
+  for (int i = 0; i < n_entries; ++i) dst[i] = host_codebook[i];
+  for (int i = 0; i + 1 < n_entries; ++i) dst[16 + i] = nuq_threshold(host_codebook[i], host_codebook[i + 1]);
+  st = hip_check(hipMemcpyAsync(c->base + c->off_cb + slot * kvq::kCbStride * sizeof(float), dst,
+                                kvq::kCbStride * sizeof(float), hipMemcpyHostToDevice,
+                                static_cast<hipStream_t>(stream)), "upload codebook");
   if (st != KVQ_OK) return st;
   c->cb_loaded[slot] = 1;
   return ok();
@@ -301,7 +344,7 @@ kvq_status kvq_quantize_append(kvq_cache c, int layer, const void* k_f16, const 
     a.max_blocks = c->max_blocks;
     a.rec = c->base + c->off_rec + (size_t)layer * c->layer_rec_bytes;
     a.tail = tail;
-    a.cb = reinterpret_cast<const float*>(c->base + c->off_cb) + (size_t)layer * cfg.n_kv_heads * 2 * 16;
+    a.cb = reinterpret_cast<const float*>(c->base + c->off_cb) + (size_t)layer * cfg.n_kv_heads * 2 * kvq::kCbStride;
     st = hip_check(kvq::launch_quantize(cfg.mode, cfg.bits, a, nb, cfg.batch, s), "launch quantize");
     if (st != KVQ_OK) return st;
   }
@@ -355,7 +398,7 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
   a.k_out = cfg.outliers_per_vec;
   a.rec = c->base + c->off_rec + (size_t)layer * c->layer_rec_bytes;
   a.tail = reinterpret_cast<const __half*>(c->base + c->off_tail + (size_t)layer * c->layer_tail_bytes);
-  a.cb = reinterpret_cast<const float*>(c->base + c->off_cb) + (size_t)layer * cfg.n_kv_heads * 2 * 16;
+  a.cb = reinterpret_cast<const float*>(c->base + c->off_cb) + (size_t)layer * cfg.n_kv_heads * 2 * kvq::kCbStride;
   a.rope_base = reinterpret_cast<const float*>(c->base + c->off_rope_base);
   a.rope_off = reinterpret_cast<const float*>(c->base + c->off_rope_off);
   a.q = static_cast<const __half*>(q_f16);

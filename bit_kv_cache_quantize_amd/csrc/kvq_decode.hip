@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   for (int i = tid; i < G * 128; i += kThreads)
     s_q[i] = __half2float(a.q[((size_t)b * a.Hq + (size_t)kvh * G) * 128 + i]);
-  if (MODE == NUQ && tid < 32) s_lut[tid] = a.cb[(kvh * 2 + (tid >> 4)) * 16 + (tid & 15)];
+  if (MODE == NUQ && tid < 32) s_lut[tid] = a.cb[(kvh * 2 + (tid >> 4)) * kCbStride + (tid & 15)];
   if (ROPE && tid < 64) s_theta[tid] = a.rope_off[128 * 64 * 2 + tid];
   __syncthreads();
 
@@ -128,18 +128,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // Merge the split partials of one (sequence, query head) with the log-sum-exp rule.
+// The (m, l) pairs of all splits are staged in LDS first, so the loads of the per-channel
+// partials are independent and stay in flight together.
 __global__ __launch_bounds__(128) void combine_kernel(const float* part_all, float* out, int Hq, int splits) {
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_l[kMaxSplits];
   const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
   const size_t row = (size_t)b * Hq + hq;
   const float* part = part_all + row * splits * kPartStride;
+  if (c < splits) {
+    s_w[c] = part[c * kPartStride];
+    s_l[c] = part[c * kPartStride + 1];
+  }
+  __syncthreads();
   float M = -INFINITY;
-  for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, part[sp * kPartStride]);
+  for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, s_w[sp]);
   float L = 0.f, o = 0.f;
+#pragma unroll 8
   for (int sp = 0; sp < splits; ++sp) {
-    const float m = part[sp * kPartStride];
-    if (m == -INFINITY) continue;
-    const float wgt = exp2f(m - M);
-    L = fmaf(wgt, part[sp * kPartStride + 1], L);
+    const float m = s_w[sp];
+    const float wgt = m == -INFINITY ? 0.f : exp2f(m - M);
+    L = fmaf(wgt, s_l[sp], L);
     o = fmaf(wgt, part[sp * kPartStride + 2 + c], o);
   }
   out[row * kD + c] = o / L;

@@ -12,6 +12,10 @@ constexpr int kT = 128;          // tokens per quantization block
 constexpr int kD = 128;          // head dimension
 constexpr int kMaxOut = 8;       // outliers per vector
 constexpr int kPartStride = 2 + kD;  // one split partial: m, l, o[128]
+constexpr int kMaxSplits = 64;       // decode splits per (sequence, kv head)
+// Device codebook slot per (layer, kv head, K/V): entries C[0..15], then the NUQ decision
+// thresholds tau[0..14] (see kvq_api.hip).
+constexpr int kCbStride = 32;
 
 enum Mode { RTN = 0, NUQ = 1, KVARN = 2, SYM = 3 };
 
@@ -34,7 +38,7 @@ struct QuantArgs {
   int Hkv, max_blocks;
   uint8_t* rec;          // records of the layer, [B][Hkv][max_blocks]
   const __half* tail;    // tails of the layer, [B][Hkv][2][128][128]
-  const float* cb;       // codebooks of the layer, [Hkv][2][16]
+  const float* cb;       // codebooks of the layer, [Hkv][2][kCbStride]
 };
 
 struct TailArgs {

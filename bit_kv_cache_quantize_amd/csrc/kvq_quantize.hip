@@ -45,13 +45,21 @@ struct Smem {
   uint32_t red[2][4][kD];         // per-channel cross-wave partials, two alternating buffers
   float rlo[4][kD], rhi[4][kD];   // per-channel min / max partials
   uint32_t omask[kD][4];          // outlier bitmask per storage row
+  uint32_t okey[kD][kMaxOut];     // selection keys of each vector's outliers
   uint16_t optr[kD + 1];          // storage row pointers
 };
 
-// Order of the top-k |x| selection: larger magnitude first, then lower element index.
-// x is a widened fp16, so the fp32 magnitude bits below bit 13 are zero.
+// Key of the top-k |x| selection: larger magnitude first, then lower element index e; the
+// lowest bit carries the sign, so that a key alone gives back the element's position and
+// its exact fp16 value (magnitude bits 8..22, sign bit 0, index 127 - bits 1..7).
 __device__ __forceinline__ uint32_t mag_key(float x, int e) {
-  return (((__float_as_uint(x) & 0x7fffffffu) >> 13) << 7) | (uint32_t)(127 - e);
+  // fp32 form (KVarN tiles, which never select outliers): magnitude bits above bit 13
+  const uint32_t u = __float_as_uint(x);
+  return (((u & 0x7fffffffu) >> 13) << 8) | ((uint32_t)(127 - e) << 1) | (u >> 31);
+}
+__device__ __forceinline__ uint32_t key_index(uint32_t key) { return 127u - ((key >> 1) & 127u); }
+__device__ __forceinline__ uint16_t key_f16_bits(uint32_t key) {
+  return (uint16_t)(((key >> 8) & 0x7fffu) | ((key & 1u) << 15));
 }
 
 // The block tile of one lane: 8 tokens x 8 channels. Non-KVarN modes keep the fp16
@@ -67,7 +75,10 @@ template <> struct Tile<false> {
   uint32_t v[8][4];
   __device__ __forceinline__ uint32_t bits(int i, int e) const { return (e & 1) ? v[i][e >> 1] >> 16 : v[i][e >> 1] & 0xffffu; }
   __device__ __forceinline__ float f(int i, int e) const { return __half2float(__ushort_as_half((unsigned short)bits(i, e))); }
-  __device__ __forceinline__ uint32_t key(int i, int e, int idx) const { return ((bits(i, e) & 0x7fffu) << 7) | (uint32_t)(127 - idx); }
+  __device__ __forceinline__ uint32_t key(int i, int e, int idx) const {
+    const uint32_t h = bits(i, e);
+    return ((h & 0x7fffu) << 8) | ((uint32_t)(127 - idx) << 1) | (h >> 15);
+  }
 };
 
 struct MaxU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
@@ -225,43 +236,80 @@ __device__ __forceinline__ void varn(float (&x)[8][8], float (&rl)[8], float (&c
   }
 }
 
-// Code of one element given the vector's statistics (sa, sb): RTN/KVarN (s, m), NUQ (z, h),
-// symmetric int4 (s, -).
-template <int MODE, int BITS>
-__device__ __forceinline__ uint32_t code_of(float x, float sa, float sb, const float* lut) {
-  constexpr int QMAX = (1 << BITS) - 1;
-  if constexpr (MODE == NUQ) {
-    float u = sb == 0.f ? 0.f : __fdiv_rn(__fsub_rn(x, sa), sb);
-    u = fminf(fmaxf(u, -1.f), 1.f);
-    float best = INFINITY;
-    uint32_t code = 0;
-#pragma unroll
-    for (int c = 0; c <= QMAX; ++c) {
-      const float d = fabsf(__fsub_rn(u, lut[c]));
-      if (d < best) { best = d; code = c; }
-    }
-    return code;
-  } else if constexpr (MODE == SYM) {
-    const float q = sa == 0.f ? 0.f : rintf(__fdiv_rn(x, sa));
-    return (uint32_t)((int)fminf(fmaxf(q, -8.f), 7.f) + 8);
+// RN(d / s) from r = RN(1 / s): q0 = RN(d r), the exact residual e = d - q0 s (one fma),
+// then RN(q0 + e r). With a correctly rounded reciprocal this correction step returns the
+// correctly rounded quotient (Markstein's theorem; no overflow or underflow occurs for
+// these operands), i.e. the same value as an IEEE division, in three instructions.
+__device__ __forceinline__ float div_rn(float d, float s, float r) {
+  const float q0 = __fmul_rn(d, r);
+  const float e = __fmaf_rn(-q0, s, d);
+  return __fmaf_rn(e, r, q0);
+}
+
+// NUQ code = number of decision thresholds tau_j <= u (tau ascending, 2^b - 1 of them; the
+// host derives them from the codebook so that this equals the first-index argmin of the
+// fp32 distances |u - C_j|), found by binary search over the bits of the code.
+template <int BITS>
+__device__ __forceinline__ uint32_t nuq_search(float u, const float* tau) {
+  if constexpr (BITS == 2) {
+    const bool b1 = u >= tau[1];
+    const bool b0 = u >= (b1 ? tau[2] : tau[0]);
+    return (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+  } else if constexpr (BITS == 3) {
+    const bool b2 = u >= tau[3];
+    const bool b1 = u >= (b2 ? tau[5] : tau[1]);
+    const bool b0 = u >= (b2 ? (b1 ? tau[6] : tau[4]) : (b1 ? tau[2] : tau[0]));
+    return (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
   } else {
-    const float q = sa == 0.f ? 0.f : rintf(__fdiv_rn(__fsub_rn(x, sb), sa));
-    return (uint32_t)fminf(fmaxf(q, 0.f), (float)QMAX);
+    const bool b3 = u >= tau[7];
+    const bool b2 = u >= (b3 ? tau[11] : tau[3]);
+    const bool b1 = u >= (b3 ? (b2 ? tau[13] : tau[9]) : (b2 ? tau[5] : tau[1]));
+    const float t0 = b3 ? (b2 ? (b1 ? tau[14] : tau[12]) : (b1 ? tau[10] : tau[8]))
+                        : (b2 ? (b1 ? tau[6] : tau[4]) : (b1 ? tau[2] : tau[0]));
+    const bool b0 = u >= t0;
+    return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
   }
 }
 
-// Statistics (sa, sb) of a vector from its min / max / max|x| over the non-outliers.
+// Statistics of one vector: (sa, sb) = RTN/KVarN (s, m), NUQ (z, h), symmetric int4 (s, -),
+// and rc = RN(1 / divisor) for the element divisions.
+struct VecStats { float sa, sb, rc; };
+
 template <int MODE, int BITS>
-__device__ __forceinline__ void stats_of(float lo, float hi, float amax, float& sa, float& sb) {
+__device__ __forceinline__ VecStats stats_of(float lo, float hi, float amax) {
+  VecStats v;
   if constexpr (MODE == NUQ) {
-    sa = __fmul_rn(__fadd_rn(hi, lo), 0.5f);   // z
-    sb = __fmul_rn(__fsub_rn(hi, lo), 0.5f);   // h
+    v.sa = __fmul_rn(__fadd_rn(hi, lo), 0.5f);   // z
+    v.sb = __fmul_rn(__fsub_rn(hi, lo), 0.5f);   // h
+    v.rc = __fdiv_rn(1.f, v.sb);
   } else if constexpr (MODE == SYM) {
-    sa = __half2float(__float2half_rn(__fdiv_rn(amax, 7.0f)));
-    sb = 0.f;
+    v.sa = __half2float(__float2half_rn(__fdiv_rn(amax, 7.0f)));
+    v.sb = 0.f;
+    v.rc = __fdiv_rn(1.f, v.sa);
   } else {
-    sa = __fdiv_rn(__fsub_rn(hi, lo), (float)((1 << BITS) - 1));   // s
-    sb = lo;                                                       // m
+    v.sa = __fdiv_rn(__fsub_rn(hi, lo), (float)((1 << BITS) - 1));   // s
+    v.sb = lo;                                                       // m
+    v.rc = __fdiv_rn(1.f, v.sa);
+  }
+  return v;
+}
+
+// Code of one element: RTN/KVarN clamp(rint((x - m) / s)), NUQ argmin over the codebook of
+// clamp((x - z) / h, -1, 1), symmetric int4 clamp(rint(x / s), -8, 7) + 8; a zero divisor
+// gives code 0 (symmetric: 8).
+template <int MODE, int BITS>
+__device__ __forceinline__ uint32_t code_of(float x, const VecStats& v, const float* tau) {
+  constexpr int QMAX = (1 << BITS) - 1;
+  if constexpr (MODE == NUQ) {
+    float u = v.sb == 0.f ? 0.f : div_rn(__fsub_rn(x, v.sa), v.sb, v.rc);
+    u = fminf(fmaxf(u, -1.f), 1.f);
+    return nuq_search<BITS>(u, tau);
+  } else if constexpr (MODE == SYM) {
+    const float q = v.sa == 0.f ? 0.f : rintf(div_rn(x, v.sa, v.rc));
+    return (uint32_t)((int)fminf(fmaxf(q, -8.f), 7.f) + 8);
+  } else {
+    const float q = v.sa == 0.f ? 0.f : rintf(div_rn(__fsub_rn(x, v.sb), v.sa, v.rc));
+    return (uint32_t)fminf(fmaxf(q, 0.f), (float)QMAX);
   }
 }
 
@@ -308,10 +356,10 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       }
     }
   }
-  float lut[16];
+  float tau[16];   // NUQ decision thresholds (uniform: scalar registers)
   if constexpr (MODE == NUQ) {
 #pragma unroll
-    for (int c = 0; c < 16; ++c) lut[c] = a.cb[(h * 2 + tensor) * 16 + c];
+    for (int c = 0; c < 16; ++c) tau[c] = a.cb[(h * 2 + tensor) * kCbStride + 16 + c];
   }
 
   // ---- KVarN: rotate, normalise, divide by s1
@@ -324,19 +372,19 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
     if (tensor == 0) {   // keys: s1 per token
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float s1 = expf(rl[i]);
+        const float s1 = expf(rl[i]), r1 = __fdiv_rn(1.f, s1);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[i][e] = __fdiv_rn(x[i][e], s1);
+        for (int e = 0; e < 8; ++e) x[i][e] = div_rn(x[i][e], s1, r1);
         if (g == 0) s1dst[32 * w + 4 * i + r] = s1;
       }
     } else {             // values: s1 per channel
-      float s1[8];
+      float s1[8], r1[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s1[e] = expf(cl[e]);
+      for (int e = 0; e < 8; ++e) { s1[e] = expf(cl[e]); r1[e] = __fdiv_rn(1.f, s1[e]); }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[i][e] = __fdiv_rn(x[i][e], s1[e]);
+        for (int e = 0; e < 8; ++e) x[i][e] = div_rn(x[i][e], s1[e], r1[e]);
       if (w == 0 && r == 0) {
         reinterpret_cast<float4*>(s1dst + 8 * g)[0] = make_float4(s1[0], s1[1], s1[2], s1[3]);
         reinterpret_cast<float4*>(s1dst + 8 * g)[1] = make_float4(s1[4], s1[5], s1[6], s1[7]);
@@ -365,6 +413,10 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       }
       chan_reduce(best, &sm.red[ph][0][0], w, r, g, MaxU());
       ph ^= 1;
+      if (w == 0 && r == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.okey[8 * g + e][p] = best[e];
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -375,6 +427,10 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
           m = (key < thr[i] && key > m) ? key : m;
         }
         best[i] = tok_reduce(m, MaxU());
+      }
+      if (g == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sm.okey[32 * w + 4 * i + r][p] = best[i];
       }
     }
 #pragma unroll
@@ -396,7 +452,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
 
   // ---- statistics over the non-outliers
   if constexpr (MODE != KVARN) opaque(X.v);   // widen again where used (keeps 32, not 64, tile registers)
-  float sa[8], sb[8];
+  VecStats vs[8];   // per channel e when per_chan, per token i otherwise
   if constexpr (per_chan) {
     float lo[8], hi[8];
 #pragma unroll
@@ -431,7 +487,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       const int c = 8 * g + e;
       const float l = fminf(fminf(fminf(sm.rlo[0][c], sm.rlo[1][c]), sm.rlo[2][c]), sm.rlo[3][c]);
       const float u = fmaxf(fmaxf(fmaxf(sm.rhi[0][c], sm.rhi[1][c]), sm.rhi[2][c]), sm.rhi[3][c]);
-      stats_of<MODE, BITS>(l, u, u, sa[e], sb[e]);
+      vs[e] = stats_of<MODE, BITS>(l, u, u);
     }
   } else {
 #pragma unroll
@@ -443,7 +499,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       }
       lo = tok_reduce(lo, MinF());
       hi = tok_reduce(hi, MaxF());
-      stats_of<MODE, BITS>(lo, hi, hi, sa[i], sb[i]);
+      vs[i] = stats_of<MODE, BITS>(lo, hi, hi);
     }
   }
 
@@ -456,13 +512,13 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
           uint32_t hw[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k)
-            hw[k] = __builtin_bit_cast(uint32_t, __halves2half2(__float2half_rn(sa[2 * k]), __float2half_rn(sa[2 * k + 1])));
+            hw[k] = __builtin_bit_cast(uint32_t, __halves2half2(__float2half_rn(vs[2 * k].sa), __float2half_rn(vs[2 * k + 1].sa)));
           *reinterpret_cast<uint4*>(st + 16 * g) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         } else {
           float4* ds = reinterpret_cast<float4*>(st) + 2 * g;
           float4* dm = reinterpret_cast<float4*>(st + 512) + 2 * g;
-          ds[0] = make_float4(sa[0], sa[1], sa[2], sa[3]); ds[1] = make_float4(sa[4], sa[5], sa[6], sa[7]);
-          dm[0] = make_float4(sb[0], sb[1], sb[2], sb[3]); dm[1] = make_float4(sb[4], sb[5], sb[6], sb[7]);
+          ds[0] = make_float4(vs[0].sa, vs[1].sa, vs[2].sa, vs[3].sa); ds[1] = make_float4(vs[4].sa, vs[5].sa, vs[6].sa, vs[7].sa);
+          dm[0] = make_float4(vs[0].sb, vs[1].sb, vs[2].sb, vs[3].sb); dm[1] = make_float4(vs[4].sb, vs[5].sb, vs[6].sb, vs[7].sb);
         }
       }
     } else if (g == 0) {
@@ -470,8 +526,8 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int t = 32 * w + 4 * i + r;
-        ds[t] = sa[i];
-        ds[128 + t] = sb[i];
+        ds[t] = vs[i].sa;
+        ds[128 + t] = vs[i].sb;
       }
     }
   }
@@ -486,7 +542,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       const int t = 32 * w + 4 * i + r;
       uint32_t c[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = code_of<MODE, BITS>(X.f(i, e), sa[e], sb[e], lut);
+      for (int e = 0; e < 8; ++e) c[e] = code_of<MODE, BITS>(X.f(i, e), vs[e], tau);
       uint8_t* row = kc + (size_t)t * R;
       if constexpr (BITS == 4) {
         uint32_t v = 0;
@@ -517,7 +573,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       uint32_t c[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        c[e] = code_of<MODE, BITS>(X.f(i, e), per_chan ? sa[e] : sa[i], per_chan ? sb[e] : sb[i], lut);
+        c[e] = code_of<MODE, BITS>(X.f(i, e), per_chan ? vs[e] : vs[i], tau);
       *reinterpret_cast<uint2*>(&sm.vq[t * kD + 8 * g]) =
           make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
     }
@@ -571,18 +627,25 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
   }
 
   // ---- outliers: keys CSR by token (row t, column c), values CSC by channel (row c,
-  // column t); entries sorted by (row, column), fp16 value bits kept exactly
+  // column t); entries sorted by (row, column), fp16 value bits kept exactly. The keys of
+  // every vector's outliers were recorded during the selection; each encodes its element.
   if (MODE != KVARN && k_out > 0) {
-    opaque(X.v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (is_out(i, e)) {
-          const int t = 32 * w + 4 * i + r, c = 8 * g + e;
-          const int row = tensor == 0 ? t : c, col = tensor == 0 ? c : t;
-          atomicOr(&sm.omask[row][col >> 5], 1u << (col & 31));
-        }
+    __syncthreads();                                   // okey complete, omask cleared
+    const int n_ent = 128 * k_out;
+    auto place = [&](int n, int& row, int& col, uint32_t& key) {
+      const int v = n & 127, p = n >> 7;
+      key = sm.okey[v][p];
+      const int e = (int)key_index(key);
+      const int t = per_chan ? e : v, c = per_chan ? v : e;
+      row = tensor == 0 ? t : c;
+      col = tensor == 0 ? c : t;
+    };
+    for (int n = tid; n < n_ent; n += kThreads) {
+      int row, col;
+      uint32_t key;
+      place(n, row, col, key);
+      atomicOr(&sm.omask[row][col >> 5], 1u << (col & 31));
+    }
     __syncthreads();
     if (w == 0) {
       const int n0 = __popc(sm.omask[2 * lane][0]) + __popc(sm.omask[2 * lane][1]) + __popc(sm.omask[2 * lane][2]) +
@@ -601,27 +664,24 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       if (lane == 63) sm.optr[128] = (uint16_t)incl;
     }
     __syncthreads();
-    __half* val = reinterpret_cast<__half*>(rec + (tensor == 0 ? a.lay.ko_val : a.lay.vo_val));
+    uint16_t* val = reinterpret_cast<uint16_t*>(rec + (tensor == 0 ? a.lay.ko_val : a.lay.vo_val));
     uint16_t* ptr = reinterpret_cast<uint16_t*>(rec + (tensor == 0 ? a.lay.ko_ptr : a.lay.vo_ptr));
     uint8_t* idx = rec + (tensor == 0 ? a.lay.ko_idx : a.lay.vo_idx);
     if (tid <= 128) ptr[tid] = sm.optr[tid];
+    for (int n = tid; n < n_ent; n += kThreads) {
+      int row, col;
+      uint32_t key;
+      place(n, row, col, key);
+      int pos = sm.optr[row];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (is_out(i, e)) {
-          const int t = 32 * w + 4 * i + r, c = 8 * g + e;
-          const int row = tensor == 0 ? t : c, col = tensor == 0 ? c : t;
-          int pos = sm.optr[row];
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const uint32_t m = sm.omask[row][d];
-            const int lim = col - 32 * d;   // bits of word d below col
-            pos += lim >= 32 ? __popc(m) : (lim > 0 ? __popc(m & ((1u << lim) - 1u)) : 0);
-          }
-          val[pos] = __float2half_rn(X.f(i, e));   // exact: x is a widened fp16
-          idx[pos] = (uint8_t)col;
-        }
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t m = sm.omask[row][d];
+        const int lim = col - 32 * d;   // bits of word d below col
+        pos += lim >= 32 ? __popc(m) : (lim > 0 ? __popc(m & ((1u << lim) - 1u)) : 0);
+      }
+      val[pos] = key_f16_bits(key);
+      idx[pos] = (uint8_t)col;
+    }
   }
 }
 

@@ -99,10 +99,15 @@ void kvq_cache_destroy(kvq_cache cache);
 
 /*
  * Load the NUQ codebook of one (layer, kv head) for keys (which = 0) or values
- * (which = 1). host_codebook: n_entries = 2^bits fp32 values, finite, strictly
- * ascending, within [-1, 1] (KVQuant notes 3.3: one datatype per layer and head;
- * this build keeps one per (layer, kv head, K/V)). The handle keeps a host copy,
- * so host_codebook may be freed on return. Only valid in KVQ_MODE_NUQ.
+ * (which = 1). host_codebook: n_entries = 2^bits fp32 values, finite, within
+ * [-1, 1], ascending with consecutive entries at least 2^-21 apart (KVQuant notes
+ * 3.3: one datatype per layer and head; this build keeps one per (layer, kv head,
+ * K/V)). The gap guarantees that the fp32 argmin of |u - C_j| (ties to the smaller
+ * j) is decided between the two entries around u; the library derives the decision
+ * threshold between each pair of consecutive entries on the host and uploads it with
+ * the entries. The handle keeps a host copy, so host_codebook may be freed on return.
+ * Errors: KVQ_ERR_ARG for a codebook that breaks these rules; KVQ_ERR_STATE outside
+ * KVQ_MODE_NUQ.
  */
 kvq_status kvq_codebook_load(kvq_cache cache, int layer, int kv_head, int which,
                              const float* host_codebook, int n_entries, void* stream);

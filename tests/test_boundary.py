@@ -60,7 +60,7 @@ def test_cache_bytes_matches_oracle_record_layout(mode, bits, k_out, pre_rope):
         return (x + 255) // 256 * 256
     total = a(rec * units * nblk * c.n_layers) + a(units * 65536 * c.n_layers)
     if mode == K.KVQ_MODE_NUQ:
-        total += a(c.n_layers * c.n_kv_heads * 2 * 16 * 4)
+        total += a(c.n_layers * c.n_kv_heads * 2 * 32 * 4)   # entries, then decision thresholds
     if pre_rope:
         total += a((nblk + 1) * 512) + a(128 * 512 + 256)
     total += a(c.batch * c.n_q_heads * K.KVQ_MAX_SPLITS * 130 * 4)
@@ -144,6 +144,29 @@ def test_codebook_load_rejected_outside_nuq():
             K.kvq_codebook_load(h, 0, 0, 0, [-1.0, -0.3, 0.1, 0.2, 0.3, 0.4, 0.5, 0.6, 0.65, 0.7, 0.75, 0.8,
                                              0.85, 0.9, 0.95, 1.0])
         assert e.value.status == K.KVQ_ERR_STATE
+    finally:
+        K.kvq_cache_destroy(h)
+
+
+def test_codebook_validation():
+    # every rule is checked on the host before the upload (the device buffer is never touched)
+    c = cfg(mode=K.KVQ_MODE_NUQ, bits=2)
+    h = K.kvq_cache_init(c, FAKE, K.kvq_cache_bytes(c))
+    try:
+        bad = [
+            [-1.0, -0.5, 0.5],                       # wrong count
+            [-1.0, 0.5, -0.5, 1.0],                  # not ascending
+            [-1.0, -0.5, 0.5, 1.5],                  # outside [-1, 1]
+            [-1.0, 0.25, 0.25 + 2.0 ** -23, 1.0],    # entries closer than 2^-21
+            [-1.0, float("nan"), 0.5, 1.0],
+        ]
+        for cb in bad:
+            with pytest.raises(K.KvqError) as e:
+                K.kvq_codebook_load(h, 0, 0, 0, cb)
+            assert e.value.status == K.KVQ_ERR_ARG, cb
+        with pytest.raises(K.KvqError) as e:
+            K.kvq_codebook_load(h, 0, 5, 0, [-1.0, -0.5, 0.5, 1.0])
+        assert e.value.status == K.KVQ_ERR_ARG
     finally:
         K.kvq_cache_destroy(h)
 

@@ -187,3 +187,48 @@ def test_errors_on_device(K):
     cache.decode(0, torch.ones((1, 1, 128), dtype=torch.float16, device="cuda"), out)
     torch.cuda.synchronize()
     assert torch.allclose(out, torch.full_like(out, 0.75), rtol=0, atol=1e-6)
+
+
+def _fp16_sweep():
+    """Every finite fp16 value in [-1, 1] (both zeros once), in bit-pattern order."""
+    pos = np.arange(0x0000, 0x3C01, dtype=np.uint16)
+    neg = np.arange(0x8001, 0xBC01, dtype=np.uint16)
+    return np.concatenate([pos, neg]).view(np.float16)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_nuq_codes_exhaustive_fp16(K, bits):
+    """NUQ argmin over every fp16 value of [-1, 1] against the oracle's brute force
+    (KVQuant notes 1.2 / 3.3; the device decides through host-derived thresholds).
+
+    Keys: tokens 0 and 1 of each block hold -1 and +1 in every channel, so every key
+    channel has z = 0, h = 1 and u = x. Values: channels 0 and 1 of each token hold -1
+    and +1, so every value token has u = x too. The other slots carry the sweep."""
+    sweep = _fp16_sweep()
+    n_blk = 2
+    L = 128 * n_blk
+    k = np.zeros((L, 128), np.float16)
+    v = np.zeros((L, 128), np.float16)
+    ks = np.resize(sweep, n_blk * 126 * 128)
+    vs = np.resize(sweep[::-1], n_blk * 128 * 126)
+    for j in range(n_blk):
+        k[128 * j] = -1.0
+        k[128 * j + 1] = 1.0
+        k[128 * j + 2:128 * (j + 1)] = ks[j * 126 * 128:(j + 1) * 126 * 128].reshape(126, 128)
+    v[:, 0] = -1.0
+    v[:, 1] = 1.0
+    v[:, 2:] = vs.reshape(L, 126)
+    wl = small("c2_llama7b_layer_32k_nuq3", bits=bits, n_layers=1, batch=1, n_q_heads=1, n_kv_heads=1,
+               outliers_per_vec=0, pre_rope=0)
+    cache = K.KVCache(H.lib_cfg(wl, L))
+    oc = O.OracleCache(H.oracle_cfg(wl, L))
+    uniform = (-1.0 + 2.0 * np.arange(1 << bits) / ((1 << bits) - 1)).astype(np.float32)
+    for w, cb in ((0, synth.gen_codebook(wl, 0, 0, 0, bits)), (1, uniform)):
+        cache.codebook_load(0, 0, w, cb)
+        oc.load_codebook(0, 0, w, cb)
+    cache.append(0, torch.from_numpy(k[None, None]).cuda(), torch.from_numpy(v[None, None]).cuda())
+    oc.append(0, k[None, None], v[None, None])
+    torch.cuda.synchronize()
+    for j in range(n_blk):
+        got = cache.block_bytes(0, 0, 0, j).cpu().numpy()
+        H.compare_record(got, oc.blocks[0][0][j], oc.cfg, where=f"block {j}")
