@@ -413,13 +413,17 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
   a.blocks_per_split = bps;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
   a.scale_log2 = scale * 1.4426950408889634f;
-  if (cfg.outliers_per_vec > 0) {
-    // per-wave staging for the sparse fix-ups: outlier segments, key S/M, value S/M of a half, RoPE base row
-    const uint32_t blob = c->lay.vo_idx + 128u * cfg.outliers_per_vec - c->lay.ko_val;
-    a.wave_lds = (int)(((blob + 15u) & ~15u) + 1024u + 512u + 512u);
-  }
   const int group = cfg.n_q_heads / cfg.n_kv_heads;
-  if (kvq::mfma_supported(cfg.mode, cfg.bits, cfg.pre_rope, cfg.outliers_per_vec))
+  const bool tab = kvq::tab_supported(cfg.mode, cfg.bits, group, cfg.pre_rope);
+  if (cfg.outliers_per_vec > 0) {
+    // per-wave staging for the sparse fix-ups: the outlier segments (table kernel), plus
+    // key S/M, value S/M of a half and a RoPE base row (VALU kernel)
+    const uint32_t blob = c->lay.vo_idx + 128u * cfg.outliers_per_vec - c->lay.ko_val;
+    a.wave_lds = (int)(((blob + 15u) & ~15u) + (tab ? 0u : 1024u + 512u + 512u));
+  }
+  if (tab)
+    st = hip_check(kvq::launch_decode_tab(cfg.mode, cfg.bits, a, cfg.batch, s), "launch decode");
+  else if (kvq::mfma_supported(cfg.mode, cfg.bits, cfg.pre_rope, cfg.outliers_per_vec))
     st = hip_check(kvq::launch_decode_mfma(cfg.mode, cfg.bits, group, a, cfg.batch, s), "launch decode");
   else
     st = hip_check(kvq::launch_decode(cfg.mode, cfg.bits, group, cfg.pre_rope, a, cfg.batch, s), "launch decode");

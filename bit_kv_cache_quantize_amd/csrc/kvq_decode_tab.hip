@@ -1,0 +1,497 @@
+// Split-K decode attention for caches with pre-RoPE keys and one query head per kv
+// head (the LLaMA-7B shapes), 2- or 3-bit RTN or NUQ codes, with or without outliers.
+//
+// Same computation as the other decode kernels ("KVQuant reading notes", Algorithm 1
+// attention part, 1.3 and 3.2 for RoPE, 3.4 for the outliers): softmax(scale * q .
+// RoPE(k_hat_n, n)) weighted sum of v_hat_n over every cached token.
+//
+// What differs is how a key reaches its score. Rotate the query back by the block's base
+// angle n0 * theta_i (pair i = channels 2i, 2i+1) and fold in the pair's dequantization;
+// the pair's contribution to the score of in-block token j is then
+//     cos(j theta_i) * U_i(a, b) + sin(j theta_i) * W_i(a, b),
+//     U_i = al_i k_x(a) + be_i k_y(b),   W_i = be_i k_x(a) - al_i k_y(b),
+// where (a, b) are the pair's two codes and (al_i, be_i) the rotated query pair. U and W
+// depend only on the block and the two codes, so the two waves that share a block
+// tabulate them in LDS for every code combination (16 entries per pair at 2 bits, 64 at
+// 3 bits), indexed by the pair's bits as they lie in the packed row. A token then costs,
+// per channel pair, the index extraction, one 8-byte LDS read and two fma; cos(j theta_i)
+// and sin(j theta_i) are per-lane registers (each lane keeps one in-block offset j).
+//
+// Values: lane = channel pair of a 64-token half-row. The codes of two adjacent tokens
+// index a constant LDS table of their code values (RTN codes, NUQ codebook entries), and
+// their weights p_t * S_t (S_t the token's value scale) are broadcast from LDS; the
+// code-independent part sum_t p_t M_t is added once per head.
+//
+// Outliers replace the dense value: each CSR (keys) / CSC (values) entry adds
+// (fp16 value - dense value) times the entry's weight.
+//
+// Work decomposition: one workgroup = one split of one (sequence, kv head); waves 2p and
+// 2p+1 process the two halves of blocks blo + p, blo + p + 2, ... in lockstep (two
+// workgroup barriers per block pair: tables built, tables consumed), with the next
+// block's loads in flight during the current one.
+#include "kvq_decode_common.h"
+
+namespace kvq {
+namespace {
+
+using namespace dec;
+
+constexpr float kInv2Pi = 0.15915494309189535f;
+
+template <int MODE, int BITS>
+struct TabDecoder {
+  static constexpr int R = 16 * BITS;                 // key row bytes
+  static constexpr int RH = R / 2;                    // value half-row bytes
+  static constexpr int PT = BITS == 3 ? 64 : 16;      // table entries per channel pair
+  static constexpr int KWD = R / 4;                   // dwords of a key row
+  static constexpr int NOB = 3;                       // outlier blob chunks per lane (inline path)
+
+  // Loads of a block issued one block ahead (key side).
+  struct Buf {
+    uint32_t kw[KWD];     // key row of token j
+    float4 kst;           // table role: (scale_x, scale_y, offset_x, offset_y) of pair ib
+    float2 rb;            // table role: (cos, sin) of the block base angle for pair ib
+  };
+  // Loads of the value side, issued when the block's key work starts.
+  struct VBuf {
+    uint32_t vw[KWD];     // value half-rows of channels 2*lane, 2*lane+1
+    float2 tst;           // value (S, M) of token j
+  };
+
+  struct Shared {
+    float2* tab;          // this wave pair's table [64][PT]
+    float2* qb;           // this wave pair's rotated query pairs [64] (al, be)
+    float2* kst;          // this wave pair's key (scale, offset) per channel [128]
+    const float2* vlut;   // value code pairs [PT]
+    float* pS;            // this wave's p * S per token of the half [64]
+    float* p;             // this wave's p per token [64]
+    float2* vst;          // this wave's value (S, M) per token [64]
+    uint8_t* blob;        // this wave's outlier staging
+    const float* q;       // query (original domain, scale folded) [128]
+    const float* trev;    // theta_i / (2 pi) [64]
+    const float* cbk;     // key codebook [16] (NUQ)
+    const float* cbv;     // value codebook [16] (NUQ)
+  };
+
+  const DecodeArgs& a;
+  const Shared S;
+  const int lane, w, par, pr, j, ib, hb;
+  int ob_bytes, ob_chunks;
+  float m_run, l_run, pm, acc0, acc1;
+
+  __device__ TabDecoder(const DecodeArgs& args, const Shared& sh, int lane_, int w_)
+      : a(args), S(sh), lane(lane_), w(w_), par(w_ & 1), pr(w_ >> 1), j(64 * (w_ & 1) + lane_),
+        ib((64 * (w_ & 1) + lane_) >> 1), hb(lane_ & 1) {
+    m_run = -INFINITY;
+    l_run = 0.f;
+    pm = 0.f;
+    acc0 = 0.f;
+    acc1 = 0.f;
+    ob_bytes = 0;
+    ob_chunks = 0;
+    if (a.k_out > 0) {
+      ob_bytes = (int)(a.lay.vo_idx + 128u * a.k_out - a.lay.ko_val);
+      ob_chunks = (ob_bytes + 15) / 16;
+    }
+  }
+
+  __device__ __forceinline__ const uint8_t* record(int blk) const {
+    return a.rec + ((size_t)(blockIdx.z * a.Hkv + blockIdx.y) * a.max_blocks + blk) * (size_t)a.lay.rec_bytes;
+  }
+
+  __device__ __forceinline__ void fetch(Buf& B, int blk) const {
+    const uint8_t* rec = record(blk);
+    load_row<R>(B.kw, rec + a.lay.kc + (size_t)j * R);
+    const float2 s2 = reinterpret_cast<const float2*>(rec + a.lay.ks)[ib];          // RTN s / NUQ z
+    const float2 m2 = reinterpret_cast<const float2*>(rec + a.lay.ks + 512)[ib];    // RTN m / NUQ h
+    if constexpr (MODE == NUQ) B.kst = make_float4(m2.x, m2.y, s2.x, s2.y);        // (h, h, z, z)
+    else B.kst = make_float4(s2.x, s2.y, m2.x, m2.y);                               // (s, s, m, m)
+    B.rb = reinterpret_cast<const float2*>(a.rope_base)[(size_t)blk * 64 + ib];
+  }
+
+  __device__ __forceinline__ void fetch_v(VBuf& V, int blk) const {
+    const uint8_t* rec = record(blk);
+    load_row<R>(V.vw, rec + a.lay.vc + (size_t)par * (128 * RH) + (size_t)lane * R);
+    if constexpr (MODE == NUQ) {
+      V.tst.x = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + j];   // h
+      V.tst.y = reinterpret_cast<const float*>(rec + a.lay.vs)[j];         // z
+    } else {
+      V.tst.x = reinterpret_cast<const float*>(rec + a.lay.vs)[j];
+      V.tst.y = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + j];
+    }
+  }
+
+  __device__ __forceinline__ float kcode(int c, uint32_t code) const {
+    if constexpr (MODE == NUQ) return S.cbk[code];
+    else return (float)code;
+  }
+
+  // Entries hb*PT/2 .. hb*PT/2 + PT/2 - 1 of pair ib's table (the other lane of the pair
+  // writes the rest), the pair's rotated query and its channel statistics.
+  __device__ __forceinline__ void build(const Buf& B) const {
+    const float qx = S.q[2 * ib], qy = S.q[2 * ib + 1];
+    const float al = fmaf(qx, B.rb.x, qy * B.rb.y);
+    const float be = fmaf(qy, B.rb.x, -qx * B.rb.y);
+    if (hb == 0) S.qb[ib] = make_float2(al, be);
+    S.kst[2 * ib + hb] = hb ? make_float2(B.kst.y, B.kst.w) : make_float2(B.kst.x, B.kst.z);
+    constexpr int NA = 1 << BITS;          // codes of the x channel
+    constexpr int NB = BITS == 3 ? 4 : 2;  // codes of the y channel covered by this lane
+    float Ax[NA], Bx[NA], Ay[NB], By[NB];
+#pragma unroll
+    for (int c = 0; c < NA; ++c) {
+      const float kx = fmaf(kcode(0, c), B.kst.x, B.kst.z);
+      Ax[c] = al * kx;
+      Bx[c] = be * kx;
+    }
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      const int b = NB * hb + c;
+      const float ky = fmaf(kcode(1, b), B.kst.y, B.kst.w);
+      Ay[c] = be * ky;
+      By[c] = -al * ky;
+    }
+    float4* dst = reinterpret_cast<float4*>(S.tab + ib * PT + hb * (PT / 2));
+#pragma unroll
+    for (int e = 0; e < PT / 2; e += 2) {
+      float2 v[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        // entry hb * PT/2 + ee; the bits that name the lane's half do not enter ca or cbl
+        const int ee = e + k;
+        int ca, cbl;   // code of x, index of the y code in this lane's range
+        if constexpr (BITS == 3) {   // idx = lo2(a) | lo2(b) << 2 | hi(a) << 4 | hi(b) << 5
+          ca = (ee & 3) | (((ee >> 4) & 1) << 2);
+          cbl = (ee >> 2) & 3;
+        } else {                     // idx = a | b << 2
+          ca = ee & 3;
+          cbl = (ee >> 2) & 1;
+        }
+        v[k] = make_float2(Ax[ca] + Ay[cbl], Bx[ca] + By[cbl]);
+      }
+      dst[e / 2] = make_float4(v[0].x, v[0].y, v[1].x, v[1].y);
+    }
+  }
+
+  // Table index of pair i of a packed row held in w[].
+  __device__ __forceinline__ uint32_t pair_index(const uint32_t* wd, int i, int nrow) const {
+    // nrow: codes in the row (128 keys, 64 values)
+    const uint32_t nib = __builtin_amdgcn_ubfe(wd[i >> 3], 4 * (i & 7), 4);
+    if constexpr (BITS == 3) {
+      const uint32_t hi = __builtin_amdgcn_ubfe(wd[nrow / 16 + (i >> 4)], 2 * (i & 15), 2);
+      return nib | (hi << 4);
+    } else {
+      return nib;
+    }
+  }
+
+  __device__ __forceinline__ void wave_sync() const {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // Online-softmax update with this lane's log2-domain score; returns p.
+  __device__ __forceinline__ float softmax_step(float sl) {
+    const float mnew = fmaxf(m_run, wave_max(sl));
+    const float alpha = exp2f(m_run - mnew);
+    const float p = exp2f(sl - mnew);
+    m_run = mnew;
+    l_run = fmaf(l_run, alpha, p);
+    pm *= alpha;
+    acc0 *= alpha;
+    acc1 *= alpha;
+    return p;
+  }
+
+  // One half block (parity par) of block blk whose loads are in B; the wave pair's table
+  // for blk is complete.
+  __device__ __forceinline__ void process(const Buf& B, int blk, const float (&rc)[64], const float (&rs)[64]) {
+    const uint8_t* rec = record(blk);
+    const bool outl = a.k_out > 0;
+    VBuf V;
+    fetch_v(V, blk);
+    uint4 ob[NOB];
+    if (outl) {
+      const uint4* src = reinterpret_cast<const uint4*>(rec + a.lay.ko_val);
+      const int last = ob_chunks - 1;
+#pragma unroll
+      for (int k = 0; k < NOB; ++k) ob[k] = src[min(lane + 64 * k, last)];
+    }
+
+    // ---- scores: two fma per channel pair on the tabulated (U, W)
+    float sc0 = 0.f, sc1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const uint32_t idx = pair_index(B.kw, i, 128);
+      const float2 uw = *reinterpret_cast<const float2*>(
+          reinterpret_cast<const uint8_t*>(S.tab) + (size_t)(i * PT + idx) * 8);
+      sc0 = fmaf(rc[i], uw.x, sc0);
+      sc1 = fmaf(rs[i], uw.y, sc1);
+    }
+    float sc = sc0 + sc1;
+
+    // ---- key outliers of row j (CSR): the fp16 value replaces the dense one
+    if (outl) {
+      if (ob_chunks <= NOB * 64) {
+        uint4* dst = reinterpret_cast<uint4*>(S.blob);
+#pragma unroll
+        for (int k = 0; k < NOB; ++k)
+          if (lane + 64 * k < ob_chunks) dst[lane + 64 * k] = ob[k];
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(rec + a.lay.ko_val);
+        uint4* dst = reinterpret_cast<uint4*>(S.blob);
+        for (int k = lane; k < ob_chunks; k += 64) dst[k] = src[k];
+      }
+      wave_sync();
+      const uint16_t* ptr = reinterpret_cast<const uint16_t*>(S.blob + (a.lay.ko_ptr - a.lay.ko_val));
+      const uint8_t* idx = S.blob + (a.lay.ko_idx - a.lay.ko_val);
+      const __half* val = reinterpret_cast<const __half*>(S.blob);
+      const int e1 = ptr[j + 1];
+      for (int e = ptr[j]; e < e1; ++e) {
+        const int c = idx[e], i = c >> 1;
+        const float2 st = S.kst[c];
+        const float dense = fmaf(kcode(c & 1, code_sel<BITS, 128>(B.kw, c)), st.x, st.y);
+        const float delta = __half2float(val[e]) - dense;
+        const float ang = (float)j * S.trev[i];
+        const float cj = __builtin_amdgcn_cosf(ang), sj = __builtin_amdgcn_sinf(ang);
+        const float2 q2 = S.qb[i];
+        const float coef = (c & 1) ? fmaf(cj, q2.y, -sj * q2.x) : fmaf(cj, q2.x, sj * q2.y);
+        sc = fmaf(delta, coef, sc);
+      }
+    }
+
+    const float p = softmax_step(sc);
+    pm = fmaf(p, V.tst.y, pm);                 // sum_t p_t M_t (code-independent part)
+    S.pS[lane] = p * V.tst.x;
+    S.p[lane] = p;
+    S.vst[lane] = V.tst;
+    wave_sync();
+
+    // ---- P.V over the 64 tokens of this half, channels 2*lane and 2*lane+1
+    float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < 32; ++pp) {
+      const int t = half_row_token(2 * pp);   // positions 2pp, 2pp+1 hold tokens t, t+1
+      const float2 ps = *reinterpret_cast<const float2*>(S.pS + t);
+      const float2 v0 = S.vlut[pair_index(V.vw, pp, 64)];
+      const float2 v1 = S.vlut[pair_index(V.vw + KWD / 2, pp, 64)];
+      o0 = fmaf(ps.x, v0.x, fmaf(ps.y, v0.y, o0));
+      o1 = fmaf(ps.x, v1.x, fmaf(ps.y, v1.y, o1));
+    }
+    acc0 += o0;
+    acc1 += o1;
+
+    // ---- value outliers of channels 2*lane, 2*lane+1 (CSC) that fall in this half
+    if (outl) {
+      const uint16_t* ptr = reinterpret_cast<const uint16_t*>(S.blob + (a.lay.vo_ptr - a.lay.ko_val));
+      const uint8_t* idx = S.blob + (a.lay.vo_idx - a.lay.ko_val);
+      const __half* val = reinterpret_cast<const __half*>(S.blob + (a.lay.vo_val - a.lay.ko_val));
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int c = 2 * lane + k;
+        const int e1 = ptr[c + 1];
+        for (int e = ptr[c]; e < e1; ++e) {
+          const int t = idx[e] - 64 * par;
+          if (t < 0 || t >= 64) continue;
+          const uint32_t code = code_sel<BITS, 64>(V.vw + k * (KWD / 2), half_row_token(t));
+          const float2 st = S.vst[t];
+          const float vc = MODE == NUQ ? S.cbv[code] : (float)code;
+          const float delta = __half2float(val[e]) - fmaf(vc, st.x, st.y);
+          if (k == 0) acc0 = fmaf(S.p[t], delta, acc0);
+          else acc1 = fmaf(S.p[t], delta, acc1);
+        }
+      }
+    }
+    wave_sync();   // the per-wave LDS areas are rewritten by the next half block
+  }
+
+  // Tokens 64*par .. 64*par+63 of the fp16 tail (position 128*nblk + j), waves 0 and 1.
+  __device__ __forceinline__ void tail_half(const float (&rc)[64], const float (&rs)[64], float2* qt) {
+    const int n_valid = min(64, a.tail_n - 64 * par);
+    const __half* tk = a.tail + (size_t)(blockIdx.z * a.Hkv + blockIdx.y) * (2 * kT * kD);
+    const __half* tv = tk + kT * kD;
+    const bool valid = lane < n_valid;
+    float sc = 0.f;
+    const uint4* krow = reinterpret_cast<const uint4*>(tk + (size_t)j * kD);
+    // fully unrolled (rc, rs are indexed by i), in chunks of 4 pairs that the scheduler may
+    // not merge, so that it does not hoist all 64 loads at once
+#pragma unroll
+    for (int i0 = 0; i0 < 64; i0 += 4) {
+      const uint4 kv = valid ? krow[i0 / 4] : make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t kd[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k;
+        const float2 kk = __half22float2(__builtin_bit_cast(__half2, kd[k]));
+        const float2 q2 = qt[i];
+        const float U = fmaf(kk.x, q2.x, kk.y * q2.y);
+        const float W = fmaf(kk.x, q2.y, -kk.y * q2.x);
+        sc = fmaf(rc[i], U, fmaf(rs[i], W, sc));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float p = softmax_step(valid ? sc : -INFINITY);
+    S.p[lane] = p;
+    wave_sync();
+    float o0 = 0.f, o1 = 0.f;
+    const __half2* vcol = reinterpret_cast<const __half2*>(tv + (size_t)(64 * par) * kD) + lane;
+    for (int t = 0; t < n_valid; ++t) {
+      const float2 vv = __half22float2(vcol[(size_t)t * (kD / 2)]);
+      const float pv = S.p[t];
+      o0 = fmaf(pv, vv.x, o0);
+      o1 = fmaf(pv, vv.y, o1);
+    }
+    acc0 += o0;
+    acc1 += o1;
+    wave_sync();
+  }
+};
+
+template <int MODE, int BITS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_tab_kernel(DecodeArgs a) {
+  using Dec = TabDecoder<MODE, BITS>;
+  constexpr int PT = Dec::PT;
+  extern __shared__ __align__(16) uint8_t s_dyn[];
+  __shared__ __align__(16) float2 s_tab[2][64 * PT];
+  __shared__ __align__(16) float2 s_vlut[PT];
+  __shared__ __align__(16) float2 s_qb[2][64];
+  __shared__ __align__(16) float2 s_kst[2][128];
+  __shared__ __align__(16) float s_q[128];
+  __shared__ float s_trev[64];
+  __shared__ float s_cb[32];
+  __shared__ __align__(16) float s_pS[4][64];
+  __shared__ __align__(16) float s_p[4][64];
+  __shared__ __align__(16) float2 s_vst[4][64];
+  __shared__ float s_m[4], s_l[4];
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  if (tid < 128) s_q[tid] = __half2float(a.q[((size_t)b * a.Hq + kvh) * 128 + tid]) * a.scale_log2;
+  if (tid < 64) s_trev[tid] = a.rope_off[128 * 64 * 2 + tid] * kInv2Pi;
+  if (MODE == NUQ && tid < 32) s_cb[tid] = a.cb[(kvh * 2 + (tid >> 4)) * kCbStride + (tid & 15)];
+  __syncthreads();
+  if (tid < PT) {
+    // code values of two adjacent value tokens, in the same index order as the key tables
+    int ca, cb2;
+    if constexpr (BITS == 3) {
+      ca = (tid & 3) | (((tid >> 4) & 1) << 2);
+      cb2 = ((tid >> 2) & 3) | (((tid >> 5) & 1) << 2);
+    } else {
+      ca = tid & 3;
+      cb2 = (tid >> 2) & 3;
+    }
+    s_vlut[tid] = MODE == NUQ ? make_float2(s_cb[16 + ca], s_cb[16 + cb2]) : make_float2((float)ca, (float)cb2);
+  }
+
+  typename Dec::Shared sh;
+  sh.tab = s_tab[w >> 1];
+  sh.qb = s_qb[w >> 1];
+  sh.kst = s_kst[w >> 1];
+  sh.vlut = s_vlut;
+  sh.pS = s_pS[w];
+  sh.p = s_p[w];
+  sh.vst = s_vst[w];
+  sh.blob = s_dyn + (size_t)w * a.wave_lds;
+  sh.q = s_q;
+  sh.trev = s_trev;
+  sh.cbk = s_cb;
+  sh.cbv = s_cb + 16;
+  Dec d(a, sh, lane, w);
+
+  float rc[64], rs[64];
+  {
+    const float2* off = reinterpret_cast<const float2*>(a.rope_off) + d.j;   // pair-major: [i][j]
+#pragma unroll
+    for (int i = 0; i < 64; ++i) { const float2 v = off[i * 128]; rc[i] = v.x; rs[i] = v.y; }
+  }
+
+  // ---- blocks of this split: wave pair pr takes blo + pr, blo + pr + 2, ...
+  const int blo = split * a.blocks_per_split;
+  const int bhi = min(a.nblk, blo + a.blocks_per_split);
+  const int n_iter = (bhi - blo + 1) >> 1;
+  typename Dec::Buf A, Bn;
+  int blk = blo + d.pr;
+  if (blk < bhi) d.fetch(A, blk);
+  __syncthreads();   // the value table is complete
+  for (int it = 0; it < n_iter; ++it, blk += 2) {
+    const bool valid = blk < bhi;
+    if (blk + 2 < bhi) d.fetch(Bn, blk + 2);
+    if (valid) d.build(A);
+    __syncthreads();
+    if (valid) d.process(A, blk, rc, rs);
+    __syncthreads();
+    A = Bn;
+  }
+
+  // ---- the fp16 tail (waves 0 and 1; it belongs to the last split)
+  if (split == a.splits - 1 && a.tail_n > 0) {
+    float2* qt = s_qb[0];
+    if (tid < 64) {
+      // query rotated back by the tail block's base angle
+      const float2 rb = reinterpret_cast<const float2*>(a.rope_base)[(size_t)a.nblk * 64 + tid];
+      const float qx = s_q[2 * tid], qy = s_q[2 * tid + 1];
+      qt[tid] = make_float2(fmaf(qx, rb.x, qy * rb.y), fmaf(qy, rb.x, -qx * rb.y));
+    }
+    __syncthreads();
+    if (w < 2 && 64 * d.par < a.tail_n) d.tail_half(rc, rs, qt);
+  }
+
+  // ---- merge the four wave states
+  float* s_o = reinterpret_cast<float*>(&s_tab[0][0]);   // [4][128], the tables are no longer read
+  __syncthreads();
+  {
+    const float l = wave_sum(d.l_run);
+    const float pmw = wave_sum(d.pm);
+    if (lane == 0) { s_m[w] = d.m_run; s_l[w] = l; }
+    s_o[w * 128 + 2 * lane] = d.acc0 + pmw;
+    s_o[w * 128 + 2 * lane + 1] = d.acc1 + pmw;
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const int c = tid;
+    const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      if (s_m[ww] == -INFINITY) continue;
+      const float sw = exp2f(s_m[ww] - M);
+      o = fmaf(sw, s_o[ww * 128 + c], o);
+      L = fmaf(sw, s_l[ww], L);
+    }
+    const size_t row = (size_t)b * a.Hq + kvh;
+    if (a.splits == 1) {
+      a.out[row * kD + c] = o / L;
+    } else {
+      float* part = a.part + (row * a.splits + split) * kPartStride;
+      part[2 + c] = o;
+      if (c == 0) { part[0] = M; part[1] = L; }
+    }
+  }
+}
+
+template <int MODE, int BITS>
+hipError_t launch_t(const DecodeArgs& a, int batch, hipStream_t s) {
+  hipLaunchKernelGGL((decode_tab_kernel<MODE, BITS>), dim3(a.splits, a.Hkv, batch), dim3(kThreads),
+                     (size_t)4 * a.wave_lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool tab_supported(int mode, int bits, int group, int rope) {
+  return rope && group == 1 && (bits == 2 || bits == 3) && (mode == RTN || mode == NUQ);
+}
+
+hipError_t launch_decode_tab(int mode, int bits, const DecodeArgs& a, int batch, hipStream_t s) {
+  switch (mode * 8 + bits) {
+    case RTN * 8 + 2: return launch_t<RTN, 2>(a, batch, s);
+    case RTN * 8 + 3: return launch_t<RTN, 3>(a, batch, s);
+    case NUQ * 8 + 2: return launch_t<NUQ, 2>(a, batch, s);
+    case NUQ * 8 + 3: return launch_t<NUQ, 3>(a, batch, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq

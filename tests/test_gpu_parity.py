@@ -87,6 +87,10 @@ CASES = {
                            n_kv_heads=2), [200, 100]),
     "rtn4_rope_g4": (small("c1_single_head_2k_rtn4", pre_rope=1, batch=1, n_q_heads=8, n_kv_heads=2), [384]),
     "nuq3_rope_out1_g1": (small("c2_llama7b_layer_32k_nuq3", n_q_heads=2, n_kv_heads=2, batch=2), [1, 299]),
+    "nuq2_rope_out2_g1": (small("c2_llama7b_layer_32k_nuq3", bits=2, outliers_per_vec=2, n_q_heads=3,
+                                n_kv_heads=3), [700]),
+    "rtn3_rope_g1": (small("c5_llama7b_1m_rtn2", n_layers=1, bits=3, outliers_per_vec=0, n_q_heads=2,
+                           n_kv_heads=2), [513]),
     "nuq2_out1_g4": (small("c2_llama7b_layer_32k_nuq3", bits=2, pre_rope=0, n_q_heads=8, n_kv_heads=2), [256]),
     "nuq4_rope_out3_g8": (small("c2_llama7b_layer_32k_nuq3", bits=4, outliers_per_vec=3, n_q_heads=16,
                                 n_kv_heads=2), [129, 130]),
@@ -115,6 +119,14 @@ def test_parity_ragged_lengths(K, L):
 @pytest.mark.parametrize("L", [1, 127, 129])
 def test_parity_ragged_kvarn(K, L):
     wl = small("c3_kvarn_gqa_b16_8k", batch=1, n_q_heads=8, n_kv_heads=2)
+    run_case(K, wl, [L])
+
+
+@pytest.mark.parametrize("L", [1, 127, 128, 129, 255, 256, 257, 640, 1000])
+@pytest.mark.parametrize("base", ["c2_llama7b_layer_32k_nuq3", "c5_llama7b_1m_rtn2"])
+def test_parity_ragged_one_query_per_kv_head(K, base, L):
+    # the pre-RoPE, one-query-head-per-kv-head layouts of the LLaMA-7B workloads
+    wl = small(base, n_layers=1, batch=2, n_q_heads=2, n_kv_heads=2)
     run_case(K, wl, [L])
 
 
