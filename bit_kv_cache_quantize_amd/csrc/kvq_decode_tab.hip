@@ -43,8 +43,11 @@ struct TabDecoder {
   static constexpr int R = 16 * BITS;                 // key row bytes
   static constexpr int RH = R / 2;                    // value half-row bytes
   static constexpr int PT = BITS == 3 ? 64 : 16;      // table entries per channel pair
+  // Pair tables are PT + 2 entries apart: the 16-byte pad staggers the LDS bank groups of
+  // consecutive pairs, so that the lanes of a build step (one pair each) do not all write
+  // the same banks. The lookups keep their immediate offsets (no extra instruction).
+  static constexpr int PS = PT + 2;
   static constexpr int KWD = R / 4;                   // dwords of a key row
-  static constexpr int NOB = 3;                       // outlier blob chunks per lane (inline path)
 
   // Loads of a block issued one block ahead (key side).
   struct Buf {
@@ -52,21 +55,25 @@ struct TabDecoder {
     float4 kst;           // table role: (scale_x, scale_y, offset_x, offset_y) of pair ib
     float2 rb;            // table role: (cos, sin) of the block base angle for pair ib
   };
-  // Loads of the value side, issued when the block's key work starts.
+  static constexpr int NOB = 1;   // outlier staging chunks per wave-pair lane held in registers (2 KB)
+  // Value-side loads and the outlier segments of a block, issued at the end of the previous
+  // block (after that block's value work), i.e. before the next key prefetch: loads
+  // complete in order, so waiting for these never waits for the key prefetch.
   struct VBuf {
     uint32_t vw[KWD];     // value half-rows of channels 2*lane, 2*lane+1
     float2 tst;           // value (S, M) of token j
+    uint4 ob[NOB];        // outlier segment chunk j (j = lane of the wave pair)
   };
 
   struct Shared {
-    float2* tab;          // this wave pair's table [64][PT]
+    float2* tab;          // this wave pair's table [64][PS]
     float2* qb;           // this wave pair's rotated query pairs [64] (al, be)
     float2* kst;          // this wave pair's key (scale, offset) per channel [128]
     const float2* vlut;   // value code pairs [PT]
     float* pS;            // this wave's p * S per token of the half [64]
     float* p;             // this wave's p per token [64]
-    float2* vst;          // this wave's value (S, M) per token [64]
-    uint8_t* blob;        // this wave's outlier staging
+    float* M;             // this wave's value offset M per token [64]
+    uint8_t* blob;        // this wave pair's outlier staging
     const float* q;       // query (original domain, scale folded) [128]
     const float* trev;    // theta_i / (2 pi) [64]
     const float* cbk;     // key codebook [16] (NUQ)
@@ -111,6 +118,11 @@ struct TabDecoder {
 
   __device__ __forceinline__ void fetch_v(VBuf& V, int blk) const {
     const uint8_t* rec = record(blk);
+    if (a.k_out > 0) {
+      const uint4* src = reinterpret_cast<const uint4*>(rec + a.lay.ko_val);
+#pragma unroll
+      for (int k = 0; k < NOB; ++k) V.ob[k] = src[min(j + 128 * k, ob_chunks - 1)];
+    }
     load_row<R>(V.vw, rec + a.lay.vc + (size_t)par * (128 * RH) + (size_t)lane * R);
     if constexpr (MODE == NUQ) {
       V.tst.x = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + j];   // h
@@ -150,7 +162,7 @@ struct TabDecoder {
       Ay[c] = be * ky;
       By[c] = -al * ky;
     }
-    float4* dst = reinterpret_cast<float4*>(S.tab + ib * PT + hb * (PT / 2));
+    float4* dst = reinterpret_cast<float4*>(S.tab + ib * PS + hb * (PT / 2));
 #pragma unroll
     for (int e = 0; e < PT / 2; e += 2) {
       float2 v[2];
@@ -203,46 +215,56 @@ struct TabDecoder {
     return p;
   }
 
-  // One half block (parity par) of block blk whose loads are in B; the wave pair's table
-  // for blk is complete.
-  __device__ __forceinline__ void process(const Buf& B, int blk, const float (&rc)[64], const float (&rs)[64]) {
+  // Outlier segments of block blk into the wave pair's LDS staging (before the barrier that
+  // precedes their use): the chunks held in V, the rest (large k) loaded here.
+  __device__ __forceinline__ void stage_blob(const VBuf& V, int blk) const {
+    uint4* dst = reinterpret_cast<uint4*>(S.blob);
+#pragma unroll
+    for (int k = 0; k < NOB; ++k)
+      if (j + 128 * k < ob_chunks) dst[j + 128 * k] = V.ob[k];
+    if (ob_chunks > 128 * NOB) {
+      const uint4* src = reinterpret_cast<const uint4*>(record(blk) + a.lay.ko_val);
+      for (int k = j + 128 * NOB; k < ob_chunks; k += 128) dst[k] = src[k];
+    }
+  }
+
+  // One half block (parity par) of block blk: key loads in B, value loads in V (both issued
+  // a block ahead); the wave pair's table and outlier staging for blk are complete.
+  __device__ __forceinline__ void process(const Buf& B, const VBuf& V, int blk, const float (&rc)[64],
+                                          const float (&rs)[64]) {
     const uint8_t* rec = record(blk);
     const bool outl = a.k_out > 0;
-    VBuf V;
-    fetch_v(V, blk);
-    uint4 ob[NOB];
-    if (outl) {
-      const uint4* src = reinterpret_cast<const uint4*>(rec + a.lay.ko_val);
-      const int last = ob_chunks - 1;
-#pragma unroll
-      for (int k = 0; k < NOB; ++k) ob[k] = src[min(lane + 64 * k, last)];
-    }
 
-    // ---- scores: two fma per channel pair on the tabulated (U, W)
+    // ---- scores: two fma per channel pair on the tabulated (U, W). Software-pipelined in
+    // chunks of CH pairs: the table reads of chunk c+1 are issued before the fma of chunk c
+    // (scheduling barriers keep that order), so 2*CH LDS reads are in flight at a time.
+    constexpr int CH = 8;
     float sc0 = 0.f, sc1 = 0.f;
+    float2 uw[2][CH];
+    auto kread = [&](int c, float2 (&dst)[CH]) {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const uint32_t idx = pair_index(B.kw, i, 128);
-      const float2 uw = *reinterpret_cast<const float2*>(
-          reinterpret_cast<const uint8_t*>(S.tab) + (size_t)(i * PT + idx) * 8);
-      sc0 = fmaf(rc[i], uw.x, sc0);
-      sc1 = fmaf(rs[i], uw.y, sc1);
+      for (int k = 0; k < CH; ++k) {
+        const int i = c * CH + k;
+        const uint32_t idx = pair_index(B.kw, i, 128);
+        dst[k] = *reinterpret_cast<const float2*>(reinterpret_cast<const uint8_t*>(S.tab) + (size_t)(i * PS + idx) * 8);
+      }
+    };
+    kread(0, uw[0]);
+#pragma unroll
+    for (int c = 0; c < 64 / CH; ++c) {
+      if (c + 1 < 64 / CH) kread(c + 1, uw[(c + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        sc0 = fmaf(rc[c * CH + k], uw[c & 1][k].x, sc0);
+        sc1 = fmaf(rs[c * CH + k], uw[c & 1][k].y, sc1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     float sc = sc0 + sc1;
 
     // ---- key outliers of row j (CSR): the fp16 value replaces the dense one
     if (outl) {
-      if (ob_chunks <= NOB * 64) {
-        uint4* dst = reinterpret_cast<uint4*>(S.blob);
-#pragma unroll
-        for (int k = 0; k < NOB; ++k)
-          if (lane + 64 * k < ob_chunks) dst[lane + 64 * k] = ob[k];
-      } else {
-        const uint4* src = reinterpret_cast<const uint4*>(rec + a.lay.ko_val);
-        uint4* dst = reinterpret_cast<uint4*>(S.blob);
-        for (int k = lane; k < ob_chunks; k += 64) dst[k] = src[k];
-      }
-      wave_sync();
       const uint16_t* ptr = reinterpret_cast<const uint16_t*>(S.blob + (a.lay.ko_ptr - a.lay.ko_val));
       const uint8_t* idx = S.blob + (a.lay.ko_idx - a.lay.ko_val);
       const __half* val = reinterpret_cast<const __half*>(S.blob);
@@ -264,19 +286,36 @@ struct TabDecoder {
     pm = fmaf(p, V.tst.y, pm);                 // sum_t p_t M_t (code-independent part)
     S.pS[lane] = p * V.tst.x;
     S.p[lane] = p;
-    S.vst[lane] = V.tst;
+    S.M[lane] = V.tst.y;
     wave_sync();
 
     // ---- P.V over the 64 tokens of this half, channels 2*lane and 2*lane+1
+    // (pipelined like the scores: reads of chunk c+1 before the fma of chunk c)
+    constexpr int CV = 4;
     float o0 = 0.f, o1 = 0.f;
+    float2 vb[2][CV][3];
+    auto vread = [&](int c, float2 (&dst)[CV][3]) {
 #pragma unroll
-    for (int pp = 0; pp < 32; ++pp) {
-      const int t = half_row_token(2 * pp);   // positions 2pp, 2pp+1 hold tokens t, t+1
-      const float2 ps = *reinterpret_cast<const float2*>(S.pS + t);
-      const float2 v0 = S.vlut[pair_index(V.vw, pp, 64)];
-      const float2 v1 = S.vlut[pair_index(V.vw + KWD / 2, pp, 64)];
-      o0 = fmaf(ps.x, v0.x, fmaf(ps.y, v0.y, o0));
-      o1 = fmaf(ps.x, v1.x, fmaf(ps.y, v1.y, o1));
+      for (int k = 0; k < CV; ++k) {
+        const int pp = c * CV + k;
+        const int t = half_row_token(2 * pp);   // positions 2pp, 2pp+1 hold tokens t, t+1
+        dst[k][0] = *reinterpret_cast<const float2*>(S.pS + t);
+        dst[k][1] = S.vlut[pair_index(V.vw, pp, 64)];
+        dst[k][2] = S.vlut[pair_index(V.vw + KWD / 2, pp, 64)];
+      }
+    };
+    vread(0, vb[0]);
+#pragma unroll
+    for (int c = 0; c < 32 / CV; ++c) {
+      if (c + 1 < 32 / CV) vread(c + 1, vb[(c + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < CV; ++k) {
+        const float2 ps = vb[c & 1][k][0], v0 = vb[c & 1][k][1], v1 = vb[c & 1][k][2];
+        o0 = fmaf(ps.x, v0.x, fmaf(ps.y, v0.y, o0));
+        o1 = fmaf(ps.x, v1.x, fmaf(ps.y, v1.y, o1));
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     acc0 += o0;
     acc1 += o1;
@@ -294,11 +333,12 @@ struct TabDecoder {
           const int t = idx[e] - 64 * par;
           if (t < 0 || t >= 64) continue;
           const uint32_t code = code_sel<BITS, 64>(V.vw + k * (KWD / 2), half_row_token(t));
-          const float2 st = S.vst[t];
           const float vc = MODE == NUQ ? S.cbv[code] : (float)code;
-          const float delta = __half2float(val[e]) - fmaf(vc, st.x, st.y);
-          if (k == 0) acc0 = fmaf(S.p[t], delta, acc0);
-          else acc1 = fmaf(S.p[t], delta, acc1);
+          // p_t (val - (vc S_t + M_t)) with p_t S_t, p_t and M_t from LDS
+          const float pt = S.p[t];
+          const float corr = fmaf(pt, __half2float(val[e]) - S.M[t], -S.pS[t] * vc);
+          if (k == 0) acc0 += corr;
+          else acc1 += corr;
         }
       }
     }
@@ -306,16 +346,17 @@ struct TabDecoder {
   }
 
   // Tokens 64*par .. 64*par+63 of the fp16 tail (position 128*nblk + j), waves 0 and 1.
-  __device__ __forceinline__ void tail_half(const float (&rc)[64], const float (&rs)[64], float2* qt) {
+  // Runs once per (sequence, kv head): the per-offset angles come from the table in memory
+  // (the main loop's registers for them are dead here).
+  __device__ __forceinline__ void tail_half(const float2* qt) {
     const int n_valid = min(64, a.tail_n - 64 * par);
     const __half* tk = a.tail + (size_t)(blockIdx.z * a.Hkv + blockIdx.y) * (2 * kT * kD);
     const __half* tv = tk + kT * kD;
     const bool valid = lane < n_valid;
     float sc = 0.f;
     const uint4* krow = reinterpret_cast<const uint4*>(tk + (size_t)j * kD);
-    // fully unrolled (rc, rs are indexed by i), in chunks of 4 pairs that the scheduler may
-    // not merge, so that it does not hoist all 64 loads at once
-#pragma unroll
+    const float2* off = reinterpret_cast<const float2*>(a.rope_off) + j;   // pair-major: [i][j]
+#pragma unroll 1
     for (int i0 = 0; i0 < 64; i0 += 4) {
       const uint4 kv = valid ? krow[i0 / 4] : make_uint4(0u, 0u, 0u, 0u);
       const uint32_t kd[4] = {kv.x, kv.y, kv.z, kv.w};
@@ -324,11 +365,11 @@ struct TabDecoder {
         const int i = i0 + k;
         const float2 kk = __half22float2(__builtin_bit_cast(__half2, kd[k]));
         const float2 q2 = qt[i];
+        const float2 cs = off[(size_t)i * 128];
         const float U = fmaf(kk.x, q2.x, kk.y * q2.y);
         const float W = fmaf(kk.x, q2.y, -kk.y * q2.x);
-        sc = fmaf(rc[i], U, fmaf(rs[i], W, sc));
+        sc = fmaf(cs.x, U, fmaf(cs.y, W, sc));
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     const float p = softmax_step(valid ? sc : -INFINITY);
     S.p[lane] = p;
@@ -352,7 +393,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   using Dec = TabDecoder<MODE, BITS>;
   constexpr int PT = Dec::PT;
   extern __shared__ __align__(16) uint8_t s_dyn[];
-  __shared__ __align__(16) float2 s_tab[2][64 * PT];
+  __shared__ __align__(16) float2 s_tab[2][64 * Dec::PS];
   __shared__ __align__(16) float2 s_vlut[PT];
   __shared__ __align__(16) float2 s_qb[2][64];
   __shared__ __align__(16) float2 s_kst[2][128];
@@ -361,7 +402,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ float s_cb[32];
   __shared__ __align__(16) float s_pS[4][64];
   __shared__ __align__(16) float s_p[4][64];
-  __shared__ __align__(16) float2 s_vst[4][64];
+  __shared__ __align__(16) float s_M[4][64];
   __shared__ float s_m[4], s_l[4];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -392,8 +433,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   sh.vlut = s_vlut;
   sh.pS = s_pS[w];
   sh.p = s_p[w];
-  sh.vst = s_vst[w];
-  sh.blob = s_dyn + (size_t)w * a.wave_lds;
+  sh.M = s_M[w];
+  sh.blob = s_dyn + (size_t)(w >> 1) * a.wave_lds;
   sh.q = s_q;
   sh.trev = s_trev;
   sh.cbk = s_cb;
@@ -411,18 +452,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int blo = split * a.blocks_per_split;
   const int bhi = min(a.nblk, blo + a.blocks_per_split);
   const int n_iter = (bhi - blo + 1) >> 1;
+  // Two key-load buffers used alternately (a register copy between them would wait for
+  // the next block's loads at the end of every iteration); one value buffer, refilled for
+  // the next block right after its use.
   typename Dec::Buf A, Bn;
+  typename Dec::VBuf V;
   int blk = blo + d.pr;
-  if (blk < bhi) d.fetch(A, blk);
+  if (blk < bhi) {
+    d.fetch(A, blk);
+    d.fetch_v(V, blk);
+  }
   __syncthreads();   // the value table is complete
-  for (int it = 0; it < n_iter; ++it, blk += 2) {
-    const bool valid = blk < bhi;
-    if (blk + 2 < bhi) d.fetch(Bn, blk + 2);
-    if (valid) d.build(A);
+  auto step = [&](typename Dec::Buf& cur, typename Dec::Buf& nxt, int bk) {
+    const bool valid = bk < bhi;
+    if (valid && a.k_out > 0) d.stage_blob(V, bk);
+    if (bk + 2 < bhi) d.fetch(nxt, bk + 2);
+    if (valid) d.build(cur);
     __syncthreads();
-    if (valid) d.process(A, blk, rc, rs);
+    if (valid) d.process(cur, V, bk, rc, rs);
+    if (bk + 2 < bhi) d.fetch_v(V, bk + 2);
     __syncthreads();
-    A = Bn;
+  };
+  for (int it = 0; it < n_iter; it += 2, blk += 4) {
+    step(A, Bn, blk);
+    if (it + 1 < n_iter) step(Bn, A, blk + 2);
   }
 
   // ---- the fp16 tail (waves 0 and 1; it belongs to the last split)
@@ -435,7 +488,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       qt[tid] = make_float2(fmaf(qx, rb.x, qy * rb.y), fmaf(qy, rb.x, -qx * rb.y));
     }
     __syncthreads();
-    if (w < 2 && 64 * d.par < a.tail_n) d.tail_half(rc, rs, qt);
+    if (w < 2 && 64 * d.par < a.tail_n) d.tail_half(qt);
   }
 
   // ---- merge the four wave states
@@ -474,7 +527,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 template <int MODE, int BITS>
 hipError_t launch_t(const DecodeArgs& a, int batch, hipStream_t s) {
   hipLaunchKernelGGL((decode_tab_kernel<MODE, BITS>), dim3(a.splits, a.Hkv, batch), dim3(kThreads),
-                     (size_t)4 * a.wave_lds, s, a);
+                     (size_t)2 * a.wave_lds, s, a);   // outlier staging per wave pair
   return hipGetLastError();
 }
 

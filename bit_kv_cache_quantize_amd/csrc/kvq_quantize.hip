@@ -248,27 +248,13 @@ __device__ __forceinline__ float div_rn(float d, float s, float r) {
 
 // NUQ code = number of decision thresholds tau_j <= u (tau ascending, 2^b - 1 of them; the
 // host derives them from the codebook so that this equals the first-index argmin of the
-// fp32 distances |u - C_j|), found by binary search over the bits of the code.
+// fp32 distances |u - C_j|). One compare and one carry-add per threshold, no branches.
 template <int BITS>
 __device__ __forceinline__ uint32_t nuq_search(float u, const float* tau) {
-  if constexpr (BITS == 2) {
-    const bool b1 = u >= tau[1];
-    const bool b0 = u >= (b1 ? tau[2] : tau[0]);
-    return (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
-  } else if constexpr (BITS == 3) {
-    const bool b2 = u >= tau[3];
-    const bool b1 = u >= (b2 ? tau[5] : tau[1]);
-    const bool b0 = u >= (b2 ? (b1 ? tau[6] : tau[4]) : (b1 ? tau[2] : tau[0]));
-    return (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
-  } else {
-    const bool b3 = u >= tau[7];
-    const bool b2 = u >= (b3 ? tau[11] : tau[3]);
-    const bool b1 = u >= (b3 ? (b2 ? tau[13] : tau[9]) : (b2 ? tau[5] : tau[1]));
-    const float t0 = b3 ? (b2 ? (b1 ? tau[14] : tau[12]) : (b1 ? tau[10] : tau[8]))
-                        : (b2 ? (b1 ? tau[6] : tau[4]) : (b1 ? tau[2] : tau[0]));
-    const bool b0 = u >= t0;
-    return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
-  }
+  uint32_t code = 0;
+#pragma unroll
+  for (int t = 0; t < (1 << BITS) - 1; ++t) code += u >= tau[t] ? 1u : 0u;
+  return code;
 }
 
 // Statistics of one vector: (sa, sb) = RTN/KVarN (s, m), NUQ (z, h), symmetric int4 (s, -),
@@ -300,16 +286,17 @@ __device__ __forceinline__ VecStats stats_of(float lo, float hi, float amax) {
 template <int MODE, int BITS>
 __device__ __forceinline__ uint32_t code_of(float x, const VecStats& v, const float* tau) {
   constexpr int QMAX = (1 << BITS) - 1;
+  // both operands of every select are computed: the selects stay branch-free
   if constexpr (MODE == NUQ) {
-    float u = v.sb == 0.f ? 0.f : div_rn(__fsub_rn(x, v.sa), v.sb, v.rc);
-    u = fminf(fmaxf(u, -1.f), 1.f);
+    const float q = div_rn(__fsub_rn(x, v.sa), v.sb, v.rc);
+    const float u = v.sb == 0.f ? 0.f : fminf(fmaxf(q, -1.f), 1.f);
     return nuq_search<BITS>(u, tau);
   } else if constexpr (MODE == SYM) {
-    const float q = v.sa == 0.f ? 0.f : rintf(div_rn(x, v.sa, v.rc));
-    return (uint32_t)((int)fminf(fmaxf(q, -8.f), 7.f) + 8);
+    const float q = rintf(div_rn(x, v.sa, v.rc));
+    return (uint32_t)((int)(v.sa == 0.f ? 0.f : fminf(fmaxf(q, -8.f), 7.f)) + 8);
   } else {
-    const float q = v.sa == 0.f ? 0.f : rintf(div_rn(__fsub_rn(x, v.sb), v.sa, v.rc));
-    return (uint32_t)fminf(fmaxf(q, 0.f), (float)QMAX);
+    const float q = rintf(div_rn(__fsub_rn(x, v.sb), v.sa, v.rc));
+    return (uint32_t)(v.sa == 0.f ? 0.f : fminf(fmaxf(q, 0.f), (float)QMAX));
   }
 }
 
@@ -436,8 +423,8 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
 #pragma unroll
     for (int k = 0; k < 8; ++k) thr[k] = best[k];
   }
-  // this lane's outliers, bit 8i + e
-  uint64_t omask = 0;
+  // this lane's outliers: bit 8(i & 3) + e of om[i >> 2]
+  uint32_t om[2] = {0u, 0u};
   if (MODE != KVARN && k_out > 0) {
     opaque(X.v);
 #pragma unroll
@@ -445,10 +432,10 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const bool o = per_chan ? X.key(i, e, 32 * w + 4 * i + r) >= thr[e] : X.key(i, e, 8 * g + e) >= thr[i];
-        omask |= (uint64_t)o << (8 * i + e);
+        om[i >> 2] |= o ? (1u << (8 * (i & 3) + e)) : 0u;
       }
   }
-  auto is_out = [&](int i, int e) -> bool { return (omask >> (8 * i + e)) & 1u; };
+  auto is_out = [&](int i, int e) -> bool { return (om[i >> 2] >> (8 * (i & 3) + e)) & 1u; };
 
   // ---- statistics over the non-outliers
   if constexpr (MODE != KVARN) opaque(X.v);   // widen again where used (keeps 32, not 64, tile registers)
@@ -460,11 +447,11 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       lo[e] = INFINITY;
       hi[e] = MODE == SYM ? 0.f : -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (!is_out(i, e)) {
-          lo[e] = fminf(lo[e], X.f(i, e));
-          hi[e] = MODE == SYM ? fmaxf(hi[e], fabsf(X.f(i, e))) : fmaxf(hi[e], X.f(i, e));
-        }
+      for (int i = 0; i < 8; ++i) {   // branch-free: an outlier enters as the neutral value
+        const bool o = is_out(i, e);
+        const float x = X.f(i, e);
+        lo[e] = fminf(lo[e], o ? INFINITY : x);
+        hi[e] = MODE == SYM ? fmaxf(hi[e], o ? 0.f : fabsf(x)) : fmaxf(hi[e], o ? -INFINITY : x);
       }
     }
     // both reductions share one barrier
@@ -495,7 +482,10 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if (!is_out(i, e)) { lo = fminf(lo, X.f(i, e)); hi = fmaxf(hi, X.f(i, e)); }
+        const bool o = is_out(i, e);
+        const float x = X.f(i, e);
+        lo = fminf(lo, o ? INFINITY : x);
+        hi = fmaxf(hi, o ? -INFINITY : x);
       }
       lo = tok_reduce(lo, MinF());
       hi = tok_reduce(hi, MaxF());
