@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--config", default=DEFAULT)
     p.add_argument("--splits", type=int, default=0, help="decode splits (0 = automatic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=8, help="kv heads in the oracle sample")
+    p.add_argument("--cpu-heads", type=int, default=32, help="(sequence, kv head) units in the oracle sample")
     return p.parse_args()
 
 
@@ -192,27 +192,74 @@ def record_payload(wl):
     return n
 
 
+CSRC = os.path.join(ROOT, "bit_kv_cache_quantize_amd", "csrc")
+KERNEL_SOURCES = {
+    "quantize_kernel": ["kvq_quantize.hip", "kvq_internal.h"],
+    "decode_tab_kernel": ["kvq_decode_tab.hip", "kvq_decode_common.h", "kvq_internal.h"],
+    "decode_mfma_kernel": ["kvq_decode_mfma.hip", "kvq_decode_common.h", "kvq_internal.h"],
+    "decode_kernel": ["kvq_decode.hip", "kvq_decode_common.h", "kvq_internal.h"],
+}
+
+
+def decode_kernel_name(wl):
+    """The decode kernel the library launches for this cache (same rule as kvq_decode_attn)."""
+    if wl.pre_rope and wl.group == 1 and wl.bits in (2, 3) and wl.mode in (0, 1):
+        return "decode_tab_kernel"
+    if not wl.pre_rope and wl.outliers_per_vec == 0 and wl.bits in (2, 4) and wl.mode in (0, 2, 3):
+        return "decode_mfma_kernel"
+    return "decode_kernel"
+
+
+def sources_sha256(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3 counter
+    summary (profiles/<workload>_hbm_traffic.txt: FETCH_SIZE and WRITE_SIZE per dispatch,
+    scaled by the copy-kernel calibration). None when there is no summary or the kernel's
+    sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if "## data" not in text:
+        return None
+    data = json.loads(text.split("## data", 1)[1].strip().splitlines()[0])
+    k = data.get("kernels", {}).get(kernel)
+    if not k or k.get("sources_sha256") != sources_sha256(kernel):
+        return None
+    return k["traffic_bytes_per_launch"]
+
+
 def median(x):
     s = sorted(x)
     return s[len(s) // 2] if s else float("nan")
 
 
 def cpu_baseline(wl, heads):
-    """The oracle, untuned, on a bounded sample: `heads` kv heads of sequence 0, layer 0,
-    full context (append = quantize every block, decode = dequantize + fp64 attention)."""
+    """The oracle, untuned, on a bounded sample of the workload: up to `heads` kv heads of
+    the first sequences of layer 0 (at most 32K tokens each), so that it takes roughly 10-20
+    s of one core. Append = quantize every block; decode = dequantize + fp64 attention."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     import synth
     from oracle import kvq_oracle as O
     ctx = min(wl.context, 32768)
-    heads = min(heads, wl.n_kv_heads)
-    cfg = O.Config(1, 1, heads, heads * wl.group, ceil128(ctx), wl.mode, wl.bits, wl.outliers_per_vec,
+    nh = min(heads, wl.n_kv_heads)
+    nb = min(wl.batch, max(1, heads // nh))
+    cfg = O.Config(1, nb, nh, nh * wl.group, ceil128(ctx), wl.mode, wl.bits, wl.outliers_per_vec,
                    wl.pre_rope, wl.rope_theta, wl.varn_iters)
-    k = np.stack([np.stack([synth.gen_k(wl, 0, 0, h, 0, ctx) for h in range(heads)])])
-    v = np.stack([np.stack([synth.gen_v(wl, 0, 0, h, 0, ctx) for h in range(heads)])])
-    q = np.stack([np.stack([synth.gen_q(wl, 0, 0, h) for h in range(heads * wl.group)])])
+    k = np.stack([np.stack([synth.gen_k(wl, 0, b, h, 0, ctx) for h in range(nh)]) for b in range(nb)])
+    v = np.stack([np.stack([synth.gen_v(wl, 0, b, h, 0, ctx) for h in range(nh)]) for b in range(nb)])
+    q = np.stack([np.stack([synth.gen_q(wl, 0, b, h) for h in range(nh * wl.group)]) for b in range(nb)])
     oc = O.OracleCache(cfg)
-    for h in range(heads):
+    for h in range(nh):
         for w in (0, 1):
             if wl.mode == 1:
                 oc.load_codebook(0, h, w, synth.gen_codebook(wl, 0, h, w, wl.bits))
@@ -225,12 +272,13 @@ def cpu_baseline(wl, heads):
         oc.decode(0, q)
         t2 = time.perf_counter()
     nblk, tail = ctx // 128, ctx % 128
-    dbytes = heads * (nblk * record_payload(wl) + tail * 512) + heads * wl.group * 128 * 6
+    units = nb * nh
+    dbytes = units * (nblk * record_payload(wl) + tail * 512) + units * wl.group * 128 * 6
     return {
         "value": dbytes / (t2 - t1) / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"layer 0, sequence 0, {heads} of {wl.n_kv_heads} kv heads, {ctx} tokens: "
+        "sample": f"layer 0, {nb} sequence(s) x {nh} of {wl.n_kv_heads} kv heads, {ctx} tokens: "
                   f"append {t1 - t0:.2f} s, decode {t2 - t1:.2f} s (numpy, one thread)",
-        "append_mtok_s": ctx * heads / wl.n_kv_heads / (t1 - t0) / 1e6,
+        "append_mtok_s": ctx * units / wl.n_kv_heads / (t1 - t0) / 1e6,
         "decode_s": t2 - t1, "append_s": t1 - t0,
     }
 
@@ -263,13 +311,23 @@ def main():
         times, n = b.append_separately(5)
         app_ms = median(times)
         app_rate = wl.batch * n / (app_ms * 1e-3) / 1e6
-        app_gbs = wl.batch * wl.n_kv_heads * (n * 512 + (n // 128) * rec_payload) / (app_ms * 1e-3) / 1e9
-    roof_dec = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "decode_kernel",
-                "bytes_per_launch": dbytes // layers, "us_per_launch": round(dec_ms * 1e3 / layers, 2)}
-    roof_app = {"bound": "hbm", "achieved": round(app_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(app_gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "quantize_kernel",
-                "us_per_step": round(app_ms * 1e3, 2)}
+        abytes = wl.batch * wl.n_kv_heads * (n * 512 + (n // 128) * rec_payload)   # the one timed chunk
+        app_gbs = abytes / (app_ms * 1e-3) / 1e9
+    dec_kernel = decode_kernel_name(wl)
+
+    def roof(achieved_gbs, kernel, us, algo_bytes):
+        t = measured_traffic(wl.name, kernel)
+        return {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None if t is None else round(t / (us * 1e-6) / 1e9, 1),
+                "kernel": kernel, "us_per_launch": round(us, 2),
+                "algorithmic_bytes_per_launch": int(algo_bytes),
+                "traffic_bytes_per_launch": t}
+
+    dec_us = dec_ms * 1e3 / layers
+    roof_dec = roof(gbs, dec_kernel, dec_us, dbytes // layers)
+    app_launches = layers * len(b.chunks) if app else 1
+    roof_app = roof(app_gbs, "quantize_kernel", app_ms * 1e3 / app_launches, abytes / app_launches)
     dominant = roof_app if (app and sum(app) > sum(dec)) else roof_dec
     line = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

@@ -99,6 +99,27 @@ def compare_record(got: np.ndarray, blk, ocfg, stats: RecordStats | None = None,
         assert e1 <= 1e-5 and e2 <= 1e-5, f"{where}: {seg} stats off by {e1}, {e2}"
 
 
+def kvarn_block_from_record(got: np.ndarray, ocfg) -> "O.Block":
+    """An oracle Block holding what a KVarN record read back from the device stores (codes,
+    RTN statistics, s1), so that the oracle's fp64 dequantization and attention can run on
+    the device-produced cache (decode parity, separate from the quantize tolerance)."""
+    off, _ = O.record_layout(ocfg.mode, ocfg.bits, ocfg.outliers_per_vec)
+    bits = ocfg.bits
+    R = 16 * bits
+    o, n = off["kc"]
+    kc = O.unpack_codes(got[o:o + n].reshape(128, R), bits).astype(np.uint8)
+    o, n = off["vc"]
+    vp = O.unpack_codes(got[o:o + n].reshape(2, 128, R // 2), bits)
+    inv = O.half_row_token(np.arange(64))
+    vc = np.concatenate([vp[0][:, inv].T, vp[1][:, inv].T]).astype(np.uint8)
+    st = {}
+    for seg in ("ks", "vs", "k1", "v1"):
+        o, n = off[seg]
+        st[seg] = got[o:o + n].view(np.float32).copy()
+    return O.Block(kc, vc, (st["ks"][:128], st["ks"][128:]), (st["vs"][:128], st["vs"][128:]),
+                   ks1=st["k1"], vs1=st["v1"])
+
+
 def attention_close(got: np.ndarray, ref: np.ndarray, rtol=1e-3):
     """max |got - ref| <= rtol * max |ref| for every (sequence, query head) row."""
     got = got.reshape(-1, 128).astype(np.float64)
