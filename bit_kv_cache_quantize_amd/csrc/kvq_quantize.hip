@@ -49,18 +49,15 @@ struct Smem {
   uint16_t optr[kD + 1];          // storage row pointers
 };
 
-// Key of the top-k |x| selection: larger magnitude first, then lower element index e; the
-// lowest bit carries the sign, so that a key alone gives back the element's position and
-// its exact fp16 value (magnitude bits 8..22, sign bit 0, index 127 - bits 1..7).
+// Key of the top-k |x| selection: larger magnitude first, then lower element index e
+// (magnitude bits from bit 7 up, 127 - e in bits 0..6); a key gives back its element's
+// position within the vector.
 __device__ __forceinline__ uint32_t mag_key(float x, int e) {
   // fp32 form (KVarN tiles, which never select outliers): magnitude bits above bit 13
   const uint32_t u = __float_as_uint(x);
-  return (((u & 0x7fffffffu) >> 13) << 8) | ((uint32_t)(127 - e) << 1) | (u >> 31);
+  return (((u & 0x7fffffffu) >> 13) << 7) | (uint32_t)(127 - e);
 }
-__device__ __forceinline__ uint32_t key_index(uint32_t key) { return 127u - ((key >> 1) & 127u); }
-__device__ __forceinline__ uint16_t key_f16_bits(uint32_t key) {
-  return (uint16_t)(((key >> 8) & 0x7fffu) | ((key & 1u) << 15));
-}
+__device__ __forceinline__ uint32_t key_index(uint32_t key) { return 127u - (key & 127u); }
 
 // The block tile of one lane: 8 tokens x 8 channels. Non-KVarN modes keep the fp16
 // input bits (two channels per register) and widen on use, which halves the live
@@ -76,8 +73,8 @@ template <> struct Tile<false> {
   __device__ __forceinline__ uint32_t bits(int i, int e) const { return (e & 1) ? v[i][e >> 1] >> 16 : v[i][e >> 1] & 0xffffu; }
   __device__ __forceinline__ float f(int i, int e) const { return __half2float(__ushort_as_half((unsigned short)bits(i, e))); }
   __device__ __forceinline__ uint32_t key(int i, int e, int idx) const {
-    const uint32_t h = bits(i, e);
-    return ((h & 0x7fffu) << 8) | ((uint32_t)(127 - idx) << 1) | (h >> 15);
+    const uint32_t mag = (e & 1) ? __builtin_amdgcn_ubfe(v[i][e >> 1], 16, 15) : v[i][e >> 1] & 0x7fffu;
+    return (mag << 7) | (uint32_t)(127 - idx);
   }
 };
 
@@ -300,8 +297,9 @@ __device__ __forceinline__ uint32_t code_of(float x, const VecStats& v, const fl
   }
 }
 
-// One tensor (TENSOR 0: keys, 1: values) of block j of (sequence b, kv head h).
-template <int MODE, int BITS, int TENSOR>
+// One tensor (TENSOR 0: keys, 1: values) of block j of (sequence b, kv head h). KO: outliers
+// per vector, 0 (none), 1 (one), 2 (two or more: a.k_out).
+template <int MODE, int BITS, int TENSOR, int KO>
 __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, int j, int h, int b) {
   constexpr int tensor = TENSOR;
   const int tid = threadIdx.x, lane = tid & 63, r = lane >> 4, g = lane & 15;
@@ -309,7 +307,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
   const size_t unit = (size_t)b * a.Hkv + h;
   uint8_t* rec = a.rec + (unit * a.max_blocks + (size_t)(a.blk0 + j)) * a.lay.rec_bytes;
   constexpr int R = 16 * BITS;                                  // bytes per 128 codes
-  const int k_out = MODE == KVARN ? 0 : a.k_out;
+  const int k_out = KO == 0 ? 0 : (KO == 1 ? 1 : a.k_out);
   constexpr bool per_chan = TENSOR == 0 || MODE == SYM;         // vector = a channel over the block's tokens
   int ph = 0;                                                   // alternating cross-wave buffer
 
@@ -379,7 +377,8 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
     }
   }
 
-  // ---- outlier thresholds: the k-th largest key of each vector (UINT_MAX: none)
+  // ---- outlier selection: per vector the k_out largest keys, one max-reduction per round
+  // (rounds after the first skip the keys already taken); thr = the last one taken
   // thr[e] for channel 8g+e when per_chan, thr[i] for token t_i otherwise
   uint32_t thr[8];
 #pragma unroll
@@ -394,7 +393,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const uint32_t key = X.key(i, e, 32 * w + 4 * i + r);
-          m = (key < thr[e] && key > m) ? key : m;
+          m = (KO == 1 || key < thr[e]) ? (key > m ? key : m) : m;
         }
         best[e] = m;
       }
@@ -411,7 +410,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t key = X.key(i, e, 8 * g + e);
-          m = (key < thr[i] && key > m) ? key : m;
+          m = (KO == 1 || key < thr[i]) ? (key > m ? key : m) : m;
         }
         best[i] = tok_reduce(m, MaxU());
       }
@@ -423,9 +422,14 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
 #pragma unroll
     for (int k = 0; k < 8; ++k) thr[k] = best[k];
   }
-  // this lane's outliers: bit 8(i & 3) + e of om[i >> 2]
+  // this lane's outliers. One per vector: its element index, compared directly (d = index
+  // minus this lane's first element). Several: bit 8(i & 3) + e of om[i >> 2].
+  int d1[8];
   uint32_t om[2] = {0u, 0u};
-  if (MODE != KVARN && k_out > 0) {
+  if constexpr (KO == 1) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) d1[k] = (int)key_index(thr[k]) - (per_chan ? 32 * w + r : 8 * g);
+  } else if constexpr (KO == 2) {
     opaque(X.v);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -435,7 +439,11 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
         om[i >> 2] |= o ? (1u << (8 * (i & 3) + e)) : 0u;
       }
   }
-  auto is_out = [&](int i, int e) -> bool { return (om[i >> 2] >> (8 * (i & 3) + e)) & 1u; };
+  auto is_out = [&](int i, int e) -> bool {
+    if constexpr (KO == 0) return false;
+    else if constexpr (KO == 1) return per_chan ? d1[e] == 4 * i : d1[i] == e;
+    else return (om[i >> 2] >> (8 * (i & 3) + e)) & 1u;
+  };
 
   // ---- statistics over the non-outliers
   if constexpr (MODE != KVARN) opaque(X.v);   // widen again where used (keeps 32, not 64, tile registers)
@@ -619,9 +627,15 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
   // ---- outliers: keys CSR by token (row t, column c), values CSC by channel (row c,
   // column t); entries sorted by (row, column), fp16 value bits kept exactly. The keys of
   // every vector's outliers were recorded during the selection; each encodes its element.
-  if (MODE != KVARN && k_out > 0) {
+  if (KO != 0) {
     __syncthreads();                                   // okey complete, omask cleared
     const int n_ent = 128 * k_out;
+    const __half* in = (tensor ? a.v_in : a.k_in) + unit * (size_t)a.n_new * kD;
+    const __half* tl = a.tail + unit * (2 * kT * kD) + (size_t)tensor * kT * kD;
+    auto value_bits = [&](int t, int c) -> uint16_t {   // the element's fp16 input, exactly
+      const __half* src = (j == 0 && t < a.t0) ? tl + (size_t)t * kD : in + ((size_t)j * kT + t - a.t0) * kD;
+      return reinterpret_cast<const uint16_t*>(src)[c];
+    };
     auto place = [&](int n, int& row, int& col, uint32_t& key) {
       const int v = n & 127, p = n >> 7;
       key = sm.okey[v][p];
@@ -669,7 +683,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
         const int lim = col - 32 * d;   // bits of word d below col
         pos += lim >= 32 ? __popc(m) : (lim > 0 ? __popc(m & ((1u << lim) - 1u)) : 0);
       }
-      val[pos] = key_f16_bits(key);
+      val[pos] = value_bits(tensor == 0 ? row : col, tensor == 0 ? col : row);
       idx[pos] = (uint8_t)col;
     }
   }
@@ -679,8 +693,18 @@ template <int MODE, int BITS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MODE == KVARN ? 2 : 4))) void quantize_kernel(QuantArgs a) {
   __shared__ Smem sm;
   const int j = blockIdx.x >> 1, h = blockIdx.y, b = blockIdx.z;
-  if (blockIdx.x & 1) quantize_tensor<MODE, BITS, 1>(a, sm, j, h, b);
-  else quantize_tensor<MODE, BITS, 0>(a, sm, j, h, b);
+  if (MODE == KVARN || a.k_out == 0) {
+    if (blockIdx.x & 1) quantize_tensor<MODE, BITS, 1, 0>(a, sm, j, h, b);
+    else quantize_tensor<MODE, BITS, 0, 0>(a, sm, j, h, b);
+  } else if constexpr (MODE != KVARN) {
+    if (a.k_out == 1) {
+      if (blockIdx.x & 1) quantize_tensor<MODE, BITS, 1, 1>(a, sm, j, h, b);
+      else quantize_tensor<MODE, BITS, 0, 1>(a, sm, j, h, b);
+    } else {
+      if (blockIdx.x & 1) quantize_tensor<MODE, BITS, 1, 2>(a, sm, j, h, b);
+      else quantize_tensor<MODE, BITS, 0, 2>(a, sm, j, h, b);
+    }
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void tail_kernel(TailArgs a) {
