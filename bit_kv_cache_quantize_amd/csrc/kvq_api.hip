@@ -377,14 +377,17 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
   if (L == 0) return fail(KVQ_ERR_STATE, "layer %d holds no tokens", layer);
   const int nblk = L / KVQ_BLOCK_TOKENS, tail_n = L % KVQ_BLOCK_TOKENS;
   const int units = cfg.batch * cfg.n_kv_heads;
+  const int group = cfg.n_q_heads / cfg.n_kv_heads;
+  const bool tab = kvq::tab_supported(cfg.mode, cfg.bits, group, cfg.pre_rope);
   int splits = 1, bps = 0;
   if (nblk > 0) {
     if (c->splits_override > 0) {
       splits = std::min(c->splits_override, nblk);
     } else {
-      // about two resident workgroups per CU (512 on 256 CUs), each streaming at least
-      // 8 blocks, so that per-workgroup set-up and the split merge stay small
-      const int target_wgs = 512;
+      // about two resident workgroups of four waves per CU (512 on 256 CUs; the table
+      // kernel's workgroups have two waves: 1024), each streaming at least 8 blocks, so
+      // that per-workgroup set-up and the split merge stay small
+      const int target_wgs = tab ? 1024 : 512;
       splits = (target_wgs + units - 1) / units;
       splits = std::min(splits, (nblk + 7) / 8);
       splits = std::max(1, std::min(splits, KVQ_MAX_SPLITS));
@@ -413,8 +416,6 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
   a.blocks_per_split = bps;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
   a.scale_log2 = scale * 1.4426950408889634f;
-  const int group = cfg.n_q_heads / cfg.n_kv_heads;
-  const bool tab = kvq::tab_supported(cfg.mode, cfg.bits, group, cfg.pre_rope);
   if (cfg.outliers_per_vec > 0) {
     // per-wave staging for the sparse fix-ups: the outlier segments (table kernel), plus
     // key S/M, value S/M of a half and a RoPE base row (VALU kernel)

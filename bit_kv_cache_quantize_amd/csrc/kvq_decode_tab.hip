@@ -25,10 +25,11 @@
 // Outliers replace the dense value: each CSR (keys) / CSC (values) entry adds
 // (fp16 value - dense value) times the entry's weight.
 //
-// Work decomposition: one workgroup = one split of one (sequence, kv head); waves 2p and
-// 2p+1 process the two halves of blocks blo + p, blo + p + 2, ... in lockstep (two
-// workgroup barriers per block pair: tables built, tables consumed), with the next
-// block's loads in flight during the current one.
+// Work decomposition: one workgroup of two waves = one split of one (sequence, kv head);
+// wave h takes the 64-token half h of every block of the split. Two barriers per block
+// (tables built, tables consumed) synchronize only these two waves. Each load of the next
+// block is issued as soon as the registers it refills are dead, so it is in flight during
+// the rest of the current block.
 #include "kvq_decode_common.h"
 
 namespace kvq {
@@ -49,31 +50,29 @@ struct TabDecoder {
   static constexpr int PS = PT + 2;
   static constexpr int KWD = R / 4;                   // dwords of a key row
 
-  // Loads of a block issued one block ahead (key side).
-  struct Buf {
-    uint32_t kw[KWD];     // key row of token j
-    float4 kst;           // table role: (scale_x, scale_y, offset_x, offset_y) of pair ib
-    float2 rb;            // table role: (cos, sin) of the block base angle for pair ib
+  // Loads of the next block, each issued as soon as the registers it refills are dead.
+  struct Meta {           // issued after the table build
+    float4 kst;           // (scale_x, scale_y, offset_x, offset_y) of pair ib
+    float2 rb;            // (cos, sin) of the block base angle for pair ib
+    uint4 ob;             // outlier segment chunk j (j = thread of the workgroup)
   };
-  static constexpr int NOB = 1;   // outlier staging chunks per wave-pair lane held in registers (2 KB)
-  // Value-side loads and the outlier segments of a block, issued at the end of the previous
-  // block (after that block's value work), i.e. before the next key prefetch: loads
-  // complete in order, so waiting for these never waits for the key prefetch.
-  struct VBuf {
+  struct Keys {           // issued after the scores
+    uint32_t kw[KWD];     // key row of token j
+  };
+  struct Vals {           // issued after the values
     uint32_t vw[KWD];     // value half-rows of channels 2*lane, 2*lane+1
     float2 tst;           // value (S, M) of token j
-    uint4 ob[NOB];        // outlier segment chunk j (j = lane of the wave pair)
   };
 
   struct Shared {
-    float2* tab;          // this wave pair's table [64][PS]
-    float2* qb;           // this wave pair's rotated query pairs [64] (al, be)
-    float2* kst;          // this wave pair's key (scale, offset) per channel [128]
+    float2* tab;          // the pair tables [64][PS]
+    float2* qb;           // rotated query pairs [64] (al, be)
+    float2* kst;          // key (scale, offset) per channel [128]
     const float2* vlut;   // value code pairs [PT]
     float* pS;            // this wave's p * S per token of the half [64]
     float* p;             // this wave's p per token [64]
     float* M;             // this wave's value offset M per token [64]
-    uint8_t* blob;        // this wave pair's outlier staging
+    uint8_t* blob;        // outlier staging
     const float* q;       // query (original domain, scale folded) [128]
     const float* trev;    // theta_i / (2 pi) [64]
     const float* cbk;     // key codebook [16] (NUQ)
@@ -82,13 +81,12 @@ struct TabDecoder {
 
   const DecodeArgs& a;
   const Shared S;
-  const int lane, w, par, pr, j, ib, hb;
+  const int lane, par, j, ib, hb;
   int ob_bytes, ob_chunks;
   float m_run, l_run, pm, acc0, acc1;
 
   __device__ TabDecoder(const DecodeArgs& args, const Shared& sh, int lane_, int w_)
-      : a(args), S(sh), lane(lane_), w(w_), par(w_ & 1), pr(w_ >> 1), j(64 * (w_ & 1) + lane_),
-        ib((64 * (w_ & 1) + lane_) >> 1), hb(lane_ & 1) {
+      : a(args), S(sh), lane(lane_), par(w_), j(64 * w_ + lane_), ib((64 * w_ + lane_) >> 1), hb(lane_ & 1) {
     m_run = -INFINITY;
     l_run = 0.f;
     pm = 0.f;
@@ -106,23 +104,22 @@ struct TabDecoder {
     return a.rec + ((size_t)(blockIdx.z * a.Hkv + blockIdx.y) * a.max_blocks + blk) * (size_t)a.lay.rec_bytes;
   }
 
-  __device__ __forceinline__ void fetch(Buf& B, int blk) const {
+  __device__ __forceinline__ void fetch_meta(Meta& Mt, int blk) const {
     const uint8_t* rec = record(blk);
-    load_row<R>(B.kw, rec + a.lay.kc + (size_t)j * R);
     const float2 s2 = reinterpret_cast<const float2*>(rec + a.lay.ks)[ib];          // RTN s / NUQ z
     const float2 m2 = reinterpret_cast<const float2*>(rec + a.lay.ks + 512)[ib];    // RTN m / NUQ h
-    if constexpr (MODE == NUQ) B.kst = make_float4(m2.x, m2.y, s2.x, s2.y);        // (h, h, z, z)
-    else B.kst = make_float4(s2.x, s2.y, m2.x, m2.y);                               // (s, s, m, m)
-    B.rb = reinterpret_cast<const float2*>(a.rope_base)[(size_t)blk * 64 + ib];
+    if constexpr (MODE == NUQ) Mt.kst = make_float4(m2.x, m2.y, s2.x, s2.y);       // (h, h, z, z)
+    else Mt.kst = make_float4(s2.x, s2.y, m2.x, m2.y);                              // (s, s, m, m)
+    Mt.rb = reinterpret_cast<const float2*>(a.rope_base)[(size_t)blk * 64 + ib];
+    if (a.k_out > 0) Mt.ob = reinterpret_cast<const uint4*>(rec + a.lay.ko_val)[min(j, ob_chunks - 1)];
   }
 
-  __device__ __forceinline__ void fetch_v(VBuf& V, int blk) const {
+  __device__ __forceinline__ void fetch_keys(Keys& K, int blk) const {
+    load_row<R>(K.kw, record(blk) + a.lay.kc + (size_t)j * R);
+  }
+
+  __device__ __forceinline__ void fetch_vals(Vals& V, int blk) const {
     const uint8_t* rec = record(blk);
-    if (a.k_out > 0) {
-      const uint4* src = reinterpret_cast<const uint4*>(rec + a.lay.ko_val);
-#pragma unroll
-      for (int k = 0; k < NOB; ++k) V.ob[k] = src[min(j + 128 * k, ob_chunks - 1)];
-    }
     load_row<R>(V.vw, rec + a.lay.vc + (size_t)par * (128 * RH) + (size_t)lane * R);
     if constexpr (MODE == NUQ) {
       V.tst.x = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + j];   // h
@@ -140,7 +137,7 @@ struct TabDecoder {
 
   // Entries hb*PT/2 .. hb*PT/2 + PT/2 - 1 of pair ib's table (the other lane of the pair
   // writes the rest), the pair's rotated query and its channel statistics.
-  __device__ __forceinline__ void build(const Buf& B) const {
+  __device__ __forceinline__ void build(const Meta& B) const {
     const float qx = S.q[2 * ib], qy = S.q[2 * ib + 1];
     const float al = fmaf(qx, B.rb.x, qy * B.rb.y);
     const float be = fmaf(qy, B.rb.x, -qx * B.rb.y);
@@ -215,24 +212,20 @@ struct TabDecoder {
     return p;
   }
 
-  // Outlier segments of block blk into the wave pair's LDS staging (before the barrier that
-  // precedes their use): the chunks held in V, the rest (large k) loaded here.
-  __device__ __forceinline__ void stage_blob(const VBuf& V, int blk) const {
+  // Outlier segments of block blk into the LDS staging (before the barrier that precedes
+  // their use): the chunk held in registers, the rest (many outliers per vector) loaded here.
+  __device__ __forceinline__ void stage_blob(const Meta& Mt, int blk) const {
     uint4* dst = reinterpret_cast<uint4*>(S.blob);
-#pragma unroll
-    for (int k = 0; k < NOB; ++k)
-      if (j + 128 * k < ob_chunks) dst[j + 128 * k] = V.ob[k];
-    if (ob_chunks > 128 * NOB) {
+    if (j < ob_chunks) dst[j] = Mt.ob;
+    if (ob_chunks > 128) {
       const uint4* src = reinterpret_cast<const uint4*>(record(blk) + a.lay.ko_val);
-      for (int k = j + 128 * NOB; k < ob_chunks; k += 128) dst[k] = src[k];
+      for (int k = j + 128; k < ob_chunks; k += 128) dst[k] = src[k];
     }
   }
 
-  // One half block (parity par) of block blk: key loads in B, value loads in V (both issued
-  // a block ahead); the wave pair's table and outlier staging for blk are complete.
-  __device__ __forceinline__ void process(const Buf& B, const VBuf& V, int blk, const float (&rc)[64],
-                                          const float (&rs)[64]) {
-    const uint8_t* rec = record(blk);
+  // Score of token j over the whole row (table, rotated query, statistics and outlier
+  // staging of the block complete).
+  __device__ __forceinline__ float scores(const Keys& B, const float (&rc)[64], const float (&rs)[64]) const {
     const bool outl = a.k_out > 0;
 
     // ---- scores: two fma per channel pair on the tabulated (U, W). Software-pipelined in
@@ -281,8 +274,13 @@ struct TabDecoder {
         sc = fmaf(delta, coef, sc);
       }
     }
+    return sc;
+  }
 
-    const float p = softmax_step(sc);
+  // Values of this half (channels 2*lane, 2*lane+1) weighted by the probabilities of its
+  // tokens; p is this lane's (token j's) probability.
+  __device__ __forceinline__ void values(const Vals& V, float p) {
+    const bool outl = a.k_out > 0;
     pm = fmaf(p, V.tst.y, pm);                 // sum_t p_t M_t (code-independent part)
     S.pS[lane] = p * V.tst.x;
     S.p[lane] = p;
@@ -342,7 +340,6 @@ struct TabDecoder {
         }
       }
     }
-    wave_sync();   // the per-wave LDS areas are rewritten by the next half block
   }
 
   // Tokens 64*par .. 64*par+63 of the fp16 tail (position 128*nblk + j), waves 0 and 1.
@@ -388,28 +385,30 @@ struct TabDecoder {
   }
 };
 
+constexpr int kTabThreads = 128;
+
 template <int MODE, int BITS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_tab_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_tab_kernel(DecodeArgs a) {
   using Dec = TabDecoder<MODE, BITS>;
   constexpr int PT = Dec::PT;
   extern __shared__ __align__(16) uint8_t s_dyn[];
-  __shared__ __align__(16) float2 s_tab[2][64 * Dec::PS];
+  __shared__ __align__(16) float2 s_tab[64 * Dec::PS];
   __shared__ __align__(16) float2 s_vlut[PT];
-  __shared__ __align__(16) float2 s_qb[2][64];
-  __shared__ __align__(16) float2 s_kst[2][128];
+  __shared__ __align__(16) float2 s_qb[64];
+  __shared__ __align__(16) float2 s_kst[128];
   __shared__ __align__(16) float s_q[128];
   __shared__ float s_trev[64];
   __shared__ float s_cb[32];
-  __shared__ __align__(16) float s_pS[4][64];
-  __shared__ __align__(16) float s_p[4][64];
-  __shared__ __align__(16) float s_M[4][64];
-  __shared__ float s_m[4], s_l[4];
+  __shared__ __align__(16) float s_pS[2][64];
+  __shared__ __align__(16) float s_p[2][64];
+  __shared__ __align__(16) float s_M[2][64];
+  __shared__ float s_m[2], s_l[2];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  if (tid < 128) s_q[tid] = __half2float(a.q[((size_t)b * a.Hq + kvh) * 128 + tid]) * a.scale_log2;
+  s_q[tid] = __half2float(a.q[((size_t)b * a.Hq + kvh) * 128 + tid]) * a.scale_log2;
   if (tid < 64) s_trev[tid] = a.rope_off[128 * 64 * 2 + tid] * kInv2Pi;
   if (MODE == NUQ && tid < 32) s_cb[tid] = a.cb[(kvh * 2 + (tid >> 4)) * kCbStride + (tid & 15)];
   __syncthreads();
@@ -427,14 +426,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 
   typename Dec::Shared sh;
-  sh.tab = s_tab[w >> 1];
-  sh.qb = s_qb[w >> 1];
-  sh.kst = s_kst[w >> 1];
+  sh.tab = s_tab;
+  sh.qb = s_qb;
+  sh.kst = s_kst;
   sh.vlut = s_vlut;
   sh.pS = s_pS[w];
   sh.p = s_p[w];
   sh.M = s_M[w];
-  sh.blob = s_dyn + (size_t)(w >> 1) * a.wave_lds;
+  sh.blob = s_dyn;
   sh.q = s_q;
   sh.trev = s_trev;
   sh.cbk = s_cb;
@@ -448,39 +447,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int i = 0; i < 64; ++i) { const float2 v = off[i * 128]; rc[i] = v.x; rs[i] = v.y; }
   }
 
-  // ---- blocks of this split: wave pair pr takes blo + pr, blo + pr + 2, ...
   const int blo = split * a.blocks_per_split;
   const int bhi = min(a.nblk, blo + a.blocks_per_split);
-  const int n_iter = (bhi - blo + 1) >> 1;
-  // Two key-load buffers used alternately (a register copy between them would wait for
-  // the next block's loads at the end of every iteration); one value buffer, refilled for
-  // the next block right after its use.
-  typename Dec::Buf A, Bn;
-  typename Dec::VBuf V;
-  int blk = blo + d.pr;
-  if (blk < bhi) {
-    d.fetch(A, blk);
-    d.fetch_v(V, blk);
+  typename Dec::Meta Mt;
+  typename Dec::Keys Kc;
+  typename Dec::Vals V;
+  if (blo < bhi) {
+    d.fetch_meta(Mt, blo);
+    d.fetch_keys(Kc, blo);
+    d.fetch_vals(V, blo);
   }
   __syncthreads();   // the value table is complete
-  auto step = [&](typename Dec::Buf& cur, typename Dec::Buf& nxt, int bk) {
-    const bool valid = bk < bhi;
-    if (valid && a.k_out > 0) d.stage_blob(V, bk);
-    if (bk + 2 < bhi) d.fetch(nxt, bk + 2);
-    if (valid) d.build(cur);
-    __syncthreads();
-    if (valid) d.process(cur, V, bk, rc, rs);
-    if (bk + 2 < bhi) d.fetch_v(V, bk + 2);
-    __syncthreads();
-  };
-  for (int it = 0; it < n_iter; it += 2, blk += 4) {
-    step(A, Bn, blk);
-    if (it + 1 < n_iter) step(Bn, A, blk + 2);
+  for (int blk = blo; blk < bhi; ++blk) {
+    const bool more = blk + 1 < bhi;
+    if (a.k_out > 0) d.stage_blob(Mt, blk);
+    d.build(Mt);
+    if (more) d.fetch_meta(Mt, blk + 1);
+    __syncthreads();   // tables, rotated query, statistics and outlier staging complete
+    const float sc = d.scores(Kc, rc, rs);
+    if (more) d.fetch_keys(Kc, blk + 1);
+    const float p = d.softmax_step(sc);
+    d.values(V, p);
+    if (more) d.fetch_vals(V, blk + 1);
+    __syncthreads();   // every read of the tables and of the staging done
   }
 
-  // ---- the fp16 tail (waves 0 and 1; it belongs to the last split)
+  // ---- the fp16 tail (it belongs to the last split)
   if (split == a.splits - 1 && a.tail_n > 0) {
-    float2* qt = s_qb[0];
+    float2* qt = s_qb;
     if (tid < 64) {
       // query rotated back by the tail block's base angle
       const float2 rb = reinterpret_cast<const float2*>(a.rope_base)[(size_t)a.nblk * 64 + tid];
@@ -488,11 +482,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       qt[tid] = make_float2(fmaf(qx, rb.x, qy * rb.y), fmaf(qy, rb.x, -qx * rb.y));
     }
     __syncthreads();
-    if (w < 2 && 64 * d.par < a.tail_n) d.tail_half(qt);
+    if (64 * d.par < a.tail_n) d.tail_half(qt);
   }
 
-  // ---- merge the four wave states
-  float* s_o = reinterpret_cast<float*>(&s_tab[0][0]);   // [4][128], the tables are no longer read
+  // ---- merge the two wave states
+  float* s_o = reinterpret_cast<float*>(&s_tab[0]);   // [2][128], the tables are no longer read
   __syncthreads();
   {
     const float l = wave_sum(d.l_run);
@@ -502,12 +496,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     s_o[w * 128 + 2 * lane + 1] = d.acc1 + pmw;
   }
   __syncthreads();
-  if (tid < 128) {
+  {
     const int c = tid;
-    const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    const float M = fmaxf(s_m[0], s_m[1]);
     float o = 0.f, L = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < 2; ++ww) {
       if (s_m[ww] == -INFINITY) continue;
       const float sw = exp2f(s_m[ww] - M);
       o = fmaf(sw, s_o[ww * 128 + c], o);
@@ -526,8 +520,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
 template <int MODE, int BITS>
 hipError_t launch_t(const DecodeArgs& a, int batch, hipStream_t s) {
-  hipLaunchKernelGGL((decode_tab_kernel<MODE, BITS>), dim3(a.splits, a.Hkv, batch), dim3(kThreads),
-                     (size_t)2 * a.wave_lds, s, a);   // outlier staging per wave pair
+  hipLaunchKernelGGL((decode_tab_kernel<MODE, BITS>), dim3(a.splits, a.Hkv, batch), dim3(kTabThreads),
+                     (size_t)a.wave_lds, s, a);   // outlier staging
   return hipGetLastError();
 }
 
