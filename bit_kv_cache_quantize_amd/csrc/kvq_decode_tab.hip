@@ -39,6 +39,8 @@ using namespace dec;
 
 constexpr float kInv2Pi = 0.15915494309189535f;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <int MODE, int BITS>
 struct TabDecoder {
   static constexpr int R = 16 * BITS;                 // key row bytes
@@ -54,7 +56,7 @@ struct TabDecoder {
   struct Meta {           // issued after the table build
     float4 kst;           // (scale_x, scale_y, offset_x, offset_y) of pair ib
     float2 rb;            // (cos, sin) of the block base angle for pair ib
-    uint4 ob;             // outlier segment chunk j (j = thread of the workgroup)
+    u32x4 ob;             // outlier segment chunk j (j = thread of the workgroup)
   };
   struct Keys {           // issued after the scores
     uint32_t kw[KWD];     // key row of token j
@@ -111,7 +113,11 @@ struct TabDecoder {
     if constexpr (MODE == NUQ) Mt.kst = make_float4(m2.x, m2.y, s2.x, s2.y);       // (h, h, z, z)
     else Mt.kst = make_float4(s2.x, s2.y, m2.x, m2.y);                              // (s, s, m, m)
     Mt.rb = reinterpret_cast<const float2*>(a.rope_base)[(size_t)blk * 64 + ib];
-    if (a.k_out > 0) Mt.ob = reinterpret_cast<const uint4*>(rec + a.lay.ko_val)[min(j, ob_chunks - 1)];
+    // Without outliers the load reads a fixed cached address instead (no branch around the
+    // load: a branch makes the memory-counter waits after it conservative).
+    const u32x4* obp = a.k_out > 0 ? reinterpret_cast<const u32x4*>(rec + a.lay.ko_val) + min(j, ob_chunks - 1)
+                                   : reinterpret_cast<const u32x4*>(a.rope_base);
+    Mt.ob = *obp;
   }
 
   __device__ __forceinline__ void fetch_keys(Keys& K, int blk) const {
@@ -215,10 +221,10 @@ struct TabDecoder {
   // Outlier segments of block blk into the LDS staging (before the barrier that precedes
   // their use): the chunk held in registers, the rest (many outliers per vector) loaded here.
   __device__ __forceinline__ void stage_blob(const Meta& Mt, int blk) const {
-    uint4* dst = reinterpret_cast<uint4*>(S.blob);
-    if (j < ob_chunks) dst[j] = Mt.ob;
+    u32x4* dst = reinterpret_cast<u32x4*>(S.blob);
+    dst[min(j, ob_chunks - 1)] = Mt.ob;   // lanes past the end rewrite the last chunk (same value)
     if (ob_chunks > 128) {
-      const uint4* src = reinterpret_cast<const uint4*>(record(blk) + a.lay.ko_val);
+      const u32x4* src = reinterpret_cast<const u32x4*>(record(blk) + a.lay.ko_val);
       for (int k = j + 128; k < ob_chunks; k += 128) dst[k] = src[k];
     }
   }
@@ -289,7 +295,7 @@ struct TabDecoder {
 
     // ---- P.V over the 64 tokens of this half, channels 2*lane and 2*lane+1
     // (pipelined like the scores: reads of chunk c+1 before the fma of chunk c)
-    constexpr int CV = 4;
+    constexpr int CV = 2;
     float o0 = 0.f, o1 = 0.f;
     float2 vb[2][CV][3];
     auto vread = [&](int c, float2 (&dst)[CV][3]) {
@@ -446,6 +452,10 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
     for (int i = 0; i < 64; ++i) { const float2 v = off[i * 128]; rc[i] = v.x; rs[i] = v.y; }
   }
+  // Wait for the angle loads here: the main loop then starts with only the block loads in
+  // flight, the same state as at the end of every iteration, so that the memory-counter
+  // waits inside the loop count exactly those loads.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   const int blo = split * a.blocks_per_split;
   const int bhi = min(a.nblk, blo + a.blocks_per_split);
@@ -459,16 +469,18 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   }
   __syncthreads();   // the value table is complete
   for (int blk = blo; blk < bhi; ++blk) {
-    const bool more = blk + 1 < bhi;
+    // the loads of the next block are unconditional (the last block reloads itself), so
+    // that no branch makes the memory-counter waits conservative
+    const int nxt = min(blk + 1, bhi - 1);
     if (a.k_out > 0) d.stage_blob(Mt, blk);
     d.build(Mt);
-    if (more) d.fetch_meta(Mt, blk + 1);
+    d.fetch_meta(Mt, nxt);
     __syncthreads();   // tables, rotated query, statistics and outlier staging complete
     const float sc = d.scores(Kc, rc, rs);
-    if (more) d.fetch_keys(Kc, blk + 1);
+    d.fetch_keys(Kc, nxt);
     const float p = d.softmax_step(sc);
     d.values(V, p);
-    if (more) d.fetch_vals(V, blk + 1);
+    d.fetch_vals(V, nxt);
     __syncthreads();   // every read of the tables and of the staging done
   }
 
