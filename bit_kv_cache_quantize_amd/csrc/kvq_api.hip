@@ -420,7 +420,8 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
     // per-wave staging for the sparse fix-ups: the outlier segments (table kernel), plus
     // key S/M, value S/M of a half and a RoPE base row (VALU kernel)
     const uint32_t blob = c->lay.vo_idx + 128u * cfg.outliers_per_vec - c->lay.ko_val;
-    a.wave_lds = (int)(((blob + 15u) & ~15u) + (tab ? 0u : 1024u + 512u + 512u));
+    // (table kernel: the staging, then its value-outlier entry list, 6 bytes per entry)
+    a.wave_lds = (int)(((blob + 15u) & ~15u) + (tab ? 768u * cfg.outliers_per_vec : 1024u + 512u + 512u));
   }
   if (tab)
     st = hip_check(kvq::launch_decode_tab(cfg.mode, cfg.bits, a, cfg.batch, s), "launch decode");

@@ -40,6 +40,9 @@ using namespace dec;
 constexpr float kInv2Pi = 0.15915494309189535f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int MODE, int BITS>
 struct TabDecoder {
@@ -51,6 +54,9 @@ struct TabDecoder {
   // the same banks. The lookups keep their immediate offsets (no extra instruction).
   static constexpr int PS = PT + 2;
   static constexpr int KWD = R / 4;                   // dwords of a key row
+  // 2-bit RTN values go through the matrix cores (codes are small integers, exact in
+  // fp16); NUQ codebook values and 3-bit codes use the LDS table of code pairs.
+  static constexpr bool MV = MODE == RTN && BITS == 2;
 
   // Loads of the next block, each issued as soon as the registers it refills are dead.
   struct Meta {           // issued after the table build
@@ -62,14 +68,14 @@ struct TabDecoder {
     uint32_t kw[KWD];     // key row of token j
   };
   struct Vals {           // issued after the values
-    uint32_t vw[KWD];     // value half-rows of channels 2*lane, 2*lane+1
+    uint32_t vw[KWD];     // value half-rows of channels ch0, ch1
     float2 tst;           // value (S, M) of token j
   };
 
   struct Shared {
     float2* tab;          // the pair tables [64][PS]
     float2* qb;           // rotated query pairs [64] (al, be)
-    float2* kst;          // key (scale, offset) per channel [128]
+    float* kd0;           // dense key value of code 0 per channel [128] (outlier corrections)
     const float2* vlut;   // value code pairs [PT]
     float* pS;            // this wave's p * S per token of the half [64]
     float* p;             // this wave's p per token [64]
@@ -79,6 +85,14 @@ struct TabDecoder {
     const float* trev;    // theta_i / (2 pi) [64]
     const float* cbk;     // key codebook [16] (NUQ)
     const float* cbv;     // value codebook [16] (NUQ)
+    _Float16* wt;         // matrix-core values: this wave's weights p*S as fp16 high and low
+                          // parts in operand order [2][16 steps][4 slots]
+    const _Float16* zero; // 64 zero fp16 (operand rows 2 and 3)
+    float* kcorr;         // key outlier corrections of the block's scores [128]
+    float* vcorr;         // this wave's value outlier corrections per channel [128]
+    float2* vst;          // value (S, M) per token of the block [128]
+    uint16_t* vent;       // value outlier entries: token | channel << 8 [128 k]
+    float* vdelta;        // value outlier entries: fp16 value - dense value [128 k]
   };
 
   const DecodeArgs& a;
@@ -86,10 +100,17 @@ struct TabDecoder {
   const int lane, par, j, ib, hb;
   int ob_bytes, ob_chunks;
   float m_run, l_run, pm, acc0, acc1;
+  f4 dacc[2];             // matrix-core accumulators of the two channel groups
+  float tps;              // sum of the weights fed to the matrix cores (this token)
 
   __device__ TabDecoder(const DecodeArgs& args, const Shared& sh, int lane_, int w_)
       : a(args), S(sh), lane(lane_), par(w_), j(64 * w_ + lane_), ib((64 * w_ + lane_) >> 1), hb(lane_ & 1) {
     m_run = -INFINITY;
+    if constexpr (MV) {
+      dacc[0] = f4{0.f, 0.f, 0.f, 0.f};
+      dacc[1] = f4{0.f, 0.f, 0.f, 0.f};
+      tps = 0.f;
+    }
     l_run = 0.f;
     pm = 0.f;
     acc0 = 0.f;
@@ -101,6 +122,11 @@ struct TabDecoder {
       ob_chunks = (ob_bytes + 15) / 16;
     }
   }
+
+  // The two value channels of this lane: pairs (2*lane, 2*lane+1) for the table path; for
+  // the matrix-core path the lane's column in each of the two 64-channel groups.
+  __device__ __forceinline__ int ch0() const { return MV ? lane : 2 * lane; }
+  __device__ __forceinline__ int ch1() const { return MV ? 64 + lane : 2 * lane + 1; }
 
   __device__ __forceinline__ const uint8_t* record(int blk) const {
     return a.rec + ((size_t)(blockIdx.z * a.Hkv + blockIdx.y) * a.max_blocks + blk) * (size_t)a.lay.rec_bytes;
@@ -126,7 +152,12 @@ struct TabDecoder {
 
   __device__ __forceinline__ void fetch_vals(Vals& V, int blk) const {
     const uint8_t* rec = record(blk);
-    load_row<R>(V.vw, rec + a.lay.vc + (size_t)par * (128 * RH) + (size_t)lane * R);
+    if constexpr (MV) {
+      load_row<RH>(V.vw, rec + a.lay.vc + (size_t)(par * 128 + ch0()) * RH);
+      load_row<RH>(V.vw + KWD / 2, rec + a.lay.vc + (size_t)(par * 128 + ch1()) * RH);
+    } else {
+      load_row<R>(V.vw, rec + a.lay.vc + (size_t)par * (128 * RH) + (size_t)lane * R);
+    }
     if constexpr (MODE == NUQ) {
       V.tst.x = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + j];   // h
       V.tst.y = reinterpret_cast<const float*>(rec + a.lay.vs)[j];         // z
@@ -148,7 +179,7 @@ struct TabDecoder {
     const float al = fmaf(qx, B.rb.x, qy * B.rb.y);
     const float be = fmaf(qy, B.rb.x, -qx * B.rb.y);
     if (hb == 0) S.qb[ib] = make_float2(al, be);
-    S.kst[2 * ib + hb] = hb ? make_float2(B.kst.y, B.kst.w) : make_float2(B.kst.x, B.kst.z);
+    if (a.k_out > 0) S.kd0[2 * ib + hb] = hb ? fmaf(kcode(1, 0u), B.kst.y, B.kst.w) : fmaf(kcode(0, 0u), B.kst.x, B.kst.z);
     constexpr int NA = 1 << BITS;          // codes of the x channel
     constexpr int NB = BITS == 3 ? 4 : 2;  // codes of the y channel covered by this lane
     float Ax[NA], Bx[NA], Ay[NB], By[NB];
@@ -215,6 +246,11 @@ struct TabDecoder {
     pm *= alpha;
     acc0 *= alpha;
     acc1 *= alpha;
+    if constexpr (MV) {
+      dacc[0] *= alpha;
+      dacc[1] *= alpha;
+      tps *= alpha;
+    }
     return p;
   }
 
@@ -232,7 +268,6 @@ struct TabDecoder {
   // Score of token j over the whole row (table, rotated query, statistics and outlier
   // staging of the block complete).
   __device__ __forceinline__ float scores(const Keys& B, const float (&rc)[64], const float (&rs)[64]) const {
-    const bool outl = a.k_out > 0;
 
     // ---- scores: two fma per channel pair on the tabulated (U, W). Software-pipelined in
     // chunks of CH pairs: the table reads of chunk c+1 are issued before the fma of chunk c
@@ -262,88 +297,152 @@ struct TabDecoder {
     }
     float sc = sc0 + sc1;
 
-    // ---- key outliers of row j (CSR): the fp16 value replaces the dense one
-    if (outl) {
-      const uint16_t* ptr = reinterpret_cast<const uint16_t*>(S.blob + (a.lay.ko_ptr - a.lay.ko_val));
-      const uint8_t* idx = S.blob + (a.lay.ko_idx - a.lay.ko_val);
-      const __half* val = reinterpret_cast<const __half*>(S.blob);
-      const int e1 = ptr[j + 1];
-      for (int e = ptr[j]; e < e1; ++e) {
-        const int c = idx[e], i = c >> 1;
-        const float2 st = S.kst[c];
-        const float dense = fmaf(kcode(c & 1, code_sel<BITS, 128>(B.kw, c)), st.x, st.y);
-        const float delta = __half2float(val[e]) - dense;
-        const float ang = (float)j * S.trev[i];
-        const float cj = __builtin_amdgcn_cosf(ang), sj = __builtin_amdgcn_sinf(ang);
-        const float2 q2 = S.qb[i];
-        const float coef = (c & 1) ? fmaf(cj, q2.y, -sj * q2.x) : fmaf(cj, q2.x, sj * q2.y);
-        sc = fmaf(delta, coef, sc);
-      }
+    // key outliers: corrections gathered per token before the scores
+    if (a.k_out > 0) {
+      sc += S.kcorr[j];
+      S.kcorr[j] = 0.f;   // cleared for the next block (its corrections follow a barrier)
     }
     return sc;
   }
 
-  // Values of this half (channels 2*lane, 2*lane+1) weighted by the probabilities of its
+  // Values of this half (channels ch0, ch1) weighted by the probabilities of its
   // tokens; p is this lane's (token j's) probability.
   __device__ __forceinline__ void values(const Vals& V, float p) {
-    const bool outl = a.k_out > 0;
     pm = fmaf(p, V.tst.y, pm);                 // sum_t p_t M_t (code-independent part)
-    S.pS[lane] = p * V.tst.x;
+    const float ps = p * V.tst.x;
+    S.pS[lane] = ps;
     S.p[lane] = p;
     S.M[lane] = V.tst.y;
-    wave_sync();
-
-    // ---- P.V over the 64 tokens of this half, channels 2*lane and 2*lane+1
-    // (pipelined like the scores: reads of chunk c+1 before the fma of chunk c)
-    constexpr int CV = 2;
-    float o0 = 0.f, o1 = 0.f;
-    float2 vb[2][CV][3];
-    auto vread = [&](int c, float2 (&dst)[CV][3]) {
-#pragma unroll
-      for (int k = 0; k < CV; ++k) {
-        const int pp = c * CV + k;
-        const int t = half_row_token(2 * pp);   // positions 2pp, 2pp+1 hold tokens t, t+1
-        dst[k][0] = *reinterpret_cast<const float2*>(S.pS + t);
-        dst[k][1] = S.vlut[pair_index(V.vw, pp, 64)];
-        dst[k][2] = S.vlut[pair_index(V.vw + KWD / 2, pp, 64)];
-      }
-    };
-    vread(0, vb[0]);
-#pragma unroll
-    for (int c = 0; c < 32 / CV; ++c) {
-      if (c + 1 < 32 / CV) vread(c + 1, vb[(c + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int k = 0; k < CV; ++k) {
-        const float2 ps = vb[c & 1][k][0], v0 = vb[c & 1][k][1], v1 = vb[c & 1][k][2];
-        o0 = fmaf(ps.x, v0.x, fmaf(ps.y, v0.y, o0));
-        o1 = fmaf(ps.x, v1.x, fmaf(ps.y, v1.y, o1));
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MV) {
+      // the weight as fp16 high and low parts, at the operand slot of token j's position
+      const _Float16 hi = (_Float16)ps;
+      const _Float16 lo = (_Float16)(ps - (float)hi);
+      tps += (float)hi + (float)lo;
+      const int pos = half_row_token(lane);   // the position map is its own inverse
+      S.wt[mv_slot(pos)] = hi;
+      S.wt[64 + mv_slot(pos)] = lo;
     }
-    acc0 += o0;
-    acc1 += o1;
-
-    // ---- value outliers of channels 2*lane, 2*lane+1 (CSC) that fall in this half
-    if (outl) {
-      const uint16_t* ptr = reinterpret_cast<const uint16_t*>(S.blob + (a.lay.vo_ptr - a.lay.ko_val));
-      const uint8_t* idx = S.blob + (a.lay.vo_idx - a.lay.ko_val);
-      const __half* val = reinterpret_cast<const __half*>(S.blob + (a.lay.vo_val - a.lay.ko_val));
+    wave_sync();
+    if constexpr (MV) {
+      // Values on the matrix cores (4x4x4 blocks): block b, column i = channel 64 g + 4 b + i;
+      // operand rows 0 and 1 = the weights' high and low fp16 parts, rows 2 and 3 zero; 16
+      // steps of 4 positions cover the half-row. D = sum w (1 + code / 4), so the code sum
+      // is 4 (D - sum w), taken at the end.
+      const int i = lane & 3;
+      const _Float16* arow = i == 0 ? S.wt : (i == 1 ? S.wt + 64 : S.zero);
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int c = 2 * lane + k;
-        const int e1 = ptr[c + 1];
-        for (int e = ptr[c]; e < e1; ++e) {
-          const int t = idx[e] - 64 * par;
-          if (t < 0 || t >= 64) continue;
-          const uint32_t code = code_sel<BITS, 64>(V.vw + k * (KWD / 2), half_row_token(t));
-          const float vc = MODE == NUQ ? S.cbv[code] : (float)code;
-          // p_t (val - (vc S_t + M_t)) with p_t S_t, p_t and M_t from LDS
-          const float pt = S.p[t];
-          const float corr = fmaf(pt, __half2float(val[e]) - S.M[t], -S.pS[t] * vc);
-          if (k == 0) acc0 += corr;
-          else acc1 += corr;
+      for (int st = 0; st < 16; ++st) {
+        const h4 A = *reinterpret_cast<const h4*>(arow + 4 * st);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const uint32_t d = V.vw[4 * g + (st >> 2)];
+          const int m = 2 * (st & 3);
+          const h4 B = __builtin_bit_cast(h4, u32x2{code_pair_f16(d, m), code_pair_f16(d, m + 1)});
+          dacc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, B, dacc[g], 0, 0, 0);
         }
+      }
+    } else {
+      // ---- P.V over the 64 tokens of this half, channels 2*lane and 2*lane+1
+      // (pipelined like the scores: reads of chunk c+1 before the fma of chunk c)
+      constexpr int CV = 2;
+      float o0 = 0.f, o1 = 0.f;
+      float2 vb[2][CV][3];
+      auto vread = [&](int c, float2 (&dst)[CV][3]) {
+#pragma unroll
+        for (int k = 0; k < CV; ++k) {
+          const int pp = c * CV + k;
+          const int t = half_row_token(2 * pp);   // positions 2pp, 2pp+1 hold tokens t, t+1
+          dst[k][0] = *reinterpret_cast<const float2*>(S.pS + t);
+          dst[k][1] = S.vlut[pair_index(V.vw, pp, 64)];
+          dst[k][2] = S.vlut[pair_index(V.vw + KWD / 2, pp, 64)];
+        }
+      };
+      vread(0, vb[0]);
+#pragma unroll
+      for (int c = 0; c < 32 / CV; ++c) {
+        if (c + 1 < 32 / CV) vread(c + 1, vb[(c + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < CV; ++k) {
+          const float2 ps = vb[c & 1][k][0], v0 = vb[c & 1][k][1], v1 = vb[c & 1][k][2];
+          o0 = fmaf(ps.x, v0.x, fmaf(ps.y, v0.y, o0));
+          o1 = fmaf(ps.x, v1.x, fmaf(ps.y, v1.y, o1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      acc0 += o0;
+      acc1 += o1;
+    }
+    // ---- value outliers: each entry whose token is in this half adds p_t (val - dense) to
+    // its channel (scattered through LDS), then each lane takes its two channels
+    if (a.k_out > 0) {
+      const int nv = 128 * a.k_out;
+      for (int e = lane; e < nv; e += 64) {
+        const uint32_t tc = S.vent[e];   // token | channel << 8
+        const int t = (int)(tc & 255u) - 64 * par;
+        if (t >= 0 && t < 64) atomicAdd(&S.vcorr[tc >> 8], S.p[t] * S.vdelta[e]);
+      }
+      wave_sync();
+      acc0 += S.vcorr[ch0()];
+      acc1 += S.vcorr[ch1()];
+      S.vcorr[ch0()] = 0.f;
+      S.vcorr[ch1()] = 0.f;
+    }
+  }
+
+  // Operand slot (4 * step + k) of half-row position pos in the matrix-core value product:
+  // step s takes positions 16q + m + {0, 8, 1, 9} (q = s / 4, m = 2 (s % 4)), the order in
+  // which two conversions of one code dword produce them.
+  static __device__ __forceinline__ int mv_slot(int pos) {
+    return 16 * (pos >> 4) + 4 * ((pos & 7) >> 1) + 2 * (pos & 1) + ((pos >> 3) & 1);
+  }
+
+  // Positions m and m + 8 of a 16-code dword as two fp16 values 1 + code / 4 (exact).
+  static __device__ __forceinline__ uint32_t code_pair_f16(uint32_t d, int m) {
+    const uint32_t x = 2 * m >= 8 ? (d >> (2 * m - 8)) : (d << (8 - 2 * m));
+    return (x & 0x03000300u) | 0x3C003C00u;
+  }
+
+  // Largest r in 0..127 with ptr[r] <= e (ptr non-decreasing, ptr[128] > e): the row of CSR
+  // entry e (binary search, 7 dependent reads).
+  static __device__ __forceinline__ int segment_of(const uint16_t* ptr, int e) {
+    int r = 0;
+#pragma unroll
+    for (int st = 64; st >= 1; st >>= 1) r = ptr[r + st] <= e ? r + st : r;
+    return r;
+  }
+
+  // Outlier corrections of the block, one entry per lane (the workgroup's 128 lanes): key
+  // entries add (val - dense) times the rotated query coefficient to their token's score;
+  // value entries are listed with their token, channel and (val - dense) for the value
+  // phase. The dense value of an outlier position is that of code 0 (the stored code).
+  __device__ __forceinline__ void outlier_prep(int tid) const {
+    const uint8_t* blob = S.blob;
+    const int n = 128 * a.k_out;
+    {
+      const uint16_t* ptr = reinterpret_cast<const uint16_t*>(blob + (a.lay.ko_ptr - a.lay.ko_val));
+      const uint8_t* idx = blob + (a.lay.ko_idx - a.lay.ko_val);
+      const __half* val = reinterpret_cast<const __half*>(blob);
+      for (int e = tid; e < n; e += 128) {
+        const int t = segment_of(ptr, e), c = idx[e], i = c >> 1;
+        const float delta = __half2float(val[e]) - S.kd0[c];
+        const float ang = (float)t * S.trev[i];
+        const float cj = __builtin_amdgcn_cosf(ang), sj = __builtin_amdgcn_sinf(ang);
+        const float2 q2 = S.qb[i];
+        const float coef = (c & 1) ? fmaf(cj, q2.y, -sj * q2.x) : fmaf(cj, q2.x, sj * q2.y);
+        atomicAdd(&S.kcorr[t], delta * coef);
+      }
+    }
+    {
+      const uint16_t* ptr = reinterpret_cast<const uint16_t*>(blob + (a.lay.vo_ptr - a.lay.ko_val));
+      const uint8_t* idx = blob + (a.lay.vo_idx - a.lay.ko_val);
+      const __half* val = reinterpret_cast<const __half*>(blob + (a.lay.vo_val - a.lay.ko_val));
+      const float v0 = MODE == NUQ ? S.cbv[0] : 0.f;
+      for (int e = tid; e < n; e += 128) {
+        const int c = segment_of(ptr, e), t = idx[e];
+        const float2 st = S.vst[t];
+        S.vent[e] = (uint16_t)(t | (c << 8));
+        S.vdelta[e] = __half2float(val[e]) - fmaf(v0, st.x, st.y);
       }
     }
   }
@@ -378,12 +477,21 @@ struct TabDecoder {
     S.p[lane] = p;
     wave_sync();
     float o0 = 0.f, o1 = 0.f;
-    const __half2* vcol = reinterpret_cast<const __half2*>(tv + (size_t)(64 * par) * kD) + lane;
-    for (int t = 0; t < n_valid; ++t) {
-      const float2 vv = __half22float2(vcol[(size_t)t * (kD / 2)]);
-      const float pv = S.p[t];
-      o0 = fmaf(pv, vv.x, o0);
-      o1 = fmaf(pv, vv.y, o1);
+    if constexpr (MV) {
+      const __half* vrow = tv + (size_t)(64 * par) * kD;
+      for (int t = 0; t < n_valid; ++t) {
+        const float pv = S.p[t];
+        o0 = fmaf(pv, __half2float(vrow[(size_t)t * kD + ch0()]), o0);
+        o1 = fmaf(pv, __half2float(vrow[(size_t)t * kD + ch1()]), o1);
+      }
+    } else {
+      const __half2* vcol = reinterpret_cast<const __half2*>(tv + (size_t)(64 * par) * kD) + lane;
+      for (int t = 0; t < n_valid; ++t) {
+        const float2 vv = __half22float2(vcol[(size_t)t * (kD / 2)]);
+        const float pv = S.p[t];
+        o0 = fmaf(pv, vv.x, o0);
+        o1 = fmaf(pv, vv.y, o1);
+      }
     }
     acc0 += o0;
     acc1 += o1;
@@ -401,13 +509,19 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   __shared__ __align__(16) float2 s_tab[64 * Dec::PS];
   __shared__ __align__(16) float2 s_vlut[PT];
   __shared__ __align__(16) float2 s_qb[64];
-  __shared__ __align__(16) float2 s_kst[128];
+  __shared__ __align__(16) float s_kd0[128];
   __shared__ __align__(16) float s_q[128];
   __shared__ float s_trev[64];
   __shared__ float s_cb[32];
-  __shared__ __align__(16) float s_pS[2][64];
-  __shared__ __align__(16) float s_p[2][64];
+  // [wave][p * S, p][token]; before the scores the same memory holds the block's value
+  // statistics per token (read by the outlier corrections, which end before the values)
+  __shared__ __align__(16) float s_pps[2][2][64];
   __shared__ __align__(16) float s_M[2][64];
+  __shared__ __align__(16) _Float16 s_wt[Dec::MV ? 2 : 1][Dec::MV ? 128 : 8];
+  __shared__ __align__(16) _Float16 s_zero[Dec::MV ? 64 : 8];
+  __shared__ __align__(16) float s_kcorr[128];
+  __shared__ __align__(16) float s_vcorr[2][128];
+  float2* s_vst = reinterpret_cast<float2*>(&s_pps[0][0][0]);
   __shared__ float s_m[2], s_l[2];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -417,6 +531,10 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   s_q[tid] = __half2float(a.q[((size_t)b * a.Hq + kvh) * 128 + tid]) * a.scale_log2;
   if (tid < 64) s_trev[tid] = a.rope_off[128 * 64 * 2 + tid] * kInv2Pi;
   if (MODE == NUQ && tid < 32) s_cb[tid] = a.cb[(kvh * 2 + (tid >> 4)) * kCbStride + (tid & 15)];
+  if (Dec::MV && tid < 64) s_zero[tid] = (_Float16)0.f;
+  s_kcorr[tid] = 0.f;
+  s_vcorr[0][tid] = 0.f;
+  s_vcorr[1][tid] = 0.f;
   __syncthreads();
   if (tid < PT) {
     // code values of two adjacent value tokens, in the same index order as the key tables
@@ -434,16 +552,25 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   typename Dec::Shared sh;
   sh.tab = s_tab;
   sh.qb = s_qb;
-  sh.kst = s_kst;
+  sh.kd0 = s_kd0;
   sh.vlut = s_vlut;
-  sh.pS = s_pS[w];
-  sh.p = s_p[w];
+  sh.pS = s_pps[w][0];
+  sh.p = s_pps[w][1];
   sh.M = s_M[w];
   sh.blob = s_dyn;
   sh.q = s_q;
   sh.trev = s_trev;
   sh.cbk = s_cb;
   sh.cbv = s_cb + 16;
+  sh.wt = s_wt[Dec::MV ? w : 0];
+  sh.zero = s_zero;
+  sh.kcorr = s_kcorr;
+  sh.vcorr = s_vcorr[w];
+  sh.vst = s_vst;
+  // after the outlier staging: the value entries (token | channel << 8, then the deltas)
+  const uint32_t blob_bytes = a.k_out > 0 ? (a.lay.vo_idx + 128u * a.k_out - a.lay.ko_val + 15u) & ~15u : 0u;
+  sh.vdelta = reinterpret_cast<float*>(s_dyn + blob_bytes);
+  sh.vent = reinterpret_cast<uint16_t*>(s_dyn + blob_bytes + 512u * a.k_out);
   Dec d(a, sh, lane, w);
 
   float rc[64], rs[64];
@@ -472,10 +599,17 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
     // the loads of the next block are unconditional (the last block reloads itself), so
     // that no branch makes the memory-counter waits conservative
     const int nxt = min(blk + 1, bhi - 1);
-    if (a.k_out > 0) d.stage_blob(Mt, blk);
+    if (a.k_out > 0) {
+      d.stage_blob(Mt, blk);
+      s_vst[tid] = V.tst;
+    }
     d.build(Mt);
     d.fetch_meta(Mt, nxt);
     __syncthreads();   // tables, rotated query, statistics and outlier staging complete
+    if (a.k_out > 0) {
+      d.outlier_prep(tid);
+      __syncthreads();   // outlier corrections complete
+    }
     const float sc = d.scores(Kc, rc, rs);
     d.fetch_keys(Kc, nxt);
     const float p = d.softmax_step(sc);
@@ -504,8 +638,14 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
     const float l = wave_sum(d.l_run);
     const float pmw = wave_sum(d.pm);
     if (lane == 0) { s_m[w] = d.m_run; s_l[w] = l; }
-    s_o[w * 128 + 2 * lane] = d.acc0 + pmw;
-    s_o[w * 128 + 2 * lane + 1] = d.acc1 + pmw;
+    float o0 = d.acc0 + pmw, o1 = d.acc1 + pmw;
+    if constexpr (Dec::MV) {
+      const float T = wave_sum(d.tps);
+      o0 += 4.f * ((d.dacc[0][0] + d.dacc[0][1]) - T);
+      o1 += 4.f * ((d.dacc[1][0] + d.dacc[1][1]) - T);
+    }
+    s_o[w * 128 + d.ch0()] = o0;
+    s_o[w * 128 + d.ch1()] = o1;
   }
   __syncthreads();
   {

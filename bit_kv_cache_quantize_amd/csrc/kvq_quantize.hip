@@ -444,6 +444,16 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
     else if constexpr (KO == 1) return per_chan ? d1[e] == 4 * i : d1[i] == e;
     else return (om[i >> 2] >> (8 * (i & 3) + e)) & 1u;
   };
+  if constexpr (KO > 0) {
+    // Outlier positions become NaN in the tile: minimum and maximum skip a NaN, so the
+    // statistics are those of the non-outliers, and the code of a NaN comes out as 0 (the
+    // code stored at an outlier position; its fp16 value replaces it at decode).
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        X.v[i][h] |= (is_out(i, 2 * h) ? 0x7fffu : 0u) | (is_out(i, 2 * h + 1) ? 0x7fff0000u : 0u);
+  }
 
   // ---- statistics over the non-outliers
   if constexpr (MODE != KVARN) opaque(X.v);   // widen again where used (keeps 32, not 64, tile registers)
@@ -455,11 +465,10 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       lo[e] = INFINITY;
       hi[e] = MODE == SYM ? 0.f : -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {   // branch-free: an outlier enters as the neutral value
-        const bool o = is_out(i, e);
+      for (int i = 0; i < 8; ++i) {   // an outlier is a NaN here: skipped
         const float x = X.f(i, e);
-        lo[e] = fminf(lo[e], o ? INFINITY : x);
-        hi[e] = MODE == SYM ? fmaxf(hi[e], o ? 0.f : fabsf(x)) : fmaxf(hi[e], o ? -INFINITY : x);
+        lo[e] = fminf(lo[e], x);
+        hi[e] = MODE == SYM ? fmaxf(hi[e], fabsf(x)) : fmaxf(hi[e], x);
       }
     }
     // both reductions share one barrier
@@ -489,11 +498,10 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
     for (int i = 0; i < 8; ++i) {
       float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool o = is_out(i, e);
+      for (int e = 0; e < 8; ++e) {   // an outlier is a NaN here: skipped
         const float x = X.f(i, e);
-        lo = fminf(lo, o ? INFINITY : x);
-        hi = fmaxf(hi, o ? -INFINITY : x);
+        lo = fminf(lo, x);
+        hi = fmaxf(hi, x);
       }
       lo = tok_reduce(lo, MinF());
       hi = tok_reduce(hi, MaxF());
@@ -530,7 +538,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
     }
   }
 
-  // ---- codes
+  // ---- codes (an outlier position, a NaN in the tile, gets code 0)
   if constexpr (MODE != KVARN) opaque(X.v);
   if constexpr (TENSOR == 0) {
     // key rows, token-major: this lane's 8 codes of row t_i go straight to memory

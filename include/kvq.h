@@ -170,7 +170,8 @@ kvq_status kvq_set_decode_splits(kvq_cache cache, int splits);
  *   outliers (outliers_per_vec = k > 0):
  *       key CSR by token:     f16 val[128k], u16 row_ptr[129], u8 channel[128k]
  *       value CSC by channel: f16 val[128k], u16 col_ptr[129], u8 token[128k]
- *       entries sorted by (row, column); val holds the original fp16 bits.
+ *       entries sorted by (row, column); val holds the original fp16 bits, and
+ *       the dense code at an outlier position is 0.
  * Code packing of n codes: 4-bit byte j = code 2j | code 2j+1 << 4; 2-bit byte j
  * = codes 4j..4j+3 at bits 2i; 3-bit = the low 2 bits of all n codes packed as
  * 2-bit (n/4 bytes) then bit 2 of code 8j+i at bit i of byte j (n/8 bytes).

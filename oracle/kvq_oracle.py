@@ -333,6 +333,13 @@ def quantize_block(k16: np.ndarray, v16: np.ndarray, cfg: Config,
         kstat, vstat = (kss,), (vss,)
     else:
         raise ValueError(mode)
+    if ko > 0:
+        # The notes zero the dense part at an outlier position ([KVQ] 3.4, Algorithm 1) and
+        # the fp16 value replaces it at decode, so the code stored there is never read for
+        # the result. Reading: it is stored as code 0 (a fixed value, so that a decoder can
+        # correct an outlier from the vector's statistics alone).
+        kc = np.where(kmask, np.uint8(0), kc).astype(kc.dtype)
+        vc = np.where(vmask, np.uint8(0), vc).astype(vc.dtype)
     blk = Block(kc, vc, kstat, vstat)
     if ko > 0:
         blk.kmask, blk.vmask = kmask, vmask
