@@ -50,14 +50,16 @@ struct Smem {
 };
 
 // Key of the top-k |x| selection: larger magnitude first, then lower element index e
-// (magnitude bits from bit 7 up, 127 - e in bits 0..6); a key gives back its element's
-// position within the vector.
+// (magnitude bits from bit 8 up, 127 - e in bits 1..7, the sign in bit 0, which never
+// decides since (magnitude, index) is unique); a key gives back its element's position
+// within the vector and, for fp16 tiles, the element's exact fp16 bits.
 __device__ __forceinline__ uint32_t mag_key(float x, int e) {
   // fp32 form (KVarN tiles, which never select outliers): magnitude bits above bit 13
   const uint32_t u = __float_as_uint(x);
-  return (((u & 0x7fffffffu) >> 13) << 7) | (uint32_t)(127 - e);
+  return (((u & 0x7fffffffu) >> 13) << 8) | ((uint32_t)(127 - e) << 1) | (u >> 31);
 }
-__device__ __forceinline__ uint32_t key_index(uint32_t key) { return 127u - (key & 127u); }
+__device__ __forceinline__ uint32_t key_index(uint32_t key) { return 127u - ((key >> 1) & 127u); }
+__device__ __forceinline__ uint16_t key_bits(uint32_t key) { return (uint16_t)(((key & 1u) << 15) | ((key >> 8) & 0x7fffu)); }
 
 // The block tile of one lane: 8 tokens x 8 channels. Non-KVarN modes keep the fp16
 // input bits (two channels per register) and widen on use, which halves the live
@@ -73,8 +75,8 @@ template <> struct Tile<false> {
   __device__ __forceinline__ uint32_t bits(int i, int e) const { return (e & 1) ? v[i][e >> 1] >> 16 : v[i][e >> 1] & 0xffffu; }
   __device__ __forceinline__ float f(int i, int e) const { return __half2float(__ushort_as_half((unsigned short)bits(i, e))); }
   __device__ __forceinline__ uint32_t key(int i, int e, int idx) const {
-    const uint32_t mag = (e & 1) ? __builtin_amdgcn_ubfe(v[i][e >> 1], 16, 15) : v[i][e >> 1] & 0x7fffu;
-    return (mag << 7) | (uint32_t)(127 - idx);
+    const uint32_t h = (e & 1) ? v[i][e >> 1] >> 16 : v[i][e >> 1] & 0xffffu;
+    return ((h & 0x7fffu) << 8) | ((uint32_t)(127 - idx) << 1) | (h >> 15);
   }
 };
 
@@ -638,12 +640,6 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
   if (KO != 0) {
     __syncthreads();                                   // okey complete, omask cleared
     const int n_ent = 128 * k_out;
-    const __half* in = (tensor ? a.v_in : a.k_in) + unit * (size_t)a.n_new * kD;
-    const __half* tl = a.tail + unit * (2 * kT * kD) + (size_t)tensor * kT * kD;
-    auto value_bits = [&](int t, int c) -> uint16_t {   // the element's fp16 input, exactly
-      const __half* src = (j == 0 && t < a.t0) ? tl + (size_t)t * kD : in + ((size_t)j * kT + t - a.t0) * kD;
-      return reinterpret_cast<const uint16_t*>(src)[c];
-    };
     auto place = [&](int n, int& row, int& col, uint32_t& key) {
       const int v = n & 127, p = n >> 7;
       key = sm.okey[v][p];
@@ -691,7 +687,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
         const int lim = col - 32 * d;   // bits of word d below col
         pos += lim >= 32 ? __popc(m) : (lim > 0 ? __popc(m & ((1u << lim) - 1u)) : 0);
       }
-      val[pos] = value_bits(tensor == 0 ? row : col, tensor == 0 ? col : row);
+      val[pos] = key_bits(key);   // the element's fp16 input bits, exactly
       idx[pos] = (uint8_t)col;
     }
   }
