@@ -68,6 +68,31 @@ float nuq_threshold(float lo, float hi) {
   return key2f(b);
 }
 
+// Code table of one codebook's decision thresholds tau[0..n): the kernel maps u in [-1, 1]
+// to bucket floor(RN(u * 512 + 512)) (one fma); RN can move u by at most 2^-23 up across a
+// bucket edge, never down, so every u that lands in bucket b lies in [B_b - 2^-23, B_b+1)
+// with B_b = -1 + b / 512. Entry b = (number of thresholds below B_b - 2^-22, the one
+// threshold in [B_b - 2^-22, B_b+1) or +inf); the code is then that count plus (u >= the
+// threshold). Two thresholds in one such range: entry 0 gets count -1 and the kernel counts.
+void nuq_code_table(const float* tau, int n, float2* lut) {
+  const double eps = std::ldexp(1.0, -22);
+  bool ok = true;
+  for (int b = 0; b <= kvq::kNuqBuckets; ++b) {
+    const double lo = -1.0 + (double)b / (kvq::kNuqBuckets / 2);
+    const double hi = b == kvq::kNuqBuckets ? 2.0 : -1.0 + (double)(b + 1) / (kvq::kNuqBuckets / 2);
+    int below = 0, inside = 0;
+    float t_in = INFINITY;
+    for (int t = 0; t < n; ++t) {
+      if ((double)tau[t] < lo - eps) ++below;
+      else if ((double)tau[t] < hi) { ++inside; t_in = tau[t]; }
+    }
+    if (inside > 1) ok = false;
+    lut[b] = make_float2((float)below, t_in);
+  }
+  for (int b = kvq::kNuqBuckets + 1; b < kvq::kNuqLutStride; ++b) lut[b] = make_float2(0.f, INFINITY);
+  if (!ok) lut[0].x = -1.f;
+}
+
 }  // namespace
 
 namespace kvq {
@@ -116,10 +141,11 @@ struct kvq_cache_s {
   int max_blocks = 0;
   size_t off_rec = 0, layer_rec_bytes = 0;
   size_t off_tail = 0, layer_tail_bytes = 0;
-  size_t off_cb = 0, off_rope_base = 0, off_rope_off = 0, off_work = 0;
+  size_t off_cb = 0, off_lut = 0, off_rope_base = 0, off_rope_off = 0, off_work = 0;
   std::vector<int32_t> len;
   std::vector<uint8_t> cb_loaded;   // [layer][kv_head][2]
-  std::vector<float> cb_host;       // [layer][kv_head][2][16]
+  std::vector<float> cb_host;       // [layer][kv_head][2][kCbStride]
+  std::vector<float2> lut_host;     // [layer][kv_head][2][kNuqLutStride]
   std::vector<float> rope_host;     // base table then offset table
   int splits_override = 0;
 };
@@ -128,8 +154,8 @@ namespace {
 
 struct Regions {
   int max_blocks;
-  size_t layer_rec, rec, layer_tail, tail, cb, rope_base, rope_off, work, total;
-  size_t off_rec, off_tail, off_cb, off_rope_base, off_rope_off, off_work;
+  size_t layer_rec, rec, layer_tail, tail, cb, lut, rope_base, rope_off, work, total;
+  size_t off_rec, off_tail, off_cb, off_lut, off_rope_base, off_rope_off, off_work;
 };
 
 kvq_status validate_config(const kvq_config* c) {
@@ -172,6 +198,7 @@ Regions regions(const kvq_config* c) {
   r.layer_tail = units * 2 * kvq::kT * kvq::kD * sizeof(__half);
   r.tail = r.layer_tail * c->n_layers;
   r.cb = c->mode == KVQ_MODE_NUQ ? (size_t)c->n_layers * c->n_kv_heads * 2 * kvq::kCbStride * sizeof(float) : 0;
+  r.lut = c->mode == KVQ_MODE_NUQ ? (size_t)c->n_layers * c->n_kv_heads * 2 * kvq::kNuqLutStride * sizeof(float2) : 0;
   r.rope_base = c->pre_rope ? (size_t)(r.max_blocks + 1) * 64 * 2 * sizeof(float) : 0;
   r.rope_off = c->pre_rope ? ((size_t)128 * 64 * 2 + 64) * sizeof(float) : 0;   // offsets, then theta_i
   r.work = (size_t)c->batch * c->n_q_heads * KVQ_MAX_SPLITS * kvq::kPartStride * sizeof(float);
@@ -180,6 +207,7 @@ Regions regions(const kvq_config* c) {
   r.off_rec = place(r.rec);
   r.off_tail = place(r.tail);
   r.off_cb = place(r.cb);
+  r.off_lut = place(r.lut);
   r.off_rope_base = place(r.rope_base);
   r.off_rope_off = place(r.rope_off);
   r.off_work = place(r.work);
@@ -233,12 +261,15 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_buf, size_t bytes, vo
   c->off_tail = r.off_tail;
   c->layer_tail_bytes = r.layer_tail;
   c->off_cb = r.off_cb;
+  c->off_lut = r.off_lut;
   c->off_rope_base = r.off_rope_base;
   c->off_rope_off = r.off_rope_off;
   c->off_work = r.off_work;
   c->len.assign(cfg->n_layers, 0);
   c->cb_loaded.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2, 0);
   c->cb_host.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2 * kvq::kCbStride, 0.f);
+  if (cfg->mode == KVQ_MODE_NUQ)
+    c->lut_host.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2 * kvq::kNuqLutStride, make_float2(0.f, 0.f));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (cfg->pre_rope) {
     // RoPE angles n * theta_i, theta_i = theta^(-2i/128), evaluated in double precision:
@@ -301,6 +332,12 @@ kvq_status kvq_codebook_load(kvq_cache c, int layer, int kv_head, int which, con
                                 kvq::kCbStride * sizeof(float), hipMemcpyHostToDevice,
                                 static_cast<hipStream_t>(stream)), "upload codebook");
   if (st != KVQ_OK) return st;
+  float2* lut = c->lut_host.data() + slot * kvq::kNuqLutStride;
+  nuq_code_table(dst + 16, n_entries - 1, lut);
+  st = hip_check(hipMemcpyAsync(c->base + c->off_lut + slot * kvq::kNuqLutStride * sizeof(float2), lut,
+                                kvq::kNuqLutStride * sizeof(float2), hipMemcpyHostToDevice,
+                                static_cast<hipStream_t>(stream)), "upload codebook table");
+  if (st != KVQ_OK) return st;
   c->cb_loaded[slot] = 1;
   return ok();
 }
@@ -345,6 +382,7 @@ kvq_status kvq_quantize_append(kvq_cache c, int layer, const void* k_f16, const 
     a.rec = c->base + c->off_rec + (size_t)layer * c->layer_rec_bytes;
     a.tail = tail;
     a.cb = reinterpret_cast<const float*>(c->base + c->off_cb) + (size_t)layer * cfg.n_kv_heads * 2 * kvq::kCbStride;
+    a.nuq_lut = reinterpret_cast<const float2*>(c->base + c->off_lut) + (size_t)layer * cfg.n_kv_heads * 2 * kvq::kNuqLutStride;
     st = hip_check(kvq::launch_quantize(cfg.mode, cfg.bits, a, nb, cfg.batch, s), "launch quantize");
     if (st != KVQ_OK) return st;
   }

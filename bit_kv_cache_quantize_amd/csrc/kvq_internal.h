@@ -16,6 +16,12 @@ constexpr int kMaxSplits = 64;       // decode splits per (sequence, kv head)
 // Device codebook slot per (layer, kv head, K/V): entries C[0..15], then the NUQ decision
 // thresholds tau[0..14] (see kvq_api.hip).
 constexpr int kCbStride = 32;
+// NUQ code table: u in [-1, 1] falls in bucket floor((u + 1) * 512) of 1024 (1024: u = 1);
+// an entry holds (number of decision thresholds below every u that can land in the bucket,
+// the one threshold that may still split it, or +inf). Entry 0 with count -1: the codebook
+// has two thresholds too close for the table and the kernel counts thresholds instead.
+constexpr int kNuqBuckets = 1024;
+constexpr int kNuqLutStride = 1032;   // entries per (layer, kv head, K/V) slot (1025 used)
 
 enum Mode { RTN = 0, NUQ = 1, KVARN = 2, SYM = 3 };
 
@@ -39,6 +45,7 @@ struct QuantArgs {
   uint8_t* rec;          // records of the layer, [B][Hkv][max_blocks]
   const __half* tail;    // tails of the layer, [B][Hkv][2][128][128]
   const float* cb;       // codebooks of the layer, [Hkv][2][kCbStride]
+  const float2* nuq_lut; // NUQ code tables of the layer, [Hkv][2][kNuqLutStride] (NUQ only)
 };
 
 struct TailArgs {

@@ -47,6 +47,7 @@ struct Smem {
   uint32_t omask[kD][4];          // outlier bitmask per storage row
   uint32_t okey[kD][kMaxOut];     // selection keys of each vector's outliers
   uint16_t optr[kD + 1];          // storage row pointers
+  float2 nlut[kNuqLutStride];     // NUQ code table of this (kv head, tensor)
 };
 
 // Key of the top-k |x| selection: larger magnitude first, then lower element index e
@@ -282,13 +283,18 @@ __device__ __forceinline__ VecStats stats_of(float lo, float hi, float amax) {
 // Code of one element: RTN/KVarN clamp(rint((x - m) / s)), NUQ argmin over the codebook of
 // clamp((x - z) / h, -1, 1), symmetric int4 clamp(rint(x / s), -8, 7) + 8; a zero divisor
 // gives code 0 (symmetric: 8).
-template <int MODE, int BITS>
-__device__ __forceinline__ uint32_t code_of(float x, const VecStats& v, const float* tau) {
+template <int MODE, int BITS, bool LUT = false>
+__device__ __forceinline__ uint32_t code_of(float x, const VecStats& v, const float* tau, const float2* lut = nullptr) {
   constexpr int QMAX = (1 << BITS) - 1;
   // both operands of every select are computed: the selects stay branch-free
   if constexpr (MODE == NUQ) {
     const float q = div_rn(__fsub_rn(x, v.sa), v.sb, v.rc);
     const float u = v.sb == 0.f ? 0.f : fminf(fmaxf(q, -1.f), 1.f);
+    if constexpr (LUT) {
+      // bucket of u (one fma, truncation of a value in [0, 1024]), then at most one compare
+      const float2 e = lut[(int)__fmaf_rn(u, 0.5f * kNuqBuckets, 0.5f * kNuqBuckets)];
+      return (uint32_t)e.x + (u >= e.y ? 1u : 0u);
+    }
     return nuq_search<BITS>(u, tau);
   } else if constexpr (MODE == SYM) {
     const float q = rintf(div_rn(x, v.sa, v.rc));
@@ -301,7 +307,7 @@ __device__ __forceinline__ uint32_t code_of(float x, const VecStats& v, const fl
 
 // One tensor (TENSOR 0: keys, 1: values) of block j of (sequence b, kv head h). KO: outliers
 // per vector, 0 (none), 1 (one), 2 (two or more: a.k_out).
-template <int MODE, int BITS, int TENSOR, int KO>
+template <int MODE, int BITS, int TENSOR, int KO, bool LUT>
 __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, int j, int h, int b) {
   constexpr int tensor = TENSOR;
   const int tid = threadIdx.x, lane = tid & 63, r = lane >> 4, g = lane & 15;
@@ -347,6 +353,10 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
   if constexpr (MODE == NUQ) {
 #pragma unroll
     for (int c = 0; c < 16; ++c) tau[c] = a.cb[(h * 2 + tensor) * kCbStride + 16 + c];
+  }
+  if constexpr (LUT) {   // the code table into LDS (read after the statistics' barriers)
+    const float2* src = a.nuq_lut + (size_t)(h * 2 + tensor) * kNuqLutStride;
+    for (int k = tid; k <= kNuqBuckets; k += kThreads) sm.nlut[k] = src[k];
   }
 
   // ---- KVarN: rotate, normalise, divide by s1
@@ -550,7 +560,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       const int t = 32 * w + 4 * i + r;
       uint32_t c[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = code_of<MODE, BITS>(X.f(i, e), vs[e], tau);
+      for (int e = 0; e < 8; ++e) c[e] = code_of<MODE, BITS, LUT>(X.f(i, e), vs[e], tau, sm.nlut);
       uint8_t* row = kc + (size_t)t * R;
       if constexpr (BITS == 4) {
         uint32_t v = 0;
@@ -581,7 +591,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       uint32_t c[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        c[e] = code_of<MODE, BITS>(X.f(i, e), per_chan ? vs[e] : vs[i], tau);
+        c[e] = code_of<MODE, BITS, LUT>(X.f(i, e), per_chan ? vs[e] : vs[i], tau, sm.nlut);
       *reinterpret_cast<uint2*>(&sm.vq[t * kD + 8 * g]) =
           make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
     }
@@ -693,20 +703,33 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
   }
 }
 
+// NUQ with 3 or 4 bits codes through the table of its codebook when the table is usable
+// (entry 0's count is -1 otherwise, and the thresholds are counted).
+template <int MODE, int BITS, int TENSOR, int KO>
+__device__ __forceinline__ void run_tensor(const QuantArgs& a, Smem& sm, int j, int h, int b) {
+  if constexpr (MODE == NUQ && BITS >= 3) {
+    if (a.nuq_lut[(size_t)(h * 2 + TENSOR) * kNuqLutStride].x >= 0.f) {
+      quantize_tensor<MODE, BITS, TENSOR, KO, true>(a, sm, j, h, b);
+      return;
+    }
+  }
+  quantize_tensor<MODE, BITS, TENSOR, KO, false>(a, sm, j, h, b);
+}
+
 template <int MODE, int BITS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MODE == KVARN ? 2 : 4))) void quantize_kernel(QuantArgs a) {
   __shared__ Smem sm;
   const int j = blockIdx.x >> 1, h = blockIdx.y, b = blockIdx.z;
   if (MODE == KVARN || a.k_out == 0) {
-    if (blockIdx.x & 1) quantize_tensor<MODE, BITS, 1, 0>(a, sm, j, h, b);
-    else quantize_tensor<MODE, BITS, 0, 0>(a, sm, j, h, b);
+    if (blockIdx.x & 1) run_tensor<MODE, BITS, 1, 0>(a, sm, j, h, b);
+    else run_tensor<MODE, BITS, 0, 0>(a, sm, j, h, b);
   } else if constexpr (MODE != KVARN) {
     if (a.k_out == 1) {
-      if (blockIdx.x & 1) quantize_tensor<MODE, BITS, 1, 1>(a, sm, j, h, b);
-      else quantize_tensor<MODE, BITS, 0, 1>(a, sm, j, h, b);
+      if (blockIdx.x & 1) run_tensor<MODE, BITS, 1, 1>(a, sm, j, h, b);
+      else run_tensor<MODE, BITS, 0, 1>(a, sm, j, h, b);
     } else {
-      if (blockIdx.x & 1) quantize_tensor<MODE, BITS, 1, 2>(a, sm, j, h, b);
-      else quantize_tensor<MODE, BITS, 0, 2>(a, sm, j, h, b);
+      if (blockIdx.x & 1) run_tensor<MODE, BITS, 1, 2>(a, sm, j, h, b);
+      else run_tensor<MODE, BITS, 0, 2>(a, sm, j, h, b);
     }
   }
 }

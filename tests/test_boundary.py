@@ -61,6 +61,7 @@ def test_cache_bytes_matches_oracle_record_layout(mode, bits, k_out, pre_rope):
     total = a(rec * units * nblk * c.n_layers) + a(units * 65536 * c.n_layers)
     if mode == K.KVQ_MODE_NUQ:
         total += a(c.n_layers * c.n_kv_heads * 2 * 32 * 4)   # entries, then decision thresholds
+        total += a(c.n_layers * c.n_kv_heads * 2 * 1032 * 8)   # code tables over the thresholds
     if pre_rope:
         total += a((nblk + 1) * 512) + a(128 * 512 + 256)
     total += a(c.batch * c.n_q_heads * K.KVQ_MAX_SPLITS * 130 * 4)
