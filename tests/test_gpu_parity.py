@@ -218,10 +218,22 @@ def _fp16_sweep():
     return np.concatenate([pos, neg]).view(np.float16)
 
 
+def _crowded_codebook(bits):
+    """Ascending entries with three of them 2^-19 apart: two decision thresholds share one
+    bucket of the device's code table, which then falls back to counting thresholds."""
+    n = 1 << bits
+    c = list(np.linspace(-1.0, 1.0, n - 2))
+    mid = c[(len(c) - 1) // 2]
+    c = sorted(c + [mid + 2.0 ** -19, mid + 2.0 ** -18])
+    return np.asarray(c, np.float32)
+
+
+@pytest.mark.parametrize("crowded", [False, True])
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_nuq_codes_exhaustive_fp16(K, bits):
+def test_nuq_codes_exhaustive_fp16(K, bits, crowded):
     """NUQ argmin over every fp16 value of [-1, 1] against the oracle's brute force
-    (KVQuant notes 1.2 / 3.3; the device decides through host-derived thresholds).
+    (KVQuant notes 1.2 / 3.3; the device decides through host-derived thresholds, for 3 and
+    4 bits through a bucket table of them unless two share a bucket: `crowded`).
 
     Keys: tokens 0 and 1 of each block hold -1 and +1 in every channel, so every key
     channel has z = 0, h = 1 and u = x. Values: channels 0 and 1 of each token hold -1
@@ -245,7 +257,8 @@ def test_nuq_codes_exhaustive_fp16(K, bits):
     cache = K.KVCache(H.lib_cfg(wl, L))
     oc = O.OracleCache(H.oracle_cfg(wl, L))
     uniform = (-1.0 + 2.0 * np.arange(1 << bits) / ((1 << bits) - 1)).astype(np.float32)
-    for w, cb in ((0, synth.gen_codebook(wl, 0, 0, 0, bits)), (1, uniform)):
+    first = _crowded_codebook(bits) if crowded else synth.gen_codebook(wl, 0, 0, 0, bits)
+    for w, cb in ((0, first), (1, uniform)):
         cache.codebook_load(0, 0, w, cb)
         oc.load_codebook(0, 0, w, cb)
     cache.append(0, torch.from_numpy(k[None, None]).cuda(), torch.from_numpy(v[None, None]).cuda())
