@@ -10,16 +10,21 @@
 // Per wave and 64-token half block (the same split / wave / prefetch structure
 // as the VALU kernel):
 //   * scores S^T = K_codes (64 tokens x 128 channels) . Q' (128 x 16): the
-//     codes enter the matrix core as exact fp16 integers; Q' = q * s_c per block
-//     (the per-channel key scale) rounded to fp16, heads padded to 16 columns;
-//     the zero point enters as a per-head bias sum_c q_c m_c.
+//     codes enter the matrix core as exact fp16 integers (one bit-field select
+//     into the exponent of 1024 and one packed fma per code pair); Q' = q * s_c
+//     per block (the per-channel key scale) as an fp16 high part in columns
+//     0..7 and the low part (the rounding error, rounded) in columns 8..15, so
+//     one product covers both and a row move adds them; the zero point enters as
+//     a per-head bias sum_c q_c m_c.
 //   * P.V as O = V_codes^T (128 channels x 64 tokens) . P' (64 x 16): P' is the
 //     probability times the per-token value scale, taken straight from the
 //     score registers (the value half-rows store tokens in the order that makes
-//     this possible); per-channel scales (KVarN s1, int4 scales) multiply the
-//     per-block product before it is accumulated.
-//   * the online softmax runs per head on the 16 scores each lane holds; the
-//     fp16 tail is handled by the VALU half-block decoder.
+//     this possible), split into the same high / low columns; per-channel
+//     scales (KVarN s1, int4 scales) multiply the per-block product before it
+//     is accumulated; the two columns of a head are added once at the end.
+//   * the online softmax runs per head on the 16 scores each lane holds (the
+//     accumulators are rescaled only when some running maximum moved); the fp16
+//     tail is handled by the VALU half-block decoder.
 #include "kvq_decode_common.h"
 
 namespace kvq {
@@ -44,11 +49,21 @@ __device__ __forceinline__ h8 make8(uint32_t a, uint32_t b, uint32_t c, uint32_t
   return __builtin_bit_cast(h8, v);
 }
 
-// A pair (1024 + c0, 1024 + c1) built with the 0x6400 exponent trick, minus (1024 + OFF):
-// the exact small integers c - OFF as fp16.
-template <int OFF>
+// (x & mask) | 0x64006400 in one v_bfi_b32 (the exponent bits of 1024 lie outside every mask
+// used here); written out because the compiler otherwise emits an and and an or.
+__device__ __forceinline__ uint32_t with_exp(uint32_t x, uint32_t mask) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(x), "s"(0x64006400u));
+  return r;
+}
+
+// A pair (1024 + K*c0, 1024 + K*c1) from with_exp (K = 1, 4, 16 or 64: a code field at bit
+// 0, 2, 4 or 6 of each 16-bit half), mapped to the exact small integers c - OFF by one fma:
+// (1024 + K*c) / K is exact in fp16 and so is the fused subtraction.
+template <int K, int OFF>
 __device__ __forceinline__ uint32_t fix(uint32_t magic_pair) {
-  const h2 d = __builtin_bit_cast(h2, magic_pair) - h2{(_Float16)(1024 + OFF), (_Float16)(1024 + OFF)};
+  constexpr _Float16 inv = (_Float16)(1.0f / K), off = (_Float16)(-(1024 / K + OFF));
+  const h2 d = __builtin_elementwise_fma(__builtin_bit_cast(h2, magic_pair), h2{inv, inv}, h2{off, off});
   return __builtin_bit_cast(uint32_t, d);
 }
 
@@ -58,17 +73,18 @@ __device__ __forceinline__ uint32_t fix(uint32_t magic_pair) {
 __host__ __device__ constexpr int slot4(int i) { return (i & 1) ? (i >> 1) + 4 : (i >> 1); }
 __host__ __device__ constexpr int slot2(int h, int i) { return (i & 1) ? (i >> 1) + 4 * h + 8 : (i >> 1) + 4 * h; }
 
-// Eight codes of operand k-step ks, as fp16 integers minus OFF.
+// Eight codes of operand k-step ks, as fp16 integers minus OFF. The code fields of the low
+// byte of each 16-bit half are masked in place; one shift by 8 brings the high bytes down.
 template <int BITS, int OFF>
 __device__ __forceinline__ h8 codes8(const uint32_t* w, int ks) {
   if constexpr (BITS == 4) {
-    const uint32_t x = w[ks];
-    return make8(fix<OFF>((x & 0x000F000Fu) | 0x64006400u), fix<OFF>(((x >> 4) & 0x000F000Fu) | 0x64006400u),
-                 fix<OFF>(((x >> 8) & 0x000F000Fu) | 0x64006400u), fix<OFF>(((x >> 12) & 0x000F000Fu) | 0x64006400u));
+    const uint32_t x = w[ks], y = x >> 8;
+    return make8(fix<1, OFF>(with_exp(x, 0x000F000Fu)), fix<16, OFF>(with_exp(x, 0x00F000F0u)),
+                 fix<1, OFF>(with_exp(y, 0x000F000Fu)), fix<16, OFF>(with_exp(y, 0x00F000F0u)));
   } else {
-    const uint32_t x = w[ks >> 1] >> (8 * (ks & 1));
-    return make8(fix<OFF>((x & 0x00030003u) | 0x64006400u), fix<OFF>(((x >> 2) & 0x00030003u) | 0x64006400u),
-                 fix<OFF>(((x >> 4) & 0x00030003u) | 0x64006400u), fix<OFF>(((x >> 6) & 0x00030003u) | 0x64006400u));
+    const uint32_t x = (ks & 1) ? w[ks >> 1] >> 8 : w[ks >> 1];
+    return make8(fix<1, OFF>(with_exp(x, 0x00030003u)), fix<4, OFF>(with_exp(x, 0x000C000Cu)),
+                 fix<16, OFF>(with_exp(x, 0x00300030u)), fix<64, OFF>(with_exp(x, 0x00C000C0u)));
   }
 }
 
@@ -83,8 +99,12 @@ __host__ __device__ constexpr int vpos(int ks, int i) {
   return BITS == 4 ? 8 * ks + slot4(i) : slot2(ks, i);
 }
 
+// Matrix-core column n (0..15) of both products: n < 8 carries the fp16 high part of head n,
+// n >= 8 the low part (the fp32 operand minus its fp16 rounding, rounded) of head n - 8, so
+// one product gives both parts and the row move "row_ror:8" (lane n <-> n ^ 8) adds them.
 template <int MODE, int BITS, int G>
 struct MfmaDecoder {
+  static_assert(G <= 8, "the high and low parts of the heads share the 16 columns");
   static constexpr int R = 16 * BITS;        // bytes per 128 codes
   static constexpr int RH = R / 2;           // bytes per 64 codes
   static constexpr int KW = R / 16;          // dwords of a lane's 32-channel key chunk
@@ -93,6 +113,7 @@ struct MfmaDecoder {
   static constexpr int OFFV = MODE == SYM ? 8 : (1 << (BITS - 1));   // value codes: c - OFFV (centred)
   static constexpr int META = MODE == SYM ? 512 : (MODE == KVARN ? 3072 : 2048);   // ks, vs (, k1, v1) bytes
   static constexpr int NMETA = (META + 1023) / 1024;                              // 16-byte chunks per lane
+  static constexpr int QF16 = MODE == SYM;   // query and key scales are fp16: operand by packed fp16 math
 
   struct Buf {
     uint32_t kw[4][KW];       // key chunks of tokens 16*tt + n, channels 32*q .. 32*q+31
@@ -102,16 +123,28 @@ struct MfmaDecoder {
 
   const DecodeArgs& a;
   const int lane, w, par, n, q;
+  const uint32_t lo_mask;     // all ones on the low-part columns (n >= 8)
   uint8_t* meta;              // this wave's LDS copy of the block statistics
-  float qv[32];               // query of head n (0 for padding heads), channels 32*q .. 32*q+31
-  f4 acc[8];                  // O[16*ct + 4*q + e][head n]
-  float m_run, l_run, pm;     // head n (l_run, pm: this lane's share)
+  uint32_t qh[QF16 ? 16 : 1]; // fp16 query pairs of head n & 7 in operand slot order (0 if n & 7 >= G)
+  float qv[QF16 ? 1 : 32];    // fp32 query of head n & 7, channels 32*q .. 32*q+31
+  f4 acc[8];                  // O[16*ct + 4*q + e][column n]
+  float m_run, l_run, pm;     // head n & 7 (l_run, pm: this lane's share)
 
   __device__ MfmaDecoder(const DecodeArgs& args, int lane_, int w_, const float* qs, uint8_t* meta_)
-      : a(args), lane(lane_), w(w_), par(w_ & 1), n(lane_ & 15), q(lane_ >> 4), meta(meta_) {
-    const float* qrow = qs + (n < G ? n : 0) * 128 + 32 * q;
+      : a(args), lane(lane_), w(w_), par(w_ & 1), n(lane_ & 15), q(lane_ >> 4),
+        lo_mask((lane_ & 8) ? 0xFFFFFFFFu : 0u), meta(meta_) {
+    const int h = n & 7;
+    const float* qrow = qs + (h < G ? h : 0) * 128 + 32 * q;
+    if constexpr (QF16) {
 #pragma unroll
-    for (int c = 0; c < 32; ++c) qv[c] = n < G ? qrow[c] : 0.f;
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          qh[4 * ks + s] = h < G ? pack2(qrow[kchan<BITS>(ks, 2 * s)], qrow[kchan<BITS>(ks, 2 * s + 1)]) : 0u;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) qv[c] = h < G ? qrow[c] : 0.f;
+    }
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
     m_run = -INFINITY;
@@ -158,15 +191,30 @@ struct MfmaDecoder {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
+  // fp32 x -> the fp16 part of this lane's column: x rounded (high columns) or x minus that
+  // rounding, rounded (low columns); two values per call.
+  __device__ __forceinline__ uint32_t part2(float xa, float xb) const {
+    const uint32_t hi = pack2(xa, xb) & lo_mask;
+    const h2 c = __builtin_bit_cast(h2, hi);
+    return pack2(xa - (float)c[0], xb - (float)c[1]);
+  }
+
   __device__ __forceinline__ void process(const Buf& B) {
-    // ---- stage the block statistics: [ks | vs | k1 | v1] as in the record
+    // ---- stage the block statistics: [ks | vs | k1 | v1] as in the record; fp16 key
+    // scales (lanes 0..15, channels 8*lane .. 8*lane+7) go in the slot-pair order (c, c+4)
 #pragma unroll
-    for (int k = 0; k < NMETA; ++k)
-      if (lane + 64 * k < META / 16) reinterpret_cast<uint4*>(meta)[lane + 64 * k] = B.meta[k];
+    for (int k = 0; k < NMETA; ++k) {
+      uint4 m = B.meta[k];
+      if constexpr (QF16) {
+        if (k == 0 && lane < 16)
+          m = uint4{(m.x & 0xFFFFu) | (m.z << 16), (m.x >> 16) | (m.z & 0xFFFF0000u),
+                    (m.y & 0xFFFFu) | (m.w << 16), (m.y >> 16) | (m.w & 0xFFFF0000u)};
+      }
+      if (lane + 64 * k < META / 16) reinterpret_cast<uint4*>(meta)[lane + 64 * k] = m;
+    }
     wave_sync();
-    const float* kS = reinterpret_cast<const float*>(meta);                 // RTN / KVarN
+    const float* kS = reinterpret_cast<const float*>(meta);                 // RTN / KVARN
     const float* kM = kS + 128;
-    const __half* kS16 = reinterpret_cast<const __half*>(meta);             // SYM
     const uint8_t* vbase = meta + (MODE == SYM ? 256 : 1024);
     const float* vS = reinterpret_cast<const float*>(vbase);
     const float* vM = vS + 128;
@@ -174,58 +222,66 @@ struct MfmaDecoder {
     const float* k1 = reinterpret_cast<const float*>(meta + 2048);
     const float* v1 = k1 + 128;
 
-    // ---- Q' = q * s_c for head n over this lane's channels, in operand slot order, as an
-    // fp16 pair hi + lo (hi = Q' rounded, lo = the rounding error rounded); bias sum_c q_c m_c
-    uint32_t qh[4][4], ql[4][4];
+    // ---- Q' = q * s_c for this lane's column and channels, in operand slot order; bias
+    // sum_c q_c m_c
+    uint32_t qo[4][4];
     float bias = 0.f;
-    {
+    if constexpr (QF16) {
+      // fp16 q times fp16 s: the high part is the product rounded once, the low part the
+      // fused q*s - high rounded once
+      const uint4* sp = reinterpret_cast<const uint4*>(meta) + 4 * q;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 s4 = sp[ks];
+        const uint32_t sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const h2 qq = __builtin_bit_cast(h2, qh[4 * ks + s]), ss = __builtin_bit_cast(h2, sv[s]);
+          const h2 c = __builtin_bit_cast(h2, __builtin_bit_cast(uint32_t, qq * ss) & lo_mask);
+          qo[ks][s] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qq, ss, -c));
+        }
+      }
+    } else {
       const int c0 = 32 * q;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int ca = kchan<BITS>(ks, 2 * s), cb = kchan<BITS>(ks, 2 * s + 1);
-          float sa, sb;
-          if constexpr (MODE == SYM) {
-            sa = __half2float(kS16[c0 + ca]);
-            sb = __half2float(kS16[c0 + cb]);
-          } else {
-            sa = kS[c0 + ca];
-            sb = kS[c0 + cb];
-          }
-          const float xa = qv[ca] * sa, xb = qv[cb] * sb;
-          const _Float16 ha = (_Float16)xa, hb = (_Float16)xb;
-          qh[ks][s] = __builtin_bit_cast(uint32_t, h2{ha, hb});
-          ql[ks][s] = pack2(xa - (float)ha, xb - (float)hb);
-          if constexpr (MODE != SYM) bias = fmaf(qv[ca], kM[c0 + ca], fmaf(qv[cb], kM[c0 + cb], bias));
+          qo[ks][s] = part2(qv[ca] * kS[c0 + ca], qv[cb] * kS[c0 + cb]);
+          bias = fmaf(qv[ca], kM[c0 + ca], fmaf(qv[cb], kM[c0 + cb], bias));
         }
-      if constexpr (MODE != SYM) {
-        bias += __shfl_xor(bias, 16);
-        bias += __shfl_xor(bias, 32);
-      }
+      bias += __shfl_xor(bias, 16);
+      bias += __shfl_xor(bias, 32);
     }
+    const h8 qb[4] = {make8(qo[0][0], qo[0][1], qo[0][2], qo[0][3]), make8(qo[1][0], qo[1][1], qo[1][2], qo[1][3]),
+                      make8(qo[2][0], qo[2][1], qo[2][2], qo[2][3]), make8(qo[3][0], qo[3][1], qo[3][2], qo[3][3])};
 
-    // ---- scores for tokens 16*tt + 4*q + e, head n (log2 domain)
+    // ---- raw scores for tokens 16*tt + 4*q + e, head n & 7 (KVarN: already in the log2
+    // domain; otherwise the log2 scale is applied inside the exponent)
+    constexpr bool PRESCALED = MODE == KVARN;
     float sc[4][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       f4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const h8 av = codes8<BITS, OFFK>(B.kw[tt], ks);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, make8(qh[ks][0], qh[ks][1], qh[ks][2], qh[ks][3]), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, make8(ql[ks][0], ql[ks][1], ql[ks][2], ql[ks][3]), d, 0, 0, 0);
-      }
+      for (int ks = 0; ks < 4; ++ks) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<BITS, OFFK>(B.kw[tt], ks), qb[ks], d, 0, 0, 0);
       float s1[4] = {1.f, 1.f, 1.f, 1.f};
       if constexpr (MODE == KVARN) {
         const float4 t = *reinterpret_cast<const float4*>(k1 + 64 * par + 16 * tt + 4 * q);
         s1[0] = t.x; s1[1] = t.y; s1[2] = t.z; s1[3] = t.w;
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sc[tt][e] = (d[e] + bias) * s1[e] * a.scale_log2;
+      for (int e = 0; e < 4; ++e) {
+        const float full = d[e] + dpp_f<0x128>(d[e]);   // high + low column
+        if constexpr (MODE == KVARN) sc[tt][e] = (full + bias) * s1[e] * a.scale_log2;
+        else if constexpr (MODE == RTN) sc[tt][e] = full + bias;
+        else sc[tt][e] = full;
+      }
     }
 
-    // ---- online softmax for head n (16 scores per lane, 4 lanes per head)
+    // ---- online softmax for head n & 7 (16 scores per lane, 4 lanes per head and part)
+    const float sl = PRESCALED ? 1.f : a.scale_log2;
     float mx = sc[0][0];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
@@ -233,8 +289,8 @@ struct MfmaDecoder {
       for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[tt][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - mnew);
+    const float mnew = fmaxf(m_run, mx * sl);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
     m_run = mnew;
     // p' = p * S_t (value scale per token; 1 for int4). The value codes enter centred, so
     // the part of sum_t p_t v_t that does not depend on the code is sum_t p_t (M_t + OFFV * S_t).
@@ -250,15 +306,17 @@ struct MfmaDecoder {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float pe = exp2f(sc[tt][e] - mnew);
+        const float pe = __builtin_amdgcn_exp2f(fmaf(sc[tt][e], sl, -mnew));
         lsum += pe;
         if constexpr (MODE != SYM) msum = fmaf(pe, fmaf((float)OFFV, S_t[e], M_t[e]), msum);
-        p[tt][e] = pe * S_t[e];
+        p[tt][e] = MODE == SYM ? pe : pe * S_t[e];
       }
     }
     l_run = fmaf(l_run, alpha, lsum);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {   // the running maximum moved somewhere
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) acc[ct] *= alpha;
+      for (int ct = 0; ct < 8; ++ct) acc[ct] *= alpha;
+    }
     float g = 0.f;                     // KVarN: code-independent part, added before the channel s1
     if constexpr (MODE == RTN) {
       pm = fmaf(pm, alpha, msum);
@@ -266,50 +324,41 @@ struct MfmaDecoder {
       g = msum;
       g += __shfl_xor(g, 16);
       g += __shfl_xor(g, 32);
+      g = lo_mask ? 0.f : g;           // once per head: on the high column
     }
 
-    // ---- P' operand (fp16 hi + lo), slots in the order of the value chunks
-    uint32_t ph[2][4], pl[2][4];
+    // ---- P' operand, this lane's part, slots in the order of the value chunks
+    uint32_t po[2][4];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int pa = vpos<BITS>(ks, 2 * s), pbp = vpos<BITS>(ks, 2 * s + 1);
-        const float xa = p[(pa >> 2) & 3][pa & 3], xb = p[(pbp >> 2) & 3][pbp & 3];
-        const _Float16 ha = (_Float16)xa, hb = (_Float16)xb;
-        ph[ks][s] = __builtin_bit_cast(uint32_t, h2{ha, hb});
-        pl[ks][s] = pack2(xa - (float)ha, xb - (float)hb);
+        po[ks][s] = part2(p[(pa >> 2) & 3][pa & 3], p[(pbp >> 2) & 3][pbp & 3]);
       }
-    const h8 b0h = make8(ph[0][0], ph[0][1], ph[0][2], ph[0][3]);
-    const h8 b0l = make8(pl[0][0], pl[0][1], pl[0][2], pl[0][3]);
-    const h8 b1h = make8(ph[1][0], ph[1][1], ph[1][2], ph[1][3]);
-    const h8 b1l = make8(pl[1][0], pl[1][1], pl[1][2], pl[1][3]);
+    const h8 b0 = make8(po[0][0], po[0][1], po[0][2], po[0][3]);
+    const h8 b1 = make8(po[1][0], po[1][1], po[1][2], po[1][3]);
 
     // ---- O += V^T P' per 16-channel tile
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-      const h8 a0 = codes8<BITS, OFFV>(B.vw[ct], 0);
-      const h8 a1 = codes8<BITS, OFFV>(B.vw[ct], 1);
       f4 t = MODE == RTN ? acc[ct] : f4{0.f, 0.f, 0.f, 0.f};
-      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0h, t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0l, t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1h, t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1l, t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<BITS, OFFV>(B.vw[ct], 0), b0, t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<BITS, OFFV>(B.vw[ct], 1), b1, t, 0, 0, 0);
       if constexpr (MODE == RTN) {
         acc[ct] = t;
-      } else {
-        float f[4];
-        if constexpr (MODE == KVARN) {
-          const float4 v = *reinterpret_cast<const float4*>(v1 + 16 * ct + 4 * q);
-          f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
-        } else {
-          const uint2 v = *reinterpret_cast<const uint2*>(vS16 + 16 * ct + 4 * q);
-          const float2 lo = __half22float2(__builtin_bit_cast(__half2, v.x));
-          const float2 hi = __half22float2(__builtin_bit_cast(__half2, v.y));
-          f[0] = lo.x; f[1] = lo.y; f[2] = hi.x; f[3] = hi.y;
-        }
+      } else if constexpr (MODE == KVARN) {
+        const float4 v = *reinterpret_cast<const float4*>(v1 + 16 * ct + 4 * q);
+        const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[ct][e] = fmaf(f[e], t[e] + g, acc[ct][e]);
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(vS16 + 16 * ct + 4 * q);
+        const h2 lo = __builtin_bit_cast(h2, v.x), hi = __builtin_bit_cast(h2, v.y);
+        acc[ct][0] = fmaf((float)lo[0], t[0], acc[ct][0]);
+        acc[ct][1] = fmaf((float)lo[1], t[1], acc[ct][1]);
+        acc[ct][2] = fmaf((float)hi[0], t[2], acc[ct][2]);
+        acc[ct][3] = fmaf((float)hi[1], t[3], acc[ct][3]);
       }
     }
     wave_sync();   // the statistics area is rewritten by the next half block
@@ -448,11 +497,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   float pmw = d.pm;
   pmw += __shfl_xor(pmw, 16);
   pmw += __shfl_xor(pmw, 32);
+  float o[8][4];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[ct][e] = d.acc[ct][e] + dpp_f<0x128>(d.acc[ct][e]);   // high + low column
   if (n < G) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s_o[w][n * 128 + 16 * ct + 4 * q + e] = d.acc[ct][e] + pmw;
+      for (int e = 0; e < 4; ++e) s_o[w][n * 128 + 16 * ct + 4 * q + e] = o[ct][e] + pmw;
     if (q == 0) { s_m[w][n] = d.m_run; s_l[w][n] = l; }
   }
   // ---- the fp16 tail (waves 0 and 1; it belongs to the last split)
