@@ -36,6 +36,7 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {   // two fp32 -> fp16 pair, RNE
   h2 v;
@@ -124,6 +125,8 @@ struct MfmaDecoder {
   const DecodeArgs& a;
   const int lane, w, par, n, q;
   const uint32_t lo_mask;     // all ones on the low-part columns (n >= 8)
+  __amdgpu_buffer_rsrc_t rs;  // this (sequence, kv head)'s records
+  uint32_t koff, voff;        // this lane's key / value chunk offsets in a record
   uint8_t* meta;              // this wave's LDS copy of the block statistics
   uint32_t qh[QF16 ? 16 : 1]; // fp16 query pairs of head n & 7 in operand slot order (0 if n & 7 >= G)
   float qv[QF16 ? 1 : 32];    // fp32 query of head n & 7, channels 32*q .. 32*q+31
@@ -133,6 +136,12 @@ struct MfmaDecoder {
   __device__ MfmaDecoder(const DecodeArgs& args, int lane_, int w_, const float* qs, uint8_t* meta_)
       : a(args), lane(lane_), w(w_), par(w_ & 1), n(lane_ & 15), q(lane_ >> 4),
         lo_mask((lane_ & 8) ? 0xFFFFFFFFu : 0u), meta(meta_) {
+    const size_t unit_bytes = (size_t)a.max_blocks * a.lay.rec_bytes;
+    const uint8_t* unit = a.rec + (size_t)(blockIdx.z * a.Hkv + blockIdx.y) * unit_bytes;
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(unit), (short)0,
+                                           (int)min(unit_bytes, (size_t)0x7FFFFFFF), 0x00020000);
+    koff = a.lay.kc + (uint32_t)((64 * par + n) * R + q * (R / 4));
+    voff = a.lay.vc + (uint32_t)(par * (128 * RH) + n * RH + q * (RH / 4));
     const int h = n & 7;
     const float* qrow = qs + (h < G ? h : 0) * 128 + 32 * q;
     if constexpr (QF16) {
@@ -152,37 +161,36 @@ struct MfmaDecoder {
     pm = 0.f;
   }
 
-  __device__ __forceinline__ const uint8_t* record(int blk) const {
-    return a.rec + ((size_t)(blockIdx.z * a.Hkv + blockIdx.y) * a.max_blocks + blk) * (size_t)a.lay.rec_bytes;
-  }
-
+  // Record loads go through a buffer resource over this (sequence, kv head)'s records: the
+  // block offset is a scalar, the lane offset a 32-bit register that is the same for every
+  // block, and the per-load displacement an immediate (no per-lane 64-bit address math).
   __device__ __forceinline__ void fetch(Buf& B, int blk) const {
-    const uint8_t* rec = record(blk);
-    const uint8_t* krow = rec + a.lay.kc + (size_t)(64 * par + n) * R + q * (R / 4);
+    const int soff = blk * (int)a.lay.rec_bytes;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       if constexpr (KW == 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(krow + (size_t)16 * tt * R);
+        const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, koff + 16 * tt * R, soff, 0);
         B.kw[tt][0] = v.x; B.kw[tt][1] = v.y; B.kw[tt][2] = v.z; B.kw[tt][3] = v.w;
       } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(krow + (size_t)16 * tt * R);
+        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rs, koff + 16 * tt * R, soff, 0);
         B.kw[tt][0] = v.x; B.kw[tt][1] = v.y;
       }
     }
-    const uint8_t* vrow = rec + a.lay.vc + (size_t)par * (128 * RH) + (size_t)n * RH + q * (RH / 4);
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       if constexpr (VW == 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(vrow + (size_t)16 * ct * RH);
+        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 16 * ct * RH, soff, 0);
         B.vw[ct][0] = v.x; B.vw[ct][1] = v.y;
       } else {
-        B.vw[ct][0] = *reinterpret_cast<const uint32_t*>(vrow + (size_t)16 * ct * RH);
+        B.vw[ct][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 16 * ct * RH, soff, 0);
       }
     }
-    const uint4* src = reinterpret_cast<const uint4*>(rec + a.lay.ks);
-    constexpr int last = META / 16 - 1;
 #pragma unroll
-    for (int k = 0; k < NMETA; ++k) B.meta[k] = src[min(lane + 64 * k, last)];
+    for (int k = 0; k < NMETA; ++k) {
+      const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, a.lay.ks + 16u * (uint32_t)min(lane + 64 * k, META / 16 - 1),
+                                                          soff, 0);
+      B.meta[k] = uint4{v.x, v.y, v.z, v.w};
+    }
   }
 
   __device__ __forceinline__ void wave_sync() const {
@@ -364,18 +372,24 @@ struct MfmaDecoder {
     wave_sync();   // the statistics area is rewritten by the next half block
   }
 
+  // The next block is fetched unconditionally (past the end: the last block again, an L2
+  // hit), so the wait before a block's first use covers that block's loads only; a fetch
+  // under a branch would make the counter wait drain the prefetch as well.
   __device__ __forceinline__ void run(int blo, int bhi) {
     Buf A, Bb;
     int blk = blo + (w >> 1);
-    if (blk < bhi) fetch(A, blk);
-    while (blk < bhi) {
-      if (blk + 2 < bhi) fetch(Bb, blk + 2);
+    if (blk >= bhi) return;
+    const int last = bhi - 1;
+    fetch(A, blk);
+    while (true) {
+      fetch(Bb, min(blk + 2, last));
       process(A);
       blk += 2;
       if (blk >= bhi) break;
-      if (blk + 2 < bhi) fetch(A, blk + 2);
+      fetch(A, min(blk + 2, last));
       process(Bb);
       blk += 2;
+      if (blk >= bhi) break;
     }
   }
 };
