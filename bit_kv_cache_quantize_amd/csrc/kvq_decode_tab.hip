@@ -44,7 +44,10 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <int MODE, int BITS>
+// BIG: the outlier segments of a block exceed one 16-byte chunk per thread; the extra chunks
+// are loaded in a loop (kept out of the common instantiation: a load loop under a branch
+// makes the counter wait at its join drain the key and value prefetches).
+template <int MODE, int BITS, bool BIG>
 struct TabDecoder {
   static constexpr int R = 16 * BITS;                 // key row bytes
   static constexpr int RH = R / 2;                    // value half-row bytes
@@ -150,20 +153,22 @@ struct TabDecoder {
     load_row<R>(K.kw, record(blk) + a.lay.kc + (size_t)j * R);
   }
 
+  // The statistics are loaded before the code rows: they are staged at the top of the next
+  // block, and the in-order load counter then leaves the rows in flight.
   __device__ __forceinline__ void fetch_vals(Vals& V, int blk) const {
     const uint8_t* rec = record(blk);
-    if constexpr (MV) {
-      load_row<RH>(V.vw, rec + a.lay.vc + (size_t)(par * 128 + ch0()) * RH);
-      load_row<RH>(V.vw + KWD / 2, rec + a.lay.vc + (size_t)(par * 128 + ch1()) * RH);
-    } else {
-      load_row<R>(V.vw, rec + a.lay.vc + (size_t)par * (128 * RH) + (size_t)lane * R);
-    }
     if constexpr (MODE == NUQ) {
       V.tst.x = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + j];   // h
       V.tst.y = reinterpret_cast<const float*>(rec + a.lay.vs)[j];         // z
     } else {
       V.tst.x = reinterpret_cast<const float*>(rec + a.lay.vs)[j];
       V.tst.y = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + j];
+    }
+    if constexpr (MV) {
+      load_row<RH>(V.vw, rec + a.lay.vc + (size_t)(par * 128 + ch0()) * RH);
+      load_row<RH>(V.vw + KWD / 2, rec + a.lay.vc + (size_t)(par * 128 + ch1()) * RH);
+    } else {
+      load_row<R>(V.vw, rec + a.lay.vc + (size_t)par * (128 * RH) + (size_t)lane * R);
     }
   }
 
@@ -259,7 +264,7 @@ struct TabDecoder {
   __device__ __forceinline__ void stage_blob(const Meta& Mt, int blk) const {
     u32x4* dst = reinterpret_cast<u32x4*>(S.blob);
     dst[min(j, ob_chunks - 1)] = Mt.ob;   // lanes past the end rewrite the last chunk (same value)
-    if (ob_chunks > 128) {
+    if constexpr (BIG) {
       const u32x4* src = reinterpret_cast<const u32x4*>(record(blk) + a.lay.ko_val);
       for (int k = j + 128; k < ob_chunks; k += 128) dst[k] = src[k];
     }
@@ -501,9 +506,9 @@ struct TabDecoder {
 
 constexpr int kTabThreads = 128;
 
-template <int MODE, int BITS>
+template <int MODE, int BITS, bool BIG>
 __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_tab_kernel(DecodeArgs a) {
-  using Dec = TabDecoder<MODE, BITS>;
+  using Dec = TabDecoder<MODE, BITS, BIG>;
   constexpr int PT = Dec::PT;
   extern __shared__ __align__(16) uint8_t s_dyn[];
   __shared__ __align__(16) float2 s_tab[64 * Dec::PS];
@@ -672,8 +677,13 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
 
 template <int MODE, int BITS>
 hipError_t launch_t(const DecodeArgs& a, int batch, hipStream_t s) {
-  hipLaunchKernelGGL((decode_tab_kernel<MODE, BITS>), dim3(a.splits, a.Hkv, batch), dim3(kTabThreads),
-                     (size_t)a.wave_lds, s, a);   // outlier staging
+  const bool big = a.k_out > 0 && (a.lay.vo_idx + 128u * a.k_out - a.lay.ko_val + 15u) / 16u > (unsigned)kTabThreads;
+  if (big)
+    hipLaunchKernelGGL((decode_tab_kernel<MODE, BITS, true>), dim3(a.splits, a.Hkv, batch), dim3(kTabThreads),
+                       (size_t)a.wave_lds, s, a);   // outlier staging
+  else
+    hipLaunchKernelGGL((decode_tab_kernel<MODE, BITS, false>), dim3(a.splits, a.Hkv, batch), dim3(kTabThreads),
+                       (size_t)a.wave_lds, s, a);
   return hipGetLastError();
 }
 
