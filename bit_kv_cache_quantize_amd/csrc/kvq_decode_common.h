@@ -69,19 +69,22 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t* w, int i) {
   }
 }
 
+// A packed code row into registers. Code rows are read once per decode: non-temporal loads.
 template <int NBYTES>
 __device__ __forceinline__ void load_row(uint32_t* w, const uint8_t* p) {
+  typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t v2 __attribute__((ext_vector_type(2)));
   static_assert(NBYTES % 8 == 0, "row bytes");
   if constexpr (NBYTES % 16 == 0) {
 #pragma unroll
     for (int k = 0; k < NBYTES / 16; ++k) {
-      const uint4 v = reinterpret_cast<const uint4*>(p)[k];
+      const v4 v = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p) + k);
       w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
     }
   } else {
 #pragma unroll
     for (int k = 0; k < NBYTES / 8; ++k) {
-      const uint2 v = reinterpret_cast<const uint2*>(p)[k];
+      const v2 v = __builtin_nontemporal_load(reinterpret_cast<const v2*>(p) + k);
       w[2 * k] = v.x; w[2 * k + 1] = v.y;
     }
   }

@@ -164,25 +164,28 @@ struct MfmaDecoder {
   // Record loads go through a buffer resource over this (sequence, kv head)'s records: the
   // block offset is a scalar, the lane offset a 32-bit register that is the same for every
   // block, and the per-load displacement an immediate (no per-lane 64-bit address math).
+  // The codes are read once: non-temporal loads (cache-policy bit "nt"); the statistics,
+  // read by both waves of a block, keep the default policy.
+  static constexpr int kNT = 2;
   __device__ __forceinline__ void fetch(Buf& B, int blk) const {
     const int soff = blk * (int)a.lay.rec_bytes;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       if constexpr (KW == 4) {
-        const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, koff + 16 * tt * R, soff, 0);
+        const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, koff + 16 * tt * R, soff, kNT);
         B.kw[tt][0] = v.x; B.kw[tt][1] = v.y; B.kw[tt][2] = v.z; B.kw[tt][3] = v.w;
       } else {
-        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rs, koff + 16 * tt * R, soff, 0);
+        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rs, koff + 16 * tt * R, soff, kNT);
         B.kw[tt][0] = v.x; B.kw[tt][1] = v.y;
       }
     }
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       if constexpr (VW == 2) {
-        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 16 * ct * RH, soff, 0);
+        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 16 * ct * RH, soff, kNT);
         B.vw[ct][0] = v.x; B.vw[ct][1] = v.y;
       } else {
-        B.vw[ct][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 16 * ct * RH, soff, 0);
+        B.vw[ct][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 16 * ct * RH, soff, kNT);
       }
     }
 #pragma unroll
