@@ -205,9 +205,14 @@ struct MfmaDecoder {
   // fp32 x -> the fp16 part of this lane's column: x rounded (high columns) or x minus that
   // rounding, rounded (low columns); two values per call.
   __device__ __forceinline__ uint32_t part2(float xa, float xb) const {
-    const uint32_t hi = pack2(xa, xb) & lo_mask;
-    const h2 c = __builtin_bit_cast(h2, hi);
-    return pack2(xa - (float)c[0], xb - (float)c[1]);
+    const uint32_t c = pack2(xa, xb) & lo_mask;
+    // x - c in one mixed-precision fma per value (fp32 x, fp16 c from the low / high half),
+    // rounded once to fp16 into the low / high half; exact before the rounding since c is x
+    // rounded to fp16, or 0
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(r) : "v"(xa), "v"(c));
+    asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(r) : "v"(xb), "v"(c));
+    return r;
   }
 
   __device__ __forceinline__ void process(const Buf& B) {
@@ -353,7 +358,7 @@ struct MfmaDecoder {
     // ---- O += V^T P' per 16-channel tile
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-      f4 t = MODE == RTN ? acc[ct] : f4{0.f, 0.f, 0.f, 0.f};
+      f4 t = MODE == RTN ? acc[ct] : f4{g, g, g, g};   // KVarN: the code-independent part enters here
       t = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<BITS, OFFV>(B.vw[ct], 0), b0, t, 0, 0, 0);
       t = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<BITS, OFFV>(B.vw[ct], 1), b1, t, 0, 0, 0);
       if constexpr (MODE == RTN) {
@@ -362,7 +367,7 @@ struct MfmaDecoder {
         const float4 v = *reinterpret_cast<const float4*>(v1 + 16 * ct + 4 * q);
         const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[ct][e] = fmaf(f[e], t[e] + g, acc[ct][e]);
+        for (int e = 0; e < 4; ++e) acc[ct][e] = fmaf(f[e], t[e], acc[ct][e]);
       } else {
         const uint2 v = *reinterpret_cast<const uint2*>(vS16 + 16 * ct + 4 * q);
         const h2 lo = __builtin_bit_cast(h2, v.x), hi = __builtin_bit_cast(h2, v.y);
