@@ -136,10 +136,6 @@ struct MfmaDecoder {
   __device__ MfmaDecoder(const DecodeArgs& args, int lane_, int w_, const float* qs, uint8_t* meta_)
       : a(args), lane(lane_), w(w_), par(w_ & 1), n(lane_ & 15), q(lane_ >> 4),
         lo_mask((lane_ & 8) ? 0xFFFFFFFFu : 0u), meta(meta_) {
-    const size_t unit_bytes = (size_t)a.max_blocks * a.lay.rec_bytes;
-    const uint8_t* unit = a.rec + (size_t)(blockIdx.z * a.Hkv + blockIdx.y) * unit_bytes;
-    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(unit), (short)0,
-                                           (int)min(unit_bytes, (size_t)0x7FFFFFFF), 0x00020000);
     koff = a.lay.kc + (uint32_t)((64 * par + n) * R + q * (R / 4));
     voff = a.lay.vc + (uint32_t)(par * (128 * RH) + n * RH + q * (RH / 4));
     const int h = n & 7;
@@ -161,37 +157,40 @@ struct MfmaDecoder {
     pm = 0.f;
   }
 
-  // Record loads go through a buffer resource over this (sequence, kv head)'s records: the
-  // block offset is a scalar, the lane offset a 32-bit register that is the same for every
-  // block, and the per-load displacement an immediate (no per-lane 64-bit address math).
+  // Record loads go through a buffer resource over this split's records: the lane offset is
+  // a 32-bit register (fixed per lane plus the block's offset in the split), the per-load
+  // displacement an immediate (no per-lane 64-bit address math). The range check of the
+  // resource covers lane offset and displacement, so a fetch past the split's last block
+  // returns zeros without touching memory.
   // The codes are read once: non-temporal loads (cache-policy bit "nt"); the statistics,
   // read by both waves of a block, keep the default policy.
   static constexpr int kNT = 2;
-  __device__ __forceinline__ void fetch(Buf& B, int blk) const {
-    const int soff = blk * (int)a.lay.rec_bytes;
+  __device__ __forceinline__ void fetch(Buf& B, int rel) const {   // rel: block index in the split
+    const uint32_t boff = (uint32_t)rel * a.lay.rec_bytes;
+    constexpr int soff = 0;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       if constexpr (KW == 4) {
-        const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, koff + 16 * tt * R, soff, kNT);
+        const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, boff + koff + 16 * tt * R, soff, kNT);
         B.kw[tt][0] = v.x; B.kw[tt][1] = v.y; B.kw[tt][2] = v.z; B.kw[tt][3] = v.w;
       } else {
-        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rs, koff + 16 * tt * R, soff, kNT);
+        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rs, boff + koff + 16 * tt * R, soff, kNT);
         B.kw[tt][0] = v.x; B.kw[tt][1] = v.y;
       }
     }
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       if constexpr (VW == 2) {
-        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 16 * ct * RH, soff, kNT);
+        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rs, boff + voff + 16 * ct * RH, soff, kNT);
         B.vw[ct][0] = v.x; B.vw[ct][1] = v.y;
       } else {
-        B.vw[ct][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 16 * ct * RH, soff, kNT);
+        B.vw[ct][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, boff + voff + 16 * ct * RH, soff, kNT);
       }
     }
 #pragma unroll
     for (int k = 0; k < NMETA; ++k) {
-      const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, a.lay.ks + 16u * (uint32_t)min(lane + 64 * k, META / 16 - 1),
-                                                          soff, 0);
+      const u4v v = __builtin_amdgcn_raw_buffer_load_b128(
+          rs, boff + a.lay.ks + 16u * (uint32_t)min(lane + 64 * k, META / 16 - 1), soff, 0);
       B.meta[k] = uint4{v.x, v.y, v.z, v.w};
     }
   }
@@ -380,24 +379,28 @@ struct MfmaDecoder {
     wave_sync();   // the statistics area is rewritten by the next half block
   }
 
-  // The next block is fetched unconditionally (past the end: the last block again, an L2
-  // hit), so the wait before a block's first use covers that block's loads only; a fetch
-  // under a branch would make the counter wait drain the prefetch as well.
   __device__ __forceinline__ void run(int blo, int bhi) {
+    const uint8_t* base =
+        a.rec + ((size_t)(blockIdx.z * a.Hkv + blockIdx.y) * a.max_blocks + blo) * (size_t)a.lay.rec_bytes;
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
+                                           (int)((bhi - blo) * a.lay.rec_bytes), 0x00020000);
     Buf A, Bb;
-    int blk = blo + (w >> 1);
-    if (blk >= bhi) return;
-    const int last = bhi - 1;
-    fetch(A, blk);
+    int rel = w >> 1;                  // this wave's blocks: rel, rel + 2, ... (relative to blo)
+    const int nb = bhi - blo;
+    if (rel >= nb) return;
+    fetch(A, rel);
+    // the next block is fetched unconditionally (past the end it reads nothing), so the wait
+    // before a block's first use covers that block's loads only; a fetch under a branch would
+    // make the counter wait drain the prefetch as well
     while (true) {
-      fetch(Bb, min(blk + 2, last));
+      fetch(Bb, rel + 2);
       process(A);
-      blk += 2;
-      if (blk >= bhi) break;
-      fetch(A, min(blk + 2, last));
+      rel += 2;
+      if (rel >= nb) break;
+      fetch(A, rel + 2);
       process(Bb);
-      blk += 2;
-      if (blk >= bhi) break;
+      rel += 2;
+      if (rel >= nb) break;
     }
   }
 };

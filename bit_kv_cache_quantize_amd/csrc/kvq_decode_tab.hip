@@ -135,40 +135,78 @@ struct TabDecoder {
     return a.rec + ((size_t)(blockIdx.z * a.Hkv + blockIdx.y) * a.max_blocks + blk) * (size_t)a.lay.rec_bytes;
   }
 
+  // Record loads go through a buffer resource over this split's records (blocks blo ..
+  // bhi-1): 32-bit lane offsets, and the resource's range check turns a load of the block
+  // after the split's last into zeros that touch no memory. Every load of the next block is
+  // therefore issued unconditionally: a load under a branch makes the memory-counter waits
+  // after the join drain every load in flight.
+  __amdgpu_buffer_rsrc_t rsb;
+  int blo_;
+  __device__ __forceinline__ void bind(int blo, int bhi) {
+    rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(record(blo)), (short)0,
+                                            (int)(max(bhi - blo, 0) * a.lay.rec_bytes), 0x00020000);
+    blo_ = blo;
+  }
+  __device__ __forceinline__ uint32_t boff(int blk) const { return (uint32_t)(blk - blo_) * a.lay.rec_bytes; }
+  static constexpr int kNT = 2;   // cache policy "nt": the code rows are read once
+
+  template <int NBYTES>
+  __device__ __forceinline__ void load_row_b(uint32_t* w, uint32_t off) const {
+    static_assert(NBYTES % 8 == 0, "row bytes");
+    if constexpr (NBYTES % 16 == 0) {
+#pragma unroll
+      for (int k = 0; k < NBYTES / 16; ++k) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsb, off + 16 * k, 0, kNT);
+        w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NBYTES / 8; ++k) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rsb, off + 8 * k, 0, kNT);
+        w[2 * k] = v.x; w[2 * k + 1] = v.y;
+      }
+    }
+  }
+
+  __device__ __forceinline__ float ldf(uint32_t off) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsb, off, 0, 0));
+  }
+
   __device__ __forceinline__ void fetch_meta(Meta& Mt, int blk) const {
-    const uint8_t* rec = record(blk);
-    const float2 s2 = reinterpret_cast<const float2*>(rec + a.lay.ks)[ib];          // RTN s / NUQ z
-    const float2 m2 = reinterpret_cast<const float2*>(rec + a.lay.ks + 512)[ib];    // RTN m / NUQ h
-    if constexpr (MODE == NUQ) Mt.kst = make_float4(m2.x, m2.y, s2.x, s2.y);       // (h, h, z, z)
-    else Mt.kst = make_float4(s2.x, s2.y, m2.x, m2.y);                              // (s, s, m, m)
-    Mt.rb = reinterpret_cast<const float2*>(a.rope_base)[(size_t)blk * 64 + ib];
-    // Without outliers the load reads a fixed cached address instead (no branch around the
-    // load: a branch makes the memory-counter waits after it conservative).
-    const u32x4* obp = a.k_out > 0 ? reinterpret_cast<const u32x4*>(rec + a.lay.ko_val) + min(j, ob_chunks - 1)
-                                   : reinterpret_cast<const u32x4*>(a.rope_base);
-    Mt.ob = *obp;
+    const uint32_t o = boff(blk);
+    // each pair is converted to float as a whole: with the two halves bit-cast one at a
+    // time, this compiler narrows the 8-byte load to 4 bytes and uses them for both halves
+    const float2 s2 = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rsb, o + a.lay.ks + 8u * ib, 0, 0));
+    const float2 m2 =
+        __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rsb, o + a.lay.ks + 512u + 8u * ib, 0, 0));
+    if constexpr (MODE == NUQ) Mt.kst = make_float4(m2.x, m2.y, s2.x, s2.y);   // (h, h, z, z)   RTN s, m / NUQ z, h
+    else Mt.kst = make_float4(s2.x, s2.y, m2.x, m2.y);                          // (s, s, m, m)
+    Mt.rb = reinterpret_cast<const float2*>(a.rope_base)[(size_t)blk * 64 + ib];   // rows 0 .. nblk exist
+    // without outliers the offset lies past the range: zeros, no memory access
+    const uint32_t oo = a.k_out > 0 ? o + a.lay.ko_val + 16u * (uint32_t)min(j, ob_chunks - 1) : 0xFFFFFFF0u;
+    Mt.ob = __builtin_amdgcn_raw_buffer_load_b128(rsb, oo, 0, 0);
   }
 
   __device__ __forceinline__ void fetch_keys(Keys& K, int blk) const {
-    load_row<R>(K.kw, record(blk) + a.lay.kc + (size_t)j * R);
+    load_row_b<R>(K.kw, boff(blk) + a.lay.kc + (uint32_t)j * R);
   }
 
   // The statistics are loaded before the code rows: they are staged at the top of the next
   // block, and the in-order load counter then leaves the rows in flight.
   __device__ __forceinline__ void fetch_vals(Vals& V, int blk) const {
-    const uint8_t* rec = record(blk);
+    const uint32_t o = boff(blk);
     if constexpr (MODE == NUQ) {
-      V.tst.x = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + j];   // h
-      V.tst.y = reinterpret_cast<const float*>(rec + a.lay.vs)[j];         // z
+      V.tst.x = ldf(o + a.lay.vs + 4u * (128 + j));   // h
+      V.tst.y = ldf(o + a.lay.vs + 4u * j);           // z
     } else {
-      V.tst.x = reinterpret_cast<const float*>(rec + a.lay.vs)[j];
-      V.tst.y = reinterpret_cast<const float*>(rec + a.lay.vs)[128 + j];
+      V.tst.x = ldf(o + a.lay.vs + 4u * j);
+      V.tst.y = ldf(o + a.lay.vs + 4u * (128 + j));
     }
     if constexpr (MV) {
-      load_row<RH>(V.vw, rec + a.lay.vc + (size_t)(par * 128 + ch0()) * RH);
-      load_row<RH>(V.vw + KWD / 2, rec + a.lay.vc + (size_t)(par * 128 + ch1()) * RH);
+      load_row_b<RH>(V.vw, o + a.lay.vc + (uint32_t)(par * 128 + ch0()) * RH);
+      load_row_b<RH>(V.vw + KWD / 2, o + a.lay.vc + (uint32_t)(par * 128 + ch1()) * RH);
     } else {
-      load_row<R>(V.vw, rec + a.lay.vc + (size_t)par * (128 * RH) + (size_t)lane * R);
+      load_row_b<R>(V.vw, o + a.lay.vc + (uint32_t)par * (128 * RH) + (uint32_t)lane * R);
     }
   }
 
@@ -265,8 +303,8 @@ struct TabDecoder {
     u32x4* dst = reinterpret_cast<u32x4*>(S.blob);
     dst[min(j, ob_chunks - 1)] = Mt.ob;   // lanes past the end rewrite the last chunk (same value)
     if constexpr (BIG) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(record(blk) + a.lay.ko_val);
-      for (int k = j + 128; k < ob_chunks; k += 128) dst[k] = src[k];
+      for (int k = j + 128; k < ob_chunks; k += 128)
+        dst[k] = __builtin_amdgcn_raw_buffer_load_b128(rsb, boff(blk) + a.lay.ko_val + 16u * k, 0, 0);
     }
   }
 
@@ -591,19 +629,19 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
 
   const int blo = split * a.blocks_per_split;
   const int bhi = min(a.nblk, blo + a.blocks_per_split);
+  d.bind(blo, bhi);
   typename Dec::Meta Mt;
   typename Dec::Keys Kc;
   typename Dec::Vals V;
-  if (blo < bhi) {
-    d.fetch_meta(Mt, blo);
-    d.fetch_keys(Kc, blo);
-    d.fetch_vals(V, blo);
-  }
+  // unconditional: an empty split's loads lie past the range (rope_base row blo <= nblk)
+  d.fetch_meta(Mt, blo);
+  d.fetch_keys(Kc, blo);
+  d.fetch_vals(V, blo);
   __syncthreads();   // the value table is complete
   for (int blk = blo; blk < bhi; ++blk) {
-    // the loads of the next block are unconditional (the last block reloads itself), so
-    // that no branch makes the memory-counter waits conservative
-    const int nxt = min(blk + 1, bhi - 1);
+    // the loads of the next block are unconditional (past the split's end they read
+    // nothing), so that no branch makes the memory-counter waits conservative
+    const int nxt = blk + 1;
     if (a.k_out > 0) {
       d.stage_blob(Mt, blk);
       s_vst[tid] = V.tst;
