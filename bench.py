@@ -17,6 +17,8 @@ rate is timed separately on one resident 256K-token chunk.
 Prints one JSON line. value = decode effective KV GB/s = the algorithmic bytes a
 decode must move (block records without padding, fp16 tail, q, out, codebooks,
 RoPE rows) / decode time, from HIP events on the stream the kernels run on.
+frac_hbm_peak divides it by the 8 TB/s spec-sheet peak, frac_copy_bw by the
+measured bandwidth of a 1 GiB device copy (copy_gbs, read + write bytes).
 """
 from __future__ import annotations
 
@@ -237,6 +239,23 @@ def measured_traffic(workload, kernel):
     return k["traffic_bytes_per_launch"]
 
 
+def measured_copy_gbs(torch, dev, nbytes=1 << 30, reps=5):
+    """Bandwidth of a plain 1 GiB device-to-device copy (read + write bytes / time, HIP
+    events): the practical HBM ceiling the decode rate is also compared against."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
+
+
 def median(x):
     s = sorted(x)
     return s[len(s) // 2] if s else float("nan")
@@ -314,6 +333,7 @@ def main():
         abytes = wl.batch * wl.n_kv_heads * (n * 512 + (n // 128) * rec_payload)   # the one timed chunk
         app_gbs = abytes / (app_ms * 1e-3) / 1e9
     dec_kernel = decode_kernel_name(wl)
+    copy_gbs = measured_copy_gbs(torch, b.dev)
 
     def roof(achieved_gbs, kernel, us, algo_bytes):
         t = measured_traffic(wl.name, kernel)
@@ -338,6 +358,8 @@ def main():
                    "bits": wl.bits, "outliers_per_vec": wl.outliers_per_vec, "pre_rope": wl.pre_rope,
                    "varn_iters": wl.varn_iters if wl.mode == 2 else 0},
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "copy_gbs": round(copy_gbs, 1),
+        "frac_copy_bw": round(gbs / copy_gbs, 4),
         "decode_us_per_step": round(dec_ms * 1e3, 2),
         "tokens_per_s": round(wl.batch / (dec_ms * 1e-3), 1),
         "append_mtok_s": round(app_rate, 2),

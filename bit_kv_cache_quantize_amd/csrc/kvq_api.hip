@@ -68,12 +68,19 @@ float nuq_threshold(float lo, float hi) {
   return key2f(b);
 }
 
+float u32_as_float(uint32_t u) {
+  float f;
+  std::memcpy(&f, &u, sizeof f);
+  return f;
+}
+
 // Code table of one codebook's decision thresholds tau[0..n): the kernel maps u in [-1, 1]
 // to bucket floor(RN(u * 512 + 512)) (one fma); RN can move u by at most 2^-23 up across a
 // bucket edge, never down, so every u that lands in bucket b lies in [B_b - 2^-23, B_b+1)
 // with B_b = -1 + b / 512. Entry b = (number of thresholds below B_b - 2^-22, the one
 // threshold in [B_b - 2^-22, B_b+1) or +inf); the code is then that count plus (u >= the
-// threshold). Two thresholds in one such range: entry 0 gets count -1 and the kernel counts.
+// threshold). The count is stored as the integer's bits. Two thresholds in one such range:
+// entry 0's count bits are all ones and the kernel counts the thresholds instead.
 void nuq_code_table(const float* tau, int n, float2* lut) {
   const double eps = std::ldexp(1.0, -22);
   bool ok = true;
@@ -87,10 +94,10 @@ void nuq_code_table(const float* tau, int n, float2* lut) {
       else if ((double)tau[t] < hi) { ++inside; t_in = tau[t]; }
     }
     if (inside > 1) ok = false;
-    lut[b] = make_float2((float)below, t_in);
+    lut[b] = make_float2(u32_as_float((uint32_t)below), t_in);   // the count's integer bits
   }
   for (int b = kvq::kNuqBuckets + 1; b < kvq::kNuqLutStride; ++b) lut[b] = make_float2(0.f, INFINITY);
-  if (!ok) lut[0].x = -1.f;
+  if (!ok) lut[0].x = u32_as_float(0xFFFFFFFFu);   // unusable: the kernel counts thresholds
 }
 
 }  // namespace

@@ -38,6 +38,7 @@ namespace kvq {
 namespace {
 
 constexpr int kThreads = 256;
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 constexpr float kInvSqrt128 = 0.08838834764831845f;
 
 struct Smem {
@@ -69,12 +70,23 @@ template <bool F32> struct Tile;
 template <> struct Tile<true> {
   float v[8][8];
   __device__ __forceinline__ float f(int i, int e) const { return v[i][e]; }
+  __device__ __forceinline__ float d(int i, int e, float off) const { return __fsub_rn(v[i][e], off); }
   __device__ __forceinline__ uint32_t key(int i, int e, int idx) const { return mag_key(v[i][e], idx); }
 };
 template <> struct Tile<false> {
   uint32_t v[8][4];
   __device__ __forceinline__ uint32_t bits(int i, int e) const { return (e & 1) ? v[i][e >> 1] >> 16 : v[i][e >> 1] & 0xffffu; }
   __device__ __forceinline__ float f(int i, int e) const { return __half2float(__ushort_as_half((unsigned short)bits(i, e))); }
+  // x - off rounded once to fp32, read straight from the fp16 half (one mixed-precision fma:
+  // x * 1 is exact, so this is the IEEE subtraction)
+  __device__ __forceinline__ float d(int i, int e, float off) const {
+    float r;
+    if (e & 1)
+      asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(v[i][e >> 1]), "v"(off));
+    else
+      asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(v[i][e >> 1]), "v"(off));
+    return r;
+  }
   __device__ __forceinline__ uint32_t key(int i, int e, int idx) const {
     const uint32_t h = (e & 1) ? v[i][e >> 1] >> 16 : v[i][e >> 1] & 0xffffu;
     return ((h & 0x7fffu) << 8) | ((uint32_t)(127 - idx) << 1) | (h >> 15);
@@ -258,8 +270,10 @@ __device__ __forceinline__ uint32_t nuq_search(float u, const float* tau) {
 }
 
 // Statistics of one vector: (sa, sb) = RTN/KVarN (s, m), NUQ (z, h), symmetric int4 (s, -),
-// and rc = RN(1 / divisor) for the element divisions.
-struct VecStats { float sa, sb, rc; };
+// rc = RN(1 / divisor) for the element divisions, 0 for a zero divisor (every quotient of a
+// finite element then comes out 0, the zero-divisor rule, with no per-element test), and
+// off = what an element's difference is taken from (m, z, or 0).
+struct VecStats { float sa, sb, rc, off; };
 
 template <int MODE, int BITS>
 __device__ __forceinline__ VecStats stats_of(float lo, float hi, float amax) {
@@ -267,41 +281,45 @@ __device__ __forceinline__ VecStats stats_of(float lo, float hi, float amax) {
   if constexpr (MODE == NUQ) {
     v.sa = __fmul_rn(__fadd_rn(hi, lo), 0.5f);   // z
     v.sb = __fmul_rn(__fsub_rn(hi, lo), 0.5f);   // h
-    v.rc = __fdiv_rn(1.f, v.sb);
+    v.rc = v.sb == 0.f ? 0.f : __fdiv_rn(1.f, v.sb);
+    v.off = v.sa;
   } else if constexpr (MODE == SYM) {
     v.sa = __half2float(__float2half_rn(__fdiv_rn(amax, 7.0f)));
     v.sb = 0.f;
-    v.rc = __fdiv_rn(1.f, v.sa);
+    v.rc = v.sa == 0.f ? 0.f : __fdiv_rn(1.f, v.sa);
+    v.off = 0.f;
   } else {
     v.sa = __fdiv_rn(__fsub_rn(hi, lo), (float)((1 << BITS) - 1));   // s
     v.sb = lo;                                                       // m
-    v.rc = __fdiv_rn(1.f, v.sa);
+    v.rc = v.sa == 0.f ? 0.f : __fdiv_rn(1.f, v.sa);
+    v.off = lo;
   }
   return v;
 }
 
-// Code of one element: RTN/KVarN clamp(rint((x - m) / s)), NUQ argmin over the codebook of
-// clamp((x - z) / h, -1, 1), symmetric int4 clamp(rint(x / s), -8, 7) + 8; a zero divisor
-// gives code 0 (symmetric: 8).
+// Code of one element from d = x - off: RTN/KVarN clamp(rint((x - m) / s)), NUQ argmin over
+// the codebook of clamp((x - z) / h, -1, 1), symmetric int4 clamp(rint(x / s), -8, 7) + 8; a
+// zero divisor gives code 0 (symmetric: 8) through rc = 0. An outlier position is a NaN: its
+// quotient clamps to the lowest code (0).
 template <int MODE, int BITS, bool LUT = false>
-__device__ __forceinline__ uint32_t code_of(float x, const VecStats& v, const float* tau, const float2* lut = nullptr) {
+__device__ __forceinline__ uint32_t code_of(float d, const VecStats& v, const float* tau, const float2* lut = nullptr) {
   constexpr int QMAX = (1 << BITS) - 1;
-  // both operands of every select are computed: the selects stay branch-free
   if constexpr (MODE == NUQ) {
-    const float q = div_rn(__fsub_rn(x, v.sa), v.sb, v.rc);
-    const float u = v.sb == 0.f ? 0.f : fminf(fmaxf(q, -1.f), 1.f);
+    const float q = div_rn(d, v.sb, v.rc);
+    const float u = fminf(fmaxf(q, -1.f), 1.f);
     if constexpr (LUT) {
-      // bucket of u (one fma, truncation of a value in [0, 1024]), then at most one compare
+      // bucket of u (one fma, truncation of a value in [0, 1024]), then at most one compare;
+      // the entry's count is stored as integer bits
       const float2 e = lut[(int)__fmaf_rn(u, 0.5f * kNuqBuckets, 0.5f * kNuqBuckets)];
-      return (uint32_t)e.x + (u >= e.y ? 1u : 0u);
+      return __float_as_uint(e.x) + (u >= e.y ? 1u : 0u);
     }
     return nuq_search<BITS>(u, tau);
   } else if constexpr (MODE == SYM) {
-    const float q = rintf(div_rn(x, v.sa, v.rc));
-    return (uint32_t)((int)(v.sa == 0.f ? 0.f : fminf(fmaxf(q, -8.f), 7.f)) + 8);
+    const float q = rintf(div_rn(d, v.sa, v.rc));
+    return (uint32_t)((int)fminf(fmaxf(q, -8.f), 7.f) + 8);
   } else {
-    const float q = rintf(div_rn(__fsub_rn(x, v.sb), v.sa, v.rc));
-    return (uint32_t)(v.sa == 0.f ? 0.f : fminf(fmaxf(q, 0.f), (float)QMAX));
+    const float q = rintf(div_rn(d, v.sa, v.rc));
+    return (uint32_t)fminf(fmaxf(q, 0.f), (float)QMAX);
   }
 }
 
@@ -472,15 +490,35 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
   VecStats vs[8];   // per channel e when per_chan, per token i otherwise
   if constexpr (per_chan) {
     float lo[8], hi[8];
+    if constexpr (MODE != KVARN) {
+      // on the fp16 tile, two channels per packed min / max (exact: the elements are fp16;
+      // a NaN, an outlier, is skipped as by fminf / fmaxf)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lo[e] = INFINITY;
-      hi[e] = MODE == SYM ? 0.f : -INFINITY;
+      for (int k = 0; k < 4; ++k) {
+        h2 mn = __builtin_bit_cast(h2, X.v[0][k]);
+        h2 mx = MODE == SYM ? __builtin_elementwise_abs(mn) : mn;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {   // an outlier is a NaN here: skipped
-        const float x = X.f(i, e);
-        lo[e] = fminf(lo[e], x);
-        hi[e] = MODE == SYM ? fmaxf(hi[e], fabsf(x)) : fmaxf(hi[e], x);
+        for (int i = 1; i < 8; ++i) {
+          const h2 x = __builtin_bit_cast(h2, X.v[i][k]);
+          mn = __builtin_elementwise_min(mn, x);
+          mx = __builtin_elementwise_max(mx, MODE == SYM ? __builtin_elementwise_abs(x) : x);
+        }
+        lo[2 * k] = (float)mn[0];
+        lo[2 * k + 1] = (float)mn[1];
+        hi[2 * k] = MODE == SYM ? fmaxf(0.f, (float)mx[0]) : (float)mx[0];
+        hi[2 * k + 1] = MODE == SYM ? fmaxf(0.f, (float)mx[1]) : (float)mx[1];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lo[e] = INFINITY;
+        hi[e] = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {   // an outlier is a NaN here: skipped
+          const float x = X.f(i, e);
+          lo[e] = fminf(lo[e], x);
+          hi[e] = fmaxf(hi[e], x);
+        }
       }
     }
     // both reductions share one barrier
@@ -509,11 +547,20 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float lo = INFINITY, hi = -INFINITY;
+      if constexpr (MODE != KVARN) {   // packed fp16 min / max over the token's 8 channels
+        const h2 a0 = __builtin_bit_cast(h2, X.v[i][0]), a1 = __builtin_bit_cast(h2, X.v[i][1]);
+        const h2 a2 = __builtin_bit_cast(h2, X.v[i][2]), a3 = __builtin_bit_cast(h2, X.v[i][3]);
+        const h2 mn = __builtin_elementwise_min(__builtin_elementwise_min(a0, a1), __builtin_elementwise_min(a2, a3));
+        const h2 mx = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1), __builtin_elementwise_max(a2, a3));
+        lo = fminf(lo, fminf((float)mn[0], (float)mn[1]));
+        hi = fmaxf(hi, fmaxf((float)mx[0], (float)mx[1]));
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {   // an outlier is a NaN here: skipped
-        const float x = X.f(i, e);
-        lo = fminf(lo, x);
-        hi = fmaxf(hi, x);
+        for (int e = 0; e < 8; ++e) {   // an outlier is a NaN here: skipped
+          const float x = X.f(i, e);
+          lo = fminf(lo, x);
+          hi = fmaxf(hi, x);
+        }
       }
       lo = tok_reduce(lo, MinF());
       hi = tok_reduce(hi, MaxF());
@@ -560,7 +607,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       const int t = 32 * w + 4 * i + r;
       uint32_t c[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = code_of<MODE, BITS, LUT>(X.f(i, e), vs[e], tau, sm.nlut);
+      for (int e = 0; e < 8; ++e) c[e] = code_of<MODE, BITS, LUT>(X.d(i, e, vs[e].off), vs[e], tau, sm.nlut);
       uint8_t* row = kc + (size_t)t * R;
       if constexpr (BITS == 4) {
         uint32_t v = 0;
@@ -591,7 +638,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       uint32_t c[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        c[e] = code_of<MODE, BITS, LUT>(X.f(i, e), per_chan ? vs[e] : vs[i], tau, sm.nlut);
+        c[e] = code_of<MODE, BITS, LUT>(X.d(i, e, (per_chan ? vs[e] : vs[i]).off), per_chan ? vs[e] : vs[i], tau, sm.nlut);
       *reinterpret_cast<uint2*>(&sm.vq[t * kD + 8 * g]) =
           make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
     }
@@ -708,7 +755,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
 template <int MODE, int BITS, int TENSOR, int KO>
 __device__ __forceinline__ void run_tensor(const QuantArgs& a, Smem& sm, int j, int h, int b) {
   if constexpr (MODE == NUQ && BITS >= 3) {
-    if (a.nuq_lut[(size_t)(h * 2 + TENSOR) * kNuqLutStride].x >= 0.f) {
+    if (__float_as_uint(a.nuq_lut[(size_t)(h * 2 + TENSOR) * kNuqLutStride].x) != 0xFFFFFFFFu) {
       quantize_tensor<MODE, BITS, TENSOR, KO, true>(a, sm, j, h, b);
       return;
     }
