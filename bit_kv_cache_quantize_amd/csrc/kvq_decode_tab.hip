@@ -66,6 +66,7 @@ struct TabDecoder {
     float4 kst;           // (scale_x, scale_y, offset_x, offset_y) of pair ib
     float2 rb;            // (cos, sin) of the block base angle for pair ib
     u32x4 ob;             // outlier segment chunk j (j = thread of the workgroup)
+    float2 vst;           // token j's value statistics, for the outlier staging (with outliers)
   };
   struct Keys {           // issued after the scores
     uint32_t kw[KWD];     // key row of token j
@@ -185,6 +186,11 @@ struct TabDecoder {
     // without outliers the offset lies past the range: zeros, no memory access
     const uint32_t oo = a.k_out > 0 ? o + a.lay.ko_val + 16u * (uint32_t)min(j, ob_chunks - 1) : 0xFFFFFFF0u;
     Mt.ob = __builtin_amdgcn_raw_buffer_load_b128(rsb, oo, 0, 0);
+    // a second copy of token j's value statistics: the staging at the top of a block then
+    // waits for these loads, not for the value rows issued last in the previous block
+    const uint32_t ov = a.k_out > 0 ? o + a.lay.vs + 4u * j : 0xFFFFFFF0u;
+    const float sv0 = ldf(ov), sv1 = ldf(a.k_out > 0 ? ov + 512u : ov);
+    Mt.vst = MODE == NUQ ? make_float2(sv1, sv0) : make_float2(sv0, sv1);
   }
 
   __device__ __forceinline__ void fetch_keys(Keys& K, int blk) const {
@@ -448,10 +454,19 @@ struct TabDecoder {
 
   // Largest r in 0..127 with ptr[r] <= e (ptr non-decreasing, ptr[128] > e): the row of CSR
   // entry e (binary search, 7 dependent reads).
+  // Row of entry e in a CSR / CSC pointer array of 129 entries: the largest r with
+  // ptr[r] <= e. The first three halvings use the pointers at multiples of 16, read together;
+  // four dependent reads finish the search.
   static __device__ __forceinline__ int segment_of(const uint16_t* ptr, int e) {
-    int r = 0;
+    int c[8];
 #pragma unroll
-    for (int st = 64; st >= 1; st >>= 1) r = ptr[r + st] <= e ? r + st : r;
+    for (int m = 0; m < 8; ++m) c[m] = ptr[16 * (m + 1)];
+    int r = c[3] <= e ? 64 : 0;                                   // ptr[64]
+    r = (r ? c[5] : c[1]) <= e ? r + 32 : r;                      // ptr[r + 32]
+    const int k = r >> 5;                                         // ptr[r + 16] = c[2 k]
+    r = (k == 0 ? c[0] : k == 1 ? c[2] : k == 2 ? c[4] : c[6]) <= e ? r + 16 : r;
+#pragma unroll
+    for (int st = 8; st >= 1; st >>= 1) r = ptr[r + st] <= e ? r + st : r;
     return r;
   }
 
@@ -462,31 +477,26 @@ struct TabDecoder {
   __device__ __forceinline__ void outlier_prep(int tid) const {
     const uint8_t* blob = S.blob;
     const int n = 128 * a.k_out;
-    {
-      const uint16_t* ptr = reinterpret_cast<const uint16_t*>(blob + (a.lay.ko_ptr - a.lay.ko_val));
-      const uint8_t* idx = blob + (a.lay.ko_idx - a.lay.ko_val);
-      const __half* val = reinterpret_cast<const __half*>(blob);
-      for (int e = tid; e < n; e += 128) {
-        const int t = segment_of(ptr, e), c = idx[e], i = c >> 1;
-        const float delta = __half2float(val[e]) - S.kd0[c];
-        const float ang = (float)t * S.trev[i];
-        const float cj = __builtin_amdgcn_cosf(ang), sj = __builtin_amdgcn_sinf(ang);
-        const float2 q2 = S.qb[i];
-        const float coef = (c & 1) ? fmaf(cj, q2.y, -sj * q2.x) : fmaf(cj, q2.x, sj * q2.y);
-        atomicAdd(&S.kcorr[t], delta * coef);
-      }
-    }
-    {
-      const uint16_t* ptr = reinterpret_cast<const uint16_t*>(blob + (a.lay.vo_ptr - a.lay.ko_val));
-      const uint8_t* idx = blob + (a.lay.vo_idx - a.lay.ko_val);
-      const __half* val = reinterpret_cast<const __half*>(blob + (a.lay.vo_val - a.lay.ko_val));
-      const float v0 = MODE == NUQ ? S.cbv[0] : 0.f;
-      for (int e = tid; e < n; e += 128) {
-        const int c = segment_of(ptr, e), t = idx[e];
-        const float2 st = S.vst[t];
-        S.vent[e] = (uint16_t)(t | (c << 8));
-        S.vdelta[e] = __half2float(val[e]) - fmaf(v0, st.x, st.y);
-      }
+    const uint16_t* kptr = reinterpret_cast<const uint16_t*>(blob + (a.lay.ko_ptr - a.lay.ko_val));
+    const uint8_t* kidx = blob + (a.lay.ko_idx - a.lay.ko_val);
+    const __half* kval = reinterpret_cast<const __half*>(blob);
+    const uint16_t* vptr = reinterpret_cast<const uint16_t*>(blob + (a.lay.vo_ptr - a.lay.ko_val));
+    const uint8_t* vidx = blob + (a.lay.vo_idx - a.lay.ko_val);
+    const __half* vval = reinterpret_cast<const __half*>(blob + (a.lay.vo_val - a.lay.ko_val));
+    const float v0 = MODE == NUQ ? S.cbv[0] : 0.f;
+    // key and value entry e in the same iteration: their pointer searches overlap
+    for (int e = tid; e < n; e += 128) {
+      const int t = segment_of(kptr, e), c = kidx[e], i = c >> 1;
+      const int vc = segment_of(vptr, e), vt = vidx[e];
+      const float delta = __half2float(kval[e]) - S.kd0[c];
+      const float ang = (float)t * S.trev[i];
+      const float cj = __builtin_amdgcn_cosf(ang), sj = __builtin_amdgcn_sinf(ang);
+      const float2 q2 = S.qb[i];
+      const float coef = (c & 1) ? fmaf(cj, q2.y, -sj * q2.x) : fmaf(cj, q2.x, sj * q2.y);
+      atomicAdd(&S.kcorr[t], delta * coef);
+      const float2 st = S.vst[vt];
+      S.vent[e] = (uint16_t)(vt | (vc << 8));
+      S.vdelta[e] = __half2float(vval[e]) - fmaf(v0, st.x, st.y);
     }
   }
 
@@ -644,7 +654,7 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
     const int nxt = blk + 1;
     if (a.k_out > 0) {
       d.stage_blob(Mt, blk);
-      s_vst[tid] = V.tst;
+      s_vst[tid] = Mt.vst;
     }
     d.build(Mt);
     d.fetch_meta(Mt, nxt);
