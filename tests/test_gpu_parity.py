@@ -267,3 +267,57 @@ def test_nuq_codes_exhaustive_fp16(K, bits, crowded):
     for j in range(n_blk):
         got = cache.block_bytes(0, 0, 0, j).cpu().numpy()
         H.compare_record(got, oc.blocks[0][0][j], oc.cfg, where=f"block {j}")
+
+
+def _degenerate_kv(L):
+    """fp16 K and V ([1][1][L][128]) whose vectors have a zero range: block 0 of the keys is
+    constant (every key channel: scale / half-range 0) and every value token is constant
+    across its channels; block 1 keys take two values per channel with one larger element
+    (an outlier when the cache keeps one per vector) and a constant remainder in half the
+    channels. The zero-divisor rule and the outlier tie-break (equal magnitudes: the lowest
+    index) decide every code ([KVQ] 3.4; statistics over the non-outliers, 3.1 / 3.3)."""
+    k = np.full((L, 128), 0.75, np.float16)
+    v = np.empty((L, 128), np.float16)
+    for t in range(L):
+        v[t, :] = np.float16(-0.5 + (t % 7) * 0.25)
+    if L > 128:
+        blk = k[128:256]
+        blk[:, :64] = np.where(np.arange(128)[:, None] % 2 == 0, 1.0, -0.5).astype(np.float16)
+        blk[5, :64] = 3.0                    # the largest |x| of the first 64 channels
+        blk[:, 64:] = -1.25                  # constant channels
+        blk[9, 64:] = -1.25                  # ties everywhere: the outlier is token 0
+    return k[None, None], v[None, None]
+
+
+@pytest.mark.parametrize("mode,bits,k_out,rope", [
+    (synth.MODE_RTN, 3, 1, 0), (synth.MODE_RTN, 2, 1, 1), (synth.MODE_RTN, 4, 0, 0),
+    (synth.MODE_NUQ, 3, 1, 1), (synth.MODE_NUQ, 4, 0, 0),
+    (synth.MODE_SYM_INT4, 4, 0, 0), (synth.MODE_SYM_INT4, 4, 1, 1)])
+def test_degenerate_vectors_match_oracle(K, mode, bits, k_out, rope):
+    """Constant and tied vectors: records byte-exact and attention against the oracle,
+    through every decode kernel the combination selects. (KVarN is not exercised: on a
+    constant block its variance normalisation divides by zero deviations again and again
+    and the log-scales diverge, a case the KVarN summary leaves undefined.)"""
+    L = 300
+    wl = small("c1_single_head_2k_rtn4", mode=mode, bits=bits, outliers_per_vec=k_out, pre_rope=rope,
+               n_layers=1, batch=1, n_q_heads=1, n_kv_heads=1)
+    _say(f"case degenerate mode={mode} bits={bits} k_out={k_out} rope={rope}")
+    cache = K.KVCache(H.lib_cfg(wl, H.ceil128(L)))
+    oc = O.OracleCache(H.oracle_cfg(wl, H.ceil128(L)))
+    if mode == synth.MODE_NUQ:
+        for (h, w), cb in H.codebooks(wl, 0).items():
+            cache.codebook_load(0, h, w, cb)
+            oc.load_codebook(0, h, w, cb)
+    k, v = _degenerate_kv(L)
+    cache.append(0, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+    oc.append(0, k, v)
+    torch.cuda.synchronize()
+    stats = H.RecordStats()
+    for j, blk in enumerate(oc.blocks[0][0]):
+        H.compare_record(cache.block_bytes(0, 0, 0, j).cpu().numpy(), blk, oc.cfg, stats, where=f"block {j}")
+    q = H.host_q(wl, 0)
+    out = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
+    cache.decode(0, torch.from_numpy(q).cuda(), out)
+    torch.cuda.synchronize()
+    worst = H.attention_close(out.cpu().numpy(), oc.decode(0, q))
+    _say(f"  ok: worst attention error {worst:.2e} of the bar")
