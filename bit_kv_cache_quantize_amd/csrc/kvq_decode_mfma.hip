@@ -554,23 +554,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   __syncthreads();
   if constexpr (MODE == KVARN) {
-    for (int s = 0; s < 7; ++s) {
-      const int hs = 1 << s;
-      for (int id = tid; id < G * 64; id += kThreads) {
-        const int h = id >> 6, k = id & 63;
-        const int i = h * 128 + (((k >> s) << (s + 1)) | (k & (hs - 1)));
-        const float x = s_o[0][i], y = s_o[0][i + hs];
-        s_o[0][i] = x + y;
-        s_o[0][i + hs] = x - y;
-      }
-      __syncthreads();
+    // back from the Hadamard domain: one wave per head, the 128-point transform in registers
+    // (the same butterflies in the same order as the query's, then the 1/sqrt(128) scale)
+    for (int h = w; h < G; h += 4) {
+      float x = s_o[0][h * 128 + 2 * lane], y = s_o[0][h * 128 + 2 * lane + 1];
+      fwht_wave(x, y, lane);
+      s_o[0][h * 128 + 2 * lane] = x;
+      s_o[0][h * 128 + 2 * lane + 1] = y;
     }
+    __syncthreads();
   }
   for (int i = tid; i < G * 128; i += kThreads) {
     const int h = i >> 7, c = i & 127;
     const size_t row = (size_t)b * a.Hq + (size_t)kvh * G + h;
-    float o = s_o[0][i];
-    if constexpr (MODE == KVARN) o *= kInvSqrt128;
+    const float o = s_o[0][i];
     float M = -INFINITY;
 #pragma unroll
     for (int s = 0; s < 6; ++s) M = fmaxf(M, s_m[s][h]);
