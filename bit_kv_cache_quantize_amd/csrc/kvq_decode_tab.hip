@@ -452,8 +452,6 @@ struct TabDecoder {
     return (x & 0x03000300u) | 0x3C003C00u;
   }
 
-  // Largest r in 0..127 with ptr[r] <= e (ptr non-decreasing, ptr[128] > e): the row of CSR
-  // entry e (binary search, 7 dependent reads).
   // Row of entry e in a CSR / CSC pointer array of 129 entries: the largest r with
   // ptr[r] <= e. The first three halvings use the pointers at multiples of 16, read together;
   // four dependent reads finish the search.
