@@ -67,8 +67,19 @@ __device__ __forceinline__ uint16_t key_bits(uint32_t key) { return (uint16_t)((
 // input bits (two channels per register) and widen on use, which halves the live
 // registers; KVarN keeps fp32, since it rotates and rescales the tile.
 template <bool F32> struct Tile;
+// (127 - element index) << 1 of four elements, one byte each: the index part of their keys.
+__device__ __forceinline__ uint32_t key_idx4(int e0, int step) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w |= (uint32_t)((127 - (e0 + k * step)) << 1) << (8 * k);
+  return w;
+}
+
 template <> struct Tile<true> {
   float v[8][8];
+  __device__ __forceinline__ uint32_t key4(int i, int e, uint32_t iw, int k) const {
+    return mag_key(v[i][e], 127 - (int)((iw >> (8 * k)) & 0xffu) / 2);
+  }
   __device__ __forceinline__ float f(int i, int e) const { return v[i][e]; }
   __device__ __forceinline__ float d(int i, int e, float off) const { return __fsub_rn(v[i][e], off); }
   __device__ __forceinline__ uint32_t key(int i, int e, int idx) const { return mag_key(v[i][e], idx); }
@@ -90,6 +101,13 @@ template <> struct Tile<false> {
   __device__ __forceinline__ uint32_t key(int i, int e, int idx) const {
     const uint32_t h = (e & 1) ? v[i][e >> 1] >> 16 : v[i][e >> 1] & 0xffffu;
     return ((h & 0x7fffu) << 8) | ((uint32_t)(127 - idx) << 1) | (h >> 15);
+  }
+  // The same key from a byte permutation: byte 0 = index byte k of iw, bytes 1-2 = the
+  // element's fp16 bits (its sign lands in bit 23), byte 3 = 0; then the sign moves to bit 0.
+  __device__ __forceinline__ uint32_t key4(int i, int e, uint32_t iw, int k) const {
+    const uint32_t sel = (uint32_t)k | ((4u + 2u * (e & 1)) << 8) | ((5u + 2u * (e & 1)) << 16) | (0x0cu << 24);
+    const uint32_t t = __builtin_amdgcn_perm(v[i][e >> 1], iw, sel);
+    return (t & 0x007fffffu) | (t >> 23);
   }
 };
 
@@ -413,6 +431,10 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
   uint32_t thr[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) thr[k] = 0xffffffffu;
+  // index bytes of this lane's elements: per channel the token 32w + 4i + r (i = 0..7), per
+  // token the channel 8g + e (e = 0..7)
+  const uint32_t kiw[2] = {per_chan ? key_idx4(32 * w + r, 4) : key_idx4(8 * g, 1),
+                           per_chan ? key_idx4(32 * w + 16 + r, 4) : key_idx4(8 * g + 4, 1)};
   for (int p = 0; p < k_out; ++p) {
     opaque(X.v);   // keeps the per-element keys from being hoisted out of the loop (64 more live registers)
     uint32_t best[8];
@@ -422,7 +444,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
         uint32_t m = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const uint32_t key = X.key(i, e, 32 * w + 4 * i + r);
+          const uint32_t key = X.key4(i, e, kiw[i >> 2], i & 3);
           m = (KO == 1 || key < thr[e]) ? (key > m ? key : m) : m;
         }
         best[e] = m;
@@ -439,7 +461,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
         uint32_t m = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint32_t key = X.key(i, e, 8 * g + e);
+          const uint32_t key = X.key4(i, e, kiw[e >> 2], e & 3);
           m = (KO == 1 || key < thr[i]) ? (key > m ? key : m) : m;
         }
         best[i] = tok_reduce(m, MaxU());
@@ -465,7 +487,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const bool o = per_chan ? X.key(i, e, 32 * w + 4 * i + r) >= thr[e] : X.key(i, e, 8 * g + e) >= thr[i];
+        const bool o = per_chan ? X.key4(i, e, kiw[i >> 2], i & 3) >= thr[e] : X.key4(i, e, kiw[e >> 2], e & 3) >= thr[i];
         om[i >> 2] |= o ? (1u << (8 * (i & 3) + e)) : 0u;
       }
   }
