@@ -7,8 +7,11 @@
 // query heads of one kv head, softmax(scale * q . k_hat) weighted sum of v_hat
 // over all cached tokens, dequantized from the packed codes on the fly.
 //
-// Per wave and 64-token half block (the same split / wave / prefetch structure
-// as the VALU kernel):
+// Work decomposition as in the VALU kernel (workgroup = one split of one
+// (sequence, kv head), wave w streams the 64-token half blocks of parity w & 1);
+// the next half block's loads are issued, unconditionally, before the current
+// one is processed, through a buffer resource over the split's records (past the
+// split's end they read nothing). Per wave and 64-token half block:
 //   * scores S^T = K_codes (64 tokens x 128 channels) . Q' (128 x 16): the
 //     codes enter the matrix core as exact fp16 integers (one bit-field select
 //     into the exponent of 1024 and one packed fma per code pair); Q' = q * s_c
