@@ -17,7 +17,8 @@
 // Every quantization decision uses IEEE fp32 operations (no contraction:
 // the library is built with -ffp-contract=off and correctly rounded division),
 // rintf (round half even) and fp16 round-to-nearest-even, so that codes and
-// scales are reproducible.
+// scales are reproducible. The one exception is KVarN's variance normalisation
+// (hardware exp / log), whose scales are specified to a relative tolerance.
 //
 // The 128 x 128 tile stays in registers: wave w holds tokens 32w .. 32w+31 and
 // lane (r = lane >> 4, g = lane & 15) holds tokens t_i = 32w + 4i + r (i = 0..7)
@@ -206,7 +207,9 @@ __device__ __forceinline__ float pop_std(float ss) { return __fsqrt_rn(__fdiv_rn
 
 // Variance normalisation: per iteration a channel step, then a token step, each adding
 // log(std) of the currently scaled tile to its log-scale (a zero std leaves it). Returns
-// the log-scales of this lane's tokens (rl) and channels (cl).
+// the log-scales of this lane's tokens (rl) and channels (cl). exp and log are the
+// hardware approximations (a few ulp): the KVarN scales are reproduced to a relative
+// tolerance, not bit for bit, and these are 16 + 16 calls per iteration and thread.
 __device__ __forceinline__ void varn(float (&x)[8][8], float (&rl)[8], float (&cl)[8], int iters, Smem& sm,
                                      int& ph, int w, int r, int g) {
 #pragma unroll
@@ -214,7 +217,7 @@ __device__ __forceinline__ void varn(float (&x)[8][8], float (&rl)[8], float (&c
   for (int it = 0; it < iters; ++it) {
     float er[8], ec[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) { er[k] = expf(-rl[k]); ec[k] = expf(-cl[k]); }
+    for (int k = 0; k < 8; ++k) { er[k] = __expf(-rl[k]); ec[k] = __expf(-cl[k]); }
     // channel step
     float s[8], ss[8];
 #pragma unroll
@@ -244,8 +247,8 @@ __device__ __forceinline__ void varn(float (&x)[8][8], float (&rl)[8], float (&c
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float sd = pop_std(ss[e]);
-      if (sd > 0.f) cl[e] = __fadd_rn(cl[e], logf(sd));
-      ec[e] = expf(-cl[e]);
+      if (sd > 0.f) cl[e] = __fadd_rn(cl[e], __logf(sd));
+      ec[e] = __expf(-cl[e]);
     }
     // token step
 #pragma unroll
@@ -261,7 +264,7 @@ __device__ __forceinline__ void varn(float (&x)[8][8], float (&rl)[8], float (&c
         sq = __fadd_rn(sq, __fmul_rn(d, d));
       }
       const float sd = pop_std(tok_reduce(sq, AddF()));
-      if (sd > 0.f) rl[i] = __fadd_rn(rl[i], logf(sd));
+      if (sd > 0.f) rl[i] = __fadd_rn(rl[i], __logf(sd));
     }
   }
 }
