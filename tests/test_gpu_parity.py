@@ -111,6 +111,14 @@ CASES = {
     "sym4_g4": (small("c4_blog_int4_32l_b32_32k", n_layers=1, batch=2, n_q_heads=8, n_kv_heads=2), [512]),
     "sym4_rope_out1_g1": (small("c4_blog_int4_32l_b32_32k", n_layers=1, batch=1, n_q_heads=2, n_kv_heads=2,
                                 pre_rope=1, outliers_per_vec=1), [257]),
+    # matrix-core kernel at the group sizes whose head columns fill 2 and all 16 of the
+    # product's columns (high and low parts of 1 and of 8 heads)
+    "rtn2_g1_mfma": (small("c1_single_head_2k_rtn4", bits=2, batch=2, n_q_heads=2, n_kv_heads=2), [640]),
+    "rtn4_g8_mfma": (small("c1_single_head_2k_rtn4", batch=1, n_q_heads=16, n_kv_heads=2), [384, 77]),
+    "sym4_g8_mfma": (small("c4_blog_int4_32l_b32_32k", n_layers=1, batch=1, n_q_heads=16, n_kv_heads=2), [512]),
+    "sym4_g1_mfma": (small("c4_blog_int4_32l_b32_32k", n_layers=1, batch=2, n_q_heads=2, n_kv_heads=2), [300]),
+    "kvarn2_g8_mfma": (small("c3_kvarn_gqa_b16_8k", batch=1, n_q_heads=16, n_kv_heads=2), [256, 100]),
+    "kvarn4_g1_mfma": (small("c3_kvarn_gqa_b16_8k", bits=4, batch=1, n_q_heads=2, n_kv_heads=2), [384]),
 }
 
 
