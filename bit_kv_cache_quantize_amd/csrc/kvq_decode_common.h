@@ -256,6 +256,9 @@ struct Decoder {
       const uint4* src = reinterpret_cast<const uint4*>(rec + a.lay.ko_val);
       uint4* dst = reinterpret_cast<uint4*>(ol.blob);
       for (int k = lane; k < ob_chunks; k += 64) dst[k] = src[k];
+      // many outliers per vector (rare): end this path with nothing in flight, so that the
+      // counter waits after the join stay exact on the common path
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     }
     ol.kS[2 * lane] = B.ks.x; ol.kS[2 * lane + 1] = B.ks.y;
     ol.kM[2 * lane] = B.km.x; ol.kM[2 * lane + 1] = B.km.y;
@@ -268,14 +271,11 @@ struct Decoder {
   __device__ __forceinline__ void process(const Buf& B, int blk, const float (&rc)[64], const float (&rs)[64]) {
     const uint8_t* rec = record(blk);
     const bool outl = MODE != KVARN && a.k_out > 0;
-    uint4 ob0, ob1, ob2;
-    if (outl) {
-      const uint4* src = reinterpret_cast<const uint4*>(rec + a.lay.ko_val);
-      const int last = ob_chunks - 1;
-      ob0 = src[min(lane, last)];
-      ob1 = src[min(lane + 64, last)];
-      ob2 = src[min(lane + 128, last)];
-    }
+    // issued unconditionally (without outliers from the record's first chunk, read anyway):
+    // a load under a branch would make the counter waits after it drain every load in flight
+    const uint4* src = reinterpret_cast<const uint4*>(rec + (outl ? a.lay.ko_val : a.lay.kc));
+    const int last = outl ? ob_chunks - 1 : 0;
+    const uint4 ob0 = src[min(lane, last)], ob1 = src[min(lane + 64, last)], ob2 = src[min(lane + 128, last)];
 
     // ---- q . K for token j
     float sc[G];
@@ -530,19 +530,25 @@ struct Decoder {
     }
   }
 
-  // All half blocks of this wave, one half block of loads in flight ahead of the math.
+  // All half blocks of this wave, one half block of loads in flight ahead of the math. The
+  // next block is fetched unconditionally (past the split's end: its last block again), so
+  // that the wait before a block covers its own loads only: a load under a branch makes the
+  // counter wait at the join drain every load in flight, the prefetch included.
   __device__ __forceinline__ void run(int blo, int bhi, const float (&rc)[64], const float (&rs)[64]) {
     Buf A, Bb;
     int blk = blo + (w >> 1);
-    if (blk < bhi) fetch(A, blk);
-    while (blk < bhi) {
-      if (blk + 2 < bhi) fetch(Bb, blk + 2);
+    if (blk >= bhi) return;
+    const int last = bhi - 1;
+    fetch(A, blk);
+    while (true) {
+      fetch(Bb, min(blk + 2, last));
       process(A, blk, rc, rs);
       blk += 2;
       if (blk >= bhi) break;
-      if (blk + 2 < bhi) fetch(A, blk + 2);
+      fetch(A, min(blk + 2, last));
       process(Bb, blk, rc, rs);
       blk += 2;
+      if (blk >= bhi) break;
     }
   }
 };
