@@ -148,7 +148,8 @@ kvq_status kvq_cache_reset(kvq_cache cache, int layer);
 
 /*
  * Number of decode splits per (sequence, kv head): 0 = automatic (default),
- * otherwise 1..KVQ_MAX_SPLITS (capped to the number of 64-token half blocks).
+ * otherwise 1..KVQ_MAX_SPLITS (capped at decode time to the layer's number of
+ * full 128-token blocks). Returns KVQ_ERR_ARG outside 0..KVQ_MAX_SPLITS.
  */
 kvq_status kvq_set_decode_splits(kvq_cache cache, int splits);
 
