@@ -115,7 +115,6 @@ template <> struct Tile<false> {
 struct MaxU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
 struct MinF { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
 struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
-struct AddF { __device__ float operator()(float a, float b) const { return __fadd_rn(a, b); } };
 
 template <typename T>
 __device__ __forceinline__ T shfl_x(T v, int m) {
@@ -202,71 +201,135 @@ __device__ __forceinline__ void opaque(T (&x)[8][N]) {
     for (int e = 0; e < N; ++e) asm volatile("" : "+v"(x[i][e]));
 }
 
-// Population standard deviation of a vector from its sum and the centred sum of squares.
-__device__ __forceinline__ float pop_std(float ss) { return __fsqrt_rn(__fdiv_rn(ss, 128.f)); }
+// Mean and centred sum of squares (m2) of a group of elements.
+struct Mom { float mean, m2; };
 
-// Variance normalisation: per iteration a channel step, then a token step, each adding
-// log(std) of the currently scaled tile to its log-scale (a zero std leaves it). Returns
-// the log-scales of this lane's tokens (rl) and channels (cl). exp and log are the
-// hardware approximations (a few ulp): the KVarN scales are reproduced to a relative
-// tolerance, not bit for bit, and these are 16 + 16 calls per iteration and thread.
-__device__ __forceinline__ void varn(float (&x)[8][8], float (&rl)[8], float (&cl)[8], int iters, Smem& sm,
-                                     int& ph, int w, int r, int g) {
+// Two groups of n elements each merged into one of 2n (the pairwise update of Chan, Golub and
+// LeVeque: m2 = m2_a + m2_b + (n / 2) (mean_b - mean_a)^2). The result does not depend on the
+// order of the operands, bit for bit (the sums commute, the difference only changes sign), so
+// partner lanes that each pass (own, other) end with identical statistics.
+__device__ __forceinline__ Mom merge(Mom a, Mom b, float half_n) {
+  const float d = __fsub_rn(b.mean, a.mean);
+  return {__fmul_rn(__fadd_rn(a.mean, b.mean), 0.5f), __fmaf_rn(__fmul_rn(d, d), half_n, __fadd_rn(a.m2, b.m2))};
+}
+
+// Moments of eight values (two passes: the mean, then the squared deviations from it).
+__device__ __forceinline__ Mom mom8(const float (&t)[8]) {
+  const float sum = __fadd_rn(__fadd_rn(__fadd_rn(t[0], t[1]), __fadd_rn(t[2], t[3])),
+                              __fadd_rn(__fadd_rn(t[4], t[5]), __fadd_rn(t[6], t[7])));
+  const float mean = __fmul_rn(sum, 0.125f);
+  float m2 = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float d = __fsub_rn(t[k], mean);
+    m2 = __fmaf_rn(d, d, m2);
+  }
+  return {mean, m2};
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ Mom merge_dpp(Mom m, float half_n) {
+  return merge(m, Mom{dpp<CTRL>(m.mean), dpp<CTRL>(m.m2)}, half_n);
+}
+// Partner rows by lane swaps: rows r and r ^ 1 (X16) or r ^ 2 (X32) of the wave; each swap
+// returns the (lower, upper) pair in every lane.
+template <bool X32>
+__device__ __forceinline__ Mom merge_rows(Mom m, float half_n) {
+  const uint32_t a = __float_as_uint(m.mean), b = __float_as_uint(m.m2);
+  if constexpr (X32) {
+    const auto pa = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+    const auto pb = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return merge(Mom{__uint_as_float(pa[0]), __uint_as_float(pb[0])}, Mom{__uint_as_float(pa[1]), __uint_as_float(pb[1])}, half_n);
+  } else {
+    const auto pa = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    const auto pb = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    return merge(Mom{__uint_as_float(pa[0]), __uint_as_float(pb[0])}, Mom{__uint_as_float(pa[1]), __uint_as_float(pb[1])}, half_n);
+  }
+}
+
+// log2 of the population standard deviation of 128 elements from their m2; a zero spread
+// keeps the previous log-scale.
+__device__ __forceinline__ float log2_std(float m2, float prev) {
+  return m2 > 0.f ? __fmaf_rn(__builtin_amdgcn_logf(m2), 0.5f, -3.5f) : prev;
+}
+
+// Variance normalisation in the log2 domain: per iteration a channel step, then a token step.
+// A step adds the log of the standard deviation of the currently scaled tile to its log-scale;
+// since scaling a channel by exp(-c) scales its deviation by the same factor, the channel
+// log-scale after its step is the log deviation of the tile scaled by the token factors
+// alone (and the token log-scale, after its step, that of the tile scaled by the channel
+// factors alone), which is what is computed here, without the accumulated increments. Each
+// statistic is one merged (mean, m2) reduction: 8 elements per lane, then lane merges
+// (rows of 16 lanes by data-parallel moves, the four rows of a wave by lane swaps, the four
+// waves through LDS). Returns the log2-scales of this lane's tokens (rl) and channels (cl).
+// exp2 and log2 are the hardware approximations (about one ulp): the KVarN scales are
+// reproduced to a relative tolerance, not bit for bit.
+__device__ __forceinline__ void varn(const float (&x)[8][8], float (&rl)[8], float (&cl)[8], int iters, Smem& sm,
+                                     int w, int r, int g) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) { rl[k] = 0.f; cl[k] = 0.f; }
   for (int it = 0; it < iters; ++it) {
-    float er[8], ec[8];
+    // channel step: per channel, the deviation over tokens of x * exp2(-rl)
+    float er[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) { er[k] = __expf(-rl[k]); ec[k] = __expf(-cl[k]); }
-    // channel step
-    float s[8], ss[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc = __fadd_rn(acc, __fmul_rn(__fmul_rn(x[i][e], er[i]), ec[e]));
-      s[e] = acc;
-    }
-    chan_reduce(s, reinterpret_cast<float*>(&sm.red[ph][0][0]), w, r, g, AddF());
-    ph ^= 1;
-    opaque(x);   // recompute the scaled tile rather than keep 64 products live
+    for (int i = 0; i < 8; ++i) er[i] = __builtin_amdgcn_exp2f(-rl[i]);
+    Mom cm[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float mean = __fdiv_rn(s[e], 128.f);
-      float acc = 0.f;
+      float t[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float d = __fsub_rn(__fmul_rn(__fmul_rn(x[i][e], er[i]), ec[e]), mean);
-        acc = __fadd_rn(acc, __fmul_rn(d, d));
-      }
-      ss[e] = acc;
+      for (int i = 0; i < 8; ++i) t[i] = __fmul_rn(x[i][e], er[i]);
+      cm[e] = merge_rows<true>(merge_rows<false>(mom8(t), 4.f), 8.f);
     }
-    chan_reduce(ss, reinterpret_cast<float*>(&sm.red[ph][0][0]), w, r, g, AddF());
-    ph ^= 1;
-    opaque(x);
+    // cross-wave: two alternating buffers (the channel and token steps in between keep a
+    // wave from rewriting a buffer another wave may still read)
+    float* bm = (it & 1) ? &sm.rlo[0][0] : reinterpret_cast<float*>(&sm.red[0][0][0]);
+    float* bq = (it & 1) ? &sm.rhi[0][0] : reinterpret_cast<float*>(&sm.red[1][0][0]);
+    if (r == 0) {
+      float4* dm = reinterpret_cast<float4*>(bm + w * kD + 8 * g);
+      float4* dq = reinterpret_cast<float4*>(bq + w * kD + 8 * g);
+      dm[0] = make_float4(cm[0].mean, cm[1].mean, cm[2].mean, cm[3].mean);
+      dm[1] = make_float4(cm[4].mean, cm[5].mean, cm[6].mean, cm[7].mean);
+      dq[0] = make_float4(cm[0].m2, cm[1].m2, cm[2].m2, cm[3].m2);
+      dq[1] = make_float4(cm[4].m2, cm[5].m2, cm[6].m2, cm[7].m2);
+    }
+    __syncthreads();
+    Mom pw[4][8];
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float4* sm4 = reinterpret_cast<const float4*>(bm + ww * kD + 8 * g);
+      const float4* sq4 = reinterpret_cast<const float4*>(bq + ww * kD + 8 * g);
+      const float4 m0 = sm4[0], m1 = sm4[1], q0 = sq4[0], q1 = sq4[1];
+      pw[ww][0] = {m0.x, q0.x}; pw[ww][1] = {m0.y, q0.y}; pw[ww][2] = {m0.z, q0.z}; pw[ww][3] = {m0.w, q0.w};
+      pw[ww][4] = {m1.x, q1.x}; pw[ww][5] = {m1.y, q1.y}; pw[ww][6] = {m1.z, q1.z}; pw[ww][7] = {m1.w, q1.w};
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float sd = pop_std(ss[e]);
-      if (sd > 0.f) cl[e] = __fadd_rn(cl[e], __logf(sd));
-      ec[e] = __expf(-cl[e]);
+      const Mom m = merge(merge(pw[0][e], pw[1][e], 16.f), merge(pw[2][e], pw[3][e], 16.f), 32.f);
+      cl[e] = log2_std(m.m2, cl[e]);
     }
-    // token step
+    // token step: per token, the deviation over channels of x * exp2(-cl)
+    float ec[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ec[e] = __builtin_amdgcn_exp2f(-cl[e]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float acc = 0.f;
+      float u[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc = __fadd_rn(acc, __fmul_rn(__fmul_rn(x[i][e], er[i]), ec[e]));
-      const float mean = __fdiv_rn(tok_reduce(acc, AddF()), 128.f);
-      float sq = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = __fsub_rn(__fmul_rn(__fmul_rn(x[i][e], er[i]), ec[e]), mean);
-        sq = __fadd_rn(sq, __fmul_rn(d, d));
-      }
-      const float sd = pop_std(tok_reduce(sq, AddF()));
-      if (sd > 0.f) rl[i] = __fadd_rn(rl[i], __logf(sd));
+      for (int e = 0; e < 8; ++e) u[e] = __fmul_rn(x[i][e], ec[e]);
+      Mom m = mom8(u);
+      m = merge_dpp<0xB1>(m, 4.f);    // quad_perm(1, 0, 3, 2)
+      m = merge_dpp<0x4E>(m, 8.f);    // quad_perm(2, 3, 0, 1)
+      m = merge_dpp<0x141>(m, 16.f);  // row_half_mirror
+      m = merge_dpp<0x140>(m, 32.f);  // row_mirror
+      rl[i] = log2_std(m.m2, rl[i]);
     }
   }
+  __syncthreads();   // the last step's buffer is free for the later phases
 }
 
 // RN(d / s) from r = RN(1 / s): q0 = RN(d r), the exact residual e = d - q0 s (one fma),
@@ -403,12 +466,12 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
     float (&x)[8][8] = X.v;
     fwht_rows(x, g);
     float rl[8], cl[8];
-    varn(x, rl, cl, a.varn_iters, sm, ph, w, r, g);
+    varn(x, rl, cl, a.varn_iters, sm, w, r, g);
     float* s1dst = reinterpret_cast<float*>(rec + (tensor == 0 ? a.lay.k1 : a.lay.v1));
     if (tensor == 0) {   // keys: s1 per token
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float s1 = expf(rl[i]), r1 = __fdiv_rn(1.f, s1);
+        const float s1 = exp2f(rl[i]), r1 = __fdiv_rn(1.f, s1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[i][e] = div_rn(x[i][e], s1, r1);
         if (g == 0) s1dst[32 * w + 4 * i + r] = s1;
@@ -416,7 +479,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
     } else {             // values: s1 per channel
       float s1[8], r1[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { s1[e] = expf(cl[e]); r1[e] = __fdiv_rn(1.f, s1[e]); }
+      for (int e = 0; e < 8; ++e) { s1[e] = exp2f(cl[e]); r1[e] = __fdiv_rn(1.f, s1[e]); }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
