@@ -53,6 +53,22 @@ __device__ __forceinline__ h8 make8(uint32_t a, uint32_t b, uint32_t c, uint32_t
   return __builtin_bit_cast(h8, v);
 }
 
+// Sum / maximum over the four rows of the wave (lanes l, l ^ 16, l ^ 32, l ^ 48) by lane swaps
+// on the vector unit; each swap returns the (even row, odd row) or (low half, high half) pair in
+// every lane, so all four lanes end with the same bits.
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float s = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // (x & mask) | 0x64006400 in one v_bfi_b32 (the exponent bits of 1024 lie outside every mask
 // used here); written out because the compiler otherwise emits an and and an or.
 __device__ __forceinline__ uint32_t with_exp(uint32_t x, uint32_t mask) {
@@ -260,17 +276,25 @@ struct MfmaDecoder {
         }
       }
     } else {
+      // this lane's 32 channels of scale and offset in 16-byte reads, then used in slot order
       const int c0 = 32 * q;
+      float ksv[32], kmv[32];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const float4 s4 = *reinterpret_cast<const float4*>(kS + c0 + 4 * v);
+        const float4 m4 = *reinterpret_cast<const float4*>(kM + c0 + 4 * v);
+        ksv[4 * v] = s4.x; ksv[4 * v + 1] = s4.y; ksv[4 * v + 2] = s4.z; ksv[4 * v + 3] = s4.w;
+        kmv[4 * v] = m4.x; kmv[4 * v + 1] = m4.y; kmv[4 * v + 2] = m4.z; kmv[4 * v + 3] = m4.w;
+      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int ca = kchan<BITS>(ks, 2 * s), cb = kchan<BITS>(ks, 2 * s + 1);
-          qo[ks][s] = part2(qv[ca] * kS[c0 + ca], qv[cb] * kS[c0 + cb]);
-          bias = fmaf(qv[ca], kM[c0 + ca], fmaf(qv[cb], kM[c0 + cb], bias));
+          qo[ks][s] = part2(qv[ca] * ksv[ca], qv[cb] * ksv[cb]);
+          bias = fmaf(qv[ca], kmv[ca], fmaf(qv[cb], kmv[cb], bias));
         }
-      bias += __shfl_xor(bias, 16);
-      bias += __shfl_xor(bias, 32);
+      bias = rows_sum(bias);
     }
     const h8 qb[4] = {make8(qo[0][0], qo[0][1], qo[0][2], qo[0][3]), make8(qo[1][0], qo[1][1], qo[1][2], qo[1][3]),
                       make8(qo[2][0], qo[2][1], qo[2][2], qo[2][3]), make8(qo[3][0], qo[3][1], qo[3][2], qo[3][3])};
@@ -305,8 +329,7 @@ struct MfmaDecoder {
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[tt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rows_max(mx);
     const float mnew = fmaxf(m_run, mx * sl);
     const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
     m_run = mnew;
@@ -340,8 +363,7 @@ struct MfmaDecoder {
       pm = fmaf(pm, alpha, msum);
     } else if constexpr (MODE == KVARN) {
       g = msum;
-      g += __shfl_xor(g, 16);
-      g += __shfl_xor(g, 32);
+      g = rows_sum(g);
       g = lo_mask ? 0.f : g;           // once per head: on the high column
     }
 
@@ -520,11 +542,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // ---- this wave's matrix-core state
   const int n = lane & 15, q = lane >> 4;
   float l = d.l_run;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = rows_sum(l);
   float pmw = d.pm;
-  pmw += __shfl_xor(pmw, 16);
-  pmw += __shfl_xor(pmw, 32);
+  pmw = rows_sum(pmw);
   float o[8][4];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct)
