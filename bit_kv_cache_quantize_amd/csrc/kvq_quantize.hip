@@ -116,6 +116,15 @@ struct MaxU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { ret
 struct MinF { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
 struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
 
+// The value of another lane by a data-parallel move within each row of 16 lanes.
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_mov(T v) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+  return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Lane l ^ m's value through the LDS permute unit (no vector-ALU instruction: this kernel is
+// bound by vector-ALU issue, so cross-row moves go there unless a move fuses into its use).
 template <typename T>
 __device__ __forceinline__ T shfl_x(T v, int m) {
   if constexpr (sizeof(T) == 4 && !__is_same(T, float)) return (T)__shfl_xor((int)v, m);
@@ -153,13 +162,23 @@ __device__ __forceinline__ void chan_reduce(T (&v)[8], T* buf, int w, int r, int
   for (int e = 0; e < 8; ++e) v[e] = op(op(op(p[0][e], p[1][e]), p[2][e]), p[3][e]);
 }
 
-// Total over the 16 g lanes of a token (identical in all of them).
+// op (minimum or maximum: exact in any order) over the 16 g lanes of a token, identical in
+// all of them. Unsigned maxima take data-parallel row moves, which fuse into the maximum
+// (one instruction per step); float operands go through the permute unit (a row move would
+// stay a separate vector instruction in front of the IEEE minimum / maximum).
 template <typename T, typename Op>
 __device__ __forceinline__ T tok_reduce(T v, Op op) {
-  v = op(v, shfl_x(v, 1));
-  v = op(v, shfl_x(v, 2));
-  v = op(v, shfl_x(v, 4));
-  v = op(v, shfl_x(v, 8));
+  if constexpr (__is_same(T, uint32_t)) {
+    v = op(v, dpp_mov<0xB1>(v));    // quad_perm(1, 0, 3, 2)
+    v = op(v, dpp_mov<0x4E>(v));    // quad_perm(2, 3, 0, 1)
+    v = op(v, dpp_mov<0x141>(v));   // row_half_mirror: the other quad of the half row
+    v = op(v, dpp_mov<0x140>(v));   // row_mirror: the other half of the row
+  } else {
+    v = op(v, shfl_x(v, 1));
+    v = op(v, shfl_x(v, 2));
+    v = op(v, shfl_x(v, 4));
+    v = op(v, shfl_x(v, 8));
+  }
   return v;
 }
 
@@ -228,12 +247,8 @@ __device__ __forceinline__ Mom mom8(const float (&t)[8]) {
 }
 
 template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-template <int CTRL>
 __device__ __forceinline__ Mom merge_dpp(Mom m, float half_n) {
-  return merge(m, Mom{dpp<CTRL>(m.mean), dpp<CTRL>(m.m2)}, half_n);
+  return merge(m, Mom{dpp_mov<CTRL>(m.mean), dpp_mov<CTRL>(m.m2)}, half_n);
 }
 // Partner rows by lane swaps: rows r and r ^ 1 (X16) or r ^ 2 (X32) of the wave; each swap
 // returns the (lower, upper) pair in every lane.
@@ -332,6 +347,28 @@ __device__ __forceinline__ void varn(const float (&x)[8][8], float (&rl)[8], flo
   __syncthreads();   // the last step's buffer is free for the later phases
 }
 
+// The two planes of eight 3-bit codes given as the nibbles of v (code e in bits 4e..4e+2, bit
+// 4e+3 clear): lo2 = the low two bits of code e at bit 2e (bits 0..15 valid), hi1 = bit 2 of code
+// e at bit e (bits 0..7 valid); the bits above are left unspecified. Each step keeps every
+// other field in place and moves its neighbour down next to it, (a & m) | (b & ~m) being one
+// bit-field insert (written out: the compiler otherwise rewrites the chain into more
+// instructions from the known-zero bits of the codes).
+template <uint32_t M>
+__device__ __forceinline__ uint32_t bsel(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(M), "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ void planes3(uint32_t v, uint32_t& lo2, uint32_t& hi1) {
+  const uint32_t v2 = v >> 2;                    // also: bit 2 of code e at bit 4e
+  uint32_t y = bsel<0x03030303u>(v, v2);          // byte k, bits 0..3: codes 2k, 2k+1
+  y = bsel<0x000F000Fu>(y, y >> 4);               // half-word m, bits 0..7: codes 4m .. 4m+3
+  lo2 = bsel<0x000000FFu>(y, y >> 8);             // bits 0..15: codes 0 .. 7
+  uint32_t z = bsel<0x01010101u>(v2, v2 >> 3);    // byte k, bits 0..1
+  z = bsel<0x00030003u>(z, z >> 6);               // half-word m, bits 0..3
+  hi1 = bsel<0x0000000Fu>(z, z >> 12);            // bits 0..7
+}
+
 // RN(d / s) from r = RN(1 / s): q0 = RN(d r), the exact residual e = d - q0 s (one fma),
 // then RN(q0 + e r). With a correctly rounded reciprocal this correction step returns the
 // correctly rounded quotient (Markstein's theorem; no overflow or underflow occurs for
@@ -379,6 +416,28 @@ __device__ __forceinline__ VecStats stats_of(float lo, float hi, float amax) {
     v.off = lo;
   }
   return v;
+}
+
+// Lane addr / 4's copy of v, through the LDS permute unit (no vector-ALU instruction).
+__device__ __forceinline__ float bperm(int addr, float v) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
+}
+// The statistics of another lane's vector (off follows from the others).
+template <int MODE>
+__device__ __forceinline__ VecStats bperm_stats(int addr, const VecStats& v) {
+  VecStats o;
+  o.sa = bperm(addr, v.sa);
+  o.sb = bperm(addr, v.sb);
+  o.rc = bperm(addr, v.rc);
+  o.off = MODE == NUQ ? o.sa : (MODE == SYM ? 0.f : o.sb);
+  return o;
+}
+// x[k] for a lane-dependent k in 0..7 (three levels of selects on the bits of k).
+__device__ __forceinline__ float sel8(const float (&x)[8], int k) {
+  const bool b0 = k & 1, b1 = k & 2, b2 = k & 4;
+  const float a0 = b0 ? x[1] : x[0], a1 = b0 ? x[3] : x[2], a2 = b0 ? x[5] : x[4], a3 = b0 ? x[7] : x[6];
+  const float c0 = b1 ? a1 : a0, c1 = b1 ? a3 : a2;
+  return b2 ? c1 : c0;
 }
 
 // Code of one element from d = x - off: RTN/KVarN clamp(rint((x - m) / s)), NUQ argmin over
@@ -624,14 +683,20 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
       dh[0] = make_float4(hi[0], hi[1], hi[2], hi[3]); dh[1] = make_float4(hi[4], hi[5], hi[6], hi[7]);
     }
     __syncthreads();
+    // the statistics (their divisions are the costly part) of channels 8g + 2r and 8g + 2r + 1
+    // are derived in row r of the wave; the other rows' come by lane permutes
+    VecStats own[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = 8 * g + e;
+    for (int k = 0; k < 2; ++k) {
+      const int c = 8 * g + 2 * r + k;
       const float l = fminf(fminf(fminf(sm.rlo[0][c], sm.rlo[1][c]), sm.rlo[2][c]), sm.rlo[3][c]);
       const float u = fmaxf(fmaxf(fmaxf(sm.rhi[0][c], sm.rhi[1][c]), sm.rhi[2][c]), sm.rhi[3][c]);
-      vs[e] = stats_of<MODE, BITS>(l, u, u);
+      own[k] = stats_of<MODE, BITS>(l, u, u);
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vs[e] = bperm_stats<MODE>(4 * g + 64 * (e >> 1), own[e & 1]);
   } else {
+    float lot[8], hit[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float lo = INFINITY, hi = -INFINITY;
@@ -650,10 +715,14 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
           hi = fmaxf(hi, x);
         }
       }
-      lo = tok_reduce(lo, MinF());
-      hi = tok_reduce(hi, MaxF());
-      vs[i] = stats_of<MODE, BITS>(lo, hi, hi);
+      lot[i] = tok_reduce(lo, MinF());
+      hit[i] = tok_reduce(hi, MaxF());
     }
+    // the statistics of token t_i are derived in lanes g = i, 8 + i of the row; the other
+    // lanes take them by lane permutes
+    const VecStats own = stats_of<MODE, BITS>(sel8(lot, g & 7), sel8(hit, g & 7), sel8(hit, g & 7));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vs[i] = bperm_stats<MODE>(64 * r + 4 * i, own);
   }
 
   // ---- statistics out
@@ -708,12 +777,10 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
         for (int e = 0; e < 8; ++e) v |= c[e] << (2 * e);
         *reinterpret_cast<uint16_t*>(row + 2 * g) = (uint16_t)v;
       } else {
-        uint32_t lo2 = 0, hi1 = 0;
+        uint32_t v = 0, lo2, hi1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          lo2 |= (c[e] & 3u) << (2 * e);
-          hi1 |= ((c[e] >> 2) & 1u) << e;
-        }
+        for (int e = 0; e < 8; ++e) v |= c[e] << (4 * e);
+        planes3(v, lo2, hi1);
         *reinterpret_cast<uint16_t*>(row + 2 * g) = (uint16_t)lo2;
         row[32 + g] = (uint8_t)hi1;
       }
@@ -764,14 +831,16 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
         uint32_t lo2[4], hi1[2] = {0u, 0u};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          uint32_t v = 0;
+          uint32_t l[2], h[2];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const uint32_t cc = code(16 * k + e);
-            v |= (cc & 3u) << (2 * e);
-            hi1[k >> 1] |= ((cc >> 2) & 1u) << (16 * (k & 1) + e);
+          for (int hh = 0; hh < 2; ++hh) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v |= code(16 * k + 8 * hh + e) << (4 * e);
+            planes3(v, l[hh], h[hh]);
           }
-          lo2[k] = v;
+          lo2[k] = (l[0] & 0xFFFFu) | (l[1] << 16);
+          hi1[k >> 1] |= ((h[0] & 0xFFu) | ((h[1] & 0xFFu) << 8)) << (16 * (k & 1));
         }
         *reinterpret_cast<uint4*>(dst) = make_uint4(lo2[0], lo2[1], lo2[2], lo2[3]);
         *reinterpret_cast<uint2*>(dst + 16) = make_uint2(hi1[0], hi1[1]);
