@@ -38,6 +38,8 @@
 namespace kvq {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 constexpr float kInvSqrt128 = 0.08838834764831845f;
@@ -489,11 +491,24 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
     const __half* in = (tensor ? a.v_in : a.k_in) + unit * (size_t)a.n_new * kD;
     const __half* tl = a.tail + unit * (2 * kT * kD) + (size_t)tensor * kT * kD;
     uint4 raw[8];
+    if (j > 0 || a.t0 == 0) {
+      // (uniform) every row from the new input: a buffer resource over the block's 128 rows,
+      // the lane's offset in a register and each row's offset in the scalar offset operand
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<__half*>(in + ((size_t)j * kT - a.t0) * kD), (short)0, kT * kD * 2, 0x00020000);
+      const uint32_t lo = (uint32_t)(((32 * w + r) * kD + 8 * g) * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = 32 * w + 4 * i + r;
-      const __half* src = (j == 0 && t < a.t0) ? tl + (size_t)t * kD : in + ((size_t)j * kT + t - a.t0) * kD;
-      raw[i] = *reinterpret_cast<const uint4*>(src + 8 * g);
+      for (int i = 0; i < 8; ++i) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, lo, 4 * i * kD * 2, 0);
+        raw[i] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = 32 * w + 4 * i + r;
+        const __half* src = t < a.t0 ? tl + (size_t)t * kD : in + ((size_t)t - a.t0) * kD;
+        raw[i] = *reinterpret_cast<const uint4*>(src + 8 * g);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
