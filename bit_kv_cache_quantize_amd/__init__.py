@@ -183,11 +183,14 @@ class KVCache:
         self.buf = raw[pad:pad + self.nbytes]
         self._raw = raw
         self.handle = kvq_cache_init(cfg, self.buf, self.nbytes, stream)
+        # held by the object: at interpreter exit the module's globals may be gone before it
+        self._destroy = lib.kvq_cache_destroy
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
-            kvq_cache_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h and destroy is not None:
+            destroy(h)
             self.handle = None
 
     def codebook_load(self, layer, kv_head, which, codebook, stream=None):
