@@ -434,12 +434,19 @@ __device__ __forceinline__ VecStats bperm_stats(int addr, const VecStats& v) {
   o.off = MODE == NUQ ? o.sa : (MODE == SYM ? 0.f : o.sb);
   return o;
 }
-// x[k] for a lane-dependent k in 0..7 (three levels of selects on the bits of k).
+// x[k] for a lane-dependent k in 0..7: three levels of per-lane selects on the bits of k, each a
+// byte permute whose selector takes all four bytes of one operand (0x03020100: the second,
+// 0x07060504: the first). Written this way because the compiler turns plain selects here into
+// an indexed load from a private-memory copy of x.
 __device__ __forceinline__ float sel8(const float (&x)[8], int k) {
-  const bool b0 = k & 1, b1 = k & 2, b2 = k & 4;
-  const float a0 = b0 ? x[1] : x[0], a1 = b0 ? x[3] : x[2], a2 = b0 ? x[5] : x[4], a3 = b0 ? x[7] : x[6];
-  const float c0 = b1 ? a1 : a0, c1 = b1 ? a3 : a2;
-  return b2 ? c1 : c0;
+  const uint32_t s0 = (k & 1) ? 0x07060504u : 0x03020100u, s1 = (k & 2) ? 0x07060504u : 0x03020100u,
+                 s2 = (k & 4) ? 0x07060504u : 0x03020100u;
+  auto pick = [](uint32_t s, float a, float b) {   // b where the selector takes the first operand
+    return __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), s));
+  };
+  const float a0 = pick(s0, x[0], x[1]), a1 = pick(s0, x[2], x[3]);
+  const float a2 = pick(s0, x[4], x[5]), a3 = pick(s0, x[6], x[7]);
+  return pick(s2, pick(s1, a0, a1), pick(s1, a2, a3));
 }
 
 // Code of one element from d = x - off: RTN/KVarN clamp(rint((x - m) / s)), NUQ argmin over

@@ -176,3 +176,35 @@ def test_strerror():
     assert K.kvq_strerror(0) == "ok"
     for s in (-1, -2, -3, -4, -5):
         assert K.kvq_strerror(s) not in ("ok", "unknown status")
+
+
+LLVM_BIN = "/opt/rocm/llvm/bin"
+HOT_KERNELS = ("quantize_kernel", "decode_tab_kernel", "decode_mfma_kernel", "combine_kernel", "tail_kernel")
+
+
+@pytest.mark.skipif(not os.path.exists(os.path.join(LLVM_BIN, "llvm-readelf")), reason="ROCm LLVM tools not installed")
+def test_hot_path_kernels_use_no_private_memory(tmp_path):
+    """The kernels of the benchmarked paths keep every value in registers or LDS: a private
+    (scratch) segment, from a spill or from an array indexed per lane, would add per-lane
+    memory traffic to an HBM-bound path. Read from the gfx950 code objects of the built
+    library (kernel metadata)."""
+    import shutil
+    import subprocess
+    so = tmp_path / "libkvq.so"
+    shutil.copy(K.LIB_PATH, so)
+    subprocess.run([os.path.join(LLVM_BIN, "llvm-objdump"), "--offloading", so.name], cwd=tmp_path,
+                   check=True, capture_output=True)
+    sizes = {}
+    for co in sorted(tmp_path.glob("libkvq.so.*gfx950")):
+        notes = subprocess.run([os.path.join(LLVM_BIN, "llvm-readelf"), "--notes", str(co)],
+                               check=True, capture_output=True, text=True).stdout
+        name = None
+        for line in notes.splitlines():
+            line = line.strip()
+            if line.startswith(".name:"):
+                name = line.split()[-1]          # the kernel's own name follows its argument names
+            elif line.startswith(".private_segment_fixed_size:") and name:
+                sizes[name] = int(line.split()[-1])
+    hot = {n: v for n, v in sizes.items() if any(k in n for k in HOT_KERNELS)}
+    assert len(hot) >= 20, sorted(sizes)
+    assert {n: v for n, v in hot.items() if v} == {}
