@@ -128,9 +128,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // Merge the split partials of one (sequence, query head) with the log-sum-exp rule.
-// The (m, l) pairs of all splits are staged in LDS first, so the loads of the per-channel
-// partials are independent and stay in flight together.
+// Up to S splits: every partial is loaded up front (indices past the split count read the last
+// partial again and are not used), so all loads are in flight together, one memory round trip;
+// the merge then runs in split order.
+template <int S>
 __global__ __launch_bounds__(128) void combine_kernel(const float* part_all, float* out, int Hq, int splits) {
+  const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const size_t row = (size_t)b * Hq + hq;
+  const float* part = part_all + row * splits * kPartStride;
+  float m[S], l[S], o[S];
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp) {
+    const float* p = part + min(sp, splits - 1) * kPartStride;
+    m[sp] = p[0];
+    l[sp] = p[1];
+    o[sp] = p[2 + c];
+  }
+  // branch-free, so that no load is deferred into a conditional: a repeated last partial does not
+  // change the maximum, and it enters the sums with weight 0 (an exact no-op)
+  float M = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp) M = fmaxf(M, m[sp]);
+  float L = 0.f, acc = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp) {
+    const float wgt = (sp >= splits || m[sp] == -INFINITY) ? 0.f : exp2f(m[sp] - M);
+    L = fmaf(wgt, l[sp], L);
+    acc = fmaf(wgt, o[sp], acc);
+  }
+  out[row * kD + c] = acc / L;
+}
+
+// The same merge for any split count: the (m, l) pairs of all splits are staged in LDS first,
+// so the loads of the per-channel partials are independent and stay in flight together.
+__global__ __launch_bounds__(128) void combine_kernel_lds(const float* part_all, float* out, int Hq, int splits) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_l[kMaxSplits];
   const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
@@ -204,7 +235,12 @@ hipError_t launch_decode(int mode, int bits, int group, int rope, const DecodeAr
 }
 
 hipError_t launch_combine(const float* part, float* out, int Hq, int splits, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(Hq, batch), dim3(128), 0, s, part, out, Hq, splits);
+  const dim3 grid(Hq, batch), block(128);
+  if (splits <= 4) hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, s, part, out, Hq, splits);
+  else if (splits <= 8) hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, s, part, out, Hq, splits);
+  else if (splits <= 16) hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, s, part, out, Hq, splits);
+  else if (splits <= 32) hipLaunchKernelGGL(combine_kernel<32>, grid, block, 0, s, part, out, Hq, splits);
+  else hipLaunchKernelGGL(combine_kernel_lds, grid, block, 0, s, part, out, Hq, splits);
   return hipGetLastError();
 }
 
