@@ -165,6 +165,19 @@ def test_split_count_invariance(K):
         assert np.max(np.abs(o - outs[0])) <= 1e-5 * np.max(np.abs(outs[0]))
 
 
+def test_split_count_invariance_across_merge_variants(K):
+    """64 full blocks plus a tail, split 1 .. 64 ways: the split merge loads all partials up
+    front for up to 4, 8, 16 or 32 splits and stages them in LDS beyond; every variant, and
+    both sides of each bound, gives the single-split result (and the oracle's)."""
+    wl = small("c1_single_head_2k_rtn4", batch=1, n_q_heads=2, n_kv_heads=1)
+    outs = []
+    for s in (1, 4, 5, 8, 9, 16, 17, 32, 33, 64):
+        _, out, _ = run_case(K, wl, [64 * 128 + 5], splits=s, check_records=(s == 1))
+        outs.append(out.cpu().numpy())
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 1e-5 * np.max(np.abs(outs[0]))
+
+
 def test_determinism(K):
     wl = small("c2_llama7b_layer_32k_nuq3", n_q_heads=4, n_kv_heads=2, batch=2)
     a, oa, _ = run_case(K, wl, [700])
