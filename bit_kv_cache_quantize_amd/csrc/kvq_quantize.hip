@@ -18,16 +18,20 @@
 // the library is built with -ffp-contract=off and correctly rounded division),
 // rintf (round half even) and fp16 round-to-nearest-even, so that codes and
 // scales are reproducible. The one exception is KVarN's variance normalisation
-// (hardware exp / log), whose scales are specified to a relative tolerance.
+// (hardware exp2 / log2), whose scales are specified to a relative tolerance.
 //
 // The 128 x 128 tile stays in registers: wave w holds tokens 32w .. 32w+31 and
 // lane (r = lane >> 4, g = lane & 15) holds tokens t_i = 32w + 4i + r (i = 0..7)
-// at channels 8g .. 8g+7, widened to fp32. Each 16-byte load covers 8 channels of
-// one token, so a wave reads four consecutive 256-byte rows per instruction.
+// at channels 8g .. 8g+7, as fp16 pairs widened on use (KVarN: fp32). Each 16-byte
+// load covers 8 channels of one token, so a wave reads four consecutive 256-byte
+// rows per instruction.
 //   per-channel reductions: the lane's 8 tokens, the four r lanes (xor 16, 32),
 //     then the four waves through LDS (all threads combine the four partials in
 //     the same order, so every holder of a channel gets the same value);
 //   per-token reductions: the lane's 8 channels, then the 16 g lanes (xor 1..8).
+// The kernel is bound by vector-ALU issue: cross-lane moves use the LDS permute
+// unit unless a row move fuses into its use, and a vector's statistics (their
+// divisions) are derived once, in an owner lane, and permuted to the others.
 // Key codes are packed straight from registers (a lane holds 8 consecutive
 // channels of a token row); value codes go through an LDS tile for the
 // channel-major layout. Outlier lists are built with a per-row bitmask in LDS:
