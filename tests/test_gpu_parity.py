@@ -108,6 +108,10 @@ CASES = {
     "kvarn3_g1": (small("c3_kvarn_gqa_b16_8k", bits=3, batch=1, n_q_heads=2, n_kv_heads=2), [300]),
     "kvarn4_g2_iters3": (small("c3_kvarn_gqa_b16_8k", bits=4, varn_iters=3, batch=1, n_q_heads=4, n_kv_heads=2),
                          [70, 200]),
+    # VarN with no iteration (s1 = 1: RTN of the rotated block) and with one (a single pass
+    # through the alternating cross-wave buffers)
+    "kvarn2_g4_iters0": (small("c3_kvarn_gqa_b16_8k", varn_iters=0, batch=1, n_q_heads=4, n_kv_heads=1), [256, 3]),
+    "kvarn2_g4_iters1": (small("c3_kvarn_gqa_b16_8k", varn_iters=1, batch=1, n_q_heads=4, n_kv_heads=1), [130, 126]),
     "sym4_g4": (small("c4_blog_int4_32l_b32_32k", n_layers=1, batch=2, n_q_heads=8, n_kv_heads=2), [512]),
     "sym4_rope_out1_g1": (small("c4_blog_int4_32l_b32_32k", n_layers=1, batch=1, n_q_heads=2, n_kv_heads=2,
                                 pre_rope=1, outliers_per_vec=1), [257]),
