@@ -59,15 +59,16 @@ struct Smem {
 };
 
 // Key of the top-k |x| selection: larger magnitude first, then lower element index e
-// (magnitude bits from bit 8 up, 127 - e in bits 1..7; (magnitude, index) is unique); a key
-// gives back its element's position within the vector (the outlier lists take the element's
-// signed fp16 value from the input rows).
+// (magnitude bits from bit 8 up, 127 - e in bits 1..7, the sign in bit 0, which never
+// decides since (magnitude, index) is unique); a key gives back its element's position
+// within the vector and, for fp16 tiles, the element's exact fp16 bits.
 __device__ __forceinline__ uint32_t mag_key(float x, int e) {
   // fp32 form (KVarN tiles, which never select outliers): magnitude bits above bit 13
   const uint32_t u = __float_as_uint(x);
-  return (((u & 0x7fffffffu) >> 13) << 8) | ((uint32_t)(127 - e) << 1);
+  return (((u & 0x7fffffffu) >> 13) << 8) | ((uint32_t)(127 - e) << 1) | (u >> 31);
 }
 __device__ __forceinline__ uint32_t key_index(uint32_t key) { return 127u - ((key >> 1) & 127u); }
+__device__ __forceinline__ uint16_t key_bits(uint32_t key) { return (uint16_t)(((key & 1u) << 15) | ((key >> 8) & 0x7fffu)); }
 
 // The block tile of one lane: 8 tokens x 8 channels. Non-KVarN modes keep the fp16
 // input bits (two channels per register) and widen on use, which halves the live
@@ -106,14 +107,14 @@ template <> struct Tile<false> {
   }
   __device__ __forceinline__ uint32_t key(int i, int e, int idx) const {
     const uint32_t h = (e & 1) ? v[i][e >> 1] >> 16 : v[i][e >> 1] & 0xffffu;
-    return ((h & 0x7fffu) << 8) | ((uint32_t)(127 - idx) << 1);
+    return ((h & 0x7fffu) << 8) | ((uint32_t)(127 - idx) << 1) | (h >> 15);
   }
-  // The same key from one byte permutation of the sign-cleared pair: byte 0 = index byte k of
-  // iw, bytes 1-2 = the element's fp16 magnitude, byte 3 = 0 (the clearing of a register
-  // serves both of its elements).
+  // The same key from a byte permutation: byte 0 = index byte k of iw, bytes 1-2 = the
+  // element's fp16 bits (its sign lands in bit 23), byte 3 = 0; then the sign moves to bit 0.
   __device__ __forceinline__ uint32_t key4(int i, int e, uint32_t iw, int k) const {
     const uint32_t sel = (uint32_t)k | ((4u + 2u * (e & 1)) << 8) | ((5u + 2u * (e & 1)) << 16) | (0x0cu << 24);
-    return __builtin_amdgcn_perm(v[i][e >> 1] & 0x7fff7fffu, iw, sel);
+    const uint32_t t = __builtin_amdgcn_perm(v[i][e >> 1], iw, sel);
+    return (t & 0x007fffffu) | (t >> 23);
   }
 };
 
@@ -497,9 +498,9 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
 
   // ---- load the block: rows < t0 of the first block come from the fp16 tail
   Tile<MODE == KVARN> X;
-  const __half* in = (tensor ? a.v_in : a.k_in) + unit * (size_t)a.n_new * kD;
-  const __half* tl = a.tail + unit * (2 * kT * kD) + (size_t)tensor * kT * kD;
   {
+    const __half* in = (tensor ? a.v_in : a.k_in) + unit * (size_t)a.n_new * kD;
+    const __half* tl = a.tail + unit * (2 * kT * kD) + (size_t)tensor * kT * kD;
     uint4 raw[8];
     if (j > 0 || a.t0 == 0) {
       // (uniform) every row from the new input: a buffer resource over the block's 128 rows,
@@ -879,17 +880,18 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
   if (KO != 0) {
     __syncthreads();                                   // okey complete, omask cleared
     const int n_ent = 128 * k_out;
-    auto place = [&](int n, int& row, int& col, int& t, int& c) {
+    auto place = [&](int n, int& row, int& col, uint32_t& key) {
       const int v = n & 127, p = n >> 7;
-      const int e = (int)key_index(sm.okey[v][p]);
-      t = per_chan ? e : v;
-      c = per_chan ? v : e;
+      key = sm.okey[v][p];
+      const int e = (int)key_index(key);
+      const int t = per_chan ? e : v, c = per_chan ? v : e;
       row = tensor == 0 ? t : c;
       col = tensor == 0 ? c : t;
     };
     for (int n = tid; n < n_ent; n += kThreads) {
-      int row, col, t, c;
-      place(n, row, col, t, c);
+      int row, col;
+      uint32_t key;
+      place(n, row, col, key);
       atomicOr(&sm.omask[row][col >> 5], 1u << (col & 31));
     }
     __syncthreads();
@@ -915,11 +917,9 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
     uint8_t* idx = rec + (tensor == 0 ? a.lay.ko_idx : a.lay.vo_idx);
     if (tid <= 128) ptr[tid] = sm.optr[tid];
     for (int n = tid; n < n_ent; n += kThreads) {
-      int row, col, t, c;
-      place(n, row, col, t, c);
-      // the element's fp16 input bits, exactly (token t of the block: a tail row or a new one)
-      const __half* src = (j == 0 && t < a.t0) ? tl + (size_t)t * kD : in + ((size_t)j * kT + t - a.t0) * kD;
-      const uint16_t bits = reinterpret_cast<const uint16_t*>(src)[c];
+      int row, col;
+      uint32_t key;
+      place(n, row, col, key);
       int pos = sm.optr[row];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -927,7 +927,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
         const int lim = col - 32 * d;   // bits of word d below col
         pos += lim >= 32 ? __popc(m) : (lim > 0 ? __popc(m & ((1u << lim) - 1u)) : 0);
       }
-      val[pos] = bits;
+      val[pos] = key_bits(key);   // the element's fp16 input bits, exactly
       idx[pos] = (uint8_t)col;
     }
   }
