@@ -305,8 +305,8 @@ def cpu_baseline(wl, heads):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(each box has one MI355X); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the hot path runs on one MI355X); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     import synth

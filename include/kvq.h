@@ -101,7 +101,7 @@ void kvq_cache_destroy(kvq_cache cache);
  * Load the NUQ codebook of one (layer, kv head) for keys (which = 0) or values
  * (which = 1). host_codebook: n_entries = 2^bits fp32 values, finite, within
  * [-1, 1], ascending with consecutive entries at least 2^-21 apart (KVQuant notes
- * 3.3: one datatype per layer and head; this build keeps one per (layer, kv head,
+ * 3.3: one datatype per layer and head; the library keeps one per (layer, kv head,
  * K/V)). The gap guarantees that the fp32 argmin of |u - C_j| (ties to the smaller
  * j) is decided between the two entries around u; the library derives the decision
  * threshold between each pair of consecutive entries on the host and uploads it with

@@ -85,7 +85,7 @@ def outlier_mask(x16: np.ndarray, k: int, axis: int) -> np.ndarray:
     """Boolean mask of the k largest |x| along ``axis``; ties go to the lower index.
 
     [KVQ] 3.4 keeps about 1% of each vector in fp16. The notes use an offline
-    per-channel threshold; with no calibration data this build selects, per
+    per-channel threshold; with no calibration data the selection takes, per
     vector, the k entries of largest magnitude (reading: per-vector top-k).
     """
     mask = np.zeros(x16.shape, bool)
