@@ -13,7 +13,7 @@ import os
 # libkvq.so makes the library bind to that same runtime, so device memory and
 # streams from torch are valid for the kernels. Loaded the other way round, the
 # process would hold two HIP runtimes.
-import torch  # noqa: F401
+import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
@@ -171,12 +171,29 @@ def kvq_last_error() -> str:
     return lib.kvq_last_error().decode()
 
 
+def check_tensors(device, named):
+    """Raise ValueError unless every (name, tensor, dtype) is a contiguous tensor of that
+    dtype on ``device``: the C ABI takes bare pointers and could not tell."""
+    dev = torch.device(device)
+    for name, t, dtype in named:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if t.device.type != dev.type or (dev.index is not None and t.device.index != dev.index):
+            raise ValueError(f"{name} must be on {dev}, got {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
 class KVCache:
     """A cache handle over a torch-allocated device buffer (the buffer lives as long as this object)."""
 
     def __init__(self, cfg: kvq_config, device="cuda", stream=None):
-        import torch
         self.cfg = cfg
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.nbytes = kvq_cache_bytes(cfg)
         raw = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device)
         pad = (-raw.data_ptr()) % 256
@@ -197,15 +214,18 @@ class KVCache:
         kvq_codebook_load(self.handle, layer, kv_head, which, codebook, stream)
 
     def append(self, layer, k, v, stream=None):
-        assert k.dtype == v.dtype and k.is_contiguous() and v.is_contiguous()
-        assert k.shape == v.shape and k.shape[0] == self.cfg.batch and k.shape[1] == self.cfg.n_kv_heads
-        assert k.shape[3] == KVQ_HEAD_DIM
+        check_tensors(self.device, [("k", k, torch.float16), ("v", v, torch.float16)])
+        shape = (self.cfg.batch, self.cfg.n_kv_heads)
+        if k.dim() != 4 or tuple(k.shape[:2]) != shape or k.shape[3] != KVQ_HEAD_DIM or k.shape != v.shape:
+            raise ValueError(f"k and v must both be [{shape[0]}][{shape[1]}][n_new][{KVQ_HEAD_DIM}], got "
+                             f"{tuple(k.shape)} and {tuple(v.shape)}")
         kvq_quantize_append(self.handle, layer, k, v, k.shape[2], stream)
 
     def decode(self, layer, q, out, softmax_scale=0.0, stream=None):
-        assert q.is_contiguous() and out.is_contiguous()
-        assert tuple(q.shape) == (self.cfg.batch, self.cfg.n_q_heads, KVQ_HEAD_DIM)
-        assert tuple(out.shape) == tuple(q.shape)
+        check_tensors(self.device, [("q", q, torch.float16), ("out", out, torch.float32)])
+        shape = (self.cfg.batch, self.cfg.n_q_heads, KVQ_HEAD_DIM)
+        if tuple(q.shape) != shape or tuple(out.shape) != shape:
+            raise ValueError(f"q and out must be {list(shape)}, got {tuple(q.shape)} and {tuple(out.shape)}")
         kvq_decode_attn(self.handle, layer, q, out, softmax_scale, stream)
 
     def length(self, layer):

@@ -24,11 +24,19 @@ Readings of the pages where they are silent or inconsistent are listed in the
 design notes; the ones that change arithmetic are repeated at the function
 that implements them.
 
+The oracle computes logical results only: codes as [token][channel] arrays,
+per-vector statistics, s1, and outlier lists of (token, channel, fp16 bits).
+How a library stores them (byte order of packed rows, record segments, sparse
+pointer arrays) is not modelled here; ``pack_codes`` is the one storage step
+kept, because the bit packing itself (4-bit nibbles, 2-bit crumbs, 48-byte
+3-bit rows) is what the pages describe.
+
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 except VarN's agreement with the KVarN paper's own algorithm, which the
 summary page does not print: VarN is pinned only by invariants (row std = 1
 after the final token step, exact reconstruction, column-scale equivariance,
-shrinking dispersion). That part is "parity unpinned" against the paper.
+shrinking dispersion, a finite fixed point on constant blocks). That part is
+"parity unpinned" against the paper.
 """
 from __future__ import annotations
 
@@ -73,7 +81,8 @@ def f16_magnitude(x16: np.ndarray) -> np.ndarray:
 
 
 def n_outliers(fraction: float, vec_len: int = 128) -> int:
-    """Outliers per vector: round-half-even(fraction * length); 1% of 128 -> 1."""
+    """Outliers per vector: round-half-even(fraction * length) ([KVQ] 3.4: about 1% of
+    each vector; 1% of 128 elements is 1.28, so one outlier per vector)."""
     return int(np.rint(fraction * vec_len))
 
 
@@ -213,13 +222,25 @@ def hadamard_rotate(x: np.ndarray) -> np.ndarray:
     return (np.asarray(x, np.float64) @ _H128) / math.sqrt(D)
 
 
+def zero_spread(sigma: np.ndarray, mag: np.ndarray) -> np.ndarray:
+    """True where a vector's deviation is zero up to the rounding of its fp64 mean.
+
+    A constant vector has no spread to normalise; numpy's std of one returns about
+    1e-16 of its magnitude rather than exactly 0 (the mean is rounded), which would
+    send the log-scale to -37 and the next steps to overflow. Deviations at most
+    2^-40 of the vector's largest |x| count as zero.
+    """
+    return sigma <= np.ldexp(1.0, -40) * mag
+
+
 def varn(y: np.ndarray, iters: int):
     """Dual-axis variance normalisation in the log-std domain (fp64).
 
     Per iteration: normalise channels, then tokens. X~ = Y * exp(-r_t - c_ch);
     c_ch += log(std over tokens of X~[:, ch]); X~ is formed again;
     r_t += log(std over channels of X~[t, :]). Population std (mean removed).
-    A zero std leaves its log-scale unchanged. Returns (r[T], c[D]).
+    A vector with zero spread (``zero_spread``) leaves its log-scale unchanged.
+    Returns (r[T], c[D]).
     Reading: channel step first, then token step, ``iters`` full iterations.
     """
     y = np.asarray(y, np.float64)
@@ -228,10 +249,12 @@ def varn(y: np.ndarray, iters: int):
     for _ in range(iters):
         xt = y * np.exp(-r[:, None] - c[None, :])
         sc = xt.std(axis=0)
-        c = c + np.where(sc > 0, np.log(np.where(sc > 0, sc, 1.0)), 0.0)
+        flat = zero_spread(sc, np.abs(xt).max(axis=0))
+        c = c + np.where(flat, 0.0, np.log(np.where(flat, 1.0, sc)))
         xt = y * np.exp(-r[:, None] - c[None, :])
         st = xt.std(axis=1)
-        r = r + np.where(st > 0, np.log(np.where(st > 0, st, 1.0)), 0.0)
+        flat = zero_spread(st, np.abs(xt).max(axis=1))
+        r = r + np.where(flat, 0.0, np.log(np.where(flat, 1.0, st)))
     return r, c
 
 
@@ -259,11 +282,12 @@ class Config:
 
 
 # ---------------------------------------------------------------------------
-# Quantizing one 128-token block (the per-block record)
+# Quantizing one 128-token block
 # ---------------------------------------------------------------------------
 
 @dataclass
 class Block:
+    """The logical content of one quantized block (no storage layout)."""
     kcodes: np.ndarray          # [T][D] u8, code of key (token t, channel c)
     vcodes: np.ndarray          # [T][D] u8, code of value (token t, channel c)
     kstat: tuple                # RTN/KVARN (s[D], m[D]); NUQ (z[D], h[D]); SYM (s16[D],)
@@ -276,6 +300,14 @@ class Block:
     vout: np.ndarray | None = None
 
 
+def outlier_entries(mask: np.ndarray, x16: np.ndarray) -> np.ndarray:
+    """The sparse part as a list of (token, channel, fp16 bits) rows sorted by (token,
+    channel): the content of a CSR matrix by token row ([KVQ] 3.4)."""
+    t, c = np.nonzero(mask)
+    bits = np.asarray(x16, np.float16)[t, c].view(np.uint16).astype(np.int64)
+    return np.stack([t, c, bits], axis=1).astype(np.int64).reshape(-1, 3)
+
+
 def quantize_block(k16: np.ndarray, v16: np.ndarray, cfg: Config,
                    cb_k: np.ndarray | None = None, cb_v: np.ndarray | None = None) -> Block:
     """Quantize one block of 128 tokens x 128 channels of keys and values.
@@ -285,11 +317,16 @@ def quantize_block(k16: np.ndarray, v16: np.ndarray, cfg: Config,
     per token over channels ([KVQ] 3.6), except symmetric int4, whose values are
     also grouped along the sequence ([BLOG] 2.1: 128-element blocks in the
     sequence direction).
+
+    Outliers ([KVQ] 3.4, Algorithm 1 step 1 and the appendix step 1): the k
+    largest |x| of each vector go to the sparse part in fp16, the dense matrix
+    holds 0 at their positions, the statistics are taken over the other entries
+    (Algorithm 1, step 4) and the dense matrix is quantized as a whole, so an
+    outlier position carries the code of 0.0.
     """
     k16 = np.asarray(k16, np.float16).reshape(T, D)
     v16 = np.asarray(v16, np.float16).reshape(T, D)
     b, mode, ko = cfg.bits, cfg.mode, cfg.outliers_per_vec
-    out = {}
     if mode == MODE_KVARN:
         yk = hadamard_rotate(k16.astype(np.float64))
         yv = hadamard_rotate(v16.astype(np.float64))
@@ -306,13 +343,13 @@ def quantize_block(k16: np.ndarray, v16: np.ndarray, cfg: Config,
                      rtn_codes(vx, vs[:, None], vm[:, None], b),
                      (ks, km), (vs, vm), ks1=ks1, vs1=vs1)
 
-    kx = k16.astype(np.float32)
-    vx = v16.astype(np.float32)
     kmask = outlier_mask(k16, ko, axis=0)      # per channel, over tokens
-    vmask = outlier_mask(v16, ko, axis=1)      # per token, over channels
-    if mode == MODE_SYM_INT4:
-        vmask = outlier_mask(v16, ko, axis=0)  # values grouped per channel too
+    vaxis = 0 if mode == MODE_SYM_INT4 else 1  # values per token (sym-int4: per channel)
+    vmask = outlier_mask(v16, ko, axis=vaxis)
     kkeep, vkeep = ~kmask, ~vmask
+    # the dense part: outlier positions hold 0
+    kx = np.where(kmask, np.float32(0), k16.astype(np.float32))
+    vx = np.where(vmask, np.float32(0), v16.astype(np.float32))
     if mode == MODE_RTN:
         ks, km = rtn_stats(kx, kkeep, b, axis=0)
         vs, vm = rtn_stats(vx, vkeep, b, axis=1)
@@ -333,13 +370,6 @@ def quantize_block(k16: np.ndarray, v16: np.ndarray, cfg: Config,
         kstat, vstat = (kss,), (vss,)
     else:
         raise ValueError(mode)
-    if ko > 0:
-        # The notes zero the dense part at an outlier position ([KVQ] 3.4, Algorithm 1) and
-        # the fp16 value replaces it at decode, so the code stored there is never read for
-        # the result. Reading: it is stored as code 0 (a fixed value, so that a decoder can
-        # correct an outlier from the vector's statistics alone).
-        kc = np.where(kmask, np.uint8(0), kc).astype(kc.dtype)
-        vc = np.where(vmask, np.uint8(0), vc).astype(vc.dtype)
     blk = Block(kc, vc, kstat, vstat)
     if ko > 0:
         blk.kmask, blk.vmask = kmask, vmask
@@ -349,8 +379,27 @@ def quantize_block(k16: np.ndarray, v16: np.ndarray, cfg: Config,
 
 
 # ---------------------------------------------------------------------------
-# Dequantization (fp64) ([KVQ] 1.2 and Algorithm 1; [KVARN] method step 5; [BLOG] 4.2)
+# Dequantization (fp64) ([KVQ] 1.2, Algorithm 1 and appendix step 5; [KVARN] method
+# steps; [BLOG] 4.2)
 # ---------------------------------------------------------------------------
+
+def dequant_rtn(codes: np.ndarray, s: np.ndarray, m: np.ndarray) -> np.ndarray:
+    """x_hat = q * s + m ([KVQ] 1.2)."""
+    return np.asarray(codes, np.float64) * np.asarray(s, np.float64) + np.asarray(m, np.float64)
+
+
+def dequant_nuq(codes: np.ndarray, z: np.ndarray, h: np.ndarray, codebook: np.ndarray) -> np.ndarray:
+    """x_hat = C[q] * h + z: the codebook entry scaled back from [-1, 1] ([KVQ] appendix
+    step 5 and Algorithm 1, with the half range as the scale and the centre as the
+    offset)."""
+    C = np.asarray(codebook, np.float32).astype(np.float64)
+    return C[np.asarray(codes, np.int64)] * np.asarray(h, np.float64) + np.asarray(z, np.float64)
+
+
+def dequant_sym(u: np.ndarray, s16: np.ndarray) -> np.ndarray:
+    """x_hat = (u - 8) * s ([BLOG] 4.2, offset-binary storage code)."""
+    return (np.asarray(u, np.float64) - 8.0) * np.asarray(s16, np.float16).astype(np.float64)
+
 
 def dequant_block(blk: Block, cfg: Config, cb_k=None, cb_v=None):
     """(K_hat, V_hat) fp64 [T][D] in the original (un-rotated, pre-RoPE) domain.
@@ -360,30 +409,22 @@ def dequant_block(blk: Block, cfg: Config, cb_k=None, cb_v=None):
     the dequantized value whenever the dense part decodes to zero; an
     asymmetric grid cannot represent zero exactly, so replacement is used.
     """
-    kc = blk.kcodes.astype(np.float64)
-    vc = blk.vcodes.astype(np.float64)
     mode = cfg.mode
     if mode in (MODE_RTN, MODE_KVARN):
-        ks, km = (a.astype(np.float64) for a in blk.kstat)
-        vs, vm = (a.astype(np.float64) for a in blk.vstat)
-        kh = kc * ks[None, :] + km[None, :]
-        vh = vc * vs[:, None] + vm[:, None]
+        kh = dequant_rtn(blk.kcodes, blk.kstat[0][None, :], blk.kstat[1][None, :])
+        vh = dequant_rtn(blk.vcodes, blk.vstat[0][:, None], blk.vstat[1][:, None])
         if mode == MODE_KVARN:
+            # K_dq = (K_q + z) * s_RTN * s1 with z = m / s_RTN ([KVARN] method steps), then
+            # back to the original domain
             kh = kh * blk.ks1.astype(np.float64)[:, None]
             vh = vh * blk.vs1.astype(np.float64)[None, :]
             return hadamard_rotate(kh), hadamard_rotate(vh)
     elif mode == MODE_NUQ:
-        kz, khh = (a.astype(np.float64) for a in blk.kstat)
-        vz, vhh = (a.astype(np.float64) for a in blk.vstat)
-        Ck = np.asarray(cb_k, np.float32).astype(np.float64)
-        Cv = np.asarray(cb_v, np.float32).astype(np.float64)
-        kh = Ck[blk.kcodes] * khh[None, :] + kz[None, :]
-        vh = Cv[blk.vcodes] * vhh[:, None] + vz[:, None]
+        kh = dequant_nuq(blk.kcodes, blk.kstat[0][None, :], blk.kstat[1][None, :], cb_k)
+        vh = dequant_nuq(blk.vcodes, blk.vstat[0][:, None], blk.vstat[1][:, None], cb_v)
     elif mode == MODE_SYM_INT4:
-        ks = blk.kstat[0].astype(np.float64)
-        vs = blk.vstat[0].astype(np.float64)
-        kh = (kc - 8.0) * ks[None, :]
-        vh = (vc - 8.0) * vs[None, :]
+        kh = dequant_sym(blk.kcodes, blk.kstat[0][None, :])
+        vh = dequant_sym(blk.vcodes, blk.vstat[0][None, :])
     else:
         raise ValueError(mode)
     if blk.kmask is not None:
@@ -393,7 +434,7 @@ def dequant_block(blk: Block, cfg: Config, cb_k=None, cb_v=None):
 
 
 # ---------------------------------------------------------------------------
-# Packing and the per-block record layout
+# Bit packing ([KVQ] 9.3; [BLOG] 4.2)
 # ---------------------------------------------------------------------------
 
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
@@ -445,98 +486,6 @@ def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
     else:
         raise ValueError(bits)
     return out.astype(np.uint8).reshape(p.shape[:-1] + (n,))
-
-
-def half_row_token(pos: np.ndarray) -> np.ndarray:
-    """Token (0..63, relative to its half) stored at position pos of a value half-row.
-
-    Position 16a + 4b + c holds token 16b + 4a + c: the 4x4 grid of 4-token groups
-    is transposed, which puts the 16 tokens a matrix-core lane contracts over next
-    to each other (a storage order only; the mapping is its own inverse).
-    """
-    pos = np.asarray(pos)
-    return 16 * ((pos >> 2) & 3) + 4 * (pos >> 4) + (pos & 3)
-
-
-def value_code_planes(vcodes: np.ndarray) -> np.ndarray:
-    """[T][D] value codes -> [2][D][64]: two token halves, channel-major within each,
-    tokens within a half-row in the order of half_row_token."""
-    v = np.asarray(vcodes).reshape(T, D)
-    order = half_row_token(np.arange(64))
-    return np.stack([v[:64][order].T, v[64:][order].T])
-
-
-def _align(x: int, a: int) -> int:
-    return (x + a - 1) // a * a
-
-
-def record_layout(mode: int, bits: int, k_out: int) -> tuple[dict, int]:
-    """Byte offsets of the segments of one block record and its padded size.
-
-    Order: key codes (128 token rows), value codes (two token halves, each
-    128 channel rows of 64 codes in the order of half_row_token), key
-    statistics, value statistics, [KVARN: key s1 per token, value s1 per
-    channel], [outliers: key CSR (values fp16, row pointers u16[129], channel
-    u8), value CSC (values fp16, column pointers u16[129], token u8)]. Each
-    segment starts on a 16-byte boundary; the record is padded to 256 bytes.
-    """
-    R = 16 * bits
-    stat = 256 if mode == MODE_SYM_INT4 else 1024
-    segs = [("kc", T * R), ("vc", D * R), ("ks", stat), ("vs", stat)]
-    if mode == MODE_KVARN:
-        segs += [("k1", 4 * T), ("v1", 4 * D)]
-    if k_out > 0:
-        n = 128 * k_out
-        for p in ("ko", "vo"):
-            segs += [(p + "_val", 2 * n), (p + "_ptr", 2 * 129), (p + "_idx", n)]
-    off, pos = {}, 0
-    for name, size in segs:
-        pos = _align(pos, 16)
-        off[name] = (pos, size)
-        pos += size
-    return off, _align(pos, 256)
-
-
-def record_payload_bytes(mode: int, bits: int, k_out: int) -> int:
-    """Bytes of a record that carry data (segment sizes without padding)."""
-    off, _ = record_layout(mode, bits, k_out)
-    return sum(size for _, size in off.values())
-
-
-def serialize_block(blk: Block, cfg: Config) -> np.ndarray:
-    """The block record as bytes, in the layout of ``record_layout``."""
-    off, size = record_layout(cfg.mode, cfg.bits, cfg.outliers_per_vec)
-    buf = np.zeros(size, np.uint8)
-
-    def put(name, arr):
-        o, n = off[name]
-        raw = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
-        assert raw.size == n, (name, raw.size, n)
-        buf[o:o + n] = raw
-
-    put("kc", pack_codes(blk.kcodes, cfg.bits))             # token-major rows
-    put("vc", pack_codes(value_code_planes(blk.vcodes), cfg.bits))   # [half][channel] rows
-    if cfg.mode == MODE_SYM_INT4:
-        put("ks", blk.kstat[0].astype(np.float16))
-        put("vs", blk.vstat[0].astype(np.float16))
-    else:
-        put("ks", np.concatenate([a.astype(np.float32) for a in blk.kstat]))
-        put("vs", np.concatenate([a.astype(np.float32) for a in blk.vstat]))
-    if cfg.mode == MODE_KVARN:
-        put("k1", blk.ks1.astype(np.float32))
-        put("v1", blk.vs1.astype(np.float32))
-    if cfg.outliers_per_vec > 0:
-        # keys: CSR by token row, entries sorted by (token, channel) [KVQ] 3.4
-        t_idx, c_idx = np.nonzero(blk.kmask)
-        put("ko_val", blk.kout[t_idx, c_idx].astype(np.float16))
-        put("ko_ptr", np.concatenate([[0], np.cumsum(blk.kmask.sum(axis=1))]).astype(np.uint16))
-        put("ko_idx", c_idx.astype(np.uint8))
-        # values: CSC by channel column, entries sorted by (channel, token) [KVQ] 3.4
-        c2, t2 = np.nonzero(blk.vmask.T)
-        put("vo_val", blk.vout[t2, c2].astype(np.float16))
-        put("vo_ptr", np.concatenate([[0], np.cumsum(blk.vmask.sum(axis=0))]).astype(np.uint16))
-        put("vo_idx", t2.astype(np.uint8))
-    return buf
 
 
 # ---------------------------------------------------------------------------

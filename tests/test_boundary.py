@@ -1,14 +1,15 @@
 """C-ABI boundary checks that need no GPU: the library loads, exports every symbol
 include/kvq.h declares, validates arguments on the host before any launch, and its
-buffer layout agrees with the oracle's independently written record layout."""
+buffer layout agrees with the record layout include/kvq.h documents (tests/_record.py)."""
 import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import bit_kv_cache_quantize_amd as K
-from oracle import kvq_oracle as O
+from tests import _record as R
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -50,9 +51,9 @@ def test_invalid_configs_are_rejected(kw):
 @pytest.mark.parametrize("mode,bits,k_out,pre_rope", [
     (K.KVQ_MODE_RTN, 4, 0, 0), (K.KVQ_MODE_NUQ, 3, 1, 1), (K.KVQ_MODE_KVARN, 2, 0, 0),
     (K.KVQ_MODE_SYM_INT4, 4, 0, 0), (K.KVQ_MODE_RTN, 2, 1, 1), (K.KVQ_MODE_NUQ, 4, 8, 0)])
-def test_cache_bytes_matches_oracle_record_layout(mode, bits, k_out, pre_rope):
+def test_cache_bytes_matches_documented_record_layout(mode, bits, k_out, pre_rope):
     c = cfg(mode=mode, bits=bits, outliers_per_vec=k_out, pre_rope=pre_rope)
-    _, rec = O.record_layout(mode, bits, k_out)
+    _, rec = R.layout(mode, bits, k_out)
     units = c.batch * c.n_kv_heads
     nblk = c.max_tokens // 128
 
@@ -69,6 +70,21 @@ def test_cache_bytes_matches_oracle_record_layout(mode, bits, k_out, pre_rope):
 
 
 FAKE = 1 << 40     # an aligned, never dereferenced address: these calls must fail or finish on the host
+
+
+def test_documented_record_sizes():
+    # record payload of the 4-bit, no-outlier layout: 144 B per token and kv head
+    assert R.payload_bytes(R.MODE_RTN, 4, 0) == 144 * 128
+    assert R.layout(R.MODE_RTN, 4, 0)[1] == 18432
+    assert R.layout(R.MODE_KVARN, 2, 0)[1] == 11264
+    assert R.layout(R.MODE_SYM_INT4, 4, 0)[1] == 16896
+    off, size = R.layout(R.MODE_NUQ, 3, 1)
+    spans = sorted(off.values())
+    for (a, n), (b, _) in zip(spans, spans[1:]):
+        assert a + n <= b and b % 16 == 0
+    assert size % 256 == 0
+    perm = R.half_row_token(np.arange(64))
+    assert sorted(perm) == list(range(64)) and np.array_equal(R.half_row_token(perm), np.arange(64))
 
 
 def test_init_validation():
@@ -91,7 +107,7 @@ def test_host_only_state_and_spans():
     h = K.kvq_cache_init(c, FAKE, n)           # no RoPE table: init touches no device memory
     try:
         assert K.kvq_cache_length(h, 0) == 0
-        _, rec = O.record_layout(K.KVQ_MODE_NUQ, 3, 1)
+        _, rec = R.layout(K.KVQ_MODE_NUQ, 3, 1)
         off0, n0 = K.kvq_block_span(h, 0, 0, 0, 0)
         off1, _ = K.kvq_block_span(h, 0, 0, 0, 1)
         off2, _ = K.kvq_block_span(h, 1, 1, 1, 7)
@@ -208,3 +224,27 @@ def test_hot_path_kernels_use_no_private_memory(tmp_path):
     hot = {n: v for n, v in sizes.items() if any(k in n for k in HOT_KERNELS)}
     assert len(hot) >= 20, sorted(sizes)
     assert {n: v for n, v in hot.items() if v} == {}
+
+
+def test_binding_rejects_wrong_dtype_device_or_layout_before_any_call():
+    """The C ABI takes bare pointers; the binding checks dtype, device and contiguity
+    itself (fp16 k, v and q, fp32 out, on the cache's device) and raises ValueError."""
+    import torch
+    cache = object.__new__(K.KVCache)            # no device buffer: nothing may reach the library
+    cache.cfg = cfg(batch=1, n_kv_heads=2, n_q_heads=4)
+    cache.device = torch.device("cuda", 0)
+    cache.handle = None
+    k32 = torch.zeros((1, 2, 4, 128), dtype=torch.float32)
+    k16 = torch.zeros((1, 2, 4, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="float16"):
+        cache.append(0, k32, k32)
+    with pytest.raises(ValueError, match="must be on"):
+        cache.append(0, k16, k16)                # a host tensor
+    with pytest.raises(ValueError, match="float32"):
+        K.check_tensors("cpu", [("out", torch.zeros(4, dtype=torch.float16), torch.float32)])
+    with pytest.raises(ValueError, match="contiguous"):
+        K.check_tensors("cpu", [("k", torch.zeros((4, 4), dtype=torch.float16).t(), torch.float16)])
+    q = torch.zeros((1, 4, 128), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        cache.decode(0, q, torch.zeros((1, 4, 128), dtype=torch.float16))
+    K.check_tensors("cpu", [("k", k16, torch.float16)])    # the right dtype on the right device passes

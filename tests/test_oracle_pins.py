@@ -55,8 +55,6 @@ def test_bit_and_byte_accounting():
     bpe = O.block_scale_bits(4, 128, 16)
     assert bpe == g["blog_bits_per_element"]
     assert g["blog_fp16_gb"] * bpe / 16 == pytest.approx(g["blog_4bit_gb_printed"], rel=g["blog_4bit_gb_rel_tol"])
-    # payload of the record layout: C1 (4-bit, no outliers) = 144 B per token.kv-head
-    assert O.record_payload_bytes(O.MODE_RTN, 4, 0) == 144 * 128
 
 
 # --------------------------------------------------------------------------- P2
@@ -358,48 +356,6 @@ def test_packing_byte_patterns_and_round_trip():
     assert p3h.size == 24 and p3h[16] == 0b11110000
 
 
-def test_record_layout_sizes():
-    assert O.record_layout(O.MODE_RTN, 4, 0)[1] == 18432
-    assert O.record_layout(O.MODE_KVARN, 2, 0)[1] == 11264
-    assert O.record_layout(O.MODE_SYM_INT4, 4, 0)[1] == 16896
-    off, size = O.record_layout(O.MODE_NUQ, 3, 1)
-    spans = sorted(off.values())
-    for (a, n), (b, _) in zip(spans, spans[1:]):
-        assert a + n <= b and b % 16 == 0
-    assert size % 256 == 0
-
-
-def test_serialized_record_reads_back():
-    r = rng(16)
-    cfg = O.Config(1, 1, 1, 1, 128, O.MODE_RTN, 3, outliers_per_vec=1)
-    k16 = r.standard_normal((128, 128)).astype(np.float16)
-    v16 = r.standard_normal((128, 128)).astype(np.float16)
-    blk = O.quantize_block(k16, v16, cfg)
-    buf = O.serialize_block(blk, cfg)
-    off, _ = O.record_layout(cfg.mode, 3, 1)
-    o, n = off["kc"]
-    kc = O.unpack_codes(buf[o:o + n].reshape(128, 48), 3)
-    assert np.array_equal(kc, blk.kcodes)
-    o, n = off["vc"]
-    vc = O.unpack_codes(buf[o:o + n].reshape(2, 128, 24), 3)      # [half][channel][64 positions]
-    for half in (0, 1):
-        for p in range(64):
-            t = 64 * half + 16 * ((p // 4) % 4) + 4 * (p // 16) + p % 4
-            assert np.array_equal(vc[half][:, p], blk.vcodes[t])
-    perm = O.half_row_token(np.arange(64))
-    assert np.array_equal(O.half_row_token(perm), np.arange(64))   # an involution
-    o, n = off["ko_ptr"]
-    ptr = buf[o:o + n].view(np.uint16)
-    o, n = off["ko_idx"]
-    col = buf[o:o + n]
-    o, n = off["ko_val"]
-    val = buf[o:o + n].view(np.float16)
-    for t in range(128):
-        for e in range(ptr[t], ptr[t + 1]):
-            assert blk.kmask[t, col[e]] and val[e] == k16[t, col[e]]
-    assert ptr[128] == 128
-
-
 # --------------------------------------------------------------------------- P14
 def _attention_loops(q, K, V, scale):
     s = [scale * sum(qi * ki for qi, ki in zip(q, k)) for k in K]
@@ -470,10 +426,18 @@ def test_append_in_chunks_equals_append_at_once(mode, bits, k_out, pre_rope):
         for u in range(4):
             assert len(c.blocks[0][u]) == 2
             for b0, b1 in zip(caches[0].blocks[0][u], c.blocks[0][u]):
-                assert np.array_equal(O.serialize_block(b0, cfg), O.serialize_block(b1, cfg))
+                _assert_same_block(b0, b1)
             assert np.array_equal(c.tail_k[0][u], caches[0].tail_k[0][u])
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
+
+
+def _assert_same_block(a, b):
+    for f in ("kcodes", "vcodes", "ks1", "vs1", "kmask", "vmask", "kout", "vout"):
+        x, y = getattr(a, f), getattr(b, f)
+        assert (x is None and y is None) or np.array_equal(x, y), f
+    for sa, sb in zip(a.kstat + a.vstat, b.kstat + b.vstat):
+        assert np.array_equal(sa, sb)
 
 
 def test_decode_single_token_returns_its_value():
@@ -514,3 +478,212 @@ def test_nuq_exact_tie_takes_the_smaller_index():
     assert q[0] == 1            # |0 - (-0.5)| == |0 - 0.5|
     assert q[1] == 2            # exactly on an entry
     assert q[2] == 0            # |-0.75 - (-1)| == |-0.75 - (-0.5)|
+
+
+# --------------------------------------------------------------------------- NUQ dequant
+def test_nuq_dequant_worked_example_step5():
+    """[KVQ] appendix step 5: x_hat = C[q] * s + z with the worked example's printed codes,
+    scales and zero point. Swapping the scale and the offset, or indexing the codebook off
+    by one, fails this."""
+    g = golden("nuq_worked_example.json")
+    C = np.array(g["codebook"], np.float32)
+    for case in g["dequant"]:
+        got = O.dequant_nuq(np.array([case["code"]]), case["z"], case["h"], C)[0]
+        assert got == pytest.approx(case["x_hat"], abs=1e-7)
+    # through dequant_block: the statistics a NUQ block carries are (z, h) in that order
+    cfg = O.Config(1, 1, 1, 1, 128, O.MODE_NUQ, 3)
+    kc = np.zeros((128, 128), np.uint8)
+    kc[0, 15], kc[0, 0] = 2, 7
+    z = np.zeros(128, np.float32)
+    h = np.full(128, 0.08, np.float32)
+    h[0] = 0.31
+    blk = O.Block(kc, kc.copy(), (z, h), (z, h))
+    kh, _ = O.dequant_block(blk, cfg, C, C)
+    assert kh[0, 15] == pytest.approx(g["dequant"][0]["x_hat"], abs=1e-7)
+    assert kh[0, 0] == pytest.approx(g["dequant"][1]["x_hat"], abs=1e-7)
+    # quantize then dequantize: every non-outlier lands on the codebook point nearest to
+    # its normalised value, mapped back through the same (z, h)
+    r = rng(30)
+    x16 = (r.standard_normal((128, 128)) * 2 + 1).astype(np.float16)
+    cfg = O.Config(1, 1, 1, 1, 128, O.MODE_NUQ, 3)
+    blk = O.quantize_block(x16, x16, cfg, C, C)
+    kh, _ = O.dequant_block(blk, cfg, C, C)
+    zk, hk = (a.astype(np.float64) for a in blk.kstat)
+    u = np.clip((x16.astype(np.float64) - zk[None]) / hk[None], -1, 1)
+    nearest = C.astype(np.float64)[np.argmin(np.abs(u[..., None] - C[None, None, :].astype(np.float64)), axis=-1)]
+    assert np.allclose(kh, nearest * hk[None] + zk[None], atol=1e-6)
+
+
+# --------------------------------------------------------------------------- RoPE at decode
+def test_decode_rope_equal_scores_when_keys_are_counter_rotated():
+    """[KVQ] 1.3 / Algorithm 1: decode rotates each cached pre-RoPE key by its own
+    position. Keys stored as R_(-n) k0 at position n all rotate back to k0, so every score
+    is the same and the output is the mean of the values (up to the fp16 rounding of the
+    stored keys). Tokens stay in the exact fp16 tail."""
+    r = rng(31)
+    L = 100
+    cfg = O.Config(1, 1, 1, 1, 256, O.MODE_RTN, 4, pre_rope=1)
+    k0 = r.standard_normal(128)
+    k0 *= 20 / np.linalg.norm(k0)
+    pos = np.arange(L)
+    keys = O.rope_rotate(np.tile(k0, (L, 1)), -pos).astype(np.float16)
+    v = r.standard_normal((L, 128)).astype(np.float16)
+    c = O.OracleCache(cfg)
+    c.append(0, keys[None, None], v[None, None])
+    q = r.standard_normal((1, 1, 128)).astype(np.float16)
+    out = c.decode(0, q)[0, 0]
+    mean = v.astype(np.float64).mean(axis=0)
+    err = np.max(np.abs(out - mean))
+    assert err < 0.03 * np.max(np.abs(v))
+    # without the rotation (or with the query rotated instead) the scores differ and the
+    # output moves far from the mean
+    c2 = O.OracleCache(O.Config(1, 1, 1, 1, 256, O.MODE_RTN, 4, pre_rope=0))
+    c2.append(0, keys[None, None], v[None, None])
+    assert np.max(np.abs(c2.decode(0, q)[0, 0] - mean)) > 10 * err
+
+
+def test_decode_rope_score_gap_closed_form():
+    """Two keys at absolute positions 133 and 168 (after one all-zero 128-token block, which
+    quantizes exactly to zero) with one channel pair each; values e_0 and e_1. The ratio of
+    the two output components is exp(s_a - s_b), where s = scale * q . R(n theta_i) k for a
+    single pair: (k_x cos a - k_y sin a, k_x sin a + k_y cos a), a = n * 10000^(-2i/128)
+    ([KVQ] 1.3). A position offset, a sign of the angle, a wrong theta_i or a rotation of
+    the query instead of the key changes it."""
+    L = 169
+    cfg = O.Config(1, 1, 1, 1, 256, O.MODE_RTN, 4, pre_rope=1)
+    k = np.zeros((L, 128), np.float16)
+    v = np.zeros((L, 128), np.float16)
+    na, nb, ia, ib = 133, 168, 3, 40
+    k[na, 2 * ia], k[na, 2 * ia + 1] = 1.5, -0.5
+    k[nb, 2 * ib], k[nb, 2 * ib + 1] = -2.0, 1.0
+    v[na, 0] = 1.0
+    v[nb, 1] = 1.0
+    q = np.zeros((1, 1, 128), np.float16)
+    q[0, 0, 2 * ia], q[0, 0, 2 * ia + 1] = 2.0, 1.0
+    q[0, 0, 2 * ib], q[0, 0, 2 * ib + 1] = 0.5, -1.5
+    c = O.OracleCache(cfg)
+    c.append(0, k[None, None], v[None, None])
+    out = c.decode(0, q)[0, 0]
+
+    def score(n, i):
+        a = n * 10000.0 ** (-2.0 * i / 128)
+        kx, ky = float(k[n, 2 * i]), float(k[n, 2 * i + 1])
+        rx, ry = kx * math.cos(a) - ky * math.sin(a), kx * math.sin(a) + ky * math.cos(a)
+        return (float(q[0, 0, 2 * i]) * rx + float(q[0, 0, 2 * i + 1]) * ry) / math.sqrt(128)
+
+    assert math.log(out[0] / out[1]) == pytest.approx(score(na, ia) - score(nb, ib), abs=1e-12)
+    # and every one of the other 167 tokens has score 0: out[0] = e^s_a / (167 + e^s_a + e^s_b)
+    ea, eb = math.exp(score(na, ia)), math.exp(score(nb, ib))
+    assert out[0] == pytest.approx(ea / (L - 2 + ea + eb), rel=1e-12)
+
+
+# --------------------------------------------------------------------------- symmetric int4 axes
+def test_symmetric_int4_groups_values_per_channel_along_the_sequence():
+    """[BLOG] 2.1 / 4.2: one fp16 scale per 128-element block in the sequence direction,
+    for the values as for the keys. v[t, c] = (c + 1) u_t makes per-channel and per-token
+    grouping give different scales and codes."""
+    r = rng(32)
+    u = r.uniform(-1, 1, 128)
+    v16 = ((np.arange(128) + 1)[None, :] * u[:, None] / 16).astype(np.float16)
+    k16 = r.standard_normal((128, 128)).astype(np.float16)
+    cfg = O.Config(1, 1, 1, 1, 128, O.MODE_SYM_INT4, 4)
+    blk = O.quantize_block(k16, v16, cfg)
+    s = blk.vstat[0]
+    assert s.shape == (128,)
+    for ch in (0, 5, 127):
+        amax = max(abs(float(v16[t, ch])) for t in range(128))
+        assert s[ch] == np.float16(np.float32(amax) / np.float32(7))
+        for t in (0, 17, 99):
+            q = min(max(round_half_even(float(np.float32(v16[t, ch]) / np.float32(s[ch]))), -8), 7)
+            assert blk.vcodes[t, ch] == q + 8
+
+
+def round_half_even(x: float) -> int:
+    f = math.floor(x)
+    d = x - f
+    if d > 0.5 or (d == 0.5 and f % 2 == 1):
+        return int(f) + 1
+    return int(f)
+
+
+# --------------------------------------------------------------------------- RTN ties
+def test_rtn_rounds_exact_ties_to_even():
+    """Codes at exact half steps: (x - m) / s = 0.5, 1.5, ..., 6.5 with m = 0, s = 1 (3 bits:
+    the vector spans [0, 7]). Round-half-even gives 0, 2, 2, 4, 4, 6, 6; round-half-up or
+    round-half-away would give 1, 2, 3, 4, 5, 6, 7."""
+    x = np.full((128, 1), 1.0, np.float32)
+    x[0, 0], x[1, 0] = 0.0, 7.0
+    halves = [0.5, 1.5, 2.5, 3.5, 4.5, 5.5, 6.5]
+    x[2:9, 0] = halves
+    s, m = O.rtn_stats(x, np.ones_like(x, bool), 3, axis=0)
+    assert s[0] == 1.0 and m[0] == 0.0
+    q = O.rtn_codes(x, s[None], m[None], 3)[:, 0]
+    assert list(q[2:9]) == [round_half_even(h) for h in halves] == [0, 2, 2, 4, 4, 6, 6]
+
+
+# --------------------------------------------------------------------------- outlier count
+def test_one_percent_of_a_vector_is_one_outlier():
+    """[KVQ] 9.3 counts 1% of a 128-element vector as about 1.28 fp16 elements; the
+    integer count per vector is round(1.28) = 1."""
+    g = golden("bit_accounting.json")
+    assert 0.01 * 128 == pytest.approx(g["outliers_per_128_printed"])
+    assert O.n_outliers(0.01) == 1
+    assert O.n_outliers(0.02) == 3 and O.n_outliers(0.0) == 0 and O.n_outliers(2.5 / 128) == 2
+    r = rng(33)
+    x16 = r.standard_normal((128, 128)).astype(np.float16)
+    cfg = O.Config(1, 1, 1, 1, 128, O.MODE_RTN, 2, outliers_per_vec=O.n_outliers(0.01))
+    blk = O.quantize_block(x16, x16, cfg)
+    assert blk.kmask.sum() == 128 and np.all(blk.kmask.sum(axis=0) == 1)
+    assert blk.vmask.sum() == 128 and np.all(blk.vmask.sum(axis=1) == 1)
+    ent = O.outlier_entries(blk.kmask, blk.kout)
+    assert ent.shape == (128, 3) and np.all(np.diff(ent[:, 0] * 128 + ent[:, 1]) > 0)
+    assert np.array_equal(ent[:, 2].astype(np.uint16).view(np.float16), x16[ent[:, 0], ent[:, 1]])
+
+
+# --------------------------------------------------------------------------- outlier code
+def test_outlier_position_carries_the_code_of_the_zeroed_dense_element():
+    """[KVQ] Algorithm 1 step 1 and the appendix step 1 set the dense element of an outlier
+    to 0 before the dense matrix is quantized: the code there is the code of 0.0 under the
+    vector's statistics (taken over the non-outliers), and decode replaces the value."""
+    k = np.zeros((128, 128), np.float16)
+    k[:, 0] = np.linspace(-1, 3, 128).astype(np.float16)      # spans [-1, 3] exactly
+    k[5, 0] = 100.0                                            # the channel's outlier
+    k[:, 1:] = 0.5
+    v = k.copy()
+    cfg = O.Config(1, 1, 1, 1, 128, O.MODE_RTN, 2, outliers_per_vec=1)
+    blk = O.quantize_block(k, v, cfg)
+    s, m = blk.kstat
+    assert m[0] == -1.0 and s[0] == np.float32(4.0) / np.float32(3.0)
+    assert blk.kcodes[5, 0] == 1                               # rint((0 + 1) / (4/3)) = rint(0.75)
+    kh, _ = O.dequant_block(blk, cfg)
+    assert kh[5, 0] == 100.0
+    C = np.array([-1.0, -0.5, 0.25, 1.0], np.float32)
+    cfg = O.Config(1, 1, 1, 1, 128, O.MODE_NUQ, 2, outliers_per_vec=1)
+    blk = O.quantize_block(k, v, cfg, C, C)
+    assert blk.kstat[0][0] == 1.0 and blk.kstat[1][0] == 2.0    # z, h of [-1, 3]
+    assert blk.kcodes[5, 0] == 1                               # u = (0 - 1) / 2 = -0.5 -> C[1]
+    cfg = O.Config(1, 1, 1, 1, 128, O.MODE_SYM_INT4, 4, outliers_per_vec=1)
+    blk = O.quantize_block(k, v, cfg)
+    assert blk.kcodes[5, 0] == 8                               # q = 0 stored as 0 + 8
+
+
+# --------------------------------------------------------------------------- VarN degenerate
+def test_varn_constant_block_reaches_a_finite_fixed_point():
+    """A constant key block rotates to one constant column (Hadamard of a constant row is
+    a multiple of e_0) and zeros: that column and the zero columns have no spread and keep
+    their log-scales; each row's spread is normalised once and then stays 1."""
+    y = O.hadamard_rotate(np.full((128, 128), 0.75))
+    r2, c2 = O.varn(y, 2)
+    r8, c8 = O.varn(y, 8)
+    assert np.all(np.isfinite(r8)) and np.all(np.isfinite(c8))
+    assert np.allclose(r8, r2, atol=1e-12) and np.all(c8 == 0)
+    xt = y * np.exp(-r8[:, None] - c8[None, :])
+    assert np.allclose(xt.std(axis=1), 1.0, atol=1e-12)
+    cfg = O.Config(1, 1, 1, 1, 128, O.MODE_KVARN, 2, varn_iters=8)
+    blk = O.quantize_block(np.full((128, 128), 0.75, np.float16), np.full((128, 128), -0.5, np.float16), cfg)
+    for a in (blk.ks1, blk.vs1, *blk.kstat, *blk.vstat):
+        assert np.all(np.isfinite(a))
+    assert np.all(blk.kcodes == 0)                             # every key channel is constant
+    assert np.all(blk.vcodes[:, 0] == 0) and np.all(blk.vcodes[:, 1:] == 3)   # rows [-0.5 sqrt(128), 0, ...]
+    kh, vh = O.dequant_block(blk, cfg)
+    assert np.allclose(kh, 0.75, atol=1e-5) and np.allclose(vh, -0.5, atol=1e-5)
