@@ -2,36 +2,42 @@
 """Benchmark of the low-bit KV-cache hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input already resident in
-HBM: quantize-append of the full context into the cache (all layers of the
-workload), then one decode-attention pass over it (all layers).
+HBM: quantize-append into the cache (every layer of the workload), then one
+decode-attention pass over it (every layer).
 
-Single-layer workloads (the default LLaMA-7B layer at 32K tokens, and the small
-and KVarN ones) keep two cache copies: step i appends into copy i % 2 and
-decodes copy (i + 1) % 2, which the previous step wrote. Between a copy's append
-and its decode, more than three times the 256 MB last-level cache of traffic
-has passed, so decode reads its cache from HBM. The 32-layer workloads append
-all layers and then decode all layers. The 1M-token workload's fp16 inputs
-(550 GB) cannot be resident: its step is the 32-layer decode and its append
-rate is timed separately on one resident 256K-token chunk.
+* Default, the 1M-token LLaMA-7B workload (32 layers, 32 heads, 2-bit RTN keys
+  before RoPE and values, one fp16 outlier per vector): the context is built
+  once; each step then appends one new 128-token block to every layer (every
+  head quantizes a block: staging, outliers, statistics, codes, packing) and
+  decodes every layer over the whole cache. The context grows by 128 tokens per
+  step (0.2% over a default run). The fp16 inputs of the full context (550 GB)
+  cannot be resident, so the bulk append rate is timed separately, on one
+  resident 256K-token chunk appended into one layer.
+* Single-layer workloads keep two cache copies: step i appends the whole context
+  into copy i % 2 and decodes copy (i + 1) % 2, which the previous step wrote, so
+  decode reads its cache from HBM rather than from the 256 MB last-level cache.
+* The 32-layer int4 workload appends every layer's context, then decodes every
+  layer.
 
 Prints one JSON line. value = decode effective KV GB/s = the algorithmic bytes a
 decode must move (block records without padding, fp16 tail, q, out, codebooks,
-RoPE rows) / decode time, from HIP events on the stream the kernels run on.
-frac_hbm_peak divides it by the 8 TB/s spec-sheet peak, frac_copy_bw by the
-measured bandwidth of a 1 GiB device copy (copy_gbs, read + write bytes).
+RoPE rows) / decode time, from HIP events on the stream the kernels run on
+(split merge included). roofline is that of the decode kernel; rooflines holds
+the decode and the append ones. cpu_baseline is the CPU oracle, untuned, on a
+bounded sample of the same workload, over the host's cores (worker processes
+started before the GPU is touched).
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
 
 METRIC = "decode-attn effective KV GB/s (% of HBM peak); quantize-append Mtok/s"
 HBM_PEAK_GBS = 8000.0
-DEFAULT = "c2_llama7b_layer_32k_nuq3"
+DEFAULT = "c5_llama7b_1m_rtn2"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -41,12 +47,13 @@ MODE_NAMES = {0: "rtn", 1: "nuq", 2: "kvarn", 3: "sym_int4"}
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", default=DEFAULT)
     p.add_argument("--splits", type=int, default=0, help="decode splits (0 = automatic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=32, help="(sequence, kv head) units in the oracle sample")
+    p.add_argument("--cpu-workers", type=int, default=0, help="oracle worker processes (0: host cores, at most 16)")
+    p.add_argument("--cpu-tokens", type=int, default=0, help="tokens per oracle unit (0: by workload)")
     return p.parse_args()
 
 
@@ -54,8 +61,13 @@ def ceil128(n):
     return (n + 127) // 128 * 128
 
 
+def is_streamed(wl):
+    """Workloads whose fp16 inputs cannot all be resident (the 1M-token context)."""
+    return wl.context >= (1 << 20)
+
+
 class Bench:
-    def __init__(self, wl, splits):
+    def __init__(self, wl, splits, steps_total):
         import torch
         import bit_kv_cache_quantize_amd as K
         import synth
@@ -65,9 +77,10 @@ class Bench:
         self.dev = torch.device("cuda", 0)
         self.gen = SD.DeviceGenerator(wl, self.dev)
         self.single = wl.n_layers == 1
-        self.resident = not wl.name.startswith("c5_")
+        self.streamed = is_streamed(wl)
         self.copies = 2 if self.single else 1
-        cfg = K.make_config(wl.n_layers, wl.batch, wl.n_kv_heads, wl.n_q_heads, ceil128(wl.context), wl.mode,
+        capacity = ceil128(wl.context) + (128 * steps_total if self.streamed else 0)
+        cfg = K.make_config(wl.n_layers, wl.batch, wl.n_kv_heads, wl.n_q_heads, capacity, wl.mode,
                             wl.bits, wl.outliers_per_vec, wl.pre_rope, wl.rope_theta, wl.varn_iters)
         self.caches = [K.KVCache(cfg, self.dev) for _ in range(self.copies)]
         for c in self.caches:
@@ -87,7 +100,20 @@ class Bench:
             self.gen.fill_q(q, layer)
             self.q.append(q)
         self.inputs = {}
-        if self.resident:
+        if self.streamed:
+            self._build_streamed()
+            # the new block of each step and layer, resident before timing
+            self.step_inputs = []
+            for s in range(steps_total):
+                t0 = wl.context + 128 * s
+                per_layer = []
+                for layer in range(wl.n_layers):
+                    k = torch.empty((wl.batch, wl.n_kv_heads, 128, 128), dtype=torch.float16, device=self.dev)
+                    v = torch.empty_like(k)
+                    self.gen.fill_kv(k, v, layer, t0, 128)
+                    per_layer.append((k, v))
+                self.step_inputs.append(per_layer)
+        else:
             for layer in range(wl.n_layers):
                 for t0, n in self.chunks:
                     k = torch.empty((wl.batch, wl.n_kv_heads, n, 128), dtype=torch.float16, device=self.dev)
@@ -96,8 +122,6 @@ class Bench:
                     self.inputs[(layer, t0)] = (k, v)
             for copy in range(self.copies):      # both copies hold the context before the first step
                 self.append_all(copy)
-        else:
-            self._build_streamed()
         torch.cuda.synchronize()
 
     def _build_streamed(self):
@@ -114,8 +138,12 @@ class Bench:
                 c.append(layer, kk, vv)
         self.stream_chunk = (k, v)
 
-    def append_all(self, copy):
+    def append_all(self, copy, step=0):
         c = self.caches[copy]
+        if self.streamed:
+            for layer, (k, v) in enumerate(self.step_inputs[step]):
+                c.append(layer, k, v)
+            return
         for layer in range(self.wl.n_layers):
             c.reset(layer)
             for t0, _ in self.chunks:
@@ -132,6 +160,7 @@ class Bench:
         return sum(c.decode_bytes(layer) for layer in range(self.wl.n_layers))
 
     def run(self, steps, warmup):
+        """Returns (ms per step, [decode ms], [append ms], [decode bytes]) over the timed steps."""
         torch = self.torch
         ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
         rec = []
@@ -142,27 +171,34 @@ class Bench:
                 torch.cuda.synchronize()
                 t_start.record()
             a0, a1, d0, d1 = ev(), ev(), ev(), ev()
-            if self.resident:
-                a0.record()
-                self.append_all(i % self.copies)
-                a1.record()
+            a0.record()
+            self.append_all(i % self.copies, step=i)
+            a1.record()
             d0.record()
             self.decode_all((i + 1) % self.copies if self.copies == 2 else 0)
             d1.record()
             if i >= warmup:
-                rec.append((a0, a1, d0, d1))
+                rec.append((a0, a1, d0, d1, self.decode_bytes() if self.streamed else None))
         t_end.record()
         torch.cuda.synchronize()
         ms_total = t_start.elapsed_time(t_end)
-        dec = [d0.elapsed_time(d1) for _, _, d0, d1 in rec]
-        app = [a0.elapsed_time(a1) for a0, a1, _, _ in rec] if self.resident else []
-        return ms_total / steps, dec, app
+        dec = [d0.elapsed_time(d1) for _, _, d0, d1, _ in rec]
+        app = [a0.elapsed_time(a1) for a0, a1, _, _, _ in rec]
+        nbytes = [b for *_, b in rec]
+        return ms_total / steps, dec, app, nbytes
 
-    def append_separately(self, reps):
-        """Append rate of the streamed workload: one resident chunk, appended into layer 0."""
-        torch = self.torch
+    def append_bulk(self, reps):
+        """Bulk append rate of the streamed workload: one resident chunk appended into layer 0
+        of a second, one-layer cache of the same shape."""
+        torch, K, wl = self.torch, self.K, self.wl
         k, v = self.stream_chunk
-        c = self.caches[0]
+        cfg = K.make_config(1, wl.batch, wl.n_kv_heads, wl.n_q_heads, ceil128(k.shape[2]), wl.mode, wl.bits,
+                            wl.outliers_per_vec, wl.pre_rope, wl.rope_theta, wl.varn_iters)
+        c = K.KVCache(cfg, self.dev)
+        if wl.mode == self.synth.MODE_NUQ:
+            for h in range(wl.n_kv_heads):
+                for w in (0, 1):
+                    c.codebook_load(0, h, w, self.synth.gen_codebook(wl, 0, h, w, wl.bits))
         times = []
         for _ in range(reps):
             c.reset(0)
@@ -172,14 +208,7 @@ class Bench:
             a1.record()
             torch.cuda.synchronize()
             times.append(a0.elapsed_time(a1))
-        # restore layer 0 to the full context
-        c.reset(0)
-        for t0, m in self.chunks:
-            kk = torch.empty((self.wl.batch, self.wl.n_kv_heads, m, 128), dtype=torch.float16, device=self.dev)
-            vv = torch.empty_like(kk)
-            self.gen.fill_kv(kk, vv, 0, t0, m)
-            c.append(0, kk, vv)
-        torch.cuda.synchronize()
+        del c
         return times, k.shape[2]
 
 
@@ -261,78 +290,130 @@ def median(x):
     return s[len(s) // 2] if s else float("nan")
 
 
-def cpu_baseline(wl, heads):
-    """The oracle, untuned, on a bounded sample of the workload: up to `heads` kv heads of
-    the first sequences of layer 0 (at most 32K tokens each), so that it takes roughly 10-20
-    s of one core. Append = quantize every block; decode = dequantize + fp64 attention."""
-    import numpy as np
+# ----------------------------------------------------------------------------- CPU baseline
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_unit(args):
+    """One (layer, sequence, kv head) unit of the workload through the oracle, on one core:
+    generate its inputs, append them (quantize every full block), decode its query heads.
+    Returns (append seconds, decode seconds, decode algorithmic bytes, tokens)."""
+    name, layer, b, h, ctx = args
     from threadpoolctl import threadpool_limits
+    import numpy as np
     import synth
     from oracle import kvq_oracle as O
-    ctx = min(wl.context, 32768)
-    nh = min(heads, wl.n_kv_heads)
-    nb = min(wl.batch, max(1, heads // nh))
-    cfg = O.Config(1, nb, nh, nh * wl.group, ceil128(ctx), wl.mode, wl.bits, wl.outliers_per_vec,
-                   wl.pre_rope, wl.rope_theta, wl.varn_iters)
-    k = np.stack([np.stack([synth.gen_k(wl, 0, b, h, 0, ctx) for h in range(nh)]) for b in range(nb)])
-    v = np.stack([np.stack([synth.gen_v(wl, 0, b, h, 0, ctx) for h in range(nh)]) for b in range(nb)])
-    q = np.stack([np.stack([synth.gen_q(wl, 0, b, h) for h in range(nh * wl.group)]) for b in range(nb)])
-    oc = O.OracleCache(cfg)
-    for h in range(nh):
-        for w in (0, 1):
-            if wl.mode == 1:
-                oc.load_codebook(0, h, w, synth.gen_codebook(wl, 0, h, w, wl.bits))
+    wl = synth.WORKLOADS[name]
+    g = wl.group
     with threadpool_limits(1):
-        t0 = time.perf_counter()
+        k = synth.gen_k(wl, layer, b, h, 0, ctx)[None, None]
+        v = synth.gen_v(wl, layer, b, h, 0, ctx)[None, None]
+        q = np.stack([synth.gen_q(wl, layer, b, h * g + i) for i in range(g)])[None]
+        cfg = O.Config(1, 1, 1, g, ceil128(ctx), wl.mode, wl.bits, wl.outliers_per_vec, wl.pre_rope,
+                       wl.rope_theta, wl.varn_iters)
+        oc = O.OracleCache(cfg)
+        if wl.mode == 1:
+            for w in (0, 1):
+                oc.load_codebook(0, 0, w, synth.gen_codebook(wl, layer, h, w, wl.bits))
         chunk = wl.append_chunk or ctx
+        t0 = time.perf_counter()
         for s in range(0, ctx, chunk):
             oc.append(0, k[:, :, s:s + chunk], v[:, :, s:s + chunk])
         t1 = time.perf_counter()
         oc.decode(0, q)
         t2 = time.perf_counter()
-    nblk, tail = ctx // 128, ctx % 128
-    units = nb * nh
-    dbytes = units * (nblk * record_payload(wl) + tail * 512) + units * wl.group * 128 * 6
+    nbytes = (ctx // 128) * record_payload(wl) + (ctx % 128) * 512 + g * 128 * 6
+    return t1 - t0, t2 - t1, nbytes, ctx
+
+
+def cpu_baseline(wl, workers, tokens):
+    """The oracle as it stands, timed on the host's cores: independent (layer, sequence,
+    kv head) units of the workload, `tokens` tokens each, spread over `workers` processes
+    (one numpy thread each). Rates are sample bytes (tokens) over the wall-clock time."""
+    import multiprocessing as mp
+    ncpu = os.cpu_count() or 1
+    workers = workers or min(ncpu, 16)
+    ctx = min(wl.context, tokens or (131072 if is_streamed(wl) else 32768))
+    units_per_worker = 8 if is_streamed(wl) else 2
+    units = []
+    i = 0
+    while len(units) < workers * units_per_worker:
+        layer = i % wl.n_layers
+        h = (i // wl.n_layers) % wl.n_kv_heads
+        b = (i // (wl.n_layers * wl.n_kv_heads)) % wl.batch
+        units.append((wl.name, layer, b, h, ctx))
+        i += 1
+    ctxm = mp.get_context("fork")        # before any GPU use in this process
+    t0 = time.perf_counter()
+    with ctxm.Pool(workers) as pool:
+        res = pool.map(_oracle_unit, units, chunksize=1)
+    wall = time.perf_counter() - t0
+    app_s = sum(r[0] for r in res)
+    dec_s = sum(r[1] for r in res)
+    nbytes = sum(r[2] for r in res)
+    toks = sum(r[3] for r in res)
+    # wall-clock split between the two phases in proportion to their summed CPU times
+    dec_wall = wall * dec_s / (app_s + dec_s)
+    app_wall = wall - dec_wall
+    # one token = one position's K and V for all kv heads of one layer
     return {
-        "value": dbytes / (t2 - t1) / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"layer 0, {nb} sequence(s) x {nh} of {wl.n_kv_heads} kv heads, {ctx} tokens: "
-                  f"append {t1 - t0:.2f} s, decode {t2 - t1:.2f} s (numpy, one thread)",
-        "append_mtok_s": ctx * units / wl.n_kv_heads / (t1 - t0) / 1e6,
-        "decode_s": t2 - t1, "append_s": t1 - t0,
+        "value": round(nbytes / dec_wall / 1e9, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
+        "sample": f"{len(units)} (layer, sequence, kv head) units of {ctx} tokens each (of {wl.context}), "
+                  f"{workers} processes of one numpy thread; append {app_s:.1f} s and decode {dec_s:.1f} s "
+                  f"of CPU time, {wall:.1f} s wall",
+        "host_cpu_count": ncpu, "cpu_model": _cpu_model(),
+        "append_mtok_s": round(toks / wl.n_kv_heads / app_wall / 1e6, 5),
+        "decode_wall_s": round(dec_wall, 3), "append_wall_s": round(app_wall, 3),
     }
 
 
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(the hot path runs on one MI355X); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: libkvq has no multi-GPU path (its kernels run on "
+              "one MI355X); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    import torch
     import synth
     wl = synth.WORKLOADS[args.config]
-    b = Bench(wl, args.splits)
-    warmup = max(args.warmup, 2 if b.copies == 2 else 1)
-    ms_step, dec, app = b.run(args.steps, warmup)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_workers, args.cpu_tokens)
+        print(f"cpu baseline done: {cpu['sample']}", file=sys.stderr, flush=True)
+    import torch
+    warmup = max(args.warmup, 2 if wl.n_layers == 1 else 1)
+    b = Bench(wl, args.splits, args.steps + warmup)
+    print("cache built", file=sys.stderr, flush=True)
+    ms_step, dec, app, step_bytes = b.run(args.steps, warmup)
     dec_ms = sum(dec) / len(dec)
-    dbytes = b.decode_bytes()
+    dbytes = sum(step_bytes) / len(step_bytes) if b.streamed else b.decode_bytes()
     gbs = dbytes / (dec_ms * 1e-3) / 1e9
     layers = wl.n_layers
-    app_tokens = wl.batch * wl.context * layers            # one token = one position's K and V, all kv heads
     rec_payload = record_payload(wl)
-    nblk = wl.context // 128
-    abytes = layers * wl.batch * wl.n_kv_heads * (wl.context * 512 + nblk * rec_payload + (wl.context % 128) * 512)
-    if app:
-        app_ms = sum(app) / len(app)
-        app_rate = app_tokens / (app_ms * 1e-3) / 1e6
-        app_gbs = abytes / (app_ms * 1e-3) / 1e9
-    else:
-        times, n = b.append_separately(5)
+    dec_kernel = decode_kernel_name(wl)
+    if b.streamed:
+        # per step: one 128-token block per layer and kv head; the bulk rate separately
+        step_app_ms = sum(app) / len(app)
+        times, n = b.append_bulk(5)
         app_ms = median(times)
         app_rate = wl.batch * n / (app_ms * 1e-3) / 1e6
         abytes = wl.batch * wl.n_kv_heads * (n * 512 + (n // 128) * rec_payload)   # the one timed chunk
-        app_gbs = abytes / (app_ms * 1e-3) / 1e9
-    dec_kernel = decode_kernel_name(wl)
+        app_launches = 1
+    else:
+        step_app_ms = app_ms = sum(app) / len(app)
+        app_rate = wl.batch * wl.context * layers / (app_ms * 1e-3) / 1e6
+        nblk = wl.context // 128
+        abytes = layers * wl.batch * wl.n_kv_heads * (wl.context * 512 + nblk * rec_payload + (wl.context % 128) * 512)
+        app_launches = layers * len(b.chunks)
+    app_gbs = abytes / (app_ms * 1e-3) / 1e9
     copy_gbs = measured_copy_gbs(torch, b.dev)
 
     def roof(achieved_gbs, kernel, us, algo_bytes):
@@ -345,10 +426,8 @@ def main():
                 "traffic_bytes_per_launch": t}
 
     dec_us = dec_ms * 1e3 / layers
-    roof_dec = roof(gbs, dec_kernel, dec_us, dbytes // layers)
-    app_launches = layers * len(b.chunks) if app else 1
+    roof_dec = roof(gbs, dec_kernel, dec_us, dbytes / layers)
     roof_app = roof(app_gbs, "quantize_kernel", app_ms * 1e3 / app_launches, abytes / app_launches)
-    dominant = roof_app if (app and sum(app) > sum(dec)) else roof_dec
     line = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -356,19 +435,22 @@ def main():
         "config": {"workload": wl.name, "layers": layers, "batch": wl.batch, "context": wl.context,
                    "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads, "mode": MODE_NAMES[wl.mode],
                    "bits": wl.bits, "outliers_per_vec": wl.outliers_per_vec, "pre_rope": wl.pre_rope,
-                   "varn_iters": wl.varn_iters if wl.mode == 2 else 0},
+                   "varn_iters": wl.varn_iters if wl.mode == 2 else 0,
+                   "step": ("append one 128-token block to every layer, then decode every layer"
+                            if b.streamed else "append the whole context to every layer, then decode every layer")},
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "copy_gbs": round(copy_gbs, 1),
         "frac_copy_bw": round(gbs / copy_gbs, 4),
         "decode_us_per_step": round(dec_ms * 1e3, 2),
-        "tokens_per_s": round(wl.batch / (dec_ms * 1e-3), 1),
+        "decode_bytes_per_step": int(dbytes),
+        "tokens_per_s": round(wl.batch / (dec_ms * 1e-3), 2),
         "append_mtok_s": round(app_rate, 2),
-        "append_us_per_step": round(app_ms * 1e3, 2),
-        "roofline": dominant,
+        "append_us_per_step": round(step_app_ms * 1e3, 2),
+        "roofline": roof_dec,
         "rooflines": {"decode": roof_dec, "append": roof_app},
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

@@ -462,11 +462,10 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
   a.scale_log2 = scale * 1.4426950408889634f;
   if (cfg.outliers_per_vec > 0) {
-    // per-wave staging for the sparse fix-ups: the outlier segments (table kernel), plus
-    // key S/M, value S/M of a half and a RoPE base row (VALU kernel)
+    // staging for the sparse fix-ups: the outlier segments (table kernel: one copy per
+    // workgroup), plus key S/M, value S/M of a half and a RoPE base row (VALU kernel: per wave)
     const uint32_t blob = c->lay.vo_idx + 128u * cfg.outliers_per_vec - c->lay.ko_val;
-    // (table kernel: the staging, then its value-outlier entry list, 6 bytes per entry)
-    a.wave_lds = (int)(((blob + 15u) & ~15u) + (tab ? 768u * cfg.outliers_per_vec : 1024u + 512u + 512u));
+    a.wave_lds = (int)(((blob + 15u) & ~15u) + (tab ? 0u : 1024u + 512u + 512u));
   }
   if (tab)
     st = hip_check(kvq::launch_decode_tab(cfg.mode, cfg.bits, a, cfg.batch, s), "launch decode");

@@ -28,6 +28,11 @@
 //   * the online softmax runs per head on the 16 scores each lane holds (the
 //     accumulators are rescaled only when some running maximum moved); the fp16
 //     tail is handled by the VALU half-block decoder.
+//   * fp16 has a narrow exponent range, so the fp32 operands are brought near 1 by a
+//     power of two before the split (exact, and undone after the product): Q' per head
+//     by its largest |q_c s_c|, P' per half block by its largest value scale S_t. Data
+//     of any magnitude in the fp16 input range, and KVarN blocks whose two scales
+//     trade magnitude (s_RTN tiny and s1 huge, or the reverse), keep full precision.
 #include "kvq_decode_common.h"
 
 namespace kvq {
@@ -151,6 +156,7 @@ struct MfmaDecoder {
   float qv[QF16 ? 1 : 32];    // fp32 query of head n & 7, channels 32*q .. 32*q+31
   f4 acc[8];                  // O[16*ct + 4*q + e][column n]
   float m_run, l_run, pm;     // head n & 7 (l_run, pm: this lane's share)
+  float vsc;                  // RTN: the power of two acc is currently scaled by (wave-uniform)
 
   __device__ MfmaDecoder(const DecodeArgs& args, int lane_, int w_, const float* qs, uint8_t* meta_)
       : a(args), lane(lane_), w(w_), par(w_ & 1), n(lane_ & 15), q(lane_ >> 4),
@@ -174,6 +180,12 @@ struct MfmaDecoder {
     m_run = -INFINITY;
     l_run = 0.f;
     pm = 0.f;
+    vsc = 1.f;
+  }
+
+  // 2^-e for the exponent e of a non-negative finite x (x * 2^-e in [0.5, 1)); 1 for x = 0.
+  static __device__ __forceinline__ float pow2_normaliser(float x) {
+    return x > 0.f ? __builtin_amdgcn_ldexpf(1.f, -__builtin_amdgcn_frexp_expf(x)) : 1.f;
   }
 
   // Record loads go through a buffer resource over this split's records: the lane offset is
@@ -260,6 +272,7 @@ struct MfmaDecoder {
     // sum_c q_c m_c
     uint32_t qo[4][4];
     float bias = 0.f;
+    float kscale = 1.f;         // Q' of this head was multiplied by kscale (a power of two)
     if constexpr (QF16) {
       // fp16 q times fp16 s: the high part is the product rounded once, the low part the
       // fused q*s - high rounded once
@@ -286,12 +299,19 @@ struct MfmaDecoder {
         ksv[4 * v] = s4.x; ksv[4 * v + 1] = s4.y; ksv[4 * v + 2] = s4.z; ksv[4 * v + 3] = s4.w;
         kmv[4 * v] = m4.x; kmv[4 * v + 1] = m4.y; kmv[4 * v + 2] = m4.z; kmv[4 * v + 3] = m4.w;
       }
+      float qs[32], qmax = 0.f;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        qs[c] = qv[c] * ksv[c];
+        qmax = fmaxf(qmax, fabsf(qs[c]));
+      }
+      kscale = pow2_normaliser(rows_max(qmax));   // per head: its 128 channels
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int ca = kchan<BITS>(ks, 2 * s), cb = kchan<BITS>(ks, 2 * s + 1);
-          qo[ks][s] = part2(qv[ca] * ksv[ca], qv[cb] * ksv[cb]);
+          qo[ks][s] = part2(qs[ca] * kscale, qs[cb] * kscale);
           bias = fmaf(qv[ca], kmv[ca], fmaf(qv[cb], kmv[cb], bias));
         }
       bias = rows_sum(bias);
@@ -302,6 +322,7 @@ struct MfmaDecoder {
     // ---- raw scores for tokens 16*tt + 4*q + e, head n & 7 (KVarN: already in the log2
     // domain; otherwise the log2 scale is applied inside the exponent)
     constexpr bool PRESCALED = MODE == KVARN;
+    const float kunscale = 1.f / kscale;   // exact: a power of two
     float sc[4][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -316,8 +337,8 @@ struct MfmaDecoder {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float full = d[e] + dpp_f<0x128>(d[e]);   // high + low column
-        if constexpr (MODE == KVARN) sc[tt][e] = (full + bias) * s1[e] * a.scale_log2;
-        else if constexpr (MODE == RTN) sc[tt][e] = full + bias;
+        if constexpr (MODE == KVARN) sc[tt][e] = fmaf(full, kunscale, bias) * s1[e] * a.scale_log2;
+        else if constexpr (MODE == RTN) sc[tt][e] = fmaf(full, kunscale, bias);
         else sc[tt][e] = full;
       }
     }
@@ -336,36 +357,55 @@ struct MfmaDecoder {
     // p' = p * S_t (value scale per token; 1 for int4). The value codes enter centred, so
     // the part of sum_t p_t v_t that does not depend on the code is sum_t p_t (M_t + OFFV * S_t).
     float p[4][4], lsum = 0.f, msum = 0.f;
+    float S_t[4][4], M_t[4][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      float S_t[4] = {1.f, 1.f, 1.f, 1.f}, M_t[4] = {0.f, 0.f, 0.f, 0.f};
       if constexpr (MODE != SYM) {
         const float4 ts = *reinterpret_cast<const float4*>(vS + 64 * par + 16 * tt + 4 * q);
         const float4 tm = *reinterpret_cast<const float4*>(vM + 64 * par + 16 * tt + 4 * q);
-        S_t[0] = ts.x; S_t[1] = ts.y; S_t[2] = ts.z; S_t[3] = ts.w;
-        M_t[0] = tm.x; M_t[1] = tm.y; M_t[2] = tm.z; M_t[3] = tm.w;
+        S_t[tt][0] = ts.x; S_t[tt][1] = ts.y; S_t[tt][2] = ts.z; S_t[tt][3] = ts.w;
+        M_t[tt][0] = tm.x; M_t[tt][1] = tm.y; M_t[tt][2] = tm.z; M_t[tt][3] = tm.w;
       }
+    }
+    // P' = p S_t vscale, vscale a power of two putting the half block's largest S_t in
+    // [0.5, 1) (wave-uniform: every row holds all 64 tokens' scales after the row maximum)
+    float vscale = 1.f;
+    if constexpr (MODE != SYM) {
+      float smax = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) smax = fmaxf(smax, S_t[tt][e]);
+      vscale = pow2_normaliser(rows_max(smax));
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float pe = __builtin_amdgcn_exp2f(fmaf(sc[tt][e], sl, -mnew));
         lsum += pe;
-        if constexpr (MODE != SYM) msum = fmaf(pe, fmaf((float)OFFV, S_t[e], M_t[e]), msum);
-        p[tt][e] = MODE == SYM ? pe : pe * S_t[e];
+        if constexpr (MODE != SYM) msum = fmaf(pe, fmaf((float)OFFV, S_t[tt][e], M_t[tt][e]), msum);
+        p[tt][e] = MODE == SYM ? pe : pe * (S_t[tt][e] * vscale);
       }
     }
     l_run = fmaf(l_run, alpha, lsum);
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {   // the running maximum moved somewhere
+    // RTN: acc holds sum p' codes in units of the current vscale; a new vscale rescales it
+    // (exactly, a power of two) together with the softmax correction
+    const float arescale = MODE == RTN ? alpha * (vscale / vsc) : alpha;
+    if (__builtin_amdgcn_ballot_w64(arescale != 1.f)) {   // a running maximum or the value scale moved
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) acc[ct] *= alpha;
+      for (int ct = 0; ct < 8; ++ct) acc[ct] *= arescale;
     }
+    if constexpr (MODE == RTN) vsc = vscale;
     float g = 0.f;                     // KVarN: code-independent part, added before the channel s1
     if constexpr (MODE == RTN) {
       pm = fmaf(pm, alpha, msum);
     } else if constexpr (MODE == KVARN) {
-      g = msum;
+      g = msum * vscale;
       g = rows_sum(g);
       g = lo_mask ? 0.f : g;           // once per head: on the high column
     }
+    const float vunscale = 1.f / vscale;   // exact: a power of two
 
     // ---- P' operand, this lane's part, slots in the order of the value chunks
     uint32_t po[2][4];
@@ -389,7 +429,7 @@ struct MfmaDecoder {
         acc[ct] = t;
       } else if constexpr (MODE == KVARN) {
         const float4 v = *reinterpret_cast<const float4*>(v1 + 16 * ct + 4 * q);
-        const float f[4] = {v.x, v.y, v.z, v.w};
+        const float f[4] = {v.x * vunscale, v.y * vunscale, v.z * vunscale, v.w * vunscale};
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[ct][e] = fmaf(f[e], t[e], acc[ct][e]);
       } else {
@@ -550,6 +590,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[ct][e] = d.acc[ct][e] + dpp_f<0x128>(d.acc[ct][e]);   // high + low column
+  if constexpr (MODE == RTN) {
+    const float un = 1.f / d.vsc;   // the accumulators' value scale, a power of two
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[ct][e] *= un;
+  }
   if (n < G) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)

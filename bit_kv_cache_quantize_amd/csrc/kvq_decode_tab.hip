@@ -23,7 +23,10 @@
 // code-independent part sum_t p_t M_t is added once per head.
 //
 // Outliers replace the dense value: each CSR (keys) / CSC (values) entry adds
-// (fp16 value - dense value) times the entry's weight.
+// (fp16 value - dense value) times the entry's weight. A token's lane walks its own CSR
+// row (its key entries, in channel order) after the table part of its score; a channel's
+// lane walks its own CSC column (value entries, in token order). Every sum therefore has
+// a fixed order: two runs give bitwise equal results.
 //
 // Work decomposition: one workgroup of two waves = one split of one (sequence, kv head);
 // wave h takes the 64-token half h of every block of the split. Two barriers per block
@@ -66,7 +69,6 @@ struct TabDecoder {
     float4 kst;           // (scale_x, scale_y, offset_x, offset_y) of pair ib
     float2 rb;            // (cos, sin) of the block base angle for pair ib
     u32x4 ob;             // outlier segment chunk j (j = thread of the workgroup)
-    float2 vst;           // token j's value statistics, for the outlier staging (with outliers)
   };
   struct Keys {           // issued after the scores
     uint32_t kw[KWD];     // key row of token j
@@ -92,11 +94,7 @@ struct TabDecoder {
     _Float16* wt;         // matrix-core values: this wave's weights p*S as fp16 high and low
                           // parts in operand order [2][16 steps][4 slots]
     const _Float16* zero; // 64 zero fp16 (operand rows 2 and 3)
-    float* kcorr;         // key outlier corrections of the block's scores [128]
-    float* vcorr;         // this wave's value outlier corrections per channel [128]
-    float2* vst;          // value (S, M) per token of the block [128]
-    uint16_t* vent;       // value outlier entries: token | channel << 8 [128 k]
-    float* vdelta;        // value outlier entries: fp16 value - dense value [128 k]
+    float* Sv;            // this wave's value scale S per token [64] (outlier corrections)
   };
 
   const DecodeArgs& a;
@@ -106,6 +104,7 @@ struct TabDecoder {
   float m_run, l_run, pm, acc0, acc1;
   f4 dacc[2];             // matrix-core accumulators of the two channel groups
   float tps;              // sum of the weights fed to the matrix cores (this token)
+  float vsc;              // the power of two dacc and tps are scaled by (wave-uniform)
 
   __device__ TabDecoder(const DecodeArgs& args, const Shared& sh, int lane_, int w_)
       : a(args), S(sh), lane(lane_), par(w_), j(64 * w_ + lane_), ib((64 * w_ + lane_) >> 1), hb(lane_ & 1) {
@@ -114,6 +113,7 @@ struct TabDecoder {
       dacc[0] = f4{0.f, 0.f, 0.f, 0.f};
       dacc[1] = f4{0.f, 0.f, 0.f, 0.f};
       tps = 0.f;
+      vsc = 1.f;
     }
     l_run = 0.f;
     pm = 0.f;
@@ -186,11 +186,6 @@ struct TabDecoder {
     // without outliers the offset lies past the range: zeros, no memory access
     const uint32_t oo = a.k_out > 0 ? o + a.lay.ko_val + 16u * (uint32_t)min(j, ob_chunks - 1) : 0xFFFFFFF0u;
     Mt.ob = __builtin_amdgcn_raw_buffer_load_b128(rsb, oo, 0, 0);
-    // a second copy of token j's value statistics: the staging at the top of a block then
-    // waits for these loads, not for the value rows issued last in the previous block
-    const uint32_t ov = a.k_out > 0 ? o + a.lay.vs + 4u * j : 0xFFFFFFF0u;
-    const float sv0 = ldf(ov), sv1 = ldf(a.k_out > 0 ? ov + 512u : ov);
-    Mt.vst = MODE == NUQ ? make_float2(sv1, sv0) : make_float2(sv0, sv1);
   }
 
   __device__ __forceinline__ void fetch_keys(Keys& K, int blk) const {
@@ -346,10 +341,25 @@ struct TabDecoder {
     }
     float sc = sc0 + sc1;
 
-    // key outliers: corrections gathered per token before the scores
+    // key outliers: this token's CSR row, in channel order. Entry (j, c) adds
+    // (fp16 value - dense value of code 0) times the query coefficient of channel c at
+    // in-block offset j: cos(j theta_i) al + sin(j theta_i) be (x channel) or
+    // cos(j theta_i) be - sin(j theta_i) al (y channel) of pair i = c / 2.
     if (a.k_out > 0) {
-      sc += S.kcorr[j];
-      S.kcorr[j] = 0.f;   // cleared for the next block (its corrections follow a barrier)
+      const uint16_t* kptr = reinterpret_cast<const uint16_t*>(S.blob + (a.lay.ko_ptr - a.lay.ko_val));
+      const uint8_t* kidx = S.blob + (a.lay.ko_idx - a.lay.ko_val);
+      const __half* kval = reinterpret_cast<const __half*>(S.blob);
+      const int e1 = kptr[j + 1];
+      float corr = 0.f;
+      for (int e = kptr[j]; e < e1; ++e) {
+        const int c = kidx[e], i = c >> 1;
+        const float ang = (float)j * S.trev[i];
+        const float cj = __builtin_amdgcn_cosf(ang), sj = __builtin_amdgcn_sinf(ang);
+        const float2 q2 = S.qb[i];
+        const float coef = (c & 1) ? fmaf(cj, q2.y, -sj * q2.x) : fmaf(cj, q2.x, sj * q2.y);
+        corr = fmaf(__half2float(kval[e]) - S.kd0[c], coef, corr);
+      }
+      sc += corr;
     }
     return sc;
   }
@@ -362,10 +372,24 @@ struct TabDecoder {
     S.pS[lane] = ps;
     S.p[lane] = p;
     S.M[lane] = V.tst.y;
+    if (a.k_out > 0) S.Sv[lane] = V.tst.x;
     if constexpr (MV) {
-      // the weight as fp16 high and low parts, at the operand slot of token j's position
-      const _Float16 hi = (_Float16)ps;
-      const _Float16 lo = (_Float16)(ps - (float)hi);
+      // the weight as fp16 high and low parts, at the operand slot of token j's position,
+      // after a power of two that puts the half block's largest value scale in [0.5, 1)
+      // (fp16's exponent range is narrow; the scaling is exact and undone at the end):
+      // the accumulators follow the current power of two
+      const float smax = wave_max(V.tst.x);
+      const float vs = smax > 0.f ? __builtin_amdgcn_ldexpf(1.f, -__builtin_amdgcn_frexp_expf(smax)) : 1.f;
+      if (vs != vsc) {
+        const float f = vs / vsc;
+        dacc[0] *= f;
+        dacc[1] *= f;
+        tps *= f;
+        vsc = vs;
+      }
+      const float psv = ps * vs;
+      const _Float16 hi = (_Float16)psv;
+      const _Float16 lo = (_Float16)(psv - (float)hi);
       tps += (float)hi + (float)lo;
       const int pos = half_row_token(lane);   // the position map is its own inverse
       S.wt[mv_slot(pos)] = hi;
@@ -422,21 +446,27 @@ struct TabDecoder {
       acc0 += o0;
       acc1 += o1;
     }
-    // ---- value outliers: each entry whose token is in this half adds p_t (val - dense) to
-    // its channel (scattered through LDS), then each lane takes its two channels
+    // ---- value outliers: each lane walks the CSC columns of its two channels (entries in
+    // token order) and adds p_t (fp16 value - dense value of code 0) for the tokens of
+    // this half
     if (a.k_out > 0) {
-      const int nv = 128 * a.k_out;
-      for (int e = lane; e < nv; e += 64) {
-        const uint32_t tc = S.vent[e];   // token | channel << 8
-        const int t = (int)(tc & 255u) - 64 * par;
-        if (t >= 0 && t < 64) atomicAdd(&S.vcorr[tc >> 8], S.p[t] * S.vdelta[e]);
-      }
-      wave_sync();
-      acc0 += S.vcorr[ch0()];
-      acc1 += S.vcorr[ch1()];
-      S.vcorr[ch0()] = 0.f;
-      S.vcorr[ch1()] = 0.f;
+      acc0 += value_corrections(ch0());
+      acc1 += value_corrections(ch1());
     }
+  }
+
+  __device__ __forceinline__ float value_corrections(int c) const {
+    const uint16_t* vptr = reinterpret_cast<const uint16_t*>(S.blob + (a.lay.vo_ptr - a.lay.ko_val));
+    const uint8_t* vidx = S.blob + (a.lay.vo_idx - a.lay.ko_val);
+    const __half* vval = reinterpret_cast<const __half*>(S.blob + (a.lay.vo_val - a.lay.ko_val));
+    const float v0 = MODE == NUQ ? S.cbv[0] : 0.f;
+    const int e1 = vptr[c + 1];
+    float corr = 0.f;
+    for (int e = vptr[c]; e < e1; ++e) {
+      const int t = (int)vidx[e] - 64 * par;
+      if (t >= 0 && t < 64) corr = fmaf(S.p[t], __half2float(vval[e]) - fmaf(v0, S.Sv[t], S.M[t]), corr);
+    }
+    return corr;
   }
 
   // Operand slot (4 * step + k) of half-row position pos in the matrix-core value product:
@@ -450,52 +480,6 @@ struct TabDecoder {
   static __device__ __forceinline__ uint32_t code_pair_f16(uint32_t d, int m) {
     const uint32_t x = 2 * m >= 8 ? (d >> (2 * m - 8)) : (d << (8 - 2 * m));
     return (x & 0x03000300u) | 0x3C003C00u;
-  }
-
-  // Row of entry e in a CSR / CSC pointer array of 129 entries: the largest r with
-  // ptr[r] <= e. The first three halvings use the pointers at multiples of 16, read together;
-  // four dependent reads finish the search.
-  static __device__ __forceinline__ int segment_of(const uint16_t* ptr, int e) {
-    int c[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) c[m] = ptr[16 * (m + 1)];
-    int r = c[3] <= e ? 64 : 0;                                   // ptr[64]
-    r = (r ? c[5] : c[1]) <= e ? r + 32 : r;                      // ptr[r + 32]
-    const int k = r >> 5;                                         // ptr[r + 16] = c[2 k]
-    r = (k == 0 ? c[0] : k == 1 ? c[2] : k == 2 ? c[4] : c[6]) <= e ? r + 16 : r;
-#pragma unroll
-    for (int st = 8; st >= 1; st >>= 1) r = ptr[r + st] <= e ? r + st : r;
-    return r;
-  }
-
-  // Outlier corrections of the block, one entry per lane (the workgroup's 128 lanes): key
-  // entries add (val - dense) times the rotated query coefficient to their token's score;
-  // value entries are listed with their token, channel and (val - dense) for the value
-  // phase. The dense value of an outlier position is that of code 0 (the stored code).
-  __device__ __forceinline__ void outlier_prep(int tid) const {
-    const uint8_t* blob = S.blob;
-    const int n = 128 * a.k_out;
-    const uint16_t* kptr = reinterpret_cast<const uint16_t*>(blob + (a.lay.ko_ptr - a.lay.ko_val));
-    const uint8_t* kidx = blob + (a.lay.ko_idx - a.lay.ko_val);
-    const __half* kval = reinterpret_cast<const __half*>(blob);
-    const uint16_t* vptr = reinterpret_cast<const uint16_t*>(blob + (a.lay.vo_ptr - a.lay.ko_val));
-    const uint8_t* vidx = blob + (a.lay.vo_idx - a.lay.ko_val);
-    const __half* vval = reinterpret_cast<const __half*>(blob + (a.lay.vo_val - a.lay.ko_val));
-    const float v0 = MODE == NUQ ? S.cbv[0] : 0.f;
-    // key and value entry e in the same iteration: their pointer searches overlap
-    for (int e = tid; e < n; e += 128) {
-      const int t = segment_of(kptr, e), c = kidx[e], i = c >> 1;
-      const int vc = segment_of(vptr, e), vt = vidx[e];
-      const float delta = __half2float(kval[e]) - S.kd0[c];
-      const float ang = (float)t * S.trev[i];
-      const float cj = __builtin_amdgcn_cosf(ang), sj = __builtin_amdgcn_sinf(ang);
-      const float2 q2 = S.qb[i];
-      const float coef = (c & 1) ? fmaf(cj, q2.y, -sj * q2.x) : fmaf(cj, q2.x, sj * q2.y);
-      atomicAdd(&S.kcorr[t], delta * coef);
-      const float2 st = S.vst[vt];
-      S.vent[e] = (uint16_t)(vt | (vc << 8));
-      S.vdelta[e] = __half2float(vval[e]) - fmaf(v0, st.x, st.y);
-    }
   }
 
   // Tokens 64*par .. 64*par+63 of the fp16 tail (position 128*nblk + j), waves 0 and 1.
@@ -564,15 +548,12 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   __shared__ __align__(16) float s_q[128];
   __shared__ float s_trev[64];
   __shared__ float s_cb[32];
-  // [wave][p * S, p][token]; before the scores the same memory holds the block's value
-  // statistics per token (read by the outlier corrections, which end before the values)
+  // [wave][p * S, p][token]
   __shared__ __align__(16) float s_pps[2][2][64];
   __shared__ __align__(16) float s_M[2][64];
   __shared__ __align__(16) _Float16 s_wt[Dec::MV ? 2 : 1][Dec::MV ? 128 : 8];
   __shared__ __align__(16) _Float16 s_zero[Dec::MV ? 64 : 8];
-  __shared__ __align__(16) float s_kcorr[128];
-  __shared__ __align__(16) float s_vcorr[2][128];
-  float2* s_vst = reinterpret_cast<float2*>(&s_pps[0][0][0]);
+  __shared__ __align__(16) float s_S[2][64];
   __shared__ float s_m[2], s_l[2];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -583,9 +564,6 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   if (tid < 64) s_trev[tid] = a.rope_off[128 * 64 * 2 + tid] * kInv2Pi;
   if (MODE == NUQ && tid < 32) s_cb[tid] = a.cb[(kvh * 2 + (tid >> 4)) * kCbStride + (tid & 15)];
   if (Dec::MV && tid < 64) s_zero[tid] = (_Float16)0.f;
-  s_kcorr[tid] = 0.f;
-  s_vcorr[0][tid] = 0.f;
-  s_vcorr[1][tid] = 0.f;
   __syncthreads();
   if (tid < PT) {
     // code values of two adjacent value tokens, in the same index order as the key tables
@@ -615,13 +593,7 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   sh.cbv = s_cb + 16;
   sh.wt = s_wt[Dec::MV ? w : 0];
   sh.zero = s_zero;
-  sh.kcorr = s_kcorr;
-  sh.vcorr = s_vcorr[w];
-  sh.vst = s_vst;
-  // after the outlier staging: the value entries (token | channel << 8, then the deltas)
-  const uint32_t blob_bytes = a.k_out > 0 ? (a.lay.vo_idx + 128u * a.k_out - a.lay.ko_val + 15u) & ~15u : 0u;
-  sh.vdelta = reinterpret_cast<float*>(s_dyn + blob_bytes);
-  sh.vent = reinterpret_cast<uint16_t*>(s_dyn + blob_bytes + 512u * a.k_out);
+  sh.Sv = s_S[w];
   Dec d(a, sh, lane, w);
 
   float rc[64], rs[64];
@@ -650,17 +622,10 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
     // the loads of the next block are unconditional (past the split's end they read
     // nothing), so that no branch makes the memory-counter waits conservative
     const int nxt = blk + 1;
-    if (a.k_out > 0) {
-      d.stage_blob(Mt, blk);
-      s_vst[tid] = Mt.vst;
-    }
+    if (a.k_out > 0) d.stage_blob(Mt, blk);
     d.build(Mt);
     d.fetch_meta(Mt, nxt);
     __syncthreads();   // tables, rotated query, statistics and outlier staging complete
-    if (a.k_out > 0) {
-      d.outlier_prep(tid);
-      __syncthreads();   // outlier corrections complete
-    }
     const float sc = d.scores(Kc, rc, rs);
     d.fetch_keys(Kc, nxt);
     const float p = d.softmax_step(sc);
@@ -692,8 +657,9 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
     float o0 = d.acc0 + pmw, o1 = d.acc1 + pmw;
     if constexpr (Dec::MV) {
       const float T = wave_sum(d.tps);
-      o0 += 4.f * ((d.dacc[0][0] + d.dacc[0][1]) - T);
-      o1 += 4.f * ((d.dacc[1][0] + d.dacc[1][1]) - T);
+      const float un = 1.f / d.vsc;   // a power of two: exact
+      o0 += 4.f * ((d.dacc[0][0] + d.dacc[0][1]) - T) * un;
+      o1 += 4.f * ((d.dacc[1][0] + d.dacc[1][1]) - T) * un;
     }
     s_o[w * 128 + d.ch0()] = o0;
     s_o[w * 128 + d.ch1()] = o1;

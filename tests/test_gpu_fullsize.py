@@ -94,9 +94,9 @@ def _check_units(K, wl, cache, gen, layer, units):
         got_g = got_out[b, h * g:(h + 1) * g][None]
         if wl.mode == synth.MODE_KVARN:
             assert stats.diff <= 1e-4 * stats.codes, f"{stats.diff} of {stats.codes} codes differ"
-            # end to end (oracle on its own cache): the codes may differ by one step in a few
-            # elements (fp32 vs fp64 VarN), so this is reported and only loosely bounded
-            e2e = H.attention_close(got_g, oc.decode(0, qg), rtol=1e-2)
+            # end to end (oracle on its own cache): the attention bar when every code matches;
+            # with codes one step apart in a few elements (fp32 vs fp64 VarN) 1e-2
+            e2e = H.attention_close(got_g, oc.decode(0, qg), rtol=1e-3 if stats.diff == 0 else 1e-2)
             # decode parity: the oracle's fp64 dequantization and attention on the device cache
             oc.blocks[0][0] = dev_blocks
         else:
