@@ -51,6 +51,7 @@ _sig = {
     "kvq_codebook_load": [_vp, _i, _i, _i, ctypes.POINTER(ctypes.c_float), _i, _vp],
     "kvq_quantize_append": [_vp, _i, _vp, _vp, _i, _vp],
     "kvq_decode_attn": [_vp, _i, _vp, _vp, ctypes.c_float, _vp],
+    "kvq_decode_attn_static": [_vp, _i, _vp, _vp, ctypes.c_float, _vp],
     "kvq_cache_length": [_vp, _i, ctypes.POINTER(ctypes.c_int32)],
     "kvq_cache_reset": [_vp, _i],
     "kvq_set_decode_splits": [_vp, _i],
@@ -129,6 +130,11 @@ def kvq_quantize_append(handle: int, layer: int, k, v, n_new: int, stream=None):
 
 def kvq_decode_attn(handle: int, layer: int, q, out, softmax_scale: float = 0.0, stream=None):
     _check(lib.kvq_decode_attn(handle, layer, _ptr(q), _ptr(out), softmax_scale, _stream(stream)), "kvq_decode_attn")
+
+
+def kvq_decode_attn_static(handle: int, layer: int, q, out, softmax_scale: float = 0.0, stream=None):
+    _check(lib.kvq_decode_attn_static(handle, layer, _ptr(q), _ptr(out), softmax_scale, _stream(stream)),
+           "kvq_decode_attn_static")
 
 
 def kvq_cache_length(handle: int, layer: int) -> int:

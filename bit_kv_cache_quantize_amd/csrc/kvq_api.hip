@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -236,6 +237,42 @@ kvq_status check_layer(kvq_cache c, int layer) {
 
 }  // namespace
 
+namespace {
+
+// Split partials of kvq_decode_attn_static: a library-owned array, one copy per GPU the
+// library runs on, held until the process ends. Every call on a GPU shares its copy.
+constexpr size_t kScratchBytes = (size_t)KVQ_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's copy of the scratch array (looked up once per device, with
+// that device current). The array's name is a host-side stand-in and is never passed on.
+kvq_status scratch_for_current_device(float** out) {
+  int dev = -1;
+  kvq_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (st != KVQ_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_HIP, "device %d outside the supported range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    st = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st != KVQ_OK) return st;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
+
+// Decode over one layer with the split partials in `part` (nullptr: the cache's workspace).
+// part_limit: bytes available at `part` (checked against what this call's splits need).
+kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, float softmax_scale,
+                       void* stream, float* part, size_t part_limit);
+
+}  // namespace
+
 extern "C" {
 
 kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes) {
@@ -411,6 +448,25 @@ kvq_status kvq_quantize_append(kvq_cache c, int layer, const void* k_f16, const 
 
 kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out, float softmax_scale,
                            void* stream) {
+  return decode_impl(c, layer, q_f16, out, softmax_scale, stream, nullptr, 0);
+}
+
+kvq_status kvq_decode_attn_static(kvq_cache c, int layer, const void* q_f16, float* out, float softmax_scale,
+                                  void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  float* part = nullptr;
+  st = scratch_for_current_device(&part);
+  if (st != KVQ_OK) return st;
+  return decode_impl(c, layer, q_f16, out, softmax_scale, stream, part, kScratchBytes);
+}
+
+}  // extern "C"
+
+namespace {
+
+kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, float softmax_scale,
+                       void* stream, float* part, size_t part_limit) {
   kvq_status st = check_layer(c, layer);
   if (st != KVQ_OK) return st;
   if (!q_f16 || !out) return fail(KVQ_ERR_ARG, "q or out is NULL");
@@ -440,6 +496,13 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
     bps = (nblk + splits - 1) / splits;
     splits = (nblk + bps - 1) / bps;
   }
+  if (part && splits > 1) {
+    const size_t need = (size_t)cfg.batch * cfg.n_q_heads * splits * kvq::kPartStride * sizeof(float);
+    if (need > part_limit)
+      return fail(KVQ_ERR_SIZE, "%d splits x %d sequences x %d query heads need %zu bytes of split partials; "
+                  "the static scratch holds %zu (lower the split count with kvq_set_decode_splits)",
+                  splits, cfg.batch, cfg.n_q_heads, need, part_limit);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   kvq::DecodeArgs a{};
   a.lay = c->lay;
@@ -450,7 +513,7 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
   a.rope_base = reinterpret_cast<const float*>(c->base + c->off_rope_base);
   a.rope_off = reinterpret_cast<const float*>(c->base + c->off_rope_off);
   a.q = static_cast<const __half*>(q_f16);
-  a.part = reinterpret_cast<float*>(c->base + c->off_work);
+  a.part = part ? part : reinterpret_cast<float*>(c->base + c->off_work);
   a.out = out;
   a.Hkv = cfg.n_kv_heads;
   a.Hq = cfg.n_q_heads;
@@ -480,6 +543,10 @@ kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out
   }
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 kvq_status kvq_cache_length(kvq_cache c, int layer, int32_t* n_tokens) {
   const kvq_status st = check_layer(c, layer);

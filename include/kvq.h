@@ -62,6 +62,7 @@ typedef enum {
 #define KVQ_MAX_OUTLIERS 8
 #define KVQ_MAX_GROUP 8
 #define KVQ_MAX_SPLITS 64
+#define KVQ_STATIC_SCRATCH_BYTES (8u << 20)
 
 typedef struct {
   int32_t n_layers;         /* >= 1 */
@@ -139,6 +140,25 @@ kvq_status kvq_quantize_append(kvq_cache cache, int layer, const void* k_f16, co
  */
 kvq_status kvq_decode_attn(kvq_cache cache, int layer, const void* q_f16, float* out,
                            float softmax_scale, void* stream);
+
+/*
+ * For callers that cannot allocate device memory or call allocating routines (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid it): kvq_decode_attn with
+ * the split partials kept in a library-owned static device array of
+ * KVQ_STATIC_SCRATCH_BYTES (8 MiB) instead of the cache buffer's workspace. Same
+ * arguments, kernels and results as kvq_decode_attn; it calls no allocating routine.
+ * Each GPU the library runs on holds its own copy of the array until the process ends
+ * (looked up once per device, with that device current). Every call on one GPU shares
+ * that copy, whatever the handle: calls that overlap on one GPU (different streams or
+ * threads) race; serialize them. Every partial is written before it is read, so the
+ * array's previous contents never matter.
+ * Errors: those of kvq_decode_attn, and KVQ_ERR_SIZE (nothing launched) when the call's
+ * split partials, splits x batch x n_q_heads x 520 bytes, exceed the array; lower the
+ * split count with kvq_set_decode_splits. KVQ_ERR_HIP if the array's device address
+ * cannot be obtained.
+ */
+kvq_status kvq_decode_attn_static(kvq_cache cache, int layer, const void* q_f16, float* out,
+                                  float softmax_scale, void* stream);
 
 /* Tokens currently held by a layer (host-side counter, no device access). */
 kvq_status kvq_cache_length(kvq_cache cache, int layer, int32_t* n_tokens);
