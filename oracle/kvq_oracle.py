@@ -275,6 +275,8 @@ class Config:
     pre_rope: int = 0
     rope_theta: float = 10000.0
     varn_iters: int = 8
+    sink_tokens: int = 0       # first tokens of a sequence kept in fp16 ([KVQ] 3.5)
+    fp16_window: int = 0       # most recent tokens kept in fp16 ([KVQ] 4.2, KIVI's residual)
 
     @property
     def group(self) -> int:
@@ -534,12 +536,17 @@ def error_decomposition(k: np.ndarray, kdq: np.ndarray):
 # ---------------------------------------------------------------------------
 
 class OracleCache:
-    """Per layer and (batch row, kv head): a list of quantized blocks plus a fp16 tail.
+    """Per layer and (batch row, kv head): fp16 sink tokens, a list of quantized blocks and a
+    fp16 tail of the most recent tokens.
 
-    Append semantics: tokens fill positions in order; every time 128 tokens of
-    a sequence have accumulated they are quantized as one block; the remaining
-    (< 128) most recent tokens stay in fp16 ([BLOG] 5.2: the last partial block
-    takes a separate fp16 path). Decode attends to every cached token.
+    Append semantics: tokens fill positions in order. The first ``sink_tokens`` tokens of
+    a sequence stay in fp16 ([KVQ] 3.5: the first token, on which attention concentrates,
+    is kept in fp16 and left out of the statistics). The tokens after them form 128-token
+    blocks; a block is quantized once ``fp16_window`` more tokens follow it ([KVQ] 4.2:
+    KIVI keeps the most recent tokens in full precision), and the tokens not yet quantized
+    stay in fp16 ([BLOG] 5.2: the last partial block takes a separate fp16 path). With
+    neither, a block is quantized as soon as it is complete. Decode attends to every cached
+    token.
     """
 
     def __init__(self, cfg: Config):
@@ -547,8 +554,9 @@ class OracleCache:
         self.len = [0] * cfg.n_layers
         nb = cfg.batch * cfg.n_kv_heads
         self.blocks = [[[] for _ in range(nb)] for _ in range(cfg.n_layers)]
-        self.tail_k = [[np.zeros((0, D), np.float16) for _ in range(nb)] for _ in range(cfg.n_layers)]
-        self.tail_v = [[np.zeros((0, D), np.float16) for _ in range(nb)] for _ in range(cfg.n_layers)]
+        empty = lambda: [[np.zeros((0, D), np.float16) for _ in range(nb)] for _ in range(cfg.n_layers)]  # noqa: E731
+        self.sink_k, self.sink_v = empty(), empty()
+        self.tail_k, self.tail_v = empty(), empty()
         self.codebooks = {}
 
     def load_codebook(self, layer: int, kv_head: int, which: int, cb: np.ndarray):
@@ -562,12 +570,16 @@ class OracleCache:
         cfg = self.cfg
         n_new = k16.shape[2]
         assert self.len[layer] + n_new <= cfg.max_tokens
+        n_sink = max(0, min(cfg.sink_tokens - self.len[layer], n_new))
         for b in range(cfg.batch):
             for h in range(cfg.n_kv_heads):
                 u = self._unit(b, h)
-                tk = np.concatenate([self.tail_k[layer][u], k16[b, h]])
-                tv = np.concatenate([self.tail_v[layer][u], v16[b, h]])
-                nfull = tk.shape[0] // T
+                self.sink_k[layer][u] = np.concatenate([self.sink_k[layer][u], k16[b, h, :n_sink]])
+                self.sink_v[layer][u] = np.concatenate([self.sink_v[layer][u], v16[b, h, :n_sink]])
+                tk = np.concatenate([self.tail_k[layer][u], k16[b, h, n_sink:]])
+                tv = np.concatenate([self.tail_v[layer][u], v16[b, h, n_sink:]])
+                # whole blocks with at least fp16_window tokens after them
+                nfull = max(0, (tk.shape[0] - cfg.fp16_window) // T)
                 cbk = self.codebooks.get((layer, h, 0))
                 cbv = self.codebooks.get((layer, h, 1))
                 for j in range(nfull):
@@ -582,7 +594,8 @@ class OracleCache:
         u = self._unit(b, h)
         cbk = self.codebooks.get((layer, h, 0))
         cbv = self.codebooks.get((layer, h, 1))
-        ks, vs = [], []
+        ks = [self.sink_k[layer][u].astype(np.float64)]
+        vs = [self.sink_v[layer][u].astype(np.float64)]
         for blk in self.blocks[layer][u]:
             kh, vh = dequant_block(blk, self.cfg, cbk, cbv)
             ks.append(kh)

@@ -400,11 +400,14 @@ def test_split_merge_equals_single_pass():
 
 
 # --------------------------------------------------------------------------- cache semantics
-@pytest.mark.parametrize("mode,bits,k_out,pre_rope", [
-    (O.MODE_RTN, 4, 0, 0), (O.MODE_NUQ, 3, 1, 1), (O.MODE_SYM_INT4, 4, 0, 0), (O.MODE_KVARN, 2, 0, 0)])
-def test_append_in_chunks_equals_append_at_once(mode, bits, k_out, pre_rope):
+@pytest.mark.parametrize("mode,bits,k_out,pre_rope,sink,window", [
+    (O.MODE_RTN, 4, 0, 0, 0, 0), (O.MODE_NUQ, 3, 1, 1, 0, 0), (O.MODE_SYM_INT4, 4, 0, 0, 0, 0),
+    (O.MODE_KVARN, 2, 0, 0, 0, 0), (O.MODE_RTN, 2, 1, 1, 1, 0), (O.MODE_NUQ, 3, 0, 1, 2, 128),
+    (O.MODE_KVARN, 2, 0, 0, 5, 128)])
+def test_append_in_chunks_equals_append_at_once(mode, bits, k_out, pre_rope, sink, window):
     r = rng(19)
-    cfg = O.Config(1, 2, 2, 4, 512, mode, bits, outliers_per_vec=k_out, pre_rope=pre_rope, varn_iters=3)
+    cfg = O.Config(1, 2, 2, 4, 512, mode, bits, outliers_per_vec=k_out, pre_rope=pre_rope, varn_iters=3,
+                   sink_tokens=sink, fp16_window=window)
     L = 300
     k = r.standard_normal((2, 2, L, 128)).astype(np.float16)
     v = r.standard_normal((2, 2, L, 128)).astype(np.float16)
@@ -424,7 +427,7 @@ def test_append_in_chunks_equals_append_at_once(mode, bits, k_out, pre_rope):
     for c in caches[1:]:
         assert c.len[0] == L
         for u in range(4):
-            assert len(c.blocks[0][u]) == 2
+            assert len(c.blocks[0][u]) == max(0, (L - sink - window) // 128)
             for b0, b1 in zip(caches[0].blocks[0][u], c.blocks[0][u]):
                 _assert_same_block(b0, b1)
             assert np.array_equal(c.tail_k[0][u], caches[0].tail_k[0][u])
@@ -687,3 +690,89 @@ def test_varn_constant_block_reaches_a_finite_fixed_point():
     assert np.all(blk.vcodes[:, 0] == 0) and np.all(blk.vcodes[:, 1:] == 3)   # rows [-0.5 sqrt(128), 0, ...]
     kh, vh = O.dequant_block(blk, cfg)
     assert np.allclose(kh, 0.75, atol=1e-5) and np.allclose(vh, -0.5, atol=1e-5)
+
+
+# --------------------------------------------------------------------------- sink and window
+def test_sink_token_stays_fp16_and_outside_the_block_statistics():
+    """[KVQ] 3.5: the first token is kept in fp16 and kept out of the statistics. A sink
+    token of magnitude 1000 in every channel: with one sink token it is reproduced exactly
+    and the first block (tokens 1..128) keeps the small range of the other tokens; without
+    it, the block's range (and so its error) is set by the sink."""
+    r = rng(40)
+    L = 257
+    k = r.uniform(-4, 4, (1, 1, L, 128)).astype(np.float16)
+    v = r.uniform(-1, 1, (1, 1, L, 128)).astype(np.float16)
+    k[0, 0, 0] = 1000.0
+    v[0, 0, 0] = -1000.0
+    errs, scales = {}, {}
+    for sink in (0, 1):
+        cfg = O.Config(1, 1, 1, 1, 384, O.MODE_RTN, 2, sink_tokens=sink)
+        c = O.OracleCache(cfg)
+        c.append(0, k, v)
+        assert len(c.blocks[0][0]) == 2 and c.tail_k[0][0].shape[0] == L - sink - 256
+        kh, vh = c.dequantized(0, 0, 0)
+        assert kh.shape == (L, 128)
+        errs[sink] = np.max(np.abs(kh[1:129] - k[0, 0, 1:129].astype(np.float64)))
+        scales[sink] = float(c.blocks[0][0][0].kstat[0].max())
+        if sink:
+            assert np.array_equal(kh[0], k[0, 0, 0].astype(np.float64))
+            assert np.array_equal(vh[0], v[0, 0, 0].astype(np.float64))
+            assert np.array_equal(c.sink_k[0][0], k[0, 0, :1])
+    assert errs[1] <= 8.0 / 3 / 2 * (1 + 1e-6)        # half a step of a range within [-4, 4]
+    assert scales[1] <= 8.0 / 3 and scales[0] > 1000.0 / 3   # the sink stretches block 0's range
+
+
+@pytest.mark.parametrize("sink,window,L", [(0, 128, 300), (1, 128, 300), (4, 256, 1000), (0, 384, 200),
+                                           (128, 0, 129), (3, 128, 131)])
+def test_fp16_window_keeps_the_most_recent_tokens_exact(sink, window, L):
+    """[KVQ] 4.2 (KIVI's fp16 residual): a 128-token block is quantized once `window`
+    newer tokens follow it, so the number of blocks is floor((L - sink - window) / 128)
+    (at least 0) and every later token, and the sink tokens, decode exactly."""
+    r = rng(41 + L)
+    k = r.standard_normal((1, 1, L, 128)).astype(np.float16)
+    v = r.standard_normal((1, 1, L, 128)).astype(np.float16)
+    cfg = O.Config(1, 1, 1, 1, H_ceil(L + 128), O.MODE_RTN, 3, sink_tokens=sink, fp16_window=window)
+    c = O.OracleCache(cfg)
+    c.append(0, k, v)
+    nblk = max(0, (L - sink - window) // 128)
+    assert len(c.blocks[0][0]) == nblk
+    kh, vh = c.dequantized(0, 0, 0)
+    first_fp16 = sink + 128 * nblk
+    assert L - first_fp16 >= min(window, L - sink)
+    assert np.array_equal(kh[first_fp16:], k[0, 0, first_fp16:].astype(np.float64))
+    assert np.array_equal(vh[:sink], v[0, 0, :sink].astype(np.float64))
+    if nblk:
+        assert not np.array_equal(kh[sink:first_fp16], k[0, 0, sink:first_fp16].astype(np.float64))
+
+
+def H_ceil(n):
+    return (n + 127) // 128 * 128
+
+
+def test_all_fp16_decode_is_dense_attention_by_hand():
+    """With the window covering every token nothing is quantized: decode is the dense
+    softmax of the fp16 keys, each rotated by its position, written out with explicit
+    cosines for three tokens and compared with the oracle's decode."""
+    r = rng(42)
+    L = 3
+    cfg = O.Config(1, 1, 1, 1, 256, O.MODE_RTN, 2, pre_rope=1, sink_tokens=1, fp16_window=128)
+    k = r.standard_normal((1, 1, L, 128)).astype(np.float16)
+    v = r.standard_normal((1, 1, L, 128)).astype(np.float16)
+    q = r.standard_normal((1, 1, 128)).astype(np.float16)
+    c = O.OracleCache(cfg)
+    c.append(0, k[:, :, :2], v[:, :, :2])
+    c.append(0, k[:, :, 2:], v[:, :, 2:])
+    out = c.decode(0, q)[0, 0]
+    scores = []
+    for n in range(L):
+        s = 0.0
+        for i in range(64):
+            a = n * 10000.0 ** (-2.0 * i / 128)
+            kx, ky = float(k[0, 0, n, 2 * i]), float(k[0, 0, n, 2 * i + 1])
+            s += float(q[0, 0, 2 * i]) * (kx * math.cos(a) - ky * math.sin(a))
+            s += float(q[0, 0, 2 * i + 1]) * (kx * math.sin(a) + ky * math.cos(a))
+        scores.append(s / math.sqrt(128))
+    m = max(scores)
+    p = [math.exp(x - m) for x in scores]
+    ref = [sum(p[t] * float(v[0, 0, t, ch]) for t in range(L)) / sum(p) for ch in range(128)]
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
