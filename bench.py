@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-workers", type=int, default=0, help="oracle worker processes (0: host cores, at most 16)")
     p.add_argument("--cpu-tokens", type=int, default=0, help="tokens per oracle unit (0: by workload)")
+    p.add_argument("--sink", type=int, default=0, help="attention-sink tokens kept in fp16")
+    p.add_argument("--window", type=int, default=0, help="fp16 window of recent tokens (multiple of 128)")
     return p.parse_args()
 
 
@@ -67,7 +69,7 @@ def is_streamed(wl):
 
 
 class Bench:
-    def __init__(self, wl, splits, steps_total):
+    def __init__(self, wl, splits, steps_total, sink=0, window=0):
         import torch
         import bit_kv_cache_quantize_amd as K
         import synth
@@ -81,7 +83,8 @@ class Bench:
         self.copies = 2 if self.single else 1
         capacity = ceil128(wl.context) + (128 * steps_total if self.streamed else 0)
         cfg = K.make_config(wl.n_layers, wl.batch, wl.n_kv_heads, wl.n_q_heads, capacity, wl.mode,
-                            wl.bits, wl.outliers_per_vec, wl.pre_rope, wl.rope_theta, wl.varn_iters)
+                            wl.bits, wl.outliers_per_vec, wl.pre_rope, wl.rope_theta, wl.varn_iters,
+                            sink_tokens=sink, fp16_window=window)
         self.caches = [K.KVCache(cfg, self.dev) for _ in range(self.copies)]
         for c in self.caches:
             if splits:
@@ -390,7 +393,7 @@ def main():
         print(f"cpu baseline done: {cpu['sample']}", file=sys.stderr, flush=True)
     import torch
     warmup = max(args.warmup, 2 if wl.n_layers == 1 else 1)
-    b = Bench(wl, args.splits, args.steps + warmup)
+    b = Bench(wl, args.splits, args.steps + warmup, args.sink, args.window)
     print("cache built", file=sys.stderr, flush=True)
     ms_step, dec, app, step_bytes = b.run(args.steps, warmup)
     dec_ms = sum(dec) / len(dec)
@@ -436,6 +439,7 @@ def main():
                    "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads, "mode": MODE_NAMES[wl.mode],
                    "bits": wl.bits, "outliers_per_vec": wl.outliers_per_vec, "pre_rope": wl.pre_rope,
                    "varn_iters": wl.varn_iters if wl.mode == 2 else 0,
+                   "sink_tokens": args.sink, "fp16_window": args.window,
                    "step": ("append one 128-token block to every layer, then decode every layer"
                             if b.streamed else "append the whole context to every layer, then decode every layer")},
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),

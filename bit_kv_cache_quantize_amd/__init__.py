@@ -31,6 +31,7 @@ class kvq_config(ctypes.Structure):
         ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
         ("mode", ctypes.c_int32), ("bits", ctypes.c_int32), ("outliers_per_vec", ctypes.c_int32),
         ("pre_rope", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("varn_iters", ctypes.c_int32),
+        ("sink_tokens", ctypes.c_int32), ("fp16_window", ctypes.c_int32),
     ]
 
 
@@ -95,9 +96,10 @@ def _stream(stream):
 
 
 def make_config(n_layers, batch, n_kv_heads, n_q_heads, max_tokens, mode, bits, outliers_per_vec=0,
-                pre_rope=0, rope_theta=10000.0, varn_iters=8, head_dim=KVQ_HEAD_DIM) -> kvq_config:
+                pre_rope=0, rope_theta=10000.0, varn_iters=8, head_dim=KVQ_HEAD_DIM, sink_tokens=0,
+                fp16_window=0) -> kvq_config:
     return kvq_config(n_layers, batch, n_kv_heads, n_q_heads, head_dim, max_tokens, mode, bits,
-                      outliers_per_vec, pre_rope, rope_theta, varn_iters)
+                      outliers_per_vec, pre_rope, rope_theta, varn_iters, sink_tokens, fp16_window)
 
 
 def kvq_cache_bytes(cfg: kvq_config) -> int:

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/kvq.h: validation, the device
 // buffer layout, RoPE tables, split planning and kernel launches on the
 // caller's stream. No device memory is allocated here.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -156,6 +157,9 @@ struct kvq_cache_s {
   std::vector<float2> lut_host;     // [layer][kv_head][2][kNuqLutStride]
   std::vector<float> rope_host;     // base table then offset table
   int splits_override = 0;
+  int sink = 0, window = 0;         // sink tokens, fp16 window (tokens)
+  int ring_rows = kvq::kT;          // fp16 ring of body tokens per tensor: window + 128
+  int tail_rows = kvq::kT;          // fp16 rows per tensor: sink + ring
 };
 
 namespace {
@@ -190,11 +194,18 @@ kvq_status validate_config(const kvq_config* c) {
       return fail(KVQ_ERR_ARG, "KVARN mode supports neither outliers nor pre-RoPE keys");
     if (c->varn_iters < 0 || c->varn_iters > 64) return fail(KVQ_ERR_ARG, "varn_iters must be in 0..64");
   }
+  if (c->sink_tokens < 0 || c->sink_tokens > KVQ_MAX_SINK)
+    return fail(KVQ_ERR_ARG, "sink_tokens must be in 0..%d (got %d)", KVQ_MAX_SINK, c->sink_tokens);
+  if (c->fp16_window < 0 || c->fp16_window > KVQ_MAX_WINDOW || c->fp16_window % KVQ_BLOCK_TOKENS != 0)
+    return fail(KVQ_ERR_ARG, "fp16_window must be a multiple of 128 in 0..%d (got %d)", KVQ_MAX_WINDOW, c->fp16_window);
   const double rec = kvq::make_layout(c->mode, c->bits, c->outliers_per_vec).rec_bytes;
   const double total = rec * c->n_layers * c->batch * c->n_kv_heads * (c->max_tokens / 128.0);
   if (total > 4.0e12) return fail(KVQ_ERR_ARG, "cache larger than 4 TB requested");
   return KVQ_OK;
 }
+
+int ring_rows_of(const kvq_config* c) { return c->fp16_window + KVQ_BLOCK_TOKENS; }
+int tail_rows_of(const kvq_config* c) { return c->sink_tokens + ring_rows_of(c); }
 
 Regions regions(const kvq_config* c) {
   Regions r{};
@@ -203,13 +214,14 @@ Regions regions(const kvq_config* c) {
   const size_t units = (size_t)c->batch * c->n_kv_heads;
   r.layer_rec = units * r.max_blocks * L.rec_bytes;
   r.rec = r.layer_rec * c->n_layers;
-  r.layer_tail = units * 2 * kvq::kT * kvq::kD * sizeof(__half);
+  r.layer_tail = units * 2 * (size_t)tail_rows_of(c) * kvq::kD * sizeof(__half);
   r.tail = r.layer_tail * c->n_layers;
   r.cb = c->mode == KVQ_MODE_NUQ ? (size_t)c->n_layers * c->n_kv_heads * 2 * kvq::kCbStride * sizeof(float) : 0;
   r.lut = c->mode == KVQ_MODE_NUQ ? (size_t)c->n_layers * c->n_kv_heads * 2 * kvq::kNuqLutStride * sizeof(float2) : 0;
   r.rope_base = c->pre_rope ? (size_t)(r.max_blocks + 1) * 64 * 2 * sizeof(float) : 0;
   r.rope_off = c->pre_rope ? ((size_t)128 * 64 * 2 + 64) * sizeof(float) : 0;   // offsets, then theta_i
-  r.work = (size_t)c->batch * c->n_q_heads * KVQ_MAX_SPLITS * kvq::kPartStride * sizeof(float);
+  // split partials: up to KVQ_MAX_SPLITS splits plus the fp16 part's partial
+  r.work = (size_t)c->batch * c->n_q_heads * (KVQ_MAX_SPLITS + 1) * kvq::kPartStride * sizeof(float);
   size_t pos = 0;
   auto place = [&](size_t size) { pos = align_up(pos, 256); const size_t at = pos; pos += size; return at; };
   r.off_rec = place(r.rec);
@@ -309,6 +321,10 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_buf, size_t bytes, vo
   c->off_rope_base = r.off_rope_base;
   c->off_rope_off = r.off_rope_off;
   c->off_work = r.off_work;
+  c->sink = cfg->sink_tokens;
+  c->window = cfg->fp16_window;
+  c->ring_rows = ring_rows_of(cfg);
+  c->tail_rows = tail_rows_of(cfg);
   c->len.assign(cfg->n_layers, 0);
   c->cb_loaded.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2, 0);
   c->cb_host.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2 * kvq::kCbStride, 0.f);
@@ -317,13 +333,14 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_buf, size_t bytes, vo
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (cfg->pre_rope) {
     // RoPE angles n * theta_i, theta_i = theta^(-2i/128), evaluated in double precision:
-    // base rows for n = 128 * block and offset rows for n = 0..127 (KVQuant notes 1.3)
+    // base rows for n = sink + 128 * block (the first position of body block `block`) and
+    // offset rows for n = 0..127 (KVQuant notes 1.3)
     const int nb = r.max_blocks + 1;
     c->rope_host.resize((size_t)nb * 128 + 128 * 128 + 64);
     for (int i = 0; i < 64; ++i) {
       const double th = std::pow((double)cfg->rope_theta, -2.0 * i / 128.0);
       for (int blk = 0; blk < nb; ++blk) {
-        const double ang = (double)blk * 128.0 * th;
+        const double ang = ((double)cfg->sink_tokens + (double)blk * 128.0) * th;
         c->rope_host[((size_t)blk * 64 + i) * 2] = (float)std::cos(ang);
         c->rope_host[((size_t)blk * 64 + i) * 2 + 1] = (float)std::sin(ang);
       }
@@ -407,9 +424,15 @@ kvq_status kvq_quantize_append(kvq_cache c, int layer, const void* k_f16, const 
           return fail(KVQ_ERR_STATE, "NUQ codebook of layer %d kv head %d (%s) not loaded", layer, h, w ? "V" : "K");
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int t0 = len % KVQ_BLOCK_TOKENS;
-  const int nb = (t0 + n_new) / KVQ_BLOCK_TOKENS;
-  const int rem = (t0 + n_new) % KVQ_BLOCK_TOKENS;
+  // positions < sink are sink tokens; body token u sits at position sink + u. Body block j
+  // is quantized once the body holds at least 128 (j + 1) + window tokens.
+  const int S = c->sink, W = c->window;
+  const int n_sink = std::max(0, std::min(S - len, n_new));
+  const int u_old = std::max(0, len - S), u_new = std::max(0, len + n_new - S);
+  const int nq_old = std::max(0, u_old - W) / KVQ_BLOCK_TOKENS;
+  const int nq_new = std::max(0, u_new - W) / KVQ_BLOCK_TOKENS;
+  const int nb = nq_new - nq_old;
+  const int in_row0 = S - len;   // input row of body token u
   __half* tail = reinterpret_cast<__half*>(c->base + c->off_tail + (size_t)layer * c->layer_tail_bytes);
   if (nb > 0) {
     kvq::QuantArgs a{};
@@ -419,8 +442,12 @@ kvq_status kvq_quantize_append(kvq_cache c, int layer, const void* k_f16, const 
     a.k_in = static_cast<const __half*>(k_f16);
     a.v_in = static_cast<const __half*>(v_f16);
     a.n_new = n_new;
-    a.t0 = t0;
-    a.blk0 = len / KVQ_BLOCK_TOKENS;
+    a.blk0 = nq_old;
+    a.u_old = u_old;
+    a.in_row0 = in_row0;
+    a.sink = S;
+    a.ring_rows = c->ring_rows;
+    a.tail_rows = c->tail_rows;
     a.Hkv = cfg.n_kv_heads;
     a.max_blocks = c->max_blocks;
     a.rec = c->base + c->off_rec + (size_t)layer * c->layer_rec_bytes;
@@ -430,15 +457,22 @@ kvq_status kvq_quantize_append(kvq_cache c, int layer, const void* k_f16, const 
     st = hip_check(kvq::launch_quantize(cfg.mode, cfg.bits, a, nb, cfg.batch, s), "launch quantize");
     if (st != KVQ_OK) return st;
   }
+  // new tokens that stay fp16: sink tokens, and body tokens of blocks not quantized now
   kvq::TailArgs ta{};
   ta.k_in = static_cast<const __half*>(k_f16);
   ta.v_in = static_cast<const __half*>(v_f16);
   ta.n_new = n_new;
   ta.Hkv = cfg.n_kv_heads;
   ta.tail = tail;
-  if (nb == 0) { ta.src0 = 0; ta.dst0 = t0; ta.count = n_new; }
-  else { ta.src0 = n_new - rem; ta.dst0 = 0; ta.count = rem; }
-  if (ta.count > 0) {
+  ta.n_sink = n_sink;
+  ta.sink_row0 = len;
+  ta.ring_u0 = std::max(u_old, nq_new * KVQ_BLOCK_TOKENS);
+  ta.ring_count = std::max(0, u_new - ta.ring_u0);
+  ta.ring_src0 = ta.ring_u0 + in_row0;
+  ta.sink = S;
+  ta.ring_rows = c->ring_rows;
+  ta.tail_rows = c->tail_rows;
+  if (ta.n_sink + ta.ring_count > 0) {
     st = hip_check(kvq::launch_tail(ta, cfg.batch, s), "launch tail copy");
     if (st != KVQ_OK) return st;
   }
@@ -476,7 +510,12 @@ kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, fl
   const kvq_config& cfg = c->cfg;
   const int L = c->len[layer];
   if (L == 0) return fail(KVQ_ERR_STATE, "layer %d holds no tokens", layer);
-  const int nblk = L / KVQ_BLOCK_TOKENS, tail_n = L % KVQ_BLOCK_TOKENS;
+  // quantized blocks and fp16 tokens (see kvq_quantize_append)
+  const int U = std::max(0, L - c->sink);
+  const int nblk = std::max(0, U - c->window) / KVQ_BLOCK_TOKENS;
+  const int fp16_body = U - nblk * KVQ_BLOCK_TOKENS;
+  const bool side = c->sink > 0 || c->window > 0;   // the fp16 part gets its own kernel
+  const int tail_n = side ? 0 : fp16_body;
   const int units = cfg.batch * cfg.n_kv_heads;
   const int group = cfg.n_q_heads / cfg.n_kv_heads;
   const bool tab = kvq::tab_supported(cfg.mode, cfg.bits, group, cfg.pre_rope);
@@ -496,12 +535,14 @@ kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, fl
     bps = (nblk + splits - 1) / splits;
     splits = (nblk + bps - 1) / bps;
   }
-  if (part && splits > 1) {
-    const size_t need = (size_t)cfg.batch * cfg.n_q_heads * splits * kvq::kPartStride * sizeof(float);
+  // partial slots per (sequence, query head): the splits, plus one for the fp16 part
+  const int part_slots = side ? (nblk > 0 ? splits + 1 : 1) : splits;
+  if (part && part_slots > 1) {
+    const size_t need = (size_t)cfg.batch * cfg.n_q_heads * part_slots * kvq::kPartStride * sizeof(float);
     if (need > part_limit)
       return fail(KVQ_ERR_SIZE, "%d splits x %d sequences x %d query heads need %zu bytes of split partials; "
                   "the static scratch holds %zu (lower the split count with kvq_set_decode_splits)",
-                  splits, cfg.batch, cfg.n_q_heads, need, part_limit);
+                  part_slots, cfg.batch, cfg.n_q_heads, need, part_limit);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   kvq::DecodeArgs a{};
@@ -522,6 +563,13 @@ kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, fl
   a.tail_n = tail_n;
   a.splits = splits;
   a.blocks_per_split = bps;
+  a.part_slots = part_slots;
+  a.sink_n = std::min(L, c->sink);
+  a.fp16_u0 = nblk * KVQ_BLOCK_TOKENS;
+  a.fp16_n = side ? fp16_body : 0;
+  a.ring_rows = c->ring_rows;
+  a.tail_rows = c->tail_rows;
+  a.side_slot = nblk > 0 ? splits : -1;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
   a.scale_log2 = scale * 1.4426950408889634f;
   if (cfg.outliers_per_vec > 0) {
@@ -530,15 +578,21 @@ kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, fl
     const uint32_t blob = c->lay.vo_idx + 128u * cfg.outliers_per_vec - c->lay.ko_val;
     a.wave_lds = (int)(((blob + 15u) & ~15u) + (tab ? 0u : 1024u + 512u + 512u));
   }
-  if (tab)
-    st = hip_check(kvq::launch_decode_tab(cfg.mode, cfg.bits, a, cfg.batch, s), "launch decode");
-  else if (kvq::mfma_supported(cfg.mode, cfg.bits, cfg.pre_rope, cfg.outliers_per_vec))
-    st = hip_check(kvq::launch_decode_mfma(cfg.mode, cfg.bits, group, a, cfg.batch, s), "launch decode");
-  else
-    st = hip_check(kvq::launch_decode(cfg.mode, cfg.bits, group, cfg.pre_rope, a, cfg.batch, s), "launch decode");
-  if (st != KVQ_OK) return st;
-  if (splits > 1) {
-    st = hip_check(kvq::launch_combine(a.part, out, cfg.n_q_heads, splits, cfg.batch, s), "launch split combine");
+  if (nblk > 0 || !side) {
+    if (tab)
+      st = hip_check(kvq::launch_decode_tab(cfg.mode, cfg.bits, a, cfg.batch, s), "launch decode");
+    else if (kvq::mfma_supported(cfg.mode, cfg.bits, cfg.pre_rope, cfg.outliers_per_vec))
+      st = hip_check(kvq::launch_decode_mfma(cfg.mode, cfg.bits, group, a, cfg.batch, s), "launch decode");
+    else
+      st = hip_check(kvq::launch_decode(cfg.mode, cfg.bits, group, cfg.pre_rope, a, cfg.batch, s), "launch decode");
+    if (st != KVQ_OK) return st;
+  }
+  if (side) {
+    st = hip_check(kvq::launch_decode_fp16(group, cfg.pre_rope, a, cfg.batch, s), "launch fp16 decode");
+    if (st != KVQ_OK) return st;
+  }
+  if (part_slots > 1) {
+    st = hip_check(kvq::launch_combine(a.part, out, cfg.n_q_heads, part_slots, cfg.batch, s), "launch split combine");
     if (st != KVQ_OK) return st;
   }
   return ok();
@@ -590,8 +644,8 @@ kvq_status kvq_tail_span(kvq_cache c, int layer, int b, int kv_head, size_t* off
     return fail(KVQ_ERR_ARG, "tail coordinates out of range");
   if (!offset || !bytes) return fail(KVQ_ERR_ARG, "offset or bytes is NULL");
   const size_t unit = (size_t)b * c->cfg.n_kv_heads + kv_head;
-  *offset = c->off_tail + (size_t)layer * c->layer_tail_bytes + unit * 2 * kvq::kT * kvq::kD * sizeof(__half);
-  *bytes = 2 * kvq::kT * kvq::kD * sizeof(__half);
+  *offset = c->off_tail + (size_t)layer * c->layer_tail_bytes + unit * 2 * (size_t)c->tail_rows * kvq::kD * sizeof(__half);
+  *bytes = 2 * (size_t)c->tail_rows * kvq::kD * sizeof(__half);
   return ok();
 }
 
@@ -602,11 +656,15 @@ kvq_status kvq_decode_bytes(kvq_cache c, int layer, size_t* bytes) {
   const kvq_config& cfg = c->cfg;
   const size_t units = (size_t)cfg.batch * cfg.n_kv_heads;
   const int L = c->len[layer];
-  const size_t nblk = L / KVQ_BLOCK_TOKENS, tail_n = L % KVQ_BLOCK_TOKENS;
+  const int U = std::max(0, L - c->sink);
+  const size_t nblk = std::max(0, U - c->window) / KVQ_BLOCK_TOKENS;
+  const size_t tail_n = (size_t)(U - (int)nblk * KVQ_BLOCK_TOKENS) + (size_t)std::min(L, c->sink);   // fp16 tokens
   size_t n = units * (nblk * c->lay.payload + tail_n * 2 * KVQ_HEAD_DIM * sizeof(__half));
   n += (size_t)cfg.batch * cfg.n_q_heads * KVQ_HEAD_DIM * (sizeof(__half) + sizeof(float));
   if (cfg.mode == KVQ_MODE_NUQ) n += (size_t)cfg.n_kv_heads * 2 * (1u << cfg.bits) * sizeof(float);
-  if (cfg.pre_rope) n += (nblk + (tail_n ? 1 : 0)) * 64 * 2 * sizeof(float) + 128 * 64 * 2 * sizeof(float);
+  if (cfg.pre_rope)
+    n += (nblk + ((size_t)(U - (int)nblk * KVQ_BLOCK_TOKENS) + 127) / 128) * 64 * 2 * sizeof(float) +
+         128 * 64 * 2 * sizeof(float);
   *bytes = n;
   return ok();
 }

@@ -117,10 +117,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww)
       if (s_m[ww][h] != -INFINITY) L = fmaf(exp2f(s_m[ww][h] - M), s_l[ww][h], L);
-    if (a.splits == 1) {
+    if (a.part_slots == 1) {
       a.out[row * kD + c] = o / L;          // one split: this workgroup saw every token
     } else {
-      float* part = a.part + (row * a.splits + split) * kPartStride;
+      float* part = a.part + (row * a.part_slots + split) * kPartStride;
       part[2 + c] = o;
       if (c == 0) { part[0] = M; part[1] = L; }
     }

@@ -645,10 +645,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int s = 0; s < 6; ++s)
       if (s_m[s][h] != -INFINITY) L = fmaf(exp2f(s_m[s][h] - M), s_l[s][h], L);
-    if (a.splits == 1) {
+    if (a.part_slots == 1) {
       a.out[row * kD + c] = o / L;
     } else {
-      float* part = a.part + (row * a.splits + split) * kPartStride;
+      float* part = a.part + (row * a.part_slots + split) * kPartStride;
       part[2 + c] = o;
       if (c == 0) { part[0] = M; part[1] = L; }
     }

@@ -677,10 +677,10 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
       L = fmaf(sw, s_l[ww], L);
     }
     const size_t row = (size_t)b * a.Hq + kvh;
-    if (a.splits == 1) {
+    if (a.part_slots == 1) {
       a.out[row * kD + c] = o / L;
     } else {
-      float* part = a.part + (row * a.splits + split) * kPartStride;
+      float* part = a.part + (row * a.part_slots + split) * kPartStride;
       part[2 + c] = o;
       if (c == 0) { part[0] = M; part[1] = L; }
     }

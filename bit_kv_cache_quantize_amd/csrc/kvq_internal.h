@@ -35,23 +35,34 @@ struct RecordLayout {
 
 RecordLayout make_layout(int mode, int bits, int k_out);
 
+// fp16 rows of one (layer, sequence, kv head): K [tail_rows][128] then V [tail_rows][128];
+// rows 0 .. sink-1 hold the attention-sink tokens, row sink + (u mod ring_rows) holds body
+// token u (the tokens after the sink, numbered from 0) while it is not quantized.
 struct QuantArgs {
   RecordLayout lay;
   int k_out, varn_iters;
   const __half* k_in;    // [B][Hkv][n_new][128]
   const __half* v_in;
-  int n_new, t0, blk0;   // t0: tokens already in the tail; blk0: index of the block being completed
+  int n_new, blk0;       // blk0: body block of the launch's first block
+  int u_old;             // body tokens appended before this call: u < u_old are in the ring
+  int in_row0;           // input row of body token u (u >= u_old) is u + in_row0
+  int sink, ring_rows, tail_rows;
   int Hkv, max_blocks;
   uint8_t* rec;          // records of the layer, [B][Hkv][max_blocks]
-  const __half* tail;    // tails of the layer, [B][Hkv][2][128][128]
+  const __half* tail;    // fp16 rows of the layer, [B][Hkv][2][tail_rows][128]
   const float* cb;       // codebooks of the layer, [Hkv][2][kCbStride]
   const float2* nuq_lut; // NUQ code tables of the layer, [Hkv][2][kNuqLutStride] (NUQ only)
 };
 
+// Staging of new fp16 rows: input rows [0, n_sink) to tail rows sink_row0 + i (sink
+// tokens), input rows [ring_src0, ring_src0 + ring_count) to body tokens ring_u0 + i.
 struct TailArgs {
   const __half* k_in;
   const __half* v_in;
-  int n_new, src0, dst0, count, Hkv;
+  int n_new, Hkv;
+  int n_sink, sink_row0;
+  int ring_src0, ring_count, ring_u0;
+  int sink, ring_rows, tail_rows;
   __half* tail;
 };
 
@@ -61,15 +72,19 @@ struct DecodeArgs {
   const uint8_t* rec;
   const __half* tail;
   const float* cb;
-  const float* rope_base;   // [max_blocks + 1][64][2]: cos, sin of (128 * block) * theta_i
+  const float* rope_base;   // [max_blocks + 1][64][2]: cos, sin of (sink + 128 * block) * theta_i
   const float* rope_off;    // [64][128][2]: cos, sin of j * theta_i (pair-major); then theta_i[64]
   const __half* q;          // [B][Hq][128]
   float* part;              // [B][Hq][splits][2 + 128]
   float* out;               // [B][Hq][128]
   int Hkv, Hq, max_blocks;
   int nblk, tail_n, splits, blocks_per_split;
+  int part_slots;           // split partials per (sequence, query head); 1: write out directly
   float scale_log2;         // softmax scale * log2(e)
   int wave_lds;             // dynamic LDS bytes per wave for outlier staging (0 without outliers)
+  // fp16 part outside the blocks (sink tokens and the body tokens not yet quantized),
+  // decoded by its own kernel when a sink or a window is configured (tail_n is then 0)
+  int sink_n, fp16_u0, fp16_n, ring_rows, tail_rows, side_slot;
 };
 
 hipError_t launch_quantize(int mode, int bits, const QuantArgs& a, int n_blocks, int batch,
@@ -84,5 +99,7 @@ hipError_t launch_decode_mfma(int mode, int bits, int group, const DecodeArgs& a
 bool tab_supported(int mode, int bits, int group, int rope);
 hipError_t launch_decode_tab(int mode, int bits, const DecodeArgs& a, int batch, hipStream_t s);
 hipError_t launch_combine(const float* part, float* out, int Hq, int splits, int batch, hipStream_t s);
+// fp16 sink and window tokens of every (sequence, kv head): partial slot side_slot (or out).
+hipError_t launch_decode_fp16(int group, int rope, const DecodeArgs& a, int batch, hipStream_t s);
 
 }  // namespace kvq

@@ -496,17 +496,18 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
   if (k_out > 0)
     for (int i = tid; i < kD * 4; i += kThreads) (&sm.omask[0][0])[i] = 0u;
 
-  // ---- load the block: rows < t0 of the first block come from the fp16 tail
+  // ---- load the block: body tokens appended before this call come from the fp16 ring
   Tile<MODE == KVARN> X;
   {
     const __half* in = (tensor ? a.v_in : a.k_in) + unit * (size_t)a.n_new * kD;
-    const __half* tl = a.tail + unit * (2 * kT * kD) + (size_t)tensor * kT * kD;
+    const __half* tl = a.tail + unit * (size_t)(2 * a.tail_rows * kD) + (size_t)tensor * a.tail_rows * kD;
+    const int u0 = (a.blk0 + j) * kT;   // body token of the block's first row
     uint4 raw[8];
-    if (j > 0 || a.t0 == 0) {
+    if (u0 >= a.u_old) {
       // (uniform) every row from the new input: a buffer resource over the block's 128 rows,
       // the lane's offset in a register and each row's offset in the scalar offset operand
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<__half*>(in + ((size_t)j * kT - a.t0) * kD), (short)0, kT * kD * 2, 0x00020000);
+          const_cast<__half*>(in + ((size_t)u0 + a.in_row0) * kD), (short)0, kT * kD * 2, 0x00020000);
       const uint32_t lo = (uint32_t)(((32 * w + r) * kD + 8 * g) * 2);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -516,8 +517,9 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int t = 32 * w + 4 * i + r;
-        const __half* src = t < a.t0 ? tl + (size_t)t * kD : in + ((size_t)t - a.t0) * kD;
+        const int u = u0 + 32 * w + 4 * i + r;
+        const __half* src = u < a.u_old ? tl + (size_t)(a.sink + u % a.ring_rows) * kD
+                                        : in + ((size_t)u + a.in_row0) * kD;
         raw[i] = *reinterpret_cast<const uint4*>(src + 8 * g);
       }
     }
@@ -964,16 +966,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MODE =
   }
 }
 
+// New fp16 rows into the (layer, sequence, kv head)'s fp16 region: sink tokens to their
+// rows, body tokens to their ring slots.
 __global__ __launch_bounds__(kThreads) void tail_kernel(TailArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t unit = (size_t)b * a.Hkv + h;
+  const int n_rows = a.n_sink + a.ring_count;
   for (int tensor = 0; tensor < 2; ++tensor) {
     const __half* in = (tensor ? a.v_in : a.k_in) + unit * (size_t)a.n_new * kD;
-    __half* tl = a.tail + unit * (2 * kT * kD) + (size_t)tensor * kT * kD;
-    for (int id = threadIdx.x; id < a.count * 16; id += kThreads) {
-      const int row = id >> 4, ch = (id & 15) * 8;
-      *reinterpret_cast<uint4*>(tl + (size_t)(a.dst0 + row) * kD + ch) =
-          *reinterpret_cast<const uint4*>(in + (size_t)(a.src0 + row) * kD + ch);
+    __half* tl = a.tail + unit * (size_t)(2 * a.tail_rows * kD) + (size_t)tensor * a.tail_rows * kD;
+    for (int id = threadIdx.x; id < n_rows * 16; id += kThreads) {
+      const int i = id >> 4, ch = (id & 15) * 8;
+      int src, dst;
+      if (i < a.n_sink) {
+        src = i;
+        dst = a.sink_row0 + i;
+      } else {
+        src = a.ring_src0 + (i - a.n_sink);
+        dst = a.sink + (a.ring_u0 + (i - a.n_sink)) % a.ring_rows;
+      }
+      *reinterpret_cast<uint4*>(tl + (size_t)dst * kD + ch) = *reinterpret_cast<const uint4*>(in + (size_t)src * kD + ch);
     }
   }
 }

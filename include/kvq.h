@@ -63,6 +63,8 @@ typedef enum {
 #define KVQ_MAX_GROUP 8
 #define KVQ_MAX_SPLITS 64
 #define KVQ_STATIC_SCRATCH_BYTES (8u << 20)
+#define KVQ_MAX_SINK 128
+#define KVQ_MAX_WINDOW 8192
 
 typedef struct {
   int32_t n_layers;         /* >= 1 */
@@ -77,6 +79,11 @@ typedef struct {
   int32_t pre_rope;         /* 1: keys are stored before RoPE and rotated at decode; 0 with KVARN */
   float rope_theta;         /* RoPE base (10000 in the pages), > 0 when pre_rope */
   int32_t varn_iters;       /* KVARN: 0..64 Sinkhorn iterations (8 in the pages) */
+  int32_t sink_tokens;      /* 0..KVQ_MAX_SINK: the first tokens of every sequence stay fp16
+                               and form no block (KVQuant notes 3.5: attention sink) */
+  int32_t fp16_window;      /* 0..KVQ_MAX_WINDOW, a multiple of 128: a block is quantized only
+                               once this many newer tokens follow it (KVQuant notes 4.2:
+                               KIVI's full-precision window of recent tokens) */
 } kvq_config;
 
 typedef struct kvq_cache_s* kvq_cache;   /* opaque host handle; owns no device memory */
@@ -117,9 +124,12 @@ kvq_status kvq_codebook_load(kvq_cache cache, int layer, int kv_head, int which,
  * Append n_new tokens to every sequence of one layer.
  * k_f16, v_f16: dev, fp16 [batch][n_kv_heads][n_new][128], contiguous; keys
  * before RoPE when pre_rope. Tokens take the next absolute positions.
- * Every time a sequence has 128 new tokens they are quantized as one block
- * (KVQuant notes Algorithm 1; KVarN method steps; blog 4.2); the rest stay in
- * the fp16 tail (blog 5.2). n_new = 0 is a no-op.
+ * Positions 0 .. sink_tokens-1 are sink tokens, kept in fp16. The later tokens
+ * (body token u at position sink_tokens + u) form 128-token blocks; body block j
+ * is quantized (KVQuant notes Algorithm 1; KVarN method steps; blog 4.2) as soon
+ * as the body holds 128 (j + 1) + fp16_window tokens; until then its tokens stay
+ * in fp16 (blog 5.2). With sink_tokens = fp16_window = 0 a block is quantized
+ * when it is complete. n_new = 0 is a no-op.
  * Errors: KVQ_ERR_CAPACITY if length + n_new > max_tokens; KVQ_ERR_STATE in
  * NUQ mode unless both codebooks of every kv head of the layer are loaded.
  */
@@ -202,7 +212,11 @@ kvq_status kvq_set_decode_splits(kvq_cache cache, int splits);
 kvq_status kvq_block_span(kvq_cache cache, int layer, int b, int kv_head, int block,
                           size_t* offset, size_t* bytes);
 
-/* Byte range of the fp16 tail of (layer, b, kv head): K [128][128] then V [128][128]. */
+/*
+ * Byte range of the fp16 rows of (layer, b, kv head): K [R][128] then V [R][128] with
+ * R = sink_tokens + fp16_window + 128. Row p < sink_tokens holds sink token p; row
+ * sink_tokens + (u mod (fp16_window + 128)) holds body token u while it is not quantized.
+ */
 kvq_status kvq_tail_span(kvq_cache cache, int layer, int b, int kv_head, size_t* offset,
                          size_t* bytes);
 

@@ -13,15 +13,17 @@ def ceil128(n: int) -> int:
     return max(128, (n + 127) // 128 * 128)
 
 
-def lib_cfg(wl, max_tokens=None):
+def lib_cfg(wl, max_tokens=None, sink=0, window=0):
     import bit_kv_cache_quantize_amd as K
     return K.make_config(wl.n_layers, wl.batch, wl.n_kv_heads, wl.n_q_heads, max_tokens or ceil128(wl.context),
-                         wl.mode, wl.bits, wl.outliers_per_vec, wl.pre_rope, wl.rope_theta, wl.varn_iters)
+                         wl.mode, wl.bits, wl.outliers_per_vec, wl.pre_rope, wl.rope_theta, wl.varn_iters,
+                         sink_tokens=sink, fp16_window=window)
 
 
-def oracle_cfg(wl, max_tokens=None):
+def oracle_cfg(wl, max_tokens=None, sink=0, window=0):
     return O.Config(wl.n_layers, wl.batch, wl.n_kv_heads, wl.n_q_heads, max_tokens or ceil128(wl.context),
-                    wl.mode, wl.bits, wl.outliers_per_vec, wl.pre_rope, wl.rope_theta, wl.varn_iters)
+                    wl.mode, wl.bits, wl.outliers_per_vec, wl.pre_rope, wl.rope_theta, wl.varn_iters,
+                    sink_tokens=sink, fp16_window=window)
 
 
 def host_kv(wl, layer: int, t0: int, n: int):

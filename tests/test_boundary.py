@@ -40,6 +40,8 @@ def cfg(**kw):
     dict(outliers_per_vec=9), dict(outliers_per_vec=-1), dict(pre_rope=1, rope_theta=0.0),
     dict(mode=K.KVQ_MODE_KVARN, outliers_per_vec=1), dict(mode=K.KVQ_MODE_KVARN, pre_rope=1),
     dict(mode=K.KVQ_MODE_KVARN, varn_iters=65), dict(n_layers=0), dict(batch=0),
+    dict(sink_tokens=129), dict(sink_tokens=-1), dict(fp16_window=100), dict(fp16_window=8320),
+    dict(fp16_window=-128),
 ])
 def test_invalid_configs_are_rejected(kw):
     with pytest.raises(K.KvqError) as e:
@@ -48,24 +50,26 @@ def test_invalid_configs_are_rejected(kw):
     assert K.kvq_last_error()
 
 
-@pytest.mark.parametrize("mode,bits,k_out,pre_rope", [
-    (K.KVQ_MODE_RTN, 4, 0, 0), (K.KVQ_MODE_NUQ, 3, 1, 1), (K.KVQ_MODE_KVARN, 2, 0, 0),
-    (K.KVQ_MODE_SYM_INT4, 4, 0, 0), (K.KVQ_MODE_RTN, 2, 1, 1), (K.KVQ_MODE_NUQ, 4, 8, 0)])
-def test_cache_bytes_matches_documented_record_layout(mode, bits, k_out, pre_rope):
-    c = cfg(mode=mode, bits=bits, outliers_per_vec=k_out, pre_rope=pre_rope)
+@pytest.mark.parametrize("mode,bits,k_out,pre_rope,sink,window", [
+    (K.KVQ_MODE_RTN, 4, 0, 0, 0, 0), (K.KVQ_MODE_NUQ, 3, 1, 1, 0, 0), (K.KVQ_MODE_KVARN, 2, 0, 0, 0, 0),
+    (K.KVQ_MODE_SYM_INT4, 4, 0, 0, 0, 0), (K.KVQ_MODE_RTN, 2, 1, 1, 0, 0), (K.KVQ_MODE_NUQ, 4, 8, 0, 0, 0),
+    (K.KVQ_MODE_RTN, 2, 1, 1, 1, 0), (K.KVQ_MODE_KVARN, 4, 0, 0, 4, 256)])
+def test_cache_bytes_matches_documented_record_layout(mode, bits, k_out, pre_rope, sink, window):
+    c = cfg(mode=mode, bits=bits, outliers_per_vec=k_out, pre_rope=pre_rope, sink_tokens=sink, fp16_window=window)
     _, rec = R.layout(mode, bits, k_out)
     units = c.batch * c.n_kv_heads
     nblk = c.max_tokens // 128
 
     def a(x):
         return (x + 255) // 256 * 256
-    total = a(rec * units * nblk * c.n_layers) + a(units * 65536 * c.n_layers)
+    rows = sink + window + 128        # fp16 rows per tensor: sink tokens, then the ring
+    total = a(rec * units * nblk * c.n_layers) + a(units * 2 * rows * 256 * c.n_layers)
     if mode == K.KVQ_MODE_NUQ:
         total += a(c.n_layers * c.n_kv_heads * 2 * 32 * 4)   # entries, then decision thresholds
         total += a(c.n_layers * c.n_kv_heads * 2 * 1032 * 8)   # code tables over the thresholds
     if pre_rope:
         total += a((nblk + 1) * 512) + a(128 * 512 + 256)
-    total += a(c.batch * c.n_q_heads * K.KVQ_MAX_SPLITS * 130 * 4)
+    total += a(c.batch * c.n_q_heads * (K.KVQ_MAX_SPLITS + 1) * 130 * 4)
     assert K.kvq_cache_bytes(c) == total
 
 

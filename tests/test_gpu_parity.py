@@ -407,3 +407,80 @@ def test_parity_extreme_magnitudes(K, case, kscale, vscale):
     assert np.all(np.isfinite(got))
     worst = H.attention_close(got, oc.decode(0, q))
     _say(f"  ok: worst attention error {worst:.2e} of the bar")
+
+
+def run_case_sw(K, wl, chunks, sink, window, scale=0.0, splits=0):
+    """run_case with attention-sink tokens and an fp16 window: the blocks, the fp16 rows
+    (sink rows and the ring slots of the body tokens not yet quantized) and the decode."""
+    L = sum(chunks)
+    _say(f"case {wl.name} B={wl.batch} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} L={L} chunks={chunks} "
+         f"sink={sink} window={window}")
+    max_tokens = H.ceil128(L)
+    cache = K.KVCache(H.lib_cfg(wl, max_tokens, sink, window))
+    oc = O.OracleCache(H.oracle_cfg(wl, max_tokens, sink, window))
+    if wl.mode == synth.MODE_NUQ:
+        for (h, w), cb in H.codebooks(wl, 0).items():
+            cache.codebook_load(0, h, w, cb)
+            oc.load_codebook(0, h, w, cb)
+    pos = 0
+    q = H.host_q(wl, 0)
+    out = torch.empty((wl.batch, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
+    if splits:
+        cache.set_splits(splits)
+    for n in chunks:
+        k, v = H.host_kv(wl, 0, pos, n)
+        cache.append(0, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        oc.append(0, k, v)
+        pos += n
+        # decode after every append: the fp16 part and the blocks change shape as tokens age
+        cache.decode(0, torch.from_numpy(q).cuda(), out, softmax_scale=scale)
+        torch.cuda.synchronize()
+        stats = H.RecordStats()
+        for b in range(wl.batch):
+            for h in range(wl.n_kv_heads):
+                u = b * wl.n_kv_heads + h
+                for j, blk in enumerate(oc.blocks[0][u]):
+                    got = cache.block_bytes(0, b, h, j).cpu().numpy()
+                    H.compare_record(got, blk, oc.cfg, stats, where=f"L={pos} b{b} h{h} block {j}")
+                    if wl.mode == synth.MODE_KVARN:
+                        oc.blocks[0][u][j] = H.kvarn_block_from_record(got, oc.cfg)
+                rows = cache.tail_bytes(0, b, h).cpu().numpy().view(np.float16).reshape(2, -1, 128)
+                R = window + 128
+                ns = min(pos, sink)
+                assert np.array_equal(rows[0, :ns], oc.sink_k[0][u]) and np.array_equal(rows[1, :ns], oc.sink_v[0][u])
+                u0 = 128 * len(oc.blocks[0][u])
+                slots = sink + (u0 + np.arange(oc.tail_k[0][u].shape[0])) % R
+                assert np.array_equal(rows[0, slots], oc.tail_k[0][u]), f"L={pos} fp16 keys"
+                assert np.array_equal(rows[1, slots], oc.tail_v[0][u]), f"L={pos} fp16 values"
+        worst = H.attention_close(out.cpu().numpy(), oc.decode(0, q, scale=scale))
+    _say(f"  ok: worst attention error {worst:.2e} of the bar")
+
+
+SW_CASES = {
+    "table_rtn2_rope_out1": (small("c5_llama7b_1m_rtn2", n_layers=1, batch=2, n_q_heads=2, n_kv_heads=2),
+                             [1, 200, 300, 77]),
+    "table_nuq3_rope_out1": (small("c2_llama7b_layer_32k_nuq3", n_q_heads=2, n_kv_heads=2, batch=1), [130, 400]),
+    "mfma_rtn4_g8": (small("c1_single_head_2k_rtn4", batch=1, n_q_heads=16, n_kv_heads=2), [300, 129, 256]),
+    "mfma_kvarn2_g4": (small("c3_kvarn_gqa_b16_8k", batch=2, n_q_heads=8, n_kv_heads=2), [128, 128, 128, 128, 50]),
+    "mfma_sym4_g4": (small("c4_blog_int4_32l_b32_32k", n_layers=1, batch=1, n_q_heads=8, n_kv_heads=2), [640]),
+    "valu_rtn3_out2_g2": (small("c1_single_head_2k_rtn4", bits=3, outliers_per_vec=2, batch=2, n_q_heads=4,
+                                n_kv_heads=2), [5, 500]),
+    "valu_nuq4_rope_out3_g8": (small("c2_llama7b_layer_32k_nuq3", bits=4, outliers_per_vec=3, n_q_heads=16,
+                                     n_kv_heads=2), [129, 260]),
+}
+
+
+@pytest.mark.parametrize("sink,window", [(1, 0), (4, 128), (0, 256), (128, 128)])
+@pytest.mark.parametrize("case", list(SW_CASES))
+def test_parity_sink_and_window(K, case, sink, window):
+    """Attention-sink fp16 tokens and an fp16 window of recent tokens ([KVQ] 3.5, 4.2) with
+    every decode kernel family: blocks, fp16 rows and attention after each of several
+    appends."""
+    wl, chunks = SW_CASES[case]
+    run_case_sw(K, wl, chunks, sink, window)
+
+
+def test_parity_sink_window_many_splits_and_scale(K):
+    wl = small("c1_single_head_2k_rtn4", batch=1, n_q_heads=4, n_kv_heads=1)
+    for splits in (1, 3, 64):
+        run_case_sw(K, wl, [64 * 128 + 300], 2, 128, scale=0.2, splits=splits)
