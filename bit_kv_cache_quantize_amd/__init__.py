@@ -53,6 +53,7 @@ _sig = {
     "kvq_quantize_append": [_vp, _i, _vp, _vp, _i, _vp],
     "kvq_decode_attn": [_vp, _i, _vp, _vp, ctypes.c_float, _vp],
     "kvq_decode_attn_static": [_vp, _i, _vp, _vp, ctypes.c_float, _vp],
+    "kvq_error_decomposition": [_vp, _i, _i, _i, _vp, _vp, _vp, _vp],
     "kvq_cache_length": [_vp, _i, ctypes.POINTER(ctypes.c_int32)],
     "kvq_cache_reset": [_vp, _i],
     "kvq_set_decode_splits": [_vp, _i],
@@ -137,6 +138,11 @@ def kvq_decode_attn(handle: int, layer: int, q, out, softmax_scale: float = 0.0,
 def kvq_decode_attn_static(handle: int, layer: int, q, out, softmax_scale: float = 0.0, stream=None):
     _check(lib.kvq_decode_attn_static(handle, layer, _ptr(q), _ptr(out), softmax_scale, _stream(stream)),
            "kvq_decode_attn_static")
+
+
+def kvq_error_decomposition(handle: int, layer: int, block0: int, n_blocks: int, k, v, out, stream=None):
+    _check(lib.kvq_error_decomposition(handle, layer, block0, n_blocks, _ptr(k), _ptr(v), _ptr(out), _stream(stream)),
+           "kvq_error_decomposition")
 
 
 def kvq_cache_length(handle: int, layer: int) -> int:

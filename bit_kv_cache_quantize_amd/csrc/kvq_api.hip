@@ -602,6 +602,35 @@ kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, fl
 
 extern "C" {
 
+kvq_status kvq_error_decomposition(kvq_cache c, int layer, int block0, int n_blocks, const void* k_f16,
+                                   const void* v_f16, double* out, void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (!k_f16 || !v_f16 || !out) return fail(KVQ_ERR_ARG, "k, v or out is NULL");
+  if (reinterpret_cast<uintptr_t>(k_f16) % 16 || reinterpret_cast<uintptr_t>(v_f16) % 16 ||
+      reinterpret_cast<uintptr_t>(out) % 8)
+    return fail(KVQ_ERR_ARG, "k and v must be 16-byte aligned, out 8-byte aligned");
+  const int U = std::max(0, c->len[layer] - c->sink);
+  const int nq = std::max(0, U - c->window) / KVQ_BLOCK_TOKENS;   // quantized blocks
+  if (n_blocks <= 0 || block0 < 0 || block0 + n_blocks > nq)
+    return fail(KVQ_ERR_ARG, "blocks %d .. %d are not all quantized (layer %d holds %d quantized blocks)", block0,
+                block0 + n_blocks - 1, layer, nq);
+  kvq::DiagArgs a{};
+  a.lay = c->lay;
+  a.k_out = c->cfg.outliers_per_vec;
+  a.rec = c->base + c->off_rec + (size_t)layer * c->layer_rec_bytes;
+  a.cb = reinterpret_cast<const float*>(c->base + c->off_cb) + (size_t)layer * c->cfg.n_kv_heads * 2 * kvq::kCbStride;
+  a.k_in = static_cast<const __half*>(k_f16);
+  a.v_in = static_cast<const __half*>(v_f16);
+  a.block0 = block0;
+  a.n_blocks = n_blocks;
+  a.Hkv = c->cfg.n_kv_heads;
+  a.max_blocks = c->max_blocks;
+  a.out = out;
+  return hip_check(kvq::launch_diag(c->cfg.mode, c->cfg.bits, a, c->cfg.batch, static_cast<hipStream_t>(stream)),
+                   "launch error diagnostic");
+}
+
 kvq_status kvq_cache_length(kvq_cache c, int layer, int32_t* n_tokens) {
   const kvq_status st = check_layer(c, layer);
   if (st != KVQ_OK) return st;

@@ -87,6 +87,19 @@ struct DecodeArgs {
   int sink_n, fp16_u0, fp16_n, ring_rows, tail_rows, side_slot;
 };
 
+// Error diagnostic over quantized blocks block0 .. block0 + n_blocks - 1 of every (sequence,
+// kv head): inputs [B][Hkv][n_blocks * 128][128] fp16, out [B][Hkv][n_blocks * 128][4] fp64.
+struct DiagArgs {
+  RecordLayout lay;
+  int k_out;
+  const uint8_t* rec;       // records of the layer
+  const float* cb;          // codebooks of the layer, [Hkv][2][kCbStride]
+  const __half* k_in;
+  const __half* v_in;
+  int block0, n_blocks, Hkv, max_blocks;
+  double* out;
+};
+
 hipError_t launch_quantize(int mode, int bits, const QuantArgs& a, int n_blocks, int batch,
                            hipStream_t s);
 hipError_t launch_tail(const TailArgs& a, int batch, hipStream_t s);
@@ -101,5 +114,6 @@ hipError_t launch_decode_tab(int mode, int bits, const DecodeArgs& a, int batch,
 hipError_t launch_combine(const float* part, float* out, int Hq, int splits, int batch, hipStream_t s);
 // fp16 sink and window tokens of every (sequence, kv head): partial slot side_slot (or out).
 hipError_t launch_decode_fp16(int group, int rope, const DecodeArgs& a, int batch, hipStream_t s);
+hipError_t launch_diag(int mode, int bits, const DiagArgs& a, int batch, hipStream_t s);
 
 }  // namespace kvq

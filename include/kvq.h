@@ -170,6 +170,23 @@ kvq_status kvq_decode_attn(kvq_cache cache, int layer, const void* q_f16, float*
 kvq_status kvq_decode_attn_static(kvq_cache cache, int layer, const void* q_f16, float* out,
                                   float softmax_scale, void* stream);
 
+/*
+ * Quantization-error diagnostic (KVarN summary, core method: the error of a token vector
+ * splits into a norm part and a direction part). For every token of quantized body blocks
+ * block0 .. block0 + n_blocks - 1 of one layer (body block j holds positions
+ * sink_tokens + 128 j ...), with x the original vector and x_hat its dequantized cache value
+ * (original domain, keys before RoPE, outliers replaced by their fp16 values):
+ *   E_M = (||x|| - ||x_hat||)^2,  E_D = 2 ||x|| ||x_hat|| (1 - cos angle(x, x_hat)),
+ * so that E_M + E_D = ||x - x_hat||^2. Computed in fp64.
+ * k_f16, v_f16: dev, fp16 [batch][n_kv_heads][n_blocks * 128][128], the original keys and
+ *   values of those blocks, contiguous, 16-byte aligned.
+ * out: dev, fp64 [batch][n_kv_heads][n_blocks * 128][4] = E_M(key), E_D(key), E_M(value),
+ *   E_D(value).
+ * Errors: KVQ_ERR_ARG unless every requested block is quantized.
+ */
+kvq_status kvq_error_decomposition(kvq_cache cache, int layer, int block0, int n_blocks, const void* k_f16,
+                                   const void* v_f16, double* out, void* stream);
+
 /* Tokens currently held by a layer (host-side counter, no device access). */
 kvq_status kvq_cache_length(kvq_cache cache, int layer, int32_t* n_tokens);
 

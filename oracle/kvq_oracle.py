@@ -531,6 +531,18 @@ def error_decomposition(k: np.ndarray, kdq: np.ndarray):
     return (nk - nd) ** 2, 2.0 * nk * nd * (1.0 - cos)
 
 
+def error_decomposition_rows(x: np.ndarray, x_hat: np.ndarray):
+    """error_decomposition per row (one token's 128-vector): arrays (E_M[t], E_D[t]),
+    E_M = (||x_t|| - ||x_hat_t||)^2 and E_D = 2 ||x_t|| ||x_hat_t|| (1 - cos angle_t), the
+    token-norm and direction parts of ||x_t - x_hat_t||^2 ([KVARN] core method)."""
+    x = np.asarray(x, np.float64)
+    xh = np.asarray(x_hat, np.float64)
+    nx = np.sqrt(np.sum(x * x, axis=1))
+    nh = np.sqrt(np.sum(xh * xh, axis=1))
+    dot = np.sum(x * xh, axis=1)
+    return (nx - nh) ** 2, 2.0 * (nx * nh - dot)
+
+
 # ---------------------------------------------------------------------------
 # The cache: append with a fp16 tail, decode over everything
 # ---------------------------------------------------------------------------

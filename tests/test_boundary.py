@@ -199,7 +199,8 @@ def test_strerror():
 
 
 LLVM_BIN = "/opt/rocm/llvm/bin"
-HOT_KERNELS = ("quantize_kernel", "decode_tab_kernel", "decode_mfma_kernel", "combine_kernel", "tail_kernel")
+HOT_KERNELS = ("quantize_kernel", "decode_tab_kernel", "decode_mfma_kernel", "combine_kernel", "tail_kernel",
+               "decode_fp16_kernel")
 
 
 @pytest.mark.skipif(not os.path.exists(os.path.join(LLVM_BIN, "llvm-readelf")), reason="ROCm LLVM tools not installed")

@@ -776,3 +776,24 @@ def test_all_fp16_decode_is_dense_attention_by_hand():
     p = [math.exp(x - m) for x in scores]
     ref = [sum(p[t] * float(v[0, 0, t, ch]) for t in range(L)) / sum(p) for ch in range(128)]
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_per_token_error_decomposition():
+    """Per token, E_M + E_D = ||x - x_hat||^2 (law of cosines); a pure rescaling of a token
+    is all magnitude (E_D = 0) and a rotation at equal norm all direction (E_M = 0)
+    ([KVARN] core method)."""
+    r = rng(43)
+    x = r.standard_normal((5, 128))
+    xh = x + 0.05 * r.standard_normal((5, 128))
+    em, ed = O.error_decomposition_rows(x, xh)
+    assert np.allclose(em + ed, np.sum((x - xh) ** 2, axis=1), rtol=1e-10)
+    em1, ed1 = O.error_decomposition(x[2], xh[2])
+    assert em[2] == pytest.approx(em1, rel=1e-12) and ed[2] == pytest.approx(ed1, rel=1e-9)
+    em, ed = O.error_decomposition_rows(x, 0.5 * x)
+    assert np.allclose(ed, 0, atol=1e-9) and np.allclose(em, 0.25 * np.sum(x ** 2, axis=1), rtol=1e-12)
+    c, s = math.cos(0.3), math.sin(0.3)
+    y = x.copy()
+    y[:, 0], y[:, 1] = c * x[:, 0] - s * x[:, 1], s * x[:, 0] + c * x[:, 1]
+    em, ed = O.error_decomposition_rows(x, y)
+    assert np.allclose(em, 0, atol=1e-12)
+    assert np.allclose(ed, (2 - 2 * c) * (x[:, 0] ** 2 + x[:, 1] ** 2), rtol=1e-9)
