@@ -182,8 +182,11 @@ kvq_status validate_config(const kvq_config* c) {
   if (c->max_tokens < KVQ_BLOCK_TOKENS || c->max_tokens % KVQ_BLOCK_TOKENS != 0)
     return fail(KVQ_ERR_ARG, "max_tokens must be a positive multiple of 128 (got %d)", c->max_tokens);
   if (c->mode < KVQ_MODE_RTN || c->mode > KVQ_MODE_SYM_INT4) return fail(KVQ_ERR_ARG, "unknown mode %d", c->mode);
-  if (c->bits < 2 || c->bits > 4) return fail(KVQ_ERR_ARG, "bits must be 2, 3 or 4 (got %d)", c->bits);
-  if (c->mode == KVQ_MODE_SYM_INT4 && c->bits != 4) return fail(KVQ_ERR_ARG, "symmetric int4 requires bits = 4");
+  if (c->bits != 2 && c->bits != 3 && c->bits != 4 && c->bits != 8)
+    return fail(KVQ_ERR_ARG, "bits must be 2, 3, 4 or 8 (got %d)", c->bits);
+  if (c->mode == KVQ_MODE_SYM_INT4 && c->bits != 4 && c->bits != 8)
+    return fail(KVQ_ERR_ARG, "symmetric mode requires bits = 4 or 8");
+  if (c->mode == KVQ_MODE_NUQ && c->bits == 8) return fail(KVQ_ERR_ARG, "NUQ codebooks have at most 16 entries");
   if (c->outliers_per_vec < 0 || c->outliers_per_vec > KVQ_MAX_OUTLIERS)
     return fail(KVQ_ERR_ARG, "outliers_per_vec must be in 0..8 (got %d)", c->outliers_per_vec);
   if (c->pre_rope != 0 && c->pre_rope != 1) return fail(KVQ_ERR_ARG, "pre_rope must be 0 or 1");

@@ -223,13 +223,16 @@ hipError_t launch_decode(int mode, int bits, int group, int rope, const DecodeAr
     case RTN * 8 + 2: return launch_r<RTN, 2>(group, rope, a, batch, s);
     case RTN * 8 + 3: return launch_r<RTN, 3>(group, rope, a, batch, s);
     case RTN * 8 + 4: return launch_r<RTN, 4>(group, rope, a, batch, s);
+    case RTN * 8 + 8: return launch_r<RTN, 8>(group, rope, a, batch, s);
     case NUQ * 8 + 2: return launch_r<NUQ, 2>(group, rope, a, batch, s);
     case NUQ * 8 + 3: return launch_r<NUQ, 3>(group, rope, a, batch, s);
     case NUQ * 8 + 4: return launch_r<NUQ, 4>(group, rope, a, batch, s);
     case KVARN * 8 + 2: return launch_r<KVARN, 2>(group, rope, a, batch, s);
     case KVARN * 8 + 3: return launch_r<KVARN, 3>(group, rope, a, batch, s);
     case KVARN * 8 + 4: return launch_r<KVARN, 4>(group, rope, a, batch, s);
+    case KVARN * 8 + 8: return launch_r<KVARN, 8>(group, rope, a, batch, s);
     case SYM * 8 + 4: return launch_r<SYM, 4>(group, rope, a, batch, s);
+    case SYM * 8 + 8: return launch_r<SYM, 8>(group, rope, a, batch, s);
     default: return hipErrorInvalidValue;
   }
 }

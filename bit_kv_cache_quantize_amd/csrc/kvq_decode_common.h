@@ -58,7 +58,9 @@ __device__ __forceinline__ void fwht_wave(float& x, float& y, int lane) {
 // code of element i of a packed row of n codes held in registers w[]
 template <int BITS, int N>
 __device__ __forceinline__ uint32_t code_at(const uint32_t* w, int i) {
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 8) {
+    return (w[i >> 2] >> (8 * (i & 3))) & 255u;
+  } else if constexpr (BITS == 4) {
     return (w[i >> 3] >> (4 * (i & 7))) & 15u;
   } else if constexpr (BITS == 2) {
     return (w[i >> 4] >> (2 * (i & 15))) & 3u;
@@ -129,6 +131,7 @@ struct OutlierLds {
 template <int MODE, int BITS, int G, bool ROPE>
 struct Decoder {
   static constexpr int R = 16 * BITS;      // bytes per 128 codes
+  static constexpr float kSymOff = (float)(1 << (BITS - 1));   // symmetric codes: u = q + 8 (int8: q + 128)
   static constexpr int RH = R / 2;         // bytes per 64 codes
   static constexpr int NOB = 3;            // prefetched 16-byte chunks of the outlier blob per lane
 
@@ -201,7 +204,7 @@ struct Decoder {
     if constexpr (MODE == SYM) {
       const __half2 k2 = reinterpret_cast<const __half2*>(rec + a.lay.ks)[lane];
       B.ks = __half22float2(k2);
-      B.km = make_float2(-8.f * B.ks.x, -8.f * B.ks.y);
+      B.km = make_float2(-kSymOff * B.ks.x, -kSymOff * B.ks.y);
       B.tst = __half22float2(reinterpret_cast<const __half2*>(rec + a.lay.vs)[lane]);
     } else if constexpr (MODE == NUQ) {
       B.km = reinterpret_cast<const float2*>(rec + a.lay.ks)[lane];          // z
@@ -423,8 +426,8 @@ struct Decoder {
     } else if constexpr (MODE == SYM) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        acc0[h] = fmaf(B.tst.x, fmaf(-8.f, pmb[h], o0[h]), acc0[h]);
-        acc1[h] = fmaf(B.tst.y, fmaf(-8.f, pmb[h], o1[h]), acc1[h]);
+        acc0[h] = fmaf(B.tst.x, fmaf(-kSymOff, pmb[h], o0[h]), acc0[h]);
+        acc1[h] = fmaf(B.tst.y, fmaf(-kSymOff, pmb[h], o1[h]), acc1[h]);
       }
     } else {
 #pragma unroll
@@ -446,7 +449,7 @@ struct Decoder {
             if (t < 0 || t >= 64) continue;
             const uint32_t code = code_sel<BITS, 64>(B.vw + k * (R / 8), half_row_token(t));
             float dense;
-            if constexpr (MODE == SYM) dense = ((float)code - 8.f) * (k ? B.tst.y : B.tst.x);
+            if constexpr (MODE == SYM) dense = ((float)code - kSymOff) * (k ? B.tst.y : B.tst.x);
             else dense = fmaf(vval(code), ol.vS[t], ol.vM[t]);
             const float delta = __half2float(val[e]) - dense;
 #pragma unroll

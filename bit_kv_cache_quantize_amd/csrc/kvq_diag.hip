@@ -42,6 +42,7 @@ struct DiagBlock {
       p = 16 * ((u >> 2) & 3) + 4 * (u >> 4) + (u & 3);
     }
     const int n = tensor == 0 ? 128 : 64;   // codes in the row
+    if constexpr (BITS == 8) return row[p];
     if constexpr (BITS == 4) return (row[p >> 1] >> (4 * (p & 1))) & 15u;
     if constexpr (BITS == 2) return (row[p >> 2] >> (2 * (p & 3))) & 3u;
     const uint32_t lo = (row[p >> 2] >> (2 * (p & 3))) & 3u;
@@ -57,7 +58,7 @@ struct DiagBlock {
     const int vi = tensor == 0 ? c : t;   // statistics index: key channel, value token
     if constexpr (MODE == SYM) {
       const __half s = reinterpret_cast<const __half*>(rec + st)[c];   // per channel for both
-      return ((double)q - 8.0) * (double)__half2float(s);
+      return ((double)q - (double)(1 << (BITS - 1))) * (double)__half2float(s);
     } else if constexpr (MODE == NUQ) {
       const double z = f32_at(st + 4 * vi), h = f32_at(st + 512 + 4 * vi);
       return (double)cb[tensor * kCbStride + q] * h + z;
@@ -185,13 +186,16 @@ hipError_t launch_diag(int mode, int bits, const DiagArgs& a, int batch, hipStre
     case RTN * 8 + 2: return launch_d<RTN, 2>(a, batch, s);
     case RTN * 8 + 3: return launch_d<RTN, 3>(a, batch, s);
     case RTN * 8 + 4: return launch_d<RTN, 4>(a, batch, s);
+    case RTN * 8 + 8: return launch_d<RTN, 8>(a, batch, s);
     case NUQ * 8 + 2: return launch_d<NUQ, 2>(a, batch, s);
     case NUQ * 8 + 3: return launch_d<NUQ, 3>(a, batch, s);
     case NUQ * 8 + 4: return launch_d<NUQ, 4>(a, batch, s);
     case KVARN * 8 + 2: return launch_d<KVARN, 2>(a, batch, s);
     case KVARN * 8 + 3: return launch_d<KVARN, 3>(a, batch, s);
     case KVARN * 8 + 4: return launch_d<KVARN, 4>(a, batch, s);
+    case KVARN * 8 + 8: return launch_d<KVARN, 8>(a, batch, s);
     case SYM * 8 + 4: return launch_d<SYM, 4>(a, batch, s);
+    case SYM * 8 + 8: return launch_d<SYM, 8>(a, batch, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -411,7 +411,7 @@ __device__ __forceinline__ VecStats stats_of(float lo, float hi, float amax) {
     v.rc = v.sb == 0.f ? 0.f : __fdiv_rn(1.f, v.sb);
     v.off = v.sa;
   } else if constexpr (MODE == SYM) {
-    v.sa = __half2float(__float2half_rn(__fdiv_rn(amax, 7.0f)));
+    v.sa = __half2float(__float2half_rn(__fdiv_rn(amax, (float)((1 << (BITS - 1)) - 1))));   // absmax / 7 (int8: 127)
     v.sb = 0.f;
     v.rc = v.sa == 0.f ? 0.f : __fdiv_rn(1.f, v.sa);
     v.off = 0.f;
@@ -472,7 +472,8 @@ __device__ __forceinline__ uint32_t code_of(float d, const VecStats& v, const fl
     return nuq_search<BITS>(u, tau);
   } else if constexpr (MODE == SYM) {
     const float q = rintf(div_rn(d, v.sa, v.rc));
-    return (uint32_t)((int)fminf(fmaxf(q, -8.f), 7.f) + 8);
+    constexpr int H = 1 << (BITS - 1);   // offset binary: u = q + 8 (int8: q + 128)
+    return (uint32_t)((int)fminf(fmaxf(q, (float)-H), (float)(H - 1)) + H);
   } else {
     const float q = rintf(div_rn(d, v.sa, v.rc));
     return (uint32_t)fminf(fmaxf(q, 0.f), (float)QMAX);
@@ -794,7 +795,10 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
 #pragma unroll
       for (int e = 0; e < 8; ++e) c[e] = code_of<MODE, BITS, LUT>(X.d(i, e, vs[e].off), vs[e], tau, sm.nlut);
       uint8_t* row = kc + (size_t)t * R;
-      if constexpr (BITS == 4) {
+      if constexpr (BITS == 8) {
+        *reinterpret_cast<uint2*>(row + 8 * g) =
+            make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+      } else if constexpr (BITS == 4) {
         uint32_t v = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) v |= c[e] << (4 * e);
@@ -834,7 +838,15 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
         return sm.vq[(64 * half + 16 * ((p >> 2) & 3) + 4 * (p >> 4) + (p & 3)) * kD + c];
       };
       uint8_t* dst = rec + a.lay.vc + (size_t)(half * 128 + c) * RH;
-      if constexpr (BITS == 4) {
+      if constexpr (BITS == 8) {
+        uint32_t wd[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          wd[k] = code(4 * k) | code(4 * k + 1) << 8 | code(4 * k + 2) << 16 | code(4 * k + 3) << 24;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          reinterpret_cast<uint4*>(dst)[k] = make_uint4(wd[4 * k], wd[4 * k + 1], wd[4 * k + 2], wd[4 * k + 3]);
+      } else if constexpr (BITS == 4) {
         uint32_t wd[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -1005,13 +1017,16 @@ hipError_t launch_quantize(int mode, int bits, const QuantArgs& a, int n_blocks,
     case RTN * 8 + 2: return launch_q<RTN, 2>(a, n_blocks, batch, s);
     case RTN * 8 + 3: return launch_q<RTN, 3>(a, n_blocks, batch, s);
     case RTN * 8 + 4: return launch_q<RTN, 4>(a, n_blocks, batch, s);
+    case RTN * 8 + 8: return launch_q<RTN, 8>(a, n_blocks, batch, s);
     case NUQ * 8 + 2: return launch_q<NUQ, 2>(a, n_blocks, batch, s);
     case NUQ * 8 + 3: return launch_q<NUQ, 3>(a, n_blocks, batch, s);
     case NUQ * 8 + 4: return launch_q<NUQ, 4>(a, n_blocks, batch, s);
     case KVARN * 8 + 2: return launch_q<KVARN, 2>(a, n_blocks, batch, s);
     case KVARN * 8 + 3: return launch_q<KVARN, 3>(a, n_blocks, batch, s);
     case KVARN * 8 + 4: return launch_q<KVARN, 4>(a, n_blocks, batch, s);
+    case KVARN * 8 + 8: return launch_q<KVARN, 8>(a, n_blocks, batch, s);
     case SYM * 8 + 4: return launch_q<SYM, 4>(a, n_blocks, batch, s);
+    case SYM * 8 + 8: return launch_q<SYM, 8>(a, n_blocks, batch, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -54,7 +54,7 @@ typedef enum {
   KVQ_MODE_RTN = 0,       /* asymmetric uniform RTN, min/range (KVQuant notes 1.2, 3.1) */
   KVQ_MODE_NUQ = 1,       /* codebook argmin on [-1, 1] (KVQuant notes 1.2, 3.3) */
   KVQ_MODE_KVARN = 2,     /* Hadamard + VarN + RTN with s1 (KVarN core method) */
-  KVQ_MODE_SYM_INT4 = 3   /* symmetric int4, fp16 scales (TurboQuant blog 4.2) */
+  KVQ_MODE_SYM_INT4 = 3   /* symmetric int4 (int8 with bits = 8), fp16 scales (TurboQuant blog 4.2) */
 } kvq_mode;
 
 #define KVQ_HEAD_DIM 128
@@ -74,7 +74,8 @@ typedef struct {
   int32_t head_dim;         /* must be 128 */
   int32_t max_tokens;       /* capacity per sequence and layer, multiple of 128, >= 128 */
   int32_t mode;             /* kvq_mode */
-  int32_t bits;             /* 2, 3 or 4; KVQ_MODE_SYM_INT4 requires 4 */
+  int32_t bits;             /* 2, 3 or 4; 8 with RTN, KVARN or SYM_INT4 (the blog's 8-bit KV for
+                               sensitive layers, 2.2 / 5.1); KVQ_MODE_SYM_INT4 requires 4 or 8 */
   int32_t outliers_per_vec; /* 0..8 fp16 outliers per quantization vector; 0 with KVARN */
   int32_t pre_rope;         /* 1: keys are stored before RoPE and rotated at decode; 0 with KVARN */
   float rope_theta;         /* RoPE base (10000 in the pages), > 0 when pre_rope */
@@ -223,8 +224,10 @@ kvq_status kvq_set_decode_splits(kvq_cache cache, int splits);
  * Code packing of n codes: 4-bit byte j = code 2j | code 2j+1 << 4; 2-bit byte j
  * = codes 4j..4j+3 at bits 2i; 3-bit = the low 2 bits of all n codes packed as
  * 2-bit (n/4 bytes) then bit 2 of code 8j+i at bit i of byte j (n/8 bytes).
+ * 8-bit: byte j = code j.
  * Codes: RTN/KVARN q in 0..2^b-1 with x = q*s + m (KVARN: times s1);
- * NUQ q indexes the codebook, x = C[q]*h + z; SYM_INT4 u = q + 8, x = (u-8)*s.
+ * NUQ q indexes the codebook, x = C[q]*h + z; SYM_INT4 u = q + 2^(b-1), x = (u - 2^(b-1))*s
+ * (4 bits: u = q + 8, s = fp16(absmax / 7); 8 bits: u = q + 128, s = fp16(absmax / 127)).
  */
 kvq_status kvq_block_span(kvq_cache cache, int layer, int b, int kv_head, int block,
                           size_t* offset, size_t* bytes);

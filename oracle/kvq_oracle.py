@@ -175,25 +175,28 @@ def nuq_codes(x32: np.ndarray, z: np.ndarray, h: np.ndarray, codebook: np.ndarra
 # Symmetric block int4 ([BLOG] 2.1 and 4.2)
 # ---------------------------------------------------------------------------
 
-def sym_scale(x32: np.ndarray, keep: np.ndarray, axis: int) -> np.ndarray:
-    """fp16 scale = f16_rne(max|x| / 7) over the vector's non-outlier entries."""
+def sym_scale(x32: np.ndarray, keep: np.ndarray, axis: int, bits: int = 4) -> np.ndarray:
+    """fp16 scale = f16_rne(max|x| / 7) over the vector's non-outlier entries (int8: / 127,
+    the largest positive code of the width)."""
     a = np.where(keep, np.abs(x32), np.float32(0)).max(axis=axis).astype(np.float32)
-    return (a / np.float32(7.0)).astype(np.float32).astype(np.float16)
+    return (a / np.float32((1 << (bits - 1)) - 1)).astype(np.float32).astype(np.float16)
 
 
-def sym_codes(x32: np.ndarray, s16: np.ndarray) -> np.ndarray:
-    """u = clamp(rint(x / s), -8, 7) + 8, offset binary in 0..15; s = 0 gives u = 8.
+def sym_codes(x32: np.ndarray, s16: np.ndarray, bits: int = 4) -> np.ndarray:
+    """u = clamp(rint(x / s), -8, 7) + 8, offset binary in 0..15; s = 0 gives u = 8
+    (int8: clamp to [-128, 127], u = q + 128).
 
     Reading: the blog's quantizer keeps q & 0xF (two's complement) while its
     dequantizer subtracts 8; the stored code here is the offset-binary q + 8 so
     that dequantisation is (u - 8) * s.
     """
+    half = 1 << (bits - 1)
     s = np.asarray(s16, np.float16).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
         u = x32 / s
-    q = np.clip(np.rint(u), -8, 7)
+    q = np.clip(np.rint(u), -half, half - 1)
     q = np.where(s == 0, 0, q)
-    return (q + 8).astype(np.uint8)
+    return (q + half).astype(np.uint8)
 
 
 # ---------------------------------------------------------------------------
@@ -365,10 +368,10 @@ def quantize_block(k16: np.ndarray, v16: np.ndarray, cfg: Config,
         vc = nuq_codes(vx, vz[:, None], vh[:, None], cb_v)
         kstat, vstat = (kz, kh), (vz, vh)
     elif mode == MODE_SYM_INT4:
-        kss = sym_scale(kx, kkeep, axis=0)
-        vss = sym_scale(vx, vkeep, axis=0)
-        kc = sym_codes(kx, kss[None, :])
-        vc = sym_codes(vx, vss[None, :])
+        kss = sym_scale(kx, kkeep, axis=0, bits=b)
+        vss = sym_scale(vx, vkeep, axis=0, bits=b)
+        kc = sym_codes(kx, kss[None, :], b)
+        vc = sym_codes(vx, vss[None, :], b)
         kstat, vstat = (kss,), (vss,)
     else:
         raise ValueError(mode)
@@ -398,9 +401,9 @@ def dequant_nuq(codes: np.ndarray, z: np.ndarray, h: np.ndarray, codebook: np.nd
     return C[np.asarray(codes, np.int64)] * np.asarray(h, np.float64) + np.asarray(z, np.float64)
 
 
-def dequant_sym(u: np.ndarray, s16: np.ndarray) -> np.ndarray:
-    """x_hat = (u - 8) * s ([BLOG] 4.2, offset-binary storage code)."""
-    return (np.asarray(u, np.float64) - 8.0) * np.asarray(s16, np.float16).astype(np.float64)
+def dequant_sym(u: np.ndarray, s16: np.ndarray, bits: int = 4) -> np.ndarray:
+    """x_hat = (u - 8) * s ([BLOG] 4.2, offset-binary storage code; int8: u - 128)."""
+    return (np.asarray(u, np.float64) - float(1 << (bits - 1))) * np.asarray(s16, np.float16).astype(np.float64)
 
 
 def dequant_block(blk: Block, cfg: Config, cb_k=None, cb_v=None):
@@ -425,8 +428,8 @@ def dequant_block(blk: Block, cfg: Config, cb_k=None, cb_v=None):
         kh = dequant_nuq(blk.kcodes, blk.kstat[0][None, :], blk.kstat[1][None, :], cb_k)
         vh = dequant_nuq(blk.vcodes, blk.vstat[0][:, None], blk.vstat[1][:, None], cb_v)
     elif mode == MODE_SYM_INT4:
-        kh = dequant_sym(blk.kcodes, blk.kstat[0][None, :])
-        vh = dequant_sym(blk.vcodes, blk.vstat[0][None, :])
+        kh = dequant_sym(blk.kcodes, blk.kstat[0][None, :], cfg.bits)
+        vh = dequant_sym(blk.vcodes, blk.vstat[0][None, :], cfg.bits)
     else:
         raise ValueError(mode)
     if blk.kmask is not None:
@@ -452,7 +455,9 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     n = c.shape[-1]
     assert n % 8 == 0
     rows = c.reshape(-1, n)
-    if bits == 4:
+    if bits == 8:
+        out = rows.copy()
+    elif bits == 4:
         out = rows[:, 0::2] | (rows[:, 1::2] << 4)
     elif bits == 2:
         r = rows.reshape(-1, n // 4, 4)
@@ -475,7 +480,9 @@ def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
     nb = p.shape[-1]
     n = nb * 8 // bits
     rows = p.reshape(-1, nb)
-    if bits == 4:
+    if bits == 8:
+        out = rows.copy()
+    elif bits == 4:
         out = np.empty((rows.shape[0], n), np.uint8)
         out[:, 0::2] = rows & 15
         out[:, 1::2] = rows >> 4

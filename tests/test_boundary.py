@@ -41,6 +41,7 @@ def cfg(**kw):
     dict(mode=K.KVQ_MODE_KVARN, outliers_per_vec=1), dict(mode=K.KVQ_MODE_KVARN, pre_rope=1),
     dict(mode=K.KVQ_MODE_KVARN, varn_iters=65), dict(n_layers=0), dict(batch=0),
     dict(sink_tokens=129), dict(sink_tokens=-1), dict(fp16_window=100), dict(fp16_window=8320),
+    dict(bits=6), dict(bits=16), dict(mode=K.KVQ_MODE_NUQ, bits=8), dict(mode=K.KVQ_MODE_SYM_INT4, bits=2),
     dict(fp16_window=-128),
 ])
 def test_invalid_configs_are_rejected(kw):

@@ -484,3 +484,49 @@ def test_parity_sink_window_many_splits_and_scale(K):
     wl = small("c1_single_head_2k_rtn4", batch=1, n_q_heads=4, n_kv_heads=1)
     for splits in (1, 3, 64):
         run_case_sw(K, wl, [64 * 128 + 300], 2, 128, scale=0.2, splits=splits)
+
+
+CASES_8BIT = {
+    "rtn8_rope_out1_g1": (small("c5_llama7b_1m_rtn2", n_layers=1, bits=8, batch=2, n_q_heads=2, n_kv_heads=2),
+                          [300]),
+    "rtn8_g4": (small("c1_single_head_2k_rtn4", bits=8, batch=1, n_q_heads=8, n_kv_heads=2), [129, 255]),
+    "sym8_g4": (small("c4_blog_int4_32l_b32_32k", n_layers=1, bits=8, batch=2, n_q_heads=8, n_kv_heads=2), [512]),
+    "sym8_rope_out1_g1": (small("c4_blog_int4_32l_b32_32k", n_layers=1, bits=8, batch=1, n_q_heads=2,
+                                n_kv_heads=2, pre_rope=1, outliers_per_vec=1), [257]),
+    "kvarn8_g2": (small("c3_kvarn_gqa_b16_8k", bits=8, batch=1, n_q_heads=4, n_kv_heads=2), [128, 200]),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES_8BIT))
+def test_parity_8bit(K, case):
+    """8-bit codes ([BLOG] 2.2 / 5.1: sensitive layers' KV at 8 bits)."""
+    wl, chunks = CASES_8BIT[case]
+    run_case(K, wl, chunks)
+
+
+def test_mixed_precision_layers(K):
+    """[BLOG] 5.1: the first and last layers at 8 bits, the others at 4 (symmetric, block-128
+    fp16 scales), as two handles over the layers of one model; every layer decodes to the
+    oracle's attention, and an 8-bit layer costs twice the code bytes of a 4-bit one."""
+    base = small("c4_blog_int4_32l_b32_32k", n_layers=2, batch=1, n_q_heads=8, n_kv_heads=2)
+    groups = {8: [0, 3], 4: [1, 2]}      # bits -> model layers
+    L = 700
+    for bits, layers in groups.items():
+        wl = base.replace(bits=bits)
+        cache = K.KVCache(H.lib_cfg(wl, H.ceil128(L)))
+        oc = O.OracleCache(H.oracle_cfg(wl, H.ceil128(L)))
+        for slot, layer in enumerate(layers):
+            k, v = H.host_kv(wl, layer, 0, L)
+            cache.append(slot, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+            oc.append(slot, k, v)
+            q = H.host_q(wl, layer)
+            out = torch.empty((1, 8, 128), dtype=torch.float32, device="cuda")
+            cache.decode(slot, torch.from_numpy(q).cuda(), out)
+            torch.cuda.synchronize()
+            H.attention_close(out.cpu().numpy(), oc.decode(slot, q))
+            for j in range(L // 128):
+                H.compare_record(cache.block_bytes(slot, 0, 1, j).cpu().numpy(), oc.blocks[slot][1][j], oc.cfg)
+        _say(f"  {bits}-bit layers {layers}: decode bytes per layer {cache.decode_bytes(0)}")
+    from tests import _record as R
+    assert R.payload_bytes(R.MODE_SYM_INT4, 8, 0) == 2 * 128 * 128 + 512
+    assert R.payload_bytes(R.MODE_SYM_INT4, 4, 0) == 128 * 128 + 512

@@ -85,7 +85,7 @@ def test_per_token_vs_per_channel_scale_example():
 
 
 # --------------------------------------------------------------------------- P3
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("k_out", [0, 1, 2])
 def test_rtn_error_bound_and_endpoints(bits, k_out):
     r = rng(bits * 10 + k_out)
@@ -354,6 +354,8 @@ def test_packing_byte_patterns_and_round_trip():
     c3h = np.arange(64) % 8
     p3h = O.pack_codes(c3h, 3)
     assert p3h.size == 24 and p3h[16] == 0b11110000
+    c8 = r.integers(0, 256, size=(3, 128)).astype(np.uint8)
+    assert np.array_equal(O.pack_codes(c8, 8), c8) and np.array_equal(O.unpack_codes(c8, 8), c8)
 
 
 # --------------------------------------------------------------------------- P14
@@ -797,3 +799,25 @@ def test_per_token_error_decomposition():
     em, ed = O.error_decomposition_rows(x, y)
     assert np.allclose(em, 0, atol=1e-12)
     assert np.allclose(ed, (2 - 2 * c) * (x[:, 0] ** 2 + x[:, 1] ** 2), rtol=1e-9)
+
+
+def test_symmetric_int8_for_sensitive_layers_matches_the_blog_semantics_at_8_bits():
+    """[BLOG] 2.2 / 5.1 keep sensitive layers' KV at 8 bits. The int4 quantizer of [BLOG]
+    4.2 written at 8 bits (absmax / 127 per 128-element sequence block, round, clamp to
+    [-128, 127]) with torch CPU ops, given the same fp16 scale; stored offset binary."""
+    r = rng(44)
+    x16 = (r.standard_normal((128, 128)) * np.array([1.0, 13.0] * 64)[None, :]).astype(np.float16)
+    x = x16.astype(np.float32)
+    keep = np.ones_like(x, bool)
+    s16 = O.sym_scale(x, keep, axis=0, bits=8)
+    u = O.sym_codes(x, s16[None, :], 8)
+    xt = torch.from_numpy(x)
+    scale_t = (xt.abs().max(dim=0, keepdim=True).values / 127.0).to(torch.float16)
+    assert np.array_equal(scale_t.numpy()[0], s16)
+    qt = (xt / scale_t.float()).clamp(-128, 127).round()
+    assert np.array_equal((qt + 128).to(torch.int16).numpy(), u.astype(np.int16))
+    deq = O.dequant_sym(u, s16[None, :], 8)
+    assert np.all(np.abs(deq - x) <= s16.astype(np.float64)[None, :] / 2 * (1 + 1e-3) + 1e-7)
+    # eight bits quantize a 4-bit block's worth of data sixteen times finer
+    deq4 = O.dequant_sym(O.sym_codes(x, O.sym_scale(x, keep, 0, 4)[None, :], 4), O.sym_scale(x, keep, 0, 4)[None, :], 4)
+    assert np.max(np.abs(deq - x)) < np.max(np.abs(deq4 - x)) / 10
