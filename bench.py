@@ -41,7 +41,7 @@ DEFAULT = "c5_llama7b_1m_rtn2"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-MODE_NAMES = {0: "rtn", 1: "nuq", 2: "kvarn", 3: "sym_int4"}
+MODE_NAMES = {0: "rtn", 1: "nuq", 2: "kvarn", 3: "sym_int4", 4: "asym_int4"}
 
 
 def parse():
@@ -218,7 +218,7 @@ class Bench:
 def record_payload(wl):
     """Payload bytes of one block record (segment sizes, as documented in include/kvq.h)."""
     R = 16 * wl.bits
-    n = 128 * R * 2 + (512 if wl.mode == 3 else 2048)
+    n = 128 * R * 2 + {3: 512, 4: 1024}.get(wl.mode, 2048)
     if wl.mode == 2:
         n += 1024
     if wl.outliers_per_vec:

@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
 KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_SIZE, KVQ_ERR_CAPACITY, KVQ_ERR_STATE, KVQ_ERR_HIP = 0, -1, -2, -3, -4, -5
-KVQ_MODE_RTN, KVQ_MODE_NUQ, KVQ_MODE_KVARN, KVQ_MODE_SYM_INT4 = 0, 1, 2, 3
+KVQ_MODE_RTN, KVQ_MODE_NUQ, KVQ_MODE_KVARN, KVQ_MODE_SYM_INT4, KVQ_MODE_ASYM_INT4 = 0, 1, 2, 3, 4
 KVQ_HEAD_DIM = 128
 KVQ_BLOCK_TOKENS = 128
 KVQ_MAX_SPLITS = 64

@@ -117,7 +117,7 @@ RecordLayout make_layout(int mode, int bits, int k_out) {
     return at;
   };
   const uint32_t R = 16u * (uint32_t)bits;
-  const uint32_t stat = mode == SYM ? 256u : 1024u;
+  const uint32_t stat = mode == SYM ? 256u : (mode == ASYM ? 512u : 1024u);
   L.kc = seg(kT * R);
   L.vc = seg(kD * R);
   L.ks = seg(stat);
@@ -181,7 +181,8 @@ kvq_status validate_config(const kvq_config* c) {
   if (g != 1 && g != 2 && g != 4 && g != 8) return fail(KVQ_ERR_ARG, "query group %d not in {1,2,4,8}", g);
   if (c->max_tokens < KVQ_BLOCK_TOKENS || c->max_tokens % KVQ_BLOCK_TOKENS != 0)
     return fail(KVQ_ERR_ARG, "max_tokens must be a positive multiple of 128 (got %d)", c->max_tokens);
-  if (c->mode < KVQ_MODE_RTN || c->mode > KVQ_MODE_SYM_INT4) return fail(KVQ_ERR_ARG, "unknown mode %d", c->mode);
+  if (c->mode < KVQ_MODE_RTN || c->mode > KVQ_MODE_ASYM_INT4) return fail(KVQ_ERR_ARG, "unknown mode %d", c->mode);
+  if (c->mode == KVQ_MODE_ASYM_INT4 && c->bits != 4) return fail(KVQ_ERR_ARG, "asymmetric int4 requires bits = 4");
   if (c->bits != 2 && c->bits != 3 && c->bits != 4 && c->bits != 8)
     return fail(KVQ_ERR_ARG, "bits must be 2, 3, 4 or 8 (got %d)", c->bits);
   if (c->mode == KVQ_MODE_SYM_INT4 && c->bits != 4 && c->bits != 8)

@@ -233,6 +233,7 @@ hipError_t launch_decode(int mode, int bits, int group, int rope, const DecodeAr
     case KVARN * 8 + 8: return launch_r<KVARN, 8>(group, rope, a, batch, s);
     case SYM * 8 + 4: return launch_r<SYM, 4>(group, rope, a, batch, s);
     case SYM * 8 + 8: return launch_r<SYM, 8>(group, rope, a, batch, s);
+    case ASYM * 8 + 4: return launch_r<ASYM, 4>(group, rope, a, batch, s);
     default: return hipErrorInvalidValue;
   }
 }

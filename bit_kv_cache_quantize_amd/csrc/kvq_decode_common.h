@@ -140,7 +140,8 @@ struct Decoder {
     uint32_t kw[R / 4];     // key row of token j
     uint32_t vw[R / 4];     // value half-rows of channels 2*lane, 2*lane+1
     float2 ks, km;          // key (S, M) of channels 2*lane, 2*lane+1
-    float2 tst;             // value (S, M) of token j; SYM: value scales of channels 2*lane, 2*lane+1
+    float2 tst;             // value (S, M) of token j; SYM / ASYM: value scales of channels 2*lane, 2*lane+1
+    float2 tz;              // ASYM: value zero points of channels 2*lane, 2*lane+1
     float s1t;              // KVarN s1 of token j
     float2 s1c;             // KVarN s1 of channels 2*lane, 2*lane+1
     float2 rb;              // RoPE (cos, sin) of the block base for pair lane
@@ -206,6 +207,12 @@ struct Decoder {
       B.ks = __half22float2(k2);
       B.km = make_float2(-kSymOff * B.ks.x, -kSymOff * B.ks.y);
       B.tst = __half22float2(reinterpret_cast<const __half2*>(rec + a.lay.vs)[lane]);
+    } else if constexpr (MODE == ASYM) {   // x = (u - 8) s + zero = u s + (zero - 8 s)
+      B.ks = __half22float2(reinterpret_cast<const __half2*>(rec + a.lay.ks)[lane]);
+      const float2 kz = __half22float2(reinterpret_cast<const __half2*>(rec + a.lay.ks + 256)[lane]);
+      B.km = make_float2(fmaf(-kSymOff, B.ks.x, kz.x), fmaf(-kSymOff, B.ks.y, kz.y));
+      B.tst = __half22float2(reinterpret_cast<const __half2*>(rec + a.lay.vs)[lane]);
+      B.tz = __half22float2(reinterpret_cast<const __half2*>(rec + a.lay.vs + 256)[lane]);
     } else if constexpr (MODE == NUQ) {
       B.km = reinterpret_cast<const float2*>(rec + a.lay.ks)[lane];          // z
       B.ks = reinterpret_cast<const float2*>(rec + a.lay.ks + 512)[lane];    // h
@@ -265,7 +272,7 @@ struct Decoder {
     }
     ol.kS[2 * lane] = B.ks.x; ol.kS[2 * lane + 1] = B.ks.y;
     ol.kM[2 * lane] = B.km.x; ol.kM[2 * lane + 1] = B.km.y;
-    if constexpr (MODE != SYM) { ol.vS[lane] = B.tst.x; ol.vM[lane] = B.tst.y; }
+    if constexpr (MODE != SYM && MODE != ASYM) { ol.vS[lane] = B.tst.x; ol.vM[lane] = B.tst.y; }
     if constexpr (ROPE) ol.rb[lane] = B.rb;
     wave_sync();
   }
@@ -382,7 +389,7 @@ struct Decoder {
 
     // ---- P . V over the 64 tokens of this half, channel pair (2*lane, 2*lane+1)
     float pp[G], pmb[G];
-    if constexpr (MODE == SYM) {
+    if constexpr (MODE == SYM || MODE == ASYM) {
 #pragma unroll
       for (int h = 0; h < G; ++h) { pp[h] = p[h]; pmb[h] = wave_sum(p[h]); }
     } else {
@@ -429,6 +436,12 @@ struct Decoder {
         acc0[h] = fmaf(B.tst.x, fmaf(-kSymOff, pmb[h], o0[h]), acc0[h]);
         acc1[h] = fmaf(B.tst.y, fmaf(-kSymOff, pmb[h], o1[h]), acc1[h]);
       }
+    } else if constexpr (MODE == ASYM) {   // s_c (sum p (u - 8)) + zero_c sum p
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        acc0[h] = fmaf(B.tz.x, pmb[h], fmaf(B.tst.x, fmaf(-kSymOff, pmb[h], o0[h]), acc0[h]));
+        acc1[h] = fmaf(B.tz.y, pmb[h], fmaf(B.tst.y, fmaf(-kSymOff, pmb[h], o1[h]), acc1[h]));
+      }
     } else {
 #pragma unroll
       for (int h = 0; h < G; ++h) { acc0[h] += o0[h]; acc1[h] += o1[h]; }
@@ -450,6 +463,8 @@ struct Decoder {
             const uint32_t code = code_sel<BITS, 64>(B.vw + k * (R / 8), half_row_token(t));
             float dense;
             if constexpr (MODE == SYM) dense = ((float)code - kSymOff) * (k ? B.tst.y : B.tst.x);
+            else if constexpr (MODE == ASYM)
+              dense = fmaf((float)code - kSymOff, k ? B.tst.y : B.tst.x, k ? B.tz.y : B.tz.x);
             else dense = fmaf(vval(code), ol.vS[t], ol.vM[t]);
             const float delta = __half2float(val[e]) - dense;
 #pragma unroll

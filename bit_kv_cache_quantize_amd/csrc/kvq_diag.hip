@@ -59,6 +59,10 @@ struct DiagBlock {
     if constexpr (MODE == SYM) {
       const __half s = reinterpret_cast<const __half*>(rec + st)[c];   // per channel for both
       return ((double)q - (double)(1 << (BITS - 1))) * (double)__half2float(s);
+    } else if constexpr (MODE == ASYM) {   // per channel for both: (u - 8) s + zero
+      const __half s = reinterpret_cast<const __half*>(rec + st)[c];
+      const __half z = reinterpret_cast<const __half*>(rec + st + 256)[c];
+      return ((double)q - 8.0) * (double)__half2float(s) + (double)__half2float(z);
     } else if constexpr (MODE == NUQ) {
       const double z = f32_at(st + 4 * vi), h = f32_at(st + 512 + 4 * vi);
       return (double)cb[tensor * kCbStride + q] * h + z;
@@ -196,6 +200,7 @@ hipError_t launch_diag(int mode, int bits, const DiagArgs& a, int batch, hipStre
     case KVARN * 8 + 8: return launch_d<KVARN, 8>(a, batch, s);
     case SYM * 8 + 4: return launch_d<SYM, 4>(a, batch, s);
     case SYM * 8 + 8: return launch_d<SYM, 8>(a, batch, s);
+    case ASYM * 8 + 4: return launch_d<ASYM, 4>(a, batch, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -23,7 +23,7 @@ constexpr int kCbStride = 32;
 constexpr int kNuqBuckets = 1024;
 constexpr int kNuqLutStride = 1032;   // entries per (layer, kv head, K/V) slot (1025 used)
 
-enum Mode { RTN = 0, NUQ = 1, KVARN = 2, SYM = 3 };
+enum Mode { RTN = 0, NUQ = 1, KVARN = 2, SYM = 3, ASYM = 4 };
 
 // Byte offsets of the segments of one block record (all 16-byte aligned).
 struct RecordLayout {

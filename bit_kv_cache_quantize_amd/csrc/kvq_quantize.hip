@@ -410,6 +410,12 @@ __device__ __forceinline__ VecStats stats_of(float lo, float hi, float amax) {
     v.sb = __fmul_rn(__fsub_rn(hi, lo), 0.5f);   // h
     v.rc = v.sb == 0.f ? 0.f : __fdiv_rn(1.f, v.sb);
     v.off = v.sa;
+  } else if constexpr (MODE == ASYM) {
+    // s = fp16((max - min) / 15), zero = fp16(min + 8 s): min maps to -8, max to 7
+    v.sa = __half2float(__float2half_rn(__fdiv_rn(__fsub_rn(hi, lo), 15.0f)));
+    v.sb = __half2float(__float2half_rn(__fadd_rn(lo, __fmul_rn(8.0f, v.sa))));
+    v.rc = v.sa == 0.f ? 0.f : __fdiv_rn(1.f, v.sa);
+    v.off = v.sb;
   } else if constexpr (MODE == SYM) {
     v.sa = __half2float(__float2half_rn(__fdiv_rn(amax, (float)((1 << (BITS - 1)) - 1))));   // absmax / 7 (int8: 127)
     v.sb = 0.f;
@@ -470,7 +476,7 @@ __device__ __forceinline__ uint32_t code_of(float d, const VecStats& v, const fl
       return __float_as_uint(e.x) + (u >= e.y ? 1u : 0u);
     }
     return nuq_search<BITS>(u, tau);
-  } else if constexpr (MODE == SYM) {
+  } else if constexpr (MODE == SYM || MODE == ASYM) {
     const float q = rintf(div_rn(d, v.sa, v.rc));
     constexpr int H = 1 << (BITS - 1);   // offset binary: u = q + 8 (int8: q + 128)
     return (uint32_t)((int)fminf(fmaxf(q, (float)-H), (float)(H - 1)) + H);
@@ -491,7 +497,7 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
   uint8_t* rec = a.rec + (unit * a.max_blocks + (size_t)(a.blk0 + j)) * a.lay.rec_bytes;
   constexpr int R = 16 * BITS;                                  // bytes per 128 codes
   const int k_out = KO == 0 ? 0 : (KO == 1 ? 1 : a.k_out);
-  constexpr bool per_chan = TENSOR == 0 || MODE == SYM;         // vector = a channel over the block's tokens
+  constexpr bool per_chan = TENSOR == 0 || MODE == SYM || MODE == ASYM;   // vector = a channel over the block's tokens
   int ph = 0;                                                   // alternating cross-wave buffer
 
   if (k_out > 0)
@@ -765,6 +771,15 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
           for (int k = 0; k < 4; ++k)
             hw[k] = __builtin_bit_cast(uint32_t, __halves2half2(__float2half_rn(vs[2 * k].sa), __float2half_rn(vs[2 * k + 1].sa)));
           *reinterpret_cast<uint4*>(st + 16 * g) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        } else if constexpr (MODE == ASYM) {   // fp16 scales, then fp16 zero points
+          uint32_t hs[4], hz[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            hs[k] = __builtin_bit_cast(uint32_t, __halves2half2(__float2half_rn(vs[2 * k].sa), __float2half_rn(vs[2 * k + 1].sa)));
+            hz[k] = __builtin_bit_cast(uint32_t, __halves2half2(__float2half_rn(vs[2 * k].sb), __float2half_rn(vs[2 * k + 1].sb)));
+          }
+          *reinterpret_cast<uint4*>(st + 16 * g) = make_uint4(hs[0], hs[1], hs[2], hs[3]);
+          *reinterpret_cast<uint4*>(st + 256 + 16 * g) = make_uint4(hz[0], hz[1], hz[2], hz[3]);
         } else {
           float4* ds = reinterpret_cast<float4*>(st) + 2 * g;
           float4* dm = reinterpret_cast<float4*>(st + 512) + 2 * g;
@@ -1027,6 +1042,7 @@ hipError_t launch_quantize(int mode, int bits, const QuantArgs& a, int n_blocks,
     case KVARN * 8 + 8: return launch_q<KVARN, 8>(a, n_blocks, batch, s);
     case SYM * 8 + 4: return launch_q<SYM, 4>(a, n_blocks, batch, s);
     case SYM * 8 + 8: return launch_q<SYM, 8>(a, n_blocks, batch, s);
+    case ASYM * 8 + 4: return launch_q<ASYM, 4>(a, n_blocks, batch, s);
     default: return hipErrorInvalidValue;
   }
 }

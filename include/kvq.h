@@ -54,7 +54,9 @@ typedef enum {
   KVQ_MODE_RTN = 0,       /* asymmetric uniform RTN, min/range (KVQuant notes 1.2, 3.1) */
   KVQ_MODE_NUQ = 1,       /* codebook argmin on [-1, 1] (KVQuant notes 1.2, 3.3) */
   KVQ_MODE_KVARN = 2,     /* Hadamard + VarN + RTN with s1 (KVarN core method) */
-  KVQ_MODE_SYM_INT4 = 3   /* symmetric int4 (int8 with bits = 8), fp16 scales (TurboQuant blog 4.2) */
+  KVQ_MODE_SYM_INT4 = 3,  /* symmetric int4 (int8 with bits = 8), fp16 scales (TurboQuant blog 4.2) */
+  KVQ_MODE_ASYM_INT4 = 4  /* asymmetric int4 clamp(round((x - zero) / scale), -8, 7), fp16 scale and
+                             zero (TurboQuant blog 2.1) */
 } kvq_mode;
 
 #define KVQ_HEAD_DIM 128
@@ -75,7 +77,8 @@ typedef struct {
   int32_t max_tokens;       /* capacity per sequence and layer, multiple of 128, >= 128 */
   int32_t mode;             /* kvq_mode */
   int32_t bits;             /* 2, 3 or 4; 8 with RTN, KVARN or SYM_INT4 (the blog's 8-bit KV for
-                               sensitive layers, 2.2 / 5.1); KVQ_MODE_SYM_INT4 requires 4 or 8 */
+                               sensitive layers, 2.2 / 5.1); KVQ_MODE_SYM_INT4 requires 4 or 8,
+                               KVQ_MODE_ASYM_INT4 4 */
   int32_t outliers_per_vec; /* 0..8 fp16 outliers per quantization vector; 0 with KVARN */
   int32_t pre_rope;         /* 1: keys are stored before RoPE and rotated at decode; 0 with KVARN */
   float rope_theta;         /* RoPE base (10000 in the pages), > 0 when pre_rope */
@@ -212,9 +215,10 @@ kvq_status kvq_set_decode_splits(kvq_cache cache, int splits);
  *       grid of 4-token groups transposed: position p holds
  *       u = 16*((p>>2)&3) + 4*(p>>4) + (p&3) (storage order only)
  *   ks  key statistics per channel: RTN/KVARN f32 s[128] then f32 m[128];
- *       NUQ f32 z[128] then f32 h[128]; SYM_INT4 f16 s[128]
+ *       NUQ f32 z[128] then f32 h[128]; SYM_INT4 f16 s[128]; ASYM_INT4 f16 s[128]
+ *       then f16 zero[128]
  *   vs  value statistics: per token (RTN/KVARN s then m, NUQ z then h, f32);
- *       SYM_INT4 per channel f16 s[128]
+ *       SYM_INT4 / ASYM_INT4 per channel, as for the keys
  *   k1  KVARN only: f32 s1[128] per token;  v1: KVARN only: f32 s1[128] per channel
  *   outliers (outliers_per_vec = k > 0):
  *       key CSR by token:     f16 val[128k], u16 row_ptr[129], u8 channel[128k]
@@ -227,7 +231,9 @@ kvq_status kvq_set_decode_splits(kvq_cache cache, int splits);
  * 8-bit: byte j = code j.
  * Codes: RTN/KVARN q in 0..2^b-1 with x = q*s + m (KVARN: times s1);
  * NUQ q indexes the codebook, x = C[q]*h + z; SYM_INT4 u = q + 2^(b-1), x = (u - 2^(b-1))*s
- * (4 bits: u = q + 8, s = fp16(absmax / 7); 8 bits: u = q + 128, s = fp16(absmax / 127)).
+ * (4 bits: u = q + 8, s = fp16(absmax / 7); 8 bits: u = q + 128, s = fp16(absmax / 127));
+ * ASYM_INT4 u = q + 8, x = (u - 8)*s + zero with s = fp16((max - min) / 15) and
+ * zero = fp16(min + 8 s) over the vector (keys and values per channel over the block).
  */
 kvq_status kvq_block_span(kvq_cache cache, int layer, int b, int kv_head, int block,
                           size_t* offset, size_t* bytes);

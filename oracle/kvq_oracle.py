@@ -48,7 +48,7 @@ import numpy as np
 T = 128          # tokens per quantization block
 D = 128          # head dimension (channels)
 
-MODE_RTN, MODE_NUQ, MODE_KVARN, MODE_SYM_INT4 = 0, 1, 2, 3
+MODE_RTN, MODE_NUQ, MODE_KVARN, MODE_SYM_INT4, MODE_ASYM_INT4 = 0, 1, 2, 3, 4
 
 
 # ---------------------------------------------------------------------------
@@ -200,6 +200,44 @@ def sym_codes(x32: np.ndarray, s16: np.ndarray, bits: int = 4) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Asymmetric block int4 ([BLOG] 2.1: q = clamp(round((x - zero) / scale), -8, 7),
+# x ~ q * scale + zero, scale and zero kept in fp16)
+# ---------------------------------------------------------------------------
+
+def asym_stats(x32: np.ndarray, keep: np.ndarray, axis: int):
+    """fp16 (scale, zero) of each vector over its non-outlier entries.
+
+    Reading: the blog gives the quantizer and the dequantizer but not how scale and zero
+    are found; the plainest choice maps the vector's range onto the 16 levels, the minimum
+    to -8 and the maximum to 7: scale = (max - min) / 15, zero = min + 8 * scale. Both are
+    rounded to fp16 as stored (scale first, zero from the rounded scale), one fp32
+    operation at a time, and the codes use the stored values.
+    """
+    lo = np.where(keep, x32, np.float32(np.inf)).min(axis=axis).astype(np.float32)
+    hi = np.where(keep, x32, np.float32(-np.inf)).max(axis=axis).astype(np.float32)
+    s16 = ((hi - lo).astype(np.float32) / np.float32(15.0)).astype(np.float32).astype(np.float16)
+    z16 = (lo + (np.float32(8.0) * s16.astype(np.float32)).astype(np.float32)).astype(np.float32).astype(np.float16)
+    return s16, z16
+
+
+def asym_codes(x32: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
+    """u = clamp(rint((x - zero) / scale), -8, 7) + 8 (offset binary); scale 0 gives u = 8."""
+    s = np.asarray(s16, np.float16).astype(np.float32)
+    z = np.asarray(z16, np.float16).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = (x32 - z).astype(np.float32) / s
+    q = np.clip(np.rint(u), -8, 7)
+    q = np.where(s == 0, 0, q)
+    return (q + 8).astype(np.uint8)
+
+
+def dequant_asym(u: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
+    """x_hat = (u - 8) * scale + zero ([BLOG] 2.1)."""
+    return ((np.asarray(u, np.float64) - 8.0) * np.asarray(s16, np.float16).astype(np.float64)
+            + np.asarray(z16, np.float16).astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
 # Hadamard rotation and VarN ([KVARN] core method and method steps)
 # ---------------------------------------------------------------------------
 
@@ -295,8 +333,8 @@ class Block:
     """The logical content of one quantized block (no storage layout)."""
     kcodes: np.ndarray          # [T][D] u8, code of key (token t, channel c)
     vcodes: np.ndarray          # [T][D] u8, code of value (token t, channel c)
-    kstat: tuple                # RTN/KVARN (s[D], m[D]); NUQ (z[D], h[D]); SYM (s16[D],)
-    vstat: tuple                # RTN/KVARN (s[T], m[T]); NUQ (z[T], h[T]); SYM (s16[D],)
+    kstat: tuple                # RTN/KVARN (s[D], m[D]); NUQ (z[D], h[D]); SYM (s16[D],); ASYM (s16[D], z16[D])
+    vstat: tuple                # RTN/KVARN (s[T], m[T]); NUQ (z[T], h[T]); SYM (s16[D],); ASYM (s16[D], z16[D])
     ks1: np.ndarray | None = None   # KVARN: f32 [T], per token
     vs1: np.ndarray | None = None   # KVARN: f32 [D], per channel
     kmask: np.ndarray | None = None  # [T][D] outlier positions of keys
@@ -349,7 +387,7 @@ def quantize_block(k16: np.ndarray, v16: np.ndarray, cfg: Config,
                      (ks, km), (vs, vm), ks1=ks1, vs1=vs1)
 
     kmask = outlier_mask(k16, ko, axis=0)      # per channel, over tokens
-    vaxis = 0 if mode == MODE_SYM_INT4 else 1  # values per token (sym-int4: per channel)
+    vaxis = 0 if mode in (MODE_SYM_INT4, MODE_ASYM_INT4) else 1   # values per token (block int4: per channel)
     vmask = outlier_mask(v16, ko, axis=vaxis)
     kkeep, vkeep = ~kmask, ~vmask
     # the dense part: outlier positions hold 0
@@ -373,6 +411,12 @@ def quantize_block(k16: np.ndarray, v16: np.ndarray, cfg: Config,
         kc = sym_codes(kx, kss[None, :], b)
         vc = sym_codes(vx, vss[None, :], b)
         kstat, vstat = (kss,), (vss,)
+    elif mode == MODE_ASYM_INT4:
+        kss, kzs = asym_stats(kx, kkeep, axis=0)
+        vss, vzs = asym_stats(vx, vkeep, axis=0)
+        kc = asym_codes(kx, kss[None, :], kzs[None, :])
+        vc = asym_codes(vx, vss[None, :], vzs[None, :])
+        kstat, vstat = (kss, kzs), (vss, vzs)
     else:
         raise ValueError(mode)
     blk = Block(kc, vc, kstat, vstat)
@@ -430,6 +474,9 @@ def dequant_block(blk: Block, cfg: Config, cb_k=None, cb_v=None):
     elif mode == MODE_SYM_INT4:
         kh = dequant_sym(blk.kcodes, blk.kstat[0][None, :], cfg.bits)
         vh = dequant_sym(blk.vcodes, blk.vstat[0][None, :], cfg.bits)
+    elif mode == MODE_ASYM_INT4:
+        kh = dequant_asym(blk.kcodes, blk.kstat[0][None, :], blk.kstat[1][None, :])
+        vh = dequant_asym(blk.vcodes, blk.vstat[0][None, :], blk.vstat[1][None, :])
     else:
         raise ValueError(mode)
     if blk.kmask is not None:

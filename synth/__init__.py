@@ -171,7 +171,7 @@ def gen_codebook(wl: "Workload", layer: int, kv_head: int, which: int, bits: int
 # Workloads: shapes, cache options and value structure (data only)
 # --------------------------------------------------------------------------
 
-MODE_RTN, MODE_NUQ, MODE_KVARN, MODE_SYM_INT4 = 0, 1, 2, 3
+MODE_RTN, MODE_NUQ, MODE_KVARN, MODE_SYM_INT4, MODE_ASYM_INT4 = 0, 1, 2, 3, 4
 
 
 @dataclass(frozen=True)
@@ -259,6 +259,6 @@ def _self_check():
 __all__ = [
     "Workload", "WORKLOADS", "gen_k", "gen_v", "gen_q", "gen_codebook", "channel_params",
     "stream_key", "words", "normals", "gains", "mix64", "device_tables", "mu_sd_table",
-    "key_table", "MODE_RTN", "MODE_NUQ", "MODE_KVARN", "MODE_SYM_INT4", "HEAD_DIM",
+    "key_table", "MODE_RTN", "MODE_NUQ", "MODE_KVARN", "MODE_SYM_INT4", "MODE_ASYM_INT4", "HEAD_DIM",
     "KIND_K", "KIND_V", "KIND_GAIN", "KIND_Q",
 ]

@@ -15,7 +15,7 @@ import numpy as np
 from oracle import kvq_oracle as O
 
 T = D = 128
-MODE_RTN, MODE_NUQ, MODE_KVARN, MODE_SYM_INT4 = 0, 1, 2, 3
+MODE_RTN, MODE_NUQ, MODE_KVARN, MODE_SYM_INT4, MODE_ASYM_INT4 = 0, 1, 2, 3, 4
 
 
 def _align(x: int, a: int) -> int:
@@ -27,7 +27,7 @@ def layout(mode: int, bits: int, k_out: int) -> tuple[dict, int]:
     vs, [k1, v1 with KVARN], [ko_val, ko_ptr, ko_idx, vo_val, vo_ptr, vo_idx with
     outliers], each on a 16-byte boundary, the record padded to 256 bytes."""
     R = 16 * bits
-    stat = 256 if mode == MODE_SYM_INT4 else 1024
+    stat = {MODE_SYM_INT4: 256, MODE_ASYM_INT4: 512}.get(mode, 1024)
     segs = [("kc", T * R), ("vc", D * R), ("ks", stat), ("vs", stat)]
     if mode == MODE_KVARN:
         segs += [("k1", 4 * T), ("v1", 4 * D)]
@@ -93,6 +93,9 @@ def read_record(buf: np.ndarray, mode: int, bits: int, k_out: int, where: str = 
         o, n = off[seg]
         if mode == MODE_SYM_INT4:
             out[seg] = (buf[o:o + n].view(np.float16).copy(),)
+        elif mode == MODE_ASYM_INT4:   # fp16 scales then fp16 zero points, per channel
+            f = buf[o:o + n].view(np.float16)
+            out[seg] = (f[:128].copy(), f[128:].copy())
         else:
             f = buf[o:o + n].view(np.float32)
             out[seg] = (f[:128].copy(), f[128:].copy())

@@ -42,6 +42,7 @@ def cfg(**kw):
     dict(mode=K.KVQ_MODE_KVARN, varn_iters=65), dict(n_layers=0), dict(batch=0),
     dict(sink_tokens=129), dict(sink_tokens=-1), dict(fp16_window=100), dict(fp16_window=8320),
     dict(bits=6), dict(bits=16), dict(mode=K.KVQ_MODE_NUQ, bits=8), dict(mode=K.KVQ_MODE_SYM_INT4, bits=2),
+    dict(mode=K.KVQ_MODE_ASYM_INT4, bits=8), dict(mode=5),
     dict(fp16_window=-128),
 ])
 def test_invalid_configs_are_rejected(kw):
@@ -54,7 +55,7 @@ def test_invalid_configs_are_rejected(kw):
 @pytest.mark.parametrize("mode,bits,k_out,pre_rope,sink,window", [
     (K.KVQ_MODE_RTN, 4, 0, 0, 0, 0), (K.KVQ_MODE_NUQ, 3, 1, 1, 0, 0), (K.KVQ_MODE_KVARN, 2, 0, 0, 0, 0),
     (K.KVQ_MODE_SYM_INT4, 4, 0, 0, 0, 0), (K.KVQ_MODE_RTN, 2, 1, 1, 0, 0), (K.KVQ_MODE_NUQ, 4, 8, 0, 0, 0),
-    (K.KVQ_MODE_RTN, 2, 1, 1, 1, 0), (K.KVQ_MODE_KVARN, 4, 0, 0, 4, 256)])
+    (K.KVQ_MODE_RTN, 2, 1, 1, 1, 0), (K.KVQ_MODE_KVARN, 4, 0, 0, 4, 256), (K.KVQ_MODE_ASYM_INT4, 4, 1, 1, 0, 0)])
 def test_cache_bytes_matches_documented_record_layout(mode, bits, k_out, pre_rope, sink, window):
     c = cfg(mode=mode, bits=bits, outliers_per_vec=k_out, pre_rope=pre_rope, sink_tokens=sink, fp16_window=window)
     _, rec = R.layout(mode, bits, k_out)

@@ -42,6 +42,9 @@ CASES = {
     "kvarn3": (small("c3_kvarn_gqa_b16_8k", bits=3, batch=1, n_q_heads=2, n_kv_heads=2), 0, 0),
     "sym4_out1": (small("c4_blog_int4_32l_b32_32k", n_layers=1, batch=1, n_q_heads=2, n_kv_heads=2,
                         outliers_per_vec=1), 0, 0),
+    "asym4_out1": (small("c4_blog_int4_32l_b32_32k", n_layers=1, mode=synth.MODE_ASYM_INT4, batch=1, n_q_heads=2,
+                         n_kv_heads=2, outliers_per_vec=1), 0, 0),
+    "sym8": (small("c4_blog_int4_32l_b32_32k", n_layers=1, bits=8, batch=1, n_q_heads=2, n_kv_heads=2), 0, 0),
 }
 
 

@@ -124,6 +124,11 @@ CASES = {
     "sym4_g8_mfma": (small("c4_blog_int4_32l_b32_32k", n_layers=1, batch=1, n_q_heads=16, n_kv_heads=2), [512]),
     "sym4_g1_mfma": (small("c4_blog_int4_32l_b32_32k", n_layers=1, batch=2, n_q_heads=2, n_kv_heads=2), [300]),
     "kvarn2_g8_mfma": (small("c3_kvarn_gqa_b16_8k", batch=1, n_q_heads=16, n_kv_heads=2), [256, 100]),
+    # the blog's asymmetric int4 variant (VALU decode)
+    "asym4_g4": (small("c4_blog_int4_32l_b32_32k", n_layers=1, mode=synth.MODE_ASYM_INT4, batch=2, n_q_heads=8,
+                       n_kv_heads=2), [512, 77]),
+    "asym4_rope_out1_g1": (small("c4_blog_int4_32l_b32_32k", n_layers=1, mode=synth.MODE_ASYM_INT4, batch=1,
+                                 n_q_heads=2, n_kv_heads=2, pre_rope=1, outliers_per_vec=1), [257]),
     "kvarn4_g1_mfma": (small("c3_kvarn_gqa_b16_8k", bits=4, batch=1, n_q_heads=2, n_kv_heads=2), [384]),
 }
 
@@ -339,7 +344,8 @@ def test_nuq_codes_exhaustive_fp16(K, bits, crowded):
     (synth.MODE_RTN, 3, 1, 0), (synth.MODE_RTN, 2, 1, 1), (synth.MODE_RTN, 4, 0, 0),
     (synth.MODE_NUQ, 3, 1, 1), (synth.MODE_NUQ, 4, 0, 0),
     (synth.MODE_SYM_INT4, 4, 0, 0), (synth.MODE_SYM_INT4, 4, 1, 1),
-    (synth.MODE_KVARN, 2, 0, 0), (synth.MODE_KVARN, 4, 0, 0)])
+    (synth.MODE_KVARN, 2, 0, 0), (synth.MODE_KVARN, 4, 0, 0),
+    (synth.MODE_ASYM_INT4, 4, 0, 0), (synth.MODE_ASYM_INT4, 4, 1, 1)])
 def test_degenerate_vectors_match_oracle(K, mode, bits, k_out, rope):
     """Constant and tied vectors: records against the oracle (KVarN within its tolerance)
     and attention, through every decode kernel the combination selects. KVarN runs on a

@@ -821,3 +821,30 @@ def test_symmetric_int8_for_sensitive_layers_matches_the_blog_semantics_at_8_bit
     # eight bits quantize a 4-bit block's worth of data sixteen times finer
     deq4 = O.dequant_sym(O.sym_codes(x, O.sym_scale(x, keep, 0, 4)[None, :], 4), O.sym_scale(x, keep, 0, 4)[None, :], 4)
     assert np.max(np.abs(deq - x)) < np.max(np.abs(deq4 - x)) / 10
+
+
+def test_asymmetric_int4_matches_the_blog_formula_in_torch():
+    """[BLOG] 2.1: q = clamp(round((x - zero) / scale), -8, 7), x ~ q * scale + zero, with
+    fp16 scale and zero per 128-element sequence block. The quantizer written with torch CPU
+    ops given the oracle's (scale, zero); the range reading maps the minimum to -8 and the
+    maximum to 7; the error stays within half a step; a constant vector is exact."""
+    r = rng(45)
+    x16 = (r.standard_normal((128, 128)) * np.array([0.5, 9.0] * 64)[None, :] + 3.0).astype(np.float16)
+    x = x16.astype(np.float32)
+    keep = np.ones_like(x, bool)
+    s16, z16 = O.asym_stats(x, keep, axis=0)
+    u = O.asym_codes(x, s16[None, :], z16[None, :])
+    xt = torch.from_numpy(x)
+    st = torch.from_numpy(s16.astype(np.float32))[None, :]
+    zt = torch.from_numpy(z16.astype(np.float32))[None, :]
+    qt = ((xt - zt) / st).round().clamp(-8, 7)
+    assert np.array_equal((qt + 8).to(torch.uint8).numpy(), u)
+    lo, hi = x.argmin(axis=0), x.argmax(axis=0)
+    assert np.all(u[lo, np.arange(128)] == 0) and np.all(u[hi, np.arange(128)] == 15)
+    xh = O.dequant_asym(u, s16[None, :], z16[None, :])
+    assert np.all(np.abs(xh - x) <= s16.astype(np.float64)[None, :] * (0.5 + 1e-2) + 1e-3 * np.abs(x))
+    # scale and zero as fp16 values of (max - min) / 15 and min + 8 scale
+    assert np.array_equal(s16, ((x.max(axis=0) - x.min(axis=0)) / np.float32(15)).astype(np.float16))
+    c = np.full((128, 1), 2.5, np.float32)
+    sc, zc = O.asym_stats(c, np.ones_like(c, bool), axis=0)
+    assert sc[0] == 0 and O.dequant_asym(O.asym_codes(c, sc[None], zc[None]), sc[None], zc[None])[0, 0] == 2.5
