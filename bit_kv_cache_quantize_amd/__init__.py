@@ -54,6 +54,8 @@ _sig = {
     "kvq_decode_attn": [_vp, _i, _vp, _vp, ctypes.c_float, _vp],
     "kvq_decode_attn_static": [_vp, _i, _vp, _vp, ctypes.c_float, _vp],
     "kvq_error_decomposition": [_vp, _i, _i, _i, _vp, _vp, _vp, _vp],
+    "kvq_codebook_build_workspace": [ctypes.c_int64, _i, ctypes.POINTER(_sz)],
+    "kvq_codebook_build": [_vp, _vp, ctypes.c_int64, _i, _i, _vp, _sz, _vp, _vp, _vp],
     "kvq_cache_length": [_vp, _i, ctypes.POINTER(ctypes.c_int32)],
     "kvq_cache_reset": [_vp, _i],
     "kvq_set_decode_splits": [_vp, _i],
@@ -143,6 +145,37 @@ def kvq_decode_attn_static(handle: int, layer: int, q, out, softmax_scale: float
 def kvq_error_decomposition(handle: int, layer: int, block0: int, n_blocks: int, k, v, out, stream=None):
     _check(lib.kvq_error_decomposition(handle, layer, block0, n_blocks, _ptr(k), _ptr(v), _ptr(out), _stream(stream)),
            "kvq_error_decomposition")
+
+
+def kvq_codebook_build_workspace(n: int, bits: int) -> int:
+    b = _sz(0)
+    _check(lib.kvq_codebook_build_workspace(n, bits, ctypes.byref(b)), "kvq_codebook_build_workspace")
+    return b.value
+
+
+def kvq_codebook_build(act, weight, n: int, bits: int, max_iters: int, workspace, workspace_bytes: int, codebook,
+                       iters=None, stream=None):
+    _check(lib.kvq_codebook_build(_ptr(act), _ptr(weight), n, bits, max_iters, _ptr(workspace), workspace_bytes,
+                                  _ptr(codebook), _ptr(iters), _stream(stream)), "kvq_codebook_build")
+
+
+def build_codebook(act, bits: int, weight=None, max_iters: int = 100, stream=None):
+    """Codebook (fp32 [2^bits] device tensor) and update steps taken (int32 [1] device tensor),
+    by kvq_codebook_build: act and weight are fp32 device tensors of the same length; the
+    workspace is a torch allocation kept alive by the returned codebook tensor."""
+    check_tensors(act.device, [("act", act, torch.float32)] + ([("weight", weight, torch.float32)] if weight is not None else []))
+    n = act.numel()
+    if weight is not None and weight.numel() != n:
+        raise ValueError("act and weight differ in length")
+    nb = kvq_codebook_build_workspace(n, bits)
+    raw = torch.empty(nb + 256, dtype=torch.uint8, device=act.device)
+    pad = (-raw.data_ptr()) % 256
+    ws = raw[pad:pad + nb]
+    cb = torch.empty(1 << bits, dtype=torch.float32, device=act.device)
+    it = torch.zeros(1, dtype=torch.int32, device=act.device)
+    kvq_codebook_build(act, weight, n, bits, max_iters, ws, nb, cb, it, stream)
+    cb._kvq_workspace = raw   # the kernels run after this returns: the workspace lives with the result
+    return cb, it
 
 
 def kvq_cache_length(handle: int, layer: int) -> int:

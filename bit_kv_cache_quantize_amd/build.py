@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
 SOURCES = ["kvq_api.hip", "kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_decode_tab.hip",
-           "kvq_decode_fp16.hip", "kvq_diag.hip"]
+           "kvq_decode_fp16.hip", "kvq_diag.hip", "kvq_codebook.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 # -ffp-contract=off: the quantize path's fp32 decisions must not be fused; the decode

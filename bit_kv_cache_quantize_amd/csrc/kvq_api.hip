@@ -635,6 +635,73 @@ kvq_status kvq_error_decomposition(kvq_cache c, int layer, int block0, int n_blo
                    "launch error diagnostic");
 }
 
+}  // extern "C"
+
+namespace {
+
+struct CodebookWs {
+  int n_ranges;
+  int64_t per_range;
+  size_t off_assign, off_partials, off_changes, off_state, total;
+};
+
+CodebookWs codebook_ws(int64_t n) {
+  CodebookWs w{};
+  w.n_ranges = (int)std::min<int64_t>(kvq::kCodebookMaxRanges, (n + 4095) / 4096);
+  w.per_range = (n + w.n_ranges - 1) / w.n_ranges;
+  size_t pos = 0;
+  auto place = [&](size_t size) { pos = align_up(pos, 256); const size_t at = pos; pos += size; return at; };
+  w.off_assign = place((size_t)n);
+  w.off_partials = place((size_t)w.n_ranges * 2 * 16 * sizeof(double));
+  w.off_changes = place((size_t)w.n_ranges * sizeof(int));
+  w.off_state = place(sizeof(kvq::CodebookState));
+  w.total = align_up(pos, 256);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_codebook_build_workspace(int64_t n, int bits, size_t* bytes) {
+  if (!bytes) return fail(KVQ_ERR_ARG, "bytes is NULL");
+  if (n < 1 || n > ((int64_t)1 << 40)) return fail(KVQ_ERR_ARG, "n must be in 1..2^40 (got %lld)", (long long)n);
+  if (bits < 2 || bits > 4) return fail(KVQ_ERR_ARG, "bits must be 2, 3 or 4 (got %d)", bits);
+  *bytes = codebook_ws(n).total;
+  return ok();
+}
+
+kvq_status kvq_codebook_build(const float* act, const float* weight, int64_t n, int bits, int max_iters,
+                              void* workspace, size_t workspace_bytes, float* codebook, int32_t* iters,
+                              void* stream) {
+  size_t need = 0;
+  kvq_status st = kvq_codebook_build_workspace(n, bits, &need);
+  if (st != KVQ_OK) return st;
+  if (!act || !workspace || !codebook) return fail(KVQ_ERR_ARG, "act, workspace or codebook is NULL");
+  if (max_iters < 1 || max_iters > 1000) return fail(KVQ_ERR_ARG, "max_iters must be in 1..1000 (got %d)", max_iters);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(KVQ_ERR_ARG, "workspace must be 256-byte aligned");
+  if (reinterpret_cast<uintptr_t>(act) % 4 || reinterpret_cast<uintptr_t>(weight) % 4 ||
+      reinterpret_cast<uintptr_t>(codebook) % 4 || reinterpret_cast<uintptr_t>(iters) % 4)
+    return fail(KVQ_ERR_ARG, "act, weight, codebook and iters must be 4-byte aligned");
+  if (workspace_bytes < need) return fail(KVQ_ERR_SIZE, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+  const CodebookWs w = codebook_ws(n);
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  kvq::CodebookArgs a{};
+  a.act = act;
+  a.weight = weight;
+  a.n = n;
+  a.per_range = w.per_range;
+  a.n_ranges = w.n_ranges;
+  a.assign = base + w.off_assign;
+  a.partials = reinterpret_cast<double*>(base + w.off_partials);
+  a.changes = reinterpret_cast<int*>(base + w.off_changes);
+  a.state = reinterpret_cast<kvq::CodebookState*>(base + w.off_state);
+  a.out = codebook;
+  a.iters_out = iters;
+  return hip_check(kvq::launch_codebook_build(bits, a, max_iters, static_cast<hipStream_t>(stream)),
+                   "launch codebook builder");
+}
+
 kvq_status kvq_cache_length(kvq_cache c, int layer, int32_t* n_tokens) {
   const kvq_status st = check_layer(c, layer);
   if (st != KVQ_OK) return st;

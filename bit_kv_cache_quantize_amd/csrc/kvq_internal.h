@@ -100,6 +100,27 @@ struct DiagArgs {
   double* out;
 };
 
+// Weighted k-means codebook builder state (device memory, in the caller's workspace).
+struct CodebookState {
+  double centres[16];
+  int converged;            // set once an iteration changes no assignment
+  int iter;                 // update steps taken
+};
+struct CodebookArgs {
+  const float* act;         // [n] normalised activations in [-1, 1]
+  const float* weight;      // [n] weights, or null for unit weights
+  int64_t n, per_range;     // samples; samples per assign workgroup
+  int n_ranges;             // assign workgroups
+  uint8_t* assign;          // [n] current centre of every sample
+  double* partials;         // [n_ranges][2 K]: sum F, sum F a per centre
+  int* changes;             // [n_ranges] changed assignments
+  CodebookState* state;
+  float* out;               // [K] the codebook
+  int32_t* iters_out;       // update steps (or null)
+};
+constexpr int kCodebookMaxRanges = 1024;
+hipError_t launch_codebook_build(int bits, const CodebookArgs& a, int max_iters, hipStream_t s);
+
 hipError_t launch_quantize(int mode, int bits, const QuantArgs& a, int n_blocks, int batch,
                            hipStream_t s);
 hipError_t launch_tail(const TailArgs& a, int batch, hipStream_t s);

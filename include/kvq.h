@@ -191,6 +191,29 @@ kvq_status kvq_decode_attn_static(kvq_cache cache, int layer, const void* q_f16,
 kvq_status kvq_error_decomposition(kvq_cache cache, int layer, int block0, int n_blocks, const void* k_f16,
                                    const void* v_f16, double* out, void* stream);
 
+/*
+ * NUQ codebook builder (KVQuant notes 3.3, Algorithm 2: sensitivity-weighted k-means on
+ * activations normalised to [-1, 1]). 2^bits centres start evenly spaced over [-1, 1];
+ * each iteration assigns every activation to its nearest centre (ties to the smaller
+ * index) and moves each centre to the weighted mean of its members (a centre without
+ * members stays); it stops when no assignment changes, after at most max_iters updates.
+ * Sums and centres are fp64 with a fixed summation order (reproducible).
+ * act:    dev, fp32 [n], the normalised activations (e.g. key channels or value tokens of
+ *         calibration data mapped to [-1, 1] by (x - z) / h as the quantizer does).
+ * weight: dev, fp32 [n], non-negative weights (Fisher information in the notes), or NULL
+ *         for unit weights.
+ * workspace: dev, 256-byte aligned, kvq_codebook_build_workspace(n, bits) bytes.
+ * codebook: dev, fp32 [2^bits] out, ascending, ready for kvq_codebook_load (which checks
+ *         its entry spacing). iters: dev int32 [1] out, the update steps taken, or NULL.
+ * Asynchronous on stream (2 max_iters + 1 launches; after convergence they do nothing).
+ * Errors: KVQ_ERR_ARG (n < 1, bits not 2..4, max_iters not 1..1000, NULL or misaligned
+ * pointers), KVQ_ERR_SIZE (workspace too small).
+ */
+kvq_status kvq_codebook_build_workspace(int64_t n, int bits, size_t* bytes);
+kvq_status kvq_codebook_build(const float* act, const float* weight, int64_t n, int bits, int max_iters,
+                              void* workspace, size_t workspace_bytes, float* codebook, int32_t* iters,
+                              void* stream);
+
 /* Tokens currently held by a layer (host-side counter, no device access). */
 kvq_status kvq_cache_length(kvq_cache cache, int layer, int32_t* n_tokens);
 

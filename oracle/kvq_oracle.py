@@ -171,6 +171,35 @@ def nuq_codes(x32: np.ndarray, z: np.ndarray, h: np.ndarray, codebook: np.ndarra
     return q
 
 
+def kmeans_codebook(a: np.ndarray, w: np.ndarray | None, bits: int, max_iters: int):
+    """Sensitivity-weighted NUQ codebook ([KVQ] 3.3, Algorithm 2): 2^b centres on normalised
+    activations a in [-1, 1] with weights w (None: unit weights).
+
+    The centres start evenly spaced over [-1, 1]; each step assigns every activation to its
+    nearest centre (ties to the smaller index, as the NUQ lookup) and moves each centre to the
+    weighted mean of its members. Readings: "until convergence" = until no assignment
+    changes, at most max_iters update steps; a centre with no members keeps its place.
+    Centres and sums in fp64. Returns (fp32 codebook, update steps taken)."""
+    a = np.asarray(a, np.float32).astype(np.float64)
+    wt = np.ones_like(a) if w is None else np.asarray(w, np.float32).astype(np.float64)
+    k = 1 << bits
+    c = -1.0 + 2.0 * np.arange(k, dtype=np.float64) / (k - 1)
+    prev = None
+    steps = 0
+    for _ in range(max_iters):
+        assign = np.argmin(np.abs(a[:, None] - c[None, :]), axis=1)   # first index on ties
+        if prev is not None and np.array_equal(assign, prev):
+            break
+        for j in range(k):
+            m = assign == j
+            sw = wt[m].sum()
+            if sw > 0:
+                c[j] = (wt[m] * a[m]).sum() / sw
+        prev = assign
+        steps += 1
+    return c.astype(np.float32), steps
+
+
 # ---------------------------------------------------------------------------
 # Symmetric block int4 ([BLOG] 2.1 and 4.2)
 # ---------------------------------------------------------------------------

@@ -848,3 +848,57 @@ def test_asymmetric_int4_matches_the_blog_formula_in_torch():
     c = np.full((128, 1), 2.5, np.float32)
     sc, zc = O.asym_stats(c, np.ones_like(c, bool), axis=0)
     assert sc[0] == 0 and O.dequant_asym(O.asym_codes(c, sc[None], zc[None]), sc[None], zc[None])[0, 0] == 2.5
+
+
+# --------------------------------------------------------------------------- codebook builder
+def test_kmeans_codebook_small_case_by_hand():
+    """[KVQ] Algorithm 2 on six points, 2 bits: centres -1, -1/3, 1/3, 1 collect
+    {-0.9, -0.8}, {-0.2}, {0.1, 0.5}, {0.95}; the weighted means follow by hand, and the
+    next assignment is unchanged, so the builder stops after one update."""
+    a = np.array([-0.9, -0.8, -0.2, 0.1, 0.5, 0.95], np.float32)
+    w = np.array([1.0, 3.0, 2.0, 1.0, 1.0, 5.0], np.float32)
+    c, steps = O.kmeans_codebook(a, w, 2, 50)
+    a64, w64 = a.astype(np.float64), w.astype(np.float64)
+    want = [(w64[0] * a64[0] + w64[1] * a64[1]) / (w64[0] + w64[1]), a64[2],
+            (w64[3] * a64[3] + w64[4] * a64[4]) / (w64[3] + w64[4]), a64[5]]
+    assert np.allclose(c, np.array(want, np.float32), rtol=0, atol=0)
+    assert steps == 1
+    cu, _ = O.kmeans_codebook(a, None, 2, 50)            # unit weights: plain means
+    assert cu[0] == np.float32((a64[0] + a64[1]) / 2)
+
+
+def test_kmeans_codebook_uniform_data_converges_to_interval_midpoints():
+    """Lloyd's fixed point for a uniform density on [-1, 1] with k centres: the midpoints of
+    k equal intervals, -1 + (2j + 1) / k (closed form); a fine uniform grid of samples
+    reaches it from the evenly spaced start."""
+    a = (np.arange(200000, dtype=np.float64) + 0.5) / 100000 - 1
+    for bits in (2, 3):
+        k = 1 << bits
+        c, steps = O.kmeans_codebook(a, None, bits, 500)
+        assert np.allclose(c, -1 + (2 * np.arange(k) + 1) / k, atol=2e-3), c
+        assert np.all(np.diff(c) > 0)
+
+
+def test_kmeans_codebook_separated_clusters_and_lloyd_invariants():
+    """Four well separated clusters with weights: each centre ends at the weighted mean of
+    its cluster (the fixed point of the update), the assignment is stable there, and the
+    weighted distortion never increases from one update to the next (Lloyd)."""
+    r = np.random.default_rng(46)
+    mus = np.array([-0.7, -0.1, 0.3, 0.8])
+    lab = r.integers(0, 4, 4000)
+    a = (mus[lab] + 0.02 * r.standard_normal(4000)).astype(np.float32)
+    w = r.lognormal(0, 1, 4000).astype(np.float32)
+    c, steps = O.kmeans_codebook(a, w, 2, 100)
+    a64, w64 = a.astype(np.float64), w.astype(np.float64)
+    for j in range(4):
+        m = lab == j
+        assert c[j] == pytest.approx(np.sum(w64[m] * a64[m]) / np.sum(w64[m]), abs=1e-7)
+    dist = []
+    for it in range(1, steps + 1):
+        ci, _ = O.kmeans_codebook(a, w, 2, it)
+        d = np.min(np.abs(a64[:, None] - ci.astype(np.float64)[None, :]), axis=1)
+        dist.append(np.sum(w64 * d * d))
+    assert all(x >= y - 1e-9 for x, y in zip(dist, dist[1:]))
+    # an empty cluster keeps its centre: all data at one point, 2 bits
+    c1, _ = O.kmeans_codebook(np.full(10, 0.9, np.float32), None, 2, 10)
+    assert np.allclose(c1, [-1.0, -1 / 3, 1 / 3, 0.9], atol=1e-7)
