@@ -23,6 +23,7 @@ KVQ_MODE_RTN, KVQ_MODE_NUQ, KVQ_MODE_KVARN, KVQ_MODE_SYM_INT4, KVQ_MODE_ASYM_INT
 KVQ_HEAD_DIM = 128
 KVQ_BLOCK_TOKENS = 128
 KVQ_MAX_SPLITS = 64
+KVQ_MAX_PAGED_BATCH = 64
 
 
 class kvq_config(ctypes.Structure):
@@ -31,7 +32,7 @@ class kvq_config(ctypes.Structure):
         ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
         ("mode", ctypes.c_int32), ("bits", ctypes.c_int32), ("outliers_per_vec", ctypes.c_int32),
         ("pre_rope", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("varn_iters", ctypes.c_int32),
-        ("sink_tokens", ctypes.c_int32), ("fp16_window", ctypes.c_int32),
+        ("sink_tokens", ctypes.c_int32), ("fp16_window", ctypes.c_int32), ("paged_pages", ctypes.c_int32),
     ]
 
 
@@ -62,6 +63,11 @@ _sig = {
     "kvq_block_span": [_vp, _i, _i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)],
     "kvq_tail_span": [_vp, _i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)],
     "kvq_decode_bytes": [_vp, _i, ctypes.POINTER(_sz)],
+    "kvq_quantize_append_paged": [_vp, _i, _vp, _vp, ctypes.POINTER(ctypes.c_int32), _i, _vp, _vp],
+    "kvq_decode_attn_paged": [_vp, _i, _vp, _vp, ctypes.c_float, _vp, _vp],
+    "kvq_sequence_length": [_vp, _i, _i, ctypes.POINTER(ctypes.c_int32)],
+    "kvq_sequence_reset": [_vp, _i, _i],
+    "kvq_page_span": [_vp, _i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)],
 }
 for _name, _args in _sig.items():
     getattr(lib, _name).argtypes = _args
@@ -100,9 +106,9 @@ def _stream(stream):
 
 def make_config(n_layers, batch, n_kv_heads, n_q_heads, max_tokens, mode, bits, outliers_per_vec=0,
                 pre_rope=0, rope_theta=10000.0, varn_iters=8, head_dim=KVQ_HEAD_DIM, sink_tokens=0,
-                fp16_window=0) -> kvq_config:
+                fp16_window=0, paged_pages=0) -> kvq_config:
     return kvq_config(n_layers, batch, n_kv_heads, n_q_heads, head_dim, max_tokens, mode, bits,
-                      outliers_per_vec, pre_rope, rope_theta, varn_iters, sink_tokens, fp16_window)
+                      outliers_per_vec, pre_rope, rope_theta, varn_iters, sink_tokens, fp16_window, paged_pages)
 
 
 def kvq_cache_bytes(cfg: kvq_config) -> int:
@@ -210,6 +216,38 @@ def kvq_decode_bytes(handle: int, layer: int) -> int:
     return n.value
 
 
+def _counts(n_new):
+    vals = [int(x) for x in n_new]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def kvq_quantize_append_paged(handle: int, layer: int, k, v, n_new, max_new: int, block_table, stream=None):
+    """n_new: one count per sequence (host sequence of ints); block_table: device int32."""
+    _check(lib.kvq_quantize_append_paged(handle, layer, _ptr(k), _ptr(v), _counts(n_new), max_new, _ptr(block_table),
+                                         _stream(stream)), "kvq_quantize_append_paged")
+
+
+def kvq_decode_attn_paged(handle: int, layer: int, q, out, softmax_scale: float, block_table, stream=None):
+    _check(lib.kvq_decode_attn_paged(handle, layer, _ptr(q), _ptr(out), softmax_scale, _ptr(block_table),
+                                     _stream(stream)), "kvq_decode_attn_paged")
+
+
+def kvq_sequence_length(handle: int, layer: int, b: int) -> int:
+    n = ctypes.c_int32(0)
+    _check(lib.kvq_sequence_length(handle, layer, b, ctypes.byref(n)), "kvq_sequence_length")
+    return n.value
+
+
+def kvq_sequence_reset(handle: int, layer: int, b: int):
+    _check(lib.kvq_sequence_reset(handle, layer, b), "kvq_sequence_reset")
+
+
+def kvq_page_span(handle: int, layer: int, page: int, kv_head: int):
+    off, n = _sz(0), _sz(0)
+    _check(lib.kvq_page_span(handle, layer, page, kv_head, ctypes.byref(off), ctypes.byref(n)), "kvq_page_span")
+    return off.value, n.value
+
+
 def kvq_strerror(status: int) -> str:
     return lib.kvq_strerror(status).decode()
 
@@ -294,3 +332,40 @@ class KVCache:
 
     def decode_bytes(self, layer):
         return kvq_decode_bytes(self.handle, layer)
+
+    # ---- paged caches (cfg.paged_pages > 0)
+    def _check_table(self, block_table):
+        check_tensors(self.device, [("block_table", block_table, torch.int32)])
+        shape = (self.cfg.batch, self.cfg.max_tokens // KVQ_BLOCK_TOKENS)
+        if tuple(block_table.shape) != shape:
+            raise ValueError(f"block_table must be {list(shape)}, got {tuple(block_table.shape)}")
+
+    def append_paged(self, layer, k, v, n_new, block_table, stream=None):
+        """k, v: fp16 [batch][n_kv_heads][max_new][128]; n_new: per-sequence counts (host)."""
+        check_tensors(self.device, [("k", k, torch.float16), ("v", v, torch.float16)])
+        self._check_table(block_table)
+        shape = (self.cfg.batch, self.cfg.n_kv_heads)
+        if k.dim() != 4 or tuple(k.shape[:2]) != shape or k.shape[3] != KVQ_HEAD_DIM or k.shape != v.shape:
+            raise ValueError(f"k and v must both be [{shape[0]}][{shape[1]}][max_new][{KVQ_HEAD_DIM}], got "
+                             f"{tuple(k.shape)} and {tuple(v.shape)}")
+        if len(n_new) != self.cfg.batch:
+            raise ValueError(f"n_new needs {self.cfg.batch} counts, got {len(n_new)}")
+        kvq_quantize_append_paged(self.handle, layer, k, v, n_new, k.shape[2], block_table, stream)
+
+    def decode_paged(self, layer, q, out, block_table, softmax_scale=0.0, stream=None):
+        check_tensors(self.device, [("q", q, torch.float16), ("out", out, torch.float32)])
+        self._check_table(block_table)
+        shape = (self.cfg.batch, self.cfg.n_q_heads, KVQ_HEAD_DIM)
+        if tuple(q.shape) != shape or tuple(out.shape) != shape:
+            raise ValueError(f"q and out must be {list(shape)}, got {tuple(q.shape)} and {tuple(out.shape)}")
+        kvq_decode_attn_paged(self.handle, layer, q, out, softmax_scale, block_table, stream)
+
+    def sequence_length(self, layer, b):
+        return kvq_sequence_length(self.handle, layer, b)
+
+    def sequence_reset(self, layer, b):
+        kvq_sequence_reset(self.handle, layer, b)
+
+    def page_bytes(self, layer, page, kv_head):
+        off, n = kvq_page_span(self.handle, layer, page, kv_head)
+        return self.buf[off:off + n]

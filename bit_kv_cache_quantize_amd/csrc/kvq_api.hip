@@ -32,6 +32,7 @@ kvq_status ok() { return KVQ_OK; }
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 static_assert(KVQ_MAX_SPLITS == kvq::kMaxSplits, "split limit");
+static_assert(KVQ_MAX_PAGED_BATCH == kvq::kMaxPagedBatch, "paged batch limit");
 
 // Smallest distance between consecutive NUQ codebook entries: with entries at least this far
 // apart, fp32 rounding of |u - C_j| (u, C_j in [-1, 1]) can never make an entry tie with or beat
@@ -151,7 +152,9 @@ struct kvq_cache_s {
   size_t off_rec = 0, layer_rec_bytes = 0;
   size_t off_tail = 0, layer_tail_bytes = 0;
   size_t off_cb = 0, off_lut = 0, off_rope_base = 0, off_rope_off = 0, off_work = 0;
-  std::vector<int32_t> len;
+  std::vector<int32_t> len;         // [layer]; paged caches: the largest sequence length
+  std::vector<int32_t> seq_len;     // paged caches: [layer][batch]
+  int pages = 0;                    // paged caches: pages per layer pool
   std::vector<uint8_t> cb_loaded;   // [layer][kv_head][2]
   std::vector<float> cb_host;       // [layer][kv_head][2][kCbStride]
   std::vector<float2> lut_host;     // [layer][kv_head][2][kNuqLutStride]
@@ -163,6 +166,38 @@ struct kvq_cache_s {
 };
 
 namespace {
+
+kvq_status check_codebooks(kvq_cache c, int layer) {
+  const kvq_config& cfg = c->cfg;
+  if (cfg.mode != KVQ_MODE_NUQ) return KVQ_OK;
+  for (int h = 0; h < cfg.n_kv_heads; ++h)
+    for (int w = 0; w < 2; ++w)
+      if (!c->cb_loaded[((size_t)layer * cfg.n_kv_heads + h) * 2 + w])
+        return fail(KVQ_ERR_STATE, "NUQ codebook of layer %d kv head %d (%s) not loaded", layer, h, w ? "V" : "K");
+  return KVQ_OK;
+}
+
+// Quantizer arguments shared by the unpaged and paged appends.
+kvq::QuantArgs quant_args(kvq_cache c, int layer, const void* k_f16, const void* v_f16, int n_rows) {
+  const kvq_config& cfg = c->cfg;
+  kvq::QuantArgs a{};
+  a.lay = c->lay;
+  a.k_out = cfg.outliers_per_vec;
+  a.varn_iters = cfg.varn_iters;
+  a.k_in = static_cast<const __half*>(k_f16);
+  a.v_in = static_cast<const __half*>(v_f16);
+  a.n_new = n_rows;
+  a.sink = c->sink;
+  a.ring_rows = c->ring_rows;
+  a.tail_rows = c->tail_rows;
+  a.Hkv = cfg.n_kv_heads;
+  a.max_blocks = c->max_blocks;
+  a.rec = c->base + c->off_rec + (size_t)layer * c->layer_rec_bytes;
+  a.tail = reinterpret_cast<__half*>(c->base + c->off_tail + (size_t)layer * c->layer_tail_bytes);
+  a.cb = reinterpret_cast<const float*>(c->base + c->off_cb) + (size_t)layer * cfg.n_kv_heads * 2 * kvq::kCbStride;
+  a.nuq_lut = reinterpret_cast<const float2*>(c->base + c->off_lut) + (size_t)layer * cfg.n_kv_heads * 2 * kvq::kNuqLutStride;
+  return a;
+}
 
 struct Regions {
   int max_blocks;
@@ -203,7 +238,18 @@ kvq_status validate_config(const kvq_config* c) {
   if (c->fp16_window < 0 || c->fp16_window > KVQ_MAX_WINDOW || c->fp16_window % KVQ_BLOCK_TOKENS != 0)
     return fail(KVQ_ERR_ARG, "fp16_window must be a multiple of 128 in 0..%d (got %d)", KVQ_MAX_WINDOW, c->fp16_window);
   const double rec = kvq::make_layout(c->mode, c->bits, c->outliers_per_vec).rec_bytes;
-  const double total = rec * c->n_layers * c->batch * c->n_kv_heads * (c->max_tokens / 128.0);
+  if (c->paged_pages < 0) return fail(KVQ_ERR_ARG, "paged_pages must be >= 0 (got %d)", c->paged_pages);
+  if (c->paged_pages > 0) {
+    if (c->batch > KVQ_MAX_PAGED_BATCH)
+      return fail(KVQ_ERR_ARG, "a paged cache holds at most %d sequences (got %d)", KVQ_MAX_PAGED_BATCH, c->batch);
+    if (c->sink_tokens != 0 || c->fp16_window != 0)
+      return fail(KVQ_ERR_ARG, "a paged cache keeps neither sink tokens nor an fp16 window");
+    if (rec * c->n_kv_heads * (double)c->paged_pages > (double)KVQ_MAX_POOL_BYTES)
+      return fail(KVQ_ERR_ARG, "page pool of %d pages exceeds %llu bytes per layer", c->paged_pages,
+                  (unsigned long long)KVQ_MAX_POOL_BYTES);
+  }
+  const double blocks = c->paged_pages > 0 ? (double)c->paged_pages : c->batch * (c->max_tokens / 128.0);
+  const double total = rec * c->n_layers * c->n_kv_heads * blocks;
   if (total > 4.0e12) return fail(KVQ_ERR_ARG, "cache larger than 4 TB requested");
   return KVQ_OK;
 }
@@ -216,7 +262,8 @@ Regions regions(const kvq_config* c) {
   const kvq::RecordLayout L = kvq::make_layout(c->mode, c->bits, c->outliers_per_vec);
   r.max_blocks = c->max_tokens / KVQ_BLOCK_TOKENS;
   const size_t units = (size_t)c->batch * c->n_kv_heads;
-  r.layer_rec = units * r.max_blocks * L.rec_bytes;
+  r.layer_rec = c->paged_pages > 0 ? (size_t)c->paged_pages * c->n_kv_heads * L.rec_bytes
+                                    : units * r.max_blocks * L.rec_bytes;
   r.rec = r.layer_rec * c->n_layers;
   r.layer_tail = units * 2 * (size_t)tail_rows_of(c) * kvq::kD * sizeof(__half);
   r.tail = r.layer_tail * c->n_layers;
@@ -284,8 +331,9 @@ kvq_status scratch_for_current_device(float** out) {
 
 // Decode over one layer with the split partials in `part` (nullptr: the cache's workspace).
 // part_limit: bytes available at `part` (checked against what this call's splits need).
+// table: the block table of a paged cache (nullptr for an unpaged one).
 kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, float softmax_scale,
-                       void* stream, float* part, size_t part_limit);
+                       void* stream, float* part, size_t part_limit, const int32_t* table);
 
 }  // namespace
 
@@ -330,6 +378,8 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_buf, size_t bytes, vo
   c->ring_rows = ring_rows_of(cfg);
   c->tail_rows = tail_rows_of(cfg);
   c->len.assign(cfg->n_layers, 0);
+  c->pages = cfg->paged_pages;
+  if (c->pages > 0) c->seq_len.assign((size_t)cfg->n_layers * cfg->batch, 0);
   c->cb_loaded.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2, 0);
   c->cb_host.assign((size_t)cfg->n_layers * cfg->n_kv_heads * 2 * kvq::kCbStride, 0.f);
   if (cfg->mode == KVQ_MODE_NUQ)
@@ -411,6 +461,7 @@ kvq_status kvq_quantize_append(kvq_cache c, int layer, const void* k_f16, const 
                                void* stream) {
   kvq_status st = check_layer(c, layer);
   if (st != KVQ_OK) return st;
+  if (c->pages > 0) return fail(KVQ_ERR_STATE, "the cache is paged: use kvq_quantize_append_paged");
   if (n_new < 0) return fail(KVQ_ERR_ARG, "n_new must be >= 0");
   if (n_new == 0) return ok();
   if (!k_f16 || !v_f16) return fail(KVQ_ERR_ARG, "k or v is NULL");
@@ -421,12 +472,8 @@ kvq_status kvq_quantize_append(kvq_cache c, int layer, const void* k_f16, const 
   if ((int64_t)len + n_new > cfg.max_tokens)
     return fail(KVQ_ERR_CAPACITY, "layer %d holds %d tokens; %d more exceed max_tokens %d", layer, len, n_new,
                 cfg.max_tokens);
-  if (cfg.mode == KVQ_MODE_NUQ) {
-    for (int h = 0; h < cfg.n_kv_heads; ++h)
-      for (int w = 0; w < 2; ++w)
-        if (!c->cb_loaded[((size_t)layer * cfg.n_kv_heads + h) * 2 + w])
-          return fail(KVQ_ERR_STATE, "NUQ codebook of layer %d kv head %d (%s) not loaded", layer, h, w ? "V" : "K");
-  }
+  st = check_codebooks(c, layer);
+  if (st != KVQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // positions < sink are sink tokens; body token u sits at position sink + u. Body block j
   // is quantized once the body holds at least 128 (j + 1) + window tokens.
@@ -439,25 +486,10 @@ kvq_status kvq_quantize_append(kvq_cache c, int layer, const void* k_f16, const 
   const int in_row0 = S - len;   // input row of body token u
   __half* tail = reinterpret_cast<__half*>(c->base + c->off_tail + (size_t)layer * c->layer_tail_bytes);
   if (nb > 0) {
-    kvq::QuantArgs a{};
-    a.lay = c->lay;
-    a.k_out = cfg.outliers_per_vec;
-    a.varn_iters = cfg.varn_iters;
-    a.k_in = static_cast<const __half*>(k_f16);
-    a.v_in = static_cast<const __half*>(v_f16);
-    a.n_new = n_new;
+    kvq::QuantArgs a = quant_args(c, layer, k_f16, v_f16, n_new);
     a.blk0 = nq_old;
     a.u_old = u_old;
     a.in_row0 = in_row0;
-    a.sink = S;
-    a.ring_rows = c->ring_rows;
-    a.tail_rows = c->tail_rows;
-    a.Hkv = cfg.n_kv_heads;
-    a.max_blocks = c->max_blocks;
-    a.rec = c->base + c->off_rec + (size_t)layer * c->layer_rec_bytes;
-    a.tail = tail;
-    a.cb = reinterpret_cast<const float*>(c->base + c->off_cb) + (size_t)layer * cfg.n_kv_heads * 2 * kvq::kCbStride;
-    a.nuq_lut = reinterpret_cast<const float2*>(c->base + c->off_lut) + (size_t)layer * cfg.n_kv_heads * 2 * kvq::kNuqLutStride;
     st = hip_check(kvq::launch_quantize(cfg.mode, cfg.bits, a, nb, cfg.batch, s), "launch quantize");
     if (st != KVQ_OK) return st;
   }
@@ -484,19 +516,91 @@ kvq_status kvq_quantize_append(kvq_cache c, int layer, const void* k_f16, const 
   return ok();
 }
 
+kvq_status kvq_quantize_append_paged(kvq_cache c, int layer, const void* k_f16, const void* v_f16,
+                                     const int32_t* n_new, int max_new, const int32_t* block_table,
+                                     void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (c->pages == 0) return fail(KVQ_ERR_STATE, "the cache is not paged: use kvq_quantize_append");
+  const kvq_config& cfg = c->cfg;
+  if (!n_new) return fail(KVQ_ERR_ARG, "n_new is NULL");
+  if (max_new < 0) return fail(KVQ_ERR_ARG, "max_new must be >= 0");
+  kvq::PagedSeq pg{};
+  int total = 0, most = 0, blocks = 0;
+  for (int b = 0; b < cfg.batch; ++b) {
+    const int n = n_new[b];
+    if (n < 0 || n > max_new) return fail(KVQ_ERR_ARG, "n_new[%d] = %d not in 0..%d", b, n, max_new);
+    const int len = c->seq_len[(size_t)layer * cfg.batch + b];
+    if ((int64_t)len + n > cfg.max_tokens)
+      return fail(KVQ_ERR_CAPACITY, "sequence %d of layer %d holds %d tokens; %d more exceed max_tokens %d", b, layer,
+                  len, n, cfg.max_tokens);
+    pg.len[b] = len;
+    pg.n_new[b] = n;
+    total += n;
+    most = std::max(most, len + n);
+    blocks = std::max(blocks, (len + n) / KVQ_BLOCK_TOKENS - len / KVQ_BLOCK_TOKENS);
+  }
+  if (total == 0) return ok();
+  if (!k_f16 || !v_f16) return fail(KVQ_ERR_ARG, "k or v is NULL");
+  if (reinterpret_cast<uintptr_t>(k_f16) % 16 || reinterpret_cast<uintptr_t>(v_f16) % 16)
+    return fail(KVQ_ERR_ARG, "k and v must be 16-byte aligned");
+  if (blocks > 0 && !block_table) return fail(KVQ_ERR_ARG, "block_table is NULL");
+  if (reinterpret_cast<uintptr_t>(block_table) % 4) return fail(KVQ_ERR_ARG, "block_table must be 4-byte aligned");
+  st = check_codebooks(c, layer);
+  if (st != KVQ_OK) return st;
+  pg.table = block_table;
+  pg.table_stride = c->max_blocks;
+  pg.n_pages = c->pages;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the blocks each sequence completes, read partly from its fp16 tail (before the tail
+  // copy below overwrites it), then the new tokens of each sequence's open block
+  if (blocks > 0) {
+    kvq::QuantArgs a = quant_args(c, layer, k_f16, v_f16, max_new);
+    a.pg = pg;
+    st = hip_check(kvq::launch_quantize(cfg.mode, cfg.bits, a, blocks, cfg.batch, s), "launch quantize");
+    if (st != KVQ_OK) return st;
+  }
+  kvq::TailArgs ta{};
+  ta.k_in = static_cast<const __half*>(k_f16);
+  ta.v_in = static_cast<const __half*>(v_f16);
+  ta.n_new = max_new;
+  ta.Hkv = cfg.n_kv_heads;
+  ta.tail = reinterpret_cast<__half*>(c->base + c->off_tail + (size_t)layer * c->layer_tail_bytes);
+  ta.sink = 0;
+  ta.ring_rows = c->ring_rows;
+  ta.tail_rows = c->tail_rows;
+  ta.pg = pg;
+  st = hip_check(kvq::launch_tail(ta, cfg.batch, s), "launch tail copy");
+  if (st != KVQ_OK) return st;
+  for (int b = 0; b < cfg.batch; ++b) c->seq_len[(size_t)layer * cfg.batch + b] += n_new[b];
+  c->len[layer] = most;
+  return ok();
+}
+
 kvq_status kvq_decode_attn(kvq_cache c, int layer, const void* q_f16, float* out, float softmax_scale,
                            void* stream) {
-  return decode_impl(c, layer, q_f16, out, softmax_scale, stream, nullptr, 0);
+  return decode_impl(c, layer, q_f16, out, softmax_scale, stream, nullptr, 0, nullptr);
+}
+
+kvq_status kvq_decode_attn_paged(kvq_cache c, int layer, const void* q_f16, float* out, float softmax_scale,
+                                 const int32_t* block_table, void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (c->pages == 0) return fail(KVQ_ERR_STATE, "the cache is not paged: use kvq_decode_attn");
+  if (!block_table) return fail(KVQ_ERR_ARG, "block_table is NULL");
+  if (reinterpret_cast<uintptr_t>(block_table) % 4) return fail(KVQ_ERR_ARG, "block_table must be 4-byte aligned");
+  return decode_impl(c, layer, q_f16, out, softmax_scale, stream, nullptr, 0, block_table);
 }
 
 kvq_status kvq_decode_attn_static(kvq_cache c, int layer, const void* q_f16, float* out, float softmax_scale,
                                   void* stream) {
   kvq_status st = check_layer(c, layer);
   if (st != KVQ_OK) return st;
+  if (c->pages > 0) return fail(KVQ_ERR_STATE, "the cache is paged: use kvq_decode_attn_paged");
   float* part = nullptr;
   st = scratch_for_current_device(&part);
   if (st != KVQ_OK) return st;
-  return decode_impl(c, layer, q_f16, out, softmax_scale, stream, part, kScratchBytes);
+  return decode_impl(c, layer, q_f16, out, softmax_scale, stream, part, kScratchBytes, nullptr);
 }
 
 }  // extern "C"
@@ -504,9 +608,10 @@ kvq_status kvq_decode_attn_static(kvq_cache c, int layer, const void* q_f16, flo
 namespace {
 
 kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, float softmax_scale,
-                       void* stream, float* part, size_t part_limit) {
+                       void* stream, float* part, size_t part_limit, const int32_t* table) {
   kvq_status st = check_layer(c, layer);
   if (st != KVQ_OK) return st;
+  if (c->pages > 0 && !table) return fail(KVQ_ERR_STATE, "the cache is paged: use kvq_decode_attn_paged");
   if (!q_f16 || !out) return fail(KVQ_ERR_ARG, "q or out is NULL");
   if (reinterpret_cast<uintptr_t>(q_f16) % 4 || reinterpret_cast<uintptr_t>(out) % 4)
     return fail(KVQ_ERR_ARG, "q and out must be 4-byte aligned");
@@ -514,7 +619,18 @@ kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, fl
   const kvq_config& cfg = c->cfg;
   const int L = c->len[layer];
   if (L == 0) return fail(KVQ_ERR_STATE, "layer %d holds no tokens", layer);
-  // quantized blocks and fp16 tokens (see kvq_quantize_append)
+  kvq::PagedSeq pg{};
+  if (table) {
+    pg.table = table;
+    pg.table_stride = c->max_blocks;
+    pg.n_pages = c->pages;
+    for (int b = 0; b < cfg.batch; ++b) {
+      pg.len[b] = c->seq_len[(size_t)layer * cfg.batch + b];
+      if (pg.len[b] == 0) return fail(KVQ_ERR_STATE, "sequence %d of layer %d holds no tokens", b, layer);
+    }
+  }
+  // quantized blocks and fp16 tokens (see kvq_quantize_append); paged caches: the longest
+  // sequence's blocks set the split plan, each sequence stops at its own length
   const int U = std::max(0, L - c->sink);
   const int nblk = std::max(0, U - c->window) / KVQ_BLOCK_TOKENS;
   const int fp16_body = U - nblk * KVQ_BLOCK_TOKENS;
@@ -574,6 +690,7 @@ kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, fl
   a.ring_rows = c->ring_rows;
   a.tail_rows = c->tail_rows;
   a.side_slot = nblk > 0 ? splits : -1;
+  a.pg = pg;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
   a.scale_log2 = scale * 1.4426950408889634f;
   if (cfg.outliers_per_vec > 0) {
@@ -614,6 +731,7 @@ kvq_status kvq_error_decomposition(kvq_cache c, int layer, int block0, int n_blo
   if (reinterpret_cast<uintptr_t>(k_f16) % 16 || reinterpret_cast<uintptr_t>(v_f16) % 16 ||
       reinterpret_cast<uintptr_t>(out) % 8)
     return fail(KVQ_ERR_ARG, "k and v must be 16-byte aligned, out 8-byte aligned");
+  if (c->pages > 0) return fail(KVQ_ERR_STATE, "the error diagnostic reads unpaged caches only");
   const int U = std::max(0, c->len[layer] - c->sink);
   const int nq = std::max(0, U - c->window) / KVQ_BLOCK_TOKENS;   // quantized blocks
   if (n_blocks <= 0 || block0 < 0 || block0 + n_blocks > nq)
@@ -714,6 +832,40 @@ kvq_status kvq_cache_reset(kvq_cache c, int layer) {
   const kvq_status st = check_layer(c, layer);
   if (st != KVQ_OK) return st;
   c->len[layer] = 0;
+  if (c->pages > 0)
+    std::fill(c->seq_len.begin() + (size_t)layer * c->cfg.batch, c->seq_len.begin() + (size_t)(layer + 1) * c->cfg.batch, 0);
+  return ok();
+}
+
+kvq_status kvq_sequence_length(kvq_cache c, int layer, int b, int32_t* n_tokens) {
+  const kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (b < 0 || b >= c->cfg.batch) return fail(KVQ_ERR_ARG, "sequence %d out of range [0, %d)", b, c->cfg.batch);
+  if (!n_tokens) return fail(KVQ_ERR_ARG, "n_tokens is NULL");
+  *n_tokens = c->pages > 0 ? c->seq_len[(size_t)layer * c->cfg.batch + b] : c->len[layer];
+  return ok();
+}
+
+kvq_status kvq_sequence_reset(kvq_cache c, int layer, int b) {
+  const kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (b < 0 || b >= c->cfg.batch) return fail(KVQ_ERR_ARG, "sequence %d out of range [0, %d)", b, c->cfg.batch);
+  if (c->pages == 0) return fail(KVQ_ERR_STATE, "the sequences of an unpaged cache keep equal lengths");
+  int32_t* l = c->seq_len.data() + (size_t)layer * c->cfg.batch;
+  l[b] = 0;
+  c->len[layer] = *std::max_element(l, l + c->cfg.batch);
+  return ok();
+}
+
+kvq_status kvq_page_span(kvq_cache c, int layer, int page, int kv_head, size_t* offset, size_t* bytes) {
+  const kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (c->pages == 0) return fail(KVQ_ERR_STATE, "the cache is not paged: use kvq_block_span");
+  if (page < 0 || page >= c->pages || kv_head < 0 || kv_head >= c->cfg.n_kv_heads)
+    return fail(KVQ_ERR_ARG, "page coordinates out of range");
+  if (!offset || !bytes) return fail(KVQ_ERR_ARG, "offset or bytes is NULL");
+  *offset = c->off_rec + (size_t)layer * c->layer_rec_bytes + ((size_t)page * c->cfg.n_kv_heads + kv_head) * c->lay.rec_bytes;
+  *bytes = c->lay.rec_bytes;
   return ok();
 }
 
@@ -727,6 +879,7 @@ kvq_status kvq_set_decode_splits(kvq_cache c, int splits) {
 kvq_status kvq_block_span(kvq_cache c, int layer, int b, int kv_head, int block, size_t* offset, size_t* bytes) {
   const kvq_status st = check_layer(c, layer);
   if (st != KVQ_OK) return st;
+  if (c->pages > 0) return fail(KVQ_ERR_STATE, "the cache is paged: use kvq_page_span");
   if (b < 0 || b >= c->cfg.batch || kv_head < 0 || kv_head >= c->cfg.n_kv_heads || block < 0 ||
       block >= c->max_blocks)
     return fail(KVQ_ERR_ARG, "block coordinates out of range");
@@ -759,7 +912,16 @@ kvq_status kvq_decode_bytes(kvq_cache c, int layer, size_t* bytes) {
   const int U = std::max(0, L - c->sink);
   const size_t nblk = std::max(0, U - c->window) / KVQ_BLOCK_TOKENS;
   const size_t tail_n = (size_t)(U - (int)nblk * KVQ_BLOCK_TOKENS) + (size_t)std::min(L, c->sink);   // fp16 tokens
-  size_t n = units * (nblk * c->lay.payload + tail_n * 2 * KVQ_HEAD_DIM * sizeof(__half));
+  size_t n = 0;
+  if (c->pages > 0) {   // each sequence its own blocks (and their block-table entries) and tail
+    for (int b = 0; b < cfg.batch; ++b) {
+      const size_t lb = (size_t)c->seq_len[(size_t)layer * cfg.batch + b];
+      n += cfg.n_kv_heads * ((lb / 128) * c->lay.payload + (lb % 128) * 2 * KVQ_HEAD_DIM * sizeof(__half)) +
+           (lb / 128) * sizeof(int32_t);
+    }
+  } else {
+    n = units * (nblk * c->lay.payload + tail_n * 2 * KVQ_HEAD_DIM * sizeof(__half));
+  }
   n += (size_t)cfg.batch * cfg.n_q_heads * KVQ_HEAD_DIM * (sizeof(__half) + sizeof(float));
   if (cfg.mode == KVQ_MODE_NUQ) n += (size_t)cfg.n_kv_heads * 2 * (1u << cfg.bits) * sizeof(float);
   if (cfg.pre_rope)

@@ -63,9 +63,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 
   const int blo = split * a.blocks_per_split;
-  const int bhi = min(a.nblk, blo + a.blocks_per_split);
+  const int bhi = min(seq_nblk(a, blockIdx.z), blo + a.blocks_per_split);
   d.run(blo, bhi, rc, rs);
-  if (split == a.splits - 1 && 64 * d.par < a.tail_n && w < 2) d.tail_half(rc, rs);
+  if (split == a.splits - 1 && 64 * d.par < seq_tail(a, blockIdx.z) && w < 2) d.tail_half(rc, rs);
 
   // ---- merge the four wave states
 #pragma unroll

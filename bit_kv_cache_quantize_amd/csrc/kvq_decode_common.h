@@ -185,7 +185,7 @@ struct Decoder {
   }
 
   __device__ __forceinline__ const uint8_t* record(int blk) const {
-    return a.rec + ((size_t)(blockIdx.z * a.Hkv + blockIdx.y) * a.max_blocks + blk) * (size_t)a.lay.rec_bytes;
+    return a.rec + record_offset(a, blockIdx.z, blockIdx.y, blk);
   }
 
   __device__ __forceinline__ float kval(uint32_t code) const {
@@ -481,7 +481,7 @@ struct Decoder {
 
   // Tokens 64*par .. 64*par+63 of the fp16 tail (n_valid of them), position 128*nblk + j.
   __device__ __forceinline__ void tail_half(const float (&rc)[64], const float (&rs)[64]) {
-    const int n_valid = min(64, a.tail_n - 64 * par);
+    const int n_valid = min(64, seq_tail(a, blockIdx.z) - 64 * par);
     const __half* tk = a.tail + (size_t)(blockIdx.z * a.Hkv + blockIdx.y) * (2 * kT * kD);
     const __half* tv = tk + kT * kD;
     const bool valid = lane < n_valid;
@@ -504,7 +504,7 @@ struct Decoder {
         }
       }
     } else {
-      const float2 cs0 = reinterpret_cast<const float2*>(a.rope_base)[(size_t)a.nblk * 64 + lane];
+      const float2 cs0 = reinterpret_cast<const float2*>(a.rope_base)[(size_t)seq_nblk(a, blockIdx.z) * 64 + lane];
       float AL[G], BE[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {

@@ -196,8 +196,17 @@ struct MfmaDecoder {
   // The codes are read once: non-temporal loads (cache-policy bit "nt"); the statistics,
   // read by both waves of a block, keep the default policy.
   static constexpr int kNT = 2;
+  // Paged caches: the resource spans the layer's page pool, a block's offset comes from the
+  // block table, and a block past the split's end gets the pool's size (reads nothing).
+  int blo_ = 0, nb_ = 0;
+  uint32_t pool_bytes_ = 0;
+  __device__ __forceinline__ uint32_t block_off(int rel) const {
+    if (a.pg.table)
+      return rel < nb_ ? (uint32_t)record_offset(a, blockIdx.z, blockIdx.y, blo_ + rel) : pool_bytes_;
+    return (uint32_t)rel * a.lay.rec_bytes;
+  }
   __device__ __forceinline__ void fetch(Buf& B, int rel) const {   // rel: block index in the split
-    const uint32_t boff = (uint32_t)rel * a.lay.rec_bytes;
+    const uint32_t boff = block_off(rel);
     constexpr int soff = 0;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -445,13 +454,19 @@ struct MfmaDecoder {
   }
 
   __device__ __forceinline__ void run(int blo, int bhi) {
-    const uint8_t* base =
-        a.rec + ((size_t)(blockIdx.z * a.Hkv + blockIdx.y) * a.max_blocks + blo) * (size_t)a.lay.rec_bytes;
-    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
-                                           (int)((bhi - blo) * a.lay.rec_bytes), 0x00020000);
+    blo_ = blo;
+    nb_ = max(bhi - blo, 0);
+    if (a.pg.table) {
+      pool_bytes_ = (uint32_t)a.pg.n_pages * (uint32_t)a.Hkv * a.lay.rec_bytes;
+      rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.rec), (short)0, (int)pool_bytes_, 0x00020000);
+    } else {
+      const uint8_t* base = a.rec + record_offset(a, blockIdx.z, blockIdx.y, blo);
+      rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)(nb_ * a.lay.rec_bytes),
+                                             0x00020000);
+    }
     Buf A, Bb;
     int rel = w >> 1;                  // this wave's blocks: rel, rel + 2, ... (relative to blo)
-    const int nb = bhi - blo;
+    const int nb = nb_;
     if (rel >= nb) return;
     fetch(A, rel);
     // the next block is fetched unconditionally (past the end it reads nothing), so the wait
@@ -477,7 +492,7 @@ struct MfmaDecoder {
 template <int MODE, int G>
 __device__ __forceinline__ void tail_half_lds(const DecodeArgs& a, int w, int lane, bool active, const float* qs,
                                               float* pbuf, float* m_out, float* l_out, float* o_out) {
-  const int n_valid = active ? min(64, a.tail_n - 64 * w) : 0;
+  const int n_valid = active ? min(64, seq_tail(a, blockIdx.z) - 64 * w) : 0;
   const __half* tk = a.tail + (size_t)(blockIdx.z * a.Hkv + blockIdx.y) * (2 * kT * kD);
   const __half* tv = tk + kT * kD;
   float sc[G];
@@ -576,7 +591,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   MfmaDecoder<MODE, BITS, G> d(a, lane, w, s_qr, s_meta[w]);
   const int blo = split * a.blocks_per_split;
-  const int bhi = min(a.nblk, blo + a.blocks_per_split);
+  const int bhi = min(seq_nblk(a, b), blo + a.blocks_per_split);
   d.run(blo, bhi);
 
   // ---- this wave's matrix-core state
@@ -606,7 +621,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   // ---- the fp16 tail (waves 0 and 1; it belongs to the last split)
   if (w < 2) {
-    const bool active = split == a.splits - 1 && 64 * w < a.tail_n;
+    const bool active = split == a.splits - 1 && 64 * w < seq_tail(a, b);
     tail_half_lds<MODE, G>(a, w, lane, active, s_q, reinterpret_cast<float*>(s_meta[w]), s_m[4 + w], s_l[4 + w],
                            s_o[4 + w]);
   }

@@ -133,7 +133,7 @@ struct TabDecoder {
   __device__ __forceinline__ int ch1() const { return MV ? 64 + lane : 2 * lane + 1; }
 
   __device__ __forceinline__ const uint8_t* record(int blk) const {
-    return a.rec + ((size_t)(blockIdx.z * a.Hkv + blockIdx.y) * a.max_blocks + blk) * (size_t)a.lay.rec_bytes;
+    return a.rec + record_offset(a, blockIdx.z, blockIdx.y, blk);
   }
 
   // Record loads go through a buffer resource over this split's records (blocks blo ..
@@ -141,14 +141,27 @@ struct TabDecoder {
   // after the split's last into zeros that touch no memory. Every load of the next block is
   // therefore issued unconditionally: a load under a branch makes the memory-counter waits
   // after the join drain every load in flight.
+  // Paged caches: the resource spans the layer's page pool and each block's offset comes
+  // from the block table; a block past the split's end gets the pool's size as offset.
   __amdgpu_buffer_rsrc_t rsb;
-  int blo_;
+  int blo_, bhi_;
+  uint32_t pool_bytes_;
   __device__ __forceinline__ void bind(int blo, int bhi) {
-    rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(record(blo)), (short)0,
-                                            (int)(max(bhi - blo, 0) * a.lay.rec_bytes), 0x00020000);
     blo_ = blo;
+    bhi_ = bhi;
+    if (a.pg.table) {
+      pool_bytes_ = (uint32_t)a.pg.n_pages * (uint32_t)a.Hkv * a.lay.rec_bytes;
+      rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.rec), (short)0, (int)pool_bytes_, 0x00020000);
+    } else {
+      rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(record(blo)), (short)0,
+                                              (int)(max(bhi - blo, 0) * a.lay.rec_bytes), 0x00020000);
+    }
   }
-  __device__ __forceinline__ uint32_t boff(int blk) const { return (uint32_t)(blk - blo_) * a.lay.rec_bytes; }
+  __device__ __forceinline__ uint32_t boff(int blk) const {
+    if (a.pg.table)
+      return blk < bhi_ ? (uint32_t)record_offset(a, blockIdx.z, blockIdx.y, blk) : pool_bytes_;
+    return (uint32_t)(blk - blo_) * a.lay.rec_bytes;
+  }
   static constexpr int kNT = 2;   // cache policy "nt": the code rows are read once
 
   template <int NBYTES>
@@ -486,7 +499,7 @@ struct TabDecoder {
   // Runs once per (sequence, kv head): the per-offset angles come from the table in memory
   // (the main loop's registers for them are dead here).
   __device__ __forceinline__ void tail_half(const float2* qt) {
-    const int n_valid = min(64, a.tail_n - 64 * par);
+    const int n_valid = min(64, seq_tail(a, blockIdx.z) - 64 * par);
     const __half* tk = a.tail + (size_t)(blockIdx.z * a.Hkv + blockIdx.y) * (2 * kT * kD);
     const __half* tv = tk + kT * kD;
     const bool valid = lane < n_valid;
@@ -608,7 +621,7 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   const int blo = split * a.blocks_per_split;
-  const int bhi = min(a.nblk, blo + a.blocks_per_split);
+  const int bhi = min(seq_nblk(a, b), blo + a.blocks_per_split);
   d.bind(blo, bhi);
   typename Dec::Meta Mt;
   typename Dec::Keys Kc;
@@ -635,16 +648,16 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   }
 
   // ---- the fp16 tail (it belongs to the last split)
-  if (split == a.splits - 1 && a.tail_n > 0) {
+  if (split == a.splits - 1 && seq_tail(a, b) > 0) {
     float2* qt = s_qb;
     if (tid < 64) {
       // query rotated back by the tail block's base angle
-      const float2 rb = reinterpret_cast<const float2*>(a.rope_base)[(size_t)a.nblk * 64 + tid];
+      const float2 rb = reinterpret_cast<const float2*>(a.rope_base)[(size_t)seq_nblk(a, b) * 64 + tid];
       const float qx = s_q[2 * tid], qy = s_q[2 * tid + 1];
       qt[tid] = make_float2(fmaf(qx, rb.x, qy * rb.y), fmaf(qy, rb.x, -qx * rb.y));
     }
     __syncthreads();
-    if (64 * d.par < a.tail_n) d.tail_half(qt);
+    if (64 * d.par < seq_tail(a, b)) d.tail_half(qt);
   }
 
   // ---- merge the two wave states

@@ -35,6 +35,24 @@ struct RecordLayout {
 
 RecordLayout make_layout(int mode, int bits, int k_out);
 
+// Paged caches: each layer's records live in a pool of pages, page p holding one 128-token
+// block of every kv head ([n_pages][Hkv] records); a caller-owned device table maps block j
+// of sequence b to its page. Sequences hold their own token counts (ragged batches).
+constexpr int kMaxPagedBatch = 64;
+struct PagedSeq {
+  const int32_t* table;       // [batch][table_stride] page of each block (device), or null
+  int table_stride, n_pages;
+  int len[kMaxPagedBatch];    // tokens of each sequence before this call (append) / held (decode)
+  int n_new[kMaxPagedBatch];  // tokens this call appends to each sequence (append)
+};
+
+// Page of block blk of sequence b, clamped into the pool: a bad table entry gives wrong
+// results, never an access outside the pool.
+__device__ __forceinline__ int page_of(const PagedSeq& p, int b, int blk) {
+  const int v = p.table[(size_t)b * p.table_stride + blk];
+  return v < 0 ? 0 : (v >= p.n_pages ? p.n_pages - 1 : v);
+}
+
 // fp16 rows of one (layer, sequence, kv head): K [tail_rows][128] then V [tail_rows][128];
 // rows 0 .. sink-1 hold the attention-sink tokens, row sink + (u mod ring_rows) holds body
 // token u (the tokens after the sink, numbered from 0) while it is not quantized.
@@ -48,10 +66,11 @@ struct QuantArgs {
   int in_row0;           // input row of body token u (u >= u_old) is u + in_row0
   int sink, ring_rows, tail_rows;
   int Hkv, max_blocks;
-  uint8_t* rec;          // records of the layer, [B][Hkv][max_blocks]
+  uint8_t* rec;          // records of the layer, [B][Hkv][max_blocks] (paged: the page pool)
   const __half* tail;    // fp16 rows of the layer, [B][Hkv][2][tail_rows][128]
   const float* cb;       // codebooks of the layer, [Hkv][2][kCbStride]
   const float2* nuq_lut; // NUQ code tables of the layer, [Hkv][2][kNuqLutStride] (NUQ only)
+  PagedSeq pg;           // paged caches: blk0, u_old and in_row0 follow from pg.len[b]
 };
 
 // Staging of new fp16 rows: input rows [0, n_sink) to tail rows sink_row0 + i (sink
@@ -64,6 +83,7 @@ struct TailArgs {
   int ring_src0, ring_count, ring_u0;
   int sink, ring_rows, tail_rows;
   __half* tail;
+  PagedSeq pg;           // paged caches: the ranges follow from pg.len[b] and pg.n_new[b]
 };
 
 struct DecodeArgs {
@@ -85,7 +105,17 @@ struct DecodeArgs {
   // fp16 part outside the blocks (sink tokens and the body tokens not yet quantized),
   // decoded by its own kernel when a sink or a window is configured (tail_n is then 0)
   int sink_n, fp16_u0, fp16_n, ring_rows, tail_rows, side_slot;
+  PagedSeq pg;              // paged caches: per-sequence lengths and the block table
 };
+
+// Full blocks and fp16 tail tokens of sequence b.
+__device__ __forceinline__ int seq_nblk(const DecodeArgs& a, int b) { return a.pg.table ? a.pg.len[b] >> 7 : a.nblk; }
+__device__ __forceinline__ int seq_tail(const DecodeArgs& a, int b) { return a.pg.table ? a.pg.len[b] & 127 : a.tail_n; }
+// Byte offset of the record of block blk of (sequence b, kv head h) from a.rec.
+__device__ __forceinline__ size_t record_offset(const DecodeArgs& a, int b, int h, int blk) {
+  if (a.pg.table) return ((size_t)page_of(a.pg, b, blk) * a.Hkv + h) * a.lay.rec_bytes;
+  return (((size_t)b * a.Hkv + h) * a.max_blocks + blk) * a.lay.rec_bytes;
+}
 
 // Error diagnostic over quantized blocks block0 .. block0 + n_blocks - 1 of every (sequence,
 // kv head): inputs [B][Hkv][n_blocks * 128][128] fp16, out [B][Hkv][n_blocks * 128][4] fp64.

@@ -494,7 +494,13 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
   const int tid = threadIdx.x, lane = tid & 63, r = lane >> 4, g = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t unit = (size_t)b * a.Hkv + h;
-  uint8_t* rec = a.rec + (unit * a.max_blocks + (size_t)(a.blk0 + j)) * a.lay.rec_bytes;
+  // paged caches: the sequence's own length places the block and its input rows
+  const int len_b = a.pg.table ? a.pg.len[b] : 0;
+  const int blk0 = a.pg.table ? len_b >> 7 : a.blk0;
+  const int u_old = a.pg.table ? len_b : a.u_old;
+  const int in_row0 = a.pg.table ? -len_b : a.in_row0;
+  uint8_t* rec = a.rec + (a.pg.table ? ((size_t)page_of(a.pg, b, blk0 + j) * a.Hkv + h)
+                                     : (unit * a.max_blocks + (size_t)(blk0 + j))) * a.lay.rec_bytes;
   constexpr int R = 16 * BITS;                                  // bytes per 128 codes
   const int k_out = KO == 0 ? 0 : (KO == 1 ? 1 : a.k_out);
   constexpr bool per_chan = TENSOR == 0 || MODE == SYM || MODE == ASYM;   // vector = a channel over the block's tokens
@@ -508,13 +514,13 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
   {
     const __half* in = (tensor ? a.v_in : a.k_in) + unit * (size_t)a.n_new * kD;
     const __half* tl = a.tail + unit * (size_t)(2 * a.tail_rows * kD) + (size_t)tensor * a.tail_rows * kD;
-    const int u0 = (a.blk0 + j) * kT;   // body token of the block's first row
+    const int u0 = (blk0 + j) * kT;   // body token of the block's first row
     uint4 raw[8];
-    if (u0 >= a.u_old) {
+    if (u0 >= u_old) {
       // (uniform) every row from the new input: a buffer resource over the block's 128 rows,
       // the lane's offset in a register and each row's offset in the scalar offset operand
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<__half*>(in + ((size_t)u0 + a.in_row0) * kD), (short)0, kT * kD * 2, 0x00020000);
+          const_cast<__half*>(in + ((size_t)u0 + in_row0) * kD), (short)0, kT * kD * 2, 0x00020000);
       const uint32_t lo = (uint32_t)(((32 * w + r) * kD + 8 * g) * 2);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -525,8 +531,8 @@ __device__ __forceinline__ void quantize_tensor(const QuantArgs& a, Smem& sm, in
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int u = u0 + 32 * w + 4 * i + r;
-        const __half* src = u < a.u_old ? tl + (size_t)(a.sink + u % a.ring_rows) * kD
-                                        : in + ((size_t)u + a.in_row0) * kD;
+        const __half* src = u < u_old ? tl + (size_t)(a.sink + u % a.ring_rows) * kD
+                                      : in + ((size_t)u + in_row0) * kD;
         raw[i] = *reinterpret_cast<const uint4*>(src + 8 * g);
       }
     }
@@ -979,6 +985,8 @@ template <int MODE, int BITS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MODE == KVARN ? 2 : 4))) void quantize_kernel(QuantArgs a) {
   __shared__ Smem sm;
   const int j = blockIdx.x >> 1, h = blockIdx.y, b = blockIdx.z;
+  // paged caches: the grid covers the largest number of blocks any sequence completes
+  if (a.pg.table && j >= ((a.pg.len[b] + a.pg.n_new[b]) >> 7) - (a.pg.len[b] >> 7)) return;
   if (MODE == KVARN || a.k_out == 0) {
     if (blockIdx.x & 1) run_tensor<MODE, BITS, 1, 0>(a, sm, j, h, b);
     else run_tensor<MODE, BITS, 0, 0>(a, sm, j, h, b);
@@ -998,19 +1006,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MODE =
 __global__ __launch_bounds__(kThreads) void tail_kernel(TailArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t unit = (size_t)b * a.Hkv + h;
-  const int n_rows = a.n_sink + a.ring_count;
+  int n_sink = a.n_sink, ring_src0 = a.ring_src0, ring_count = a.ring_count, ring_u0 = a.ring_u0;
+  if (a.pg.table) {   // paged: the new tokens after the sequence's last complete block
+    const int len = a.pg.len[b], end = len + a.pg.n_new[b];
+    n_sink = 0;
+    ring_u0 = max(len, end & ~(kT - 1));
+    ring_count = end - ring_u0;
+    ring_src0 = ring_u0 - len;
+  }
+  const int n_rows = n_sink + ring_count;
   for (int tensor = 0; tensor < 2; ++tensor) {
     const __half* in = (tensor ? a.v_in : a.k_in) + unit * (size_t)a.n_new * kD;
     __half* tl = a.tail + unit * (size_t)(2 * a.tail_rows * kD) + (size_t)tensor * a.tail_rows * kD;
     for (int id = threadIdx.x; id < n_rows * 16; id += kThreads) {
       const int i = id >> 4, ch = (id & 15) * 8;
       int src, dst;
-      if (i < a.n_sink) {
+      if (i < n_sink) {
         src = i;
         dst = a.sink_row0 + i;
       } else {
-        src = a.ring_src0 + (i - a.n_sink);
-        dst = a.sink + (a.ring_u0 + (i - a.n_sink)) % a.ring_rows;
+        src = ring_src0 + (i - n_sink);
+        dst = a.sink + (ring_u0 + (i - n_sink)) % a.ring_rows;
       }
       *reinterpret_cast<uint4*>(tl + (size_t)dst * kD + ch) = *reinterpret_cast<const uint4*>(in + (size_t)src * kD + ch);
     }

@@ -67,10 +67,13 @@ typedef enum {
 #define KVQ_STATIC_SCRATCH_BYTES (8u << 20)
 #define KVQ_MAX_SINK 128
 #define KVQ_MAX_WINDOW 8192
+#define KVQ_MAX_PAGED_BATCH 64
+#define KVQ_MAX_POOL_BYTES (4294967296ull - 131072ull)
 
 typedef struct {
   int32_t n_layers;         /* >= 1 */
-  int32_t batch;            /* >= 1; every sequence holds the same number of tokens */
+  int32_t batch;            /* >= 1; every sequence holds the same number of tokens, except in
+                               a paged cache (paged_pages > 0), where each has its own */
   int32_t n_kv_heads;       /* >= 1 */
   int32_t n_q_heads;        /* multiple of n_kv_heads, group n_q_heads/n_kv_heads in {1,2,4,8} */
   int32_t head_dim;         /* must be 128 */
@@ -88,6 +91,13 @@ typedef struct {
   int32_t fp16_window;      /* 0..KVQ_MAX_WINDOW, a multiple of 128: a block is quantized only
                                once this many newer tokens follow it (KVQuant notes 4.2:
                                KIVI's full-precision window of recent tokens) */
+  int32_t paged_pages;      /* 0: each (layer, sequence, kv head) owns max_tokens / 128 block
+                               records in place. > 0: a paged cache. Each layer keeps a pool of
+                               this many pages, a page being one 128-token block of one sequence
+                               (its n_kv_heads records), and a caller-owned block table maps the
+                               blocks of every sequence to pages; sequences hold ragged lengths.
+                               Requires batch <= KVQ_MAX_PAGED_BATCH, sink_tokens = fp16_window
+                               = 0, and a pool of at most KVQ_MAX_POOL_BYTES per layer. */
 } kvq_config;
 
 typedef struct kvq_cache_s* kvq_cache;   /* opaque host handle; owns no device memory */
@@ -166,7 +176,8 @@ kvq_status kvq_decode_attn(kvq_cache cache, int layer, const void* q_f16, float*
  * that copy, whatever the handle: calls that overlap on one GPU (different streams or
  * threads) race; serialize them. Every partial is written before it is read, so the
  * array's previous contents never matter.
- * Errors: those of kvq_decode_attn, and KVQ_ERR_SIZE (nothing launched) when the call's
+ * Errors: those of kvq_decode_attn (KVQ_ERR_STATE for a paged cache, before any device
+ * call), and KVQ_ERR_SIZE (nothing launched) when the call's
  * split partials, splits x batch x n_q_heads x 520 bytes, exceed the array; lower the
  * split count with kvq_set_decode_splits. KVQ_ERR_HIP if the array's device address
  * cannot be obtained.
@@ -214,10 +225,63 @@ kvq_status kvq_codebook_build(const float* act, const float* weight, int64_t n, 
                               void* workspace, size_t workspace_bytes, float* codebook, int32_t* iters,
                               void* stream);
 
-/* Tokens currently held by a layer (host-side counter, no device access). */
+/*
+ * Paged caches (paged_pages > 0; KVQuant notes 7.2 (b-3) and 7.3 item 5: the packed cache
+ * and its outliers in a paged memory pool for serving with requests of different lengths;
+ * TurboQuant blog 4.1: the block allocator and index table of a paged KV cache).
+ * Ragged batches: sequence b of the batch holds its own number of tokens n_b.
+ * Records of a layer live in a pool of paged_pages pages; page p holds one block of
+ * one sequence: the records of kv heads 0 .. n_kv_heads-1 back to back (kvq_page_span).
+ * block_table: dev, int32 [batch][max_tokens / 128], caller-owned: entry [b][j] is the
+ * page of block j of sequence b (positions 128 j .. 128 j + 127). The caller allocates
+ * pages (distinct pages for distinct blocks) and writes the entries before the call
+ * that first quantizes that block; entries of blocks not yet complete are not read.
+ * An entry outside 0 .. paged_pages-1 is clamped into the pool: wrong results, never an
+ * access outside the cache buffer. The at most 127 newest tokens of each sequence (its
+ * incomplete last block) stay in fp16 in a fixed per-(sequence, kv head) tail, as in
+ * unpaged caches (kvq_tail_span).
+ */
+
+/*
+ * Append to the sequences of one layer of a paged cache, each its own number of tokens.
+ * k_f16, v_f16: dev, fp16 [batch][n_kv_heads][max_new][128]; rows 0 .. n_new[b]-1 of
+ *   sequence b are appended at its next positions (keys before RoPE when pre_rope).
+ * n_new: host, int32 [batch], each in 0 .. max_new.
+ * Every block that a sequence completes is quantized exactly as kvq_quantize_append does
+ * and written to its page. One launch quantizes the blocks of all sequences.
+ * Errors: KVQ_ERR_STATE for an unpaged cache (and in NUQ mode without loaded codebooks);
+ * KVQ_ERR_CAPACITY if a sequence would exceed max_tokens (nothing appended);
+ * KVQ_ERR_ARG for a bad n_new or NULL pointers.
+ */
+kvq_status kvq_quantize_append_paged(kvq_cache cache, int layer, const void* k_f16, const void* v_f16,
+                                     const int32_t* n_new, int max_new, const int32_t* block_table,
+                                     void* stream);
+
+/*
+ * Decode attention over one layer of a paged cache: sequence b attends to its own n_b
+ * tokens (its blocks through block_table, then its fp16 tail). Arguments, scores and
+ * output as for kvq_decode_attn; block_table as above.
+ * Errors: KVQ_ERR_STATE for an unpaged cache or if a sequence of the layer holds no token.
+ */
+kvq_status kvq_decode_attn_paged(kvq_cache cache, int layer, const void* q_f16, float* out,
+                                 float softmax_scale, const int32_t* block_table, void* stream);
+
+/* Tokens held by sequence b of a layer (either kind of cache; host-side counter). */
+kvq_status kvq_sequence_length(kvq_cache cache, int layer, int b, int32_t* n_tokens);
+
+/* Forget the tokens of sequence b of a layer of a paged cache (its pages are the caller's to
+ * reuse). KVQ_ERR_STATE for an unpaged cache, whose sequences keep equal lengths. */
+kvq_status kvq_sequence_reset(kvq_cache cache, int layer, int b);
+
+/* Byte range inside dev_buf of the record of kv_head in page `page` of a layer's pool
+ * (layout as for kvq_block_span). KVQ_ERR_STATE for an unpaged cache. */
+kvq_status kvq_page_span(kvq_cache cache, int layer, int page, int kv_head, size_t* offset, size_t* bytes);
+
+/* Tokens currently held by a layer (host-side counter, no device access); in a paged
+ * cache, the largest length over its sequences. */
 kvq_status kvq_cache_length(kvq_cache cache, int layer, int32_t* n_tokens);
 
-/* Forget the tokens of a layer (length = 0; device memory is not touched). */
+/* Forget the tokens of a layer, every sequence (length = 0; device memory is not touched). */
 kvq_status kvq_cache_reset(kvq_cache cache, int layer);
 
 /*

@@ -642,11 +642,18 @@ class OracleCache:
     stay in fp16 ([BLOG] 5.2: the last partial block takes a separate fp16 path). With
     neither, a block is quantized as soon as it is complete. Decode attends to every cached
     token.
+
+    Ragged batches: ``append`` may give each sequence its own number of new tokens; every
+    sequence then holds its own length and its own block boundaries (positions count from
+    0 in each sequence). Where the blocks are stored (a page pool and a block table, as the
+    notes' 7.2 and 7.3 item 5 ask for serving) does not change what is computed, so the
+    oracle has no pages.
     """
 
     def __init__(self, cfg: Config):
         self.cfg = cfg
         self.len = [0] * cfg.n_layers
+        self.seq_len = [[0] * cfg.batch for _ in range(cfg.n_layers)]
         nb = cfg.batch * cfg.n_kv_heads
         self.blocks = [[[] for _ in range(nb)] for _ in range(cfg.n_layers)]
         empty = lambda: [[np.zeros((0, D), np.float16) for _ in range(nb)] for _ in range(cfg.n_layers)]  # noqa: E731
@@ -660,19 +667,24 @@ class OracleCache:
     def _unit(self, b: int, h: int) -> int:
         return b * self.cfg.n_kv_heads + h
 
-    def append(self, layer: int, k16: np.ndarray, v16: np.ndarray):
-        """k16, v16: fp16 [B][Hkv][n_new][128]."""
+    def append(self, layer: int, k16: np.ndarray, v16: np.ndarray, n_new=None):
+        """k16, v16: fp16 [B][Hkv][rows][128]. n_new: None (every sequence appends all rows)
+        or one count per sequence (sequence b appends its first n_new[b] rows)."""
         cfg = self.cfg
-        n_new = k16.shape[2]
-        assert self.len[layer] + n_new <= cfg.max_tokens
-        n_sink = max(0, min(cfg.sink_tokens - self.len[layer], n_new))
+        rows = k16.shape[2]
+        counts = [rows] * cfg.batch if n_new is None else [int(n) for n in n_new]
+        assert len(counts) == cfg.batch and all(0 <= n <= rows for n in counts)
         for b in range(cfg.batch):
+            n_b = counts[b]
+            held = self.seq_len[layer][b]
+            assert held + n_b <= cfg.max_tokens
+            n_sink = max(0, min(cfg.sink_tokens - held, n_b))
             for h in range(cfg.n_kv_heads):
                 u = self._unit(b, h)
                 self.sink_k[layer][u] = np.concatenate([self.sink_k[layer][u], k16[b, h, :n_sink]])
                 self.sink_v[layer][u] = np.concatenate([self.sink_v[layer][u], v16[b, h, :n_sink]])
-                tk = np.concatenate([self.tail_k[layer][u], k16[b, h, n_sink:]])
-                tv = np.concatenate([self.tail_v[layer][u], v16[b, h, n_sink:]])
+                tk = np.concatenate([self.tail_k[layer][u], k16[b, h, n_sink:n_b]])
+                tv = np.concatenate([self.tail_v[layer][u], v16[b, h, n_sink:n_b]])
                 # whole blocks with at least fp16_window tokens after them
                 nfull = max(0, (tk.shape[0] - cfg.fp16_window) // T)
                 cbk = self.codebooks.get((layer, h, 0))
@@ -682,7 +694,8 @@ class OracleCache:
                         quantize_block(tk[j * T:(j + 1) * T], tv[j * T:(j + 1) * T], cfg, cbk, cbv))
                 self.tail_k[layer][u] = tk[nfull * T:].copy()
                 self.tail_v[layer][u] = tv[nfull * T:].copy()
-        self.len[layer] += n_new
+            self.seq_len[layer][b] = held + n_b
+        self.len[layer] = max(self.seq_len[layer])
 
     def dequantized(self, layer: int, b: int, h: int):
         """(K_hat, V_hat) fp64 [L][128] of one sequence/kv-head, keys pre-RoPE."""

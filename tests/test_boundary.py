@@ -44,6 +44,9 @@ def cfg(**kw):
     dict(bits=6), dict(bits=16), dict(mode=K.KVQ_MODE_NUQ, bits=8), dict(mode=K.KVQ_MODE_SYM_INT4, bits=2),
     dict(mode=K.KVQ_MODE_ASYM_INT4, bits=8), dict(mode=5),
     dict(fp16_window=-128),
+    # paged caches: at most 64 sequences, no sink or window, a pool within 4 GiB - 128 KiB
+    dict(paged_pages=-1), dict(paged_pages=8, batch=65), dict(paged_pages=8, sink_tokens=1),
+    dict(paged_pages=8, fp16_window=128), dict(paged_pages=120000, n_kv_heads=2, n_q_heads=2),
 ])
 def test_invalid_configs_are_rejected(kw):
     with pytest.raises(K.KvqError) as e:
@@ -155,6 +158,72 @@ def test_host_only_state_and_spans():
         K.kvq_cache_reset(h, 1)
         # empty layer: q (fp16) + out (fp32) of 2 x 8 heads + 2 kv heads x 2 codebooks of 8 fp32
         assert K.kvq_decode_bytes(h, 0) == 2 * 8 * 128 * (2 + 4) + 2 * 2 * 8 * 4
+    finally:
+        K.kvq_cache_destroy(h)
+
+
+def test_paged_cache_bytes_and_host_state():
+    c = cfg(paged_pages=13, batch=3, n_q_heads=2, n_kv_heads=2, pre_rope=0)
+    _, rec = R.layout(K.KVQ_MODE_RTN, 4, 0)
+
+    def a(x):
+        return (x + 255) // 256 * 256
+    # the pool replaces the per-sequence block arrays; the fp16 tails stay per sequence
+    total = a(13 * 2 * rec * c.n_layers) + a(3 * 2 * 2 * 128 * 256 * c.n_layers)
+    total += a(3 * 2 * (K.KVQ_MAX_SPLITS + 1) * 130 * 4)
+    assert K.kvq_cache_bytes(c) == total
+    n = K.kvq_cache_bytes(c)
+    h = K.kvq_cache_init(c, FAKE, n)
+    try:
+        off0, n0 = K.kvq_page_span(h, 0, 0, 0)
+        off1, _ = K.kvq_page_span(h, 0, 0, 1)
+        off2, _ = K.kvq_page_span(h, 1, 5, 1)
+        assert off0 == 0 and n0 == rec and off1 == rec
+        assert off2 == 13 * 2 * rec + (5 * 2 + 1) * rec
+        for bad in [(0, 13, 0), (0, -1, 0), (0, 0, 2), (2, 0, 0)]:
+            with pytest.raises(K.KvqError):
+                K.kvq_page_span(h, *bad)
+        # unpaged entry points refuse a paged cache, and the other way round below
+        for call in (lambda: K.kvq_quantize_append(h, 0, FAKE, FAKE, 1),
+                     lambda: K.kvq_decode_attn(h, 0, FAKE, FAKE),
+                     lambda: K.kvq_decode_attn_static(h, 0, FAKE, FAKE),
+                     lambda: K.kvq_block_span(h, 0, 0, 0, 0),
+                     lambda: K.kvq_error_decomposition(h, 0, 0, 1, FAKE, FAKE, FAKE)):
+            with pytest.raises(K.KvqError) as e:
+                call()
+            assert e.value.status == K.KVQ_ERR_STATE, K.kvq_last_error()
+        with pytest.raises(K.KvqError) as e:
+            K.kvq_quantize_append_paged(h, 0, FAKE, FAKE, [1, 2], 4, FAKE)
+        with pytest.raises(K.KvqError) as e:      # a count above max_new
+            K.kvq_quantize_append_paged(h, 0, FAKE, FAKE, [1, 5, 0], 4, FAKE)
+        assert e.value.status == K.KVQ_ERR_ARG
+        with pytest.raises(K.KvqError) as e:      # over capacity (1024 tokens per sequence)
+            K.kvq_quantize_append_paged(h, 0, FAKE, FAKE, [0, 1025, 0], 1025, FAKE)
+        assert e.value.status == K.KVQ_ERR_CAPACITY
+        with pytest.raises(K.KvqError) as e:      # blocks complete, no table
+            K.kvq_quantize_append_paged(h, 0, FAKE, FAKE, [0, 128, 0], 128, 0)
+        assert e.value.status == K.KVQ_ERR_ARG
+        K.kvq_quantize_append_paged(h, 0, FAKE, FAKE, [0, 0, 0], 16, 0)   # nothing to append
+        with pytest.raises(K.KvqError) as e:
+            K.kvq_decode_attn_paged(h, 0, FAKE, FAKE, 0.0, FAKE)          # sequences hold nothing
+        assert e.value.status == K.KVQ_ERR_STATE
+        assert [K.kvq_sequence_length(h, 0, b) for b in range(3)] == [0, 0, 0]
+        with pytest.raises(K.KvqError):
+            K.kvq_sequence_length(h, 0, 3)
+        K.kvq_sequence_reset(h, 0, 2)
+    finally:
+        K.kvq_cache_destroy(h)
+    u = cfg()
+    h = K.kvq_cache_init(u, FAKE, K.kvq_cache_bytes(u))
+    try:
+        for call in (lambda: K.kvq_quantize_append_paged(h, 0, FAKE, FAKE, [1, 1], 1, FAKE),
+                     lambda: K.kvq_decode_attn_paged(h, 0, FAKE, FAKE, 0.0, FAKE),
+                     lambda: K.kvq_page_span(h, 0, 0, 0),
+                     lambda: K.kvq_sequence_reset(h, 0, 0)):
+            with pytest.raises(K.KvqError) as e:
+                call()
+            assert e.value.status == K.KVQ_ERR_STATE
+        assert K.kvq_sequence_length(h, 0, 1) == 0
     finally:
         K.kvq_cache_destroy(h)
 

@@ -437,6 +437,50 @@ def test_append_in_chunks_equals_append_at_once(mode, bits, k_out, pre_rope, sin
         assert np.array_equal(o, outs[0])
 
 
+@pytest.mark.parametrize("mode,bits,k_out,pre_rope", [
+    (O.MODE_RTN, 2, 1, 1), (O.MODE_NUQ, 3, 0, 1), (O.MODE_KVARN, 2, 0, 0), (O.MODE_ASYM_INT4, 4, 1, 0)])
+def test_ragged_batch_equals_each_sequence_alone(mode, bits, k_out, pre_rope):
+    """Sequences that append different numbers of tokens per call: each one's blocks, tail and
+    attention are those of a batch-1 cache fed its own token stream, positions counting from
+    0 in every sequence; rows past a sequence's count are never read (they hold garbage)."""
+    r = rng(31)
+    B = 3
+    schedule = [[5, 0, 300], [200, 128, 1], [0, 1, 127], [60, 130, 0]]
+    lens = [sum(s[b] for s in schedule) for b in range(B)]
+    cfg = O.Config(1, B, 1, 2, 512, mode, bits, outliers_per_vec=k_out, pre_rope=pre_rope, varn_iters=2)
+    streams = [(r.standard_normal((1, max(lens), 128)).astype(np.float16),
+                r.standard_normal((1, max(lens), 128)).astype(np.float16)) for _ in range(B)]
+    cb = np.linspace(-1, 1, 1 << bits).astype(np.float32)
+    ragged = O.OracleCache(cfg)
+    for w in (0, 1):
+        ragged.load_codebook(0, 0, w, cb)
+    pos = [0] * B
+    for counts in schedule:
+        rows = max(counts)
+        k = np.full((B, 1, rows, 128), 1000.0, np.float16)   # garbage past each count
+        v = np.full((B, 1, rows, 128), -1000.0, np.float16)
+        for b in range(B):
+            k[b, :, :counts[b]] = streams[b][0][:, pos[b]:pos[b] + counts[b]]
+            v[b, :, :counts[b]] = streams[b][1][:, pos[b]:pos[b] + counts[b]]
+            pos[b] += counts[b]
+        ragged.append(0, k, v, n_new=counts)
+    assert ragged.seq_len[0] == lens and ragged.len[0] == max(lens)
+    q = r.standard_normal((B, 2, 128)).astype(np.float16)
+    out = ragged.decode(0, q)
+    one = O.Config(1, 1, 1, 2, 512, mode, bits, outliers_per_vec=k_out, pre_rope=pre_rope, varn_iters=2)
+    for b in range(B):
+        alone = O.OracleCache(one)
+        for w in (0, 1):
+            alone.load_codebook(0, 0, w, cb)
+        alone.append(0, streams[b][0][None, :, :lens[b]], streams[b][1][None, :, :lens[b]])
+        assert len(alone.blocks[0][0]) == len(ragged.blocks[0][b]) == lens[b] // 128
+        for x, y in zip(alone.blocks[0][0], ragged.blocks[0][b]):
+            _assert_same_block(x, y)
+        assert np.array_equal(alone.tail_k[0][0], ragged.tail_k[0][b])
+        assert np.array_equal(alone.tail_v[0][0], ragged.tail_v[0][b])
+        assert np.array_equal(alone.decode(0, q[b:b + 1])[0], out[b])
+
+
 def _assert_same_block(a, b):
     for f in ("kcodes", "vcodes", "ks1", "vs1", "kmask", "vmask", "kout", "vout"):
         x, y = getattr(a, f), getattr(b, f)
