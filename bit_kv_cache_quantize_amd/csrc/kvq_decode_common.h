@@ -32,12 +32,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x141>(v));
-  v = fmaxf(v, dpp_f<0x140>(v));
-  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+// Maximum of non-NaN values on their integer images: flipping the magnitude bits of
+// negative values makes signed integer order equal float order, and the integer max fuses
+// with the lane moves (one instruction per step; a float max would first quiet its inputs).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  const int b = __float_as_int(x);
+  int v = b ^ ((b >> 31) & 0x7FFFFFFF);
+  v = max(v, dpp_i<0xB1>(v));
+  v = max(v, dpp_i<0x4E>(v));
+  v = max(v, dpp_i<0x141>(v));
+  v = max(v, dpp_i<0x140>(v));
+  const int m = max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+                    max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+  return __int_as_float(m ^ ((m >> 31) & 0x7FFFFFFF));
 }
 
 // Orthonormal 128-point Hadamard transform of a vector held as channel pairs

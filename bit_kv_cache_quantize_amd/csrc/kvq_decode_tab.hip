@@ -95,6 +95,7 @@ struct TabDecoder {
                           // parts in operand order [2][16 steps][4 slots]
     const _Float16* zero; // 64 zero fp16 (operand rows 2 and 3)
     float* Sv;            // this wave's value scale S per token [64] (outlier corrections)
+    float* pref;          // this wave's prefix sums of the value-outlier corrections [128k + 1]
   };
 
   const DecodeArgs& a;
@@ -105,6 +106,9 @@ struct TabDecoder {
   f4 dacc[2];             // matrix-core accumulators of the two channel groups
   float tps;              // sum of the weights fed to the matrix cores (this token)
   float vsc;              // the power of two dacc and tps are scaled by (wave-uniform)
+  float wpre;             // power of two undoing the code scale of this token's operand slot
+  uint32_t orc;           // 0x3C003C00 (fp16 1.0 in both halves) in a vector register
+  uint32_t mask2, mask3, mask4;   // the code bits at slots 2, 3, 4 of both halves
 
   __device__ TabDecoder(const DecodeArgs& args, const Shared& sh, int lane_, int w_)
       : a(args), S(sh), lane(lane_), par(w_), j(64 * w_ + lane_), ib((64 * w_ + lane_) >> 1), hb(lane_ & 1) {
@@ -114,6 +118,14 @@ struct TabDecoder {
       dacc[1] = f4{0.f, 0.f, 0.f, 0.f};
       tps = 0.f;
       vsc = 1.f;
+      wpre = __builtin_amdgcn_ldexpf(1.f, 10 - 2 * code_slot(half_row_token(lane_) & 7));
+      // the constants live in registers (scalar masks, a vector 1.0 pair), so that the
+      // and-or is one three-operand instruction rather than two with literals
+      orc = __builtin_amdgcn_readfirstlane(0x3C003C00);
+      mask2 = __builtin_amdgcn_readfirstlane(0x00300030);
+      mask3 = __builtin_amdgcn_readfirstlane(0x00C000C0);
+      mask4 = __builtin_amdgcn_readfirstlane(0x03000300);
+      asm volatile("" : "+v"(orc), "+s"(mask2), "+s"(mask3), "+s"(mask4));
     }
     l_run = 0.f;
     pm = 0.f;
@@ -294,10 +306,13 @@ struct TabDecoder {
   }
 
   // Online-softmax update with this lane's log2-domain score; returns p.
+  // The exponent arguments are <= 0 (differences to the running maximum): the hardware
+  // exp2 is used directly (results below 2^-126 are flushed to zero; they are below the
+  // rounding of any sum they enter).
   __device__ __forceinline__ float softmax_step(float sl) {
     const float mnew = fmaxf(m_run, wave_max(sl));
-    const float alpha = exp2f(m_run - mnew);
-    const float p = exp2f(sl - mnew);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+    const float p = __builtin_amdgcn_exp2f(sl - mnew);
     m_run = mnew;
     l_run = fmaf(l_run, alpha, p);
     pm *= alpha;
@@ -332,12 +347,31 @@ struct TabDecoder {
     constexpr int CH = 8;
     float sc0 = 0.f, sc1 = 0.f;
     float2 uw[2][CH];
+    // 2 bits: the byte offsets (index * 8) of all pairs come from two masked shifts per
+    // code dword, even nibbles in one word and odd nibbles in the other, one byte each;
+    // a pair's offset is then a single byte extraction. The empty asm keeps the compiler
+    // from folding the shared shifts back into two operations per pair.
+    uint32_t ev[KWD], od[KWD];
+    if constexpr (BITS == 2) {
+#pragma unroll
+      for (int d = 0; d < KWD; ++d) {
+        ev[d] = (B.kw[d] << 3) & 0x78787878u;
+        od[d] = (B.kw[d] >> 1) & 0x78787878u;
+        asm volatile("" : "+v"(ev[d]), "+v"(od[d]));
+      }
+    }
     auto kread = [&](int c, float2 (&dst)[CH]) {
 #pragma unroll
       for (int k = 0; k < CH; ++k) {
         const int i = c * CH + k;
-        const uint32_t idx = pair_index(B.kw, i, 128);
-        dst[k] = *reinterpret_cast<const float2*>(reinterpret_cast<const uint8_t*>(S.tab) + (size_t)(i * PS + idx) * 8);
+        uint32_t off;
+        if constexpr (BITS == 2) {
+          const uint32_t w = (i & 1) ? od[i >> 3] : ev[i >> 3];
+          off = __builtin_amdgcn_ubfe(w, 8 * ((i & 7) >> 1), 8);
+        } else {
+          off = pair_index(B.kw, i, 128) * 8;
+        }
+        dst[k] = *reinterpret_cast<const float2*>(reinterpret_cast<const uint8_t*>(S.tab) + (size_t)i * PS * 8 + off);
       }
     };
     kread(0, uw[0]);
@@ -400,7 +434,7 @@ struct TabDecoder {
         tps *= f;
         vsc = vs;
       }
-      const float psv = ps * vs;
+      const float psv = ps * vs * wpre;
       const _Float16 hi = (_Float16)psv;
       const _Float16 lo = (_Float16)(psv - (float)hi);
       tps += (float)hi + (float)lo;
@@ -412,19 +446,30 @@ struct TabDecoder {
     if constexpr (MV) {
       // Values on the matrix cores (4x4x4 blocks): block b, column i = channel 64 g + 4 b + i;
       // operand rows 0 and 1 = the weights' high and low fp16 parts, rows 2 and 3 zero; 16
-      // steps of 4 positions cover the half-row. D = sum w (1 + code / 4), so the code sum
-      // is 4 (D - sum w), taken at the end.
+      // steps of 4 positions cover the half-row. A code enters as 1 + code * 2^(2 s - 10)
+      // (code_pair_f16) and its weight was multiplied by 2^(10 - 2 s), so D = sum w' + sum
+      // w code: the code sum is D - sum w', taken at the end.
       const int i = lane & 3;
       const _Float16* arow = i == 0 ? S.wt : (i == 1 ? S.wt + 64 : S.zero);
 #pragma unroll
-      for (int st = 0; st < 16; ++st) {
-        const h4 A = *reinterpret_cast<const h4*>(arow + 4 * st);
+      for (int q = 0; q < 4; ++q) {
+        uint32_t x[2][3];   // per group: the code dword shifted left by 4, as is, right by 6
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-          const uint32_t d = V.vw[4 * g + (st >> 2)];
-          const int m = 2 * (st & 3);
-          const h4 B = __builtin_bit_cast(h4, u32x2{code_pair_f16(d, m), code_pair_f16(d, m + 1)});
-          dacc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, B, dacc[g], 0, 0, 0);
+          const uint32_t d = V.vw[4 * g + q];
+          x[g][0] = d << 4;
+          x[g][1] = d;
+          x[g][2] = d >> 6;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int st = 4 * q + t;
+          const h4 A = *reinterpret_cast<const h4*>(arow + 4 * st);
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const h4 B = __builtin_bit_cast(h4, u32x2{code_pair_f16(x[g], 2 * t), code_pair_f16(x[g], 2 * t + 1)});
+            dacc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, B, dacc[g], 0, 0, 0);
+          }
         }
       }
     } else {
@@ -459,27 +504,62 @@ struct TabDecoder {
       acc0 += o0;
       acc1 += o1;
     }
-    // ---- value outliers: each lane walks the CSC columns of its two channels (entries in
-    // token order) and adds p_t (fp16 value - dense value of code 0) for the tokens of
-    // this half
+    // ---- value outliers: entry e of the CSC list (token t, fp16 value x) adds
+    // p_t (x - dense value of code 0) to its channel, for the tokens of this half. The
+    // entries are spread over the lanes (2k per lane, in list order), their corrections
+    // summed into a prefix array; a channel's correction is the difference of the prefix
+    // at its two column pointers. No loop depends on a column's length, and every sum has
+    // a fixed order.
     if (a.k_out > 0) {
-      acc0 += value_corrections(ch0());
-      acc1 += value_corrections(ch1());
+      value_prefix();
+      const uint16_t* vptr = reinterpret_cast<const uint16_t*>(S.blob + (a.lay.vo_ptr - a.lay.ko_val));
+      acc0 += S.pref[vptr[ch0() + 1]] - S.pref[vptr[ch0()]];
+      acc1 += S.pref[vptr[ch1() + 1]] - S.pref[vptr[ch1()]];
+      wave_sync();   // the prefix array is rewritten by the next block
     }
   }
 
-  __device__ __forceinline__ float value_corrections(int c) const {
-    const uint16_t* vptr = reinterpret_cast<const uint16_t*>(S.blob + (a.lay.vo_ptr - a.lay.ko_val));
+  // Exclusive prefix sums of the value-outlier corrections of this half into S.pref[0 .. E]
+  // (E = 128 k entries; S.pref[E] = the total).
+  __device__ __forceinline__ void value_prefix() const {
     const uint8_t* vidx = S.blob + (a.lay.vo_idx - a.lay.ko_val);
     const __half* vval = reinterpret_cast<const __half*>(S.blob + (a.lay.vo_val - a.lay.ko_val));
     const float v0 = MODE == NUQ ? S.cbv[0] : 0.f;
-    const int e1 = vptr[c + 1];
-    float corr = 0.f;
-    for (int e = vptr[c]; e < e1; ++e) {
+    const int per = 2 * a.k_out;   // entries per lane
+    const int e0 = lane * per;
+    float tot = 0.f;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
       const int t = (int)vidx[e] - 64 * par;
-      if (t >= 0 && t < 64) corr = fmaf(S.p[t], __half2float(vval[e]) - fmaf(v0, S.Sv[t], S.M[t]), corr);
+      const bool mine = t >= 0 && t < 64;
+      const int tt = mine ? t : 0;
+      const float c = mine ? S.p[tt] * (__half2float(vval[e]) - fmaf(v0, S.Sv[tt], S.M[tt])) : 0.f;
+      S.pref[e] = c;
+      tot += c;
     }
-    return corr;
+    const float incl = wave_scan(tot);
+    float run = incl - tot;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      const float c = S.pref[e];
+      S.pref[e] = run;
+      run += c;
+    }
+    if (lane == 63) S.pref[64 * per] = run;
+    wave_sync();
+  }
+
+  // Inclusive prefix sum over the 64 lanes (shifts within 16-lane rows, then the row totals
+  // broadcast to the following rows).
+  static __device__ __forceinline__ float wave_scan(float x) {
+    int v = __float_as_int(x);
+    v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false)));
+    v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false)));
+    v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false)));
+    v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false)));
+    v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false)));
+    v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false)));
+    return __int_as_float(v);
   }
 
   // Operand slot (4 * step + k) of half-row position pos in the matrix-core value product:
@@ -489,10 +569,19 @@ struct TabDecoder {
     return 16 * (pos >> 4) + 4 * ((pos & 7) >> 1) + 2 * (pos & 1) + ((pos >> 3) & 1);
   }
 
-  // Positions m and m + 8 of a 16-code dword as two fp16 values 1 + code / 4 (exact).
-  static __device__ __forceinline__ uint32_t code_pair_f16(uint32_t d, int m) {
-    const uint32_t x = 2 * m >= 8 ? (d >> (2 * m - 8)) : (d << (8 - 2 * m));
-    return (x & 0x03000300u) | 0x3C003C00u;
+  // Slot s (bits 2s, 2s + 1 of each 16-bit half) at which the code of position p of a
+  // 16-code dword (and of p + 8) is read: positions 0, 1 from the dword shifted left by 4,
+  // 2 .. 4 from the dword itself, 5 .. 7 from the dword shifted right by 6.
+  static constexpr __host__ __device__ int code_slot(int p) { return p < 2 ? p + 2 : (p < 5 ? p : p - 3); }
+
+  // Positions p and p + 8 of a 16-code dword as two fp16 values 1 + code * 2^(2 s - 10)
+  // (exact; s = code_slot(p)): the code bits at slot s, or the exponent of 1.0.
+  // x: the dword shifted left by 4, as is, right by 6.
+  __device__ __forceinline__ uint32_t code_pair_f16(const uint32_t (&x)[3], int p) const {
+    const int s = code_slot(p);
+    const uint32_t src = x[p < 2 ? 0 : (p < 5 ? 1 : 2)];
+    const uint32_t mask = s == 2 ? mask2 : (s == 3 ? mask3 : mask4);
+    return (src & mask) | orc;
   }
 
   // Tokens 64*par .. 64*par+63 of the fp16 tail (position 128*nblk + j), waves 0 and 1.
@@ -607,6 +696,12 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   sh.wt = s_wt[Dec::MV ? w : 0];
   sh.zero = s_zero;
   sh.Sv = s_S[w];
+  {
+    // dynamic LDS: the outlier segments, then one prefix array per wave
+    const int blob16 = a.k_out > 0 ? ((int)(a.lay.vo_idx + 128u * a.k_out - a.lay.ko_val) + 15) & ~15 : 0;
+    const int pref16 = ((128 * a.k_out + 1) * 4 + 15) & ~15;
+    sh.pref = reinterpret_cast<float*>(s_dyn + blob16 + w * pref16);
+  }
   Dec d(a, sh, lane, w);
 
   float rc[64], rs[64];
@@ -671,8 +766,8 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
     if constexpr (Dec::MV) {
       const float T = wave_sum(d.tps);
       const float un = 1.f / d.vsc;   // a power of two: exact
-      o0 += 4.f * ((d.dacc[0][0] + d.dacc[0][1]) - T) * un;
-      o1 += 4.f * ((d.dacc[1][0] + d.dacc[1][1]) - T) * un;
+      o0 += ((d.dacc[0][0] + d.dacc[0][1]) - T) * un;
+      o1 += ((d.dacc[1][0] + d.dacc[1][1]) - T) * un;
     }
     s_o[w * 128 + d.ch0()] = o0;
     s_o[w * 128 + d.ch1()] = o1;
