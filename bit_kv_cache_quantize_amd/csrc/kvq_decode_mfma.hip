@@ -75,7 +75,8 @@ __device__ __forceinline__ float rows_max(float v) {
 }
 
 // (x & mask) | 0x64006400 in one v_bfi_b32 (the exponent bits of 1024 lie outside every mask
-// used here); written out because the compiler otherwise emits an and and an or.
+// used here); written out because the compiler otherwise emits an and and an or. The result
+// only feeds vector instructions (fix), never a matrix-core operand directly.
 __device__ __forceinline__ uint32_t with_exp(uint32_t x, uint32_t mask) {
   uint32_t r;
   asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(x), "s"(0x64006400u));
@@ -248,9 +249,12 @@ struct MfmaDecoder {
     // x - c in one mixed-precision fma per value (fp32 x, fp16 c from the low / high half),
     // rounded once to fp16 into the low / high half; exact before the rounding since c is x
     // rounded to fp16, or 0
+    // The result is a matrix-core operand. The compiler's hazard tracking does not see into
+    // assembler statements, and a vector write needs two wait states before a matrix-core
+    // read of the same register: the statement ends with them (s_nop 1).
     uint32_t r;
     asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(r) : "v"(xa), "v"(c));
-    asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(r) : "v"(xb), "v"(c));
+    asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\ts_nop 1" : "+v"(r) : "v"(xb), "v"(c));
     return r;
   }
 

@@ -104,11 +104,8 @@ struct TabDecoder {
   int ob_bytes, ob_chunks;
   float m_run, l_run, pm, acc0, acc1;
   f4 dacc[2];             // matrix-core accumulators of the two channel groups
-  float tps;              // sum of the weights fed to the matrix cores (this token)
-  float vsc;              // the power of two dacc and tps are scaled by (wave-uniform)
+  float vsc;              // the power of two dacc is scaled by (wave-uniform)
   float wpre;             // power of two undoing the code scale of this token's operand slot
-  uint32_t orc;           // 0x3C003C00 (fp16 1.0 in both halves) in a vector register
-  uint32_t mask2, mask3, mask4;   // the code bits at slots 2, 3, 4 of both halves
 
   __device__ TabDecoder(const DecodeArgs& args, const Shared& sh, int lane_, int w_)
       : a(args), S(sh), lane(lane_), par(w_), j(64 * w_ + lane_), ib((64 * w_ + lane_) >> 1), hb(lane_ & 1) {
@@ -116,16 +113,8 @@ struct TabDecoder {
     if constexpr (MV) {
       dacc[0] = f4{0.f, 0.f, 0.f, 0.f};
       dacc[1] = f4{0.f, 0.f, 0.f, 0.f};
-      tps = 0.f;
       vsc = 1.f;
-      wpre = __builtin_amdgcn_ldexpf(1.f, 10 - 2 * code_slot(half_row_token(lane_) & 7));
-      // the constants live in registers (scalar masks, a vector 1.0 pair), so that the
-      // and-or is one three-operand instruction rather than two with literals
-      orc = __builtin_amdgcn_readfirstlane(0x3C003C00);
-      mask2 = __builtin_amdgcn_readfirstlane(0x00300030);
-      mask3 = __builtin_amdgcn_readfirstlane(0x00C000C0);
-      mask4 = __builtin_amdgcn_readfirstlane(0x03000300);
-      asm volatile("" : "+v"(orc), "+s"(mask2), "+s"(mask3), "+s"(mask4));
+      wpre = __builtin_amdgcn_ldexpf(1.f, 19 - 2 * code_slot(half_row_token(lane_) & 7));
     }
     l_run = 0.f;
     pm = 0.f;
@@ -321,7 +310,6 @@ struct TabDecoder {
     if constexpr (MV) {
       dacc[0] *= alpha;
       dacc[1] *= alpha;
-      tps *= alpha;
     }
     return p;
   }
@@ -422,22 +410,20 @@ struct TabDecoder {
     if (a.k_out > 0) S.Sv[lane] = V.tst.x;
     if constexpr (MV) {
       // the weight as fp16 high and low parts, at the operand slot of token j's position,
-      // after a power of two that puts the half block's largest value scale in [0.5, 1)
-      // (fp16's exponent range is narrow; the scaling is exact and undone at the end):
-      // the accumulators follow the current power of two
+      // after a power of two that puts the half block's largest value scale in [0.5, 1) and
+      // the slot's power of two (at most 2^15: within fp16's range; both exact and undone at
+      // the end); the accumulators follow the current power of two
       const float smax = wave_max(V.tst.x);
       const float vs = smax > 0.f ? __builtin_amdgcn_ldexpf(1.f, -__builtin_amdgcn_frexp_expf(smax)) : 1.f;
       if (vs != vsc) {
         const float f = vs / vsc;
         dacc[0] *= f;
         dacc[1] *= f;
-        tps *= f;
         vsc = vs;
       }
       const float psv = ps * vs * wpre;
       const _Float16 hi = (_Float16)psv;
       const _Float16 lo = (_Float16)(psv - (float)hi);
-      tps += (float)hi + (float)lo;
       const int pos = half_row_token(lane);   // the position map is its own inverse
       S.wt[mv_slot(pos)] = hi;
       S.wt[64 + mv_slot(pos)] = lo;
@@ -446,9 +432,10 @@ struct TabDecoder {
     if constexpr (MV) {
       // Values on the matrix cores (4x4x4 blocks): block b, column i = channel 64 g + 4 b + i;
       // operand rows 0 and 1 = the weights' high and low fp16 parts, rows 2 and 3 zero; 16
-      // steps of 4 positions cover the half-row. A code enters as 1 + code * 2^(2 s - 10)
-      // (code_pair_f16) and its weight was multiplied by 2^(10 - 2 s), so D = sum w' + sum
-      // w code: the code sum is D - sum w', taken at the end.
+      // steps of 4 positions cover the half-row. A code enters as the fp16 subnormal
+      // code * 2^(2 s - 24) (code_pair_f16: the code bits left in place at slot s) and its
+      // weight was multiplied by 2^(19 - 2 s): every product is weight * code * 2^-5,
+      // exactly, with no constant part to subtract.
       const int i = lane & 3;
       const _Float16* arow = i == 0 ? S.wt : (i == 1 ? S.wt + 64 : S.zero);
 #pragma unroll
@@ -574,14 +561,13 @@ struct TabDecoder {
   // 2 .. 4 from the dword itself, 5 .. 7 from the dword shifted right by 6.
   static constexpr __host__ __device__ int code_slot(int p) { return p < 2 ? p + 2 : (p < 5 ? p : p - 3); }
 
-  // Positions p and p + 8 of a 16-code dword as two fp16 values 1 + code * 2^(2 s - 10)
-  // (exact; s = code_slot(p)): the code bits at slot s, or the exponent of 1.0.
+  // Positions p and p + 8 of a 16-code dword as two fp16 subnormals code * 2^(2 s - 24)
+  // (exact; s = code_slot(p)): only the code bits at slot s are kept, one and per pair.
   // x: the dword shifted left by 4, as is, right by 6.
-  __device__ __forceinline__ uint32_t code_pair_f16(const uint32_t (&x)[3], int p) const {
+  static __device__ __forceinline__ uint32_t code_pair_f16(const uint32_t (&x)[3], int p) {
     const int s = code_slot(p);
     const uint32_t src = x[p < 2 ? 0 : (p < 5 ? 1 : 2)];
-    const uint32_t mask = s == 2 ? mask2 : (s == 3 ? mask3 : mask4);
-    return (src & mask) | orc;
+    return src & (s == 2 ? 0x00300030u : (s == 3 ? 0x00C000C0u : 0x03000300u));
   }
 
   // Tokens 64*par .. 64*par+63 of the fp16 tail (position 128*nblk + j), waves 0 and 1.
@@ -764,10 +750,9 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
     if (lane == 0) { s_m[w] = d.m_run; s_l[w] = l; }
     float o0 = d.acc0 + pmw, o1 = d.acc1 + pmw;
     if constexpr (Dec::MV) {
-      const float T = wave_sum(d.tps);
-      const float un = 1.f / d.vsc;   // a power of two: exact
-      o0 += ((d.dacc[0][0] + d.dacc[0][1]) - T) * un;
-      o1 += ((d.dacc[1][0] + d.dacc[1][1]) - T) * un;
+      const float un = 32.f / d.vsc;   // 2^5 undoes the operand scaling; powers of two: exact
+      o0 += (d.dacc[0][0] + d.dacc[0][1]) * un;
+      o1 += (d.dacc[1][0] + d.dacc[1][1]) * un;
     }
     s_o[w * 128 + d.ch0()] = o0;
     s_o[w * 128 + d.ch1()] = o1;
