@@ -38,6 +38,11 @@
 namespace kvq {
 namespace {
 
+// 1 / x for x a power of two (normal), exactly: 2^(1 - e) with x = 0.5 * 2^e.
+__device__ __forceinline__ float recip_pow2(float x) {
+  return __builtin_amdgcn_ldexpf(1.f, 1 - __builtin_amdgcn_frexp_expf(x));
+}
+
 using namespace dec;
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -335,7 +340,7 @@ struct MfmaDecoder {
     // ---- raw scores for tokens 16*tt + 4*q + e, head n & 7 (KVarN: already in the log2
     // domain; otherwise the log2 scale is applied inside the exponent)
     constexpr bool PRESCALED = MODE == KVARN;
-    const float kunscale = 1.f / kscale;   // exact: a power of two
+    const float kunscale = recip_pow2(kscale);   // exact: a power of two
     float sc[4][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -404,7 +409,7 @@ struct MfmaDecoder {
     l_run = fmaf(l_run, alpha, lsum);
     // RTN: acc holds sum p' codes in units of the current vscale; a new vscale rescales it
     // (exactly, a power of two) together with the softmax correction
-    const float arescale = MODE == RTN ? alpha * (vscale / vsc) : alpha;
+    const float arescale = MODE == RTN ? alpha * (vscale * recip_pow2(vsc)) : alpha;   // powers of two: exact
     if (__builtin_amdgcn_ballot_w64(arescale != 1.f)) {   // a running maximum or the value scale moved
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) acc[ct] *= arescale;
@@ -418,7 +423,7 @@ struct MfmaDecoder {
       g = rows_sum(g);
       g = lo_mask ? 0.f : g;           // once per head: on the high column
     }
-    const float vunscale = 1.f / vscale;   // exact: a power of two
+    const float vunscale = recip_pow2(vscale);   // exact: a power of two
 
     // ---- P' operand, this lane's part, slots in the order of the value chunks
     uint32_t po[2][4];
@@ -610,7 +615,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[ct][e] = d.acc[ct][e] + dpp_f<0x128>(d.acc[ct][e]);   // high + low column
   if constexpr (MODE == RTN) {
-    const float un = 1.f / d.vsc;   // the accumulators' value scale, a power of two
+    const float un = recip_pow2(d.vsc);   // the accumulators' value scale, a power of two (exact)
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll

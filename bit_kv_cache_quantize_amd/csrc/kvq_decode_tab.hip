@@ -38,6 +38,11 @@
 namespace kvq {
 namespace {
 
+// 1 / x for x a power of two (normal), exactly: 2^(1 - e) with x = 0.5 * 2^e.
+__device__ __forceinline__ float recip_pow2(float x) {
+  return __builtin_amdgcn_ldexpf(1.f, 1 - __builtin_amdgcn_frexp_expf(x));
+}
+
 using namespace dec;
 
 constexpr float kInv2Pi = 0.15915494309189535f;
@@ -416,7 +421,7 @@ struct TabDecoder {
       const float smax = wave_max(V.tst.x);
       const float vs = smax > 0.f ? __builtin_amdgcn_ldexpf(1.f, -__builtin_amdgcn_frexp_expf(smax)) : 1.f;
       if (vs != vsc) {
-        const float f = vs / vsc;
+        const float f = vs * recip_pow2(vsc);   // powers of two: exact
         dacc[0] *= f;
         dacc[1] *= f;
         vsc = vs;
@@ -750,7 +755,7 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
     if (lane == 0) { s_m[w] = d.m_run; s_l[w] = l; }
     float o0 = d.acc0 + pmw, o1 = d.acc1 + pmw;
     if constexpr (Dec::MV) {
-      const float un = 32.f / d.vsc;   // 2^5 undoes the operand scaling; powers of two: exact
+      const float un = 32.f * recip_pow2(d.vsc);   // 2^5 undoes the operand scaling; powers of two: exact
       o0 += (d.dacc[0][0] + d.dacc[0][1]) * un;
       o1 += (d.dacc[1][0] + d.dacc[1][1]) * un;
     }
