@@ -161,6 +161,17 @@ kvq_status kvq_quantize_append(kvq_cache cache, int layer, const void* k_f16, co
  * absolute position); softmax_scale <= 0 selects 1/sqrt(128)
  * (KVQuant notes Algorithm 1, attention part).
  * Errors: KVQ_ERR_STATE if the layer holds no tokens.
+ *
+ * Kernel selection (fixed by the configuration; results agree within the tolerance the
+ * tests state, records are the same):
+ *   - pre_rope = 1, one query head per kv head, 2 or 3 bits, RTN or NUQ: the table kernel
+ *     (per-block LDS tables of the rotated query over the code pairs of each channel pair);
+ *   - pre_rope = 0, no outliers, 2 or 4 bits, RTN, KVARN or SYM_INT4: the matrix-core
+ *     kernel (products on v_mfma_f32_16x16x32_f16);
+ *   - every other configuration: the vector-unit kernel. It is correct for all of them but
+ *     not tuned: with pre_rope = 1 and with 8 query heads per kv head its per-lane state
+ *     exceeds the register file and part of it lives in scratch memory.
+ * Caches with sink tokens or an fp16 window run one more kernel for the fp16 tokens.
  */
 kvq_status kvq_decode_attn(kvq_cache cache, int layer, const void* q_f16, float* out,
                            float softmax_scale, void* stream);
