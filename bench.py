@@ -56,6 +56,10 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=0, help="tokens per oracle unit (0: by workload)")
     p.add_argument("--sink", type=int, default=0, help="attention-sink tokens kept in fp16")
     p.add_argument("--window", type=int, default=0, help="fp16 window of recent tokens (multiple of 128)")
+    p.add_argument("--paged", action="store_true",
+                   help="paged cache: records in a page pool behind a shuffled block table")
+    p.add_argument("--ragged", action="store_true",
+                   help="with --paged: sequence b holds its own length in [context/2, context]")
     return p.parse_args()
 
 
@@ -69,7 +73,7 @@ def is_streamed(wl):
 
 
 class Bench:
-    def __init__(self, wl, splits, steps_total, sink=0, window=0):
+    def __init__(self, wl, splits, steps_total, sink=0, window=0, paged=False, ragged=False):
         import torch
         import bit_kv_cache_quantize_amd as K
         import synth
@@ -82,9 +86,23 @@ class Bench:
         self.streamed = is_streamed(wl)
         self.copies = 2 if self.single else 1
         capacity = ceil128(wl.context) + (128 * steps_total if self.streamed else 0)
+        self.paged = paged
+        # ragged: sequence b holds context - (a seeded share of up to half of it) tokens
+        self.lens = [wl.context] * wl.batch
+        if paged and ragged:
+            import numpy as np
+            r = np.random.default_rng(wl.seed + 99)
+            self.lens = [int(wl.context - r.integers(0, wl.context // 2 + 1)) for _ in range(wl.batch)]
+        max_blocks = capacity // 128
         cfg = K.make_config(wl.n_layers, wl.batch, wl.n_kv_heads, wl.n_q_heads, capacity, wl.mode,
                             wl.bits, wl.outliers_per_vec, wl.pre_rope, wl.rope_theta, wl.varn_iters,
-                            sink_tokens=sink, fp16_window=window)
+                            sink_tokens=sink, fp16_window=window,
+                            paged_pages=wl.batch * max_blocks if paged else 0)
+        if paged:
+            # every (sequence, block) gets its own page, in a seeded random order
+            import numpy as np
+            perm = np.random.default_rng(wl.seed + 7).permutation(wl.batch * max_blocks).astype(np.int32)
+            self.table = torch.from_numpy(perm.reshape(wl.batch, max_blocks)).to(torch.device("cuda", 0))
         self.caches = [K.KVCache(cfg, self.dev) for _ in range(self.copies)]
         for c in self.caches:
             if splits:
@@ -138,25 +156,37 @@ class Bench:
             for t0, m in self.chunks:
                 kk, vv = (k, v) if m == n else (k[:, :, :m].contiguous(), v[:, :, :m].contiguous())
                 self.gen.fill_kv(kk, vv, layer, t0, m)
-                c.append(layer, kk, vv)
+                self._append(c, layer, kk, vv, t0)
         self.stream_chunk = (k, v)
 
     def append_all(self, copy, step=0):
         c = self.caches[copy]
         if self.streamed:
             for layer, (k, v) in enumerate(self.step_inputs[step]):
-                c.append(layer, k, v)
+                self._append(c, layer, k, v, None)
             return
         for layer in range(self.wl.n_layers):
             c.reset(layer)
             for t0, _ in self.chunks:
                 k, v = self.inputs[(layer, t0)]
-                c.append(layer, k, v)
+                self._append(c, layer, k, v, t0)
+
+    def _append(self, c, layer, k, v, t0):
+        """Append rows starting at position t0 (None: a step's new block, every sequence)."""
+        if not self.paged:
+            c.append(layer, k, v)
+            return
+        n = k.shape[2]
+        counts = [n if t0 is None else max(0, min(n, L - t0)) for L in self.lens]
+        c.append_paged(layer, k, v, counts, self.table)
 
     def decode_all(self, copy):
         c = self.caches[copy]
         for layer in range(self.wl.n_layers):
-            c.decode(layer, self.q[layer], self.out)
+            if self.paged:
+                c.decode_paged(layer, self.q[layer], self.out, self.table)
+            else:
+                c.decode(layer, self.q[layer], self.out)
 
     def decode_bytes(self):
         c = self.caches[0]
@@ -393,7 +423,10 @@ def main():
         print(f"cpu baseline done: {cpu['sample']}", file=sys.stderr, flush=True)
     import torch
     warmup = max(args.warmup, 2 if wl.n_layers == 1 else 1)
-    b = Bench(wl, args.splits, args.steps + warmup, args.sink, args.window)
+    if args.ragged and (not args.paged or is_streamed(wl)):
+        print("--ragged needs --paged and a resident workload (not the 1M-token one)", file=sys.stderr)
+        sys.exit(2)
+    b = Bench(wl, args.splits, args.steps + warmup, args.sink, args.window, args.paged, args.ragged)
     print("cache built", file=sys.stderr, flush=True)
     ms_step, dec, app, step_bytes = b.run(args.steps, warmup)
     dec_ms = sum(dec) / len(dec)
@@ -412,9 +445,8 @@ def main():
         app_launches = 1
     else:
         step_app_ms = app_ms = sum(app) / len(app)
-        app_rate = wl.batch * wl.context * layers / (app_ms * 1e-3) / 1e6
-        nblk = wl.context // 128
-        abytes = layers * wl.batch * wl.n_kv_heads * (wl.context * 512 + nblk * rec_payload + (wl.context % 128) * 512)
+        app_rate = sum(b.lens) * layers / (app_ms * 1e-3) / 1e6
+        abytes = layers * wl.n_kv_heads * sum(L * 512 + (L // 128) * rec_payload + (L % 128) * 512 for L in b.lens)
         app_launches = layers * len(b.chunks)
     app_gbs = abytes / (app_ms * 1e-3) / 1e9
     copy_gbs = measured_copy_gbs(torch, b.dev)
@@ -440,6 +472,7 @@ def main():
                    "bits": wl.bits, "outliers_per_vec": wl.outliers_per_vec, "pre_rope": wl.pre_rope,
                    "varn_iters": wl.varn_iters if wl.mode == 2 else 0,
                    "sink_tokens": args.sink, "fp16_window": args.window,
+                   "paged": args.paged, "ragged_lengths": b.lens if args.ragged else None,
                    "step": ("append one 128-token block to every layer, then decode every layer"
                             if b.streamed else "append the whole context to every layer, then decode every layer")},
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),

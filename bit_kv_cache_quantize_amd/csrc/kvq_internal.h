@@ -48,8 +48,12 @@ struct PagedSeq {
 
 // Page of block blk of sequence b, clamped into the pool: a bad table entry gives wrong
 // results, never an access outside the pool.
+// The table is read through the constant address space: the index is uniform across the
+// workgroup, so the read is one scalar load (a vector load would make the next wait on the
+// vector memory counter drain every record prefetch in flight).
 __device__ __forceinline__ int page_of(const PagedSeq& p, int b, int blk) {
-  const int v = p.table[(size_t)b * p.table_stride + blk];
+  typedef const __attribute__((address_space(4))) int32_t* ConstI32;
+  const int v = ((ConstI32)p.table)[(size_t)b * p.table_stride + blk];
   return v < 0 ? 0 : (v >= p.n_pages ? p.n_pages - 1 : v);
 }
 
