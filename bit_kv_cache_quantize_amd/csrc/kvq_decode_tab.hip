@@ -111,10 +111,13 @@ struct TabDecoder {
   f4 dacc[2];             // matrix-core accumulators of the two channel groups
   float vsc;              // the power of two dacc is scaled by (wave-uniform)
   float wpre;             // power of two undoing the code scale of this token's operand slot
+  float qx_, qy_;         // the query pair ib (scale folded), read once
 
   __device__ TabDecoder(const DecodeArgs& args, const Shared& sh, int lane_, int w_)
       : a(args), S(sh), lane(lane_), par(w_), j(64 * w_ + lane_), ib((64 * w_ + lane_) >> 1), hb(lane_ & 1) {
     m_run = -INFINITY;
+    qx_ = S.q[2 * ib];
+    qy_ = S.q[2 * ib + 1];
     if constexpr (MV) {
       dacc[0] = f4{0.f, 0.f, 0.f, 0.f};
       dacc[1] = f4{0.f, 0.f, 0.f, 0.f};
@@ -238,7 +241,7 @@ struct TabDecoder {
   // Entries hb*PT/2 .. hb*PT/2 + PT/2 - 1 of pair ib's table (the other lane of the pair
   // writes the rest), the pair's rotated query and its channel statistics.
   __device__ __forceinline__ void build(const Meta& B) const {
-    const float qx = S.q[2 * ib], qy = S.q[2 * ib + 1];
+    const float qx = qx_, qy = qy_;
     const float al = fmaf(qx, B.rb.x, qy * B.rb.y);
     const float be = fmaf(qy, B.rb.x, -qx * B.rb.y);
     if (hb == 0) S.qb[ib] = make_float2(al, be);
