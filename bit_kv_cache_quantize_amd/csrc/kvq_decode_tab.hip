@@ -60,9 +60,15 @@ struct TabDecoder {
   static constexpr int R = 16 * BITS;                 // key row bytes
   static constexpr int RH = R / 2;                    // value half-row bytes
   static constexpr int PT = BITS == 3 ? 64 : 16;      // table entries per channel pair
-  // Pair tables are PT + 2 entries apart: the 16-byte pad staggers the LDS bank groups of
-  // consecutive pairs, so that the lanes of a build step (one pair each) do not all write
-  // the same banks. The lookups keep their immediate offsets (no extra instruction).
+  // Pair tables: entry idx of pair i at byte 8 * (PS * i + idx), (U, W) as 8 bytes, with
+  // idx = a | b << 2 at 2 bits (x code a, y code b) and n | h << 4 at 3 bits (n: the pair's
+  // nibble of the crumb plane, the two low bits of a and of b; h: its crumb of the bit plane,
+  // bit 2 of a and of b). The tables are PT + 2 entries apart: the 16-byte pad staggers the
+  // LDS bank groups of consecutive pairs, so that the lanes of a build step (one pair each)
+  // do not all write the same banks. The lookups keep their immediate offsets (no extra
+  // instruction). (A 3-bit table spans 512 bytes, two entries per 8-byte bank: random
+  // lookups conflict; U and W as separate 256-byte arrays of 4-byte entries measured more
+  // conflicts, not fewer.)
   static constexpr int PS = PT + 2;
   static constexpr int KWD = R / 4;                   // dwords of a key row
   // 2-bit RTN values go through the matrix cores (codes are small integers, exact in
@@ -92,7 +98,6 @@ struct TabDecoder {
     float* p;             // this wave's p per token [64]
     float* M;             // this wave's value offset M per token [64]
     uint8_t* blob;        // outlier staging
-    const float* q;       // query (original domain, scale folded) [128]
     const float* trev;    // theta_i / (2 pi) [64]
     const float* cbk;     // key codebook [16] (NUQ)
     const float* cbv;     // value codebook [16] (NUQ)
@@ -116,8 +121,9 @@ struct TabDecoder {
   __device__ TabDecoder(const DecodeArgs& args, const Shared& sh, int lane_, int w_)
       : a(args), S(sh), lane(lane_), par(w_), j(64 * w_ + lane_), ib((64 * w_ + lane_) >> 1), hb(lane_ & 1) {
     m_run = -INFINITY;
-    qx_ = S.q[2 * ib];
-    qy_ = S.q[2 * ib + 1];
+    const __half2 q2 = reinterpret_cast<const __half2*>(a.q + ((size_t)blockIdx.z * a.Hq + blockIdx.y) * 128)[ib];
+    qx_ = __low2float(q2) * a.scale_log2;
+    qy_ = __high2float(q2) * a.scale_log2;
     if constexpr (MV) {
       dacc[0] = f4{0.f, 0.f, 0.f, 0.f};
       dacc[1] = f4{0.f, 0.f, 0.f, 0.f};
@@ -238,8 +244,10 @@ struct TabDecoder {
     else return (float)code;
   }
 
-  // Entries hb*PT/2 .. hb*PT/2 + PT/2 - 1 of pair ib's table (the other lane of the pair
-  // writes the rest), the pair's rotated query and its channel statistics.
+  // Half of pair ib's table (the other lane of the pair writes the rest), the pair's rotated
+  // query and its channel statistics. Lane hb writes the entries whose y code has its top
+  // bit (bit 1 at 2 bits, bit 2 at 3 bits) equal to hb, so that the two lanes' stores land
+  // in different banks.
   __device__ __forceinline__ void build(const Meta& B) const {
     const float qx = qx_, qy = qy_;
     const float al = fmaf(qx, B.rb.x, qy * B.rb.y);
@@ -257,30 +265,29 @@ struct TabDecoder {
     }
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
-      const int b = NB * hb + c;
-      const float ky = fmaf(kcode(1, b), B.kst.y, B.kst.w);
+      const int y = NB * hb + c;
+      const float ky = fmaf(kcode(1, y), B.kst.y, B.kst.w);
       Ay[c] = be * ky;
       By[c] = -al * ky;
     }
-    float4* dst = reinterpret_cast<float4*>(S.tab + ib * PS + hb * (PT / 2));
+    uint8_t* tab = reinterpret_cast<uint8_t*>(S.tab) + ib * PS * 8;
+    // the lane's entries idx = hb * PT/2 + ee; the bits that name the lane's half do not
+    // enter ca (x code) or cbl (index of the y code in this lane's range)
+    auto entry = [&](int ee) {
+      int ca, cbl;
+      if constexpr (BITS == 3) {   // idx = lo2(a) | lo2(b) << 2 | hi(a) << 4 | hi(b) << 5
+        ca = (ee & 3) | (((ee >> 4) & 1) << 2);
+        cbl = (ee >> 2) & 3;
+      } else {                     // idx = a | b << 2
+        ca = ee & 3;
+        cbl = (ee >> 2) & 1;
+      }
+      return make_float2(Ax[ca] + Ay[cbl], Bx[ca] + By[cbl]);
+    };
 #pragma unroll
     for (int e = 0; e < PT / 2; e += 2) {
-      float2 v[2];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        // entry hb * PT/2 + ee; the bits that name the lane's half do not enter ca or cbl
-        const int ee = e + k;
-        int ca, cbl;   // code of x, index of the y code in this lane's range
-        if constexpr (BITS == 3) {   // idx = lo2(a) | lo2(b) << 2 | hi(a) << 4 | hi(b) << 5
-          ca = (ee & 3) | (((ee >> 4) & 1) << 2);
-          cbl = (ee >> 2) & 3;
-        } else {                     // idx = a | b << 2
-          ca = ee & 3;
-          cbl = (ee >> 2) & 1;
-        }
-        v[k] = make_float2(Ax[ca] + Ay[cbl], Bx[ca] + By[cbl]);
-      }
-      dst[e / 2] = make_float4(v[0].x, v[0].y, v[1].x, v[1].y);
+      const float2 v0 = entry(e), v1 = entry(e + 1);
+      *reinterpret_cast<float4*>(tab + 8 * (hb * (PT / 2) + e)) = make_float4(v0.x, v0.y, v1.x, v1.y);
     }
   }
 
@@ -295,6 +302,43 @@ struct TabDecoder {
       return nib;
     }
   }
+
+  // A 3-bit row (NC dwords of the crumb plane: pair i's two low-bit crumbs are nibble i;
+  // NC / 2 dwords of the bit plane: pair i's two high bits are crumb i) spread once so that
+  // the table offset 8 * (n | h << 4) of any pair costs a byte permute and a shift:
+  //   ev[d], od[d]: the even / odd nibbles of crumb dword d, times 16, one per byte;
+  //   hm[e][m]:     crumb m of every byte of bit-plane dword e, in bits 0-1 of that byte.
+  // Pair i's nibble is byte ((i & 7) >> 1) of ev / od[i >> 3], its crumb is byte
+  // ((i & 15) >> 2) of hm[i >> 4][i & 3]; the permute puts them in bytes 0 and 1 (zeros in
+  // bytes 2 and 3): 16 n + 256 h, twice the offset. (Offsets without the shift, 8 n + 256 h,
+  // put both high bits above the LDS bank bits and measured slower: more bank conflicts.)
+  // The empty asm keeps the compiler from folding the shared shifts back into per-pair
+  // operations.
+  template <int NC>
+  struct Spread3 {
+    uint32_t ev[NC], od[NC], hm[NC / 2][4];
+    __device__ __forceinline__ void make(const uint32_t* w) {
+#pragma unroll
+      for (int d = 0; d < NC; ++d) {
+        ev[d] = (w[d] << 4) & 0xF0F0F0F0u;
+        od[d] = w[d] & 0xF0F0F0F0u;
+        asm volatile("" : "+v"(ev[d]), "+v"(od[d]));
+      }
+#pragma unroll
+      for (int e = 0; e < NC / 2; ++e) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          hm[e][m] = (w[NC + e] >> (2 * m)) & 0x03030303u;
+          asm volatile("" : "+v"(hm[e][m]));
+        }
+      }
+    }
+    __device__ __forceinline__ uint32_t off(int i) const {
+      const uint32_t E = (i & 1) ? od[i >> 3] : ev[i >> 3];
+      const uint32_t sel = 0x0C0C0000u | ((4u + ((i & 15) >> 2)) << 8) | (uint32_t)((i & 7) >> 1);
+      return __builtin_amdgcn_perm(hm[i >> 4][i & 3], E, sel) >> 1;
+    }
+  };
 
   __device__ __forceinline__ void wave_sync() const {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -347,27 +391,31 @@ struct TabDecoder {
     // code dword, even nibbles in one word and odd nibbles in the other, one byte each;
     // a pair's offset is then a single byte extraction. The empty asm keeps the compiler
     // from folding the shared shifts back into two operations per pair.
-    uint32_t ev[KWD], od[KWD];
+    // 3 bits: the same for both planes (Spread3), a pair's offset is a byte permute and a
+    // shift.
+    uint32_t ev[8], od[8];
+    Spread3<8> sp;
     if constexpr (BITS == 2) {
 #pragma unroll
-      for (int d = 0; d < KWD; ++d) {
+      for (int d = 0; d < 8; ++d) {
         ev[d] = (B.kw[d] << 3) & 0x78787878u;
         od[d] = (B.kw[d] >> 1) & 0x78787878u;
         asm volatile("" : "+v"(ev[d]), "+v"(od[d]));
       }
+    } else {
+      sp.make(B.kw);
     }
     auto kread = [&](int c, float2 (&dst)[CH]) {
 #pragma unroll
       for (int k = 0; k < CH; ++k) {
         const int i = c * CH + k;
-        uint32_t off;
+        const uint8_t* t = reinterpret_cast<const uint8_t*>(S.tab) + (size_t)i * PS * 8;
         if constexpr (BITS == 2) {
           const uint32_t w = (i & 1) ? od[i >> 3] : ev[i >> 3];
-          off = __builtin_amdgcn_ubfe(w, 8 * ((i & 7) >> 1), 8);
+          dst[k] = *reinterpret_cast<const float2*>(t + __builtin_amdgcn_ubfe(w, 8 * ((i & 7) >> 1), 8));
         } else {
-          off = pair_index(B.kw, i, 128) * 8;
+          dst[k] = *reinterpret_cast<const float2*>(t + sp.off(i));
         }
-        dst[k] = *reinterpret_cast<const float2*>(reinterpret_cast<const uint8_t*>(S.tab) + (size_t)i * PS * 8 + off);
       }
     };
     kread(0, uw[0]);
@@ -473,14 +521,29 @@ struct TabDecoder {
       constexpr int CV = 2;
       float o0 = 0.f, o1 = 0.f;
       float2 vb[2][CV][3];
+      // 3 bits: the two half-rows spread once (Spread3). The weights of the two token pairs
+      // of a chunk (tokens t .. t + 3 of the half-row order) come in one 16-byte read.
+      static_assert(CV == 2, "one weight read per two token pairs");
+      Spread3<4> s0, s1;
+      if constexpr (BITS == 3) {
+        s0.make(V.vw);
+        s1.make(V.vw + KWD / 2);
+      }
+      const uint8_t* vl = reinterpret_cast<const uint8_t*>(S.vlut);
       auto vread = [&](int c, float2 (&dst)[CV][3]) {
+        const float4 w4 = *reinterpret_cast<const float4*>(S.pS + half_row_token(2 * CV * c));
+        dst[0][0] = make_float2(w4.x, w4.y);
+        dst[1][0] = make_float2(w4.z, w4.w);
 #pragma unroll
         for (int k = 0; k < CV; ++k) {
-          const int pp = c * CV + k;
-          const int t = half_row_token(2 * pp);   // positions 2pp, 2pp+1 hold tokens t, t+1
-          dst[k][0] = *reinterpret_cast<const float2*>(S.pS + t);
-          dst[k][1] = S.vlut[pair_index(V.vw, pp, 64)];
-          dst[k][2] = S.vlut[pair_index(V.vw + KWD / 2, pp, 64)];
+          const int pp = c * CV + k;   // positions 2pp, 2pp+1: tokens half_row_token(2pp) + 0, 1
+          if constexpr (BITS == 3) {
+            dst[k][1] = *reinterpret_cast<const float2*>(vl + s0.off(pp));
+            dst[k][2] = *reinterpret_cast<const float2*>(vl + s1.off(pp));
+          } else {
+            dst[k][1] = *reinterpret_cast<const float2*>(vl + 8u * pair_index(V.vw, pp, 64));
+            dst[k][2] = *reinterpret_cast<const float2*>(vl + 8u * pair_index(V.vw + KWD / 2, pp, 64));
+          }
         }
       };
       vread(0, vb[0]);
@@ -641,7 +704,6 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   __shared__ __align__(16) float2 s_vlut[PT];
   __shared__ __align__(16) float2 s_qb[64];
   __shared__ __align__(16) float s_kd0[128];
-  __shared__ __align__(16) float s_q[128];
   __shared__ float s_trev[64];
   __shared__ float s_cb[32];
   // [wave][p * S, p][token]
@@ -656,7 +718,6 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  s_q[tid] = __half2float(a.q[((size_t)b * a.Hq + kvh) * 128 + tid]) * a.scale_log2;
   if (tid < 64) s_trev[tid] = a.rope_off[128 * 64 * 2 + tid] * kInv2Pi;
   if (MODE == NUQ && tid < 32) s_cb[tid] = a.cb[(kvh * 2 + (tid >> 4)) * kCbStride + (tid & 15)];
   if (Dec::MV && tid < 64) s_zero[tid] = (_Float16)0.f;
@@ -683,7 +744,6 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   sh.p = s_pps[w][1];
   sh.M = s_M[w];
   sh.blob = s_dyn;
-  sh.q = s_q;
   sh.trev = s_trev;
   sh.cbk = s_cb;
   sh.cbv = s_cb + 16;
@@ -739,11 +799,11 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   // ---- the fp16 tail (it belongs to the last split)
   if (split == a.splits - 1 && seq_tail(a, b) > 0) {
     float2* qt = s_qb;
-    if (tid < 64) {
-      // query rotated back by the tail block's base angle
-      const float2 rb = reinterpret_cast<const float2*>(a.rope_base)[(size_t)seq_nblk(a, b) * 64 + tid];
-      const float qx = s_q[2 * tid], qy = s_q[2 * tid + 1];
-      qt[tid] = make_float2(fmaf(qx, rb.x, qy * rb.y), fmaf(qy, rb.x, -qx * rb.y));
+    if (d.hb == 0) {
+      // query pair ib rotated back by the tail block's base angle
+      const float2 rb = reinterpret_cast<const float2*>(a.rope_base)[(size_t)seq_nblk(a, b) * 64 + d.ib];
+      const float qx = d.qx_, qy = d.qy_;
+      qt[d.ib] = make_float2(fmaf(qx, rb.x, qy * rb.y), fmaf(qy, rb.x, -qx * rb.y));
     }
     __syncthreads();
     if (64 * d.par < seq_tail(a, b)) d.tail_half(qt);
