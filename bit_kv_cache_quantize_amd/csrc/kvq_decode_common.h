@@ -52,6 +52,19 @@ __device__ __forceinline__ float wave_max(float x) {
   return __int_as_float(m ^ ((m >> 31) & 0x7FFFFFFF));
 }
 
+// Bit pattern of the maximum of non-negative values (the integer order of their bit
+// patterns is their order; a negative value is never above a non-negative one). The result
+// is a scalar: callers derive powers of two from its exponent field with scalar operations.
+__device__ __forceinline__ int wave_max_bits_nonneg(float x) {
+  int v = __float_as_int(x);
+  v = max(v, dpp_i<0xB1>(v));
+  v = max(v, dpp_i<0x4E>(v));
+  v = max(v, dpp_i<0x141>(v));
+  v = max(v, dpp_i<0x140>(v));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
 // Orthonormal 128-point Hadamard transform of a vector held as channel pairs
 // (2*lane, 2*lane+1) across the 64 lanes of a wave.
 __device__ __forceinline__ void fwht_wave(float& x, float& y, int lane) {

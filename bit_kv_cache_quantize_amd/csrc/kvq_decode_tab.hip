@@ -349,19 +349,24 @@ struct TabDecoder {
   // Online-softmax update with this lane's log2-domain score; returns p.
   // The exponent arguments are <= 0 (differences to the running maximum): the hardware
   // exp2 is used directly (results below 2^-126 are flushed to zero; they are below the
-  // rounding of any sum they enter).
+  // rounding of any sum they enter). The running sums are rescaled only when the (wave-
+  // uniform) maximum moved: otherwise the factor is exactly 1.
   __device__ __forceinline__ float softmax_step(float sl) {
     const float mnew = fmaxf(m_run, wave_max(sl));
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
     const float p = __builtin_amdgcn_exp2f(sl - mnew);
-    m_run = mnew;
-    l_run = fmaf(l_run, alpha, p);
-    pm *= alpha;
-    acc0 *= alpha;
-    acc1 *= alpha;
-    if constexpr (MV) {
-      dacc[0] *= alpha;
-      dacc[1] *= alpha;
+    if (mnew != m_run) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+      l_run = fmaf(l_run, alpha, p);
+      pm *= alpha;
+      acc0 *= alpha;
+      acc1 *= alpha;
+      if constexpr (MV) {
+        dacc[0] *= alpha;
+        dacc[1] *= alpha;
+      }
+      m_run = mnew;
+    } else {
+      l_run += p;
     }
     return p;
   }
@@ -469,8 +474,14 @@ struct TabDecoder {
       // after a power of two that puts the half block's largest value scale in [0.5, 1) and
       // the slot's power of two (at most 2^15: within fp16's range; both exact and undone at
       // the end); the accumulators follow the current power of two
-      const float smax = wave_max(V.tst.x);
-      const float vs = smax > 0.f ? __builtin_amdgcn_ldexpf(1.f, -__builtin_amdgcn_frexp_expf(smax)) : 1.f;
+      // (value scales are >= 0; vs = 2^-e for the largest one m * 2^e, m in [0.5, 1): for a
+      // normal maximum of biased exponent E, the float of biased exponent 253 - E)
+      const int sb = wave_max_bits_nonneg(V.tst.x);
+      const int E = (sb >> 23) & 0xFF;
+      float vs;
+      if (sb <= 0) vs = 1.f;
+      else if (E >= 1 && E <= 252) vs = __int_as_float((253 - E) << 23);
+      else vs = __builtin_amdgcn_ldexpf(1.f, -__builtin_amdgcn_frexp_expf(__int_as_float(sb)));
       if (vs != vsc) {
         const float f = vs * recip_pow2(vsc);   // powers of two: exact
         dacc[0] *= f;
@@ -583,27 +594,44 @@ struct TabDecoder {
     const uint8_t* vidx = S.blob + (a.lay.vo_idx - a.lay.ko_val);
     const __half* vval = reinterpret_cast<const __half*>(S.blob + (a.lay.vo_val - a.lay.ko_val));
     const float v0 = MODE == NUQ ? S.cbv[0] : 0.f;
-    const int per = 2 * a.k_out;   // entries per lane
-    const int e0 = lane * per;
-    float tot = 0.f;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      const int t = (int)vidx[e] - 64 * par;
+    // correction of an entry at token t of the block (0 unless t lies in this half)
+    auto corr = [&](int tok, __half x) {
+      const int t = tok - 64 * par;
       const bool mine = t >= 0 && t < 64;
       const int tt = mine ? t : 0;
-      const float c = mine ? S.p[tt] * (__half2float(vval[e]) - fmaf(v0, S.Sv[tt], S.M[tt])) : 0.f;
-      S.pref[e] = c;
-      tot += c;
+      const float c = S.p[tt] * (__half2float(x) - fmaf(v0, S.Sv[tt], S.M[tt]));
+      return mine ? c : 0.f;
+    };
+    const int per = 2 * a.k_out;   // entries per lane
+    const int e0 = lane * per;
+    if (per == 2) {
+      // one outlier per vector: the lane's two entries come in one read each for the
+      // token indices and the values, and stay in registers
+      const uint32_t ti = *reinterpret_cast<const uint16_t*>(vidx + e0);
+      const __half2 xv = *reinterpret_cast<const __half2*>(vval + e0);
+      const float c0 = corr((int)(ti & 0xFF), __low2half(xv));
+      const float c1 = corr((int)(ti >> 8), __high2half(xv));
+      const float tot = c0 + c1;
+      const float run = wave_scan(tot) - tot;
+      *reinterpret_cast<float2*>(S.pref + e0) = make_float2(run, run + c0);
+      if (lane == 63) S.pref[128] = run + tot;
+    } else {
+      float tot = 0.f;
+      for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        const float c = corr((int)vidx[e], vval[e]);
+        S.pref[e] = c;
+        tot += c;
+      }
+      float run = wave_scan(tot) - tot;
+      for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        const float c = S.pref[e];
+        S.pref[e] = run;
+        run += c;
+      }
+      if (lane == 63) S.pref[64 * per] = run;
     }
-    const float incl = wave_scan(tot);
-    float run = incl - tot;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      const float c = S.pref[e];
-      S.pref[e] = run;
-      run += c;
-    }
-    if (lane == 63) S.pref[64 * per] = run;
     wave_sync();
   }
 
