@@ -697,8 +697,10 @@ kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, fl
     // staging for the sparse fix-ups: the outlier segments (table kernel: one copy per
     // workgroup), plus key S/M, value S/M of a half and a RoPE base row (VALU kernel: per wave)
     const uint32_t blob = c->lay.vo_idx + 128u * cfg.outliers_per_vec - c->lay.ko_val;
-    // (table kernel: plus one prefix array of the value-outlier corrections per wave)
-    const uint32_t pref = 2u * (((128u * cfg.outliers_per_vec + 1u) * 4u + 15u) & ~15u);
+    // (table kernel: plus one prefix array of the value-outlier corrections per wave and,
+    // at 2 bits, one array of folded key-outlier entries per wave)
+    const uint32_t pref = 2u * (((128u * cfg.outliers_per_vec + 1u) * 4u + 15u) & ~15u) +
+                          (cfg.bits == 2 ? 2u * 128u * 16u * (uint32_t)cfg.outliers_per_vec : 0u);
     a.wave_lds = (int)(((blob + 15u) & ~15u) + (tab ? pref : 1024u + 512u + 512u));
   }
   if (nblk > 0 || !side) {

@@ -106,6 +106,7 @@ struct TabDecoder {
     const _Float16* zero; // 64 zero fp16 (operand rows 2 and 3)
     float* Sv;            // this wave's value scale S per token [64] (outlier corrections)
     float* pref;          // this wave's prefix sums of the value-outlier corrections [128k + 1]
+    float4* kent;         // 2 bits: this wave's key-outlier entries, folded (see key_outliers) [128k]
   };
 
   const DecodeArgs& a;
@@ -441,12 +442,38 @@ struct TabDecoder {
     // (fp16 value - dense value of code 0) times the query coefficient of channel c at
     // in-block offset j: cos(j theta_i) al + sin(j theta_i) be (x channel) or
     // cos(j theta_i) be - sin(j theta_i) al (y channel) of pair i = c / 2.
-    if (a.k_out > 0) {
-      const uint16_t* kptr = reinterpret_cast<const uint16_t*>(S.blob + (a.lay.ko_ptr - a.lay.ko_val));
-      const uint8_t* kidx = S.blob + (a.lay.ko_idx - a.lay.ko_val);
-      const __half* kval = reinterpret_cast<const __half*>(S.blob);
+    if (a.k_out > 0) sc += key_outliers();
+    return sc;
+  }
+
+  // The key-outlier correction of token j. A row holds as many entries as the token has
+  // outlier channels, so the wave runs its loop as often as its longest row. 2 bits: first
+  // every entry of this half's rows is folded once, spread over the lanes in CSR order, into
+  // (x qa, x qb, theta_i / 2 pi) with x = fp16 value - dense value and (qa, qb) = (al, be)
+  // or (be, -al); a row step is then one 16-byte read, the angle and two fma.
+  __device__ __forceinline__ float key_outliers() const {
+    const uint16_t* kptr = reinterpret_cast<const uint16_t*>(S.blob + (a.lay.ko_ptr - a.lay.ko_val));
+    const uint8_t* kidx = S.blob + (a.lay.ko_idx - a.lay.ko_val);
+    const __half* kval = reinterpret_cast<const __half*>(S.blob);
+    float corr = 0.f;
+    if constexpr (BITS == 2) {
+      const int E0 = kptr[64 * par], E1 = kptr[64 * par + 64];
+      for (int e = E0 + lane; e < E1; e += 64) {
+        const int c = kidx[e], i = c >> 1;
+        const float2 q2 = S.qb[i];
+        const float x = __half2float(kval[e]) - S.kd0[c];
+        S.kent[e - E0] = (c & 1) ? make_float4(x * q2.y, -(x * q2.x), S.trev[i], 0.f)
+                                 : make_float4(x * q2.x, x * q2.y, S.trev[i], 0.f);
+      }
+      wave_sync();
+      const int e1 = kptr[j + 1] - E0;
+      for (int e = kptr[j] - E0; e < e1; ++e) {
+        const float4 t = S.kent[e];
+        const float ang = (float)j * t.z;
+        corr = fmaf(__builtin_amdgcn_cosf(ang), t.x, fmaf(__builtin_amdgcn_sinf(ang), t.y, corr));
+      }
+    } else {
       const int e1 = kptr[j + 1];
-      float corr = 0.f;
       for (int e = kptr[j]; e < e1; ++e) {
         const int c = kidx[e], i = c >> 1;
         const float ang = (float)j * S.trev[i];
@@ -455,9 +482,8 @@ struct TabDecoder {
         const float coef = (c & 1) ? fmaf(cj, q2.y, -sj * q2.x) : fmaf(cj, q2.x, sj * q2.y);
         corr = fmaf(__half2float(kval[e]) - S.kd0[c], coef, corr);
       }
-      sc += corr;
     }
-    return sc;
+    return corr;
   }
 
   // Values of this half (channels ch0, ch1) weighted by the probabilities of its
@@ -783,6 +809,8 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
     const int blob16 = a.k_out > 0 ? ((int)(a.lay.vo_idx + 128u * a.k_out - a.lay.ko_val) + 15) & ~15 : 0;
     const int pref16 = ((128 * a.k_out + 1) * 4 + 15) & ~15;
     sh.pref = reinterpret_cast<float*>(s_dyn + blob16 + w * pref16);
+    // 2 bits: then one array of folded key-outlier entries per wave
+    sh.kent = reinterpret_cast<float4*>(s_dyn + blob16 + 2 * pref16 + w * (128 * 16 * a.k_out));
   }
   Dec d(a, sh, lane, w);
 
