@@ -40,17 +40,22 @@ __device__ __forceinline__ int dpp_i(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-  const int b = __float_as_int(x);
-  int v = b ^ ((b >> 31) & 0x7FFFFFFF);
+// The integer image (an involution: it also maps an image back to its float's bits).
+__device__ __forceinline__ int ord_image(int b) { return b ^ ((b >> 31) & 0x7FFFFFFF); }
+
+// Maximum over the wave as an integer image (a scalar: callers can keep running maxima in
+// this form and compare them on the scalar unit).
+__device__ __forceinline__ int wave_max_ord(float x) {
+  int v = ord_image(__float_as_int(x));
   v = max(v, dpp_i<0xB1>(v));
   v = max(v, dpp_i<0x4E>(v));
   v = max(v, dpp_i<0x141>(v));
   v = max(v, dpp_i<0x140>(v));
-  const int m = max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-                    max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
-  return __int_as_float(m ^ ((m >> 31) & 0x7FFFFFFF));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
+
+__device__ __forceinline__ float wave_max(float x) { return __int_as_float(ord_image(wave_max_ord(x))); }
 
 // Bit pattern of the maximum of non-negative values (the integer order of their bit
 // patterns is their order; a negative value is never above a non-negative one). The result

@@ -113,7 +113,8 @@ struct TabDecoder {
   const Shared S;
   const int lane, par, j, ib, hb;
   int ob_bytes, ob_chunks;
-  float m_run, l_run, pm, acc0, acc1;
+  int m_ord;              // running maximum of the scores, as its integer image (ord_image)
+  float l_run, pm, acc0, acc1;
   f4 dacc[2];             // matrix-core accumulators of the two channel groups
   float vsc;              // the power of two dacc is scaled by (wave-uniform)
   float wpre;             // power of two undoing the code scale of this token's operand slot
@@ -121,7 +122,7 @@ struct TabDecoder {
 
   __device__ TabDecoder(const DecodeArgs& args, const Shared& sh, int lane_, int w_)
       : a(args), S(sh), lane(lane_), par(w_), j(64 * w_ + lane_), ib((64 * w_ + lane_) >> 1), hb(lane_ & 1) {
-    m_run = -INFINITY;
+    m_ord = ord_image(__float_as_int(-INFINITY));
     const __half2 q2 = reinterpret_cast<const __half2*>(a.q + ((size_t)blockIdx.z * a.Hq + blockIdx.y) * 128)[ib];
     qx_ = __low2float(q2) * a.scale_log2;
     qy_ = __high2float(q2) * a.scale_log2;
@@ -257,13 +258,10 @@ struct TabDecoder {
     if (a.k_out > 0) S.kd0[2 * ib + hb] = hb ? fmaf(kcode(1, 0u), B.kst.y, B.kst.w) : fmaf(kcode(0, 0u), B.kst.x, B.kst.z);
     constexpr int NA = 1 << BITS;          // codes of the x channel
     constexpr int NB = BITS == 3 ? 4 : 2;  // codes of the y channel covered by this lane
-    float Ax[NA], Bx[NA], Ay[NB], By[NB];
+    // U(a, b) = al kx(a) + be ky(b), W(a, b) = be kx(a) - al ky(b): one fma per value
+    float kx[NA], Ay[NB], By[NB];
 #pragma unroll
-    for (int c = 0; c < NA; ++c) {
-      const float kx = fmaf(kcode(0, c), B.kst.x, B.kst.z);
-      Ax[c] = al * kx;
-      Bx[c] = be * kx;
-    }
+    for (int c = 0; c < NA; ++c) kx[c] = fmaf(kcode(0, c), B.kst.x, B.kst.z);
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
       const int y = NB * hb + c;
@@ -283,7 +281,7 @@ struct TabDecoder {
         ca = ee & 3;
         cbl = (ee >> 2) & 1;
       }
-      return make_float2(Ax[ca] + Ay[cbl], Bx[ca] + By[cbl]);
+      return make_float2(fmaf(al, kx[ca], Ay[cbl]), fmaf(be, kx[ca], By[cbl]));
     };
 #pragma unroll
     for (int e = 0; e < PT / 2; e += 2) {
@@ -347,16 +345,20 @@ struct TabDecoder {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
+  __device__ __forceinline__ float m_run() const { return __int_as_float(ord_image(m_ord)); }
+
   // Online-softmax update with this lane's log2-domain score; returns p.
   // The exponent arguments are <= 0 (differences to the running maximum): the hardware
   // exp2 is used directly (results below 2^-126 are flushed to zero; they are below the
   // rounding of any sum they enter). The running sums are rescaled only when the (wave-
   // uniform) maximum moved: otherwise the factor is exactly 1.
   __device__ __forceinline__ float softmax_step(float sl) {
-    const float mnew = fmaxf(m_run, wave_max(sl));
+    // the maximum on integer images: scalar operations (scores are never NaN)
+    const int mi = max(m_ord, wave_max_ord(sl));
+    const float mnew = __int_as_float(ord_image(mi));
     const float p = __builtin_amdgcn_exp2f(sl - mnew);
-    if (mnew != m_run) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+    if (mi != m_ord) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run() - mnew);
       l_run = fmaf(l_run, alpha, p);
       pm *= alpha;
       acc0 *= alpha;
@@ -365,7 +367,7 @@ struct TabDecoder {
         dacc[0] *= alpha;
         dacc[1] *= alpha;
       }
-      m_run = mnew;
+      m_ord = mi;
     } else {
       l_run += p;
     }
@@ -871,7 +873,7 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   {
     const float l = wave_sum(d.l_run);
     const float pmw = wave_sum(d.pm);
-    if (lane == 0) { s_m[w] = d.m_run; s_l[w] = l; }
+    if (lane == 0) { s_m[w] = d.m_run(); s_l[w] = l; }
     float o0 = d.acc0 + pmw, o1 = d.acc1 + pmw;
     if constexpr (Dec::MV) {
       const float un = 32.f * recip_pow2(d.vsc);   // 2^5 undoes the operand scaling; powers of two: exact
