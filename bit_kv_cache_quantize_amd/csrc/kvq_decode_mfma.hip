@@ -144,11 +144,16 @@ struct MfmaDecoder {
   static constexpr int OFFV = MODE == SYM ? 8 : (1 << (BITS - 1));   // value codes: c - OFFV (centred)
   static constexpr int META = MODE == SYM ? 512 : (MODE == KVARN ? 3072 : 2048);   // ks, vs (, k1, v1) bytes
   static constexpr int NMETA = (META + 1023) / 1024;                              // 16-byte chunks per lane
-  static constexpr int QF16 = MODE == SYM;   // query and key scales are fp16: operand by packed fp16 math
+  static constexpr bool QF16 = MODE == SYM;   // query and key scales are fp16: operand by packed fp16 math
+  // 64-token halves a wave processes per block. 2 bits: whole blocks, so that the block's
+  // Q' operand, statistics and softmax update are made once per block, not once per half;
+  // 4 bits: the record buffers would not fit twice in registers, so a wave takes one half
+  // of every other block (the two waves of a pair share the blocks).
+  static constexpr int NH = BITS == 2 ? 2 : 1;
 
   struct Buf {
-    uint32_t kw[4][KW];       // key chunks of tokens 16*tt + n, channels 32*q .. 32*q+31
-    uint32_t vw[8][VW];       // value chunks of channels 16*ct + n, positions 16*q .. 16*q+15
+    uint32_t kw[4 * NH][KW];  // key chunks of tokens 16*tt + n of the wave's halves, channels 32*q .. 32*q+31
+    uint32_t vw[NH][8][VW];   // per half: value chunks of channels 16*ct + n, positions 16*q .. 16*q+15
     uint4 meta[NMETA];        // block statistics (staged in LDS)
   };
 
@@ -167,8 +172,8 @@ struct MfmaDecoder {
   __device__ MfmaDecoder(const DecodeArgs& args, int lane_, int w_, const float* qs, uint8_t* meta_)
       : a(args), lane(lane_), w(w_), par(w_ & 1), n(lane_ & 15), q(lane_ >> 4),
         lo_mask((lane_ & 8) ? 0xFFFFFFFFu : 0u), meta(meta_) {
-    koff = a.lay.kc + (uint32_t)((64 * par + n) * R + q * (R / 4));
-    voff = a.lay.vc + (uint32_t)(par * (128 * RH) + n * RH + q * (RH / 4));
+    koff = a.lay.kc + (uint32_t)(((NH == 1 ? 64 * par : 0) + n) * R + q * (R / 4));
+    voff = a.lay.vc + (uint32_t)((NH == 1 ? par * (128 * RH) : 0) + n * RH + q * (RH / 4));
     const int h = n & 7;
     const float* qrow = qs + (h < G ? h : 0) * 128 + 32 * q;
     if constexpr (QF16) {
@@ -188,6 +193,9 @@ struct MfmaDecoder {
     pm = 0.f;
     vsc = 1.f;
   }
+
+  // First token of half h of the wave's block (2 bits: both halves; 4 bits: its own half).
+  __device__ __forceinline__ int tb(int h) const { return 64 * (NH == 1 ? par : h); }
 
   // 2^-e for the exponent e of a non-negative finite x (x * 2^-e in [0.5, 1)); 1 for x = 0.
   static __device__ __forceinline__ float pow2_normaliser(float x) {
@@ -215,7 +223,7 @@ struct MfmaDecoder {
     const uint32_t boff = block_off(rel);
     constexpr int soff = 0;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < 4 * NH; ++tt) {
       if constexpr (KW == 4) {
         const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, boff + koff + 16 * tt * R, soff, kNT);
         B.kw[tt][0] = v.x; B.kw[tt][1] = v.y; B.kw[tt][2] = v.z; B.kw[tt][3] = v.w;
@@ -225,14 +233,17 @@ struct MfmaDecoder {
       }
     }
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      if constexpr (VW == 2) {
-        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rs, boff + voff + 16 * ct * RH, soff, kNT);
-        B.vw[ct][0] = v.x; B.vw[ct][1] = v.y;
-      } else {
-        B.vw[ct][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, boff + voff + 16 * ct * RH, soff, kNT);
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const uint32_t o = boff + voff + (uint32_t)h * (128 * RH) + 16 * ct * RH;
+        if constexpr (VW == 2) {
+          const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rs, o, soff, kNT);
+          B.vw[h][ct][0] = v.x; B.vw[h][ct][1] = v.y;
+        } else {
+          B.vw[h][ct][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, o, soff, kNT);
+        }
       }
-    }
 #pragma unroll
     for (int k = 0; k < NMETA; ++k) {
       const u4v v = __builtin_amdgcn_raw_buffer_load_b128(
@@ -337,75 +348,86 @@ struct MfmaDecoder {
     const h8 qb[4] = {make8(qo[0][0], qo[0][1], qo[0][2], qo[0][3]), make8(qo[1][0], qo[1][1], qo[1][2], qo[1][3]),
                       make8(qo[2][0], qo[2][1], qo[2][2], qo[2][3]), make8(qo[3][0], qo[3][1], qo[3][2], qo[3][3])};
 
-    // ---- raw scores for tokens 16*tt + 4*q + e, head n & 7 (KVarN: already in the log2
-    // domain; otherwise the log2 scale is applied inside the exponent)
+    // ---- raw scores for tokens tb(h) + 16*tt + 4*q + e of each half h, head n & 7 (KVarN:
+    // already in the log2 domain; otherwise the log2 scale is applied inside the exponent)
     constexpr bool PRESCALED = MODE == KVARN;
     const float kunscale = recip_pow2(kscale);   // exact: a power of two
-    float sc[4][4];
+    float sc[NH][4][4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      f4 d = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<BITS, OFFK>(B.kw[tt], ks), qb[ks], d, 0, 0, 0);
-      float s1[4] = {1.f, 1.f, 1.f, 1.f};
-      if constexpr (MODE == KVARN) {
-        const float4 t = *reinterpret_cast<const float4*>(k1 + 64 * par + 16 * tt + 4 * q);
-        s1[0] = t.x; s1[1] = t.y; s1[2] = t.z; s1[3] = t.w;
+      for (int tt = 0; tt < 4; ++tt) {
+        f4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<BITS, OFFK>(B.kw[4 * h + tt], ks), qb[ks], d, 0, 0, 0);
+        float s1[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (MODE == KVARN) {
+          const float4 t = *reinterpret_cast<const float4*>(k1 + tb(h) + 16 * tt + 4 * q);
+          s1[0] = t.x; s1[1] = t.y; s1[2] = t.z; s1[3] = t.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float full = d[e] + dpp_f<0x128>(d[e]);   // high + low column
+          if constexpr (MODE == KVARN) sc[h][tt][e] = fmaf(full, kunscale, bias) * s1[e] * a.scale_log2;
+          else if constexpr (MODE == RTN) sc[h][tt][e] = fmaf(full, kunscale, bias);
+          else sc[h][tt][e] = full;
+        }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float full = d[e] + dpp_f<0x128>(d[e]);   // high + low column
-        if constexpr (MODE == KVARN) sc[tt][e] = fmaf(full, kunscale, bias) * s1[e] * a.scale_log2;
-        else if constexpr (MODE == RTN) sc[tt][e] = fmaf(full, kunscale, bias);
-        else sc[tt][e] = full;
-      }
-    }
 
-    // ---- online softmax for head n & 7 (16 scores per lane, 4 lanes per head and part)
+    // ---- online softmax for head n & 7 (16 scores per half and lane, 4 lanes per head and part)
     const float sl = PRESCALED ? 1.f : a.scale_log2;
-    float mx = sc[0][0];
+    float mx = sc[0][0][0];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[tt][e]);
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[h][tt][e]);
     mx = rows_max(mx);
     const float mnew = fmaxf(m_run, mx * sl);
     const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
     m_run = mnew;
     // p' = p * S_t (value scale per token; 1 for int4). The value codes enter centred, so
     // the part of sum_t p_t v_t that does not depend on the code is sum_t p_t (M_t + OFFV * S_t).
-    float p[4][4], lsum = 0.f, msum = 0.f;
-    float S_t[4][4], M_t[4][4];
+    float p[NH][4][4], lsum = 0.f, msum = 0.f;
+    float S_t[NH][4][4], M_t[NH][4][4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      if constexpr (MODE != SYM) {
-        const float4 ts = *reinterpret_cast<const float4*>(vS + 64 * par + 16 * tt + 4 * q);
-        const float4 tm = *reinterpret_cast<const float4*>(vM + 64 * par + 16 * tt + 4 * q);
-        S_t[tt][0] = ts.x; S_t[tt][1] = ts.y; S_t[tt][2] = ts.z; S_t[tt][3] = ts.w;
-        M_t[tt][0] = tm.x; M_t[tt][1] = tm.y; M_t[tt][2] = tm.z; M_t[tt][3] = tm.w;
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        if constexpr (MODE != SYM) {
+          const float4 ts = *reinterpret_cast<const float4*>(vS + tb(h) + 16 * tt + 4 * q);
+          const float4 tm = *reinterpret_cast<const float4*>(vM + tb(h) + 16 * tt + 4 * q);
+          S_t[h][tt][0] = ts.x; S_t[h][tt][1] = ts.y; S_t[h][tt][2] = ts.z; S_t[h][tt][3] = ts.w;
+          M_t[h][tt][0] = tm.x; M_t[h][tt][1] = tm.y; M_t[h][tt][2] = tm.z; M_t[h][tt][3] = tm.w;
+        }
       }
-    }
-    // P' = p S_t vscale, vscale a power of two putting the half block's largest S_t in
-    // [0.5, 1) (wave-uniform: every row holds all 64 tokens' scales after the row maximum)
+    // P' = p S_t vscale, vscale a power of two putting the largest S_t of the wave's tokens
+    // in [0.5, 1) (wave-uniform: every row holds all the tokens' scales after the row maximum)
     float vscale = 1.f;
     if constexpr (MODE != SYM) {
       float smax = 0.f;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) smax = fmaxf(smax, S_t[tt][e]);
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) smax = fmaxf(smax, S_t[h][tt][e]);
       vscale = pow2_normaliser(rows_max(smax));
     }
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(fmaf(sc[tt][e], sl, -mnew));
-        lsum += pe;
-        if constexpr (MODE != SYM) msum = fmaf(pe, fmaf((float)OFFV, S_t[tt][e], M_t[tt][e]), msum);
-        p[tt][e] = MODE == SYM ? pe : pe * (S_t[tt][e] * vscale);
+      for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pe = __builtin_amdgcn_exp2f(fmaf(sc[h][tt][e], sl, -mnew));
+          lsum += pe;
+          if constexpr (MODE != SYM) msum = fmaf(pe, fmaf((float)OFFV, S_t[h][tt][e], M_t[h][tt][e]), msum);
+          p[h][tt][e] = MODE == SYM ? pe : pe * (S_t[h][tt][e] * vscale);
+        }
       }
-    }
     l_run = fmaf(l_run, alpha, lsum);
     // RTN: acc holds sum p' codes in units of the current vscale; a new vscale rescales it
     // (exactly, a power of two) together with the softmax correction
@@ -425,24 +447,32 @@ struct MfmaDecoder {
     }
     const float vunscale = recip_pow2(vscale);   // exact: a power of two
 
-    // ---- P' operand, this lane's part, slots in the order of the value chunks
-    uint32_t po[2][4];
+    // ---- P' operand per half, this lane's part, slots in the order of the value chunks
+    h8 b0[NH], b1[NH];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int h = 0; h < NH; ++h) {
+      uint32_t po[2][4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int pa = vpos<BITS>(ks, 2 * s), pbp = vpos<BITS>(ks, 2 * s + 1);
-        po[ks][s] = part2(p[(pa >> 2) & 3][pa & 3], p[(pbp >> 2) & 3][pbp & 3]);
-      }
-    const h8 b0 = make8(po[0][0], po[0][1], po[0][2], po[0][3]);
-    const h8 b1 = make8(po[1][0], po[1][1], po[1][2], po[1][3]);
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int pa = vpos<BITS>(ks, 2 * s), pbp = vpos<BITS>(ks, 2 * s + 1);
+          po[ks][s] = part2(p[h][(pa >> 2) & 3][pa & 3], p[h][(pbp >> 2) & 3][pbp & 3]);
+        }
+      b0[h] = make8(po[0][0], po[0][1], po[0][2], po[0][3]);
+      b1[h] = make8(po[1][0], po[1][1], po[1][2], po[1][3]);
+    }
 
-    // ---- O += V^T P' per 16-channel tile
+    // ---- O += V^T P' per 16-channel tile (every half of the wave's block, then the channel
+    // scales)
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       f4 t = MODE == RTN ? acc[ct] : f4{g, g, g, g};   // KVarN: the code-independent part enters here
-      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<BITS, OFFV>(B.vw[ct], 0), b0, t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<BITS, OFFV>(B.vw[ct], 1), b1, t, 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<BITS, OFFV>(B.vw[h][ct], 0), b0[h], t, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<BITS, OFFV>(B.vw[h][ct], 1), b1[h], t, 0, 0, 0);
+      }
       if constexpr (MODE == RTN) {
         acc[ct] = t;
       } else if constexpr (MODE == KVARN) {
@@ -459,7 +489,7 @@ struct MfmaDecoder {
         acc[ct][3] = fmaf((float)hi[1], t[3], acc[ct][3]);
       }
     }
-    wave_sync();   // the statistics area is rewritten by the next half block
+    wave_sync();   // the statistics area is rewritten by the next block
   }
 
   __device__ __forceinline__ void run(int blo, int bhi) {
@@ -474,7 +504,10 @@ struct MfmaDecoder {
                                              0x00020000);
     }
     Buf A, Bb;
-    int rel = w >> 1;                  // this wave's blocks: rel, rel + 2, ... (relative to blo)
+    // this wave's blocks (relative to blo): 2 bits rel = w, w + 4, ...; 4 bits rel = w / 2,
+    // w / 2 + 2, ... (its half of each)
+    constexpr int step = NH == 2 ? 4 : 2;
+    int rel = NH == 2 ? w : w >> 1;
     const int nb = nb_;
     if (rel >= nb) return;
     fetch(A, rel);
@@ -482,13 +515,13 @@ struct MfmaDecoder {
     // before a block's first use covers that block's loads only; a fetch under a branch would
     // make the counter wait drain the prefetch as well
     while (true) {
-      fetch(Bb, rel + 2);
+      fetch(Bb, rel + step);
       process(A);
-      rel += 2;
+      rel += step;
       if (rel >= nb) break;
-      fetch(A, rel + 2);
+      fetch(A, rel + step);
       process(Bb);
-      rel += 2;
+      rel += step;
       if (rel >= nb) break;
     }
   }
