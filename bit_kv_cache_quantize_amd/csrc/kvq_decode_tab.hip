@@ -180,6 +180,9 @@ struct TabDecoder {
     return (uint32_t)(blk - blo_) * a.lay.rec_bytes;
   }
   static constexpr int kNT = 2;   // cache policy "nt": the code rows are read once
+  // loads of one block: fetch_meta (4), fetch_keys, fetch_vals (2 + the code rows)
+  static constexpr int row_loads(int nbytes) { return nbytes % 16 == 0 ? nbytes / 16 : nbytes / 8; }
+  static constexpr int kBlockLoads = 4 + row_loads(R) + 2 + (MV ? 2 * row_loads(RH) : row_loads(R));
 
   template <int NBYTES>
   __device__ __forceinline__ void load_row_b(uint32_t* w, uint32_t off) const {
@@ -822,10 +825,7 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
     for (int i = 0; i < 64; ++i) { const float2 v = off[i * 128]; rc[i] = v.x; rs[i] = v.y; }
   }
-  // Wait for the angle loads here: the main loop then starts with only the block loads in
-  // flight, the same state as at the end of every iteration, so that the memory-counter
-  // waits inside the loop count exactly those loads.
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);   // the angle loads are issued before the block's
 
   const int blo = split * a.blocks_per_split;
   const int bhi = min(seq_nblk(a, b), blo + a.blocks_per_split);
@@ -837,6 +837,12 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   d.fetch_meta(Mt, blo);
   d.fetch_keys(Kc, blo);
   d.fetch_vals(V, blo);
+  // Wait for the angle loads (the memory counter counts in order) but not for the first
+  // block's: the two latencies overlap, and the main loop starts with only the block loads
+  // in flight, the same state as at the end of every iteration, so that the memory-counter
+  // waits inside the loop count exactly those loads.
+  static_assert(Dec::kBlockLoads < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | Dec::kBlockLoads);   // vmcnt(kBlockLoads)
   __syncthreads();   // the value table is complete
   for (int blk = blo; blk < bhi; ++blk) {
     // the loads of the next block are unconditional (past the split's end they read
