@@ -169,11 +169,21 @@ struct MfmaDecoder {
   float m_run, l_run, pm;     // head n & 7 (l_run, pm: this lane's share)
   float vsc;                  // RTN: the power of two acc is currently scaled by (wave-uniform)
 
-  __device__ MfmaDecoder(const DecodeArgs& args, int lane_, int w_, const float* qs, uint8_t* meta_)
+  __device__ MfmaDecoder(const DecodeArgs& args, int lane_, int w_, uint8_t* meta_)
       : a(args), lane(lane_), w(w_), par(w_ & 1), n(lane_ & 15), q(lane_ >> 4),
         lo_mask((lane_ & 8) ? 0xFFFFFFFFu : 0u), meta(meta_) {
     koff = a.lay.kc + (uint32_t)(((NH == 1 ? 64 * par : 0) + n) * R + q * (R / 4));
     voff = a.lay.vc + (uint32_t)((NH == 1 ? par * (128 * RH) : 0) + n * RH + q * (RH / 4));
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+    pm = 0.f;
+    vsc = 1.f;
+  }
+
+  // The query of head n & 7 (qs: [G][128] in LDS, KVarN: rotated), once per workgroup.
+  __device__ __forceinline__ void set_query(const float* qs) {
     const int h = n & 7;
     const float* qrow = qs + (h < G ? h : 0) * 128 + 32 * q;
     if constexpr (QF16) {
@@ -186,12 +196,6 @@ struct MfmaDecoder {
 #pragma unroll
       for (int c = 0; c < 32; ++c) qv[c] = h < G ? qrow[c] : 0.f;
     }
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
-    m_run = -INFINITY;
-    l_run = 0.f;
-    pm = 0.f;
-    vsc = 1.f;
   }
 
   // First token of half h of the wave's block (2 bits: both halves; 4 bits: its own half).
@@ -492,7 +496,12 @@ struct MfmaDecoder {
     wave_sync();   // the statistics area is rewritten by the next block
   }
 
-  __device__ __forceinline__ void run(int blo, int bhi) {
+  // The split's records (blocks blo .. bhi-1) and the first block's loads, issued before the
+  // query is ready (the kernel's set-up then overlaps them). Unconditional: a wave without
+  // blocks reads past the resource's range, which returns zeros without a memory access.
+  Buf A, Bb;
+  int rel;
+  __device__ __forceinline__ void begin(int blo, int bhi) {
     blo_ = blo;
     nb_ = max(bhi - blo, 0);
     if (a.pg.table) {
@@ -503,14 +512,16 @@ struct MfmaDecoder {
       rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)(nb_ * a.lay.rec_bytes),
                                              0x00020000);
     }
-    Buf A, Bb;
     // this wave's blocks (relative to blo): 2 bits rel = w, w + 4, ...; 4 bits rel = w / 2,
     // w / 2 + 2, ... (its half of each)
+    rel = NH == 2 ? w : w >> 1;
+    fetch(A, rel);
+  }
+
+  __device__ __forceinline__ void run() {
     constexpr int step = NH == 2 ? 4 : 2;
-    int rel = NH == 2 ? w : w >> 1;
     const int nb = nb_;
     if (rel >= nb) return;
-    fetch(A, rel);
     // the next block is fetched unconditionally (past the end it reads nothing), so the wait
     // before a block's first use covers that block's loads only; a fetch under a branch would
     // make the counter wait drain the prefetch as well
@@ -614,10 +625,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  for (int i = tid; i < G * 128; i += kThreads) {
-    const float v = __half2float(a.q[((size_t)b * a.Hq + (size_t)kvh * G) * 128 + i]);
-    s_q[i] = v;
-    s_qr[i] = v;
+  // the query's loads, then the first block's (their latencies overlap), then the query
+  // into LDS: the compiler's wait for the query registers leaves the block's loads in flight
+  constexpr int NQ = (G * 128 + kThreads - 1) / kThreads;
+  const uint16_t* qsrc = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)kvh * G) * 128;
+  uint32_t qreg[NQ];   // fp16 bits (threads past the end reread the last element)
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) qreg[k] = qsrc[min(tid + k * kThreads, G * 128 - 1)];
+  MfmaDecoder<MODE, BITS, G> d(a, lane, w, s_meta[w]);
+  const int blo = split * a.blocks_per_split;
+  const int bhi = min(seq_nblk(a, b), blo + a.blocks_per_split);
+  d.begin(blo, bhi);
+  __builtin_amdgcn_sched_barrier(0);   // the query's first use stays behind the block's loads
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < G * 128) {
+      const float v = __half2float(__ushort_as_half((unsigned short)qreg[k]));
+      s_q[i] = v;
+      s_qr[i] = v;
+    }
   }
   __syncthreads();
   if constexpr (MODE == KVARN) {
@@ -631,10 +658,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __syncthreads();
   }
 
-  MfmaDecoder<MODE, BITS, G> d(a, lane, w, s_qr, s_meta[w]);
-  const int blo = split * a.blocks_per_split;
-  const int bhi = min(seq_nblk(a, b), blo + a.blocks_per_split);
-  d.run(blo, bhi);
+  d.set_query(s_qr);
+  d.run();
 
   // ---- this wave's matrix-core state
   const int n = lane & 15, q = lane >> 4;
