@@ -7,11 +7,15 @@
 // query heads of one kv head, softmax(scale * q . k_hat) weighted sum of v_hat
 // over all cached tokens, dequantized from the packed codes on the fly.
 //
-// Work decomposition as in the VALU kernel (workgroup = one split of one
-// (sequence, kv head), wave w streams the 64-token half blocks of parity w & 1);
-// the next half block's loads are issued, unconditionally, before the current
-// one is processed, through a buffer resource over the split's records (past the
-// split's end they read nothing). Per wave and 64-token half block:
+// Work decomposition: workgroup = one split of one (sequence, kv head), four
+// waves. At 2 bits wave w streams whole blocks w, w + 4, ... (both 64-token halves:
+// the block's Q' operand, statistics and softmax update are made once); at 4 bits
+// the waves of a pair share blocks, wave w taking half w & 1 of blocks w / 2,
+// w / 2 + 2, ... (two halves' record buffers would not fit in registers). The next
+// block's loads are issued, unconditionally, before the current one is processed,
+// through a buffer resource over the split's records (past the split's end they
+// read nothing); the first block's loads are issued before the query is staged.
+// Per wave and 64-token half block:
 //   * scores S^T = K_codes (64 tokens x 128 channels) . Q' (128 x 16): the
 //     codes enter the matrix core as exact fp16 integers (one bit-field select
 //     into the exponent of 1024 and one packed fma per code pair); Q' = q * s_c
@@ -25,12 +29,12 @@
 //     this possible), split into the same high / low columns; per-channel
 //     scales (KVarN s1, int4 scales) multiply the per-block product before it
 //     is accumulated; the two columns of a head are added once at the end.
-//   * the online softmax runs per head on the 16 scores each lane holds (the
-//     accumulators are rescaled only when some running maximum moved); the fp16
-//     tail is handled by the VALU half-block decoder.
+//   * the online softmax runs per head on the 16 scores per half each lane holds
+//     (the accumulators are rescaled only when some running maximum moved); the
+//     fp16 tail is handled by a vector-unit pass over its rows.
 //   * fp16 has a narrow exponent range, so the fp32 operands are brought near 1 by a
 //     power of two before the split (exact, and undone after the product): Q' per head
-//     by its largest |q_c s_c|, P' per half block by its largest value scale S_t. Data
+//     by its largest |q_c s_c|, P' per block by its largest value scale S_t. Data
 //     of any magnitude in the fp16 input range, and KVarN blocks whose two scales
 //     trade magnitude (s_RTN tiny and s1 huge, or the reverse), keep full precision.
 #include "kvq_decode_common.h"
