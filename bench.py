@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--window", type=int, default=0, help="fp16 window of recent tokens (multiple of 128)")
     p.add_argument("--paged", action="store_true",
                    help="paged cache: records in a page pool behind a shuffled block table")
+    p.add_argument("--no-matrix-cores", action="store_true",
+                   help="decode with every product on the vector unit (kvq_set_matrix_cores(0)), "
+                        "to measure what the matrix cores contribute")
     p.add_argument("--ragged", action="store_true",
                    help="with --paged: sequence b holds its own length in [context/2, context]")
     return p.parse_args()
@@ -73,7 +76,7 @@ def is_streamed(wl):
 
 
 class Bench:
-    def __init__(self, wl, splits, steps_total, sink=0, window=0, paged=False, ragged=False):
+    def __init__(self, wl, splits, steps_total, sink=0, window=0, paged=False, ragged=False, matrix_cores=True):
         import torch
         import bit_kv_cache_quantize_amd as K
         import synth
@@ -107,6 +110,8 @@ class Bench:
         for c in self.caches:
             if splits:
                 c.set_splits(splits)
+            if not matrix_cores:
+                c.set_matrix_cores(0)
             if wl.mode == synth.MODE_NUQ:
                 for layer in range(wl.n_layers):
                     for h in range(wl.n_kv_heads):
@@ -265,11 +270,11 @@ KERNEL_SOURCES = {
 }
 
 
-def decode_kernel_name(wl):
+def decode_kernel_name(wl, matrix_cores=True):
     """The decode kernel the library launches for this cache (same rule as kvq_decode_attn)."""
     if wl.pre_rope and wl.group == 1 and wl.bits in (2, 3) and wl.mode in (0, 1):
         return "decode_tab_kernel"
-    if not wl.pre_rope and wl.outliers_per_vec == 0 and wl.bits in (2, 4) and wl.mode in (0, 2, 3):
+    if matrix_cores and not wl.pre_rope and wl.outliers_per_vec == 0 and wl.bits in (2, 4) and wl.mode in (0, 2, 3):
         return "decode_mfma_kernel"
     return "decode_kernel"
 
@@ -426,7 +431,8 @@ def main():
     if args.ragged and (not args.paged or is_streamed(wl)):
         print("--ragged needs --paged and a resident workload (not the 1M-token one)", file=sys.stderr)
         sys.exit(2)
-    b = Bench(wl, args.splits, args.steps + warmup, args.sink, args.window, args.paged, args.ragged)
+    mc = not args.no_matrix_cores
+    b = Bench(wl, args.splits, args.steps + warmup, args.sink, args.window, args.paged, args.ragged, mc)
     print("cache built", file=sys.stderr, flush=True)
     ms_step, dec, app, step_bytes = b.run(args.steps, warmup)
     dec_ms = sum(dec) / len(dec)
@@ -434,7 +440,7 @@ def main():
     gbs = dbytes / (dec_ms * 1e-3) / 1e9
     layers = wl.n_layers
     rec_payload = record_payload(wl)
-    dec_kernel = decode_kernel_name(wl)
+    dec_kernel = decode_kernel_name(wl, mc)
     if b.streamed:
         # per step: one 128-token block per layer and kv head; the bulk rate separately
         step_app_ms = sum(app) / len(app)
@@ -451,8 +457,9 @@ def main():
     app_gbs = abytes / (app_ms * 1e-3) / 1e9
     copy_gbs = measured_copy_gbs(torch, b.dev)
 
-    def roof(achieved_gbs, kernel, us, algo_bytes):
-        t = measured_traffic(wl.name, kernel)
+    def roof(achieved_gbs, kernel, us, algo_bytes, profiled=True):
+        # the committed counters are those of the default build's kernels
+        t = measured_traffic(wl.name, kernel) if profiled else None
         return {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                 "traffic": None if t is None else round(t / (us * 1e-6) / 1e9, 1),
@@ -461,7 +468,7 @@ def main():
                 "traffic_bytes_per_launch": t}
 
     dec_us = dec_ms * 1e3 / layers
-    roof_dec = roof(gbs, dec_kernel, dec_us, dbytes / layers)
+    roof_dec = roof(gbs, dec_kernel, dec_us, dbytes / layers, profiled=mc)
     roof_app = roof(app_gbs, "quantize_kernel", app_ms * 1e3 / app_launches, abytes / app_launches)
     line = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -473,6 +480,7 @@ def main():
                    "varn_iters": wl.varn_iters if wl.mode == 2 else 0,
                    "sink_tokens": args.sink, "fp16_window": args.window,
                    "paged": args.paged, "ragged_lengths": b.lens if args.ragged else None,
+                   "matrix_cores": mc,
                    "step": ("append one 128-token block to every layer, then decode every layer"
                             if b.streamed else "append the whole context to every layer, then decode every layer")},
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),

@@ -60,6 +60,7 @@ _sig = {
     "kvq_cache_length": [_vp, _i, ctypes.POINTER(ctypes.c_int32)],
     "kvq_cache_reset": [_vp, _i],
     "kvq_set_decode_splits": [_vp, _i],
+    "kvq_set_matrix_cores": [_vp, _i],
     "kvq_block_span": [_vp, _i, _i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)],
     "kvq_tail_span": [_vp, _i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)],
     "kvq_decode_bytes": [_vp, _i, ctypes.POINTER(_sz)],
@@ -198,6 +199,10 @@ def kvq_set_decode_splits(handle: int, splits: int):
     _check(lib.kvq_set_decode_splits(handle, splits), "kvq_set_decode_splits")
 
 
+def kvq_set_matrix_cores(handle: int, enable: int):
+    _check(lib.kvq_set_matrix_cores(handle, enable), "kvq_set_matrix_cores")
+
+
 def kvq_block_span(handle: int, layer: int, b: int, kv_head: int, block: int):
     off, n = _sz(0), _sz(0)
     _check(lib.kvq_block_span(handle, layer, b, kv_head, block, ctypes.byref(off), ctypes.byref(n)), "kvq_block_span")
@@ -321,6 +326,9 @@ class KVCache:
 
     def set_splits(self, splits):
         kvq_set_decode_splits(self.handle, splits)
+
+    def set_matrix_cores(self, enable):
+        kvq_set_matrix_cores(self.handle, int(enable))
 
     def block_bytes(self, layer, b, kv_head, block):
         off, n = kvq_block_span(self.handle, layer, b, kv_head, block)

@@ -160,6 +160,7 @@ struct kvq_cache_s {
   std::vector<float2> lut_host;     // [layer][kv_head][2][kNuqLutStride]
   std::vector<float> rope_host;     // base table then offset table
   int splits_override = 0;
+  bool matrix_cores = true;         // kvq_set_matrix_cores
   int sink = 0, window = 0;         // sink tokens, fp16 window (tokens)
   int ring_rows = kvq::kT;          // fp16 ring of body tokens per tensor: window + 128
   int tail_rows = kvq::kT;          // fp16 rows per tensor: sink + ring
@@ -705,8 +706,8 @@ kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, fl
   }
   if (nblk > 0 || !side) {
     if (tab)
-      st = hip_check(kvq::launch_decode_tab(cfg.mode, cfg.bits, a, cfg.batch, s), "launch decode");
-    else if (kvq::mfma_supported(cfg.mode, cfg.bits, cfg.pre_rope, cfg.outliers_per_vec))
+      st = hip_check(kvq::launch_decode_tab(cfg.mode, cfg.bits, c->matrix_cores, a, cfg.batch, s), "launch decode");
+    else if (c->matrix_cores && kvq::mfma_supported(cfg.mode, cfg.bits, cfg.pre_rope, cfg.outliers_per_vec))
       st = hip_check(kvq::launch_decode_mfma(cfg.mode, cfg.bits, group, a, cfg.batch, s), "launch decode");
     else
       st = hip_check(kvq::launch_decode(cfg.mode, cfg.bits, group, cfg.pre_rope, a, cfg.batch, s), "launch decode");
@@ -877,6 +878,13 @@ kvq_status kvq_set_decode_splits(kvq_cache c, int splits) {
   if (!c) return fail(KVQ_ERR_ARG, "cache handle is NULL");
   if (splits < 0 || splits > KVQ_MAX_SPLITS) return fail(KVQ_ERR_ARG, "splits must be in 0..%d", KVQ_MAX_SPLITS);
   c->splits_override = splits;
+  return ok();
+}
+
+kvq_status kvq_set_matrix_cores(kvq_cache c, int enable) {
+  if (!c) return fail(KVQ_ERR_ARG, "cache handle is NULL");
+  if (enable != 0 && enable != 1) return fail(KVQ_ERR_ARG, "enable must be 0 or 1");
+  c->matrix_cores = enable == 1;
   return ok();
 }
 

@@ -55,7 +55,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // BIG: the outlier segments of a block exceed one 16-byte chunk per thread; the extra chunks
 // are loaded in a loop (kept out of the common instantiation: a load loop under a branch
 // makes the counter wait at its join drain the key and value prefetches).
-template <int MODE, int BITS, bool BIG>
+// MC: matrix cores allowed (false: the 2-bit RTN values use the LDS table of code pairs too,
+// the configuration a caller selects to compare the two).
+template <int MODE, int BITS, bool BIG, bool MC>
 struct TabDecoder {
   static constexpr int R = 16 * BITS;                 // key row bytes
   static constexpr int RH = R / 2;                    // value half-row bytes
@@ -73,7 +75,7 @@ struct TabDecoder {
   static constexpr int KWD = R / 4;                   // dwords of a key row
   // 2-bit RTN values go through the matrix cores (codes are small integers, exact in
   // fp16); NUQ codebook values and 3-bit codes use the LDS table of code pairs.
-  static constexpr bool MV = MODE == RTN && BITS == 2;
+  static constexpr bool MV = MC && MODE == RTN && BITS == 2;
 
   // Loads of the next block, each issued as soon as the registers it refills are dead.
   struct Meta {           // issued after the table build
@@ -754,9 +756,9 @@ struct TabDecoder {
 
 constexpr int kTabThreads = 128;
 
-template <int MODE, int BITS, bool BIG>
+template <int MODE, int BITS, bool BIG, bool MC>
 __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_tab_kernel(DecodeArgs a) {
-  using Dec = TabDecoder<MODE, BITS, BIG>;
+  using Dec = TabDecoder<MODE, BITS, BIG, MC>;
   constexpr int PT = Dec::PT;
   extern __shared__ __align__(16) uint8_t s_dyn[];
   __shared__ __align__(16) float2 s_tab[64 * Dec::PS];
@@ -912,14 +914,14 @@ __global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(2))
   }
 }
 
-template <int MODE, int BITS>
+template <int MODE, int BITS, bool MC = true>
 hipError_t launch_t(const DecodeArgs& a, int batch, hipStream_t s) {
   const bool big = a.k_out > 0 && (a.lay.vo_idx + 128u * a.k_out - a.lay.ko_val + 15u) / 16u > (unsigned)kTabThreads;
   if (big)
-    hipLaunchKernelGGL((decode_tab_kernel<MODE, BITS, true>), dim3(a.splits, a.Hkv, batch), dim3(kTabThreads),
+    hipLaunchKernelGGL((decode_tab_kernel<MODE, BITS, true, MC>), dim3(a.splits, a.Hkv, batch), dim3(kTabThreads),
                        (size_t)a.wave_lds, s, a);   // outlier staging
   else
-    hipLaunchKernelGGL((decode_tab_kernel<MODE, BITS, false>), dim3(a.splits, a.Hkv, batch), dim3(kTabThreads),
+    hipLaunchKernelGGL((decode_tab_kernel<MODE, BITS, false, MC>), dim3(a.splits, a.Hkv, batch), dim3(kTabThreads),
                        (size_t)a.wave_lds, s, a);
   return hipGetLastError();
 }
@@ -930,9 +932,9 @@ bool tab_supported(int mode, int bits, int group, int rope) {
   return rope && group == 1 && (bits == 2 || bits == 3) && (mode == RTN || mode == NUQ);
 }
 
-hipError_t launch_decode_tab(int mode, int bits, const DecodeArgs& a, int batch, hipStream_t s) {
+hipError_t launch_decode_tab(int mode, int bits, bool matrix_cores, const DecodeArgs& a, int batch, hipStream_t s) {
   switch (mode * 8 + bits) {
-    case RTN * 8 + 2: return launch_t<RTN, 2>(a, batch, s);
+    case RTN * 8 + 2: return matrix_cores ? launch_t<RTN, 2>(a, batch, s) : launch_t<RTN, 2, false>(a, batch, s);
     case RTN * 8 + 3: return launch_t<RTN, 3>(a, batch, s);
     case NUQ * 8 + 2: return launch_t<NUQ, 2>(a, batch, s);
     case NUQ * 8 + 3: return launch_t<NUQ, 3>(a, batch, s);

@@ -165,7 +165,7 @@ bool mfma_supported(int mode, int bits, int rope, int k_out);
 hipError_t launch_decode_mfma(int mode, int bits, int group, const DecodeArgs& a, int batch, hipStream_t s);
 // Table decode: pre-RoPE keys, one query head per kv head, 2 or 3 bits, RTN / NUQ.
 bool tab_supported(int mode, int bits, int group, int rope);
-hipError_t launch_decode_tab(int mode, int bits, const DecodeArgs& a, int batch, hipStream_t s);
+hipError_t launch_decode_tab(int mode, int bits, bool matrix_cores, const DecodeArgs& a, int batch, hipStream_t s);
 hipError_t launch_combine(const float* part, float* out, int Hq, int splits, int batch, hipStream_t s);
 // fp16 sink and window tokens of every (sequence, kv head): partial slot side_slot (or out).
 hipError_t launch_decode_fp16(int group, int rope, const DecodeArgs& a, int batch, hipStream_t s);

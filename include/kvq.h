@@ -303,6 +303,16 @@ kvq_status kvq_cache_reset(kvq_cache cache, int layer);
 kvq_status kvq_set_decode_splits(kvq_cache cache, int splits);
 
 /*
+ * Whether decode may use the matrix cores: 1 (default) or 0. With 0 every product runs on the
+ * vector unit: the table kernel's 2-bit RTN value product goes through its LDS table of code
+ * pairs, and caches the matrix-core kernel would take go to the vector-unit kernel. Results
+ * agree within the decode tolerance either way (summation orders differ); the switch exists
+ * to measure what the matrix cores contribute ("KVQuant reading notes" 3.7 and 3.8 run both
+ * products as vector kernels). Returns KVQ_ERR_ARG for another value.
+ */
+kvq_status kvq_set_matrix_cores(kvq_cache cache, int enable);
+
+/*
  * Byte range of one block record inside dev_buf. The record of block j of
  * (layer, sequence b, kv head h) holds, each segment starting on a 16-byte
  * boundary, the record padded to 256 bytes (T = 128 tokens, D = 128 channels,

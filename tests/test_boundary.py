@@ -155,6 +155,12 @@ def test_host_only_state_and_spans():
             K.kvq_set_decode_splits(h, K.KVQ_MAX_SPLITS + 1)
         assert e.value.status == K.KVQ_ERR_ARG
         K.kvq_set_decode_splits(h, 3)
+        for bad in (-1, 2):
+            with pytest.raises(K.KvqError) as e:
+                K.kvq_set_matrix_cores(h, bad)
+            assert e.value.status == K.KVQ_ERR_ARG
+        K.kvq_set_matrix_cores(h, 0)
+        K.kvq_set_matrix_cores(h, 1)
         K.kvq_cache_reset(h, 1)
         # empty layer: q (fp16) + out (fp32) of 2 x 8 heads + 2 kv heads x 2 codebooks of 8 fp32
         assert K.kvq_decode_bytes(h, 0) == 2 * 8 * 128 * (2 + 4) + 2 * 2 * 8 * 4

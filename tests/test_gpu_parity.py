@@ -31,9 +31,10 @@ def K():
     return K
 
 
-def run_case(K, wl, chunks, splits=0, layer=0, check_records=True, scale=0.0):
+def run_case(K, wl, chunks, splits=0, layer=0, check_records=True, scale=0.0, matrix_cores=True):
     """Append the same inputs on both sides, compare every record and the tail, then decode."""
-    _say(f"case {wl.name} B={wl.batch} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} L={sum(chunks)} chunks={chunks}")
+    _say(f"case {wl.name} B={wl.batch} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} L={sum(chunks)} chunks={chunks}"
+         f"{'' if matrix_cores else ' (no matrix cores)'}")
     L = sum(chunks)
     max_tokens = H.ceil128(L)
     cache = K.KVCache(H.lib_cfg(wl, max_tokens))
@@ -72,6 +73,8 @@ def run_case(K, wl, chunks, splits=0, layer=0, check_records=True, scale=0.0):
     out = torch.empty((wl.batch, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
     if splits:
         cache.set_splits(splits)
+    if not matrix_cores:
+        cache.set_matrix_cores(0)
     cache.decode(layer, torch.from_numpy(q).cuda(), out, softmax_scale=scale)
     torch.cuda.synchronize()
     ref = oc.decode(layer, q, scale=scale)
@@ -137,6 +140,22 @@ CASES = {
 def test_parity_modes(K, case):
     wl, chunks = CASES[case]
     run_case(K, wl, chunks)
+
+
+# kvq_set_matrix_cores(0): the table kernel with its 2-bit values through the LDS table, and
+# the vector-unit kernel for the caches the matrix-core kernel takes; the same oracle bar
+NO_MC_CASES = {
+    **{c: CASES[c] for c in ("rtn2_rope_out1_g1", "nuq3_rope_out1_g1", "kvarn2_g4", "sym4_g4", "rtn2_g1_mfma",
+                             "rtn4_g8_mfma", "kvarn2_g8_mfma", "kvarn4_g1_mfma")},
+    "rtn2_rope_out1_g1_long": (small("c5_llama7b_1m_rtn2", n_layers=1, batch=1, n_q_heads=2, n_kv_heads=2),
+                               [4096 + 77]),
+}
+
+
+@pytest.mark.parametrize("case", list(NO_MC_CASES))
+def test_parity_without_matrix_cores(K, case):
+    wl, chunks = NO_MC_CASES[case]
+    run_case(K, wl, chunks, matrix_cores=False)
 
 
 @pytest.mark.parametrize("L", [1, 2, 64, 65, 127, 128, 129, 255, 256, 257])
