@@ -171,7 +171,7 @@ struct MfmaDecoder {
   float qv[QF16 ? 1 : 32];    // fp32 query of head n & 7, channels 32*q .. 32*q+31
   f4 acc[8];                  // O[16*ct + 4*q + e][column n]
   float m_run, l_run, pm;     // head n & 7 (l_run, pm: this lane's share)
-  float vsc;                  // RTN: the power of two acc is currently scaled by (wave-uniform)
+  float vsc;                  // RTN, KVarN: the power of two acc is currently scaled by (wave-uniform)
 
   __device__ MfmaDecoder(const DecodeArgs& args, int lane_, int w_, uint8_t* meta_)
       : a(args), lane(lane_), w(w_), par(w_ & 1), n(lane_ & 15), q(lane_ >> 4),
@@ -360,6 +360,9 @@ struct MfmaDecoder {
     // already in the log2 domain; otherwise the log2 scale is applied inside the exponent)
     constexpr bool PRESCALED = MODE == KVARN;
     const float kunscale = recip_pow2(kscale);   // exact: a power of two
+    // KVarN: the log2 scale folded into the fma's constants (the per-token s1 multiplies after)
+    const float ku = PRESCALED ? kunscale * a.scale_log2 : kunscale;
+    const float kb = PRESCALED ? bias * a.scale_log2 : bias;
     float sc[NH][4][4];
 #pragma unroll
     for (int h = 0; h < NH; ++h)
@@ -377,7 +380,7 @@ struct MfmaDecoder {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float full = d[e] + dpp_f<0x128>(d[e]);   // high + low column
-          if constexpr (MODE == KVARN) sc[h][tt][e] = fmaf(full, kunscale, bias) * s1[e] * a.scale_log2;
+          if constexpr (MODE == KVARN) sc[h][tt][e] = fmaf(full, ku, kb) * s1[e];
           else if constexpr (MODE == RTN) sc[h][tt][e] = fmaf(full, kunscale, bias);
           else sc[h][tt][e] = full;
         }
@@ -424,36 +427,40 @@ struct MfmaDecoder {
           for (int e = 0; e < 4; ++e) smax = fmaxf(smax, S_t[h][tt][e]);
       vscale = pow2_normaliser(rows_max(smax));
     }
+    // pv = p * vscale straight from the exponent (vscale = 2^ev); the sums are taken back to
+    // p's units after the loop (powers of two: exact)
+    const float vunscale = recip_pow2(vscale);   // exact: a power of two
+    const float eshift = MODE == SYM ? -mnew : (float)(__builtin_amdgcn_frexp_expf(vscale) - 1) - mnew;
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(sc[h][tt][e], sl, -mnew));
-          lsum += pe;
-          if constexpr (MODE != SYM) msum = fmaf(pe, fmaf((float)OFFV, S_t[h][tt][e], M_t[h][tt][e]), msum);
-          p[h][tt][e] = MODE == SYM ? pe : pe * (S_t[h][tt][e] * vscale);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[h][tt][e], sl, eshift));
+          lsum += pv;
+          if constexpr (MODE != SYM) msum = fmaf(pv, fmaf((float)OFFV, S_t[h][tt][e], M_t[h][tt][e]), msum);
+          p[h][tt][e] = MODE == SYM ? pv : pv * S_t[h][tt][e];
         }
       }
+    if constexpr (MODE != SYM) lsum *= vunscale;
     l_run = fmaf(l_run, alpha, lsum);
-    // RTN: acc holds sum p' codes in units of the current vscale; a new vscale rescales it
-    // (exactly, a power of two) together with the softmax correction
-    const float arescale = MODE == RTN ? alpha * (vscale * recip_pow2(vsc)) : alpha;   // powers of two: exact
+    // RTN and KVarN: acc holds its sums in units of the current vscale; a new vscale rescales
+    // it (exactly, a power of two) together with the softmax correction
+    constexpr bool VSC = MODE == RTN || MODE == KVARN;
+    const float arescale = VSC ? alpha * (vscale * recip_pow2(vsc)) : alpha;   // powers of two: exact
     if (__builtin_amdgcn_ballot_w64(arescale != 1.f)) {   // a running maximum or the value scale moved
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) acc[ct] *= arescale;
     }
-    if constexpr (MODE == RTN) vsc = vscale;
+    if constexpr (VSC) vsc = vscale;
     float g = 0.f;                     // KVarN: code-independent part, added before the channel s1
     if constexpr (MODE == RTN) {
-      pm = fmaf(pm, alpha, msum);
+      pm = fmaf(pm, alpha, msum * vunscale);
     } else if constexpr (MODE == KVARN) {
-      g = msum * vscale;
-      g = rows_sum(g);
+      g = rows_sum(msum);              // in units of vscale, as the accumulators
       g = lo_mask ? 0.f : g;           // once per head: on the high column
     }
-    const float vunscale = recip_pow2(vscale);   // exact: a power of two
 
     // ---- P' operand per half, this lane's part, slots in the order of the value chunks
     h8 b0[NH], b1[NH];
@@ -485,7 +492,7 @@ struct MfmaDecoder {
         acc[ct] = t;
       } else if constexpr (MODE == KVARN) {
         const float4 v = *reinterpret_cast<const float4*>(v1 + 16 * ct + 4 * q);
-        const float f[4] = {v.x * vunscale, v.y * vunscale, v.z * vunscale, v.w * vunscale};
+        const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[ct][e] = fmaf(f[e], t[e], acc[ct][e]);
       } else {
@@ -676,7 +683,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[ct][e] = d.acc[ct][e] + dpp_f<0x128>(d.acc[ct][e]);   // high + low column
-  if constexpr (MODE == RTN) {
+  if constexpr (MODE == RTN || MODE == KVARN) {
     const float un = recip_pow2(d.vsc);   // the accumulators' value scale, a power of two (exact)
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
