@@ -167,7 +167,7 @@ kvq_status kvq_quantize_append(kvq_cache cache, int layer, const void* k_f16, co
  *   - pre_rope = 1, one query head per kv head, 2 or 3 bits, RTN or NUQ: the table kernel
  *     (per-block LDS tables of the rotated query over the code pairs of each channel pair);
  *   - pre_rope = 0, no outliers, 2 or 4 bits, RTN, KVARN or SYM_INT4: the matrix-core
- *     kernel (products on v_mfma_f32_16x16x32_f16);
+ *     kernel (products on v_mfma_f32_16x16x32_f16), unless kvq_set_matrix_cores(cache, 0);
  *   - every other configuration: the vector-unit kernel. It is correct for all of them but
  *     not tuned: with pre_rope = 1 and with 8 query heads per kv head its per-lane state
  *     exceeds the register file and part of it lives in scratch memory.
