@@ -84,10 +84,11 @@ def _check_state(K, cache, oc, pages, wl, layer, stats, dev_blocks):
             assert np.array_equal(tail[1, :nt], oc.tail_v[layer][u]), f"b{b} h{h} value tail"
 
 
-def _decode(K, cache, oc, pages, wl, layer, stats, dev_blocks, splits=0, scale=0.0):
+def _decode(K, cache, oc, pages, wl, layer, stats, dev_blocks, splits=0, scale=0.0, matrix_cores=True):
     q = H.host_q(wl, layer)
     out = torch.empty((wl.batch, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
     cache.set_splits(splits)
+    cache.set_matrix_cores(matrix_cores)
     table = torch.from_numpy(pages.table).cuda()
     cache.decode_paged(layer, torch.from_numpy(q).cuda(), out, table, softmax_scale=scale)
     torch.cuda.synchronize()
@@ -103,7 +104,7 @@ def _decode(K, cache, oc, pages, wl, layer, stats, dev_blocks, splits=0, scale=0
     return H.attention_close(got, ref), got
 
 
-def run_paged(K, wl, schedule, spare_pages=3, splits=(0,), layer=0, seed=0, scale=0.0):
+def run_paged(K, wl, schedule, spare_pages=3, splits=(0,), layer=0, seed=0, scale=0.0, matrix_cores=True):
     """Append the per-call, per-sequence counts of `schedule` on both sides; check records,
     tails and attention after every call (attention with each split count in `splits`)."""
     B = wl.batch
@@ -137,7 +138,8 @@ def run_paged(K, wl, schedule, spare_pages=3, splits=(0,), layer=0, seed=0, scal
             assert stats.diff <= 1e-4 * stats.codes, f"{stats.diff} of {stats.codes} codes differ"
         if min(pos) > 0:
             for sp in splits:
-                w, _ = _decode(K, cache, oc, pages, wl, layer, stats, dev_blocks, splits=sp, scale=scale)
+                w, _ = _decode(K, cache, oc, pages, wl, layer, stats, dev_blocks, splits=sp, scale=scale,
+                               matrix_cores=matrix_cores)
                 worst = max(worst, w)
     _say(f"  ok: worst attention error {worst:.2e} of the bar")
     return cache, oc, pages
@@ -172,6 +174,13 @@ PAGED_CASES = {
 def test_paged_ragged_parity(K, case):
     wl, schedule = PAGED_CASES[case]
     run_paged(K, wl, schedule)
+
+
+@pytest.mark.parametrize("case", ["rtn2_rope_out1_g1_tab", "kvarn2_g4_mfma", "sym4_g4_mfma"])
+def test_paged_ragged_parity_without_matrix_cores(K, case):
+    """kvq_set_matrix_cores(0) on a paged cache: the same oracle bar on the vector-unit path."""
+    wl, schedule = PAGED_CASES[case]
+    run_paged(K, wl, schedule, splits=(0, 3), matrix_cores=False)
 
 
 def test_paged_split_plans_with_short_sequences(K):
