@@ -656,8 +656,23 @@ kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, fl
     bps = (nblk + splits - 1) / splits;
     splits = (nblk + bps - 1) / bps;
   }
-  // partial slots per (sequence, query head): the splits, plus one for the fp16 part
-  const int part_slots = side ? (nblk > 0 ? splits + 1 : 1) : splits;
+  // the fp16 part (sink tokens and body tokens not yet quantized) in chunks of whole 16-token
+  // groups, one workgroup and one partial each, as many as the free partial slots allow
+  const int q_slots = nblk > 0 ? splits : 0;
+  const int n_fp16 = side ? std::min(L, c->sink) + fp16_body : 0;
+  int n_side = 0, side_chunk = 0;
+  if (side) {
+    int free_slots = KVQ_MAX_SPLITS + 1 - q_slots;
+    if (part) {   // a caller-sized partial array (the static entry point): its capacity too
+      const size_t row_bytes = (size_t)cfg.batch * cfg.n_q_heads * kvq::kPartStride * sizeof(float);
+      free_slots = std::min(free_slots, (int)std::min<size_t>(part_limit / row_bytes, KVQ_MAX_SPLITS + 1) - q_slots);
+    }
+    n_side = std::max(1, std::min((n_fp16 + kvq::kSideChunk - 1) / kvq::kSideChunk, free_slots));
+    side_chunk = std::max(16, ((n_fp16 + n_side - 1) / n_side + 15) / 16 * 16);
+    n_side = std::max(1, (n_fp16 + side_chunk - 1) / side_chunk);
+  }
+  // partial slots per (sequence, query head): the splits, then the fp16 part's
+  const int part_slots = side ? q_slots + n_side : splits;
   if (part && part_slots > 1) {
     const size_t need = (size_t)cfg.batch * cfg.n_q_heads * part_slots * kvq::kPartStride * sizeof(float);
     if (need > part_limit)
@@ -690,7 +705,8 @@ kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, fl
   a.fp16_n = side ? fp16_body : 0;
   a.ring_rows = c->ring_rows;
   a.tail_rows = c->tail_rows;
-  a.side_slot = nblk > 0 ? splits : -1;
+  a.side_slot = part_slots > 1 ? q_slots : -1;
+  a.side_chunk = side_chunk;
   a.pg = pg;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -714,7 +730,7 @@ kvq_status decode_impl(kvq_cache c, int layer, const void* q_f16, float* out, fl
     if (st != KVQ_OK) return st;
   }
   if (side) {
-    st = hip_check(kvq::launch_decode_fp16(group, cfg.pre_rope, a, cfg.batch, s), "launch fp16 decode");
+    st = hip_check(kvq::launch_decode_fp16(group, cfg.pre_rope, a, cfg.batch, n_side, s), "launch fp16 decode");
     if (st != KVQ_OK) return st;
   }
   if (part_slots > 1) {

@@ -162,8 +162,9 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* part_all, flo
 // The same merge for any split count: the (m, l) pairs of all splits are staged in LDS first,
 // so the loads of the per-channel partials are independent and stay in flight together.
 __global__ __launch_bounds__(128) void combine_kernel_lds(const float* part_all, float* out, int Hq, int splits) {
-  __shared__ float s_w[kMaxSplits];
-  __shared__ float s_l[kMaxSplits];
+  // up to kMaxSplits splits plus the partials of the fp16 part (at most kMaxSplits + 1 in all)
+  __shared__ float s_w[kMaxSplits + 1];
+  __shared__ float s_l[kMaxSplits + 1];
   const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
   const size_t row = (size_t)b * Hq + hq;
   const float* part = part_all + row * splits * kPartStride;

@@ -13,6 +13,7 @@ constexpr int kD = 128;          // head dimension
 constexpr int kMaxOut = 8;       // outliers per vector
 constexpr int kPartStride = 2 + kD;  // one split partial: m, l, o[128]
 constexpr int kMaxSplits = 64;       // decode splits per (sequence, kv head)
+constexpr int kSideChunk = 64;       // fp16-part tokens per workgroup (four waves of 16 tokens)
 // Device codebook slot per (layer, kv head, K/V): entries C[0..15], then the NUQ decision
 // thresholds tau[0..14] (see kvq_api.hip).
 constexpr int kCbStride = 32;
@@ -107,8 +108,10 @@ struct DecodeArgs {
   float scale_log2;         // softmax scale * log2(e)
   int wave_lds;             // dynamic LDS bytes per wave for outlier staging (0 without outliers)
   // fp16 part outside the blocks (sink tokens and the body tokens not yet quantized),
-  // decoded by its own kernel when a sink or a window is configured (tail_n is then 0)
-  int sink_n, fp16_u0, fp16_n, ring_rows, tail_rows, side_slot;
+  // decoded by its own kernel when a sink or a window is configured (tail_n is then 0):
+  // side_chunk tokens per workgroup, the partial of workgroup z in slot side_slot + z
+  // (side_slot < 0: one workgroup writes the output itself)
+  int sink_n, fp16_u0, fp16_n, ring_rows, tail_rows, side_slot, side_chunk;
   PagedSeq pg;              // paged caches: per-sequence lengths and the block table
 };
 
@@ -168,7 +171,7 @@ bool tab_supported(int mode, int bits, int group, int rope);
 hipError_t launch_decode_tab(int mode, int bits, bool matrix_cores, const DecodeArgs& a, int batch, hipStream_t s);
 hipError_t launch_combine(const float* part, float* out, int Hq, int splits, int batch, hipStream_t s);
 // fp16 sink and window tokens of every (sequence, kv head): partial slot side_slot (or out).
-hipError_t launch_decode_fp16(int group, int rope, const DecodeArgs& a, int batch, hipStream_t s);
+hipError_t launch_decode_fp16(int group, int rope, const DecodeArgs& a, int batch, int n_side, hipStream_t s);
 hipError_t launch_diag(int mode, int bits, const DiagArgs& a, int batch, hipStream_t s);
 
 }  // namespace kvq

@@ -511,6 +511,22 @@ def test_parity_sink_window_many_splits_and_scale(K):
         run_case_sw(K, wl, [64 * 128 + 300], 2, 128, scale=0.2, splits=splits)
 
 
+def test_parity_sink_window_65_partials(K):
+    """64 block splits plus the fp16 part: 65 partials, the most the merge takes (its LDS
+    staging holds one slot more than the split limit)."""
+    wl = small("c1_single_head_2k_rtn4", batch=1, n_q_heads=2, n_kv_heads=1)
+    run_case_sw(K, wl, [2 + 64 * 128 + 128 + 50], 2, 128, splits=64)
+
+
+@pytest.mark.parametrize("splits", [0, 64])
+def test_parity_long_fp16_part_in_chunks(K, splits):
+    """An fp16 part of 1,184 tokens (100 sink tokens, a 1,024-token window): with automatic
+    splits it is cut into 19 chunks of one 16-token group per wave; with 64 splits one
+    partial slot is left, so one chunk's waves walk 74 groups."""
+    wl = small("c5_llama7b_1m_rtn2", n_layers=1, batch=1, n_q_heads=2, n_kv_heads=2)
+    run_case_sw(K, wl, [100 + 64 * 128 + 1024 + 60], 100, 1024, splits=splits)
+
+
 CASES_8BIT = {
     "rtn8_rope_out1_g1": (small("c5_llama7b_1m_rtn2", n_layers=1, bits=8, batch=2, n_q_heads=2, n_kv_heads=2),
                           [300]),
