@@ -1015,10 +1015,14 @@ __global__ __launch_bounds__(kThreads) void tail_kernel(TailArgs a) {
     ring_src0 = ring_u0 - len;
   }
   const int n_rows = n_sink + ring_count;
+  // workgroup z copies rows 16z .. 16z + 15 of the list (one 16-byte piece per thread and
+  // tensor: a single memory round trip)
+  const int r0 = 16 * (int)blockIdx.z, r1 = min(n_rows, r0 + 16);
+  if (r0 >= r1) return;
   for (int tensor = 0; tensor < 2; ++tensor) {
     const __half* in = (tensor ? a.v_in : a.k_in) + unit * (size_t)a.n_new * kD;
     __half* tl = a.tail + unit * (size_t)(2 * a.tail_rows * kD) + (size_t)tensor * a.tail_rows * kD;
-    for (int id = threadIdx.x; id < n_rows * 16; id += kThreads) {
+    for (int id = r0 * 16 + threadIdx.x; id < r1 * 16; id += kThreads) {
       const int i = id >> 4, ch = (id & 15) * 8;
       int src, dst;
       if (i < n_sink) {
@@ -1064,7 +1068,8 @@ hipError_t launch_quantize(int mode, int bits, const QuantArgs& a, int n_blocks,
 }
 
 hipError_t launch_tail(const TailArgs& a, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(tail_kernel, dim3(a.Hkv, batch), dim3(kThreads), 0, s, a);
+  // one workgroup per 16 rows of the largest list (sink rows and ring slots: tail_rows)
+  hipLaunchKernelGGL(tail_kernel, dim3(a.Hkv, batch, (a.tail_rows + 15) / 16), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
