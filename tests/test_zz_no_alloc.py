@@ -74,3 +74,23 @@ def test_static_scratch_rejects_partials_beyond_its_size():
     cache.set_splits(16)                    # 2.1 MB: fits
     ref, got = _both(K, cache, q)
     assert np.array_equal(got, ref)
+
+
+def test_static_scratch_caps_the_fp16_part_chunks():
+    """A cache with sink tokens and a long fp16 window: kvq_decode_attn cuts the fp16 part into
+    34 chunks (one partial each), but 8 sequences x 64 query heads leave room for only 31
+    partials per (sequence, query head) in the static array, so the static call takes fewer,
+    longer chunks. Both results agree to the attention bar (the merge order differs)."""
+    import bit_kv_cache_quantize_amd as K
+    wl = synth.WORKLOADS["c1_single_head_2k_rtn4"].replace(batch=8, n_q_heads=64, n_kv_heads=8)
+    sink, window = 4, 2048
+    L = sink + 16 * 128 + window + 100
+    _say(f"case sink {sink} window {window} L {L}, batch 8 x 64 query heads")
+    cache = K.KVCache(H.lib_cfg(wl, H.ceil128(L), sink, window))
+    k, v = H.host_kv(wl, 0, 0, L)
+    cache.append(0, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+    q = torch.from_numpy(H.host_q(wl, 0)).cuda()
+    for rep in range(2):
+        ref, got = _both(K, cache, q)
+        assert np.all(np.isfinite(got))
+        H.attention_close(got, ref)
