@@ -181,7 +181,9 @@ kvq_status kvq_decode_attn(kvq_cache cache, int layer, const void* q_f16, float*
  * HIP graph capture, tight serving loops, harnesses that forbid it): kvq_decode_attn with
  * the split partials kept in a library-owned static device array of
  * KVQ_STATIC_SCRATCH_BYTES (8 MiB) instead of the cache buffer's workspace. Same
- * arguments, kernels and results as kvq_decode_attn; it calls no allocating routine.
+ * arguments, kernels and results as kvq_decode_attn (with sink tokens or an fp16 window, the
+ * fp16 part may be cut into fewer chunks, one partial each, to fit the array: the results then
+ * agree within the decode tolerance, not bit for bit); it calls no allocating routine.
  * Each GPU the library runs on holds its own copy of the array until the process ends
  * (looked up once per device, with that device current). Every call on one GPU shares
  * that copy, whatever the handle: calls that overlap on one GPU (different streams or
@@ -189,7 +191,8 @@ kvq_status kvq_decode_attn(kvq_cache cache, int layer, const void* q_f16, float*
  * array's previous contents never matter.
  * Errors: those of kvq_decode_attn (KVQ_ERR_STATE for a paged cache, before any device
  * call), and KVQ_ERR_SIZE (nothing launched) when the call's
- * split partials, splits x batch x n_q_heads x 520 bytes, exceed the array; lower the
+ * split partials, (splits + 1 if the cache keeps an fp16 part) x batch x n_q_heads x 520
+ * bytes, exceed the array; lower the
  * split count with kvq_set_decode_splits. KVQ_ERR_HIP if the array's device address
  * cannot be obtained.
  */
