@@ -434,7 +434,7 @@ def test_parity_extreme_magnitudes(K, case, kscale, vscale):
     _say(f"  ok: worst attention error {worst:.2e} of the bar")
 
 
-def run_case_sw(K, wl, chunks, sink, window, scale=0.0, splits=0):
+def run_case_sw(K, wl, chunks, sink, window, scale=0.0, splits=0, matrix_cores=True):
     """run_case with attention-sink tokens and an fp16 window: the blocks, the fp16 rows
     (sink rows and the ring slots of the body tokens not yet quantized) and the decode."""
     L = sum(chunks)
@@ -452,6 +452,7 @@ def run_case_sw(K, wl, chunks, sink, window, scale=0.0, splits=0):
     out = torch.empty((wl.batch, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
     if splits:
         cache.set_splits(splits)
+    cache.set_matrix_cores(matrix_cores)
     for n in chunks:
         k, v = H.host_kv(wl, 0, pos, n)
         cache.append(0, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
@@ -509,6 +510,12 @@ def test_parity_sink_window_many_splits_and_scale(K):
     wl = small("c1_single_head_2k_rtn4", batch=1, n_q_heads=4, n_kv_heads=1)
     for splits in (1, 3, 64):
         run_case_sw(K, wl, [64 * 128 + 300], 2, 128, scale=0.2, splits=splits)
+
+
+@pytest.mark.parametrize("case", ["table_rtn2_rope_out1", "mfma_kvarn2_g4"])
+def test_parity_sink_and_window_without_matrix_cores(K, case):
+    wl, chunks = SW_CASES[case]
+    run_case_sw(K, wl, chunks, 4, 128, matrix_cores=False)
 
 
 def test_parity_sink_window_65_partials(K):
